@@ -1,0 +1,137 @@
+"""Pins of the oracle's number formats and pool addressing (CPU only)."""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from conftest import golden_rows
+from oracle import numerics as nx
+from oracle import paged
+
+
+# ---- f16 ---------------------------------------------------------------------------------
+
+def test_f16_rounding_worked_example():
+    rows = golden_rows("f16_rounding.txt")
+    assert len(rows) == 2
+    for row in rows:
+        x, want = row[0].split()
+        got = int(nx.f32_to_f16(np.float32(float.fromhex(x)))[()])
+        assert got == int(want, 16), (x, hex(got), want)
+
+
+def test_f16_widening_matches_numpy_for_every_pattern():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = nx.f16_to_f32(bits)
+    lib = bits.view(np.float16).astype(np.float32)
+    nan = np.isnan(lib)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan].view(np.uint32), lib[~nan].view(np.uint32))
+
+
+def test_f16_every_pattern_round_trips():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    back = nx.f32_to_f16(nx.f16_to_f32(bits))
+    e = (bits >> 10) & 0x1F
+    m = bits & 0x3FF
+    is_nan = (e == 31) & (m != 0)
+    assert np.array_equal(back[~is_nan], bits[~is_nan])
+    # NaN stays NaN (quiet NaN, same sign)
+    bn = back[is_nan]
+    assert np.all(((bn >> 10) & 0x1F) == 31) and np.all((bn & 0x3FF) != 0)
+    assert np.array_equal(bn >> 15, bits[is_nan] >> 15)
+
+
+def test_f16_rounding_matches_numpy_on_ties_overflow_subnormals():
+    rng = np.random.default_rng(7)
+    # exact midpoints between neighbouring f16 values (normal and subnormal), and
+    # values a hair above/below them, plus a spread of random magnitudes
+    h = np.arange(0, 0x7BFF, dtype=np.uint32).astype(np.uint16)
+    lo = nx.f16_to_f32(h).astype(np.float64)
+    hi = nx.f16_to_f32(h + 1).astype(np.float64)
+    mids = ((lo + hi) / 2).astype(np.float32)
+    nudged = np.concatenate([np.nextafter(mids, np.float32(np.inf)), np.nextafter(mids, np.float32(0))])
+    special = np.array([65504.0, 65519.0, 65519.996, 65520.0, 65536.0, 1e6, 2.0 ** -24,
+                        2.0 ** -25, 2.0 ** -25 * 1.0000001, 2.0 ** -26, 1e-10, 0.0, -0.0,
+                        np.inf, -np.inf], dtype=np.float32)
+    rand = (rng.standard_normal(200_000) * np.exp(rng.uniform(-20, 12, 200_000))).astype(np.float32)
+    for xs in (mids, -mids, nudged, special, rand):
+        with np.errstate(over="ignore"):
+            lib = xs.astype(np.float16).view(np.uint16)
+        ours = nx.f32_to_f16(xs)
+        assert np.array_equal(ours, lib)
+    assert np.isnan(nx.f16_to_f32(nx.f32_to_f16(np.float32(np.nan))))
+
+
+def test_f16_relative_error_bound():
+    # "Candle model runner" 2.4 "The f16 bound": relative error at most 2^-11 in the normal range
+    rng = np.random.default_rng(3)
+    x = (rng.uniform(-1, 1, 100_000) * np.exp(rng.uniform(-9, 10, 100_000))).astype(np.float32)
+    x = x[(np.abs(x) >= 2.0 ** -14) & (np.abs(x) <= 65504)]
+    y = nx.f16_to_f32(nx.f32_to_f16(x)).astype(np.float64)
+    rel = np.abs(y - x) / np.abs(x.astype(np.float64))
+    assert rel.max() <= 2.0 ** -11
+
+
+# ---- bf16 --------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits,value", [(0x3F80, 1.0), (0xC000, -2.0), (0x4049, 3.140625),
+                                        (0x3EAB, 0.333984375), (0x0001, 2.0 ** -133),
+                                        (0x7F80, np.inf), (0x8000, -0.0)])
+def test_bf16_widening_values(bits, value):
+    got = float(nx.bf16_to_f32(np.uint16(bits)))
+    assert got == value and np.signbit(got) == np.signbit(value)
+
+
+# ---- uint4-g32 dequantisation --------------------------------------------------------------
+
+def test_uint4_dequant_is_exact_rational():
+    rng = np.random.default_rng(11)
+    out, inp = 8, 128
+    q = rng.integers(0, 16, size=(out, inp)).astype(np.uint8)
+    # bf16 scales spanning many binades, bf16 zero points in [0, 15] with fraction bits
+    sc = (rng.uniform(1e-4, 0.05, size=(out, inp // 32))).astype(np.float32)
+    zp = rng.uniform(0, 15, size=(out, inp // 32)).astype(np.float32)
+    from synthetic import fp32_to_bf16_bits
+    sb, zb = fp32_to_bf16_bits(sc), fp32_to_bf16_bits(zp)
+    w = nx.dequant_uint4_g32(q, sb, zb)
+    scv = nx.bf16_to_f32(sb)
+    zpv = nx.bf16_to_f32(zb)
+    for o in range(out):
+        for i in range(inp):
+            g = i // 32
+            exact = (Fraction(int(q[o, i])) - Fraction(float(zpv[o, g]))) * Fraction(float(scv[o, g]))
+            assert Fraction(float(w[o, i])) == exact
+
+
+def test_uint4_dequant_group_boundaries():
+    # code q, zp and scale of element (o, i) come from group i // 32 of row o
+    q = np.full((2, 64), 3, np.uint8)
+    from synthetic import fp32_to_bf16_bits
+    sb = fp32_to_bf16_bits(np.array([[1.0, 2.0], [4.0, 8.0]], np.float32))
+    zb = fp32_to_bf16_bits(np.array([[1.0, 0.0], [2.0, 3.0]], np.float32))
+    w = nx.dequant_uint4_g32(q, sb, zb)
+    assert np.all(w[0, :32] == 2.0) and np.all(w[0, 32:] == 6.0)
+    assert np.all(w[1, :32] == 4.0) and np.all(w[1, 32:] == 0.0)
+
+
+# ---- paged KV pool addressing ----------------------------------------------------------------
+
+def test_kv_address_worked_example():
+    (row,) = golden_rows("kv_address.txt")
+    B = int(row[0])
+    table = [int(v) for v in row[1].split()]
+    pos = int(row[2])
+    blk, slot = paged.kv_location(pos, table, B)
+    assert (blk, slot) == (int(row[3]), int(row[4]))
+    D = 128
+    for h in range(8):
+        assert paged.slab_offset(h, slot, B, D) == (h * 16 + 5) * D
+    # in the pool: the block's slab of layer l's K part, then that offset
+    n_blocks, Hkv, L = 12, 8, 3
+    for layer in range(L):
+        for is_v in (False, True):
+            off = paged.kv_element_offset(layer, is_v, pos, 3, table, n_blocks, Hkv, B, D)
+            slab = B * Hkv * D
+            assert off == ((layer * 2 + int(is_v)) * n_blocks + 9) * slab + (3 * 16 + 5) * D
