@@ -1,0 +1,205 @@
+"""ctypes binding of the C ABI in include/dec.h -- argument marshalling only.
+
+Every function has the name of its C counterpart. Host arrays are numpy int32
+arrays; device buffers are passed as integer addresses (e.g. a torch tensor's
+``data_ptr()``) and streams as integer hipStream_t handles (torch's
+``cuda_stream``). Non-zero return codes raise ``DecError`` with the library's
+message. Nothing here computes any part of the forward pass.
+
+torch is imported before the library is loaded so that the library binds to
+the HIP runtime torch already loaded (same soname), and device pointers and
+streams from torch are valid in it.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+import torch  # noqa: F401  (loads the process's HIP runtime first)
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdec.so")
+
+DEC_OK = 0
+DEC_E_ARG = -1
+DEC_E_UNSUPPORTED = -2
+DEC_E_CAPACITY = -3
+DEC_E_BLOCK = -4
+DEC_E_POSITION = -5
+DEC_E_TOKEN = -6
+DEC_E_HIP = -7
+
+DEC_F32, DEC_BF16, DEC_F16, DEC_UINT4_G32 = 0, 1, 2, 3
+DEC_LOGITS_ALL, DEC_LOGITS_LAST, DEC_LOGITS_NONE = 0, 1, 2
+
+ERROR_NAMES = {DEC_E_ARG: "DEC_E_ARG", DEC_E_UNSUPPORTED: "DEC_E_UNSUPPORTED", DEC_E_CAPACITY: "DEC_E_CAPACITY",
+               DEC_E_BLOCK: "DEC_E_BLOCK", DEC_E_POSITION: "DEC_E_POSITION", DEC_E_TOKEN: "DEC_E_TOKEN",
+               DEC_E_HIP: "DEC_E_HIP"}
+
+
+class DecError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{ERROR_NAMES.get(code, code)}: {msg}")
+        self.code = code
+
+
+class dec_config(ctypes.Structure):
+    _fields_ = [
+        ("n_layers", ctypes.c_int32), ("d_model", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+        ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("ff_hidden", ctypes.c_int32),
+        ("vocab", ctypes.c_int32), ("max_context", ctypes.c_int32), ("rms_eps", ctypes.c_float),
+        ("rope_base", ctypes.c_double), ("rope_split", ctypes.c_int32), ("qk_norm", ctypes.c_int32),
+        ("tie_embeddings", ctypes.c_int32), ("weight_dtype", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+        ("block_tokens", ctypes.c_int32), ("n_blocks", ctypes.c_int32), ("max_rows", ctypes.c_int32),
+        ("max_seqs", ctypes.c_int32),
+    ]
+
+
+class dec_weight_info(ctypes.Structure):
+    _fields_ = [
+        ("name", ctypes.c_char * 32), ("layer", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("offset", ctypes.c_size_t),
+        ("bytes", ctypes.c_size_t), ("scale_offset", ctypes.c_size_t), ("zp_offset", ctypes.c_size_t),
+        ("group_bytes", ctypes.c_size_t),
+    ]
+
+
+EXPORTS = ["dec_check_config", "dec_weight_bytes", "dec_weight_count", "dec_weight_entry", "dec_kv_pool_bytes",
+           "dec_workspace_bytes", "dec_init", "dec_free", "dec_last_error", "dec_prefill", "dec_decode_step",
+           "dec_check_step", "dec_debug_dequant"]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m decoder_forward_pass_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ, VP = ctypes.POINTER, ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p
+    cfgp = P(dec_config)
+    i32p = P(ctypes.c_int32)
+    sig = {
+        "dec_check_config": (ctypes.c_int, [cfgp]),
+        "dec_weight_bytes": (SZ, [cfgp]),
+        "dec_weight_count": (ctypes.c_int, [cfgp]),
+        "dec_weight_entry": (ctypes.c_int, [cfgp, ctypes.c_int, P(dec_weight_info)]),
+        "dec_kv_pool_bytes": (SZ, [cfgp]),
+        "dec_workspace_bytes": (SZ, [cfgp]),
+        "dec_init": (ctypes.c_int, [cfgp, VP, SZ, VP, SZ, VP, SZ, VP, P(VP)]),
+        "dec_free": (None, [VP]),
+        "dec_last_error": (ctypes.c_char_p, [VP]),
+        "dec_prefill": (ctypes.c_int, [VP, VP, I32, i32p, i32p, i32p, i32p, I32, I32, VP]),
+        "dec_decode_step": (ctypes.c_int, [VP, VP, I32, i32p, VP, i32p, i32p, I32, VP, VP]),
+        "dec_check_step": (ctypes.c_int, [cfgp, I32, i32p, i32p, i32p, i32p, I32, I32, ctypes.c_char_p, SZ]),
+        "dec_debug_dequant": (ctypes.c_int, [VP, VP, ctypes.c_int, VP]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+_lib = _load()
+lib = _lib
+
+
+def _i32(a):
+    """A C-contiguous int32 numpy array and its pointer (None stays NULL)."""
+    if a is None:
+        return None, None
+    arr = np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+    return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _check(rc: int, ctx=None) -> None:
+    if rc != DEC_OK:
+        msg = _lib.dec_last_error(ctx)
+        raise DecError(rc, msg.decode() if msg else "")
+
+
+def dec_check_config(cfg: dec_config) -> None:
+    _check(_lib.dec_check_config(ctypes.byref(cfg)))
+
+
+def dec_weight_bytes(cfg: dec_config) -> int:
+    n = _lib.dec_weight_bytes(ctypes.byref(cfg))
+    if n == 0:
+        _check(_lib.dec_check_config(ctypes.byref(cfg)))
+    return n
+
+
+def dec_weight_count(cfg: dec_config) -> int:
+    return _lib.dec_weight_count(ctypes.byref(cfg))
+
+
+def dec_weight_entry(cfg: dec_config, index: int) -> dec_weight_info:
+    info = dec_weight_info()
+    _check(_lib.dec_weight_entry(ctypes.byref(cfg), index, ctypes.byref(info)))
+    return info
+
+
+def dec_kv_pool_bytes(cfg: dec_config) -> int:
+    return _lib.dec_kv_pool_bytes(ctypes.byref(cfg))
+
+
+def dec_workspace_bytes(cfg: dec_config) -> int:
+    return _lib.dec_workspace_bytes(ctypes.byref(cfg))
+
+
+def dec_init(cfg: dec_config, weights: int, weight_bytes: int, kv_pool: int, kv_bytes: int, workspace: int,
+             workspace_bytes: int, stream: int = 0) -> int:
+    out = ctypes.c_void_p()
+    _check(_lib.dec_init(ctypes.byref(cfg), weights, weight_bytes, kv_pool, kv_bytes, workspace, workspace_bytes,
+                         stream or None, ctypes.byref(out)))
+    return out.value
+
+
+def dec_free(ctx: int) -> None:
+    _lib.dec_free(ctx)
+
+
+def dec_last_error(ctx) -> str:
+    m = _lib.dec_last_error(ctx)
+    return m.decode() if m else ""
+
+
+def dec_prefill(ctx: int, stream: int, start, n_new, tokens, block_tables, logits_mode: int, logits: int) -> None:
+    _, sp = _i32(start)
+    nn, np_ = _i32(n_new)
+    _, tp = _i32(tokens)
+    bt = np.ascontiguousarray(np.asarray(block_tables, dtype=np.int32))
+    if bt.ndim != 2:
+        raise ValueError("block_tables must be [n_seqs, max_blocks]")
+    bp = bt.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    _check(_lib.dec_prefill(ctx, stream or None, len(nn), sp, np_, tp, bp, bt.shape[1], logits_mode,
+                            logits or None), ctx)
+
+
+def dec_decode_step(ctx: int, stream: int, positions, block_tables, logits: int, next_tokens: int = 0,
+                    tokens_host=None, tokens_device: int = 0) -> None:
+    pos, pp = _i32(positions)
+    _, tp = _i32(tokens_host)
+    bt = np.ascontiguousarray(np.asarray(block_tables, dtype=np.int32))
+    bp = bt.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    _check(_lib.dec_decode_step(ctx, stream or None, len(pos), tp, tokens_device or None, pp, bp, bt.shape[1],
+                                logits or None, next_tokens or None), ctx)
+
+
+def dec_check_step(cfg: dec_config, start, n_new, tokens, block_tables, logits_mode: int):
+    """Returns (code, message) without raising."""
+    st, sp = _i32(start)
+    _, np_ = _i32(n_new)
+    _, tp = _i32(tokens)
+    bt = np.ascontiguousarray(np.asarray(block_tables, dtype=np.int32))
+    if bt.ndim != 2:
+        bt = bt.reshape(len(st), -1)
+    bp = bt.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    buf = ctypes.create_string_buffer(512)
+    rc = _lib.dec_check_step(ctypes.byref(cfg), len(st), sp, np_, tp, bp, bt.shape[1], logits_mode, buf, 512)
+    return rc, buf.value.decode()
+
+
+def dec_debug_dequant(ctx: int, stream: int, index: int, out: int) -> None:
+    _check(_lib.dec_debug_dequant(ctx, stream or None, index, out), ctx)

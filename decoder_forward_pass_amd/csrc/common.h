@@ -1,0 +1,100 @@
+// Shared definitions of the decoder kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dec.h"
+
+namespace dec {
+
+// ---- vector types ------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// ---- scalar conversions (bit exact, no library rounding modes involved) -------------------
+
+// float -> bf16 bits, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// float -> f16 bits, round to nearest, ties to even (hardware conversion, RNE mode).
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+  _Float16 h = (_Float16)f;
+  return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// uint4-g32 weight: (q - zp) * scale as two separately rounded float32 operations.
+__device__ __forceinline__ float dequant_u4(uint32_t q, float zp, float scale) {
+#pragma clang fp contract(off)
+  float t = (float)q - zp;
+  return t * scale;
+}
+
+// ---- wave reductions (fixed butterfly order: deterministic) -------------------------------
+template <int WIDTH>
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = WIDTH / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, WIDTH);
+  return v;
+}
+template <int WIDTH>
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = WIDTH / 2; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WIDTH));
+  return v;
+}
+
+// ---- per-call batch description (device copies of the host-validated metadata) ------------
+struct BatchDev {
+  const int32_t* row_tok;      // [n_rows]
+  const int32_t* row_pos;      // [n_rows] absolute position
+  const int32_t* row_seq;      // [n_rows] sequence index
+  const int32_t* seq_start;    // [n_seqs]
+  const int32_t* seq_nnew;     // [n_seqs]
+  const int32_t* seq_row0;     // [n_seqs] first row of the sequence
+  const int32_t* block_tables; // [n_seqs][tbl_stride]
+  const int32_t* out_rows;     // [n_out] rows that get logits
+  const int32_t* tiles;        // [n_tiles][2] (sequence, first query row) for prefill attention
+  int32_t tbl_stride;
+  int32_t n_rows, n_seqs, n_out, n_tiles;
+};
+
+// Paged KV pool geometry. The pool is [layers][2][n_blocks][Hkv][B][D].
+struct PoolDev {
+  void* base;
+  int64_t n_blocks;
+  int32_t n_kv_heads, block_tokens, head_dim;
+  __device__ __forceinline__ int64_t slab_elems() const {
+    return (int64_t)n_kv_heads * block_tokens * head_dim;
+  }
+  // element offset of channel 0 of (layer, K=0/V=1, block, kv head, slot)
+  __device__ __forceinline__ int64_t offset(int layer, int kv, int64_t block, int h, int slot) const {
+    return ((((int64_t)layer * 2 + kv) * n_blocks + block) * n_kv_heads + h) * (int64_t)block_tokens *
+               head_dim +
+           (int64_t)slot * head_dim;
+  }
+};
+
+// One weight matrix as a GEMM B operand (rows are output features, [out][in]).
+struct WMat {
+  const void* w;         // f32 / bf16 values, or uint4 codes [out][in/2]
+  const uint16_t* scale; // uint4 only: bf16 [out][in/32]
+  const uint16_t* zp;    // uint4 only
+  int32_t rows;
+};
+
+}  // namespace dec

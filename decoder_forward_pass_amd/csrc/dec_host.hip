@@ -1,0 +1,580 @@
+// Host runtime of the C ABI in dec.h: configuration checks, blob / pool / workspace
+// layout, validation of every call before anything is enqueued, the pinned metadata ring,
+// the RoPE table, and the per-call launch sequence on the caller's stream.
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+
+using namespace dec;
+
+namespace {
+
+thread_local std::string g_err;  // message of the last failure without a ctx
+
+constexpr size_t kAlign = 256;
+constexpr int kSlots = 4;  // pinned metadata staging slots
+constexpr int kPerLayer = 11;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int fail(std::string* err, int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  if (err) *err = buf;
+  return code;
+}
+
+int check_config(const dec_config* c, std::string* err) {
+  if (!c) return fail(err, DEC_E_ARG, "config is NULL");
+  if (c->rope_split != 1) return fail(err, DEC_E_UNSUPPORTED, "rope_split must be 1 (pairs j, j + head_dim/2)");
+  if (c->qk_norm != 1) return fail(err, DEC_E_UNSUPPORTED, "qk_norm must be 1");
+  if (c->tie_embeddings != 1) return fail(err, DEC_E_UNSUPPORTED, "tie_embeddings must be 1");
+  if (c->n_layers < 1) return fail(err, DEC_E_UNSUPPORTED, "n_layers must be >= 1");
+  if (c->d_model < 64 || c->d_model % 64) return fail(err, DEC_E_UNSUPPORTED, "d_model must be a positive multiple of 64");
+  if (c->n_heads < 1 || c->n_kv_heads < 1 || c->n_heads % c->n_kv_heads)
+    return fail(err, DEC_E_UNSUPPORTED, "n_heads must be a positive multiple of n_kv_heads");
+  const int group = c->n_heads / c->n_kv_heads;
+  if (group != 1 && group != 2 && group != 4 && group != 8)
+    return fail(err, DEC_E_UNSUPPORTED, "n_heads / n_kv_heads must be 1, 2, 4 or 8");
+  if (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128)
+    return fail(err, DEC_E_UNSUPPORTED, "head_dim must be 32, 64 or 128");
+  if ((c->n_heads * c->head_dim) % 64 || (c->n_kv_heads * c->head_dim) % 64)
+    return fail(err, DEC_E_UNSUPPORTED, "n_heads*head_dim and n_kv_heads*head_dim must be multiples of 64");
+  if (c->ff_hidden < 64 || c->ff_hidden % 64) return fail(err, DEC_E_UNSUPPORTED, "ff_hidden must be a positive multiple of 64");
+  if (c->vocab < 1) return fail(err, DEC_E_UNSUPPORTED, "vocab must be >= 1");
+  if (c->max_context < 1) return fail(err, DEC_E_UNSUPPORTED, "max_context must be >= 1");
+  if (!(c->rms_eps > 0.f) || !std::isfinite(c->rms_eps)) return fail(err, DEC_E_UNSUPPORTED, "rms_eps must be positive");
+  if (!(c->rope_base > 1.0) || !std::isfinite(c->rope_base)) return fail(err, DEC_E_UNSUPPORTED, "rope_base must be > 1");
+  if (c->weight_dtype != DEC_F32 && c->weight_dtype != DEC_BF16 && c->weight_dtype != DEC_UINT4_G32)
+    return fail(err, DEC_E_UNSUPPORTED, "weight_dtype must be DEC_F32, DEC_BF16 or DEC_UINT4_G32");
+  if (c->kv_dtype != DEC_F32 && c->kv_dtype != DEC_F16) return fail(err, DEC_E_UNSUPPORTED, "kv_dtype must be DEC_F32 or DEC_F16");
+  if (c->block_tokens != 16 && c->block_tokens != 32 && c->block_tokens != 64)
+    return fail(err, DEC_E_UNSUPPORTED, "block_tokens must be 16, 32 or 64");
+  if (c->n_blocks < 1) return fail(err, DEC_E_UNSUPPORTED, "n_blocks must be >= 1 (a pool without blocks is refused)");
+  if (c->max_rows < 1 || c->max_seqs < 1 || c->max_seqs > c->max_rows)
+    return fail(err, DEC_E_UNSUPPORTED, "need 1 <= max_seqs <= max_rows");
+  return DEC_OK;
+}
+
+// ---- weights blob layout -------------------------------------------------------------------
+
+struct Blob {
+  std::vector<dec_weight_info> e;
+  size_t total = 0;
+};
+
+Blob blob_layout(const dec_config& c) {
+  Blob b;
+  size_t off = 0;
+  auto gain = [&](const char* name, int layer, int64_t n) {
+    dec_weight_info w{};
+    snprintf(w.name, sizeof w.name, "%s", name);
+    w.layer = layer;
+    w.dtype = DEC_F32;
+    w.rows = 1;
+    w.cols = n;
+    w.offset = off;
+    w.bytes = (size_t)n * 4;
+    off = align_up(off + w.bytes);
+    b.e.push_back(w);
+  };
+  auto mat = [&](const char* name, int layer, int64_t rows, int64_t cols) {
+    dec_weight_info w{};
+    snprintf(w.name, sizeof w.name, "%s", name);
+    w.layer = layer;
+    w.dtype = c.weight_dtype;
+    w.rows = rows;
+    w.cols = cols;
+    w.offset = off;
+    if (c.weight_dtype == DEC_UINT4_G32) {
+      w.bytes = (size_t)(rows * cols / 2);
+      w.group_bytes = (size_t)(rows * (cols / 32) * 2);
+      w.scale_offset = align_up(off + w.bytes);
+      w.zp_offset = align_up(w.scale_offset + w.group_bytes);
+      off = align_up(w.zp_offset + w.group_bytes);
+    } else {
+      w.bytes = (size_t)(rows * cols * (c.weight_dtype == DEC_F32 ? 4 : 2));
+      off = align_up(off + w.bytes);
+    }
+    b.e.push_back(w);
+  };
+  const int64_t d = c.d_model, qw = (int64_t)c.n_heads * c.head_dim, kvw = (int64_t)c.n_kv_heads * c.head_dim;
+  mat("embed", -1, c.vocab, d);
+  for (int l = 0; l < c.n_layers; ++l) {
+    gain("attn_norm", l, d);
+    mat("wq", l, qw, d);
+    mat("wk", l, kvw, d);
+    mat("wv", l, kvw, d);
+    gain("q_norm", l, c.head_dim);
+    gain("k_norm", l, c.head_dim);
+    mat("wo", l, d, qw);
+    gain("ffn_norm", l, d);
+    mat("w_gate", l, c.ff_hidden, d);
+    mat("w_up", l, c.ff_hidden, d);
+    mat("w_down", l, d, c.ff_hidden);
+  }
+  gain("final_norm", -1, d);
+  b.total = off;
+  return b;
+}
+
+size_t kv_bytes(const dec_config& c) {
+  return (size_t)c.n_layers * 2 * (size_t)c.n_blocks * c.n_kv_heads * c.block_tokens * c.head_dim *
+         (c.kv_dtype == DEC_F32 ? 4 : 2);
+}
+
+// ---- workspace layout ----------------------------------------------------------------------
+
+struct Ws {
+  size_t rope, meta, x, h, qkv, q, o, a, part, total;
+  size_t meta_ints;  // capacity of the metadata region in int32
+  int chunk, nch_max, max_blocks_per_seq, max_tiles;
+  int act_bytes, kv_el;
+};
+
+Ws ws_layout(const dec_config& c) {
+  Ws w{};
+  const size_t R = (size_t)c.max_rows, S = (size_t)c.max_seqs;
+  const size_t d = c.d_model, D = c.head_dim, H = c.n_heads;
+  const size_t qw = H * D, qkvw = qw + 2 * (size_t)c.n_kv_heads * D, ff = c.ff_hidden;
+  w.act_bytes = c.weight_dtype == DEC_F32 ? 4 : 2;
+  w.kv_el = c.kv_dtype == DEC_F32 ? 4 : 2;
+  w.max_blocks_per_seq = (c.max_context + c.block_tokens - 1) / c.block_tokens;
+  w.max_tiles = (int)(R / 64 + S);
+  w.chunk = attn_rows_chunk(c.head_dim, c.kv_dtype == DEC_F16, c.n_heads / c.n_kv_heads);
+  w.nch_max = w.chunk ? (c.max_context + w.chunk - 1) / w.chunk : 0;
+  w.meta_ints = 3 * R + 3 * S + R + 2 * (size_t)w.max_tiles + S * (size_t)w.max_blocks_per_seq;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  w.rope = take((size_t)c.max_context * (D / 2) * sizeof(float2));
+  w.meta = take(w.meta_ints * 4);
+  w.x = take(R * d * 4);
+  w.h = take(R * d * w.act_bytes);
+  w.qkv = take(R * qkvw * 4);
+  w.q = take(R * qw * w.kv_el);
+  w.o = take(R * qw * w.act_bytes);
+  w.a = take(R * ff * w.act_bytes);
+  w.part = take(R * H * (size_t)w.nch_max * (D + 2) * 4);
+  w.total = off;
+  return w;
+}
+
+struct LayerW {
+  const float *attn_norm, *q_norm, *k_norm, *ffn_norm;
+  WMat wq, wk, wv, wo, wg, wu, wd;
+};
+
+// Validation of one step; shared by dec_check_step, dec_prefill and dec_decode_step.
+int check_step(const dec_config& c, int32_t S, const int32_t* start, const int32_t* n_new,
+               const int32_t* tokens, const int32_t* tables, int32_t max_blocks, int32_t mode,
+               std::string* err) {
+  if (S <= 0) return fail(err, DEC_E_ARG, "n_seqs must be >= 1");
+  if (S > c.max_seqs) return fail(err, DEC_E_CAPACITY, "n_seqs %d exceeds max_seqs %d", S, c.max_seqs);
+  if (!start) return fail(err, DEC_E_ARG, "start/positions is NULL");
+  if (!tables) return fail(err, DEC_E_ARG, "block_tables is NULL");
+  if (max_blocks <= 0) return fail(err, DEC_E_ARG, "max_blocks must be >= 1");
+  if (mode != DEC_LOGITS_ALL && mode != DEC_LOGITS_LAST && mode != DEC_LOGITS_NONE)
+    return fail(err, DEC_E_ARG, "unknown logits mode %d", mode);
+  int64_t N = 0;
+  for (int s = 0; s < S; ++s) {
+    const int64_t n = n_new ? n_new[s] : 1;
+    if (n < 1) return fail(err, DEC_E_ARG, "sequence %d: n_new must be >= 1", s);
+    if (start[s] < 0) return fail(err, DEC_E_POSITION, "sequence %d: start %d is negative", s, start[s]);
+    if ((int64_t)start[s] + n > c.max_context)
+      return fail(err, DEC_E_POSITION, "sequence %d: positions up to %lld pass max_context %d", s,
+                  (long long)(start[s] + n - 1), c.max_context);
+    N += n;
+  }
+  if (N > c.max_rows) return fail(err, DEC_E_CAPACITY, "%lld new tokens exceed max_rows %d", (long long)N, c.max_rows);
+  if (tokens) {
+    for (int64_t i = 0; i < N; ++i)
+      if (tokens[i] < 0 || tokens[i] >= c.vocab)
+        return fail(err, DEC_E_TOKEN, "token %lld: id %d outside [0, %d)", (long long)i, tokens[i], c.vocab);
+  }
+  // blocks: table long enough, ids in range, blocks receiving new positions not shared
+  std::vector<std::pair<int32_t, int32_t>> written;
+  for (int s = 0; s < S; ++s) {
+    const int64_t n = n_new ? n_new[s] : 1;
+    const int64_t need = (start[s] + n + c.block_tokens - 1) / c.block_tokens;
+    if (need > max_blocks)
+      return fail(err, DEC_E_BLOCK, "sequence %d: block table of %d entries, %lld needed", s, max_blocks, (long long)need);
+    const int32_t* row = tables + (int64_t)s * max_blocks;
+    for (int64_t j = 0; j < need; ++j)
+      if (row[j] < 0 || row[j] >= c.n_blocks)
+        return fail(err, DEC_E_BLOCK, "sequence %d: block id %d at table entry %lld outside [0, %d)", s, row[j],
+                    (long long)j, c.n_blocks);
+    for (int64_t j = start[s] / c.block_tokens; j < need; ++j) written.push_back({row[j], s});
+  }
+  std::sort(written.begin(), written.end());
+  for (size_t i = 1; i < written.size(); ++i)
+    if (written[i].first == written[i - 1].first && written[i].second != written[i - 1].second)
+      return fail(err, DEC_E_BLOCK, "block %d receives new positions of sequences %d and %d", written[i].first,
+                  written[i - 1].second, written[i].second);
+  return DEC_OK;
+}
+
+}  // namespace
+
+struct dec_ctx {
+  dec_config cfg;
+  Blob blob;
+  Ws ws;
+  const uint8_t* w;
+  void* pool;
+  uint8_t* wsp;
+  std::vector<LayerW> layers;
+  WMat embed;
+  const float* final_norm;
+  int32_t* staging[kSlots];
+  hipEvent_t ev[kSlots];
+  int slot;
+  std::string err;
+};
+
+namespace {
+
+WMat wmat(const dec_ctx* c, int idx) {
+  const dec_weight_info& e = c->blob.e[idx];
+  WMat m;
+  m.w = c->w + e.offset;
+  m.scale = e.dtype == DEC_UINT4_G32 ? (const uint16_t*)(c->w + e.scale_offset) : nullptr;
+  m.zp = e.dtype == DEC_UINT4_G32 ? (const uint16_t*)(c->w + e.zp_offset) : nullptr;
+  m.rows = (int32_t)e.rows;
+  return m;
+}
+
+const float* gainp(const dec_ctx* c, int idx) { return (const float*)(c->w + c->blob.e[idx].offset); }
+
+#define HIPCHECK(expr)                                                                        \
+  do {                                                                                        \
+    hipError_t e_ = (expr);                                                                   \
+    if (e_ != hipSuccess) return fail(&ctx->err, DEC_E_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+// Pack the call's metadata into a pinned slot, upload it, and describe it for the kernels.
+int upload_meta(dec_ctx* ctx, hipStream_t st, int32_t S, const int32_t* start, const int32_t* n_new,
+                const int32_t* tokens, const int32_t* tables, int32_t max_blocks, int32_t mode, BatchDev* b,
+                int* max_ctx) {
+  const dec_config& c = ctx->cfg;
+  int32_t N = 0, stride = 1, mc = 0;
+  for (int s = 0; s < S; ++s) {
+    const int32_t n = n_new ? n_new[s] : 1;
+    N += n;
+    stride = std::max<int32_t>(stride, (start[s] + n + c.block_tokens - 1) / c.block_tokens);
+    mc = std::max<int32_t>(mc, start[s] + n);
+  }
+  const int32_t n_out = mode == DEC_LOGITS_ALL ? N : (mode == DEC_LOGITS_LAST ? S : 0);
+  int32_t n_tiles = 0;
+  for (int s = 0; s < S; ++s) n_tiles += ((n_new ? n_new[s] : 1) + 63) / 64;
+  const size_t o_tok = 0, o_pos = N, o_seq = 2 * (size_t)N, o_sst = 3 * (size_t)N, o_snn = o_sst + S,
+               o_sr0 = o_snn + S, o_out = o_sr0 + S, o_til = o_out + n_out, o_tbl = o_til + 2 * (size_t)n_tiles;
+  const size_t total = o_tbl + (size_t)S * stride;
+  if (total > ctx->ws.meta_ints) return fail(&ctx->err, DEC_E_CAPACITY, "call metadata exceeds the workspace");
+
+  const int slot = ctx->slot;
+  ctx->slot = (slot + 1) % kSlots;
+  HIPCHECK(hipEventSynchronize(ctx->ev[slot]));  // the slot's previous upload has finished
+  int32_t* m = ctx->staging[slot];
+  int32_t r = 0, t = 0;
+  for (int s = 0; s < S; ++s) {
+    const int32_t n = n_new ? n_new[s] : 1;
+    m[o_sst + s] = start[s];
+    m[o_snn + s] = n;
+    m[o_sr0 + s] = r;
+    for (int32_t i = 0; i < n; ++i, ++r) {
+      m[o_tok + r] = tokens ? tokens[r] : 0;
+      m[o_pos + r] = start[s] + i;
+      m[o_seq + r] = s;
+      if (mode == DEC_LOGITS_ALL) m[o_out + r] = r;
+    }
+    if (mode == DEC_LOGITS_LAST) m[o_out + s] = r - 1;
+    for (int32_t i = 0; i < n; i += 64, ++t) {
+      m[o_til + 2 * t] = s;
+      m[o_til + 2 * t + 1] = m[o_sr0 + s] + i;
+    }
+    const int32_t need = (start[s] + n + c.block_tokens - 1) / c.block_tokens;
+    for (int32_t j = 0; j < stride; ++j) m[o_tbl + (size_t)s * stride + j] = j < need ? tables[(size_t)s * max_blocks + j] : 0;
+  }
+  int32_t* dm = (int32_t*)(ctx->wsp + ctx->ws.meta);
+  HIPCHECK(hipMemcpyAsync(dm, m, total * 4, hipMemcpyHostToDevice, st));
+  HIPCHECK(hipEventRecord(ctx->ev[slot], st));
+  b->row_tok = dm + o_tok;
+  b->row_pos = dm + o_pos;
+  b->row_seq = dm + o_seq;
+  b->seq_start = dm + o_sst;
+  b->seq_nnew = dm + o_snn;
+  b->seq_row0 = dm + o_sr0;
+  b->out_rows = dm + o_out;
+  b->tiles = dm + o_til;
+  b->block_tables = dm + o_tbl;
+  b->tbl_stride = stride;
+  b->n_rows = N;
+  b->n_seqs = S;
+  b->n_out = n_out;
+  b->n_tiles = n_tiles;
+  *max_ctx = mc;
+  return DEC_OK;
+}
+
+#define LAUNCH(expr)                                                                               \
+  do {                                                                                             \
+    hipError_t e_ = (expr);                                                                        \
+    if (e_ != hipSuccess) return fail(&ctx->err, DEC_E_HIP, "launch %s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+// The forward pass over the uploaded batch: embedding, layers, final norm + LM head, argmax.
+int run_forward(dec_ctx* ctx, hipStream_t st, const BatchDev& b, const int32_t* tok_dev, int max_ctx,
+                float* logits, int32_t* next) {
+  const dec_config& c = ctx->cfg;
+  const Ws& w = ctx->ws;
+  const int N = b.n_rows, d = c.d_model, H = c.n_heads, Hkv = c.n_kv_heads, D = c.head_dim;
+  const int qw = H * D, qkvw = qw + 2 * Hkv * D, ff = c.ff_hidden;
+  const bool act_bf16 = c.weight_dtype != DEC_F32;
+  const bool kv_f16 = c.kv_dtype == DEC_F16;
+  float* x = (float*)(ctx->wsp + w.x);
+  void* h = ctx->wsp + w.h;
+  float* qkv = (float*)(ctx->wsp + w.qkv);
+  void* q = ctx->wsp + w.q;
+  void* o = ctx->wsp + w.o;
+  void* act = ctx->wsp + w.a;
+  float* part = (float*)(ctx->wsp + w.part);
+  const float2* rope = (const float2*)(ctx->wsp + w.rope);
+  PoolDev pool{ctx->pool, c.n_blocks, Hkv, c.block_tokens, D};
+  const int nch = (max_ctx + w.chunk - 1) / w.chunk;
+
+  LAUNCH(launch_embed(tok_dev ? tok_dev : b.row_tok, N, c.vocab, d, c.weight_dtype, ctx->embed, x, st));
+  for (int l = 0; l < c.n_layers; ++l) {
+    const LayerW& L = ctx->layers[l];
+    LAUNCH(launch_rmsnorm(x, nullptr, N, d, L.attn_norm, c.rms_eps, h, act_bf16, st));
+    GemmArgs g{};
+    g.A = h; g.lda = d; g.M = N; g.N = qkvw; g.K = d;
+    g.seg[0] = L.wq; g.seg[1] = L.wk; g.seg[2] = L.wv; g.nseg = 3;
+    g.C = qkv; g.ldc = qkvw;
+    LAUNCH(launch_gemm(c.weight_dtype, EPI_STORE, g, st));
+    QkRopeArgs qa{qkv, L.q_norm, L.k_norm, rope, q, pool, l, H, Hkv, D, c.rms_eps, kv_f16, b};
+    LAUNCH(launch_qk_rope_kv(qa, st));
+    AttnRowsArgs ra{q, pool, l, H, Hkv, D, kv_f16, nch, part, b};
+    LAUNCH(launch_attn_rows(ra, st));
+    LAUNCH(launch_attn_combine(part, N, H, D, nch, w.chunk, b.row_pos, o, act_bf16, st));
+    g = GemmArgs{};
+    g.A = o; g.lda = qw; g.M = N; g.N = d; g.K = qw;
+    g.seg[0] = L.wo; g.nseg = 1; g.C = x; g.ldc = d;
+    LAUNCH(launch_gemm(c.weight_dtype, EPI_RESID, g, st));
+    LAUNCH(launch_rmsnorm(x, nullptr, N, d, L.ffn_norm, c.rms_eps, h, act_bf16, st));
+    g = GemmArgs{};
+    g.A = h; g.lda = d; g.M = N; g.N = ff; g.K = d;
+    g.seg[0] = L.wg; g.seg[1] = L.wu; g.nseg = 2; g.C = act; g.ldc = ff; g.c_bf16 = act_bf16;
+    LAUNCH(launch_gemm(c.weight_dtype, EPI_SWIGLU, g, st));
+    g = GemmArgs{};
+    g.A = act; g.lda = ff; g.M = N; g.N = d; g.K = ff;
+    g.seg[0] = L.wd; g.nseg = 1; g.C = x; g.ldc = d;
+    LAUNCH(launch_gemm(c.weight_dtype, EPI_RESID, g, st));
+  }
+  if (b.n_out > 0 && logits) {
+    LAUNCH(launch_rmsnorm(x, b.out_rows, b.n_out, d, ctx->final_norm, c.rms_eps, h, act_bf16, st));
+    GemmArgs g{};
+    g.A = h; g.lda = d; g.M = b.n_out; g.N = c.vocab; g.K = d;
+    g.seg[0] = ctx->embed; g.nseg = 1; g.C = logits; g.ldc = c.vocab;
+    LAUNCH(launch_gemm(c.weight_dtype, EPI_STORE, g, st));
+    if (next) LAUNCH(launch_argmax(logits, b.n_out, c.vocab, next, st));
+  }
+  return DEC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dec_check_config(const dec_config* cfg) { return check_config(cfg, &g_err); }
+
+size_t dec_weight_bytes(const dec_config* cfg) {
+  if (check_config(cfg, &g_err)) return 0;
+  return blob_layout(*cfg).total;
+}
+
+int dec_weight_count(const dec_config* cfg) {
+  if (check_config(cfg, &g_err)) return 0;
+  return 2 + kPerLayer * cfg->n_layers;
+}
+
+int dec_weight_entry(const dec_config* cfg, int index, dec_weight_info* out) {
+  int rc = check_config(cfg, &g_err);
+  if (rc) return rc;
+  if (!out) return fail(&g_err, DEC_E_ARG, "out is NULL");
+  Blob b = blob_layout(*cfg);
+  if (index < 0 || index >= (int)b.e.size()) return fail(&g_err, DEC_E_ARG, "entry index %d out of range", index);
+  *out = b.e[index];
+  return DEC_OK;
+}
+
+size_t dec_kv_pool_bytes(const dec_config* cfg) {
+  if (check_config(cfg, &g_err)) return 0;
+  return kv_bytes(*cfg);
+}
+
+size_t dec_workspace_bytes(const dec_config* cfg) {
+  if (check_config(cfg, &g_err)) return 0;
+  return ws_layout(*cfg).total;
+}
+
+int dec_check_step(const dec_config* cfg, int32_t n_seqs, const int32_t* start, const int32_t* n_new,
+                   const int32_t* tokens, const int32_t* block_tables, int32_t max_blocks, int32_t logits_mode,
+                   char* msg, size_t msg_len) {
+  std::string err;
+  int rc = check_config(cfg, &err);
+  if (!rc) rc = check_step(*cfg, n_seqs, start, n_new, tokens, block_tables, max_blocks, logits_mode, &err);
+  if (msg && msg_len) snprintf(msg, msg_len, "%s", rc ? err.c_str() : "");
+  return rc;
+}
+
+const char* dec_last_error(const dec_ctx* ctx) { return ctx ? ctx->err.c_str() : g_err.c_str(); }
+
+int dec_init(const dec_config* cfg, const void* weights, size_t weight_bytes, void* kv_pool, size_t kv_bytes_in,
+             void* workspace, size_t workspace_bytes, void* stream, dec_ctx** out) {
+  if (!out) return fail(&g_err, DEC_E_ARG, "out is NULL");
+  *out = nullptr;
+  int rc = check_config(cfg, &g_err);
+  if (rc) return rc;
+  if (!weights || !kv_pool || !workspace) return fail(&g_err, DEC_E_ARG, "weights, kv_pool and workspace must be non-NULL");
+  if (((uintptr_t)weights | (uintptr_t)kv_pool | (uintptr_t)workspace) % kAlign)
+    return fail(&g_err, DEC_E_ARG, "weights, kv_pool and workspace must be 256-byte aligned");
+  dec_ctx* ctx = new dec_ctx();
+  ctx->cfg = *cfg;
+  ctx->blob = blob_layout(*cfg);
+  ctx->ws = ws_layout(*cfg);
+  if (weight_bytes < ctx->blob.total || kv_bytes_in < kv_bytes(*cfg) || workspace_bytes < ctx->ws.total) {
+    rc = fail(&g_err, DEC_E_CAPACITY, "buffers too small: weights %zu < %zu, kv %zu < %zu or workspace %zu < %zu",
+              weight_bytes, ctx->blob.total, kv_bytes_in, kv_bytes(*cfg), workspace_bytes, ctx->ws.total);
+    delete ctx;
+    return rc;
+  }
+  ctx->w = (const uint8_t*)weights;
+  ctx->pool = kv_pool;
+  ctx->wsp = (uint8_t*)workspace;
+  ctx->slot = 0;
+  for (int i = 0; i < kSlots; ++i) {
+    ctx->staging[i] = nullptr;
+    ctx->ev[i] = nullptr;
+  }
+  ctx->embed = wmat(ctx, 0);
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const int b = 1 + l * kPerLayer;
+    LayerW L;
+    L.attn_norm = gainp(ctx, b + 0);
+    L.wq = wmat(ctx, b + 1);
+    L.wk = wmat(ctx, b + 2);
+    L.wv = wmat(ctx, b + 3);
+    L.q_norm = gainp(ctx, b + 4);
+    L.k_norm = gainp(ctx, b + 5);
+    L.wo = wmat(ctx, b + 6);
+    L.ffn_norm = gainp(ctx, b + 7);
+    L.wg = wmat(ctx, b + 8);
+    L.wu = wmat(ctx, b + 9);
+    L.wd = wmat(ctx, b + 10);
+    ctx->layers.push_back(L);
+  }
+  ctx->final_norm = gainp(ctx, 1 + cfg->n_layers * kPerLayer);
+
+  hipStream_t st = (hipStream_t)stream;
+  auto bail = [&](hipError_t e, const char* what) {
+    rc = fail(&g_err, DEC_E_HIP, "%s: %s", what, hipGetErrorString(e));
+    dec_free(ctx);
+    return rc;
+  };
+  for (int i = 0; i < kSlots; ++i) {
+    hipError_t e = hipHostMalloc((void**)&ctx->staging[i], ctx->ws.meta_ints * 4, hipHostMallocDefault);
+    if (e != hipSuccess) return bail(e, "hipHostMalloc");
+    e = hipEventCreateWithFlags(&ctx->ev[i], hipEventDisableTiming);
+    if (e != hipSuccess) return bail(e, "hipEventCreate");
+  }
+  // RoPE table: angle p * base^(-2j/D) in double precision, cos/sin rounded once to float
+  const int half = cfg->head_dim / 2;
+  std::vector<float2> rope((size_t)cfg->max_context * half);
+  for (int j = 0; j < half; ++j) {
+    const double inv = std::pow(cfg->rope_base, -2.0 * j / cfg->head_dim);
+    for (int p = 0; p < cfg->max_context; ++p) {
+      const double ang = (double)p * inv;
+      rope[(size_t)p * half + j] = make_float2((float)std::cos(ang), (float)std::sin(ang));
+    }
+  }
+  hipError_t e = hipMemcpyAsync(ctx->wsp + ctx->ws.rope, rope.data(), rope.size() * sizeof(float2),
+                                hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return bail(e, "hipMemcpyAsync(rope)");
+  e = hipStreamSynchronize(st);  // the host copy of the table goes out of scope
+  if (e != hipSuccess) return bail(e, "hipStreamSynchronize");
+  *out = ctx;
+  return DEC_OK;
+}
+
+void dec_free(dec_ctx* ctx) {
+  if (!ctx) return;
+  for (int i = 0; i < kSlots; ++i) {
+    if (ctx->ev[i]) {
+      (void)hipEventSynchronize(ctx->ev[i]);
+      (void)hipEventDestroy(ctx->ev[i]);
+    }
+    if (ctx->staging[i]) (void)hipHostFree(ctx->staging[i]);
+  }
+  delete ctx;
+}
+
+int dec_prefill(dec_ctx* ctx, void* stream, int32_t n_seqs, const int32_t* start, const int32_t* n_new,
+                const int32_t* tokens, const int32_t* block_tables, int32_t max_blocks, int32_t logits_mode,
+                float* logits) {
+  if (!ctx) return fail(&g_err, DEC_E_ARG, "ctx is NULL");
+  if (!n_new) return fail(&ctx->err, DEC_E_ARG, "n_new is NULL");
+  if (!tokens) return fail(&ctx->err, DEC_E_ARG, "tokens is NULL");
+  int rc = check_step(ctx->cfg, n_seqs, start, n_new, tokens, block_tables, max_blocks, logits_mode, &ctx->err);
+  if (rc) return rc;
+  if (logits_mode != DEC_LOGITS_NONE && !logits) return fail(&ctx->err, DEC_E_ARG, "logits is NULL");
+  hipStream_t st = (hipStream_t)stream;
+  BatchDev b{};
+  int max_ctx = 0;
+  rc = upload_meta(ctx, st, n_seqs, start, n_new, tokens, block_tables, max_blocks, logits_mode, &b, &max_ctx);
+  if (rc) return rc;
+  return run_forward(ctx, st, b, nullptr, max_ctx, logits_mode == DEC_LOGITS_NONE ? nullptr : logits, nullptr);
+}
+
+int dec_decode_step(dec_ctx* ctx, void* stream, int32_t n_seqs, const int32_t* tokens_host,
+                    const int32_t* tokens_device, const int32_t* positions, const int32_t* block_tables,
+                    int32_t max_blocks, float* logits, int32_t* next_tokens) {
+  if (!ctx) return fail(&g_err, DEC_E_ARG, "ctx is NULL");
+  if ((tokens_host == nullptr) == (tokens_device == nullptr))
+    return fail(&ctx->err, DEC_E_ARG, "exactly one of tokens_host and tokens_device must be given");
+  if (next_tokens && !logits) return fail(&ctx->err, DEC_E_ARG, "next_tokens needs logits");
+  const int mode = logits ? DEC_LOGITS_LAST : DEC_LOGITS_NONE;
+  int rc = check_step(ctx->cfg, n_seqs, positions, nullptr, tokens_host, block_tables, max_blocks, mode, &ctx->err);
+  if (rc) return rc;
+  hipStream_t st = (hipStream_t)stream;
+  BatchDev b{};
+  int max_ctx = 0;
+  rc = upload_meta(ctx, st, n_seqs, positions, nullptr, tokens_host, block_tables, max_blocks, mode, &b, &max_ctx);
+  if (rc) return rc;
+  return run_forward(ctx, st, b, tokens_device, max_ctx, logits, next_tokens);
+}
+
+int dec_debug_dequant(dec_ctx* ctx, void* stream, int index, float* out) {
+  if (!ctx) return fail(&g_err, DEC_E_ARG, "ctx is NULL");
+  if (!out) return fail(&ctx->err, DEC_E_ARG, "out is NULL");
+  if (index < 0 || index >= (int)ctx->blob.e.size()) return fail(&ctx->err, DEC_E_ARG, "entry index out of range");
+  const dec_weight_info& e = ctx->blob.e[index];
+  if (e.rows == 1 && e.dtype == DEC_F32 && std::strstr(e.name, "norm"))
+    return fail(&ctx->err, DEC_E_ARG, "entry %d (%s) is a gain vector, not a matrix", index, e.name);
+  LAUNCH(launch_dequant(e.dtype, wmat(ctx, index), (int)e.rows, (int)e.cols, out, (hipStream_t)stream));
+  return DEC_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,211 @@
+// Projections as MFMA GEMMs: C = A . W^T with W stored [out][in] ("Candle model runner"
+// 2.4: W stored [out, in], y = x W^T). A is the activation (float32 for float32 weights,
+// bf16 otherwise); W is float32, bf16, or uint4-g32 dequantised in registers while the tile
+// is staged in LDS: w = (q - zp) * scale ("Byte-identical...", "The bar we set"), rounded to
+// bf16 as the MFMA operand.
+//
+// Batch invariance: every output element is accumulated by one MFMA instruction type per
+// weight format (v_mfma_f32_16x16x4_f32 or v_mfma_f32_16x16x32_bf16), over K in ascending
+// order into a single accumulator, with no split of K. The row's result therefore does not
+// depend on M, on the tile a row falls in, or on the other rows.
+//
+// Epilogues: store float32 (Q/K/V, logits), add into the float32 residual stream (output
+// projection, down projection), SwiGLU silu(gate) * up on two B matrices computed by the same
+// block ("Candle model runner" 2.4, silu on the gate only).
+#include "kernels.h"
+
+namespace dec {
+
+template <int WF, int EPI>
+__global__ __launch_bounds__(256) void gemm_tile64(GemmArgs a) {
+  constexpr bool F32 = WF == DEC_F32;
+  constexpr int BM = 64, BN = 64;
+  constexpr int BK = F32 ? 16 : 64;  // elements of K per LDS tile
+  constexpr int RW = F32 ? 17 : 36;  // LDS row stride in 32-bit words (padded)
+  constexpr int NB = EPI == EPI_SWIGLU ? 2 : 1;
+  __shared__ uint32_t As[BM * RW];
+  __shared__ uint32_t Bs[NB][BN * RW];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int M = a.M, K = a.K;
+
+  WMat bm[NB];
+  int br0;
+  if constexpr (EPI == EPI_SWIGLU) {
+    bm[0] = a.seg[0];
+    bm[1] = a.seg[1];
+    br0 = n0;
+  } else {
+    int s = 0, base = 0;
+    while (s < a.nseg - 1 && n0 >= base + a.seg[s].rows) {
+      base += a.seg[s].rows;
+      ++s;
+    }
+    bm[0] = a.seg[s];
+    br0 = n0 - base;
+  }
+
+  f32x4 acc[NB][2][2];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[nb][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int k0 = 0; k0 < K; k0 += BK) {
+    // ---- stage A
+    if constexpr (F32) {
+      const int row = tid >> 2, c4 = tid & 3;
+      const int gm = min(m0 + row, M - 1);
+      const float4 v = *(const float4*)((const float*)a.A + (int64_t)gm * a.lda + k0 + c4 * 4);
+      uint32_t* d = As + row * RW + c4 * 4;
+      d[0] = __float_as_uint(v.x);
+      d[1] = __float_as_uint(v.y);
+      d[2] = __float_as_uint(v.z);
+      d[3] = __float_as_uint(v.w);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int c = tid + 256 * i;
+        const int row = c >> 3, c8 = c & 7;
+        const int gm = min(m0 + row, M - 1);
+        const u32x4 v = *(const u32x4*)((const uint16_t*)a.A + (int64_t)gm * a.lda + k0 + c8 * 8);
+        *(u32x4*)(As + row * RW + c8 * 4) = v;
+      }
+    }
+    // ---- stage B (one or two matrices)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int brows = bm[nb].rows;
+      if constexpr (WF == DEC_F32) {
+        const int row = tid >> 2, c4 = tid & 3;
+        const int gr = min(br0 + row, brows - 1);
+        const float4 v = *(const float4*)((const float*)bm[nb].w + (int64_t)gr * K + k0 + c4 * 4);
+        uint32_t* d = Bs[nb] + row * RW + c4 * 4;
+        d[0] = __float_as_uint(v.x);
+        d[1] = __float_as_uint(v.y);
+        d[2] = __float_as_uint(v.z);
+        d[3] = __float_as_uint(v.w);
+      } else if constexpr (WF == DEC_BF16) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int c = tid + 256 * i;
+          const int row = c >> 3, c8 = c & 7;
+          const int gr = min(br0 + row, brows - 1);
+          const u32x4 v = *(const u32x4*)((const uint16_t*)bm[nb].w + (int64_t)gr * K + k0 + c8 * 8);
+          *(u32x4*)(Bs[nb] + row * RW + c8 * 4) = v;
+        }
+      } else {
+        const int row = tid >> 2, kq = (tid & 3) * 16;
+        const int gr = min(br0 + row, brows - 1);
+        const u32x2 codes =
+            *(const u32x2*)((const uint8_t*)bm[nb].w + (int64_t)gr * (K / 2) + (k0 + kq) / 2);
+        const int64_t gi = (int64_t)gr * (K / 32) + (k0 + kq) / 32;
+        const float zp = bf16_bits_to_f32(bm[nb].zp[gi]);
+        const float sc = bf16_bits_to_f32(bm[nb].scale[gi]);
+        uint32_t* d = Bs[nb] + row * RW + kq / 2;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const uint32_t byte = (codes[j >> 2] >> ((j & 3) * 8)) & 0xffu;
+          const float lo = dequant_u4(byte & 15u, zp, sc);
+          const float hi = dequant_u4(byte >> 4, zp, sc);
+          d[j] = (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- MFMA over the tile, K ascending
+    if constexpr (F32) {
+#pragma unroll
+      for (int ks = 0; ks < BK / 4; ++ks) {
+        float af[2];
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+          af[bi] = __uint_as_float(As[(wm * 32 + bi * 16 + (lane & 15)) * RW + ks * 4 + (lane >> 4)]);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int bj = 0; bj < 2; ++bj) {
+            const float bf =
+                __uint_as_float(Bs[nb][(wn * 32 + bj * 16 + (lane & 15)) * RW + ks * 4 + (lane >> 4)]);
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi)
+              acc[nb][bi][bj] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[bi], bf, acc[nb][bi][bj], 0, 0, 0);
+          }
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < BK / 32; ++ks) {
+        bf16x8 af[2];
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi)
+          af[bi] = __builtin_bit_cast(
+              bf16x8, *(const u32x4*)(As + (wm * 32 + bi * 16 + (lane & 15)) * RW + ks * 16 + (lane >> 4) * 4));
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int bj = 0; bj < 2; ++bj) {
+            const bf16x8 bf = __builtin_bit_cast(
+                bf16x8,
+                *(const u32x4*)(Bs[nb] + (wn * 32 + bj * 16 + (lane & 15)) * RW + ks * 16 + (lane >> 4) * 4));
+#pragma unroll
+            for (int bi = 0; bi < 2; ++bi)
+              acc[nb][bi][bj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[bi], bf, acc[nb][bi][bj], 0, 0, 0);
+          }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds column (lane & 15), rows 4*(lane >> 4) + r of each 16x16 block
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + wm * 32 + bi * 16 + (lane >> 4) * 4 + r;
+        const int n = n0 + wn * 32 + bj * 16 + (lane & 15);
+        if (m >= M || n >= a.N) continue;
+        const int64_t o = (int64_t)m * a.ldc + n;
+        const float v = acc[0][bi][bj][r];
+        if constexpr (EPI == EPI_STORE) {
+          ((float*)a.C)[o] = v;
+        } else if constexpr (EPI == EPI_RESID) {
+          ((float*)a.C)[o] += v;
+        } else {
+          const float u = acc[NB - 1][bi][bj][r];
+          const float y = v / (1.0f + __expf(-v)) * u;
+          if (a.c_bf16)
+            ((uint16_t*)a.C)[o] = f32_to_bf16_bits(y);
+          else
+            ((float*)a.C)[o] = y;
+        }
+      }
+}
+
+template <int WF>
+static hipError_t gemm_epi(int epi, const GemmArgs& a, hipStream_t s) {
+  dim3 g((a.N + 63) / 64, (a.M + 63) / 64), b(256);
+  switch (epi) {
+    case EPI_STORE: gemm_tile64<WF, EPI_STORE><<<g, b, 0, s>>>(a); break;
+    case EPI_RESID: gemm_tile64<WF, EPI_RESID><<<g, b, 0, s>>>(a); break;
+    case EPI_SWIGLU: gemm_tile64<WF, EPI_SWIGLU><<<g, b, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm(int wdtype, int epi, const GemmArgs& a, hipStream_t s) {
+  if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  if (wdtype == DEC_F32) return gemm_epi<DEC_F32>(epi, a, s);
+  if (wdtype == DEC_BF16) return gemm_epi<DEC_BF16>(epi, a, s);
+  if (wdtype == DEC_UINT4_G32) return gemm_epi<DEC_UINT4_G32>(epi, a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dec

@@ -1,0 +1,250 @@
+// Row-wise kernels of the decoder: embedding gather, RMSNorm, fused per-head
+// q/k RMSNorm + split-halves RoPE + paged KV write, greedy argmax, and the
+// debug dequantisation. Every kernel handles each row independently, so a
+// row's result does not depend on the rest of the batch.
+#include "kernels.h"
+
+namespace dec {
+
+// ---- embedding ("Candle model runner" 2.4: the LM head is the embedding matrix itself;
+// x = E[id] for each new token) -----------------------------------------------------------
+
+template <int WF>
+__global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ tok, int vocab, int d,
+                                                    WMat E, float* __restrict__ x) {
+  const int r = blockIdx.x;
+  const int t = tok[r];
+  float* xr = x + (int64_t)r * d;
+  if (t < 0 || t >= vocab) {
+    for (int i = threadIdx.x; i < d; i += blockDim.x) xr[i] = __builtin_nanf("");
+    return;
+  }
+  if constexpr (WF == DEC_F32) {
+    const float* er = (const float*)E.w + (int64_t)t * d;
+    for (int i = threadIdx.x; i < d; i += blockDim.x) xr[i] = er[i];
+  } else if constexpr (WF == DEC_BF16) {
+    const uint16_t* er = (const uint16_t*)E.w + (int64_t)t * d;
+    for (int i = threadIdx.x; i < d; i += blockDim.x) xr[i] = bf16_bits_to_f32(er[i]);
+  } else {
+    const uint8_t* er = (const uint8_t*)E.w + (int64_t)t * (d / 2);
+    const uint16_t* sr = E.scale + (int64_t)t * (d / 32);
+    const uint16_t* zr = E.zp + (int64_t)t * (d / 32);
+    for (int i = threadIdx.x; i < d; i += blockDim.x) {
+      uint32_t byte = er[i >> 1];
+      uint32_t q = (i & 1) ? (byte >> 4) : (byte & 15u);
+      xr[i] = dequant_u4(q, bf16_bits_to_f32(zr[i >> 5]), bf16_bits_to_f32(sr[i >> 5]));
+    }
+  }
+}
+
+hipError_t launch_embed(const int32_t* tok, int n_rows, int vocab, int d, int wdtype, const WMat& E,
+                        float* x, hipStream_t s) {
+  if (n_rows <= 0) return hipSuccess;
+  dim3 g(n_rows), b(256);
+  if (wdtype == DEC_F32)
+    embed_kernel<DEC_F32><<<g, b, 0, s>>>(tok, vocab, d, E, x);
+  else if (wdtype == DEC_BF16)
+    embed_kernel<DEC_BF16><<<g, b, 0, s>>>(tok, vocab, d, E, x);
+  else
+    embed_kernel<DEC_UINT4_G32><<<g, b, 0, s>>>(tok, vocab, d, E, x);
+  return hipGetLastError();
+}
+
+// ---- RMSNorm ("Candle model runner" 2.4, first equation: x / sqrt(mean(x^2) + eps) * w) ---
+// One wave per row; lane i holds elements i, i+64, ...; the sum of squares is
+// added in a fixed order (per lane, then a butterfly), so it is deterministic.
+
+template <bool BF16_OUT>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x,
+                                                      const int32_t* __restrict__ rows, int n, int d,
+                                                      const float* __restrict__ g, float eps,
+                                                      void* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= n) return;
+  const int src = rows ? rows[r] : r;
+  const float* xr = x + (int64_t)src * d;
+  float ss = 0.f;
+  for (int i = lane; i < d; i += 64) ss += xr[i] * xr[i];
+  ss = wave_sum<64>(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+  if constexpr (BF16_OUT) {
+    uint16_t* o = (uint16_t*)out + (int64_t)r * d;
+    for (int i = lane; i < d; i += 64) o[i] = f32_to_bf16_bits(xr[i] * inv * g[i]);
+  } else {
+    float* o = (float*)out + (int64_t)r * d;
+    for (int i = lane; i < d; i += 64) o[i] = xr[i] * inv * g[i];
+  }
+}
+
+hipError_t launch_rmsnorm(const float* x, const int32_t* rows, int n, int d, const float* g, float eps,
+                          void* out, bool out_bf16, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  dim3 grid((n + 3) / 4), b(256);
+  if (out_bf16)
+    rmsnorm_kernel<true><<<grid, b, 0, s>>>(x, rows, n, d, g, eps, out);
+  else
+    rmsnorm_kernel<false><<<grid, b, 0, s>>>(x, rows, n, d, g, eps, out);
+  return hipGetLastError();
+}
+
+// ---- q/k RMSNorm + RoPE + KV write --------------------------------------------------------
+// "A real model in our own decoder": switch 5, an RMSNorm on each query head and each key head
+// before RoPE; "Which channels rotate together": channel j pairs with j + D/2. Angle of pair j
+// at position p: p * base^(-2j/D) ("Byte-identical...", rope table section), precomputed on the
+// host in double precision. Keys/values go to pool block table[pos / B], slot pos % B
+// ("Candle model runner" 2.4 and section 3 "Where a key lands").
+// One wave per (row, head) over the H query heads, H_kv key heads and H_kv value heads; lane j
+// holds the pair (j, j + D/2).
+
+template <bool KV_F16>
+__global__ __launch_bounds__(256) void qk_rope_kv_kernel(QkRopeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x;
+  const int hh = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int H = a.n_heads, Hkv = a.n_kv_heads, D = a.head_dim, half = D / 2;
+  if (hh >= H + 2 * Hkv) return;
+  const int pos = a.b.row_pos[r];
+  const float* src = a.qkv + (int64_t)r * (H + 2 * Hkv) * D + (int64_t)hh * D;
+  const bool active = lane < half;
+  float x1 = active ? src[lane] : 0.f;
+  float x2 = active ? src[lane + half] : 0.f;
+  const bool is_v = hh >= H + Hkv;
+  if (!is_v) {
+    const float* g = hh < H ? a.q_norm : a.k_norm;
+    float ss = wave_sum<64>(x1 * x1 + x2 * x2);
+    const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
+    if (active) {
+      x1 = x1 * inv * g[lane];
+      x2 = x2 * inv * g[lane + half];
+      const float2 cs = a.rope[(int64_t)pos * half + lane];
+      const float y1 = x1 * cs.x - x2 * cs.y;
+      const float y2 = x2 * cs.x + x1 * cs.y;
+      x1 = y1;
+      x2 = y2;
+    }
+  }
+  if (!active) return;
+  if (hh < H) {
+    const int64_t o = ((int64_t)r * H + hh) * D;
+    if constexpr (KV_F16) {
+      uint16_t* q = (uint16_t*)a.q_out;
+      q[o + lane] = f32_to_f16_bits(x1);
+      q[o + lane + half] = f32_to_f16_bits(x2);
+    } else {
+      float* q = (float*)a.q_out;
+      q[o + lane] = x1;
+      q[o + lane + half] = x2;
+    }
+    return;
+  }
+  const int kvh = is_v ? hh - H - Hkv : hh - H;
+  const int seq = a.b.row_seq[r];
+  const int B = a.pool.block_tokens;
+  const int64_t blk = a.b.block_tables[(int64_t)seq * a.b.tbl_stride + pos / B];
+  const int64_t off = a.pool.offset(a.layer, is_v ? 1 : 0, blk, kvh, pos % B);
+  if constexpr (KV_F16) {
+    uint16_t* p = (uint16_t*)a.pool.base + off;
+    p[lane] = f32_to_f16_bits(x1);
+    p[lane + half] = f32_to_f16_bits(x2);
+  } else {
+    float* p = (float*)a.pool.base + off;
+    p[lane] = x1;
+    p[lane + half] = x2;
+  }
+}
+
+hipError_t launch_qk_rope_kv(const QkRopeArgs& a, hipStream_t s) {
+  if (a.b.n_rows <= 0) return hipSuccess;
+  const int heads = a.n_heads + 2 * a.n_kv_heads;
+  dim3 g(a.b.n_rows, (heads + 3) / 4), b(256);
+  if (a.kv_f16)
+    qk_rope_kv_kernel<true><<<g, b, 0, s>>>(a);
+  else
+    qk_rope_kv_kernel<false><<<g, b, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// ---- greedy argmax ("Candle model runner" 2.6: greedy takes the argmax, ties to the lowest
+// id). NaN entries never win. -------------------------------------------------------------
+
+__device__ __forceinline__ void better(float& bv, int& bi, float v, int i) {
+  if (v > bv || (v == bv && i < bi)) {
+    bv = v;
+    bi = i;
+  }
+}
+
+__global__ __launch_bounds__(256) void argmax_kernel(const float* __restrict__ logits, int vocab,
+                                                     int32_t* __restrict__ next) {
+  const int r = blockIdx.x;
+  const float* row = logits + (int64_t)r * vocab;
+  float bv = -__builtin_inff();
+  int bi = 0x7fffffff;
+  for (int i = threadIdx.x; i < vocab; i += blockDim.x) better(bv, bi, row[i], i);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    float v = __shfl_xor(bv, o, 64);
+    int i = __shfl_xor(bi, o, 64);
+    better(bv, bi, v, i);
+  }
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sv[w] = bv;
+    si[w] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int k = 1; k < 4; ++k) better(bv, bi, sv[k], si[k]);
+    next[r] = bi == 0x7fffffff ? 0 : bi;
+  }
+}
+
+hipError_t launch_argmax(const float* logits, int n_rows, int vocab, int32_t* next, hipStream_t s) {
+  if (n_rows <= 0) return hipSuccess;
+  argmax_kernel<<<n_rows, 256, 0, s>>>(logits, vocab, next);
+  return hipGetLastError();
+}
+
+// ---- debug dequantisation (same device arithmetic as the GEMM B-tile loader and the
+// embedding gather) ---------------------------------------------------------------------------
+
+template <int WF>
+__global__ __launch_bounds__(256) void dequant_kernel(WMat w, int rows, int cols, float* __restrict__ out) {
+  const int64_t total = (int64_t)rows * cols;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / cols;
+    const int c = (int)(i - r * cols);
+    float v;
+    if constexpr (WF == DEC_F32) {
+      v = ((const float*)w.w)[i];
+    } else if constexpr (WF == DEC_BF16) {
+      v = bf16_bits_to_f32(((const uint16_t*)w.w)[i]);
+    } else {
+      uint32_t byte = ((const uint8_t*)w.w)[r * (cols / 2) + (c >> 1)];
+      uint32_t q = (c & 1) ? (byte >> 4) : (byte & 15u);
+      const int64_t gi = r * (cols / 32) + (c >> 5);
+      v = dequant_u4(q, bf16_bits_to_f32(w.zp[gi]), bf16_bits_to_f32(w.scale[gi]));
+    }
+    out[i] = v;
+  }
+}
+
+hipError_t launch_dequant(int wdtype, const WMat& w, int rows, int cols, float* out, hipStream_t s) {
+  const int64_t total = (int64_t)rows * cols;
+  int blocks = (int)((total + 255) / 256);
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  if (wdtype == DEC_F32)
+    dequant_kernel<DEC_F32><<<blocks, 256, 0, s>>>(w, rows, cols, out);
+  else if (wdtype == DEC_BF16)
+    dequant_kernel<DEC_BF16><<<blocks, 256, 0, s>>>(w, rows, cols, out);
+  else
+    dequant_kernel<DEC_UINT4_G32><<<blocks, 256, 0, s>>>(w, rows, cols, out);
+  return hipGetLastError();
+}
+
+}  // namespace dec

@@ -1,0 +1,84 @@
+// Launchers of the decoder kernels. All launch on the given stream and return
+// the launch status; shapes are validated by the host runtime before any call.
+#pragma once
+
+#include "common.h"
+
+namespace dec {
+
+// x[r][:] = widened/dequantised E[tok[r]][:] as float32; an id outside [0, vocab) gives NaN.
+hipError_t launch_embed(const int32_t* tok, int n_rows, int vocab, int d, int wdtype, const WMat& E,
+                        float* x, hipStream_t s);
+
+// out[r][:] = x[rows ? rows[r] : r][:] / sqrt(mean(x^2) + eps) * g, stored as float32 or bf16.
+hipError_t launch_rmsnorm(const float* x, const int32_t* rows, int n, int d, const float* g, float eps,
+                          void* out, bool out_bf16, hipStream_t s);
+
+// Per-head q/k RMSNorm + split-halves RoPE on q and k, then q -> q_out and k, v -> pool.
+struct QkRopeArgs {
+  const float* qkv;  // [n_rows][(H + 2 Hkv) D]
+  const float* q_norm;
+  const float* k_norm;
+  const float2* rope;  // [max_context][D/2] (cos, sin)
+  void* q_out;         // [n_rows][H][D] in kv dtype
+  PoolDev pool;
+  int layer;
+  int n_heads, n_kv_heads, head_dim;
+  float eps;
+  bool kv_f16;
+  BatchDev b;
+};
+hipError_t launch_qk_rope_kv(const QkRopeArgs& a, hipStream_t s);
+
+// Attention of single query rows over their sequence's paged keys, split in
+// fixed chunks of keys; writes per-chunk partial (max, sum, unnormalised acc).
+struct AttnRowsArgs {
+  const void* q;  // [n_rows][H][D] kv dtype
+  PoolDev pool;
+  int layer;
+  int n_heads, n_kv_heads, head_dim;
+  bool kv_f16;
+  int n_chunks;   // chunks per row in this call (max over rows)
+  float* partial; // [n_rows][H][n_chunks][D + 2]
+  BatchDev b;
+};
+int attn_rows_chunk(int head_dim, bool kv_f16, int group);
+hipError_t launch_attn_rows(const AttnRowsArgs& a, hipStream_t s);
+
+// o[r][h*D + d] = combined attention output (float32 or bf16).
+hipError_t launch_attn_combine(const float* partial, int n_rows, int n_heads, int head_dim, int n_chunks,
+                               int chunk, const int32_t* row_pos, void* o, bool out_bf16, hipStream_t s);
+
+// Flash-style causal prefill attention on an f16 pool (MFMA), query tiles of one sequence.
+struct AttnPrefillArgs {
+  const uint16_t* q;  // [n_rows][H][D] f16
+  PoolDev pool;
+  int layer;
+  int n_heads, n_kv_heads, head_dim;
+  void* o;  // [n_rows][H*D] float32 or bf16
+  bool out_bf16;
+  BatchDev b;
+};
+hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t s);
+
+// C[M][N] (epilogue) = A[M][K] . B^T, B = concatenation of weight matrices along N.
+enum Epi { EPI_STORE = 0, EPI_RESID = 1, EPI_SWIGLU = 2 };
+struct GemmArgs {
+  const void* A;  // [M][K], float32 (f32 weights) or bf16
+  int lda;
+  int M, N, K;
+  WMat seg[3];  // B segments along N (EPI_SWIGLU: seg[0] gate, seg[1] up, N = ff)
+  int nseg;
+  void* C;  // float32 [M][ldc] (STORE, RESID) or act dtype (SWIGLU)
+  int ldc;
+  bool c_bf16;  // SWIGLU output in bf16
+};
+hipError_t launch_gemm(int wdtype, int epi, const GemmArgs& a, hipStream_t s);
+
+// next[r] = argmax_v logits[r][v], ties to the lowest id.
+hipError_t launch_argmax(const float* logits, int n_rows, int vocab, int32_t* next, hipStream_t s);
+
+// out[rows][cols] = widened / dequantised matrix (float32).
+hipError_t launch_dequant(int wdtype, const WMat& w, int rows, int cols, float* out, hipStream_t s);
+
+}  // namespace dec

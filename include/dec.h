@@ -1,0 +1,245 @@
+/*
+ * dec.h -- C ABI of the decoder forward pass on one AMD MI355X (gfx950).
+ *
+ * The library runs the forward pass of a pre-norm decoder with the Qwen3
+ * switches: token ids -> tied embedding -> n_layers x [RMSNorm -> Q/K/V
+ * projections (Q wider than the residual stream) -> per-head q/k RMSNorm ->
+ * split-halves RoPE at absolute positions -> paged KV write -> causal
+ * grouped-query attention -> output projection + residual -> RMSNorm ->
+ * SwiGLU + residual] -> final RMSNorm -> tied LM head -> float32 logits.
+ * Passages that define each step:
+ *   - "Candle model runner (Llama + bigram, int4), Rust KV cache, sampler and
+ *     PCG32", section 2.4 "The Llama forward, one step" (symbols table,
+ *     RMSNorm / projection / attention / SwiGLU equations, paged KV
+ *     placement, last-token LM head) and section 4 "The interface" (a step
+ *     is a batch of sequences, each a run of new tokens at absolute
+ *     positions; forward writes K and V into the blocks its table names; the
+ *     caller allocates the blocks).
+ *   - "A real model in our own decoder", section "Same design, bigger
+ *     numbers, five switches" (head_dim, ff_hidden, rope_base, rope_split,
+ *     qk_norm) and the qwen_config whitelist; section "Which channels rotate
+ *     together" (channel j pairs with j + head_dim/2).
+ *   - "Proving it's the same model", section "Every logit, every position"
+ *     (logits at every position) and "Remove every source of noise first"
+ *     (full path and cached path).
+ *   - "Byte-identical: 1,000 tokens of proof", section "The bar we set"
+ *     (uint4 weights W = (q - zp) * scale) and "The rope table that was too
+ *     accurate" (angle pos * base^(-2j/head_dim)).
+ *
+ * Memory ownership. The caller allocates every device buffer (weights blob,
+ * KV pool, workspace, logits, next-token ids) and keeps it alive until
+ * dec_free. The library never frees or reallocates them. A dec_ctx owns only
+ * host memory (a pinned staging ring for per-call metadata and the RoPE
+ * table) and HIP events. Host arrays passed to a call are read during the
+ * call only.
+ *
+ * Streams. `stream` is a hipStream_t passed as void* (NULL = the default
+ * stream). Every call enqueues its work on that stream and returns without
+ * waiting for it; the caller synchronises before reading results. One host
+ * thread may use a ctx at a time. Calls on one ctx must be issued on one
+ * stream, or the caller must order them: they share the ctx's workspace.
+ *
+ * Errors. Functions return DEC_OK (0) or a negative DEC_E_* code. Every
+ * argument, size, token id, position and block id is validated on the host
+ * before any work is enqueued, so a rejected call leaves the KV pool and the
+ * outputs untouched ("Candle model runner", section 4, test
+ * forward_refuses_bad_batches: a short block table or a position past the
+ * context is an error; pitfall s21: token ids are checked against the
+ * vocabulary). dec_last_error returns a message for the last failure.
+ */
+#ifndef DEC_H
+#define DEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- codes ---------------------------------------------------------------------- */
+
+#define DEC_OK 0
+#define DEC_E_ARG (-1)         /* null pointer, non-positive count, misaligned buffer */
+#define DEC_E_UNSUPPORTED (-2) /* configuration outside what the library runs */
+#define DEC_E_CAPACITY (-3)    /* more rows/sequences than configured, buffer too small */
+#define DEC_E_BLOCK (-4)       /* block id >= n_blocks, or block table too short */
+#define DEC_E_POSITION (-5)    /* a position at or past max_context */
+#define DEC_E_TOKEN (-6)       /* token id outside [0, vocab) */
+#define DEC_E_HIP (-7)         /* a HIP runtime call failed */
+
+/* storage formats */
+#define DEC_F32 0
+#define DEC_BF16 1
+#define DEC_F16 2
+#define DEC_UINT4_G32 3 /* 4-bit codes, bf16 scale and bf16 zero point per 32 input columns */
+
+/* which rows get logits */
+#define DEC_LOGITS_ALL 0  /* every new row, in batch order: [sum n_new][vocab] */
+#define DEC_LOGITS_LAST 1 /* each sequence's last new row: [n_seqs][vocab] */
+#define DEC_LOGITS_NONE 2 /* no logits (KV cache is still written) */
+
+/* ---- configuration ----------------------------------------------------------------- */
+
+/*
+ * Model and memory configuration. Accepted only with the switches of the
+ * Qwen3 layout: rope_split = 1 (pairs j, j + head_dim/2), qk_norm = 1,
+ * tie_embeddings = 1; anything else is refused at dec_init, never served
+ * wrong ("Candle model runner" section 2.3; "A real model in our own
+ * decoder", qwen_config). Size rules: d_model, n_heads*head_dim and ff_hidden
+ * multiples of 64; head_dim in {32, 64, 128}; n_heads a multiple of
+ * n_kv_heads; block_tokens in {16, 32, 64}.
+ */
+typedef struct dec_config {
+  int32_t n_layers;
+  int32_t d_model;
+  int32_t n_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t ff_hidden;
+  int32_t vocab;
+  int32_t max_context; /* positions 0 .. max_context-1 are valid */
+  float rms_eps;       /* used by all four norms (attention, q/k, ffn, final) */
+  double rope_base;
+  int32_t rope_split;     /* must be 1 */
+  int32_t qk_norm;        /* must be 1 */
+  int32_t tie_embeddings; /* must be 1 */
+  int32_t weight_dtype;   /* DEC_F32 | DEC_BF16 | DEC_UINT4_G32 */
+  int32_t kv_dtype;       /* DEC_F32 | DEC_F16 */
+  int32_t block_tokens;   /* B: positions per KV block */
+  int32_t n_blocks;       /* blocks in the KV pool */
+  int32_t max_rows;       /* most new tokens in one call (sizes the workspace) */
+  int32_t max_seqs;       /* most sequences in one call */
+} dec_config;
+
+/* Host-only check of a configuration; DEC_OK or DEC_E_UNSUPPORTED / DEC_E_ARG. */
+int dec_check_config(const dec_config* cfg);
+
+/* ---- memory layout ----------------------------------------------------------------- */
+
+/*
+ * Weights blob. One device buffer holding, at 256-byte aligned offsets, in this
+ * order: E [vocab][d_model] (the tied embedding, also the LM head); for each
+ * layer: attn_norm [d], W_q [H*D][d], W_k [Hkv*D][d], W_v [Hkv*D][d],
+ * q_norm [D], k_norm [D], W_o [d][H*D], ffn_norm [d], W_gate [ff][d],
+ * W_up [ff][d], W_down [d][ff]; then final_norm [d]. Matrices are [out][in]
+ * row-major ("Candle model runner" 2.4: W stored [out, in], y = x W^T) in
+ * weight_dtype; gains are float32. A DEC_UINT4_G32 matrix is three arrays:
+ * codes uint8 [out][in/2] (column 2b in the low nibble, 2b+1 in the high
+ * nibble, the order of "Candle model runner" 2.5), then scale bf16
+ * [out][in/32], then zero point bf16 [out][in/32]; element (o, i) is
+ * (code - zp[o][i/32]) * scale[o][i/32].
+ * The library only reads the blob.
+ */
+size_t dec_weight_bytes(const dec_config* cfg);
+
+/* One entry of the blob, by index 0 .. dec_weight_count(cfg)-1 in the order above. */
+typedef struct dec_weight_info {
+  char name[32];      /* "embed", "attn_norm", "wq", ..., "final_norm" */
+  int32_t layer;      /* -1 for embed / final_norm */
+  int32_t dtype;      /* DEC_F32 (gains) or the config's weight_dtype (matrices) */
+  int64_t rows, cols; /* logical shape; gains are [1][n] */
+  size_t offset;      /* byte offset of the data (codes, for uint4) */
+  size_t bytes;       /* bytes of the data (codes, for uint4) */
+  size_t scale_offset, zp_offset; /* uint4 only: byte offsets of scale and zero point */
+  size_t group_bytes;             /* uint4 only: bytes of each of scale and zp */
+} dec_weight_info;
+int dec_weight_count(const dec_config* cfg);
+int dec_weight_entry(const dec_config* cfg, int index, dec_weight_info* out);
+
+/*
+ * KV pool: [n_layers][2 (K, V)][n_blocks][n_kv_heads][block_tokens][head_dim]
+ * of kv_dtype, so one block's slab of one layer's K is [H_kv][B][D] ("Candle
+ * model runner" section 3, "Where a key lands": position j of a sequence is
+ * block floor(j/B) of its table, slot j mod B, and KV head h's key starts at
+ * element (h*B + slot)*D of the slab). f16 values are the round-to-nearest-
+ * even conversion of the float32 key/value.
+ */
+size_t dec_kv_pool_bytes(const dec_config* cfg);
+
+/* Scratch device memory for activations and per-call metadata (caller-owned). */
+size_t dec_workspace_bytes(const dec_config* cfg);
+
+/* ---- lifetime ---------------------------------------------------------------------- */
+
+typedef struct dec_ctx dec_ctx;
+
+/*
+ * Bind a configuration to caller-owned device buffers. Checks the config and
+ * that each buffer is at least the size above and 256-byte aligned, builds the
+ * RoPE cos/sin table (angles in double precision, stored float32) and uploads
+ * it into the workspace on `stream`. The weights blob is not modified.
+ * On success *out is a new context; on failure *out is NULL.
+ */
+int dec_init(const dec_config* cfg, const void* weights, size_t weight_bytes, void* kv_pool,
+             size_t kv_bytes, void* workspace, size_t workspace_bytes, void* stream,
+             dec_ctx** out);
+
+/* Release the context's host memory and events. Device buffers stay with the caller. */
+void dec_free(dec_ctx* ctx);
+
+/* Message of the last failure of a call on ctx (or of dec_init, for ctx == NULL). */
+const char* dec_last_error(const dec_ctx* ctx);
+
+/* ---- forward ----------------------------------------------------------------------- */
+
+/*
+ * One forward step over a batch of n_seqs sequences (prefill, chunked prefill
+ * or a cached continuation). Sequence s brings n_new[s] >= 1 new tokens that
+ * sit at absolute positions start[s] .. start[s]+n_new[s]-1; its keys and
+ * values for positions < start[s] must already be in the pool (from earlier
+ * calls), and this call writes those of the new positions. Rows are ordered
+ * sequence by sequence (batch order).
+ *   start, n_new:  host int32 [n_seqs]
+ *   tokens:        host int32 [sum n_new], batch order
+ *   block_tables:  host int32 [n_seqs][max_blocks], row-major; entries
+ *                  0 .. ceil((start+n_new)/B)-1 of each row are used
+ *   logits:        device float32 [sum n_new][vocab] (ALL), [n_seqs][vocab]
+ *                  (LAST), or NULL (NONE)
+ * A row's results do not depend on which other sequences share the call or
+ * where it sits in the batch: bit for bit ("Candle model runner" 2.4,
+ * batch invariance).
+ */
+int dec_prefill(dec_ctx* ctx, void* stream, int32_t n_seqs, const int32_t* start,
+                const int32_t* n_new, const int32_t* tokens, const int32_t* block_tables,
+                int32_t max_blocks, int32_t logits_mode, float* logits);
+
+/*
+ * One decode step: one new token per sequence at position positions[s] (the
+ * sequence's current length). Token ids come from host memory (tokens_host,
+ * checked against the vocabulary) or from device memory (tokens_device, e.g.
+ * the next_tokens of the previous step; exactly one of the two is non-NULL;
+ * an out-of-range device id makes that row's logits NaN).
+ *   logits:      device float32 [n_seqs][vocab], or NULL
+ *   next_tokens: device int32 [n_seqs] or NULL: greedy choice, the argmax of
+ *                the row with ties to the lowest id ("Candle model runner"
+ *                section 2.6); needs logits != NULL.
+ */
+int dec_decode_step(dec_ctx* ctx, void* stream, int32_t n_seqs, const int32_t* tokens_host,
+                    const int32_t* tokens_device, const int32_t* positions,
+                    const int32_t* block_tables, int32_t max_blocks, float* logits,
+                    int32_t* next_tokens);
+
+/*
+ * Host-only validation of a step, exactly as dec_prefill performs it before
+ * enqueuing anything (for callers and tests without a GPU). For a decode step
+ * pass n_new = NULL (one token each) and positions as start. tokens may be
+ * NULL to skip the id check. Returns DEC_OK or the code dec_prefill would
+ * return; `msg` (may be NULL) receives the message.
+ */
+int dec_check_step(const dec_config* cfg, int32_t n_seqs, const int32_t* start,
+                   const int32_t* n_new, const int32_t* tokens, const int32_t* block_tables,
+                   int32_t max_blocks, int32_t logits_mode, char* msg, size_t msg_len);
+
+/*
+ * Test hook: write weight entry `index` (a matrix) as float32 [rows][cols] to
+ * device memory `out`, widened/dequantised by the same device code the
+ * projections and the embedding use (uint4: t = f32(q) - f32(zp), then
+ * w = t * f32(scale), no fused multiply-add).
+ */
+int dec_debug_dequant(dec_ctx* ctx, void* stream, int index, float* out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DEC_H */

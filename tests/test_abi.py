@@ -1,0 +1,186 @@
+"""The C ABI on the host: exports, struct layout, refusals, layout functions and the
+validation every call runs before enqueuing work. No GPU needed: nothing here
+launches a kernel."""
+
+import os
+import re
+import subprocess
+import tempfile
+
+import numpy as np
+import pytest
+
+from conftest import ROOT, golden_rows
+from decoder_forward_pass_amd import binding as B
+from decoder_forward_pass_amd.blob import pack_blob, pack_uint4
+from decoder_forward_pass_amd.session import make_config
+from synthetic import MODELS, make_weights, param_count
+
+HEADER = os.path.join(ROOT, "include", "dec.h")
+
+
+def tiny_cfg(**kw):
+    c = make_config(MODELS["tiny_f32"], max_context=64, n_blocks=32, max_rows=64, max_seqs=4)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_library_exports_every_declared_function():
+    text = open(HEADER).read()
+    declared = set(re.findall(r"\b(dec_[a-z_]+)\s*\(", text))
+    assert declared == set(B.EXPORTS)
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (dec_\w+)", out))
+    assert declared <= exported
+
+
+def test_struct_layout_matches_the_header():
+    src = r"""
+    #include <stdio.h>
+    #include <stddef.h>
+    #include "dec.h"
+    int main(void) {
+      printf("%zu %zu %zu %zu %zu\n", sizeof(dec_config), offsetof(dec_config, rope_base),
+             offsetof(dec_config, max_seqs), sizeof(dec_weight_info), offsetof(dec_weight_info, group_bytes));
+      return 0;
+    }
+    """
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "t.c")
+        open(c, "w").write(src)
+        exe = os.path.join(d, "t")
+        subprocess.run(["gcc", "-I", os.path.dirname(HEADER), c, "-o", exe], check=True)
+        got = [int(v) for v in subprocess.run([exe], capture_output=True, text=True).stdout.split()]
+    import ctypes
+    want = [ctypes.sizeof(B.dec_config), B.dec_config.rope_base.offset, B.dec_config.max_seqs.offset,
+            ctypes.sizeof(B.dec_weight_info), B.dec_weight_info.group_bytes.offset]
+    assert got == want
+
+
+@pytest.mark.parametrize("field,value", [
+    ("rope_split", 0), ("qk_norm", 0), ("tie_embeddings", 0), ("n_blocks", 0), ("head_dim", 96),
+    ("n_kv_heads", 3), ("weight_dtype", 7), ("kv_dtype", B.DEC_BF16), ("block_tokens", 10), ("d_model", 96),
+    ("ff_hidden", 100), ("max_rows", 0), ("rms_eps", 0.0), ("rope_base", 1.0)])
+def test_config_refusals(field, value):
+    with pytest.raises(B.DecError) as e:
+        B.dec_check_config(tiny_cfg(**{field: value}))
+    assert e.value.code == B.DEC_E_UNSUPPORTED
+
+
+def test_blob_layout_is_aligned_ordered_and_complete():
+    for name in ("tiny_f32", "q06b_bf16", "q06b_uint4"):
+        m = MODELS[name]
+        cfg = make_config(m, max_context=64, n_blocks=8, max_rows=64, max_seqs=4)
+        n = B.dec_weight_count(cfg)
+        assert n == 2 + 11 * m.n_layers
+        end, params = 0, 0
+        for i in range(n):
+            e = B.dec_weight_entry(cfg, i)
+            assert e.offset % 256 == 0 and e.offset >= end
+            end = e.offset + e.bytes
+            if e.dtype == B.DEC_UINT4_G32:
+                assert e.bytes == e.rows * e.cols // 2 and e.group_bytes == e.rows * (e.cols // 32) * 2
+                assert e.scale_offset % 256 == 0 and e.scale_offset >= end
+                assert e.zp_offset % 256 == 0 and e.zp_offset >= e.scale_offset + e.group_bytes
+                end = e.zp_offset + e.group_bytes
+            params += e.rows * e.cols
+        assert end <= B.dec_weight_bytes(cfg)
+        assert params == param_count(m)
+        assert B.dec_weight_entry(cfg, 0).name == b"embed"
+        assert B.dec_weight_entry(cfg, n - 1).name == b"final_norm"
+
+
+def test_kv_pool_bytes():
+    cfg = tiny_cfg()
+    assert B.dec_kv_pool_bytes(cfg) == 2 * 2 * 32 * 2 * 16 * 32 * 4
+    cfg.kv_dtype = B.DEC_F16
+    assert B.dec_kv_pool_bytes(cfg) == 2 * 2 * 32 * 2 * 16 * 32 * 2
+
+
+def test_uint4_nibble_order_worked_example():
+    (row,) = golden_rows("int4_nibbles.txt")
+    codes = np.array([[int(v) for v in row[0].split()]], np.uint8)
+    want = [int(v, 16) for v in row[1].split()]
+    assert pack_uint4(codes).reshape(-1).tolist() == want
+
+
+def test_pack_blob_places_every_array():
+    w = make_weights("tiny_f32")
+    cfg = tiny_cfg()
+    blob = pack_blob(cfg, w)
+    e = B.dec_weight_entry(cfg, 2)  # layer 0 W_q
+    assert e.name == b"wq" and e.layer == 0
+    got = blob[e.offset:e.offset + e.bytes].view(np.float32).reshape(e.rows, e.cols)
+    assert np.array_equal(got, w.layers[0]["wq"])
+    e = B.dec_weight_entry(cfg, B.dec_weight_count(cfg) - 1)
+    assert np.array_equal(blob[e.offset:e.offset + e.bytes].view(np.float32), w.final_norm)
+
+
+def step(cfg, start, n_new, tokens, tables, mode=B.DEC_LOGITS_ALL):
+    return B.dec_check_step(cfg, start, n_new, tokens, np.asarray(tables, np.int32).reshape(len(start), -1), mode)
+
+
+def test_step_validation_accepts_a_good_batch():
+    cfg = tiny_cfg()
+    rc, msg = step(cfg, [0, 20], [16, 5], np.arange(21) % 512, [[3, 4], [5, 6]])
+    assert rc == B.DEC_OK, msg
+
+
+@pytest.mark.parametrize("case,code", [
+    (dict(tokens_bad=512), B.DEC_E_TOKEN),          # id outside the vocabulary (pitfall s21)
+    (dict(tokens_bad=-1), B.DEC_E_TOKEN),
+    (dict(short_table=True), B.DEC_E_BLOCK),        # block table shorter than the positions need
+    (dict(block_id=32), B.DEC_E_BLOCK),             # block id past the pool
+    (dict(past_context=True), B.DEC_E_POSITION),    # position past max_context
+    (dict(n_new0=True), B.DEC_E_ARG),
+    (dict(negative_start=True), B.DEC_E_POSITION),
+    (dict(shared_block=True), B.DEC_E_BLOCK),       # two sequences writing one block
+    (dict(too_many_rows=True), B.DEC_E_CAPACITY),
+    (dict(too_many_seqs=True), B.DEC_E_CAPACITY),
+    (dict(bad_mode=True), B.DEC_E_ARG),
+])
+def test_step_validation_errors(case, code):
+    cfg = tiny_cfg()
+    start, n_new = [0, 20], [16, 5]
+    tokens = np.arange(21) % 512
+    tables = [[3, 4], [5, 6]]
+    mode = B.DEC_LOGITS_ALL
+    if "tokens_bad" in case:
+        tokens[7] = case["tokens_bad"]
+    if case.get("short_table"):
+        tables = [[3], [5]]
+    if "block_id" in case:
+        tables[1][1] = case["block_id"]
+    if case.get("past_context"):
+        start, n_new, tokens = [0, 60], [16, 5], np.arange(21) % 512
+        tables = [[3, 4, 7, 8], [5, 6, 9, 10]]
+    if case.get("n_new0"):
+        n_new = [16, 0]
+        tokens = tokens[:16]
+    if case.get("negative_start"):
+        start = [0, -1]
+    if case.get("shared_block"):
+        tables = [[3, 4], [5, 3]]
+    if case.get("too_many_rows"):
+        start, n_new, tokens = [0, 0], [40, 30], np.zeros(70, np.int32)
+        tables = [[1, 2, 3], [4, 5, 6]]
+    if case.get("too_many_seqs"):
+        start, n_new, tokens = [0] * 5, [1] * 5, np.zeros(5, np.int32)
+        tables = [[i] for i in range(5)]
+    if case.get("bad_mode"):
+        mode = 9
+    rc, msg = step(cfg, start, n_new, tokens, tables, mode)
+    assert rc == code, msg
+    assert msg
+
+
+def test_decode_step_validation_uses_positions():
+    cfg = tiny_cfg()
+    # decode: one token each at positions 16 and 33; table must cover position+1 tokens
+    rc, msg = B.dec_check_step(cfg, [16, 33], None, [1, 2], np.array([[1, 2, 0], [3, 4, 5]], np.int32),
+                               B.DEC_LOGITS_LAST)
+    assert rc == B.DEC_OK, msg
+    rc, msg = B.dec_check_step(cfg, [16, 33], None, [1, 2], np.array([[1, 2], [3, 4]], np.int32),
+                               B.DEC_LOGITS_LAST)
+    assert rc == B.DEC_E_BLOCK

@@ -1,0 +1,50 @@
+"""GPU parity on the Qwen3-0.6B-shaped decoder in float32: 188 prompt tokens, full path and
+cached path split at 94, every logit at every position against the float64 oracle, max-abs
+<= 1e-3 ("Proving it's the same model": the procedure of ``logits_parity`` and the tolerance
+fixed before the first run)."""
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+from gpu_util import compare, report
+import oracle.model as om
+from synthetic import MODELS, WORKLOADS, make_prompts, make_weights
+
+TOL = 1e-3
+
+
+@pytest.fixture(scope="module")
+def case():
+    from decoder_forward_pass_amd.session import BlockAllocator, Session
+    wl = WORKLOADS["q06b_f32_t188"]
+    shape = MODELS[wl.model]
+    w = make_weights(shape)
+    prompt = make_prompts(wl)[0]
+    s = Session(shape, w, max_context=256, n_blocks=64, max_rows=188, max_seqs=2)
+    yield wl, shape, w, prompt, s, BlockAllocator(64, shape.block_tokens, seed=9)
+    s.close()
+
+
+def test_full_and_cached_match_oracle(case):
+    wl, shape, w, prompt, s, alloc = case
+    from decoder_forward_pass_amd.binding import DEC_LOGITS_ALL
+    T, split = len(prompt), wl.split
+    assert split == T // 2
+    alloc.ensure("full", T)
+    full = s.prefill([0], [T], prompt, alloc.table_array(["full"]), DEC_LOGITS_ALL).cpu().numpy()
+    alloc.ensure("cached", T)
+    tbl = alloc.table_array(["cached"])
+    a = s.prefill([0], [split], prompt[:split], tbl, DEC_LOGITS_ALL)
+    b = s.prefill([split], [T - split], prompt[split:], tbl, DEC_LOGITS_ALL)
+    cached = torch.cat([a, b]).cpu().numpy()
+    dec = om.OracleDecoder(w)
+    ref = dec.forward([(prompt, dec.new_cache())], logits="all")
+    assert ref.shape == (188, 151936)
+    for path, got in (("full", full), ("cached", cached)):
+        row = compare(got, ref, tol=TOL)
+        row.update(type="logit_parity", case=wl.name, path=path)
+        report(row)
+        assert row["pass"], row
