@@ -186,7 +186,7 @@ def test_greedy_next_tokens_are_the_argmax(setup, prompt):
 def test_dequant_hook_is_bit_exact(setup):
     name, shape, w, s, alloc = setup
     from decoder_forward_pass_amd import binding as B
-    for idx in (0, 2, 11, 12):
+    for idx in (0, 2, 9, 11, 13):
         e = B.dec_weight_entry(s.cfg, idx)
         nm = e.name.decode()
         src = w.embed if nm == "embed" else w.layers[e.layer][nm]
