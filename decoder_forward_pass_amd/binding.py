@@ -69,7 +69,10 @@ class dec_weight_info(ctypes.Structure):
 
 EXPORTS = ["dec_check_config", "dec_weight_bytes", "dec_weight_count", "dec_weight_entry", "dec_kv_pool_bytes",
            "dec_workspace_bytes", "dec_init", "dec_free", "dec_last_error", "dec_prefill", "dec_decode_step",
-           "dec_check_step", "dec_debug_dequant"]
+           "dec_check_step", "dec_debug_dequant", "dec_timing_enable", "dec_timing_read"]
+
+KERNEL_CLASSES = ["embed", "rmsnorm", "gemm_qkv", "qk_rope_kv", "attn_prefill", "attn_rows", "attn_combine",
+                  "gemm_o", "gemm_gateup", "gemm_down", "gemm_lmhead", "argmax"]
 
 
 def _load():
@@ -89,10 +92,12 @@ def _load():
         "dec_init": (ctypes.c_int, [cfgp, VP, SZ, VP, SZ, VP, SZ, VP, P(VP)]),
         "dec_free": (None, [VP]),
         "dec_last_error": (ctypes.c_char_p, [VP]),
-        "dec_prefill": (ctypes.c_int, [VP, VP, I32, i32p, i32p, i32p, i32p, I32, I32, VP]),
+        "dec_prefill": (ctypes.c_int, [VP, VP, I32, i32p, i32p, i32p, i32p, I32, I32, VP, VP]),
         "dec_decode_step": (ctypes.c_int, [VP, VP, I32, i32p, VP, i32p, i32p, I32, VP, VP]),
         "dec_check_step": (ctypes.c_int, [cfgp, I32, i32p, i32p, i32p, i32p, I32, I32, ctypes.c_char_p, SZ]),
         "dec_debug_dequant": (ctypes.c_int, [VP, VP, ctypes.c_int, VP]),
+        "dec_timing_enable": (ctypes.c_int, [VP, ctypes.c_uint32]),
+        "dec_timing_read": (ctypes.c_int, [VP, ctypes.c_int, P(ctypes.c_double), P(ctypes.c_int64)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -165,7 +170,8 @@ def dec_last_error(ctx) -> str:
     return m.decode() if m else ""
 
 
-def dec_prefill(ctx: int, stream: int, start, n_new, tokens, block_tables, logits_mode: int, logits: int) -> None:
+def dec_prefill(ctx: int, stream: int, start, n_new, tokens, block_tables, logits_mode: int, logits: int,
+                next_tokens: int = 0) -> None:
     _, sp = _i32(start)
     nn, np_ = _i32(n_new)
     _, tp = _i32(tokens)
@@ -174,7 +180,7 @@ def dec_prefill(ctx: int, stream: int, start, n_new, tokens, block_tables, logit
         raise ValueError("block_tables must be [n_seqs, max_blocks]")
     bp = bt.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
     _check(_lib.dec_prefill(ctx, stream or None, len(nn), sp, np_, tp, bp, bt.shape[1], logits_mode,
-                            logits or None), ctx)
+                            logits or None, next_tokens or None), ctx)
 
 
 def dec_decode_step(ctx: int, stream: int, positions, block_tables, logits: int, next_tokens: int = 0,
@@ -203,3 +209,15 @@ def dec_check_step(cfg: dec_config, start, n_new, tokens, block_tables, logits_m
 
 def dec_debug_dequant(ctx: int, stream: int, index: int, out: int) -> None:
     _check(_lib.dec_debug_dequant(ctx, stream or None, index, out), ctx)
+
+
+def dec_timing_enable(ctx: int, class_mask: int) -> None:
+    _check(_lib.dec_timing_enable(ctx, class_mask), ctx)
+
+
+def dec_timing_read(ctx: int, kernel_class: int):
+    """(total milliseconds, launches) of the recorded launches of one kernel class."""
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    _check(_lib.dec_timing_read(ctx, kernel_class, ctypes.byref(ms), ctypes.byref(n)), ctx)
+    return ms.value, n.value

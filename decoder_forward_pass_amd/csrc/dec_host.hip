@@ -139,6 +139,7 @@ struct Ws {
   size_t meta_ints;  // capacity of the metadata region in int32
   int chunk, nch_max, max_blocks_per_seq, max_tiles;
   int act_bytes, kv_el;
+  bool flash;  // prefill attention by the MFMA tile kernel
 };
 
 Ws ws_layout(const dec_config& c) {
@@ -167,7 +168,11 @@ Ws ws_layout(const dec_config& c) {
   w.q = take(R * qw * w.kv_el);
   w.o = take(R * qw * w.act_bytes);
   w.a = take(R * ff * w.act_bytes);
-  w.part = take(R * H * (size_t)w.nch_max * (D + 2) * 4);
+  // split-key partials: every row of a call when prefill also takes the per-row kernel,
+  // else only decode rows (one per sequence)
+  w.flash = c.kv_dtype == DEC_F16 && attn_prefill_supported(c.head_dim, c.n_heads / c.n_kv_heads);
+  const size_t prow = w.flash ? S : R;
+  w.part = take(prow * H * (size_t)w.nch_max * (D + 2) * 4);
   w.total = off;
   return w;
 }
@@ -228,7 +233,15 @@ int check_step(const dec_config& c, int32_t S, const int32_t* start, const int32
 
 }  // namespace
 
+// Event pairs around launches of the timed kernel classes.
+struct Timing {
+  uint32_t mask = 0;
+  std::vector<hipEvent_t> pool;                       // free events
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> rec[DEC_K_COUNT];
+};
+
 struct dec_ctx {
+  Timing timing;
   dec_config cfg;
   Blob blob;
   Ws ws;
@@ -329,15 +342,51 @@ int upload_meta(dec_ctx* ctx, hipStream_t st, int32_t S, const int32_t* start, c
   return DEC_OK;
 }
 
+hipEvent_t timing_event(dec_ctx* ctx) {
+  if (!ctx->timing.pool.empty()) {
+    hipEvent_t e = ctx->timing.pool.back();
+    ctx->timing.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Record the start event of a timed launch; returns false when the class is not timed.
+bool timing_begin(dec_ctx* ctx, int cls, hipStream_t st, hipEvent_t* start) {
+  if (!(ctx->timing.mask & (1u << cls))) return false;
+  *start = timing_event(ctx);
+  if (!*start) return false;
+  (void)hipEventRecord(*start, st);
+  return true;
+}
+
+void timing_end(dec_ctx* ctx, int cls, hipStream_t st, hipEvent_t start) {
+  hipEvent_t stop = timing_event(ctx);
+  if (!stop) return;
+  (void)hipEventRecord(stop, st);
+  ctx->timing.rec[cls].push_back({start, stop});
+}
+
 #define LAUNCH(expr)                                                                               \
   do {                                                                                             \
     hipError_t e_ = (expr);                                                                        \
     if (e_ != hipSuccess) return fail(&ctx->err, DEC_E_HIP, "launch %s: %s", #expr, hipGetErrorString(e_)); \
   } while (0)
 
+// A launch of kernel class `cls`, bracketed by events when that class is timed.
+#define TLAUNCH(cls, expr)                                 \
+  do {                                                     \
+    hipEvent_t t0_ = nullptr;                              \
+    const bool timed_ = timing_begin(ctx, cls, st, &t0_);  \
+    LAUNCH(expr);                                          \
+    if (timed_) timing_end(ctx, cls, st, t0_);             \
+  } while (0)
+
 // The forward pass over the uploaded batch: embedding, layers, final norm + LM head, argmax.
 int run_forward(dec_ctx* ctx, hipStream_t st, const BatchDev& b, const int32_t* tok_dev, int max_ctx,
-                float* logits, int32_t* next) {
+                bool decode, float* logits, int32_t* next) {
   const dec_config& c = ctx->cfg;
   const Ws& w = ctx->ws;
   const int N = b.n_rows, d = c.d_model, H = c.n_heads, Hkv = c.n_kv_heads, D = c.head_dim;
@@ -355,41 +404,46 @@ int run_forward(dec_ctx* ctx, hipStream_t st, const BatchDev& b, const int32_t* 
   PoolDev pool{ctx->pool, c.n_blocks, Hkv, c.block_tokens, D};
   const int nch = (max_ctx + w.chunk - 1) / w.chunk;
 
-  LAUNCH(launch_embed(tok_dev ? tok_dev : b.row_tok, N, c.vocab, d, c.weight_dtype, ctx->embed, x, st));
+  TLAUNCH(DEC_K_EMBED, launch_embed(tok_dev ? tok_dev : b.row_tok, N, c.vocab, d, c.weight_dtype, ctx->embed, x, st));
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerW& L = ctx->layers[l];
-    LAUNCH(launch_rmsnorm(x, nullptr, N, d, L.attn_norm, c.rms_eps, h, act_bf16, st));
+    TLAUNCH(DEC_K_RMSNORM, launch_rmsnorm(x, nullptr, N, d, L.attn_norm, c.rms_eps, h, act_bf16, st));
     GemmArgs g{};
     g.A = h; g.lda = d; g.M = N; g.N = qkvw; g.K = d;
     g.seg[0] = L.wq; g.seg[1] = L.wk; g.seg[2] = L.wv; g.nseg = 3;
     g.C = qkv; g.ldc = qkvw;
-    LAUNCH(launch_gemm(c.weight_dtype, EPI_STORE, g, st));
+    TLAUNCH(DEC_K_GEMM_QKV, launch_gemm(c.weight_dtype, EPI_STORE, g, st));
     QkRopeArgs qa{qkv, L.q_norm, L.k_norm, rope, q, pool, l, H, Hkv, D, c.rms_eps, kv_f16, b};
-    LAUNCH(launch_qk_rope_kv(qa, st));
-    AttnRowsArgs ra{q, pool, l, H, Hkv, D, kv_f16, nch, part, b};
-    LAUNCH(launch_attn_rows(ra, st));
-    LAUNCH(launch_attn_combine(part, N, H, D, nch, w.chunk, b.row_pos, o, act_bf16, st));
+    TLAUNCH(DEC_K_QK_ROPE_KV, launch_qk_rope_kv(qa, st));
+    if (w.flash && !decode) {
+      AttnPrefillArgs pa{(const uint16_t*)q, pool, l, H, Hkv, D, o, act_bf16, b};
+      TLAUNCH(DEC_K_ATTN_PREFILL, launch_attn_prefill(pa, st));
+    } else {
+      AttnRowsArgs ra{q, pool, l, H, Hkv, D, kv_f16, nch, part, b};
+      TLAUNCH(DEC_K_ATTN_ROWS, launch_attn_rows(ra, st));
+      TLAUNCH(DEC_K_ATTN_COMBINE, launch_attn_combine(part, N, H, D, nch, w.chunk, b.row_pos, o, act_bf16, st));
+    }
     g = GemmArgs{};
     g.A = o; g.lda = qw; g.M = N; g.N = d; g.K = qw;
     g.seg[0] = L.wo; g.nseg = 1; g.C = x; g.ldc = d;
-    LAUNCH(launch_gemm(c.weight_dtype, EPI_RESID, g, st));
-    LAUNCH(launch_rmsnorm(x, nullptr, N, d, L.ffn_norm, c.rms_eps, h, act_bf16, st));
+    TLAUNCH(DEC_K_GEMM_O, launch_gemm(c.weight_dtype, EPI_RESID, g, st));
+    TLAUNCH(DEC_K_RMSNORM, launch_rmsnorm(x, nullptr, N, d, L.ffn_norm, c.rms_eps, h, act_bf16, st));
     g = GemmArgs{};
     g.A = h; g.lda = d; g.M = N; g.N = ff; g.K = d;
     g.seg[0] = L.wg; g.seg[1] = L.wu; g.nseg = 2; g.C = act; g.ldc = ff; g.c_bf16 = act_bf16;
-    LAUNCH(launch_gemm(c.weight_dtype, EPI_SWIGLU, g, st));
+    TLAUNCH(DEC_K_GEMM_GATEUP, launch_gemm(c.weight_dtype, EPI_SWIGLU, g, st));
     g = GemmArgs{};
     g.A = act; g.lda = ff; g.M = N; g.N = d; g.K = ff;
     g.seg[0] = L.wd; g.nseg = 1; g.C = x; g.ldc = d;
-    LAUNCH(launch_gemm(c.weight_dtype, EPI_RESID, g, st));
+    TLAUNCH(DEC_K_GEMM_DOWN, launch_gemm(c.weight_dtype, EPI_RESID, g, st));
   }
   if (b.n_out > 0 && logits) {
-    LAUNCH(launch_rmsnorm(x, b.out_rows, b.n_out, d, ctx->final_norm, c.rms_eps, h, act_bf16, st));
+    TLAUNCH(DEC_K_RMSNORM, launch_rmsnorm(x, b.out_rows, b.n_out, d, ctx->final_norm, c.rms_eps, h, act_bf16, st));
     GemmArgs g{};
     g.A = h; g.lda = d; g.M = b.n_out; g.N = c.vocab; g.K = d;
     g.seg[0] = ctx->embed; g.nseg = 1; g.C = logits; g.ldc = c.vocab;
-    LAUNCH(launch_gemm(c.weight_dtype, EPI_STORE, g, st));
-    if (next) LAUNCH(launch_argmax(logits, b.n_out, c.vocab, next, st));
+    TLAUNCH(DEC_K_GEMM_LMHEAD, launch_gemm(c.weight_dtype, EPI_STORE, g, st));
+    if (next) TLAUNCH(DEC_K_ARGMAX, launch_argmax(logits, b.n_out, c.vocab, next, st));
   }
   return DEC_OK;
 }
@@ -519,8 +573,41 @@ int dec_init(const dec_config* cfg, const void* weights, size_t weight_bytes, vo
   return DEC_OK;
 }
 
+int dec_timing_enable(dec_ctx* ctx, uint32_t class_mask) {
+  if (!ctx) return fail(&g_err, DEC_E_ARG, "ctx is NULL");
+  ctx->timing.mask = class_mask & ((1u << DEC_K_COUNT) - 1);
+  return DEC_OK;
+}
+
+int dec_timing_read(dec_ctx* ctx, int kernel_class, double* total_ms, int64_t* launches) {
+  if (!ctx) return fail(&g_err, DEC_E_ARG, "ctx is NULL");
+  if (kernel_class < 0 || kernel_class >= DEC_K_COUNT) return fail(&ctx->err, DEC_E_ARG, "unknown kernel class");
+  double total = 0.0;
+  auto& rec = ctx->timing.rec[kernel_class];
+  for (auto& pr : rec) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(pr.second);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, pr.first, pr.second);
+    if (e != hipSuccess) return fail(&ctx->err, DEC_E_HIP, "timing events: %s", hipGetErrorString(e));
+    total += ms;
+    ctx->timing.pool.push_back(pr.first);
+    ctx->timing.pool.push_back(pr.second);
+  }
+  if (total_ms) *total_ms = total;
+  if (launches) *launches = (int64_t)rec.size();
+  rec.clear();
+  return DEC_OK;
+}
+
 void dec_free(dec_ctx* ctx) {
   if (!ctx) return;
+  for (auto& rec : ctx->timing.rec)
+    for (auto& pr : rec) {
+      (void)hipEventSynchronize(pr.second);
+      ctx->timing.pool.push_back(pr.first);
+      ctx->timing.pool.push_back(pr.second);
+    }
+  for (hipEvent_t e : ctx->timing.pool) (void)hipEventDestroy(e);
   for (int i = 0; i < kSlots; ++i) {
     if (ctx->ev[i]) {
       (void)hipEventSynchronize(ctx->ev[i]);
@@ -533,19 +620,21 @@ void dec_free(dec_ctx* ctx) {
 
 int dec_prefill(dec_ctx* ctx, void* stream, int32_t n_seqs, const int32_t* start, const int32_t* n_new,
                 const int32_t* tokens, const int32_t* block_tables, int32_t max_blocks, int32_t logits_mode,
-                float* logits) {
+                float* logits, int32_t* next_tokens) {
   if (!ctx) return fail(&g_err, DEC_E_ARG, "ctx is NULL");
   if (!n_new) return fail(&ctx->err, DEC_E_ARG, "n_new is NULL");
   if (!tokens) return fail(&ctx->err, DEC_E_ARG, "tokens is NULL");
   int rc = check_step(ctx->cfg, n_seqs, start, n_new, tokens, block_tables, max_blocks, logits_mode, &ctx->err);
   if (rc) return rc;
   if (logits_mode != DEC_LOGITS_NONE && !logits) return fail(&ctx->err, DEC_E_ARG, "logits is NULL");
+  if (next_tokens && logits_mode == DEC_LOGITS_NONE) return fail(&ctx->err, DEC_E_ARG, "next_tokens needs logits");
   hipStream_t st = (hipStream_t)stream;
   BatchDev b{};
   int max_ctx = 0;
   rc = upload_meta(ctx, st, n_seqs, start, n_new, tokens, block_tables, max_blocks, logits_mode, &b, &max_ctx);
   if (rc) return rc;
-  return run_forward(ctx, st, b, nullptr, max_ctx, logits_mode == DEC_LOGITS_NONE ? nullptr : logits, nullptr);
+  return run_forward(ctx, st, b, nullptr, max_ctx, false, logits_mode == DEC_LOGITS_NONE ? nullptr : logits,
+                     next_tokens);
 }
 
 int dec_decode_step(dec_ctx* ctx, void* stream, int32_t n_seqs, const int32_t* tokens_host,
@@ -563,7 +652,7 @@ int dec_decode_step(dec_ctx* ctx, void* stream, int32_t n_seqs, const int32_t* t
   int max_ctx = 0;
   rc = upload_meta(ctx, st, n_seqs, positions, nullptr, tokens_host, block_tables, max_blocks, mode, &b, &max_ctx);
   if (rc) return rc;
-  return run_forward(ctx, st, b, tokens_device, max_ctx, logits, next_tokens);
+  return run_forward(ctx, st, b, tokens_device, max_ctx, true, logits, next_tokens);
 }
 
 int dec_debug_dequant(dec_ctx* ctx, void* stream, int index, float* out) {

@@ -260,6 +260,210 @@ hipError_t launch_attn_combine(const float* partial, int n_rows, int n_heads, in
   return hipGetLastError();
 }
 
-hipError_t launch_attn_prefill(const AttnPrefillArgs&, hipStream_t) { return hipErrorNotSupported; }
+// ---- flash-style prefill attention (f16 pool, MFMA) ----------------------------------------
+// One block per (64-position query tile of one sequence, KV head); the 4 waves take 16 query
+// positions each, for all GROUP query heads of the KV head. Key tiles of 64 positions, aligned
+// to position 0 of the sequence, are staged in LDS (K row-major, V transposed) straight from
+// the pool blocks. Per key tile: S^T = K . Q^T (v_mfma_f32_16x16x32_f16, D/32 steps), causal
+// mask on absolute positions, online softmax in the exp2 domain, then O^T += V^T . P^T with P^T
+// taken directly from the S^T accumulators: in both products a lane's eight k-slots stand for
+// keys 4g..4g+3 of two adjacent 16-key blocks (g = lane / 16), which is a fixed relabelling of
+// the summation index, applied identically to both operands.
+// A query always sees the key tiles 0 .. floor(pos / 64) in order; later, fully masked tiles
+// leave its state unchanged bit for bit. The result therefore does not depend on how queries
+// are grouped into tiles, so batched, chunked and single-shot prefill agree exactly.
+
+template <int D, int G, bool BF16_OUT>
+__global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
+  constexpr int KT = 64;
+  constexpr int QT = 64;
+  constexpr int KSTR = D + 8;   // K tile row stride (halves)
+  constexpr int VSTR = KT + 8;  // V^T tile row stride (halves)
+  constexpr int NDK = D / 32;
+  constexpr int NDB = D / 16;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * KSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VSTR];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tile = blockIdx.x, kvh = blockIdx.y;
+  const int seq = a.b.tiles[2 * tile], row0 = a.b.tiles[2 * tile + 1];
+  const int s_start = a.b.seq_start[seq], s_n = a.b.seq_nnew[seq], s_row0 = a.b.seq_row0[seq];
+  const int ctx_end = s_start + s_n;
+  const int p0 = s_start + (row0 - s_row0);
+  const int tile_rows = min(QT, s_n - (row0 - s_row0));
+  const int pmax = p0 + tile_rows - 1;
+  const int H = a.n_heads;
+  const int B = a.pool.block_tokens;
+  const int32_t* table = a.b.block_tables + (int64_t)seq * a.b.tbl_stride;
+  const uint16_t* pool = (const uint16_t*)a.pool.base;
+
+  const int qi = wave * 16 + (lane & 15);
+  const bool qvalid = qi < tile_rows;
+  const int qrow = row0 + min(qi, tile_rows - 1);
+  const int qpos = p0 + qi;
+
+  f16x8 qf[G][NDK];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int dk = 0; dk < NDK; ++dk)
+      qf[g][dk] = __builtin_bit_cast(
+          f16x8, *(const u32x4*)(a.q + ((int64_t)qrow * H + kvh * G + g) * D + dk * 32 + (lane >> 4) * 8));
+
+  f32x4 o[G][NDB];
+  float m[G], l[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = -__builtin_inff();
+    l[g] = 0.f;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o[g][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const float sl2 = 1.4426950408889634f / sqrtf((float)D);
+  const int n_kt = pmax / KT + 1;
+
+  for (int kt = 0; kt < n_kt; ++kt) {
+    __syncthreads();
+    for (int c = tid; c < KT * (D / 8); c += 256) {
+      const int key = c / (D / 8), part = c % (D / 8);
+      const int kpos = kt * KT + key;
+      u32x4 kv = u32x4{0u, 0u, 0u, 0u}, vv = u32x4{0u, 0u, 0u, 0u};
+      if (kpos < ctx_end) {
+        const int64_t blk = table[kpos / B];
+        kv = *(const u32x4*)(pool + a.pool.offset(a.layer, 0, blk, kvh, kpos % B) + part * 8);
+        vv = *(const u32x4*)(pool + a.pool.offset(a.layer, 1, blk, kvh, kpos % B) + part * 8);
+      }
+      *(u32x4*)(Ks + key * KSTR + part * 8) = kv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Vt[(part * 8 + 2 * e) * VSTR + key] = (uint16_t)(vv[e] & 0xffffu);
+        Vt[(part * 8 + 2 * e + 1) * VSTR + key] = (uint16_t)(vv[e] >> 16);
+      }
+    }
+    __syncthreads();
+
+    f32x4 s[G][4];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) s[g][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int dk = 0; dk < NDK; ++dk) {
+        const f16x8 kf = __builtin_bit_cast(
+            f16x8, *(const u32x4*)(Ks + (kb * 16 + (lane & 15)) * KSTR + dk * 32 + (lane >> 4) * 8));
+#pragma unroll
+        for (int g = 0; g < G; ++g) s[g][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[g][dk], s[g][kb], 0, 0, 0);
+      }
+
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float mt = -__builtin_inff();
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int kpos = kt * KT + kb * 16 + (lane >> 4) * 4 + r;
+          float v = s[g][kb][r] * sl2;
+          if (kpos > qpos) v = -__builtin_inff();
+          s[g][kb][r] = v;
+          mt = fmaxf(mt, v);
+        }
+      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      const float mnew = fmaxf(m[g], mt);
+      const bool none = mnew == -__builtin_inff();
+      const float alpha = none ? 1.f : exp2f(m[g] - mnew);
+      float ps = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = none ? 0.f : exp2f(s[g][kb][r] - mnew);
+          s[g][kb][r] = p;
+          ps += p;
+        }
+      ps += __shfl_xor(ps, 16, 64);
+      ps += __shfl_xor(ps, 32, 64);
+      l[g] = l[g] * alpha + ps;
+      m[g] = mnew;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) o[g][db] *= alpha;
+    }
+
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      f16x8 pf[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pf[g][r] = (_Float16)s[g][2 * ks][r];
+          pf[g][4 + r] = (_Float16)s[g][2 * ks + 1][r];
+        }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const uint16_t* vr = Vt + (db * 16 + (lane & 15)) * VSTR + ks * 32 + (lane >> 4) * 4;
+        const u32x2 lo = *(const u32x2*)vr;
+        const u32x2 hi = *(const u32x2*)(vr + 16);
+        const f16x8 vf = __builtin_bit_cast(f16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+#pragma unroll
+        for (int g = 0; g < G; ++g) o[g][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[g], o[g][db], 0, 0, 0);
+      }
+    }
+  }
+
+  if (!qvalid) return;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const float inv = 1.0f / l[g];
+    const int64_t ob = (int64_t)qrow * H * D + (int64_t)(kvh * G + g) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int d = db * 16 + (lane >> 4) * 4 + r;
+        const float v = o[g][db][r] * inv;
+        if constexpr (BF16_OUT)
+          ((uint16_t*)a.o)[ob + d] = f32_to_bf16_bits(v);
+        else
+          ((float*)a.o)[ob + d] = v;
+      }
+  }
+}
+
+bool attn_prefill_supported(int head_dim, int group) {
+  return (head_dim == 32 || head_dim == 64 || head_dim == 128) && (group == 1 || group == 2);
+}
+
+template <int D, int G>
+static void prefill_launch(const AttnPrefillArgs& a, dim3 g, hipStream_t s) {
+  if (a.out_bf16)
+    attn_prefill_kernel<D, G, true><<<g, 256, 0, s>>>(a);
+  else
+    attn_prefill_kernel<D, G, false><<<g, 256, 0, s>>>(a);
+}
+
+template <int D>
+static hipError_t prefill_dispatch(const AttnPrefillArgs& a, dim3 g, hipStream_t s) {
+  const int group = a.n_heads / a.n_kv_heads;
+  if (group == 1)
+    prefill_launch<D, 1>(a, g, s);
+  else if (group == 2)
+    prefill_launch<D, 2>(a, g, s);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t s) {
+  if (a.b.n_tiles <= 0) return hipSuccess;
+  dim3 g(a.b.n_tiles, a.n_kv_heads);
+  if (a.head_dim == 32) return prefill_dispatch<32>(a, g, s);
+  if (a.head_dim == 64) return prefill_dispatch<64>(a, g, s);
+  if (a.head_dim == 128) return prefill_dispatch<128>(a, g, s);
+  return hipErrorInvalidValue;
+}
 
 }  // namespace dec

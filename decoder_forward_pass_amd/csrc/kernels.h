@@ -59,6 +59,7 @@ struct AttnPrefillArgs {
   bool out_bf16;
   BatchDev b;
 };
+bool attn_prefill_supported(int head_dim, int group);
 hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t s);
 
 // C[M][N] (epilogue) = A[M][K] . B^T, B = concatenation of weight matrices along N.

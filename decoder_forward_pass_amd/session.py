@@ -98,13 +98,15 @@ class Session:
     def vocab(self) -> int:
         return self.cfg.vocab
 
-    def prefill(self, start, n_new, tokens, block_tables, mode: int = B.DEC_LOGITS_ALL, logits=None):
+    def prefill(self, start, n_new, tokens, block_tables, mode: int = B.DEC_LOGITS_ALL, logits=None,
+                next_tokens=None):
         """One dec_prefill call; returns the logits tensor (allocated if not given)."""
         n_out = int(np.sum(n_new)) if mode == B.DEC_LOGITS_ALL else (len(n_new) if mode == B.DEC_LOGITS_LAST else 0)
         if logits is None and n_out:
             logits = torch.empty((n_out, self.vocab), dtype=torch.float32, device=self.device)
         B.dec_prefill(self.ctx, self.stream, start, n_new, tokens, block_tables, mode,
-                      logits.data_ptr() if n_out else 0)
+                      logits.data_ptr() if n_out else 0,
+                      next_tokens.data_ptr() if next_tokens is not None else 0)
         return logits
 
     def decode_step(self, positions, block_tables, *, tokens_host=None, tokens_device=None, logits=None,

@@ -196,13 +196,16 @@ const char* dec_last_error(const dec_ctx* ctx);
  *                  0 .. ceil((start+n_new)/B)-1 of each row are used
  *   logits:        device float32 [sum n_new][vocab] (ALL), [n_seqs][vocab]
  *                  (LAST), or NULL (NONE)
+ *   next_tokens:   device int32, one per logits row, or NULL: greedy choice,
+ *                  the argmax of the row with ties to the lowest id ("Candle
+ *                  model runner" section 2.6); needs logits.
  * A row's results do not depend on which other sequences share the call or
  * where it sits in the batch: bit for bit ("Candle model runner" 2.4,
  * batch invariance).
  */
 int dec_prefill(dec_ctx* ctx, void* stream, int32_t n_seqs, const int32_t* start,
                 const int32_t* n_new, const int32_t* tokens, const int32_t* block_tables,
-                int32_t max_blocks, int32_t logits_mode, float* logits);
+                int32_t max_blocks, int32_t logits_mode, float* logits, int32_t* next_tokens);
 
 /*
  * One decode step: one new token per sequence at position positions[s] (the
@@ -238,6 +241,36 @@ int dec_check_step(const dec_config* cfg, int32_t n_seqs, const int32_t* start,
  * w = t * f32(scale), no fused multiply-add).
  */
 int dec_debug_dequant(dec_ctx* ctx, void* stream, int index, float* out);
+
+/* ---- per-kernel timing (diagnostics) ------------------------------------------------ */
+
+/* kernel classes */
+#define DEC_K_EMBED 0
+#define DEC_K_RMSNORM 1
+#define DEC_K_GEMM_QKV 2
+#define DEC_K_QK_ROPE_KV 3
+#define DEC_K_ATTN_PREFILL 4 /* tile attention of prefill calls (f16 pool) */
+#define DEC_K_ATTN_ROWS 5    /* split-key attention of decode steps (and float32-pool prefill) */
+#define DEC_K_ATTN_COMBINE 6
+#define DEC_K_GEMM_O 7
+#define DEC_K_GEMM_GATEUP 8
+#define DEC_K_GEMM_DOWN 9
+#define DEC_K_GEMM_LMHEAD 10
+#define DEC_K_ARGMAX 11
+#define DEC_K_COUNT 12
+
+/*
+ * Bracket every later launch of the kernel classes in `class_mask` (bit k =
+ * class k) with a pair of HIP events on the call's stream; 0 turns timing
+ * off. Recorded launches accumulate until dec_timing_read.
+ */
+int dec_timing_enable(dec_ctx* ctx, uint32_t class_mask);
+
+/*
+ * Wait for the recorded launches of `kernel_class`, return the sum of their
+ * durations in milliseconds and their count, and forget them.
+ */
+int dec_timing_read(dec_ctx* ctx, int kernel_class, double* total_ms, int64_t* launches);
 
 #ifdef __cplusplus
 }

@@ -106,11 +106,12 @@ def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, qpos: np.ndarray,
     keys = np.arange(K.shape[0])
     for h in range(H):
         kvh = h // group
-        Kh, Vh = K[:, kvh, :], V[:, kvh, :]
         for t0 in range(0, n, tile):
             t1 = min(n, t0 + tile)
+            kend = min(K.shape[0], int(qpos[t0:t1].max()) + 1)  # keys past the tile's last query are never visible
+            Kh, Vh = K[:kend, kvh, :], V[:kend, kvh, :]
             s = (q[t0:t1, h, :] @ Kh.T) * scale
-            visible = keys[None, :] <= qpos[t0:t1, None]
+            visible = keys[None, :kend] <= qpos[t0:t1, None]
             s = np.where(visible, s, -np.inf)
             s = s - s.max(axis=-1, keepdims=True)
             p = np.exp(s)

@@ -40,8 +40,8 @@ def setup(request):
     from decoder_forward_pass_amd.session import BlockAllocator, Session
     shape = VARIANTS[request.param]
     w = make_weights(shape)
-    s = Session(shape, w, max_context=128, n_blocks=64, max_rows=96, max_seqs=8)
-    yield request.param, shape, w, s, BlockAllocator(64, shape.block_tokens, seed=5)
+    s = Session(shape, w, max_context=256, n_blocks=160, max_rows=256, max_seqs=8)
+    yield request.param, shape, w, s, BlockAllocator(160, shape.block_tokens, seed=5)
     s.close()
 
 
@@ -212,3 +212,33 @@ def test_rejected_call_leaves_pool_untouched(setup, prompt):
     assert e.value.code == B.DEC_E_POSITION
     torch.cuda.synchronize()
     assert torch.equal(before, s.pool)
+
+
+def test_long_prompt_tiles_cached_split_and_chunks(setup):
+    """200 tokens: several 64-key tiles, a cached split at an unaligned position, and chunked
+    prefill; chunked and cached logits equal the single-shot ones bit for bit."""
+    name, shape, w, s, alloc = setup
+    from decoder_forward_pass_amd.binding import DEC_LOGITS_ALL
+    rng = np.random.default_rng(31)
+    T = 200
+    prompt = rng.integers(0, shape.vocab, T).astype(np.int32)
+    ref, _ = oracle_full(w, prompt)
+    alloc.ensure(("long", name), T)
+    full = s.prefill([0], [T], prompt, alloc.table_array([("long", name)]), DEC_LOGITS_ALL).clone()
+    row = compare(full.cpu().numpy(), ref, **gate(name))
+    row.update(type="logit_parity", case=f"tiny_{name}_t200", path="full")
+    report(row)
+    assert row["pass"], row
+    for chunk in (77, 64, 50):
+        seq = ("long", name, chunk)
+        alloc.ensure(seq, T)
+        tbl = alloc.table_array([seq])
+        parts = [s.prefill([c0], [min(chunk, T - c0)], prompt[c0:c0 + chunk], tbl, DEC_LOGITS_ALL).clone()
+                 for c0 in range(0, T, chunk)]
+        got = torch.cat(parts)
+        torch.cuda.synchronize()
+        same = int(torch.sum(torch.all(got == full, dim=1)))
+        report({"type": "chunk_invariance", "case": f"tiny_{name}_t200", "chunk": chunk,
+                "identical_rows": same, "rows": T,
+                "max_absolute_error": float((got - full).abs().max())})
+        assert torch.equal(got, full), f"chunk {chunk}: {same}/{T} rows identical"
