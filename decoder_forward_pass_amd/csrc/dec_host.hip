@@ -135,7 +135,7 @@ size_t kv_bytes(const dec_config& c) {
 // ---- workspace layout ----------------------------------------------------------------------
 
 struct Ws {
-  size_t rope, meta, x, h, qkv, q, o, a, part, total;
+  size_t rope, meta, x, h, qkv, q, o, a, part, amax, total;
   size_t meta_ints;  // capacity of the metadata region in int32
   int chunk, nch_max, max_blocks_per_seq, max_tiles;
   int act_bytes, kv_el;
@@ -168,11 +168,12 @@ Ws ws_layout(const dec_config& c) {
   w.q = take(R * qw * w.kv_el);
   w.o = take(R * qw * w.act_bytes);
   w.a = take(R * ff * w.act_bytes);
-  // split-key partials: every row of a call when prefill also takes the per-row kernel,
-  // else only decode rows (one per sequence)
+  // split-key partials: only prefill calls that take the per-row kernel (float32 pool, or a
+  // head shape the tile kernel does not take) use them; decode merges its chunks in-block
   w.flash = c.kv_dtype == DEC_F16 && attn_prefill_supported(c.head_dim, c.n_heads / c.n_kv_heads);
-  const size_t prow = w.flash ? S : R;
+  const size_t prow = w.flash ? 0 : R;
   w.part = take(prow * H * (size_t)w.nch_max * (D + 2) * 4);
+  w.amax = take(argmax_scratch_bytes((int)R));
   w.total = off;
   return w;
 }
@@ -403,6 +404,12 @@ int run_forward(dec_ctx* ctx, hipStream_t st, const BatchDev& b, const int32_t* 
   const float2* rope = (const float2*)(ctx->wsp + w.rope);
   PoolDev pool{ctx->pool, c.n_blocks, Hkv, c.block_tokens, D};
   const int nch = (max_ctx + w.chunk - 1) / w.chunk;
+  // decode steps take the decode GEMM (K split inside a block) where the weight format has one;
+  // prefill calls always take the tile GEMM
+  const bool dec_gemm = decode && gemm_decode_supported(c.weight_dtype);
+  auto gemm = [&](int epi, const GemmArgs& g) {
+    return dec_gemm ? launch_gemm_decode(c.weight_dtype, epi, g, st) : launch_gemm(c.weight_dtype, epi, g, st);
+  };
 
   TLAUNCH(DEC_K_EMBED, launch_embed(tok_dev ? tok_dev : b.row_tok, N, c.vocab, d, c.weight_dtype, ctx->embed, x, st));
   for (int l = 0; l < c.n_layers; ++l) {
@@ -412,10 +419,13 @@ int run_forward(dec_ctx* ctx, hipStream_t st, const BatchDev& b, const int32_t* 
     g.A = h; g.lda = d; g.M = N; g.N = qkvw; g.K = d;
     g.seg[0] = L.wq; g.seg[1] = L.wk; g.seg[2] = L.wv; g.nseg = 3;
     g.C = qkv; g.ldc = qkvw;
-    TLAUNCH(DEC_K_GEMM_QKV, launch_gemm(c.weight_dtype, EPI_STORE, g, st));
+    TLAUNCH(DEC_K_GEMM_QKV, gemm(EPI_STORE, g));
     QkRopeArgs qa{qkv, L.q_norm, L.k_norm, rope, q, pool, l, H, Hkv, D, c.rms_eps, kv_f16, b};
     TLAUNCH(DEC_K_QK_ROPE_KV, launch_qk_rope_kv(qa, st));
-    if (w.flash && !decode) {
+    if (decode) {
+      AttnRowsArgs ra{q, pool, l, H, Hkv, D, kv_f16, nch, part, b};
+      TLAUNCH(DEC_K_ATTN_ROWS, launch_attn_decode(ra, o, act_bf16, st));
+    } else if (w.flash) {
       AttnPrefillArgs pa{(const uint16_t*)q, pool, l, H, Hkv, D, o, act_bf16, b};
       TLAUNCH(DEC_K_ATTN_PREFILL, launch_attn_prefill(pa, st));
     } else {
@@ -426,24 +436,24 @@ int run_forward(dec_ctx* ctx, hipStream_t st, const BatchDev& b, const int32_t* 
     g = GemmArgs{};
     g.A = o; g.lda = qw; g.M = N; g.N = d; g.K = qw;
     g.seg[0] = L.wo; g.nseg = 1; g.C = x; g.ldc = d;
-    TLAUNCH(DEC_K_GEMM_O, launch_gemm(c.weight_dtype, EPI_RESID, g, st));
+    TLAUNCH(DEC_K_GEMM_O, gemm(EPI_RESID, g));
     TLAUNCH(DEC_K_RMSNORM, launch_rmsnorm(x, nullptr, N, d, L.ffn_norm, c.rms_eps, h, act_bf16, st));
     g = GemmArgs{};
     g.A = h; g.lda = d; g.M = N; g.N = ff; g.K = d;
     g.seg[0] = L.wg; g.seg[1] = L.wu; g.nseg = 2; g.C = act; g.ldc = ff; g.c_bf16 = act_bf16;
-    TLAUNCH(DEC_K_GEMM_GATEUP, launch_gemm(c.weight_dtype, EPI_SWIGLU, g, st));
+    TLAUNCH(DEC_K_GEMM_GATEUP, gemm(EPI_SWIGLU, g));
     g = GemmArgs{};
     g.A = act; g.lda = ff; g.M = N; g.N = d; g.K = ff;
     g.seg[0] = L.wd; g.nseg = 1; g.C = x; g.ldc = d;
-    TLAUNCH(DEC_K_GEMM_DOWN, launch_gemm(c.weight_dtype, EPI_RESID, g, st));
+    TLAUNCH(DEC_K_GEMM_DOWN, gemm(EPI_RESID, g));
   }
   if (b.n_out > 0 && logits) {
     TLAUNCH(DEC_K_RMSNORM, launch_rmsnorm(x, b.out_rows, b.n_out, d, ctx->final_norm, c.rms_eps, h, act_bf16, st));
     GemmArgs g{};
     g.A = h; g.lda = d; g.M = b.n_out; g.N = c.vocab; g.K = d;
     g.seg[0] = ctx->embed; g.nseg = 1; g.C = logits; g.ldc = c.vocab;
-    TLAUNCH(DEC_K_GEMM_LMHEAD, launch_gemm(c.weight_dtype, EPI_STORE, g, st));
-    if (next) TLAUNCH(DEC_K_ARGMAX, launch_argmax(logits, b.n_out, c.vocab, next, st));
+    TLAUNCH(DEC_K_GEMM_LMHEAD, gemm(EPI_STORE, g));
+    if (next) TLAUNCH(DEC_K_ARGMAX, launch_argmax(logits, b.n_out, c.vocab, next, ctx->wsp + w.amax, st));
   }
   return DEC_OK;
 }

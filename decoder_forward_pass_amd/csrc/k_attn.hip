@@ -260,6 +260,185 @@ hipError_t launch_attn_combine(const float* partial, int n_rows, int n_heads, in
   return hipGetLastError();
 }
 
+// ---- decode attention: one workgroup per (sequence, KV head) ------------------------------
+// A decode step has one query row per sequence. The workgroup's 8 waves take the fixed chunks
+// of the row's keys (chunk size as attn_rows) in turn: wave w handles chunks w, w+8, ... in
+// increasing order, keeping a running (max, sum, accumulator) per query head; the block ids of
+// a chunk are wave-uniform, and the K and V loads of a whole chunk are issued before any
+// arithmetic (keys past the context read a valid slot of the last block and are masked).
+// The 8 wave states are then merged in wave order through LDS and the output row is written:
+// no partials leave the workgroup and no combine launch is needed. The split depends only on
+// the row's context length, so the result does not depend on the other sequences.
+
+template <typename KVT, int D, int GROUP, bool BF16_OUT>
+__global__ __launch_bounds__(512) void attn_decode_kernel(AttnRowsArgs a, void* out) {
+  using G = RowsGeom<KVT, D, GROUP>;
+  constexpr int EPL = G::EPL, LPK = G::LPK, KPI = G::KPI, KPG = G::KPG, CHUNK = G::CHUNK;
+  constexpr int NWV = 8;
+  __shared__ float s_m[NWV][GROUP], s_l[NWV][GROUP];
+  __shared__ float s_acc[NWV][GROUP][D];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int grp = lane / LPK, sub = lane % LPK;
+  const int Hkv = a.n_kv_heads, H = a.n_heads;
+  const int row = blockIdx.x / Hkv, kvh = blockIdx.x % Hkv;
+  const int pos = a.b.row_pos[row];
+  const int ctx = pos + 1;
+  const int nch = (ctx + CHUNK - 1) / CHUNK;
+  const int seq = a.b.row_seq[row];
+  const int32_t* table = a.b.block_tables + (int64_t)seq * a.b.tbl_stride;
+  const int B = a.pool.block_tokens;
+  const int last_blk = (ctx - 1) / B;
+  const KVT* pool = (const KVT*)a.pool.base;
+
+  const float qscale = 1.4426950408889634f / sqrtf((float)D);
+  float qv[GROUP][EPL];
+#pragma unroll
+  for (int i = 0; i < GROUP; ++i) {
+    load_kv<KVT, EPL>((const KVT*)a.q + ((int64_t)row * H + kvh * GROUP + i) * D + sub * EPL, qv[i]);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qv[i][e] *= qscale;
+  }
+  float m[GROUP], l[GROUP], acc[GROUP][EPL];
+#pragma unroll
+  for (int i = 0; i < GROUP; ++i) {
+    m[i] = -__builtin_inff();
+    l[i] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[i][e] = 0.f;
+  }
+
+  for (int c = wave; c < nch; c += NWV) {
+    const int key0 = c * CHUNK;
+    u32x4 kraw[KPG], vraw[KPG];
+#pragma unroll
+    for (int kk = 0; kk < KPG; ++kk) {
+      const int kb = min((key0 + kk * KPI) / B, last_blk);  // same block for the KPI keys of a load
+      const int64_t blk = table[kb];
+      const int slot = (key0 + kk * KPI + grp) % B;
+      kraw[kk] = *(const u32x4*)(pool + a.pool.offset(a.layer, 0, blk, kvh, slot) + sub * EPL);
+      vraw[kk] = *(const u32x4*)(pool + a.pool.offset(a.layer, 1, blk, kvh, slot) + sub * EPL);
+    }
+    float sc[KPG][GROUP];
+#pragma unroll
+    for (int kk = 0; kk < KPG; ++kk) {
+      float kv[EPL];
+      load_kv<KVT, EPL>((const KVT*)&kraw[kk], kv);
+      const bool valid = key0 + kk * KPI + grp < ctx;
+#pragma unroll
+      for (int i = 0; i < GROUP; ++i) {
+        float d = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) d += qv[i][e] * kv[e];
+        d = wave_sum<LPK>(d);
+        sc[kk][i] = valid ? d : -__builtin_inff();
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < GROUP; ++i) {
+      float mc = sc[0][i];
+#pragma unroll
+      for (int kk = 1; kk < KPG; ++kk) mc = fmaxf(mc, sc[kk][i]);
+#pragma unroll
+      for (int o = LPK; o < 64; o <<= 1) mc = fmaxf(mc, __shfl_xor(mc, o, 64));
+      const float mn = fmaxf(m[i], mc);
+      const float alpha = exp2f(m[i] - mn);  // 0 on the first chunk (m = -inf)
+      m[i] = mn;
+      l[i] *= alpha;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[i][e] *= alpha;
+    }
+#pragma unroll
+    for (int kk = 0; kk < KPG; ++kk) {
+      // a masked key's slot holds whatever the block held before: zero it, as p * NaN is NaN
+      if (key0 + kk * KPI + grp >= ctx) vraw[kk] = u32x4{0u, 0u, 0u, 0u};
+      float vv[EPL];
+      load_kv<KVT, EPL>((const KVT*)&vraw[kk], vv);
+#pragma unroll
+      for (int i = 0; i < GROUP; ++i) {
+        const float p = exp2f(sc[kk][i] - m[i]);
+        l[i] += p;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[i][e] += p * vv[e];
+      }
+    }
+  }
+  // this wave's state: sum the lane groups (each holds distinct keys)
+#pragma unroll
+  for (int o = LPK; o < 64; o <<= 1) {
+#pragma unroll
+    for (int i = 0; i < GROUP; ++i) {
+      l[i] += __shfl_xor(l[i], o, 64);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[i][e] += __shfl_xor(acc[i][e], o, 64);
+    }
+  }
+  if (grp == 0) {
+#pragma unroll
+    for (int i = 0; i < GROUP; ++i) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s_acc[wave][i][sub * EPL + e] = acc[i][e];
+      if (sub == 0) {
+        s_m[wave][i] = m[i];
+        s_l[wave][i] = l[i];
+      }
+    }
+  }
+  __syncthreads();
+  const int nw = min(NWV, nch);  // waves that saw at least one chunk
+  for (int t = threadIdx.x; t < GROUP * D; t += 512) {
+    const int i = t / D, d = t % D;
+    float M = s_m[0][i];
+    for (int w = 1; w < nw; ++w) M = fmaxf(M, s_m[w][i]);
+    float L = 0.f, A = 0.f;
+    for (int w = 0; w < nw; ++w) {
+      const float sc = exp2f(s_m[w][i] - M);
+      L += sc * s_l[w][i];
+      A += sc * s_acc[w][i][d];
+    }
+    const float v = A / L;
+    const int64_t o = (int64_t)row * H * D + (int64_t)(kvh * GROUP + i) * D + d;
+    if constexpr (BF16_OUT)
+      ((uint16_t*)out)[o] = f32_to_bf16_bits(v);
+    else
+      ((float*)out)[o] = v;
+  }
+}
+
+template <typename KVT, int D, int GROUP>
+static void decode_launch(const AttnRowsArgs& a, void* o, bool bf16_out, hipStream_t s) {
+  dim3 g(a.b.n_rows * a.n_kv_heads);
+  if (bf16_out)
+    attn_decode_kernel<KVT, D, GROUP, true><<<g, 512, 0, s>>>(a, o);
+  else
+    attn_decode_kernel<KVT, D, GROUP, false><<<g, 512, 0, s>>>(a, o);
+}
+
+template <typename KVT, int D>
+static hipError_t decode_dispatch_group(const AttnRowsArgs& a, void* o, bool bf16_out, hipStream_t s) {
+  switch (a.n_heads / a.n_kv_heads) {
+    case 1: decode_launch<KVT, D, 1>(a, o, bf16_out, s); break;
+    case 2: decode_launch<KVT, D, 2>(a, o, bf16_out, s); break;
+    case 4: decode_launch<KVT, D, 4>(a, o, bf16_out, s); break;
+    case 8: decode_launch<KVT, D, 8>(a, o, bf16_out, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_decode(const AttnRowsArgs& a, void* o, bool out_bf16, hipStream_t s) {
+  if (a.b.n_rows <= 0) return hipSuccess;
+  if (a.kv_f16) {
+    if (a.head_dim == 32) return decode_dispatch_group<uint16_t, 32>(a, o, out_bf16, s);
+    if (a.head_dim == 64) return decode_dispatch_group<uint16_t, 64>(a, o, out_bf16, s);
+    if (a.head_dim == 128) return decode_dispatch_group<uint16_t, 128>(a, o, out_bf16, s);
+  } else {
+    if (a.head_dim == 32) return decode_dispatch_group<float, 32>(a, o, out_bf16, s);
+    if (a.head_dim == 64) return decode_dispatch_group<float, 64>(a, o, out_bf16, s);
+    if (a.head_dim == 128) return decode_dispatch_group<float, 128>(a, o, out_bf16, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 // ---- flash-style prefill attention (f16 pool, MFMA) ----------------------------------------
 // One block per (64-position query tile of one sequence, KV head); the 4 waves take 16 query
 // positions each, for all GROUP query heads of the KV head. Key tiles of 64 positions, aligned

@@ -208,4 +208,162 @@ hipError_t launch_gemm(int wdtype, int epi, const GemmArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+
+
+// ---- decode GEMM -----------------------------------------------------------------------------
+// Used by decode steps only (M = sequences in the step, small). One block computes 16 output
+// columns (and the matching 16 up columns for SwiGLU) for up to 32 rows; its 8 waves split K
+// into 8 fixed ranges (by K alone), each accumulating its range in ascending order with
+// v_mfma_f32_16x16x32_bf16, and the 8 partial tiles are added in wave order through LDS. A
+// row's result therefore depends on K and the row only, never on how many sequences share
+// the step. Weight fragments of a wave's whole K range are loaded before the first MFMA so the
+// weight stream (the HBM traffic) is in flight at once; activations are small and L2-resident.
+
+namespace {
+
+constexpr int kDecWaves = 8;
+constexpr int kDecKsMax = 12;  // k-steps of 32 held in registers per wave and pass
+
+template <int WF>
+__device__ __forceinline__ bf16x8 load_b_frag(const WMat& m, int row, int K, int k) {
+  if constexpr (WF == DEC_BF16) {
+    return __builtin_bit_cast(bf16x8, *(const u32x4*)((const uint16_t*)m.w + (int64_t)row * K + k));
+  } else {
+    const uint32_t codes = *(const uint32_t*)((const uint8_t*)m.w + (int64_t)row * (K / 2) + k / 2);
+    const int64_t gi = (int64_t)row * (K / 32) + k / 32;
+    const float zp = bf16_bits_to_f32(m.zp[gi]);
+    const float sc = bf16_bits_to_f32(m.scale[gi]);
+    u32x4 w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t byte = (codes >> (8 * j)) & 0xffu;
+      w[j] = (uint32_t)f32_to_bf16_bits(dequant_u4(byte & 15u, zp, sc)) |
+             ((uint32_t)f32_to_bf16_bits(dequant_u4(byte >> 4, zp, sc)) << 16);
+    }
+    return __builtin_bit_cast(bf16x8, w);
+  }
+}
+
+}  // namespace
+
+template <int WF, int EPI, int MT>
+__global__ __launch_bounds__(512) void gemm_decode(GemmArgs a) {
+  constexpr int NB = EPI == EPI_SWIGLU ? 2 : 1;
+  __shared__ float red[kDecWaves][NB][MT][4][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n0 = blockIdx.x * 16;
+  const int m0 = blockIdx.y * 16 * MT;
+  const int M = a.M, K = a.K;
+
+  WMat bm[NB];
+  int br0;
+  if constexpr (EPI == EPI_SWIGLU) {
+    bm[0] = a.seg[0];
+    bm[1] = a.seg[1];
+    br0 = n0;
+  } else {
+    int s = 0, base = 0;
+    while (s < a.nseg - 1 && n0 >= base + a.seg[s].rows) {
+      base += a.seg[s].rows;
+      ++s;
+    }
+    bm[0] = a.seg[s];
+    br0 = n0 - base;
+  }
+  const int brow = min(br0 + (lane & 15), bm[0].rows - 1);
+  const int ksteps = K / 32;
+  const int ks0 = wave * ksteps / kDecWaves, ks1 = (wave + 1) * ksteps / kDecWaves;
+  int arow[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) arow[mt] = min(m0 + mt * 16 + (lane & 15), M - 1);
+  const int kl = (lane >> 4) * 8;
+
+  f32x4 acc[NB][MT];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[nb][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int kb = ks0; kb < ks1; kb += kDecKsMax) {
+    const int n = min(kDecKsMax, ks1 - kb);
+    bf16x8 bf[NB][kDecKsMax];
+#pragma unroll
+    for (int i = 0; i < kDecKsMax; ++i)
+      if (i < n)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) bf[nb][i] = load_b_frag<WF>(bm[nb], brow, K, (kb + i) * 32 + kl);
+#pragma unroll
+    for (int i = 0; i < kDecKsMax; ++i) {
+      if (i < n) {
+        const int k = (kb + i) * 32 + kl;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const bf16x8 af =
+              __builtin_bit_cast(bf16x8, *(const u32x4*)((const uint16_t*)a.A + (int64_t)arow[mt] * a.lda + k));
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+            acc[nb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[nb][i], acc[nb][mt], 0, 0, 0);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[wave][nb][mt][r][lane] = acc[nb][mt][r];
+  __syncthreads();
+
+  // sum the wave partials in wave order, then the epilogue; thread t -> (mt, r, source lane)
+  for (int t = threadIdx.x; t < MT * 4 * 64; t += 512) {
+    const int mt = t / 256, r = (t / 64) % 4, sl = t % 64;
+    float v[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float s = red[0][nb][mt][r][sl];
+#pragma unroll
+      for (int w = 1; w < kDecWaves; ++w) s += red[w][nb][mt][r][sl];
+      v[nb] = s;
+    }
+    const int m = m0 + mt * 16 + (sl >> 4) * 4 + r;
+    const int ncol = n0 + (sl & 15);
+    if (m >= M || ncol >= a.N) continue;
+    const int64_t o = (int64_t)m * a.ldc + ncol;
+    if constexpr (EPI == EPI_STORE) {
+      ((float*)a.C)[o] = v[0];
+    } else if constexpr (EPI == EPI_RESID) {
+      ((float*)a.C)[o] += v[0];
+    } else {
+      const float y = v[0] / (1.0f + __expf(-v[0])) * v[NB - 1];
+      if (a.c_bf16)
+        ((uint16_t*)a.C)[o] = f32_to_bf16_bits(y);
+      else
+        ((float*)a.C)[o] = y;
+    }
+  }
+}
+
+template <int WF, int MT>
+static hipError_t gemm_decode_epi(int epi, const GemmArgs& a, hipStream_t s) {
+  dim3 g((a.N + 15) / 16, (a.M + 16 * MT - 1) / (16 * MT)), b(512);
+  switch (epi) {
+    case EPI_STORE: gemm_decode<WF, EPI_STORE, MT><<<g, b, 0, s>>>(a); break;
+    case EPI_RESID: gemm_decode<WF, EPI_RESID, MT><<<g, b, 0, s>>>(a); break;
+    case EPI_SWIGLU: gemm_decode<WF, EPI_SWIGLU, MT><<<g, b, 0, s>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+bool gemm_decode_supported(int wdtype) { return wdtype == DEC_BF16 || wdtype == DEC_UINT4_G32; }
+
+hipError_t launch_gemm_decode(int wdtype, int epi, const GemmArgs& a, hipStream_t s) {
+  if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  if (wdtype == DEC_BF16) return a.M <= 16 ? gemm_decode_epi<DEC_BF16, 1>(epi, a, s) : gemm_decode_epi<DEC_BF16, 2>(epi, a, s);
+  if (wdtype == DEC_UINT4_G32)
+    return a.M <= 16 ? gemm_decode_epi<DEC_UINT4_G32, 1>(epi, a, s) : gemm_decode_epi<DEC_UINT4_G32, 2>(epi, a, s);
+  return hipErrorInvalidValue;
+}
+
 }  // namespace dec

@@ -77,9 +77,65 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   }
 }
 
+// Widths that are multiples of 256: each lane loads its d/256 float4 of the row at once, the
+// sum of squares is added per lane in a fixed order and then by a butterfly.
+template <bool BF16_OUT, int VPL>
+__global__ __launch_bounds__(256) void rmsnorm_vec_kernel(const float* __restrict__ x,
+                                                          const int32_t* __restrict__ rows, int n, int d,
+                                                          const float* __restrict__ g, float eps,
+                                                          void* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= n) return;
+  const int src = rows ? rows[r] : r;
+  const float4* xr = (const float4*)(x + (int64_t)src * d);
+  const float4* g4 = (const float4*)g;
+  float4 v[VPL], gv[VPL];
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) {
+    v[j] = xr[lane + 64 * j];
+    gv[j] = g4[lane + 64 * j];
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
+  ss = wave_sum<64>(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) {
+    const float y0 = v[j].x * inv * gv[j].x, y1 = v[j].y * inv * gv[j].y;
+    const float y2 = v[j].z * inv * gv[j].z, y3 = v[j].w * inv * gv[j].w;
+    const int64_t o = (int64_t)r * d + 4 * (lane + 64 * j);
+    if constexpr (BF16_OUT) {
+      u32x2 w;
+      w[0] = (uint32_t)f32_to_bf16_bits(y0) | ((uint32_t)f32_to_bf16_bits(y1) << 16);
+      w[1] = (uint32_t)f32_to_bf16_bits(y2) | ((uint32_t)f32_to_bf16_bits(y3) << 16);
+      *(u32x2*)((uint16_t*)out + o) = w;
+    } else {
+      *(float4*)((float*)out + o) = make_float4(y0, y1, y2, y3);
+    }
+  }
+}
+
+template <bool BF16_OUT>
+static bool rmsnorm_vec(const float* x, const int32_t* rows, int n, int d, const float* g, float eps, void* out,
+                        hipStream_t s) {
+  dim3 grid((n + 3) / 4), b(256);
+  switch (d) {
+    case 256: rmsnorm_vec_kernel<BF16_OUT, 1><<<grid, b, 0, s>>>(x, rows, n, d, g, eps, out); return true;
+    case 512: rmsnorm_vec_kernel<BF16_OUT, 2><<<grid, b, 0, s>>>(x, rows, n, d, g, eps, out); return true;
+    case 1024: rmsnorm_vec_kernel<BF16_OUT, 4><<<grid, b, 0, s>>>(x, rows, n, d, g, eps, out); return true;
+    case 2048: rmsnorm_vec_kernel<BF16_OUT, 8><<<grid, b, 0, s>>>(x, rows, n, d, g, eps, out); return true;
+    case 4096: rmsnorm_vec_kernel<BF16_OUT, 16><<<grid, b, 0, s>>>(x, rows, n, d, g, eps, out); return true;
+  }
+  return false;
+}
+
 hipError_t launch_rmsnorm(const float* x, const int32_t* rows, int n, int d, const float* g, float eps,
                           void* out, bool out_bf16, hipStream_t s) {
   if (n <= 0) return hipSuccess;
+  if (out_bf16 ? rmsnorm_vec<true>(x, rows, n, d, g, eps, out, s) : rmsnorm_vec<false>(x, rows, n, d, g, eps, out, s))
+    return hipGetLastError();
   dim3 grid((n + 3) / 4), b(256);
   if (out_bf16)
     rmsnorm_kernel<true><<<grid, b, 0, s>>>(x, rows, n, d, g, eps, out);
@@ -175,13 +231,20 @@ __device__ __forceinline__ void better(float& bv, int& bi, float v, int i) {
   }
 }
 
-__global__ __launch_bounds__(256) void argmax_kernel(const float* __restrict__ logits, int vocab,
-                                                     int32_t* __restrict__ next) {
-  const int r = blockIdx.x;
+// Two passes: 64 slices of each row in parallel, then the 64 candidates of a row in one wave.
+// The comparison (larger value, or equal value and lower id) finds the lowest id of the
+// maximum in any order of combination.
+constexpr int kArgmaxSlices = 64;
+
+__global__ __launch_bounds__(256) void argmax_slices_kernel(const float* __restrict__ logits, int vocab,
+                                                            float* __restrict__ pv, int32_t* __restrict__ pi) {
+  const int r = blockIdx.y, sl = blockIdx.x;
+  const int len = (vocab + kArgmaxSlices - 1) / kArgmaxSlices;
+  const int lo = sl * len, hi = min(vocab, lo + len);
   const float* row = logits + (int64_t)r * vocab;
   float bv = -__builtin_inff();
   int bi = 0x7fffffff;
-  for (int i = threadIdx.x; i < vocab; i += blockDim.x) better(bv, bi, row[i], i);
+  for (int i = lo + threadIdx.x; i < hi; i += blockDim.x) better(bv, bi, row[i], i);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     float v = __shfl_xor(bv, o, 64);
@@ -198,13 +261,37 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float* __restrict__ l
   __syncthreads();
   if (threadIdx.x == 0) {
     for (int k = 1; k < 4; ++k) better(bv, bi, sv[k], si[k]);
-    next[r] = bi == 0x7fffffff ? 0 : bi;
+    pv[r * kArgmaxSlices + sl] = bv;
+    pi[r * kArgmaxSlices + sl] = bi;
   }
 }
 
-hipError_t launch_argmax(const float* logits, int n_rows, int vocab, int32_t* next, hipStream_t s) {
+__global__ __launch_bounds__(256) void argmax_final_kernel(const float* __restrict__ pv, const int32_t* __restrict__ pi,
+                                                           int n_rows, int32_t* __restrict__ next) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= n_rows) return;
+  float bv = pv[r * kArgmaxSlices + lane];
+  int bi = pi[r * kArgmaxSlices + lane];
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    float v = __shfl_xor(bv, o, 64);
+    int i = __shfl_xor(bi, o, 64);
+    better(bv, bi, v, i);
+  }
+  if (lane == 0) next[r] = bi == 0x7fffffff ? 0 : bi;
+}
+
+size_t argmax_scratch_bytes(int max_rows) { return (size_t)max_rows * kArgmaxSlices * 8; }
+
+hipError_t launch_argmax(const float* logits, int n_rows, int vocab, int32_t* next, void* scratch, hipStream_t s) {
   if (n_rows <= 0) return hipSuccess;
-  argmax_kernel<<<n_rows, 256, 0, s>>>(logits, vocab, next);
+  float* pv = (float*)scratch;
+  int32_t* pi = (int32_t*)(pv + (size_t)n_rows * kArgmaxSlices);
+  argmax_slices_kernel<<<dim3(kArgmaxSlices, n_rows), 256, 0, s>>>(logits, vocab, pv, pi);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  argmax_final_kernel<<<(n_rows + 3) / 4, 256, 0, s>>>(pv, pi, n_rows, next);
   return hipGetLastError();
 }
 

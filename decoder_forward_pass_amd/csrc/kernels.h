@@ -45,6 +45,10 @@ struct AttnRowsArgs {
 int attn_rows_chunk(int head_dim, bool kv_f16, int group);
 hipError_t launch_attn_rows(const AttnRowsArgs& a, hipStream_t s);
 
+// Decode attention: one workgroup per (row, KV head), chunk states merged in the workgroup;
+// writes o[r][h*D + d] (float32 or bf16) directly. Uses a.n_chunks / a.partial not at all.
+hipError_t launch_attn_decode(const AttnRowsArgs& a, void* o, bool out_bf16, hipStream_t s);
+
 // o[r][h*D + d] = combined attention output (float32 or bf16).
 hipError_t launch_attn_combine(const float* partial, int n_rows, int n_heads, int head_dim, int n_chunks,
                                int chunk, const int32_t* row_pos, void* o, bool out_bf16, hipStream_t s);
@@ -76,8 +80,14 @@ struct GemmArgs {
 };
 hipError_t launch_gemm(int wdtype, int epi, const GemmArgs& a, hipStream_t s);
 
-// next[r] = argmax_v logits[r][v], ties to the lowest id.
-hipError_t launch_argmax(const float* logits, int n_rows, int vocab, int32_t* next, hipStream_t s);
+// The same product for decode steps: K split over 8 waves of a block (fixed by K), summed in
+// wave order; bf16 and uint4 weights only.
+bool gemm_decode_supported(int wdtype);
+hipError_t launch_gemm_decode(int wdtype, int epi, const GemmArgs& a, hipStream_t s);
+
+// next[r] = argmax_v logits[r][v], ties to the lowest id; scratch holds argmax_scratch_bytes.
+size_t argmax_scratch_bytes(int max_rows);
+hipError_t launch_argmax(const float* logits, int n_rows, int vocab, int32_t* next, void* scratch, hipStream_t s);
 
 // out[rows][cols] = widened / dequantised matrix (float32).
 hipError_t launch_dequant(int wdtype, const WMat& w, int rows, int cols, float* out, hipStream_t s);
