@@ -44,6 +44,29 @@ __device__ __forceinline__ float dequant_u4(uint32_t q, float zp, float scale) {
   return t * scale;
 }
 
+// ---- cross-lane data movement -------------------------------------------------------------
+// DPP row operations move data between lanes of a 16-lane row inside a VALU instruction
+// (no LDS traffic): quad_perm [1,0,3,2] pairs lanes i ^ 1, quad_perm [2,3,0,1] pairs i ^ 2,
+// row_half_mirror pairs i with 7 - i within 8 lanes, row_mirror pairs i with 15 - i.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+// Sum over aligned groups of WIDTH lanes (WIDTH in 2..64); every lane gets its group's sum.
+// Within a 16-lane row the pairing order is fixed, so the result is deterministic.
+template <int WIDTH>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr (WIDTH >= 2) v += dpp<kDppXor1>(v);
+  if constexpr (WIDTH >= 4) v += dpp<kDppXor2>(v);
+  if constexpr (WIDTH >= 8) v += dpp<kDppHalfMirror>(v);
+  if constexpr (WIDTH >= 16) v += dpp<kDppMirror>(v);
+  if constexpr (WIDTH >= 32) v += __shfl_xor(v, 16, 64);
+  if constexpr (WIDTH >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
 // ---- wave reductions (fixed butterfly order: deterministic) -------------------------------
 template <int WIDTH>
 __device__ __forceinline__ float wave_sum(float v) {
@@ -73,11 +96,12 @@ struct BatchDev {
   int32_t n_rows, n_seqs, n_out, n_tiles;
 };
 
-// Paged KV pool geometry. The pool is [layers][2][n_blocks][Hkv][B][D].
+// Paged KV pool geometry. The pool is [layers][2][n_blocks][Hkv][B][D]; B is a power of two.
 struct PoolDev {
   void* base;
   int64_t n_blocks;
   int32_t n_kv_heads, block_tokens, head_dim;
+  int32_t block_shift;  // log2(block_tokens)
   __device__ __forceinline__ int64_t slab_elems() const {
     return (int64_t)n_kv_heads * block_tokens * head_dim;
   }

@@ -402,13 +402,13 @@ int run_forward(dec_ctx* ctx, hipStream_t st, const BatchDev& b, const int32_t* 
   void* act = ctx->wsp + w.a;
   float* part = (float*)(ctx->wsp + w.part);
   const float2* rope = (const float2*)(ctx->wsp + w.rope);
-  PoolDev pool{ctx->pool, c.n_blocks, Hkv, c.block_tokens, D};
+  PoolDev pool{ctx->pool, c.n_blocks, Hkv, c.block_tokens, D, __builtin_ctz((unsigned)c.block_tokens)};
   const int nch = (max_ctx + w.chunk - 1) / w.chunk;
   // decode steps take the decode GEMM (K split inside a block) where the weight format has one;
   // prefill calls always take the tile GEMM
-  const bool dec_gemm = decode && gemm_decode_supported(c.weight_dtype);
   auto gemm = [&](int epi, const GemmArgs& g) {
-    return dec_gemm ? launch_gemm_decode(c.weight_dtype, epi, g, st) : launch_gemm(c.weight_dtype, epi, g, st);
+    return decode && gemm_decode_supported(c.weight_dtype, g.K) ? launch_gemm_decode(c.weight_dtype, epi, g, st)
+                                                               : launch_gemm(c.weight_dtype, epi, g, st);
   };
 
   TLAUNCH(DEC_K_EMBED, launch_embed(tok_dev ? tok_dev : b.row_tok, N, c.vocab, d, c.weight_dtype, ctx->embed, x, st));

@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnRowsArgs a) {
       float d = 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) d += qv[i][e] * kv[e];
-      d = wave_sum<LPK>(d);
+      d = group_sum<LPK>(d);
       sc[kk][i] = valid ? d : -__builtin_inff();
     }
   }
@@ -277,7 +277,8 @@ __global__ __launch_bounds__(512) void attn_decode_kernel(AttnRowsArgs a, void* 
   constexpr int NWV = 8;
   __shared__ float s_m[NWV][GROUP], s_l[NWV][GROUP];
   __shared__ float s_acc[NWV][GROUP][D];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar table loads
   const int grp = lane / LPK, sub = lane % LPK;
   const int Hkv = a.n_kv_heads, H = a.n_heads;
   const int row = blockIdx.x / Hkv, kvh = blockIdx.x % Hkv;
@@ -286,9 +287,13 @@ __global__ __launch_bounds__(512) void attn_decode_kernel(AttnRowsArgs a, void* 
   const int nch = (ctx + CHUNK - 1) / CHUNK;
   const int seq = a.b.row_seq[row];
   const int32_t* table = a.b.block_tables + (int64_t)seq * a.b.tbl_stride;
-  const int B = a.pool.block_tokens;
-  const int last_blk = (ctx - 1) / B;
-  const KVT* pool = (const KVT*)a.pool.base;
+  const int bsh = a.pool.block_shift, bmask = a.pool.block_tokens - 1;
+  const int last_blk = (ctx - 1) >> bsh;
+  // element offsets: K part of this layer and KV head; V part is one layer-half further
+  const int64_t slab = (int64_t)Hkv * a.pool.block_tokens * D;
+  const KVT* kbase = (const KVT*)a.pool.base + (int64_t)a.layer * 2 * a.pool.n_blocks * slab +
+                     (int64_t)kvh * a.pool.block_tokens * D + sub * EPL;
+  const KVT* vbase = kbase + a.pool.n_blocks * slab;
 
   const float qscale = 1.4426950408889634f / sqrtf((float)D);
   float qv[GROUP][EPL];
@@ -307,17 +312,25 @@ __global__ __launch_bounds__(512) void attn_decode_kernel(AttnRowsArgs a, void* 
     for (int e = 0; e < EPL; ++e) acc[i][e] = 0.f;
   }
 
+  static_assert(CHUNK <= 64 * 16, "a chunk spans at most 64 blocks of 16 positions");
   for (int c = wave; c < nch; c += NWV) {
     const int key0 = c * CHUNK;
+    // the chunk's block ids, one per lane (lane i: the chunk's i-th block), in one load
+    const int b0 = key0 >> bsh;
+    const int blk_lane = table[min(b0 + lane, last_blk)];
     u32x4 kraw[KPG], vraw[KPG];
 #pragma unroll
     for (int kk = 0; kk < KPG; ++kk) {
-      const int kb = min((key0 + kk * KPI) / B, last_blk);  // same block for the KPI keys of a load
-      const int64_t blk = table[kb];
-      const int slot = (key0 + kk * KPI + grp) % B;
-      kraw[kk] = *(const u32x4*)(pool + a.pool.offset(a.layer, 0, blk, kvh, slot) + sub * EPL);
-      vraw[kk] = *(const u32x4*)(pool + a.pool.offset(a.layer, 1, blk, kvh, slot) + sub * EPL);
+      // the KPI keys of one load share a block (B is a multiple of KPI); keys past the context
+      // read a slot of the last block and are masked below
+      const int kb = min((key0 + kk * KPI) >> bsh, last_blk) - b0;
+      const int64_t off = (int64_t)__builtin_amdgcn_readlane(blk_lane, kb) * slab +
+                          ((key0 + kk * KPI + grp) & bmask) * D;
+      kraw[kk] = *(const u32x4*)(kbase + off);
+      vraw[kk] = *(const u32x4*)(vbase + off);
     }
+    // keep the chunk's loads issued together, ahead of the arithmetic that consumes them
+    __builtin_amdgcn_sched_barrier(0);
     float sc[KPG][GROUP];
 #pragma unroll
     for (int kk = 0; kk < KPG; ++kk) {
@@ -329,7 +342,7 @@ __global__ __launch_bounds__(512) void attn_decode_kernel(AttnRowsArgs a, void* 
         float d = 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) d += qv[i][e] * kv[e];
-        d = wave_sum<LPK>(d);
+        d = group_sum<LPK>(d);
         sc[kk][i] = valid ? d : -__builtin_inff();
       }
     }
@@ -472,9 +485,12 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
   const int tile_rows = min(QT, s_n - (row0 - s_row0));
   const int pmax = p0 + tile_rows - 1;
   const int H = a.n_heads;
-  const int B = a.pool.block_tokens;
+  const int bsh = a.pool.block_shift, bmask = a.pool.block_tokens - 1;
   const int32_t* table = a.b.block_tables + (int64_t)seq * a.b.tbl_stride;
-  const uint16_t* pool = (const uint16_t*)a.pool.base;
+  const int64_t slab = (int64_t)a.n_kv_heads * a.pool.block_tokens * D;
+  const uint16_t* kbase = (const uint16_t*)a.pool.base + (int64_t)a.layer * 2 * a.pool.n_blocks * slab +
+                          (int64_t)kvh * a.pool.block_tokens * D;
+  const uint16_t* vbase = kbase + a.pool.n_blocks * slab;
 
   const int qi = wave * 16 + (lane & 15);
   const bool qvalid = qi < tile_rows;
@@ -508,9 +524,9 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
       const int kpos = kt * KT + key;
       u32x4 kv = u32x4{0u, 0u, 0u, 0u}, vv = u32x4{0u, 0u, 0u, 0u};
       if (kpos < ctx_end) {
-        const int64_t blk = table[kpos / B];
-        kv = *(const u32x4*)(pool + a.pool.offset(a.layer, 0, blk, kvh, kpos % B) + part * 8);
-        vv = *(const u32x4*)(pool + a.pool.offset(a.layer, 1, blk, kvh, kpos % B) + part * 8);
+        const int64_t off = (int64_t)table[kpos >> bsh] * slab + (kpos & bmask) * D + part * 8;
+        kv = *(const u32x4*)(kbase + off);
+        vv = *(const u32x4*)(vbase + off);
       }
       *(u32x4*)(Ks + key * KSTR + part * 8) = kv;
 #pragma unroll

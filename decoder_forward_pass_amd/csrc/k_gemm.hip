@@ -212,31 +212,55 @@ hipError_t launch_gemm(int wdtype, int epi, const GemmArgs& a, hipStream_t s) {
 
 // ---- decode GEMM -----------------------------------------------------------------------------
 // Used by decode steps only (M = sequences in the step, small). One block computes 16 output
-// columns (and the matching 16 up columns for SwiGLU) for up to 32 rows; its 8 waves split K
-// into 8 fixed ranges (by K alone), each accumulating its range in ascending order with
-// v_mfma_f32_16x16x32_bf16, and the 8 partial tiles are added in wave order through LDS. A
+// columns (and the matching 16 up columns for SwiGLU) for up to 32 rows. The K/32 k-steps are
+// split into NW equal ranges of NKS steps (NW = 8, or fewer when K/32 is not a multiple of 8;
+// both follow from K alone); wave w accumulates its range in ascending order with
+// v_mfma_f32_16x16x32_bf16, and the NW partial tiles are added in wave order through LDS. A
 // row's result therefore depends on K and the row only, never on how many sequences share
-// the step. Weight fragments of a wave's whole K range are loaded before the first MFMA so the
-// weight stream (the HBM traffic) is in flight at once; activations are small and L2-resident.
+// the step. Every weight and activation fragment of a wave's range is loaded before the first
+// MFMA (a scheduling barrier keeps the compiler from sinking the loads to their uses), so the
+// weight stream -- the HBM traffic -- is in flight at once.
 
 namespace {
 
 constexpr int kDecWaves = 8;
-constexpr int kDecKsMax = 12;  // k-steps of 32 held in registers per wave and pass
 
 template <int WF>
-__device__ __forceinline__ bf16x8 load_b_frag(const WMat& m, int row, int K, int k) {
+struct BRaw;
+template <>
+struct BRaw<DEC_BF16> {
+  u32x4 w;
+};
+template <>
+struct BRaw<DEC_UINT4_G32> {
+  uint32_t codes;
+  uint16_t scale, zp;
+};
+
+template <int WF>
+__device__ __forceinline__ BRaw<WF> load_b_raw(const WMat& m, int row, int K, int k) {
+  BRaw<WF> r;
   if constexpr (WF == DEC_BF16) {
-    return __builtin_bit_cast(bf16x8, *(const u32x4*)((const uint16_t*)m.w + (int64_t)row * K + k));
+    r.w = *(const u32x4*)((const uint16_t*)m.w + (int64_t)row * K + k);
   } else {
-    const uint32_t codes = *(const uint32_t*)((const uint8_t*)m.w + (int64_t)row * (K / 2) + k / 2);
+    r.codes = *(const uint32_t*)((const uint8_t*)m.w + (int64_t)row * (K / 2) + k / 2);
     const int64_t gi = (int64_t)row * (K / 32) + k / 32;
-    const float zp = bf16_bits_to_f32(m.zp[gi]);
-    const float sc = bf16_bits_to_f32(m.scale[gi]);
+    r.scale = m.scale[gi];
+    r.zp = m.zp[gi];
+  }
+  return r;
+}
+
+template <int WF>
+__device__ __forceinline__ bf16x8 b_frag(const BRaw<WF>& r) {
+  if constexpr (WF == DEC_BF16) {
+    return __builtin_bit_cast(bf16x8, r.w);
+  } else {
+    const float zp = bf16_bits_to_f32(r.zp), sc = bf16_bits_to_f32(r.scale);
     u32x4 w;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t byte = (codes >> (8 * j)) & 0xffu;
+      const uint32_t byte = (r.codes >> (8 * j)) & 0xffu;
       w[j] = (uint32_t)f32_to_bf16_bits(dequant_u4(byte & 15u, zp, sc)) |
              ((uint32_t)f32_to_bf16_bits(dequant_u4(byte >> 4, zp, sc)) << 16);
     }
@@ -246,11 +270,12 @@ __device__ __forceinline__ bf16x8 load_b_frag(const WMat& m, int row, int K, int
 
 }  // namespace
 
-template <int WF, int EPI, int MT>
-__global__ __launch_bounds__(512) void gemm_decode(GemmArgs a) {
+template <int WF, int EPI, int MT, int NKS>
+__global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
   constexpr int NB = EPI == EPI_SWIGLU ? 2 : 1;
   __shared__ float red[kDecWaves][NB][MT][4][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n0 = blockIdx.x * 16;
   const int m0 = blockIdx.y * 16 * MT;
   const int M = a.M, K = a.K;
@@ -270,49 +295,49 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a) {
     bm[0] = a.seg[s];
     br0 = n0 - base;
   }
-  const int brow = min(br0 + (lane & 15), bm[0].rows - 1);
-  const int ksteps = K / 32;
-  const int ks0 = wave * ksteps / kDecWaves, ks1 = (wave + 1) * ksteps / kDecWaves;
-  int arow[MT];
+  if (wave < nw) {
+    const int brow = min(br0 + (lane & 15), bm[0].rows - 1);
+    const int kl = (lane >> 4) * 8;
+    const int k0 = wave * NKS * 32 + kl;
+    BRaw<WF> braw[NB][NKS];
+    u32x4 araw[MT][NKS];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) arow[mt] = min(m0 + mt * 16 + (lane & 15), M - 1);
-  const int kl = (lane >> 4) * 8;
-
-  f32x4 acc[NB][MT];
+    for (int i = 0; i < NKS; ++i)
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
+      for (int nb = 0; nb < NB; ++nb) braw[nb][i] = load_b_raw<WF>(bm[nb], brow, K, k0 + i * 32);
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[nb][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int kb = ks0; kb < ks1; kb += kDecKsMax) {
-    const int n = min(kDecKsMax, ks1 - kb);
-    bf16x8 bf[NB][kDecKsMax];
+    for (int mt = 0; mt < MT; ++mt) {
+      const int arow = min(m0 + mt * 16 + (lane & 15), M - 1);
+      const uint16_t* ap = (const uint16_t*)a.A + (int64_t)arow * a.lda + k0;
 #pragma unroll
-    for (int i = 0; i < kDecKsMax; ++i)
-      if (i < n)
+      for (int i = 0; i < NKS; ++i) araw[mt][i] = *(const u32x4*)(ap + i * 32);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 acc[NB][MT];
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) bf[nb][i] = load_b_frag<WF>(bm[nb], brow, K, (kb + i) * 32 + kl);
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-    for (int i = 0; i < kDecKsMax; ++i) {
-      if (i < n) {
-        const int k = (kb + i) * 32 + kl;
+      for (int mt = 0; mt < MT; ++mt) acc[nb][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const bf16x8 af =
-              __builtin_bit_cast(bf16x8, *(const u32x4*)((const uint16_t*)a.A + (int64_t)arow[mt] * a.lda + k));
+    for (int i = 0; i < NKS; ++i) {
+      bf16x8 bf[NB];
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-            acc[nb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[nb][i], acc[nb][mt], 0, 0, 0);
-        }
+      for (int nb = 0; nb < NB; ++nb) bf[nb] = b_frag<WF>(braw[nb][i]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const bf16x8 af = __builtin_bit_cast(bf16x8, araw[mt][i]);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          acc[nb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[nb], acc[nb][mt], 0, 0, 0);
       }
     }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[wave][nb][mt][r][lane] = acc[nb][mt][r];
   }
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) red[wave][nb][mt][r][lane] = acc[nb][mt][r];
   __syncthreads();
 
   // sum the wave partials in wave order, then the epilogue; thread t -> (mt, r, source lane)
@@ -322,8 +347,7 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       float s = red[0][nb][mt][r][sl];
-#pragma unroll
-      for (int w = 1; w < kDecWaves; ++w) s += red[w][nb][mt][r][sl];
+      for (int w = 1; w < nw; ++w) s += red[w][nb][mt][r][sl];
       v[nb] = s;
     }
     const int m = m0 + mt * 16 + (sl >> 4) * 4 + r;
@@ -344,25 +368,51 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a) {
   }
 }
 
-template <int WF, int MT>
-static hipError_t gemm_decode_epi(int epi, const GemmArgs& a, hipStream_t s) {
+template <int WF, int MT, int NKS>
+static hipError_t gemm_decode_go(int epi, const GemmArgs& a, int nw, hipStream_t s) {
   dim3 g((a.N + 15) / 16, (a.M + 16 * MT - 1) / (16 * MT)), b(512);
   switch (epi) {
-    case EPI_STORE: gemm_decode<WF, EPI_STORE, MT><<<g, b, 0, s>>>(a); break;
-    case EPI_RESID: gemm_decode<WF, EPI_RESID, MT><<<g, b, 0, s>>>(a); break;
-    case EPI_SWIGLU: gemm_decode<WF, EPI_SWIGLU, MT><<<g, b, 0, s>>>(a); break;
+    case EPI_STORE: gemm_decode<WF, EPI_STORE, MT, NKS><<<g, b, 0, s>>>(a, nw); break;
+    case EPI_RESID: gemm_decode<WF, EPI_RESID, MT, NKS><<<g, b, 0, s>>>(a, nw); break;
+    case EPI_SWIGLU: gemm_decode<WF, EPI_SWIGLU, MT, NKS><<<g, b, 0, s>>>(a, nw); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-bool gemm_decode_supported(int wdtype) { return wdtype == DEC_BF16 || wdtype == DEC_UINT4_G32; }
+template <int WF, int MT>
+static hipError_t gemm_decode_nks(int epi, const GemmArgs& a, hipStream_t s) {
+  // K split: nw waves of nks k-steps each, nw the largest of 8, 4, 2, 1 dividing K/32
+  const int ksteps = a.K / 32;
+  int nw = kDecWaves;
+  while (ksteps % nw) nw >>= 1;
+  switch (ksteps / nw) {
+    case 1: return gemm_decode_go<WF, MT, 1>(epi, a, nw, s);
+    case 2: return gemm_decode_go<WF, MT, 2>(epi, a, nw, s);
+    case 3: return gemm_decode_go<WF, MT, 3>(epi, a, nw, s);
+    case 4: return gemm_decode_go<WF, MT, 4>(epi, a, nw, s);
+    case 6: return gemm_decode_go<WF, MT, 6>(epi, a, nw, s);
+    case 8: return gemm_decode_go<WF, MT, 8>(epi, a, nw, s);
+    case 12: return gemm_decode_go<WF, MT, 12>(epi, a, nw, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+bool gemm_decode_supported(int wdtype, int K) {
+  if (wdtype != DEC_BF16 && wdtype != DEC_UINT4_G32) return false;
+  const int ksteps = K / 32;
+  int nw = kDecWaves;
+  while (ksteps % nw) nw >>= 1;
+  const int nks = ksteps / nw;
+  return nks == 1 || nks == 2 || nks == 3 || nks == 4 || nks == 6 || nks == 8 || nks == 12;
+}
 
 hipError_t launch_gemm_decode(int wdtype, int epi, const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
-  if (wdtype == DEC_BF16) return a.M <= 16 ? gemm_decode_epi<DEC_BF16, 1>(epi, a, s) : gemm_decode_epi<DEC_BF16, 2>(epi, a, s);
+  if (wdtype == DEC_BF16)
+    return a.M <= 16 ? gemm_decode_nks<DEC_BF16, 1>(epi, a, s) : gemm_decode_nks<DEC_BF16, 2>(epi, a, s);
   if (wdtype == DEC_UINT4_G32)
-    return a.M <= 16 ? gemm_decode_epi<DEC_UINT4_G32, 1>(epi, a, s) : gemm_decode_epi<DEC_UINT4_G32, 2>(epi, a, s);
+    return a.M <= 16 ? gemm_decode_nks<DEC_UINT4_G32, 1>(epi, a, s) : gemm_decode_nks<DEC_UINT4_G32, 2>(epi, a, s);
   return hipErrorInvalidValue;
 }
 

@@ -196,9 +196,8 @@ __global__ __launch_bounds__(256) void qk_rope_kv_kernel(QkRopeArgs a) {
   }
   const int kvh = is_v ? hh - H - Hkv : hh - H;
   const int seq = a.b.row_seq[r];
-  const int B = a.pool.block_tokens;
-  const int64_t blk = a.b.block_tables[(int64_t)seq * a.b.tbl_stride + pos / B];
-  const int64_t off = a.pool.offset(a.layer, is_v ? 1 : 0, blk, kvh, pos % B);
+  const int64_t blk = a.b.block_tables[(int64_t)seq * a.b.tbl_stride + (pos >> a.pool.block_shift)];
+  const int64_t off = a.pool.offset(a.layer, is_v ? 1 : 0, blk, kvh, pos & (a.pool.block_tokens - 1));
   if constexpr (KV_F16) {
     uint16_t* p = (uint16_t*)a.pool.base + off;
     p[lane] = f32_to_f16_bits(x1);

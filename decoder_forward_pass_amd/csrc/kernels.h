@@ -80,9 +80,9 @@ struct GemmArgs {
 };
 hipError_t launch_gemm(int wdtype, int epi, const GemmArgs& a, hipStream_t s);
 
-// The same product for decode steps: K split over 8 waves of a block (fixed by K), summed in
-// wave order; bf16 and uint4 weights only.
-bool gemm_decode_supported(int wdtype);
+// The same product for decode steps: K split over up to 8 waves of a block (fixed by K),
+// summed in wave order; bf16 and uint4 weights, K/32 with a supported per-wave step count.
+bool gemm_decode_supported(int wdtype, int K);
 hipError_t launch_gemm_decode(int wdtype, int epi, const GemmArgs& a, hipStream_t s);
 
 // next[r] = argmax_v logits[r][v], ties to the lowest id; scratch holds argmax_scratch_bytes.
