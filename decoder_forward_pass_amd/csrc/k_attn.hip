@@ -261,24 +261,41 @@ hipError_t launch_attn_combine(const float* partial, int n_rows, int n_heads, in
 }
 
 // ---- decode attention: one workgroup per (sequence, KV head) ------------------------------
-// A decode step has one query row per sequence. The workgroup's 8 waves take the fixed chunks
-// of the row's keys (chunk size as attn_rows) in turn: wave w handles chunks w, w+8, ... in
-// increasing order, keeping a running (max, sum, accumulator) per query head; the block ids of
-// a chunk are wave-uniform, and the K and V loads of a whole chunk are issued before any
-// arithmetic (keys past the context read a valid slot of the last block and are masked).
-// The 8 wave states are then merged in wave order through LDS and the output row is written:
-// no partials leave the workgroup and no combine launch is needed. The split depends only on
-// the row's context length, so the result does not depend on the other sequences.
+// A decode step has one query row per sequence. The workgroup's 16 waves take fixed chunks of
+// the row's keys in turn: wave w handles chunks w, w+16, ... in increasing order, keeping a
+// running (max, sum, accumulator) per query head. A chunk is KPI keys per wave-wide load times
+// DKPG loads; the chunk's block ids arrive in one load (lane i: the chunk's i-th block; the
+// next chunk's ids are requested before the current chunk is consumed), and all K and V
+// loads of a chunk are issued before any arithmetic (keys past the context read a valid slot
+// of the last block and are masked). The 16 wave states are merged in wave order through
+// LDS and the output row is written: no partials leave the workgroup. The split depends only
+// on the row's context length, so the result does not depend on the other sequences.
+
+template <typename KVT, int D, int GROUP>
+struct DecodeGeom {
+  static constexpr int EPL = 16 / (int)sizeof(KVT);
+  static constexpr int LPK = D / EPL;
+  static constexpr int KPI = 64 / LPK;
+  static constexpr int DKPG = (16 / GROUP) > 1 ? 16 / GROUP : 1;  // loads per chunk
+  static constexpr int CHUNK = DKPG * KPI;
+  static constexpr int NWV = 16;
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+// (taken by value: a bit cast applied directly to an element of an ext_vector is miscompiled
+// here into a cast of element 0)
+__device__ __forceinline__ half2v as_half2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
 
 template <typename KVT, int D, int GROUP, bool BF16_OUT>
-__global__ __launch_bounds__(512) void attn_decode_kernel(AttnRowsArgs a, void* out) {
-  using G = RowsGeom<KVT, D, GROUP>;
-  constexpr int EPL = G::EPL, LPK = G::LPK, KPI = G::KPI, KPG = G::KPG, CHUNK = G::CHUNK;
-  constexpr int NWV = 8;
+__global__ __launch_bounds__(1024) void attn_decode_kernel(AttnRowsArgs a, void* out) {
+  using G = DecodeGeom<KVT, D, GROUP>;
+  constexpr int EPL = G::EPL, LPK = G::LPK, KPI = G::KPI, KPG = G::DKPG, CHUNK = G::CHUNK, NWV = G::NWV;
+  static_assert(CHUNK <= 64 * 16, "a chunk spans at most 64 blocks of 16 positions");
   __shared__ float s_m[NWV][GROUP], s_l[NWV][GROUP];
   __shared__ float s_acc[NWV][GROUP][D];
   const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar table loads
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar math
   const int grp = lane / LPK, sub = lane % LPK;
   const int Hkv = a.n_kv_heads, H = a.n_heads;
   const int row = blockIdx.x / Hkv, kvh = blockIdx.x % Hkv;
@@ -289,20 +306,19 @@ __global__ __launch_bounds__(512) void attn_decode_kernel(AttnRowsArgs a, void* 
   const int32_t* table = a.b.block_tables + (int64_t)seq * a.b.tbl_stride;
   const int bsh = a.pool.block_shift, bmask = a.pool.block_tokens - 1;
   const int last_blk = (ctx - 1) >> bsh;
-  // element offsets: K part of this layer and KV head; V part is one layer-half further
   const int64_t slab = (int64_t)Hkv * a.pool.block_tokens * D;
   const KVT* kbase = (const KVT*)a.pool.base + (int64_t)a.layer * 2 * a.pool.n_blocks * slab +
                      (int64_t)kvh * a.pool.block_tokens * D + sub * EPL;
   const KVT* vbase = kbase + a.pool.n_blocks * slab;
 
+  // q . k: f16 pairs through v_dot2_f32_f16 (products exact in the float32 sum), float32
+  // pools through FMAs; the score is scaled by log2(e)/sqrt(D) afterwards
+  constexpr bool F16 = sizeof(KVT) == 2;
   const float qscale = 1.4426950408889634f / sqrtf((float)D);
-  float qv[GROUP][EPL];
+  u32x4 qraw[GROUP];
 #pragma unroll
-  for (int i = 0; i < GROUP; ++i) {
-    load_kv<KVT, EPL>((const KVT*)a.q + ((int64_t)row * H + kvh * GROUP + i) * D + sub * EPL, qv[i]);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) qv[i][e] *= qscale;
-  }
+  for (int i = 0; i < GROUP; ++i)
+    qraw[i] = *(const u32x4*)((const KVT*)a.q + ((int64_t)row * H + kvh * GROUP + i) * D + sub * EPL);
   float m[GROUP], l[GROUP], acc[GROUP][EPL];
 #pragma unroll
   for (int i = 0; i < GROUP; ++i) {
@@ -312,37 +328,40 @@ __global__ __launch_bounds__(512) void attn_decode_kernel(AttnRowsArgs a, void* 
     for (int e = 0; e < EPL; ++e) acc[i][e] = 0.f;
   }
 
-  static_assert(CHUNK <= 64 * 16, "a chunk spans at most 64 blocks of 16 positions");
+  int blk_lane = wave < nch ? table[min(((wave * CHUNK) >> bsh) + lane, last_blk)] : 0;
   for (int c = wave; c < nch; c += NWV) {
     const int key0 = c * CHUNK;
-    // the chunk's block ids, one per lane (lane i: the chunk's i-th block), in one load
     const int b0 = key0 >> bsh;
-    const int blk_lane = table[min(b0 + lane, last_blk)];
     u32x4 kraw[KPG], vraw[KPG];
 #pragma unroll
     for (int kk = 0; kk < KPG; ++kk) {
-      // the KPI keys of one load share a block (B is a multiple of KPI); keys past the context
-      // read a slot of the last block and are masked below
+      // the KPI keys of one load share a block (B is a multiple of KPI)
       const int kb = min((key0 + kk * KPI) >> bsh, last_blk) - b0;
       const int64_t off = (int64_t)__builtin_amdgcn_readlane(blk_lane, kb) * slab +
                           ((key0 + kk * KPI + grp) & bmask) * D;
       kraw[kk] = *(const u32x4*)(kbase + off);
       vraw[kk] = *(const u32x4*)(vbase + off);
     }
+    const int cn = c + NWV;
+    if (cn < nch) blk_lane = table[min(((cn * CHUNK) >> bsh) + lane, last_blk)];
     // keep the chunk's loads issued together, ahead of the arithmetic that consumes them
     __builtin_amdgcn_sched_barrier(0);
     float sc[KPG][GROUP];
 #pragma unroll
     for (int kk = 0; kk < KPG; ++kk) {
-      float kv[EPL];
-      load_kv<KVT, EPL>((const KVT*)&kraw[kk], kv);
       const bool valid = key0 + kk * KPI + grp < ctx;
 #pragma unroll
       for (int i = 0; i < GROUP; ++i) {
         float d = 0.f;
+        if constexpr (F16) {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) d += qv[i][e] * kv[e];
-        d = group_sum<LPK>(d);
+          for (int j = 0; j < 4; ++j)
+            d = __builtin_amdgcn_fdot2(as_half2(qraw[i][j]), as_half2(kraw[kk][j]), d, false);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) d += __uint_as_float(qraw[i][j]) * __uint_as_float(kraw[kk][j]);
+        }
+        d = group_sum<LPK>(d) * qscale;
         sc[kk][i] = valid ? d : -__builtin_inff();
       }
     }
@@ -354,7 +373,7 @@ __global__ __launch_bounds__(512) void attn_decode_kernel(AttnRowsArgs a, void* 
 #pragma unroll
       for (int o = LPK; o < 64; o <<= 1) mc = fmaxf(mc, __shfl_xor(mc, o, 64));
       const float mn = fmaxf(m[i], mc);
-      const float alpha = exp2f(m[i] - mn);  // 0 on the first chunk (m = -inf)
+      const float alpha = fast_exp2(m[i] - mn);  // 0 on the first chunk (m = -inf)
       m[i] = mn;
       l[i] *= alpha;
 #pragma unroll
@@ -368,7 +387,7 @@ __global__ __launch_bounds__(512) void attn_decode_kernel(AttnRowsArgs a, void* 
       load_kv<KVT, EPL>((const KVT*)&vraw[kk], vv);
 #pragma unroll
       for (int i = 0; i < GROUP; ++i) {
-        const float p = exp2f(sc[kk][i] - m[i]);
+        const float p = fast_exp2(sc[kk][i] - m[i]);
         l[i] += p;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[i][e] += p * vv[e];
@@ -398,13 +417,13 @@ __global__ __launch_bounds__(512) void attn_decode_kernel(AttnRowsArgs a, void* 
   }
   __syncthreads();
   const int nw = min(NWV, nch);  // waves that saw at least one chunk
-  for (int t = threadIdx.x; t < GROUP * D; t += 512) {
+  for (int t = threadIdx.x; t < GROUP * D; t += 1024) {
     const int i = t / D, d = t % D;
     float M = s_m[0][i];
     for (int w = 1; w < nw; ++w) M = fmaxf(M, s_m[w][i]);
     float L = 0.f, A = 0.f;
     for (int w = 0; w < nw; ++w) {
-      const float sc = exp2f(s_m[w][i] - M);
+      const float sc = fast_exp2(s_m[w][i] - M);
       L += sc * s_l[w][i];
       A += sc * s_acc[w][i][d];
     }
@@ -421,9 +440,9 @@ template <typename KVT, int D, int GROUP>
 static void decode_launch(const AttnRowsArgs& a, void* o, bool bf16_out, hipStream_t s) {
   dim3 g(a.b.n_rows * a.n_kv_heads);
   if (bf16_out)
-    attn_decode_kernel<KVT, D, GROUP, true><<<g, 512, 0, s>>>(a, o);
+    attn_decode_kernel<KVT, D, GROUP, true><<<g, 1024, 0, s>>>(a, o);
   else
-    attn_decode_kernel<KVT, D, GROUP, false><<<g, 512, 0, s>>>(a, o);
+    attn_decode_kernel<KVT, D, GROUP, false><<<g, 1024, 0, s>>>(a, o);
 }
 
 template <typename KVT, int D>
