@@ -44,8 +44,27 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="q06b_bf16_b32_p1024_d256")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--profile-steps", type=int, default=None, help=argparse.SUPPRESS)
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="first run one device-to-device copy of this many MiB (a reference dispatch of known "
+                         "traffic for hardware-counter runs)")
     return ap.parse_args()
+
+
+def measured_traffic(name):
+    """Bytes per launch from the committed hardware-counter summary, or None when the kernel's
+    sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", name)
+    try:
+        with open(path) as f:
+            d = json.load(f)
+        h = hashlib.sha256()
+        for src in d["sources"]:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        return d["traffic_bytes_per_launch"] if h.hexdigest() == d["source_sha256"] else None
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(wl, shape, weights, prompts, decode_steps=8):
@@ -99,6 +118,13 @@ def main():
     logits = torch.empty((S, shape.vocab), dtype=torch.float32, device="cuda")
     positions = [np.full(S, P + t, np.int32) for t in range(steps)]
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    if args.copy_mb:
+        src = torch.empty(args.copy_mb << 18, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # kernel classes timed live over the timed region: the prefill's gate/up GEMM and the
     # decode steps' attention
@@ -181,9 +207,10 @@ def main():
         "prefill_ms": round(pre_ms, 3),
         "decode_ms_per_step": round(dec_ms / steps, 4),
         "roofline": {
-            "kernel": "attn_rows (decode attention)",
+            "kernel": "attn_decode_kernel (decode attention, q/k norm + RoPE + KV write fused)",
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(f"attn_decode_kernel_{wl.name}_pmc.json"),
             "launches": rows_n, "launches_expected": rows_launches_expected,
             "avg_launch_us": round(rows_avg_ms * 1e3, 2), "algorithmic_bytes_per_launch": rows_launch_bytes,
         },

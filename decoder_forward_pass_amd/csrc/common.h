@@ -81,6 +81,23 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// ---- per-head q/k RMSNorm + split-halves RoPE ----------------------------------------------
+// Lane j < D/2 holds channels (j, j + D/2) of one head (other lanes hold zeros). RMSNorm over
+// the D channels with gain g, then rotation of the pair by the angle's (cos, sin).
+__device__ __forceinline__ void norm_rope_pair(float& x1, float& x2, const float* g, float2 cs, int lane, int D,
+                                               float eps) {
+  const int half = D / 2;
+  const float ss = wave_sum<64>(x1 * x1 + x2 * x2);
+  const float inv = 1.0f / sqrtf(ss / (float)D + eps);
+  if (lane < half) {
+    const float a = x1 * inv * g[lane];
+    const float b = x2 * inv * g[lane + half];
+    x1 = a * cs.x - b * cs.y;
+    x2 = b * cs.x + a * cs.y;
+  }
+}
+
+
 // ---- per-call batch description (device copies of the host-validated metadata) ------------
 struct BatchDev {
   const int32_t* row_tok;      // [n_rows]

@@ -135,7 +135,7 @@ size_t kv_bytes(const dec_config& c) {
 // ---- workspace layout ----------------------------------------------------------------------
 
 struct Ws {
-  size_t rope, meta, x, h, qkv, q, o, a, part, amax, total;
+  size_t rope, meta, x, h, qkv, q, o, a, part, amax, ssq, total;
   size_t meta_ints;  // capacity of the metadata region in int32
   int chunk, nch_max, max_blocks_per_seq, max_tiles;
   int act_bytes, kv_el;
@@ -174,6 +174,7 @@ Ws ws_layout(const dec_config& c) {
   const size_t prow = w.flash ? 0 : R;
   w.part = take(prow * H * (size_t)w.nch_max * (D + 2) * 4);
   w.amax = take(argmax_scratch_bytes((int)R));
+  w.ssq = take(S * (d / 16) * 4);  // decode: sums of squares of the residual in 16-column partials
   w.total = off;
   return w;
 }
@@ -401,58 +402,87 @@ int run_forward(dec_ctx* ctx, hipStream_t st, const BatchDev& b, const int32_t* 
   void* o = ctx->wsp + w.o;
   void* act = ctx->wsp + w.a;
   float* part = (float*)(ctx->wsp + w.part);
+  float* ssq = (float*)(ctx->wsp + w.ssq);
   const float2* rope = (const float2*)(ctx->wsp + w.rope);
   PoolDev pool{ctx->pool, c.n_blocks, Hkv, c.block_tokens, D, __builtin_ctz((unsigned)c.block_tokens)};
   const int nch = (max_ctx + w.chunk - 1) / w.chunk;
-  // decode steps take the decode GEMM (K split inside a block) where the weight format has one;
-  // prefill calls always take the tile GEMM
+  // Decode steps take the decode GEMM (K split inside a block) when the weight format has one:
+  // it normalises its input on the fly from the residual's 16-column sums of squares, which
+  // the embedding and the residual epilogues write, so decode needs no separate RMSNorm
+  // launch. Prefill calls always take the tile GEMM after an RMSNorm launch.
+  const bool dgemm = decode && gemm_decode_supported(c.weight_dtype, d) &&
+                     gemm_decode_supported(c.weight_dtype, qw) && gemm_decode_supported(c.weight_dtype, ff);
   auto gemm = [&](int epi, const GemmArgs& g) {
-    return decode && gemm_decode_supported(c.weight_dtype, g.K) ? launch_gemm_decode(c.weight_dtype, epi, g, st)
-                                                               : launch_gemm(c.weight_dtype, epi, g, st);
+    return dgemm ? launch_gemm_decode(c.weight_dtype, epi, g, st) : launch_gemm(c.weight_dtype, epi, g, st);
+  };
+  // A of a normalising GEMM: the residual itself (decode GEMM) or the RMSNorm output
+  auto norm_input = [&](GemmArgs& g, const float* gain) {
+    if (dgemm) {
+      g.A = x; g.lda = d; g.gain = gain; g.ssq_in = ssq; g.eps = c.rms_eps;
+    } else {
+      g.A = h; g.lda = d;
+    }
   };
 
-  TLAUNCH(DEC_K_EMBED, launch_embed(tok_dev ? tok_dev : b.row_tok, N, c.vocab, d, c.weight_dtype, ctx->embed, x, st));
+  TLAUNCH(DEC_K_EMBED, launch_embed(tok_dev ? tok_dev : b.row_tok, N, c.vocab, d, c.weight_dtype, ctx->embed, x,
+                                    dgemm ? ssq : nullptr, st));
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerW& L = ctx->layers[l];
-    TLAUNCH(DEC_K_RMSNORM, launch_rmsnorm(x, nullptr, N, d, L.attn_norm, c.rms_eps, h, act_bf16, st));
+    if (!dgemm) TLAUNCH(DEC_K_RMSNORM, launch_rmsnorm(x, nullptr, N, d, L.attn_norm, c.rms_eps, h, act_bf16, st));
     GemmArgs g{};
-    g.A = h; g.lda = d; g.M = N; g.N = qkvw; g.K = d;
+    norm_input(g, L.attn_norm);
+    g.M = N; g.N = qkvw; g.K = d;
     g.seg[0] = L.wq; g.seg[1] = L.wk; g.seg[2] = L.wv; g.nseg = 3;
     g.C = qkv; g.ldc = qkvw;
     TLAUNCH(DEC_K_GEMM_QKV, gemm(EPI_STORE, g));
     QkRopeArgs qa{qkv, L.q_norm, L.k_norm, rope, q, pool, l, H, Hkv, D, c.rms_eps, kv_f16, b};
-    TLAUNCH(DEC_K_QK_ROPE_KV, launch_qk_rope_kv(qa, st));
     if (decode) {
       AttnRowsArgs ra{q, pool, l, H, Hkv, D, kv_f16, nch, part, b};
-      TLAUNCH(DEC_K_ATTN_ROWS, launch_attn_decode(ra, o, act_bf16, st));
-    } else if (w.flash) {
-      AttnPrefillArgs pa{(const uint16_t*)q, pool, l, H, Hkv, D, o, act_bf16, b};
-      TLAUNCH(DEC_K_ATTN_PREFILL, launch_attn_prefill(pa, st));
+      TLAUNCH(DEC_K_ATTN_ROWS, launch_attn_decode(qa, ra, o, act_bf16, st));
     } else {
-      AttnRowsArgs ra{q, pool, l, H, Hkv, D, kv_f16, nch, part, b};
-      TLAUNCH(DEC_K_ATTN_ROWS, launch_attn_rows(ra, st));
-      TLAUNCH(DEC_K_ATTN_COMBINE, launch_attn_combine(part, N, H, D, nch, w.chunk, b.row_pos, o, act_bf16, st));
+      TLAUNCH(DEC_K_QK_ROPE_KV, launch_qk_rope_kv(qa, st));
+      if (w.flash) {
+        AttnPrefillArgs pa{(const uint16_t*)q, pool, l, H, Hkv, D, o, act_bf16, b};
+        TLAUNCH(DEC_K_ATTN_PREFILL, launch_attn_prefill(pa, st));
+      } else {
+        AttnRowsArgs ra{q, pool, l, H, Hkv, D, kv_f16, nch, part, b};
+        TLAUNCH(DEC_K_ATTN_ROWS, launch_attn_rows(ra, st));
+        TLAUNCH(DEC_K_ATTN_COMBINE, launch_attn_combine(part, N, H, D, nch, w.chunk, b.row_pos, o, act_bf16, st));
+      }
     }
     g = GemmArgs{};
     g.A = o; g.lda = qw; g.M = N; g.N = d; g.K = qw;
     g.seg[0] = L.wo; g.nseg = 1; g.C = x; g.ldc = d;
+    g.ssq_out = dgemm ? ssq : nullptr;
     TLAUNCH(DEC_K_GEMM_O, gemm(EPI_RESID, g));
-    TLAUNCH(DEC_K_RMSNORM, launch_rmsnorm(x, nullptr, N, d, L.ffn_norm, c.rms_eps, h, act_bf16, st));
+    if (!dgemm) TLAUNCH(DEC_K_RMSNORM, launch_rmsnorm(x, nullptr, N, d, L.ffn_norm, c.rms_eps, h, act_bf16, st));
     g = GemmArgs{};
-    g.A = h; g.lda = d; g.M = N; g.N = ff; g.K = d;
+    norm_input(g, L.ffn_norm);
+    g.M = N; g.N = ff; g.K = d;
     g.seg[0] = L.wg; g.seg[1] = L.wu; g.nseg = 2; g.C = act; g.ldc = ff; g.c_bf16 = act_bf16;
     TLAUNCH(DEC_K_GEMM_GATEUP, gemm(EPI_SWIGLU, g));
     g = GemmArgs{};
     g.A = act; g.lda = ff; g.M = N; g.N = d; g.K = ff;
     g.seg[0] = L.wd; g.nseg = 1; g.C = x; g.ldc = d;
+    g.ssq_out = dgemm ? ssq : nullptr;
     TLAUNCH(DEC_K_GEMM_DOWN, gemm(EPI_RESID, g));
   }
   if (b.n_out > 0 && logits) {
-    TLAUNCH(DEC_K_RMSNORM, launch_rmsnorm(x, b.out_rows, b.n_out, d, ctx->final_norm, c.rms_eps, h, act_bf16, st));
     GemmArgs g{};
-    g.A = h; g.lda = d; g.M = b.n_out; g.N = c.vocab; g.K = d;
+    if (dgemm) {
+      // decode: every row gets logits, in row order (one row per sequence)
+      norm_input(g, ctx->final_norm);
+    } else {
+      TLAUNCH(DEC_K_RMSNORM, launch_rmsnorm(x, b.out_rows, b.n_out, d, ctx->final_norm, c.rms_eps, h, act_bf16, st));
+      g.A = h; g.lda = d;
+    }
+    g.M = b.n_out; g.N = c.vocab; g.K = d;
     g.seg[0] = ctx->embed; g.nseg = 1; g.C = logits; g.ldc = c.vocab;
-    TLAUNCH(DEC_K_GEMM_LMHEAD, gemm(EPI_STORE, g));
+    if (dgemm && lmhead_decode_supported(c.weight_dtype, b.n_out, d)) {
+      TLAUNCH(DEC_K_GEMM_LMHEAD, launch_lmhead_decode(c.weight_dtype, g, st));
+    } else {
+      TLAUNCH(DEC_K_GEMM_LMHEAD, gemm(EPI_STORE, g));
+    }
     if (next) TLAUNCH(DEC_K_ARGMAX, launch_argmax(logits, b.n_out, c.vocab, next, ctx->wsp + w.amax, st));
   }
   return DEC_OK;

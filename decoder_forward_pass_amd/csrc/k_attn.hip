@@ -288,12 +288,13 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ half2v as_half2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
 
 template <typename KVT, int D, int GROUP, bool BF16_OUT>
-__global__ __launch_bounds__(1024) void attn_decode_kernel(AttnRowsArgs a, void* out) {
+__global__ __launch_bounds__(1024) void attn_decode_kernel(QkRopeArgs qk, AttnRowsArgs a, void* out) {
   using G = DecodeGeom<KVT, D, GROUP>;
   constexpr int EPL = G::EPL, LPK = G::LPK, KPI = G::KPI, KPG = G::DKPG, CHUNK = G::CHUNK, NWV = G::NWV;
   static_assert(CHUNK <= 64 * 16, "a chunk spans at most 64 blocks of 16 positions");
   __shared__ float s_m[NWV][GROUP], s_l[NWV][GROUP];
   __shared__ float s_acc[NWV][GROUP][D];
+  __shared__ __attribute__((aligned(16))) KVT s_q[GROUP][D];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar math
   const int grp = lane / LPK, sub = lane % LPK;
@@ -311,14 +312,45 @@ __global__ __launch_bounds__(1024) void attn_decode_kernel(AttnRowsArgs a, void*
                      (int64_t)kvh * a.pool.block_tokens * D + sub * EPL;
   const KVT* vbase = kbase + a.pool.n_blocks * slab;
 
+  constexpr bool F16 = sizeof(KVT) == 2;
+  // The row's new query heads, key and value: wave i < GROUP normalises and rotates query head
+  // kvh*GROUP + i into LDS (in the pool's format, as the q buffer holds it for prefill); wave
+  // GROUP does the key and wave GROUP + 1 copies the value into the pool at (table[pos / B],
+  // pos % B). The barrier makes the pool writes visible to the waves that read the last chunk.
+  if (wave <= GROUP + 1) {
+    const int half = D / 2;
+    const int hh = wave < GROUP ? kvh * GROUP + wave : (wave == GROUP ? H + kvh : H + Hkv + kvh);
+    const float* src = qk.qkv + (int64_t)row * (H + 2 * Hkv) * D + (int64_t)hh * D;
+    float x1 = lane < half ? src[lane] : 0.f, x2 = lane < half ? src[lane + half] : 0.f;
+    if (wave <= GROUP) {
+      const float2 cs = lane < half ? qk.rope[(int64_t)pos * half + lane] : make_float2(1.f, 0.f);
+      norm_rope_pair(x1, x2, wave < GROUP ? qk.q_norm : qk.k_norm, cs, lane, D, qk.eps);
+    }
+    if (lane < half) {
+      KVT* dst;
+      if (wave < GROUP) {
+        dst = s_q[wave];
+      } else {
+        const int64_t blk = table[pos >> bsh];
+        dst = (KVT*)a.pool.base + a.pool.offset(a.layer, wave == GROUP ? 0 : 1, blk, kvh, pos & bmask);
+      }
+      if constexpr (F16) {
+        dst[lane] = f32_to_f16_bits(x1);
+        dst[lane + half] = f32_to_f16_bits(x2);
+      } else {
+        dst[lane] = x1;
+        dst[lane + half] = x2;
+      }
+    }
+  }
+  __syncthreads();
+
   // q . k: f16 pairs through v_dot2_f32_f16 (products exact in the float32 sum), float32
   // pools through FMAs; the score is scaled by log2(e)/sqrt(D) afterwards
-  constexpr bool F16 = sizeof(KVT) == 2;
   const float qscale = 1.4426950408889634f / sqrtf((float)D);
   u32x4 qraw[GROUP];
 #pragma unroll
-  for (int i = 0; i < GROUP; ++i)
-    qraw[i] = *(const u32x4*)((const KVT*)a.q + ((int64_t)row * H + kvh * GROUP + i) * D + sub * EPL);
+  for (int i = 0; i < GROUP; ++i) qraw[i] = *(const u32x4*)(&s_q[i][sub * EPL]);
   float m[GROUP], l[GROUP], acc[GROUP][EPL];
 #pragma unroll
   for (int i = 0; i < GROUP; ++i) {
@@ -437,36 +469,37 @@ __global__ __launch_bounds__(1024) void attn_decode_kernel(AttnRowsArgs a, void*
 }
 
 template <typename KVT, int D, int GROUP>
-static void decode_launch(const AttnRowsArgs& a, void* o, bool bf16_out, hipStream_t s) {
+static void decode_launch(const QkRopeArgs& qk, const AttnRowsArgs& a, void* o, bool bf16_out, hipStream_t s) {
   dim3 g(a.b.n_rows * a.n_kv_heads);
   if (bf16_out)
-    attn_decode_kernel<KVT, D, GROUP, true><<<g, 1024, 0, s>>>(a, o);
+    attn_decode_kernel<KVT, D, GROUP, true><<<g, 1024, 0, s>>>(qk, a, o);
   else
-    attn_decode_kernel<KVT, D, GROUP, false><<<g, 1024, 0, s>>>(a, o);
+    attn_decode_kernel<KVT, D, GROUP, false><<<g, 1024, 0, s>>>(qk, a, o);
 }
 
 template <typename KVT, int D>
-static hipError_t decode_dispatch_group(const AttnRowsArgs& a, void* o, bool bf16_out, hipStream_t s) {
+static hipError_t decode_dispatch_group(const QkRopeArgs& qk, const AttnRowsArgs& a, void* o, bool bf16_out,
+                                        hipStream_t s) {
   switch (a.n_heads / a.n_kv_heads) {
-    case 1: decode_launch<KVT, D, 1>(a, o, bf16_out, s); break;
-    case 2: decode_launch<KVT, D, 2>(a, o, bf16_out, s); break;
-    case 4: decode_launch<KVT, D, 4>(a, o, bf16_out, s); break;
-    case 8: decode_launch<KVT, D, 8>(a, o, bf16_out, s); break;
+    case 1: decode_launch<KVT, D, 1>(qk, a, o, bf16_out, s); break;
+    case 2: decode_launch<KVT, D, 2>(qk, a, o, bf16_out, s); break;
+    case 4: decode_launch<KVT, D, 4>(qk, a, o, bf16_out, s); break;
+    case 8: decode_launch<KVT, D, 8>(qk, a, o, bf16_out, s); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_attn_decode(const AttnRowsArgs& a, void* o, bool out_bf16, hipStream_t s) {
+hipError_t launch_attn_decode(const QkRopeArgs& qk, const AttnRowsArgs& a, void* o, bool out_bf16, hipStream_t s) {
   if (a.b.n_rows <= 0) return hipSuccess;
   if (a.kv_f16) {
-    if (a.head_dim == 32) return decode_dispatch_group<uint16_t, 32>(a, o, out_bf16, s);
-    if (a.head_dim == 64) return decode_dispatch_group<uint16_t, 64>(a, o, out_bf16, s);
-    if (a.head_dim == 128) return decode_dispatch_group<uint16_t, 128>(a, o, out_bf16, s);
+    if (a.head_dim == 32) return decode_dispatch_group<uint16_t, 32>(qk, a, o, out_bf16, s);
+    if (a.head_dim == 64) return decode_dispatch_group<uint16_t, 64>(qk, a, o, out_bf16, s);
+    if (a.head_dim == 128) return decode_dispatch_group<uint16_t, 128>(qk, a, o, out_bf16, s);
   } else {
-    if (a.head_dim == 32) return decode_dispatch_group<float, 32>(a, o, out_bf16, s);
-    if (a.head_dim == 64) return decode_dispatch_group<float, 64>(a, o, out_bf16, s);
-    if (a.head_dim == 128) return decode_dispatch_group<float, 128>(a, o, out_bf16, s);
+    if (a.head_dim == 32) return decode_dispatch_group<float, 32>(qk, a, o, out_bf16, s);
+    if (a.head_dim == 64) return decode_dispatch_group<float, 64>(qk, a, o, out_bf16, s);
+    if (a.head_dim == 128) return decode_dispatch_group<float, 128>(qk, a, o, out_bf16, s);
   }
   return hipErrorInvalidValue;
 }

@@ -272,8 +272,12 @@ __device__ __forceinline__ bf16x8 b_frag(const BRaw<WF>& r) {
 
 template <int WF, int EPI, int MT, int NKS>
 __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
+  // STORE / SWIGLU read the float32 residual and normalise it on the fly (RMSNorm fused);
+  // RESID reads a bf16 activation and writes the sums of squares of the new residual.
+  constexpr bool NORM = EPI != EPI_RESID;
   constexpr int NB = EPI == EPI_SWIGLU ? 2 : 1;
   __shared__ float red[kDecWaves][NB][MT][4][64];
+  __shared__ float s_inv[16 * MT];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n0 = blockIdx.x * 16;
@@ -295,12 +299,25 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
     bm[0] = a.seg[s];
     br0 = n0 - base;
   }
-  if (wave < nw) {
-    const int brow = min(br0 + (lane & 15), bm[0].rows - 1);
-    const int kl = (lane >> 4) * 8;
-    const int k0 = wave * NKS * 32 + kl;
-    BRaw<WF> braw[NB][NKS];
-    u32x4 araw[MT][NKS];
+  const bool active = wave < nw;
+  // RESID: the residual values this thread updates in the epilogue, requested with the
+  // operand loads instead of after the reduction
+  float xres = 0.f;
+  if constexpr (EPI == EPI_RESID) {
+    if (threadIdx.x < MT * 256) {
+      const int t = threadIdx.x, sl = t % 64;
+      const int m = m0 + (t / 256) * 16 + (sl >> 4) * 4 + (t / 64) % 4, ncol = n0 + (sl & 15);
+      if (m < M && ncol < a.N) xres = ((const float*)a.C)[(int64_t)m * a.ldc + ncol];
+    }
+  }
+  const int brow = min(br0 + (lane & 15), bm[0].rows - 1);
+  const int kl = (lane >> 4) * 8;
+  const int k0 = wave * NKS * 32 + kl;
+  BRaw<WF> braw[NB][NKS];
+  u32x4 araw[MT][NKS][NORM ? 2 : 1];
+  float4 graw[NORM ? NKS : 1][2];
+  float4 sraw[NORM ? 4 : 1];
+  if (active) {
 #pragma unroll
     for (int i = 0; i < NKS; ++i)
 #pragma unroll
@@ -308,11 +325,56 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int arow = min(m0 + mt * 16 + (lane & 15), M - 1);
-      const uint16_t* ap = (const uint16_t*)a.A + (int64_t)arow * a.lda + k0;
+      if constexpr (NORM) {
+        const float* ap = (const float*)a.A + (int64_t)arow * a.lda + k0;
 #pragma unroll
-      for (int i = 0; i < NKS; ++i) araw[mt][i] = *(const u32x4*)(ap + i * 32);
+        for (int i = 0; i < NKS; ++i) {
+          araw[mt][i][0] = *(const u32x4*)(ap + i * 32);
+          araw[mt][i][1] = *(const u32x4*)(ap + i * 32 + 4);
+        }
+      } else {
+        const uint16_t* ap = (const uint16_t*)a.A + (int64_t)arow * a.lda + k0;
+#pragma unroll
+        for (int i = 0; i < NKS; ++i) araw[mt][i][0] = *(const u32x4*)(ap + i * 32);
+      }
     }
-    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (NORM) {
+#pragma unroll
+      for (int i = 0; i < NKS; ++i) {
+        graw[i][0] = *(const float4*)(a.gain + k0 + i * 32);
+        graw[i][1] = *(const float4*)(a.gain + k0 + i * 32 + 4);
+      }
+    }
+  }
+  // the rows' sums of squares: 4 threads per row, each adding a quarter of the row's K/16
+  // partials in order, then the 4 quarters through a fixed DPP pairing
+  const int nq = K / 64;
+  const float* sp = nullptr;
+  if constexpr (NORM) {
+    if (threadIdx.x < 64 * MT) {
+      sp = a.ssq_in + (int64_t)min(m0 + (int)(threadIdx.x >> 2), M - 1) * (K / 16) + (threadIdx.x & 3) * nq;
+      if (nq == 16)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sraw[j] = *(const float4*)(sp + 4 * j);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (NORM) {
+    if (threadIdx.x < 64 * MT) {
+      float s = 0.f;
+      if (nq == 16) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s += sraw[j].x + sraw[j].y + sraw[j].z + sraw[j].w;
+      } else {
+        for (int j = 0; j < nq; ++j) s += sp[j];
+      }
+      s += dpp<kDppXor1>(s);
+      s += dpp<kDppXor2>(s);
+      if ((threadIdx.x & 3) == 0) s_inv[threadIdx.x >> 2] = 1.0f / sqrtf(s / (float)K + a.eps);
+    }
+    __syncthreads();
+  }
+  if (active) {
     f32x4 acc[NB][MT];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -325,7 +387,23 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
       for (int nb = 0; nb < NB; ++nb) bf[nb] = b_frag<WF>(braw[nb][i]);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const bf16x8 af = __builtin_bit_cast(bf16x8, araw[mt][i]);
+        bf16x8 af;
+        if constexpr (NORM) {
+          const float inv = s_inv[mt * 16 + (lane & 15)];
+          u32x4 w;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const float* xv = (const float*)&araw[mt][i][h];
+            const float* gv = (const float*)&graw[i][h];
+            w[2 * h] = (uint32_t)f32_to_bf16_bits(xv[0] * inv * gv[0]) |
+                       ((uint32_t)f32_to_bf16_bits(xv[1] * inv * gv[1]) << 16);
+            w[2 * h + 1] = (uint32_t)f32_to_bf16_bits(xv[2] * inv * gv[2]) |
+                           ((uint32_t)f32_to_bf16_bits(xv[3] * inv * gv[3]) << 16);
+          }
+          af = __builtin_bit_cast(bf16x8, w);
+        } else {
+          af = __builtin_bit_cast(bf16x8, araw[mt][i][0]);
+        }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
           acc[nb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[nb], acc[nb][mt], 0, 0, 0);
@@ -340,7 +418,9 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
   }
   __syncthreads();
 
-  // sum the wave partials in wave order, then the epilogue; thread t -> (mt, r, source lane)
+  // sum the wave partials in wave order, then the epilogue; thread t -> (mt, r, source lane);
+  // a wave covers one (mt, r) for all 64 source lanes, so the 16 columns of a row are 16
+  // consecutive lanes
   for (int t = threadIdx.x; t < MT * 4 * 64; t += 512) {
     const int mt = t / 256, r = (t / 64) % 4, sl = t % 64;
     float v[NB];
@@ -352,20 +432,148 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
     }
     const int m = m0 + mt * 16 + (sl >> 4) * 4 + r;
     const int ncol = n0 + (sl & 15);
-    if (m >= M || ncol >= a.N) continue;
+    const bool in = m < M && ncol < a.N;
     const int64_t o = (int64_t)m * a.ldc + ncol;
     if constexpr (EPI == EPI_STORE) {
-      ((float*)a.C)[o] = v[0];
+      if (in) ((float*)a.C)[o] = v[0];
     } else if constexpr (EPI == EPI_RESID) {
-      ((float*)a.C)[o] += v[0];
+      float xn = 0.f;
+      if (in) {
+        xn = xres + v[0];  // (each thread runs this loop body at most once: MT * 256 <= 512)
+        ((float*)a.C)[o] = xn;
+      }
+      if (a.ssq_out) {
+        const float sq = group_sum<16>(xn * xn);
+        if (m < M && (sl & 15) == 0) a.ssq_out[(int64_t)m * (a.N / 16) + blockIdx.x] = sq;
+      }
     } else {
-      const float y = v[0] / (1.0f + __expf(-v[0])) * v[NB - 1];
-      if (a.c_bf16)
-        ((uint16_t*)a.C)[o] = f32_to_bf16_bits(y);
-      else
-        ((float*)a.C)[o] = y;
+      if (in) {
+        const float y = v[0] / (1.0f + __expf(-v[0])) * v[NB - 1];
+        if (a.c_bf16)
+          ((uint16_t*)a.C)[o] = f32_to_bf16_bits(y);
+        else
+          ((float*)a.C)[o] = y;
+      }
     }
   }
+}
+
+// ---- decode LM head ---------------------------------------------------------------------------
+// logits = RMSNorm(x) . E^T for the decode rows (M <= 64). One block of 16 waves covers 256
+// vocabulary columns: it normalises the M residual rows once (final gain; sum of squares over
+// the full row, added per thread in order and then by a fixed butterfly) into bf16 rows in
+// LDS, then each wave streams its 16 rows of E over the whole K in ascending order -- the same
+// per-element MFMA sequence as the tile GEMM -- with the next 8 k-steps of weight fragments
+// loaded while the current ones are consumed. E is read once per step; the normalised rows
+// cost one LDS fill per 256 columns.
+
+template <int WF, int MT>
+__global__ __launch_bounds__(1024) void lmhead_decode(GemmArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t s_h[];  // [MT*16][K + 8]
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int M = a.M, K = a.K, KS = K + 8;
+  const int rows = MT * 16;
+  // normalise: 32 threads per row (a wave half), each 1/32 of the row
+  {
+    const int per = K / 32;
+    for (int r0 = 0; r0 < rows; r0 += 32) {
+      const int r = r0 + (threadIdx.x >> 5);
+      const int c0 = (threadIdx.x & 31) * per;
+      const bool live = r < rows;
+      const float* xr = (const float*)a.A + (int64_t)min(r, M - 1) * a.lda + c0;
+      float ss = 0.f;
+      if (live)
+        for (int j = 0; j < per; j += 4) {
+          const float4 v = *(const float4*)(xr + j);
+          ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+        }
+      ss = group_sum<32>(ss);
+      const float inv = 1.0f / sqrtf(ss / (float)K + a.eps);
+      if (live)
+        for (int j = 0; j < per; j += 4) {
+          const float4 v = *(const float4*)(xr + j);
+          const float4 g = *(const float4*)(a.gain + c0 + j);
+          uint32_t* d = (uint32_t*)(s_h + r * KS + c0 + j);
+          d[0] = (uint32_t)f32_to_bf16_bits(v.x * inv * g.x) | ((uint32_t)f32_to_bf16_bits(v.y * inv * g.y) << 16);
+          d[1] = (uint32_t)f32_to_bf16_bits(v.z * inv * g.z) | ((uint32_t)f32_to_bf16_bits(v.w * inv * g.w) << 16);
+        }
+    }
+  }
+  __syncthreads();
+  const int n0 = blockIdx.x * 256 + wave * 16;
+  if (n0 >= a.N) return;
+  const WMat E = a.seg[0];
+  const int brow = min(n0 + (lane & 15), E.rows - 1);
+  const int kl = (lane >> 4) * 8;
+  const int ksteps = K / 32;
+  f32x4 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  constexpr int G = 8;  // k-steps per batch of weight loads
+  BRaw<WF> cur[G], nxt[G];
+#pragma unroll
+  for (int i = 0; i < G; ++i) cur[i] = load_b_raw<WF>(E, brow, K, min(i, ksteps - 1) * 32 + kl);
+  for (int kb = 0; kb < ksteps; kb += G) {
+    if (kb + G < ksteps) {
+#pragma unroll
+      for (int i = 0; i < G; ++i) nxt[i] = load_b_raw<WF>(E, brow, K, min(kb + G + i, ksteps - 1) * 32 + kl);
+    }
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      if (kb + i < ksteps) {
+        const bf16x8 bf = b_frag<WF>(cur[i]);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const bf16x8 af = __builtin_bit_cast(bf16x8, *(const u32x4*)(s_h + (mt * 16 + (lane & 15)) * KS +
+                                                                       (kb + i) * 32 + kl));
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc[mt], 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < G; ++i) cur[i] = nxt[i];
+  }
+  const int ncol = n0 + (lane & 15);
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = mt * 16 + (lane >> 4) * 4 + r;
+      if (m < M && ncol < a.N) ((float*)a.C)[(int64_t)m * a.ldc + ncol] = acc[mt][r];
+    }
+}
+
+template <int WF, int MT>
+static hipError_t lmhead_go(const GemmArgs& a, hipStream_t s) {
+  const size_t lds = (size_t)MT * 16 * (a.K + 8) * 2;
+  static bool attr = false;  // raise the dynamic LDS limit once per instantiation
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void*)lmhead_decode<WF, MT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lds);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  lmhead_decode<WF, MT><<<(a.N + 255) / 256, 1024, lds, s>>>(a);
+  return hipGetLastError();
+}
+
+bool lmhead_decode_supported(int wdtype, int M, int K) {
+  // each of 32 threads per row normalises K/32 columns in float4 steps
+  return (wdtype == DEC_BF16 || wdtype == DEC_UINT4_G32) && M <= 64 && K % 128 == 0 && (size_t)64 * (K + 8) * 2 <= 160 * 1024;
+}
+
+hipError_t launch_lmhead_decode(int wdtype, const GemmArgs& a, hipStream_t s) {
+  if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  const int mt = a.M <= 16 ? 1 : (a.M <= 32 ? 2 : 4);
+  if (wdtype == DEC_BF16) {
+    if (mt == 1) return lmhead_go<DEC_BF16, 1>(a, s);
+    if (mt == 2) return lmhead_go<DEC_BF16, 2>(a, s);
+    return lmhead_go<DEC_BF16, 4>(a, s);
+  }
+  if (mt == 1) return lmhead_go<DEC_UINT4_G32, 1>(a, s);
+  if (mt == 2) return lmhead_go<DEC_UINT4_G32, 2>(a, s);
+  return lmhead_go<DEC_UINT4_G32, 4>(a, s);
 }
 
 template <int WF, int MT, int NKS>

@@ -10,15 +10,34 @@ namespace dec {
 // x = E[id] for each new token) -----------------------------------------------------------
 
 template <int WF>
+__device__ __forceinline__ void embed_row(const WMat& E, int t, int d, float* __restrict__ xr);
+
+template <int WF>
 __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ tok, int vocab, int d,
-                                                    WMat E, float* __restrict__ x) {
+                                                    WMat E, float* __restrict__ x, float* __restrict__ ssq) {
   const int r = blockIdx.x;
   const int t = tok[r];
   float* xr = x + (int64_t)r * d;
   if (t < 0 || t >= vocab) {
     for (int i = threadIdx.x; i < d; i += blockDim.x) xr[i] = __builtin_nanf("");
+    if (ssq)
+      for (int i = threadIdx.x; i < d / 16; i += blockDim.x) ssq[(int64_t)r * (d / 16) + i] = __builtin_nanf("");
     return;
   }
+  embed_row<WF>(E, t, d, xr);
+  if (ssq) {
+    __syncthreads();  // the row is in global memory; each thread sums its 16-column groups
+    for (int i = threadIdx.x; i < d / 16; i += blockDim.x) {
+      float s = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) s += xr[16 * i + j] * xr[16 * i + j];
+      ssq[(int64_t)r * (d / 16) + i] = s;
+    }
+  }
+}
+
+template <int WF>
+__device__ __forceinline__ void embed_row(const WMat& E, int t, int d, float* __restrict__ xr) {
   if constexpr (WF == DEC_F32) {
     const float* er = (const float*)E.w + (int64_t)t * d;
     for (int i = threadIdx.x; i < d; i += blockDim.x) xr[i] = er[i];
@@ -38,15 +57,15 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
 }
 
 hipError_t launch_embed(const int32_t* tok, int n_rows, int vocab, int d, int wdtype, const WMat& E,
-                        float* x, hipStream_t s) {
+                        float* x, float* ssq, hipStream_t s) {
   if (n_rows <= 0) return hipSuccess;
   dim3 g(n_rows), b(256);
   if (wdtype == DEC_F32)
-    embed_kernel<DEC_F32><<<g, b, 0, s>>>(tok, vocab, d, E, x);
+    embed_kernel<DEC_F32><<<g, b, 0, s>>>(tok, vocab, d, E, x, ssq);
   else if (wdtype == DEC_BF16)
-    embed_kernel<DEC_BF16><<<g, b, 0, s>>>(tok, vocab, d, E, x);
+    embed_kernel<DEC_BF16><<<g, b, 0, s>>>(tok, vocab, d, E, x, ssq);
   else
-    embed_kernel<DEC_UINT4_G32><<<g, b, 0, s>>>(tok, vocab, d, E, x);
+    embed_kernel<DEC_UINT4_G32><<<g, b, 0, s>>>(tok, vocab, d, E, x, ssq);
   return hipGetLastError();
 }
 
@@ -167,18 +186,8 @@ __global__ __launch_bounds__(256) void qk_rope_kv_kernel(QkRopeArgs a) {
   float x2 = active ? src[lane + half] : 0.f;
   const bool is_v = hh >= H + Hkv;
   if (!is_v) {
-    const float* g = hh < H ? a.q_norm : a.k_norm;
-    float ss = wave_sum<64>(x1 * x1 + x2 * x2);
-    const float inv = 1.0f / sqrtf(ss / (float)D + a.eps);
-    if (active) {
-      x1 = x1 * inv * g[lane];
-      x2 = x2 * inv * g[lane + half];
-      const float2 cs = a.rope[(int64_t)pos * half + lane];
-      const float y1 = x1 * cs.x - x2 * cs.y;
-      const float y2 = x2 * cs.x + x1 * cs.y;
-      x1 = y1;
-      x2 = y2;
-    }
+    const float2 cs = active ? a.rope[(int64_t)pos * half + lane] : make_float2(1.f, 0.f);
+    norm_rope_pair(x1, x2, hh < H ? a.q_norm : a.k_norm, cs, lane, D, a.eps);
   }
   if (!active) return;
   if (hh < H) {

@@ -7,8 +7,9 @@
 namespace dec {
 
 // x[r][:] = widened/dequantised E[tok[r]][:] as float32; an id outside [0, vocab) gives NaN.
+// ssq (optional, [n_rows][d/16]): sums of squares of each 16 columns of the row.
 hipError_t launch_embed(const int32_t* tok, int n_rows, int vocab, int d, int wdtype, const WMat& E,
-                        float* x, hipStream_t s);
+                        float* x, float* ssq, hipStream_t s);
 
 // out[r][:] = x[rows ? rows[r] : r][:] / sqrt(mean(x^2) + eps) * g, stored as float32 or bf16.
 hipError_t launch_rmsnorm(const float* x, const int32_t* rows, int n, int d, const float* g, float eps,
@@ -45,9 +46,10 @@ struct AttnRowsArgs {
 int attn_rows_chunk(int head_dim, bool kv_f16, int group);
 hipError_t launch_attn_rows(const AttnRowsArgs& a, hipStream_t s);
 
-// Decode attention: one workgroup per (row, KV head), chunk states merged in the workgroup;
-// writes o[r][h*D + d] (float32 or bf16) directly. Uses a.n_chunks / a.partial not at all.
-hipError_t launch_attn_decode(const AttnRowsArgs& a, void* o, bool out_bf16, hipStream_t s);
+// Decode attention: one workgroup per (row, KV head). It first applies the q/k norm and RoPE
+// of the row (qk.qkv) and writes the row's key and value to the pool, then attends; chunk
+// states merge inside the workgroup; writes o[r][h*D + d] (float32 or bf16) directly.
+hipError_t launch_attn_decode(const QkRopeArgs& qk, const AttnRowsArgs& a, void* o, bool out_bf16, hipStream_t s);
 
 // o[r][h*D + d] = combined attention output (float32 or bf16).
 hipError_t launch_attn_combine(const float* partial, int n_rows, int n_heads, int head_dim, int n_chunks,
@@ -77,6 +79,13 @@ struct GemmArgs {
   void* C;  // float32 [M][ldc] (STORE, RESID) or act dtype (SWIGLU)
   int ldc;
   bool c_bf16;  // SWIGLU output in bf16
+  // Decode GEMM only. STORE / SWIGLU: A is RMSNorm(x) computed on the fly from the float32
+  // residual x [M][K] (lda), the gain, and ssq_in, per-row sums of squares in K/16 partials
+  // of 16 columns [M][K/16]. RESID: ssq_out receives those partials of the new x [M][N/16].
+  const float* gain;
+  const float* ssq_in;
+  float* ssq_out;
+  float eps;
 };
 hipError_t launch_gemm(int wdtype, int epi, const GemmArgs& a, hipStream_t s);
 
@@ -84,6 +93,11 @@ hipError_t launch_gemm(int wdtype, int epi, const GemmArgs& a, hipStream_t s);
 // summed in wave order; bf16 and uint4 weights, K/32 with a supported per-wave step count.
 bool gemm_decode_supported(int wdtype, int K);
 hipError_t launch_gemm_decode(int wdtype, int epi, const GemmArgs& a, hipStream_t s);
+
+// Decode LM head: logits[M][N] = RMSNorm(x)[M][K] . E^T with the norm computed from the float32
+// residual (a.A, a.lda) and a.gain inside each block; bf16 / uint4 E, M <= 64.
+bool lmhead_decode_supported(int wdtype, int M, int K);
+hipError_t launch_lmhead_decode(int wdtype, const GemmArgs& a, hipStream_t s);
 
 // next[r] = argmax_v logits[r][v], ties to the lowest id; scratch holds argmax_scratch_bytes.
 size_t argmax_scratch_bytes(int max_rows);
