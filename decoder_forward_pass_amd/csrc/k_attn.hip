@@ -276,7 +276,7 @@ struct DecodeGeom {
   static constexpr int EPL = 16 / (int)sizeof(KVT);
   static constexpr int LPK = D / EPL;
   static constexpr int KPI = 64 / LPK;
-  static constexpr int DKPG = (16 / GROUP) > 1 ? 16 / GROUP : 1;  // loads per chunk
+  static constexpr int DKPG = (8 / GROUP) > 1 ? 8 / GROUP : 1;  // loads per chunk
   static constexpr int CHUNK = DKPG * KPI;
   static constexpr int NWV = 16;
 };
@@ -312,6 +312,43 @@ __global__ __launch_bounds__(1024) void attn_decode_kernel(QkRopeArgs qk, AttnRo
                      (int64_t)kvh * a.pool.block_tokens * D + sub * EPL;
   const KVT* vbase = kbase + a.pool.n_blocks * slab;
 
+  // block ids of this wave's chunks (see the chunk loop below), requested before the prologue
+  const int bpc = CHUNK > a.pool.block_tokens ? CHUNK >> bsh : 1;  // blocks per chunk
+  const int cpl = 64 / bpc;                                         // chunks per table load
+  auto load_tab = [&](int base) {
+    const int c = wave + (base + lane / bpc) * NWV;
+    return table[min(((min(c, nch - 1) * CHUNK) >> bsh) + lane % bpc, last_blk)];
+  };
+  int tab_base = 0;
+  int tab = load_tab(0);
+
+  // Software pipeline: the K and V loads of a wave's next chunk are issued before the current
+  // chunk is consumed, so two chunks are in flight per wave. Block ids come from tab (loaded
+  // before the q/k prologue): lane j holds block j % bpc of the wave's chunk number
+  // tab_base + j / bpc; it is reloaded every 64 / bpc chunks.
+  auto issue = [&](int ci, u32x4 (&kr)[KPG], u32x4 (&vr)[KPG]) {
+    const int key0 = (wave + ci * NWV) * CHUNK;
+    if (ci >= tab_base + cpl) {  // wave-uniform, rare
+      tab_base += cpl;
+      tab = load_tab(tab_base);
+    }
+#pragma unroll
+    for (int kk = 0; kk < KPG; ++kk) {
+      // the KPI keys of one load share a block (B is a multiple of KPI); keys past the context
+      // read a slot of the last block and are masked below
+      const int b = min((key0 + kk * KPI) >> bsh, last_blk);
+      const int64_t off = (int64_t)__builtin_amdgcn_readlane(tab, (ci - tab_base) * bpc + b - (key0 >> bsh)) * slab +
+                          ((key0 + kk * KPI + grp) & bmask) * D;
+      kr[kk] = *(const u32x4*)(kbase + off);
+      vr[kk] = *(const u32x4*)(vbase + off);
+    }
+  };
+  const int nmine = wave < nch ? (nch - 1 - wave) / NWV + 1 : 0;  // chunks of this wave
+  u32x4 kraw[KPG], vraw[KPG], knext[KPG], vnext[KPG];
+  // A wave's first chunk is requested before the q/k prologue, except the chunk that holds the
+  // new position, which is read after the barrier that publishes the new key and value.
+  const bool early = nmine > 0 && wave != nch - 1;
+  if (early) issue(0, kraw, vraw);
   constexpr bool F16 = sizeof(KVT) == 2;
   // The row's new query heads, key and value: wave i < GROUP normalises and rotates query head
   // kvh*GROUP + i into LDS (in the pool's format, as the q buffer holds it for prefill); wave
@@ -344,6 +381,7 @@ __global__ __launch_bounds__(1024) void attn_decode_kernel(QkRopeArgs qk, AttnRo
     }
   }
   __syncthreads();
+  if (nmine > 0 && !early) issue(0, kraw, vraw);
 
   // q . k: f16 pairs through v_dot2_f32_f16 (products exact in the float32 sum), float32
   // pools through FMAs; the score is scaled by log2(e)/sqrt(D) afterwards
@@ -360,23 +398,10 @@ __global__ __launch_bounds__(1024) void attn_decode_kernel(QkRopeArgs qk, AttnRo
     for (int e = 0; e < EPL; ++e) acc[i][e] = 0.f;
   }
 
-  int blk_lane = wave < nch ? table[min(((wave * CHUNK) >> bsh) + lane, last_blk)] : 0;
-  for (int c = wave; c < nch; c += NWV) {
-    const int key0 = c * CHUNK;
-    const int b0 = key0 >> bsh;
-    u32x4 kraw[KPG], vraw[KPG];
-#pragma unroll
-    for (int kk = 0; kk < KPG; ++kk) {
-      // the KPI keys of one load share a block (B is a multiple of KPI)
-      const int kb = min((key0 + kk * KPI) >> bsh, last_blk) - b0;
-      const int64_t off = (int64_t)__builtin_amdgcn_readlane(blk_lane, kb) * slab +
-                          ((key0 + kk * KPI + grp) & bmask) * D;
-      kraw[kk] = *(const u32x4*)(kbase + off);
-      vraw[kk] = *(const u32x4*)(vbase + off);
-    }
-    const int cn = c + NWV;
-    if (cn < nch) blk_lane = table[min(((cn * CHUNK) >> bsh) + lane, last_blk)];
-    // keep the chunk's loads issued together, ahead of the arithmetic that consumes them
+  for (int ci = 0; ci < nmine; ++ci) {
+    const int key0 = (wave + ci * NWV) * CHUNK;
+    if (ci + 1 < nmine) issue(ci + 1, knext, vnext);
+    // keep the loads issued together, ahead of the arithmetic that consumes the current chunk
     __builtin_amdgcn_sched_barrier(0);
     float sc[KPG][GROUP];
 #pragma unroll
@@ -424,6 +449,11 @@ __global__ __launch_bounds__(1024) void attn_decode_kernel(QkRopeArgs qk, AttnRo
 #pragma unroll
         for (int e = 0; e < EPL; ++e) acc[i][e] += p * vv[e];
       }
+    }
+#pragma unroll
+    for (int kk = 0; kk < KPG; ++kk) {
+      kraw[kk] = knext[kk];
+      vraw[kk] = vnext[kk];
     }
   }
   // this wave's state: sum the lane groups (each holds distinct keys)
