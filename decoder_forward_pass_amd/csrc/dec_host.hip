@@ -412,8 +412,17 @@ int run_forward(dec_ctx* ctx, hipStream_t st, const BatchDev& b, const int32_t* 
   // launch. Prefill calls always take the tile GEMM after an RMSNorm launch.
   const bool dgemm = decode && gemm_decode_supported(c.weight_dtype, d) &&
                      gemm_decode_supported(c.weight_dtype, qw) && gemm_decode_supported(c.weight_dtype, ff);
+  // Prefill calls with bf16 / uint4 weights take the 256 x 256 tile GEMM, which also applies
+  // the q/k norm, RoPE and the KV write in its Q|K|V epilogue (chosen by the configuration
+  // alone, so every prefill call of a model computes the same way).
+  // The other products take it when it fills the chip (>= 256 tiles, M >= 1024); both give
+  // identical results, so the choice never changes a row's bits.
+  const bool big = !decode && gemm_big_supported(c.weight_dtype, EPI_QKV, D);
   auto gemm = [&](int epi, const GemmArgs& g) {
-    return dgemm ? launch_gemm_decode(c.weight_dtype, epi, g, st) : launch_gemm(c.weight_dtype, epi, g, st);
+    if (dgemm) return launch_gemm_decode(c.weight_dtype, epi, g, st);
+    const int tiles = (g.M + 255) / 256 * (epi == EPI_SWIGLU ? (g.N + 127) / 128 : (g.N + 255) / 256);
+    if (big && tiles >= 256 && g.M >= 1024) return launch_gemm_big(c.weight_dtype, epi, g, nullptr, st);
+    return launch_gemm(c.weight_dtype, epi, g, st);
   };
   // A of a normalising GEMM: the residual itself (decode GEMM) or the RMSNorm output
   auto norm_input = [&](GemmArgs& g, const float* gain) {
@@ -434,13 +443,16 @@ int run_forward(dec_ctx* ctx, hipStream_t st, const BatchDev& b, const int32_t* 
     g.M = N; g.N = qkvw; g.K = d;
     g.seg[0] = L.wq; g.seg[1] = L.wk; g.seg[2] = L.wv; g.nseg = 3;
     g.C = qkv; g.ldc = qkvw;
-    TLAUNCH(DEC_K_GEMM_QKV, gemm(EPI_STORE, g));
     QkRopeArgs qa{qkv, L.q_norm, L.k_norm, rope, q, pool, l, H, Hkv, D, c.rms_eps, kv_f16, b};
+    if (big)
+      TLAUNCH(DEC_K_GEMM_QKV, launch_gemm_big(c.weight_dtype, EPI_QKV, g, &qa, st));
+    else
+      TLAUNCH(DEC_K_GEMM_QKV, gemm(EPI_STORE, g));
     if (decode) {
       AttnRowsArgs ra{q, pool, l, H, Hkv, D, kv_f16, nch, part, b};
       TLAUNCH(DEC_K_ATTN_ROWS, launch_attn_decode(qa, ra, o, act_bf16, st));
     } else {
-      TLAUNCH(DEC_K_QK_ROPE_KV, launch_qk_rope_kv(qa, st));
+      if (!big) TLAUNCH(DEC_K_QK_ROPE_KV, launch_qk_rope_kv(qa, st));
       if (w.flash) {
         AttnPrefillArgs pa{(const uint16_t*)q, pool, l, H, Hkv, D, o, act_bf16, b};
         TLAUNCH(DEC_K_ATTN_PREFILL, launch_attn_prefill(pa, st));

@@ -5,7 +5,7 @@
 // bf16 as the MFMA operand.
 //
 // Batch invariance: every output element is accumulated by one MFMA instruction type per
-// weight format (v_mfma_f32_16x16x4_f32 or v_mfma_f32_16x16x32_bf16), over K in ascending
+// weight format (v_mfma_f32_16x16x4_f32 or v_mfma_f32_32x32x16_bf16), over K in ascending
 // order into a single accumulator, with no split of K. The row's result therefore does not
 // depend on M, on the tile a row falls in, or on the other rows.
 //
@@ -47,13 +47,19 @@ __global__ __launch_bounds__(256) void gemm_tile64(GemmArgs a) {
     br0 = n0 - base;
   }
 
+  // float32 weights: 2 x 2 blocks of 16 x 16 per wave (v_mfma_f32_16x16x4_f32); bf16 / uint4:
+  // one 32 x 32 block per wave (v_mfma_f32_32x32x16_bf16, the full-rate bf16 shape)
   f32x4 acc[NB][2][2];
+  f32x16 acc32[NB];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb)
+  for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) acc[nb][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc32[nb][e] = 0.f;
+  }
 
   for (int k0 = 0; k0 < K; k0 += BK) {
     // ---- stage A
@@ -138,54 +144,54 @@ __global__ __launch_bounds__(256) void gemm_tile64(GemmArgs a) {
           }
       }
     } else {
+      // lane l: row l % 32 of its 32-row block, k = 16 ks + 8 (l / 32) .. +8
 #pragma unroll
-      for (int ks = 0; ks < BK / 32; ++ks) {
-        bf16x8 af[2];
+      for (int ks = 0; ks < BK / 16; ++ks) {
+        const bf16x8 af =
+            __builtin_bit_cast(bf16x8, *(const u32x4*)(As + (wm * 32 + (lane & 31)) * RW + ks * 8 + (lane >> 5) * 4));
 #pragma unroll
-        for (int bi = 0; bi < 2; ++bi)
-          af[bi] = __builtin_bit_cast(
-              bf16x8, *(const u32x4*)(As + (wm * 32 + bi * 16 + (lane & 15)) * RW + ks * 16 + (lane >> 4) * 4));
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int bj = 0; bj < 2; ++bj) {
-            const bf16x8 bf = __builtin_bit_cast(
-                bf16x8,
-                *(const u32x4*)(Bs[nb] + (wn * 32 + bj * 16 + (lane & 15)) * RW + ks * 16 + (lane >> 4) * 4));
-#pragma unroll
-            for (int bi = 0; bi < 2; ++bi)
-              acc[nb][bi][bj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[bi], bf, acc[nb][bi][bj], 0, 0, 0);
-          }
+        for (int nb = 0; nb < NB; ++nb) {
+          const bf16x8 bf = __builtin_bit_cast(
+              bf16x8, *(const u32x4*)(Bs[nb] + (wn * 32 + (lane & 31)) * RW + ks * 8 + (lane >> 5) * 4));
+          acc32[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc32[nb], 0, 0, 0);
+        }
       }
     }
     __syncthreads();
   }
 
-  // ---- epilogue: lane holds column (lane & 15), rows 4*(lane >> 4) + r of each 16x16 block
+  // ---- epilogue. 16 x 16 blocks: lane holds column lane % 16, rows 4 (lane / 16) + r.
+  // 32 x 32 block: lane holds column lane % 32, rows 8 (i / 4) + 4 (lane / 32) + i % 4.
+  auto put = [&](int m, int n, float v, float u) {
+    if (m >= M || n >= a.N) return;
+    const int64_t o = (int64_t)m * a.ldc + n;
+    if constexpr (EPI == EPI_STORE) {
+      ((float*)a.C)[o] = v;
+    } else if constexpr (EPI == EPI_RESID) {
+      ((float*)a.C)[o] += v;
+    } else {
+      const float y = v / (1.0f + __expf(-v)) * u;
+      if (a.c_bf16)
+        ((uint16_t*)a.C)[o] = f32_to_bf16_bits(y);
+      else
+        ((float*)a.C)[o] = y;
+    }
+  };
+  if constexpr (F32) {
 #pragma unroll
-  for (int bi = 0; bi < 2; ++bi)
+    for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
-    for (int bj = 0; bj < 2; ++bj)
+      for (int bj = 0; bj < 2; ++bj)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = m0 + wm * 32 + bi * 16 + (lane >> 4) * 4 + r;
-        const int n = n0 + wn * 32 + bj * 16 + (lane & 15);
-        if (m >= M || n >= a.N) continue;
-        const int64_t o = (int64_t)m * a.ldc + n;
-        const float v = acc[0][bi][bj][r];
-        if constexpr (EPI == EPI_STORE) {
-          ((float*)a.C)[o] = v;
-        } else if constexpr (EPI == EPI_RESID) {
-          ((float*)a.C)[o] += v;
-        } else {
-          const float u = acc[NB - 1][bi][bj][r];
-          const float y = v / (1.0f + __expf(-v)) * u;
-          if (a.c_bf16)
-            ((uint16_t*)a.C)[o] = f32_to_bf16_bits(y);
-          else
-            ((float*)a.C)[o] = y;
-        }
-      }
+        for (int r = 0; r < 4; ++r)
+          put(m0 + wm * 32 + bi * 16 + (lane >> 4) * 4 + r, n0 + wn * 32 + bj * 16 + (lane & 15), acc[0][bi][bj][r],
+              acc[NB - 1][bi][bj][r]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      put(m0 + wm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3), n0 + wn * 32 + (lane & 31), acc32[0][i],
+          acc32[NB - 1][i]);
+  }
 }
 
 template <int WF>

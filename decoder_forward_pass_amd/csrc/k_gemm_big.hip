@@ -1,0 +1,375 @@
+// Prefill projections as large MFMA tiles: C = A . W^T with W stored [out][in] ("Candle model
+// runner" 2.4). A is the bf16 activation; W is bf16, or uint4-g32 dequantised while the tile is
+// staged in LDS: w = (q - zp) * scale ("Byte-identical...", "The bar we set"), rounded to bf16.
+//
+// Tiling: a block of 8 waves computes a 256 x 256 tile of C (waves 4 x 2, 64 x 128 each) over
+// K in steps of 64, with the next step's operands loaded from memory into registers while the
+// current step's LDS copy feeds the MFMAs (two LDS stages, one barrier per step). Every output
+// element is accumulated by v_mfma_f32_32x32x16_bf16 (the full-rate bf16 shape on this chip;
+// the 16x16x32 shape issues at half the rate) over K in ascending order into a single
+// accumulator, exactly as in the 64 x 64 tile kernel, so both give identical results and a
+// row's result does not depend on M or on the other rows.
+//
+// Block order: the hardware deals consecutive block ids to the chip's 8 L2 domains in turn;
+// the id is remapped so that each domain receives a contiguous run of tiles, walked 8 M tiles
+// at a time, so concurrently running blocks share their A rows and W rows in one L2.
+//
+// Epilogues: store, residual add, SwiGLU (silu on the gate only, "Candle model runner" 2.4),
+// and the attention input ("A real model in our own decoder", switch 5, and "Which channels
+// rotate together"): per-head RMSNorm over head_dim with the layer's q_norm / k_norm gains,
+// then the rotation of channel pairs (j, j + D/2) by pos * base^(-2j/D), q stored in the KV
+// format, K and V written to the pool at block table[pos / B], slot pos % B ("Candle model
+// runner" section 3, "Where a key lands"). A wave's 128 columns hold whole heads and channels
+// j and j + D/2 of a head sit in the same lane, so this is all done in registers.
+#include "kernels.h"
+
+#include <utility>
+
+namespace dec {
+
+namespace {
+
+constexpr int kBT = 256;            // block tile rows and columns
+constexpr int kBK = 64;             // K per step
+constexpr int kLR = kBK + 8;        // LDS row stride in bf16 (padded: conflict-free fragment reads)
+constexpr int kStage = kBT * kLR;   // bf16 elements of one operand tile
+constexpr size_t kBigLds = (size_t)2 * 2 * kStage * 2;  // two stages of A and B, bytes
+
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>), expanded at compile time so
+// that accumulator indices are constants (an unroll the optimizer may decline)
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+struct BigRowsB {
+  const uint16_t* p[4];  // bf16: the thread's four B rows
+};
+
+}  // namespace
+
+template <int WF, int EPI, int D, bool KV_F16>
+__global__ __launch_bounds__(512) void gemm_big(GemmArgs a, QkRopeArgs qk) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];  // [stage][A | B][256][kLR]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int M = a.M, K = a.K;
+  const int mt_n = (M + kBT - 1) / kBT;
+  const int nt_n = EPI == EPI_SWIGLU ? (a.N + 127) / 128 : (a.N + kBT - 1) / kBT;
+
+  // ---- block id -> tile (contiguous runs per L2 domain, 8 M tiles per group)
+  const int nblk = gridDim.x;
+  int bid = blockIdx.x;
+  if (nblk % 8 == 0) bid = (bid % 8) * (nblk / 8) + bid / 8;
+  const int gsz = 8 * nt_n;
+  const int grp = bid / gsz, gm0 = grp * 8, gmn = min(8, mt_n - gm0);
+  const int tm = gm0 + (bid % gsz) % gmn, tn = (bid % gsz) / gmn;
+  const int m0 = tm * kBT;
+  const int n0 = EPI == EPI_SWIGLU ? tn * 128 : tn * kBT;
+
+  // ---- per-thread staging sources: A and B chunks of 16 B (8 bf16), rows tid/8 + 64 i
+  const int srow = tid >> 3, sc8 = tid & 7;
+  const uint16_t* ap[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    ap[i] = (const uint16_t*)a.A + (int64_t)min(m0 + srow + 64 * i, M - 1) * a.lda + sc8 * 8;
+  // B row of LDS row r: SwiGLU rows 0..127 gate, 128..255 up (features n0 + r % 128); otherwise
+  // row n0 + r of the Q|K|V (or single) concatenation
+  // (segments are selected with constant indices, so the arguments stay in registers)
+  auto b_src = [&](int r, int& rr) -> WMat {
+    if constexpr (EPI == EPI_SWIGLU) {
+      const WMat m = r < 128 ? a.seg[0] : a.seg[1];
+      rr = min(n0 + (r & 127), m.rows - 1);
+      return m;
+    } else {
+      int n = min(n0 + r, a.N - 1);
+      if (a.nseg > 1 && n >= a.seg[0].rows) {
+        n -= a.seg[0].rows;
+        if (a.nseg > 2 && n >= a.seg[1].rows) {
+          rr = n - a.seg[1].rows;
+          return a.seg[2];
+        }
+        rr = n;
+        return a.seg[1];
+      }
+      rr = n;
+      return a.seg[0];
+    }
+  };
+  BigRowsB bp;
+  const uint8_t* qcodes = nullptr;
+  const uint16_t *qscale = nullptr, *qzp = nullptr;
+  const int urow = tid >> 1, uhalf = tid & 1;  // uint4: a thread dequantises 32 k of one row
+  if constexpr (WF == DEC_BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int rr;
+      const WMat m = b_src(srow + 64 * i, rr);
+      bp.p[i] = (const uint16_t*)m.w + (int64_t)rr * K + sc8 * 8;
+    }
+  } else {
+    int rr;
+    const WMat m = b_src(urow, rr);
+    qcodes = (const uint8_t*)m.w + (int64_t)rr * (K / 2) + uhalf * 16;
+    qscale = m.scale + (int64_t)rr * (K / 32) + uhalf;
+    qzp = m.zp + (int64_t)rr * (K / 32) + uhalf;
+  }
+
+  u32x4 ra[4], rb[4];
+  uint32_t rsz = 0;  // uint4: scale | zp << 16
+  auto load_step = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ra[i] = *(const u32x4*)(ap[i] + k0);
+    if constexpr (WF == DEC_BF16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rb[i] = *(const u32x4*)(bp.p[i] + k0);
+    } else {
+      rb[0] = *(const u32x4*)(qcodes + k0 / 2);
+      rsz = (uint32_t)qscale[k0 / 32] | ((uint32_t)qzp[k0 / 32] << 16);
+    }
+  };
+  auto store_step = [&](int st) {
+    uint16_t* As = lds + (size_t)st * 2 * kStage;
+    uint16_t* Bs = As + kStage;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *(u32x4*)(As + (srow + 64 * i) * kLR + sc8 * 8) = ra[i];
+    if constexpr (WF == DEC_BF16) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *(u32x4*)(Bs + (srow + 64 * i) * kLR + sc8 * 8) = rb[i];
+    } else {
+      const float sc = bf16_bits_to_f32(rsz & 0xffffu), zp = bf16_bits_to_f32(rsz >> 16);
+      uint16_t* d = Bs + urow * kLR + uhalf * 32;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        u32x4 w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t byte = (rb[0][q] >> (8 * j)) & 0xffu;
+          w[j] = (uint32_t)f32_to_bf16_bits(dequant_u4(byte & 15u, zp, sc)) |
+                 ((uint32_t)f32_to_bf16_bits(dequant_u4(byte >> 4, zp, sc)) << 16);
+        }
+        *(u32x4*)(d + q * 8) = w;
+      }
+    }
+  };
+
+  // LDS row of the wave's 32-column block bj (SwiGLU: blocks 0-1 gate, 2-3 up, same features)
+  auto brow_of = [&](int bj) {
+    if constexpr (EPI == EPI_SWIGLU)
+      return (bj >> 1) * 128 + wn * 64 + (bj & 1) * 32;
+    else
+      return wn * 128 + bj * 32;
+  };
+
+  // v_mfma_f32_32x32x16_bf16: operand lane l holds row l % 32, k = 8 * (l / 32) .. +8;
+  // accumulator register i of lane l is row 8 * (i / 4) + 4 * (l / 32) + i % 4, column l % 32
+  f32x16 acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  const int nk = K / kBK;
+  load_step(0);
+  store_step(0);
+  __syncthreads();
+  const int fr = lane & 31, fk = (lane >> 5) * 8;
+  for (int t = 0; t < nk; ++t) {
+    if (t + 1 < nk) load_step((t + 1) * kBK);
+    const uint16_t* As = lds + (size_t)(t & 1) * 2 * kStage;
+    const uint16_t* Bs = As + kStage;
+#pragma unroll
+    for (int ks = 0; ks < kBK / 16; ++ks) {
+      bf16x8 af[2], bf[4];
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi)
+        af[bi] = __builtin_bit_cast(bf16x8, *(const u32x4*)(As + (wm * 64 + bi * 32 + fr) * kLR + ks * 16 + fk));
+#pragma unroll
+      for (int bj = 0; bj < 4; ++bj)
+        bf[bj] = __builtin_bit_cast(bf16x8, *(const u32x4*)(Bs + (brow_of(bj) + fr) * kLR + ks * 16 + fk));
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj)
+          acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[bi], bf[bj], acc[bi][bj], 0, 0, 0);
+    }
+    if (t + 1 < nk) store_step((t + 1) & 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds column fr of each 32 x 32 block, rows 8 g + 4 (lane / 32) + r
+  const int rbase = m0 + wm * 64 + (lane >> 5) * 4;
+  auto row_of = [&](int bi, int i) { return rbase + bi * 32 + 8 * (i >> 2) + (i & 3); };
+  if constexpr (EPI == EPI_STORE || EPI == EPI_RESID) {
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int m = row_of(bi, i);
+        if (m >= M) continue;
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj) {
+          const int n = n0 + wn * 128 + bj * 32 + fr;
+          if (n >= a.N) continue;
+          float* c = (float*)a.C + (int64_t)m * a.ldc + n;
+          if constexpr (EPI == EPI_STORE)
+            *c = acc[bi][bj][i];
+          else
+            *c += acc[bi][bj][i];
+        }
+      }
+  } else if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int m = row_of(bi, i);
+        if (m >= M) continue;
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj) {
+          const int f = n0 + wn * 64 + bj * 32 + fr;
+          if (f >= a.N) continue;
+          const float g = acc[bi][bj][i], u = acc[bi][bj + 2][i];
+          const float y = g / (1.0f + __expf(-g)) * u;
+          if (a.c_bf16)
+            ((uint16_t*)a.C)[(int64_t)m * a.ldc + f] = f32_to_bf16_bits(y);
+          else
+            ((float*)a.C)[(int64_t)m * a.ldc + f] = y;
+        }
+      }
+  } else {
+    // Q|K|V: heads of D channels; a head spans BPH 32-column blocks, HPW heads per wave
+    constexpr int BPH = D >= 32 ? D / 32 : 1, HPW = 128 / D, HALF = D / 2;
+    const int H = qk.n_heads, Hkv = qk.n_kv_heads;
+    const int hw0 = (n0 + wn * 128) / D;  // global head index of the wave's first head
+    static_for<2>([&](auto bi_c) {
+      constexpr int bi = decltype(bi_c)::value;
+      static_for<16>([&](auto i_c) {
+        constexpr int i = decltype(i_c)::value;
+        const int m = row_of(bi, i);
+        const int mc = min(m, M - 1);
+        const int pos = qk.b.row_pos[mc];
+        const int seq = qk.b.row_seq[mc];
+        const int64_t blk = qk.b.block_tables[(int64_t)seq * qk.b.tbl_stride + (pos >> qk.pool.block_shift)];
+        const int slot = pos & (qk.pool.block_tokens - 1);
+        static_for<HPW>([&](auto hw_c) {
+          constexpr int hw = decltype(hw_c)::value;
+          const int hh = hw0 + hw;  // wave-uniform
+          if (hh >= H + 2 * Hkv) return;
+          // channel of this lane in block b of the head: (b * 32 + fr) for D >= 64; fr for D = 32
+          float v[BPH];
+#pragma unroll
+          for (int b = 0; b < BPH; ++b) v[b] = acc[bi][(hw * D) / 32 + b][i];
+          if (hh < H + Hkv) {
+            // RMSNorm over the head's D channels: BPH blocks in the lane, then 32 lanes
+            float ss = 0.f;
+#pragma unroll
+            for (int b = 0; b < BPH; ++b) ss += v[b] * v[b];
+            ss = group_sum<32>(ss);
+            const float inv = 1.0f / sqrtf(ss / (float)D + qk.eps);
+            const float* gain = hh < H ? qk.q_norm : qk.k_norm;
+            if constexpr (D >= 64) {
+#pragma unroll
+              for (int b = 0; b < BPH / 2; ++b) {
+                const int j = b * 32 + fr;
+                const float2 cs = qk.rope[(int64_t)pos * HALF + j];
+                const float x1 = v[b] * inv * gain[j];
+                const float x2 = v[b + BPH / 2] * inv * gain[j + HALF];
+                v[b] = x1 * cs.x - x2 * cs.y;
+                v[b + BPH / 2] = x2 * cs.x + x1 * cs.y;
+              }
+            } else {
+              // D = 32: the head is one block; channel fr pairs with channel fr ^ 16, held by
+              // the lane 16 away
+              const int j = fr & 15;
+              const float2 cs = qk.rope[(int64_t)pos * HALF + j];
+              const float xs = v[0] * inv * gain[fr];
+              const float xo = __shfl_xor(xs, 16, 64);
+              v[0] = fr < 16 ? xs * cs.x - xo * cs.y : xs * cs.x + xo * cs.y;
+            }
+          }
+          if (m >= M) return;
+          if (hh < H) {
+            const int64_t o = ((int64_t)m * H + hh) * D + fr;
+#pragma unroll
+            for (int b = 0; b < BPH; ++b) {
+              if constexpr (KV_F16)
+                ((uint16_t*)qk.q_out)[o + b * 32] = f32_to_f16_bits(v[b]);
+              else
+                ((float*)qk.q_out)[o + b * 32] = v[b];
+            }
+          } else {
+            const int kv = hh < H + Hkv ? 0 : 1;
+            const int kvh = hh - H - kv * Hkv;
+            const int64_t o = qk.pool.offset(qk.layer, kv, blk, kvh, slot) + fr;
+#pragma unroll
+            for (int b = 0; b < BPH; ++b) {
+              if constexpr (KV_F16)
+                ((uint16_t*)qk.pool.base)[o + b * 32] = f32_to_f16_bits(v[b]);
+              else
+                ((float*)qk.pool.base)[o + b * 32] = v[b];
+            }
+          }
+        });
+      });
+    });
+  }
+}
+
+template <int WF, int EPI, int D, bool KV_F16>
+static hipError_t big_go(const GemmArgs& a, const QkRopeArgs& qk, hipStream_t s) {
+  static bool attr = false;  // raise the dynamic LDS limit once per instantiation
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_big<WF, EPI, D, KV_F16>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBigLds);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  const int mt = (a.M + kBT - 1) / kBT;
+  const int nt = EPI == EPI_SWIGLU ? (a.N + 127) / 128 : (a.N + kBT - 1) / kBT;
+  gemm_big<WF, EPI, D, KV_F16><<<mt * nt, 512, kBigLds, s>>>(a, qk);
+  return hipGetLastError();
+}
+
+template <int WF>
+static hipError_t big_epi(int epi, const GemmArgs& a, const QkRopeArgs* qk, hipStream_t s) {
+  const QkRopeArgs none{};
+  switch (epi) {
+    case EPI_STORE: return big_go<WF, EPI_STORE, 128, false>(a, none, s);
+    case EPI_RESID: return big_go<WF, EPI_RESID, 128, false>(a, none, s);
+    case EPI_SWIGLU: return big_go<WF, EPI_SWIGLU, 128, false>(a, none, s);
+    case EPI_QKV:
+      if (!qk) return hipErrorInvalidValue;
+      switch (qk->head_dim) {
+        case 32: return qk->kv_f16 ? big_go<WF, EPI_QKV, 32, true>(a, *qk, s) : big_go<WF, EPI_QKV, 32, false>(a, *qk, s);
+        case 64: return qk->kv_f16 ? big_go<WF, EPI_QKV, 64, true>(a, *qk, s) : big_go<WF, EPI_QKV, 64, false>(a, *qk, s);
+        case 128:
+          return qk->kv_f16 ? big_go<WF, EPI_QKV, 128, true>(a, *qk, s) : big_go<WF, EPI_QKV, 128, false>(a, *qk, s);
+      }
+      return hipErrorInvalidValue;
+  }
+  return hipErrorInvalidValue;
+}
+
+bool gemm_big_supported(int wdtype, int epi, int head_dim) {
+  if (wdtype != DEC_BF16 && wdtype != DEC_UINT4_G32) return false;
+  if (epi == EPI_QKV) return head_dim == 32 || head_dim == 64 || head_dim == 128;
+  return epi == EPI_STORE || epi == EPI_RESID || epi == EPI_SWIGLU;
+}
+
+hipError_t launch_gemm_big(int wdtype, int epi, const GemmArgs& a, const QkRopeArgs* qk, hipStream_t s) {
+  if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  if (a.K % kBK) return hipErrorInvalidValue;
+  if (wdtype == DEC_BF16) return big_epi<DEC_BF16>(epi, a, qk, s);
+  if (wdtype == DEC_UINT4_G32) return big_epi<DEC_UINT4_G32>(epi, a, qk, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dec

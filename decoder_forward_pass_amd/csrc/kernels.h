@@ -89,6 +89,15 @@ struct GemmArgs {
 };
 hipError_t launch_gemm(int wdtype, int epi, const GemmArgs& a, hipStream_t s);
 
+// Prefill GEMM for bf16 / uint4 weights: 256 x 256 block tiles, double-buffered LDS, the same
+// per-element MFMA sequence as launch_gemm (identical results). Epilogues EPI_STORE,
+// EPI_RESID, EPI_SWIGLU, and EPI_QKV: the Q|K|V product goes through the per-head q/k
+// RMSNorm and RoPE in registers and is stored as q (qk->q_out) and paged K/V (qk->pool), as
+// launch_qk_rope_kv does from a stored product.
+enum { EPI_QKV = 3 };
+bool gemm_big_supported(int wdtype, int epi, int head_dim);
+hipError_t launch_gemm_big(int wdtype, int epi, const GemmArgs& a, const QkRopeArgs* qk, hipStream_t s);
+
 // The same product for decode steps: K split over up to 8 waves of a block (fixed by K),
 // summed in wave order; bf16 and uint4 weights, K/32 with a supported per-wave step count.
 bool gemm_decode_supported(int wdtype, int K);
