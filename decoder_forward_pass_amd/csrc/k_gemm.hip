@@ -162,35 +162,52 @@ __global__ __launch_bounds__(256) void gemm_tile64(GemmArgs a) {
 
   // ---- epilogue. 16 x 16 blocks: lane holds column lane % 16, rows 4 (lane / 16) + r.
   // 32 x 32 block: lane holds column lane % 32, rows 8 (i / 4) + 4 (lane / 32) + i % 4.
-  auto put = [&](int m, int n, float v, float u) {
-    if (m >= M || n >= a.N) return;
-    const int64_t o = (int64_t)m * a.ldc + n;
-    if constexpr (EPI == EPI_STORE) {
-      ((float*)a.C)[o] = v;
-    } else if constexpr (EPI == EPI_RESID) {
-      ((float*)a.C)[o] += v;
-    } else {
-      const float y = v / (1.0f + __expf(-v)) * u;
-      if (a.c_bf16)
-        ((uint16_t*)a.C)[o] = f32_to_bf16_bits(y);
-      else
-        ((float*)a.C)[o] = y;
-    }
-  };
+  // the 16 outputs of a lane: (row, column, value, SwiGLU up value); the residual values are
+  // all requested before any is updated
+  int om[16], on[16];
+  float ov[16], ou[16];
   if constexpr (F32) {
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
       for (int bj = 0; bj < 2; ++bj)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          put(m0 + wm * 32 + bi * 16 + (lane >> 4) * 4 + r, n0 + wn * 32 + bj * 16 + (lane & 15), acc[0][bi][bj][r],
-              acc[NB - 1][bi][bj][r]);
+        for (int r = 0; r < 4; ++r) {
+          const int e = (bi * 2 + bj) * 4 + r;
+          om[e] = m0 + wm * 32 + bi * 16 + (lane >> 4) * 4 + r;
+          on[e] = n0 + wn * 32 + bj * 16 + (lane & 15);
+          ov[e] = acc[0][bi][bj][r];
+          ou[e] = acc[NB - 1][bi][bj][r];
+        }
   } else {
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-      put(m0 + wm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3), n0 + wn * 32 + (lane & 31), acc32[0][i],
-          acc32[NB - 1][i]);
+    for (int i = 0; i < 16; ++i) {
+      om[i] = m0 + wm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+      on[i] = n0 + wn * 32 + (lane & 31);
+      ov[i] = acc32[0][i];
+      ou[i] = acc32[NB - 1][i];
+    }
+  }
+  float xo[16];
+  if constexpr (EPI == EPI_RESID) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) xo[e] = ((const float*)a.C)[(int64_t)min(om[e], M - 1) * a.ldc + min(on[e], a.N - 1)];
+  }
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    if (om[e] >= M || on[e] >= a.N) continue;
+    const int64_t o = (int64_t)om[e] * a.ldc + on[e];
+    if constexpr (EPI == EPI_STORE) {
+      ((float*)a.C)[o] = ov[e];
+    } else if constexpr (EPI == EPI_RESID) {
+      ((float*)a.C)[o] = xo[e] + ov[e];
+    } else {
+      const float y = ov[e] / (1.0f + __expf(-ov[e])) * ou[e];
+      if (a.c_bf16)
+        ((uint16_t*)a.C)[o] = f32_to_bf16_bits(y);
+      else
+        ((float*)a.C)[o] = y;
+    }
   }
 }
 

@@ -72,6 +72,19 @@ __global__ __launch_bounds__(512) void gemm_big(GemmArgs a, QkRopeArgs qk) {
   const int m0 = tm * kBT;
   const int n0 = EPI == EPI_SWIGLU ? tn * 128 : tn * kBT;
 
+  // Q|K|V: position and pool block of each of the tile's rows, fetched once up front (the
+  // barriers of the main loop publish them)
+  __shared__ int s_pos[EPI == EPI_QKV ? kBT : 1];
+  __shared__ int64_t s_blk[EPI == EPI_QKV ? kBT : 1];
+  if constexpr (EPI == EPI_QKV) {
+    if (tid < kBT) {
+      const int mc = min(m0 + tid, M - 1);
+      const int pos = qk.b.row_pos[mc];
+      s_pos[tid] = pos;
+      s_blk[tid] = qk.b.block_tables[(int64_t)qk.b.row_seq[mc] * qk.b.tbl_stride + (pos >> qk.pool.block_shift)];
+    }
+  }
+
   // ---- per-thread staging sources: A and B chunks of 16 B (8 bf16), rows tid/8 + 64 i
   const int srow = tid >> 3, sc8 = tid & 7;
   const uint16_t* ap[4];
@@ -177,52 +190,77 @@ __global__ __launch_bounds__(512) void gemm_big(GemmArgs a, QkRopeArgs qk) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   const int nk = K / kBK;
+  constexpr int NKS = kBK / 16;  // MFMA k-steps per K step
+  const int fr = lane & 31, fk = (lane >> 5) * 8;
+  // fragments of k-step ks of the LDS stage st
+  auto read_frags = [&](int st, int ks, bf16x8 (&af)[2], bf16x8 (&bf)[4]) {
+    const uint16_t* As = lds + (size_t)st * 2 * kStage;
+    const uint16_t* Bs = As + kStage;
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+      af[bi] = __builtin_bit_cast(bf16x8, *(const u32x4*)(As + (wm * 64 + bi * 32 + fr) * kLR + ks * 16 + fk));
+#pragma unroll
+    for (int bj = 0; bj < 4; ++bj)
+      bf[bj] = __builtin_bit_cast(bf16x8, *(const u32x4*)(Bs + (brow_of(bj) + fr) * kLR + ks * 16 + fk));
+  };
+  auto mfma_step = [&](const bf16x8 (&af)[2], const bf16x8 (&bf)[4]) {
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < 4; ++bj)
+        acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[bi], bf[bj], acc[bi][bj], 0, 0, 0);
+  };
+
+  // Pipeline: the fragments of the next k-step are read from LDS while the current k-step's
+  // MFMAs run (two fragment sets). The next K step's operands are loaded from memory during
+  // the first k-steps, written to the other LDS stage before the last k-step, and published
+  // by the barrier, so the last k-step's MFMAs cover the first reads of the next stage.
+  bf16x8 fa[2][2], fb[2][4];
   load_step(0);
   store_step(0);
   __syncthreads();
-  const int fr = lane & 31, fk = (lane >> 5) * 8;
+  read_frags(0, 0, fa[0], fb[0]);
   for (int t = 0; t < nk; ++t) {
-    if (t + 1 < nk) load_step((t + 1) * kBK);
-    const uint16_t* As = lds + (size_t)(t & 1) * 2 * kStage;
-    const uint16_t* Bs = As + kStage;
+    const int st = t & 1;
+    const bool more = t + 1 < nk;
+    if (more) load_step((t + 1) * kBK);
 #pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      bf16x8 af[2], bf[4];
-#pragma unroll
-      for (int bi = 0; bi < 2; ++bi)
-        af[bi] = __builtin_bit_cast(bf16x8, *(const u32x4*)(As + (wm * 64 + bi * 32 + fr) * kLR + ks * 16 + fk));
-#pragma unroll
-      for (int bj = 0; bj < 4; ++bj)
-        bf[bj] = __builtin_bit_cast(bf16x8, *(const u32x4*)(Bs + (brow_of(bj) + fr) * kLR + ks * 16 + fk));
-#pragma unroll
-      for (int bi = 0; bi < 2; ++bi)
-#pragma unroll
-        for (int bj = 0; bj < 4; ++bj)
-          acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[bi], bf[bj], acc[bi][bj], 0, 0, 0);
+    for (int ks = 0; ks < NKS - 1; ++ks) {
+      read_frags(st, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+      mfma_step(fa[ks & 1], fb[ks & 1]);
     }
-    if (t + 1 < nk) store_step((t + 1) & 1);
+    if (more) store_step(st ^ 1);
     __syncthreads();
+    if (more) read_frags(st ^ 1, 0, fa[NKS & 1], fb[NKS & 1]);
+    mfma_step(fa[(NKS - 1) & 1], fb[(NKS - 1) & 1]);
   }
 
   // ---- epilogue: lane holds column fr of each 32 x 32 block, rows 8 g + 4 (lane / 32) + r
   const int rbase = m0 + wm * 64 + (lane >> 5) * 4;
   auto row_of = [&](int bi, int i) { return rbase + bi * 32 + 8 * (i >> 2) + (i & 3); };
   if constexpr (EPI == EPI_STORE || EPI == EPI_RESID) {
+    // per 32 x 32 block: the 16 residual values are all requested before any is updated
 #pragma unroll
     for (int bi = 0; bi < 2; ++bi)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int m = row_of(bi, i);
-        if (m >= M) continue;
+      for (int bj = 0; bj < 4; ++bj) {
+        const int n = n0 + wn * 128 + bj * 32 + fr;
+        const int nc = min(n, a.N - 1);
+        float xo[16];
+        if constexpr (EPI == EPI_RESID) {
 #pragma unroll
-        for (int bj = 0; bj < 4; ++bj) {
-          const int n = n0 + wn * 128 + bj * 32 + fr;
-          if (n >= a.N) continue;
-          float* c = (float*)a.C + (int64_t)m * a.ldc + n;
-          if constexpr (EPI == EPI_STORE)
-            *c = acc[bi][bj][i];
-          else
-            *c += acc[bi][bj][i];
+          for (int i = 0; i < 16; ++i) xo[i] = ((const float*)a.C)[(int64_t)min(row_of(bi, i), M - 1) * a.ldc + nc];
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int m = row_of(bi, i);
+          if (m < M && n < a.N) {
+            float* c = (float*)a.C + (int64_t)m * a.ldc + n;
+            if constexpr (EPI == EPI_STORE)
+              *c = acc[bi][bj][i];
+            else
+              *c = xo[i] + acc[bi][bj][i];
+          }
         }
       }
   } else if constexpr (EPI == EPI_SWIGLU) {
@@ -249,21 +287,40 @@ __global__ __launch_bounds__(512) void gemm_big(GemmArgs a, QkRopeArgs qk) {
     constexpr int BPH = D >= 32 ? D / 32 : 1, HPW = 128 / D, HALF = D / 2;
     const int H = qk.n_heads, Hkv = qk.n_kv_heads;
     const int hw0 = (n0 + wn * 128) / D;  // global head index of the wave's first head
-    static_for<2>([&](auto bi_c) {
-      constexpr int bi = decltype(bi_c)::value;
-      static_for<16>([&](auto i_c) {
-        constexpr int i = decltype(i_c)::value;
+    // this lane's channels of a head are b * 32 + fr (D = 32: fr); their q and k gains
+    float gq[BPH], gk[BPH];
+#pragma unroll
+    for (int b = 0; b < BPH; ++b) {
+      gq[b] = qk.q_norm[b * 32 + fr];
+      gk[b] = qk.k_norm[b * 32 + fr];
+    }
+    static_for<4>([&](auto q_c) {
+      constexpr int bi = decltype(q_c)::value >> 1, i0 = (decltype(q_c)::value & 1) * 8;
+      // 8 rows' positions, blocks and rotation factors, requested together
+      int pos_r[8];
+      int64_t blk_r[8];
+      constexpr int NCS = D >= 64 ? BPH / 2 : 1;
+      float2 cs_r[8][NCS];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int lr = row_of(bi, i0 + r) - m0;
+        pos_r[r] = s_pos[lr];
+        blk_r[r] = s_blk[lr];
+      }
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int b = 0; b < NCS; ++b)
+          cs_r[r][b] = qk.rope[(int64_t)pos_r[r] * HALF + (D >= 64 ? b * 32 + fr : (fr & 15))];
+      static_for<8>([&](auto r_c) {
+        constexpr int r = decltype(r_c)::value, i = i0 + r;
         const int m = row_of(bi, i);
-        const int mc = min(m, M - 1);
-        const int pos = qk.b.row_pos[mc];
-        const int seq = qk.b.row_seq[mc];
-        const int64_t blk = qk.b.block_tables[(int64_t)seq * qk.b.tbl_stride + (pos >> qk.pool.block_shift)];
-        const int slot = pos & (qk.pool.block_tokens - 1);
+        const int64_t blk = blk_r[r];
+        const int slot = pos_r[r] & (qk.pool.block_tokens - 1);
         static_for<HPW>([&](auto hw_c) {
           constexpr int hw = decltype(hw_c)::value;
           const int hh = hw0 + hw;  // wave-uniform
           if (hh >= H + 2 * Hkv) return;
-          // channel of this lane in block b of the head: (b * 32 + fr) for D >= 64; fr for D = 32
           float v[BPH];
 #pragma unroll
           for (int b = 0; b < BPH; ++b) v[b] = acc[bi][(hw * D) / 32 + b][i];
@@ -274,23 +331,21 @@ __global__ __launch_bounds__(512) void gemm_big(GemmArgs a, QkRopeArgs qk) {
             for (int b = 0; b < BPH; ++b) ss += v[b] * v[b];
             ss = group_sum<32>(ss);
             const float inv = 1.0f / sqrtf(ss / (float)D + qk.eps);
-            const float* gain = hh < H ? qk.q_norm : qk.k_norm;
+            const bool isq = hh < H;
             if constexpr (D >= 64) {
 #pragma unroll
               for (int b = 0; b < BPH / 2; ++b) {
-                const int j = b * 32 + fr;
-                const float2 cs = qk.rope[(int64_t)pos * HALF + j];
-                const float x1 = v[b] * inv * gain[j];
-                const float x2 = v[b + BPH / 2] * inv * gain[j + HALF];
+                const float2 cs = cs_r[r][b];
+                const float x1 = v[b] * inv * (isq ? gq[b] : gk[b]);
+                const float x2 = v[b + BPH / 2] * inv * (isq ? gq[b + BPH / 2] : gk[b + BPH / 2]);
                 v[b] = x1 * cs.x - x2 * cs.y;
                 v[b + BPH / 2] = x2 * cs.x + x1 * cs.y;
               }
             } else {
               // D = 32: the head is one block; channel fr pairs with channel fr ^ 16, held by
               // the lane 16 away
-              const int j = fr & 15;
-              const float2 cs = qk.rope[(int64_t)pos * HALF + j];
-              const float xs = v[0] * inv * gain[fr];
+              const float2 cs = cs_r[r][0];
+              const float xs = v[0] * inv * (isq ? gq[0] : gk[0]);
               const float xo = __shfl_xor(xs, 16, 64);
               v[0] = fr < 16 ? xs * cs.x - xo * cs.y : xs * cs.x + xo * cs.y;
             }
