@@ -2,6 +2,7 @@
 // layout, validation of every call before anything is enqueued, the pinned metadata ring,
 // the RoPE table, and the per-call launch sequence on the caller's stream.
 #include <algorithm>
+#include <array>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -256,6 +257,7 @@ struct dec_ctx {
   int32_t* staging[kSlots];
   hipEvent_t ev[kSlots];
   int slot;
+  std::vector<std::array<int32_t, 3>> tile_sort;  // (last position, sequence, first row) per attention tile
   std::string err;
 };
 
@@ -292,8 +294,9 @@ int upload_meta(dec_ctx* ctx, hipStream_t st, int32_t S, const int32_t* start, c
     mc = std::max<int32_t>(mc, start[s] + n);
   }
   const int32_t n_out = mode == DEC_LOGITS_ALL ? N : (mode == DEC_LOGITS_LAST ? S : 0);
+  constexpr int QT = kPrefillQueryTile;
   int32_t n_tiles = 0;
-  for (int s = 0; s < S; ++s) n_tiles += ((n_new ? n_new[s] : 1) + 63) / 64;
+  for (int s = 0; s < S; ++s) n_tiles += ((n_new ? n_new[s] : 1) + QT - 1) / QT;
   const size_t o_tok = 0, o_pos = N, o_seq = 2 * (size_t)N, o_sst = 3 * (size_t)N, o_snn = o_sst + S,
                o_sr0 = o_snn + S, o_out = o_sr0 + S, o_til = o_out + n_out, o_tbl = o_til + 2 * (size_t)n_tiles;
   const size_t total = o_tbl + (size_t)S * stride;
@@ -316,12 +319,29 @@ int upload_meta(dec_ctx* ctx, hipStream_t st, int32_t S, const int32_t* start, c
       if (mode == DEC_LOGITS_ALL) m[o_out + r] = r;
     }
     if (mode == DEC_LOGITS_LAST) m[o_out + s] = r - 1;
-    for (int32_t i = 0; i < n; i += 64, ++t) {
+    for (int32_t i = 0; i < n; i += QT, ++t) {
       m[o_til + 2 * t] = s;
       m[o_til + 2 * t + 1] = m[o_sr0 + s] + i;
     }
     const int32_t need = (start[s] + n + c.block_tokens - 1) / c.block_tokens;
     for (int32_t j = 0; j < stride; ++j) m[o_tbl + (size_t)s * stride + j] = j < need ? tables[(size_t)s * max_blocks + j] : 0;
+  }
+  // attention tiles, the ones that see the most keys (latest last position) first
+  if (n_tiles > 1) {
+    auto& tl = ctx->tile_sort;
+    tl.resize(n_tiles);
+    for (int32_t i = 0; i < n_tiles; ++i) {
+      const int32_t sq = m[o_til + 2 * i], r0 = m[o_til + 2 * i + 1];
+      const int32_t last = start[sq] + std::min<int32_t>(r0 - m[o_sr0 + sq] + QT, m[o_snn + sq]) - 1;
+      tl[i] = {last, sq, r0};
+    }
+    std::stable_sort(tl.begin(), tl.end(), [](const std::array<int32_t, 3>& x, const std::array<int32_t, 3>& y) {
+      return x[0] > y[0];
+    });
+    for (int32_t i = 0; i < n_tiles; ++i) {
+      m[o_til + 2 * i] = tl[i][1];
+      m[o_til + 2 * i + 1] = tl[i][2];
+    }
   }
   int32_t* dm = (int32_t*)(ctx->wsp + ctx->ws.meta);
   HIPCHECK(hipMemcpyAsync(dm, m, total * 4, hipMemcpyHostToDevice, st));

@@ -535,31 +535,50 @@ hipError_t launch_attn_decode(const QkRopeArgs& qk, const AttnRowsArgs& a, void*
 }
 
 // ---- flash-style prefill attention (f16 pool, MFMA) ----------------------------------------
-// One block per (64-position query tile of one sequence, KV head); the 4 waves take 16 query
-// positions each, for all GROUP query heads of the KV head. Key tiles of 64 positions, aligned
-// to position 0 of the sequence, are staged in LDS (K row-major, V transposed) straight from
-// the pool blocks. Per key tile: S^T = K . Q^T (v_mfma_f32_16x16x32_f16, D/32 steps), causal
-// mask on absolute positions, online softmax in the exp2 domain, then O^T += V^T . P^T with P^T
-// taken directly from the S^T accumulators: in both products a lane's eight k-slots stand for
-// keys 4g..4g+3 of two adjacent 16-key blocks (g = lane / 16), which is a fixed relabelling of
-// the summation index, applied identically to both operands.
-// A query always sees the key tiles 0 .. floor(pos / 64) in order; later, fully masked tiles
-// leave its state unchanged bit for bit. The result therefore does not depend on how queries
-// are grouped into tiles, so batched, chunked and single-shot prefill agree exactly.
+// Causal attention of one sequence's new rows over its paged keys ("Candle model runner" 2.4,
+// second equation; keys up to and including the query's absolute position), read in place from
+// the pool. One block per (128-position query tile, KV head); wave w takes head w / 4 of the
+// KV head's group and 32 query positions. Key tiles of 64 positions, aligned to position 0 of
+// the sequence, are staged in LDS (K row-major, V transposed, two stages, the next tile loaded
+// while the current one is used). Per key tile and wave, with v_mfma_f32_32x32x16_f16:
+//   S^T = K . Q^T (keys x queries), scaled into the exp2 domain and causally masked;
+//   online softmax per query (a query's 64 scores sit in lanes l and l ^ 32);
+//   O^T += V^T . P^T, where P^T is taken from the S^T accumulators as they are: a lane's eight
+//   k-slots of k-step s stand for keys 16 s + 8 (j / 4) + 4 (l / 32) + j % 4, a fixed
+//   relabelling of the summation index applied to both operands.
+// A query sees the key tiles 0 .. floor(pos / 64) in order; a later, fully masked tile leaves
+// its state unchanged bit for bit (scale exp2(0) = 1, weights exp2(-inf) = 0, masked values
+// zero). The result therefore does not depend on how queries are grouped into tiles, so
+// batched, chunked and single-shot prefill agree exactly.
+
+namespace {
+constexpr int kPfKT = 64;  // keys per tile
+template <int D>
+struct PrefillLds {
+  static constexpr int KSTR = D + 8;      // K row stride (halves): 32-row fragment reads conflict-free
+  static constexpr int VSTR = kPfKT + 8;  // V^T row stride (halves)
+  static constexpr int KS = kPfKT * KSTR, VS = D * VSTR;
+  static constexpr size_t bytes = (size_t)2 * (KS + VS) * 2;  // two stages
+};
+}  // namespace
 
 template <int D, int G, bool BF16_OUT>
-__global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
-  constexpr int KT = 64;
-  constexpr int QT = 64;
-  constexpr int KSTR = D + 8;   // K tile row stride (halves)
-  constexpr int VSTR = KT + 8;  // V^T tile row stride (halves)
-  constexpr int NDK = D / 32;
-  constexpr int NDB = D / 16;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VSTR];
+__global__ __launch_bounds__(256 * G) void attn_prefill_kernel(AttnPrefillArgs a) {
+  using L = PrefillLds<D>;
+  constexpr int KT = kPfKT, QT = kPrefillQueryTile;
+  constexpr int NT = 256 * G;              // threads: G heads x 4 waves of 32 queries
+  constexpr int KSTR = L::KSTR, VSTR = L::VSTR;
+  constexpr int NDS = D / 16;              // k-steps of S^T over the head dimension
+  constexpr int NDB = D / 32;              // 32-row blocks of O^T
+  constexpr int NKC = KT * (D / 8);        // 16-byte K chunks per tile
+  constexpr int NVB = (KT / 8) * (D / 8);  // 8 x 8 V blocks per tile
+  static_assert(QT == 128, "4 waves of 32 query positions per head");
+  extern __shared__ __attribute__((aligned(16))) uint16_t plds[];  // [stage][K | V^T]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int tile = blockIdx.x, kvh = blockIdx.y;
+  const int hl = lane >> 5, ql = lane & 31;
+  const int gh = wave >> 2, qsub = wave & 3;
+  const int kvh = blockIdx.x, tile = blockIdx.y;
   const int seq = a.b.tiles[2 * tile], row0 = a.b.tiles[2 * tile + 1];
   const int s_start = a.b.seq_start[seq], s_n = a.b.seq_nnew[seq], s_row0 = a.b.seq_row0[seq];
   const int ctx_end = s_start + s_n;
@@ -573,141 +592,169 @@ __global__ __launch_bounds__(256) void attn_prefill_kernel(AttnPrefillArgs a) {
   const uint16_t* kbase = (const uint16_t*)a.pool.base + (int64_t)a.layer * 2 * a.pool.n_blocks * slab +
                           (int64_t)kvh * a.pool.block_tokens * D;
   const uint16_t* vbase = kbase + a.pool.n_blocks * slab;
+  const int head = kvh * G + gh;
 
-  const int qi = wave * 16 + (lane & 15);
+  // this lane's query (column of S^T and O^T)
+  const int qi = qsub * 32 + ql;
   const bool qvalid = qi < tile_rows;
   const int qrow = row0 + min(qi, tile_rows - 1);
   const int qpos = p0 + qi;
+  f16x8 qf[NDS];
+#pragma unroll
+  for (int ks = 0; ks < NDS; ++ks)
+    qf[ks] = __builtin_bit_cast(f16x8, *(const u32x4*)(a.q + ((int64_t)qrow * H + head) * D + ks * 16 + hl * 8));
 
-  f16x8 qf[G][NDK];
+  // ---- staging of key tile kt: K chunks and transposed 8 x 8 V blocks through registers
+  constexpr int KPT = (NKC + NT - 1) / NT;
+  u32x4 kreg[KPT], vreg[8];
+  auto load_tile = [&](int kt) {
 #pragma unroll
-  for (int g = 0; g < G; ++g)
+    for (int j = 0; j < KPT; ++j) {
+      const int c = tid + j * NT;
+      const int key = c / (D / 8), part = c % (D / 8);
+      const int kpos = kt * KT + key;
+      kreg[j] = u32x4{0u, 0u, 0u, 0u};
+      if (c < NKC && kpos < ctx_end)
+        kreg[j] = *(const u32x4*)(kbase + (int64_t)table[kpos >> bsh] * slab + (kpos & bmask) * D + part * 8);
+    }
+    if (tid < NVB) {
+      const int k8 = tid / (D / 8), d8 = tid % (D / 8);
 #pragma unroll
-    for (int dk = 0; dk < NDK; ++dk)
-      qf[g][dk] = __builtin_bit_cast(
-          f16x8, *(const u32x4*)(a.q + ((int64_t)qrow * H + kvh * G + g) * D + dk * 32 + (lane >> 4) * 8));
+      for (int e = 0; e < 8; ++e) {
+        const int kpos = kt * KT + k8 * 8 + e;
+        vreg[e] = u32x4{0u, 0u, 0u, 0u};
+        if (kpos < ctx_end)
+          vreg[e] = *(const u32x4*)(vbase + (int64_t)table[kpos >> bsh] * slab + (kpos & bmask) * D + d8 * 8);
+      }
+    }
+  };
+  auto store_tile = [&](int st) {
+    uint16_t* Ks = plds + (size_t)st * (L::KS + L::VS);
+    uint16_t* Vt = Ks + L::KS;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      const int c = tid + j * NT;
+      if (c < NKC) *(u32x4*)(Ks + (c / (D / 8)) * KSTR + (c % (D / 8)) * 8) = kreg[j];
+    }
+    if (tid < NVB) {
+      const int k8 = tid / (D / 8), d8 = tid % (D / 8);
+      // vreg[e] word w holds channels (2w, 2w + 1) of key e; row d of the transposed block
+      // holds keys 0..7 of channel d
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        u32x4 t;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t x0 = vreg[2 * w][d >> 1], x1 = vreg[2 * w + 1][d >> 1];
+          t[w] = (d & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
+        }
+        *(u32x4*)(Vt + (d8 * 8 + d) * VSTR + k8 * 8) = t;
+      }
+    }
+  };
 
-  f32x4 o[G][NDB];
-  float m[G], l[G];
+  f32x16 o[NDB];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = -__builtin_inff();
-    l[g] = 0.f;
+  for (int db = 0; db < NDB; ++db)
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) o[g][db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+    for (int e = 0; e < 16; ++e) o[db][e] = 0.f;
+  float m = -__builtin_inff(), l = 0.f;
   const float sl2 = 1.4426950408889634f / sqrtf((float)D);
   const int n_kt = pmax / KT + 1;
 
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
   for (int kt = 0; kt < n_kt; ++kt) {
-    __syncthreads();
-    for (int c = tid; c < KT * (D / 8); c += 256) {
-      const int key = c / (D / 8), part = c % (D / 8);
-      const int kpos = kt * KT + key;
-      u32x4 kv = u32x4{0u, 0u, 0u, 0u}, vv = u32x4{0u, 0u, 0u, 0u};
-      if (kpos < ctx_end) {
-        const int64_t off = (int64_t)table[kpos >> bsh] * slab + (kpos & bmask) * D + part * 8;
-        kv = *(const u32x4*)(kbase + off);
-        vv = *(const u32x4*)(vbase + off);
-      }
-      *(u32x4*)(Ks + key * KSTR + part * 8) = kv;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        Vt[(part * 8 + 2 * e) * VSTR + key] = (uint16_t)(vv[e] & 0xffffu);
-        Vt[(part * 8 + 2 * e + 1) * VSTR + key] = (uint16_t)(vv[e] >> 16);
-      }
-    }
-    __syncthreads();
+    const int st = kt & 1;
+    const bool more = kt + 1 < n_kt;
+    if (more) load_tile(kt + 1);
+    const uint16_t* Ks = plds + (size_t)st * (L::KS + L::VS);
+    const uint16_t* Vt = Ks + L::KS;
 
-    f32x4 s[G][4];
+    // S^T = K . Q^T for the tile's 64 keys (two 32-key blocks)
+    f32x16 sacc[2];
 #pragma unroll
-    for (int g = 0; g < G; ++g)
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) s[g][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int dk = 0; dk < NDK; ++dk) {
-        const f16x8 kf = __builtin_bit_cast(
-            f16x8, *(const u32x4*)(Ks + (kb * 16 + (lane & 15)) * KSTR + dk * 32 + (lane >> 4) * 8));
-#pragma unroll
-        for (int g = 0; g < G; ++g) s[g][kb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf, qf[g][dk], s[g][kb], 0, 0, 0);
-      }
-
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float mt = -__builtin_inff();
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int kpos = kt * KT + kb * 16 + (lane >> 4) * 4 + r;
-          float v = s[g][kb][r] * sl2;
-          if (kpos > qpos) v = -__builtin_inff();
-          s[g][kb][r] = v;
-          mt = fmaxf(mt, v);
-        }
-      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float mnew = fmaxf(m[g], mt);
-      const bool none = mnew == -__builtin_inff();
-      const float alpha = none ? 1.f : exp2f(m[g] - mnew);
-      float ps = 0.f;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = none ? 0.f : exp2f(s[g][kb][r] - mnew);
-          s[g][kb][r] = p;
-          ps += p;
-        }
-      ps += __shfl_xor(ps, 16, 64);
-      ps += __shfl_xor(ps, 32, 64);
-      l[g] = l[g] * alpha + ps;
-      m[g] = mnew;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) o[g][db] *= alpha;
-    }
-
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      f16x8 pf[G];
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          pf[g][r] = (_Float16)s[g][2 * ks][r];
-          pf[g][4 + r] = (_Float16)s[g][2 * ks + 1][r];
-        }
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const uint16_t* vr = Vt + (db * 16 + (lane & 15)) * VSTR + ks * 32 + (lane >> 4) * 4;
-        const u32x2 lo = *(const u32x2*)vr;
-        const u32x2 hi = *(const u32x2*)(vr + 16);
-        const f16x8 vf = __builtin_bit_cast(f16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-#pragma unroll
-        for (int g = 0; g < G; ++g) o[g][db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf[g], o[g][db], 0, 0, 0);
+      for (int ks = 0; ks < NDS; ++ks) {
+        const f16x8 kf = __builtin_bit_cast(f16x8, *(const u32x4*)(Ks + (kb * 32 + ql) * KSTR + ks * 16 + hl * 8));
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], sacc[kb], 0, 0, 0);
       }
     }
-  }
-
-  if (!qvalid) return;
+    // online softmax of this lane's query over the tile
+    float mt = -__builtin_inff();
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const float inv = 1.0f / l[g];
-    const int64_t ob = (int64_t)qrow * H * D + (int64_t)(kvh * G + g) * D;
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kpos = kt * KT + kb * 32 + 8 * (i >> 2) + 4 * hl + (i & 3);
+        float v = sacc[kb][i] * sl2;
+        if (kpos > qpos) v = -__builtin_inff();
+        sacc[kb][i] = v;
+        mt = fmaxf(mt, v);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float mnew = fmaxf(m, mt);
+    const bool none = mnew == -__builtin_inff();
+    const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m - mnew);
+    float ps = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = none ? 0.f : __builtin_amdgcn_exp2f(sacc[kb][i] - mnew);
+        sacc[kb][i] = p;
+        ps += p;
+      }
+    ps += __shfl_xor(ps, 32, 64);
+    l = l * alpha + ps;
+    m = mnew;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int d = db * 16 + (lane >> 4) * 4 + r;
-        const float v = o[g][db][r] * inv;
-        if constexpr (BF16_OUT)
-          ((uint16_t*)a.o)[ob + d] = f32_to_bf16_bits(v);
-        else
-          ((float*)a.o)[ob + d] = v;
+      for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+
+    // O^T += V^T . P^T over four 16-key steps
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      f16x8 pf;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) pf[j] = (_Float16)sacc[s4 >> 1][8 * (s4 & 1) + j];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const uint16_t* vr = Vt + (db * 32 + ql) * VSTR + 16 * s4 + 4 * hl;
+        const u32x2 lo = *(const u32x2*)vr;
+        const u32x2 hi = *(const u32x2*)(vr + 8);
+        const f16x8 vf = __builtin_bit_cast(f16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf, o[db], 0, 0, 0);
       }
+    }
+    if (more) store_tile(st ^ 1);
+    __syncthreads();
   }
+
+  if (!qvalid) return;
+  const float inv = 1.0f / l;
+  const int64_t ob = (int64_t)qrow * H * D + (int64_t)head * D;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d = db * 32 + 8 * g + 4 * hl;
+      const float v0 = o[db][4 * g] * inv, v1 = o[db][4 * g + 1] * inv, v2 = o[db][4 * g + 2] * inv,
+                  v3 = o[db][4 * g + 3] * inv;
+      if constexpr (BF16_OUT) {
+        uint2 w;
+        w.x = (uint32_t)f32_to_bf16_bits(v0) | ((uint32_t)f32_to_bf16_bits(v1) << 16);
+        w.y = (uint32_t)f32_to_bf16_bits(v2) | ((uint32_t)f32_to_bf16_bits(v3) << 16);
+        *(uint2*)((uint16_t*)a.o + ob + d) = w;
+      } else {
+        *(float4*)((float*)a.o + ob + d) = make_float4(v0, v1, v2, v3);
+      }
+    }
 }
 
 bool attn_prefill_supported(int head_dim, int group) {
@@ -715,28 +762,36 @@ bool attn_prefill_supported(int head_dim, int group) {
 }
 
 template <int D, int G>
-static void prefill_launch(const AttnPrefillArgs& a, dim3 g, hipStream_t s) {
+static hipError_t prefill_launch(const AttnPrefillArgs& a, dim3 g, hipStream_t s) {
+  constexpr size_t lds = PrefillLds<D>::bytes;
+  static bool attr = false;  // raise the dynamic LDS limit once per instantiation
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void*)attn_prefill_kernel<D, G, true>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)attn_prefill_kernel<D, G, false>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
   if (a.out_bf16)
-    attn_prefill_kernel<D, G, true><<<g, 256, 0, s>>>(a);
+    attn_prefill_kernel<D, G, true><<<g, 256 * G, lds, s>>>(a);
   else
-    attn_prefill_kernel<D, G, false><<<g, 256, 0, s>>>(a);
+    attn_prefill_kernel<D, G, false><<<g, 256 * G, lds, s>>>(a);
+  return hipGetLastError();
 }
 
 template <int D>
 static hipError_t prefill_dispatch(const AttnPrefillArgs& a, dim3 g, hipStream_t s) {
   const int group = a.n_heads / a.n_kv_heads;
-  if (group == 1)
-    prefill_launch<D, 1>(a, g, s);
-  else if (group == 2)
-    prefill_launch<D, 2>(a, g, s);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (group == 1) return prefill_launch<D, 1>(a, g, s);
+  if (group == 2) return prefill_launch<D, 2>(a, g, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_attn_prefill(const AttnPrefillArgs& a, hipStream_t s) {
   if (a.b.n_tiles <= 0) return hipSuccess;
-  dim3 g(a.b.n_tiles, a.n_kv_heads);
+  dim3 g(a.n_kv_heads, a.b.n_tiles);  // KV heads fastest: a tile's heads run side by side
   if (a.head_dim == 32) return prefill_dispatch<32>(a, g, s);
   if (a.head_dim == 64) return prefill_dispatch<64>(a, g, s);
   if (a.head_dim == 128) return prefill_dispatch<128>(a, g, s);

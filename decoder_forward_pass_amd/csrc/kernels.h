@@ -6,6 +6,8 @@
 
 namespace dec {
 
+constexpr int kPrefillQueryTile = 128;
+
 // x[r][:] = widened/dequantised E[tok[r]][:] as float32; an id outside [0, vocab) gives NaN.
 // ssq (optional, [n_rows][d/16]): sums of squares of each 16 columns of the row.
 hipError_t launch_embed(const int32_t* tok, int n_rows, int vocab, int d, int wdtype, const WMat& E,
@@ -55,7 +57,8 @@ hipError_t launch_attn_decode(const QkRopeArgs& qk, const AttnRowsArgs& a, void*
 hipError_t launch_attn_combine(const float* partial, int n_rows, int n_heads, int head_dim, int n_chunks,
                                int chunk, const int32_t* row_pos, void* o, bool out_bf16, hipStream_t s);
 
-// Flash-style causal prefill attention on an f16 pool (MFMA), query tiles of one sequence.
+// Flash-style causal prefill attention on an f16 pool (MFMA), query tiles of one sequence
+// (BatchDev::tiles lists (sequence, first row) of tiles of kPrefillQueryTile rows).
 struct AttnPrefillArgs {
   const uint16_t* q;  // [n_rows][H][D] f16
   PoolDev pool;
