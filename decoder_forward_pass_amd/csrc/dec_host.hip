@@ -2,7 +2,6 @@
 // layout, validation of every call before anything is enqueued, the pinned metadata ring,
 // the RoPE table, and the per-call launch sequence on the caller's stream.
 #include <algorithm>
-#include <array>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -257,7 +256,6 @@ struct dec_ctx {
   int32_t* staging[kSlots];
   hipEvent_t ev[kSlots];
   int slot;
-  std::vector<std::array<int32_t, 3>> tile_sort;  // (last position, sequence, first row) per attention tile
   std::string err;
 };
 
@@ -326,21 +324,16 @@ int upload_meta(dec_ctx* ctx, hipStream_t st, int32_t S, const int32_t* start, c
     const int32_t need = (start[s] + n + c.block_tokens - 1) / c.block_tokens;
     for (int32_t j = 0; j < stride; ++j) m[o_tbl + (size_t)s * stride + j] = j < need ? tables[(size_t)s * max_blocks + j] : 0;
   }
-  // attention tiles, the ones that see the most keys (latest last position) first
+  // attention tiles: sequence by sequence, each sequence's tiles from the last (most keys) to
+  // the first, so that blocks running side by side share a sequence's keys in L2
   if (n_tiles > 1) {
-    auto& tl = ctx->tile_sort;
-    tl.resize(n_tiles);
-    for (int32_t i = 0; i < n_tiles; ++i) {
-      const int32_t sq = m[o_til + 2 * i], r0 = m[o_til + 2 * i + 1];
-      const int32_t last = start[sq] + std::min<int32_t>(r0 - m[o_sr0 + sq] + QT, m[o_snn + sq]) - 1;
-      tl[i] = {last, sq, r0};
-    }
-    std::stable_sort(tl.begin(), tl.end(), [](const std::array<int32_t, 3>& x, const std::array<int32_t, 3>& y) {
-      return x[0] > y[0];
-    });
-    for (int32_t i = 0; i < n_tiles; ++i) {
-      m[o_til + 2 * i] = tl[i][1];
-      m[o_til + 2 * i + 1] = tl[i][2];
+    int32_t t2 = 0;
+    for (int s = 0; s < S; ++s) {
+      const int32_t n = n_new ? n_new[s] : 1, nt = (n + QT - 1) / QT;
+      for (int32_t i = nt - 1; i >= 0; --i, ++t2) {
+        m[o_til + 2 * t2] = s;
+        m[o_til + 2 * t2 + 1] = m[o_sr0 + s] + i * QT;
+      }
     }
   }
   int32_t* dm = (int32_t*)(ctx->wsp + ctx->ws.meta);

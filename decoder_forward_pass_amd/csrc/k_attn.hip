@@ -556,7 +556,9 @@ constexpr int kPfKT = 64;  // keys per tile
 template <int D>
 struct PrefillLds {
   static constexpr int KSTR = D + 8;      // K row stride (halves): 32-row fragment reads conflict-free
-  static constexpr int VSTR = kPfKT + 8;  // V^T row stride (halves)
+  // V^T row stride (halves): 34 words, so the 32 rows of a 64-bit fragment read fall on 32
+  // distinct bank pairs
+  static constexpr int VSTR = kPfKT + 4;
   static constexpr int KS = kPfKT * KSTR, VS = D * VSTR;
   static constexpr size_t bytes = (size_t)2 * (KS + VS) * 2;  // two stages
 };
@@ -571,7 +573,6 @@ __global__ __launch_bounds__(256 * G) void attn_prefill_kernel(AttnPrefillArgs a
   constexpr int NDS = D / 16;              // k-steps of S^T over the head dimension
   constexpr int NDB = D / 32;              // 32-row blocks of O^T
   constexpr int NKC = KT * (D / 8);        // 16-byte K chunks per tile
-  constexpr int NVB = (KT / 8) * (D / 8);  // 8 x 8 V blocks per tile
   static_assert(QT == 128, "4 waves of 32 query positions per head");
   extern __shared__ __attribute__((aligned(16))) uint16_t plds[];  // [stage][K | V^T]
 
@@ -604,51 +605,62 @@ __global__ __launch_bounds__(256 * G) void attn_prefill_kernel(AttnPrefillArgs a
   for (int ks = 0; ks < NDS; ++ks)
     qf[ks] = __builtin_bit_cast(f16x8, *(const u32x4*)(a.q + ((int64_t)qrow * H + head) * D + ks * 16 + hl * 8));
 
-  // ---- staging of key tile kt: K chunks and transposed 8 x 8 V blocks through registers
+  // ---- staging of key tile kt through registers: K in 16-byte chunks, V in blocks of 2 keys x
+  // 8 channels transposed in registers (32 consecutive threads fill one row of V^T). The pool
+  // block of every key of a tile is fetched ahead (lane j of each wave: key j of the tile) and
+  // handed out by lane shuffles.
   constexpr int KPT = (NKC + NT - 1) / NT;
-  u32x4 kreg[KPT], vreg[8];
-  auto load_tile = [&](int kt) {
+  constexpr int NV2 = (KT / 2) * (D / 8);  // 2 x 8 V blocks per tile
+  constexpr int VPT = (NV2 + NT - 1) / NT;
+  const int last_key = ctx_end - 1;
+  auto block_ids = [&](int kt) {
+    return table[min(kt * KT + lane, last_key) >> bsh];
+  };
+  struct Regs {
+    u32x4 k[KPT], v[VPT][2];
+  };
+  auto load_tile = [&](int kt, int bids, Regs& r) {
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
-      const int c = tid + j * NT;
+      const int c = min(tid + j * NT, NKC - 1);
       const int key = c / (D / 8), part = c % (D / 8);
       const int kpos = kt * KT + key;
-      kreg[j] = u32x4{0u, 0u, 0u, 0u};
-      if (c < NKC && kpos < ctx_end)
-        kreg[j] = *(const u32x4*)(kbase + (int64_t)table[kpos >> bsh] * slab + (kpos & bmask) * D + part * 8);
+      const int64_t blk = __shfl(bids, key, 64);
+      r.k[j] = *(const u32x4*)(kbase + blk * slab + (min(kpos, last_key) & bmask) * D + part * 8);
+      if (kpos > last_key) r.k[j] = u32x4{0u, 0u, 0u, 0u};
     }
-    if (tid < NVB) {
-      const int k8 = tid / (D / 8), d8 = tid % (D / 8);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int kpos = kt * KT + k8 * 8 + e;
-        vreg[e] = u32x4{0u, 0u, 0u, 0u};
-        if (kpos < ctx_end)
-          vreg[e] = *(const u32x4*)(vbase + (int64_t)table[kpos >> bsh] * slab + (kpos & bmask) * D + d8 * 8);
+    for (int j = 0; j < VPT; ++j) {
+      const int vb = min(tid + j * NT, NV2 - 1);
+      const int k2 = vb % (KT / 2), d8 = vb / (KT / 2);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int key = k2 * 2 + e, kpos = kt * KT + key;
+        const int64_t blk = __shfl(bids, key, 64);
+        r.v[j][e] = *(const u32x4*)(vbase + blk * slab + (min(kpos, last_key) & bmask) * D + d8 * 8);
+        if (kpos > last_key) r.v[j][e] = u32x4{0u, 0u, 0u, 0u};
       }
     }
   };
-  auto store_tile = [&](int st) {
+  auto store_tile = [&](int st, const Regs& r) {
     uint16_t* Ks = plds + (size_t)st * (L::KS + L::VS);
     uint16_t* Vt = Ks + L::KS;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       const int c = tid + j * NT;
-      if (c < NKC) *(u32x4*)(Ks + (c / (D / 8)) * KSTR + (c % (D / 8)) * 8) = kreg[j];
+      if (c < NKC) *(u32x4*)(Ks + (c / (D / 8)) * KSTR + (c % (D / 8)) * 8) = r.k[j];
     }
-    if (tid < NVB) {
-      const int k8 = tid / (D / 8), d8 = tid % (D / 8);
-      // vreg[e] word w holds channels (2w, 2w + 1) of key e; row d of the transposed block
-      // holds keys 0..7 of channel d
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+      const int vb = tid + j * NT;
+      if (vb >= NV2) continue;
+      const int k2 = vb % (KT / 2), d8 = vb / (KT / 2);
+      // r.v[j][e] word w holds channels (2w, 2w + 1) of key e; row d of V^T gets keys 0..1
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
-        u32x4 t;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t x0 = vreg[2 * w][d >> 1], x1 = vreg[2 * w + 1][d >> 1];
-          t[w] = (d & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
-        }
-        *(u32x4*)(Vt + (d8 * 8 + d) * VSTR + k8 * 8) = t;
+        const uint32_t x0 = r.v[j][0][d >> 1], x1 = r.v[j][1][d >> 1];
+        *(uint32_t*)(Vt + (d8 * 8 + d) * VSTR + k2 * 2) =
+            (d & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
       }
     }
   };
@@ -662,13 +674,22 @@ __global__ __launch_bounds__(256 * G) void attn_prefill_kernel(AttnPrefillArgs a
   const float sl2 = 1.4426950408889634f / sqrtf((float)D);
   const int n_kt = pmax / KT + 1;
 
-  load_tile(0);
-  store_tile(0);
+  // Pipeline: tile kt is used from LDS stage kt % 2 while tile kt + 1 (in registers since the
+  // previous step) is written to the other stage and tile kt + 2 is requested from memory.
+  Regs ra, rb;
+  int bids = block_ids(0);
+  load_tile(0, bids, ra);
+  bids = block_ids(min(1, n_kt - 1));
+  if (n_kt > 1) load_tile(1, bids, rb);
+  bids = block_ids(min(2, n_kt - 1));
+  store_tile(0, ra);
   __syncthreads();
-  for (int kt = 0; kt < n_kt; ++kt) {
+  auto step = [&](int kt, const Regs& next, Regs& fill) {
     const int st = kt & 1;
-    const bool more = kt + 1 < n_kt;
-    if (more) load_tile(kt + 1);
+    if (kt + 2 < n_kt) {
+      load_tile(kt + 2, bids, fill);
+      bids = block_ids(min(kt + 3, n_kt - 1));
+    }
     const uint16_t* Ks = plds + (size_t)st * (L::KS + L::VS);
     const uint16_t* Vt = Ks + L::KS;
 
@@ -732,8 +753,12 @@ __global__ __launch_bounds__(256 * G) void attn_prefill_kernel(AttnPrefillArgs a
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf, o[db], 0, 0, 0);
       }
     }
-    if (more) store_tile(st ^ 1);
+    if (kt + 1 < n_kt) store_tile(st ^ 1, next);
     __syncthreads();
+  };
+  for (int kt = 0; kt < n_kt; kt += 2) {
+    step(kt, rb, ra);
+    if (kt + 1 < n_kt) step(kt + 1, ra, rb);
   }
 
   if (!qvalid) return;
