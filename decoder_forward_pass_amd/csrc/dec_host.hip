@@ -164,7 +164,9 @@ Ws ws_layout(const dec_config& c) {
   w.meta = take(w.meta_ints * 4);
   w.x = take(R * d * 4);
   w.h = take(R * d * w.act_bytes);
-  w.qkv = take(R * qkvw * 4);
+  // float32 Q|K|V product (prefill rows), or the decode step's partial products along K
+  const int dparts = gemm_decode_parts(c.weight_dtype, (int)qkvw, (int)d);
+  w.qkv = take(std::max(R, (size_t)std::max(dparts, 1) * S) * qkvw * 4);
   w.q = take(R * qw * w.kv_el);
   w.o = take(R * qw * w.act_bytes);
   w.a = take(R * ff * w.act_bytes);
@@ -425,6 +427,7 @@ int run_forward(dec_ctx* ctx, hipStream_t st, const BatchDev& b, const int32_t* 
   // launch. Prefill calls always take the tile GEMM after an RMSNorm launch.
   const bool dgemm = decode && gemm_decode_supported(c.weight_dtype, d) &&
                      gemm_decode_supported(c.weight_dtype, qw) && gemm_decode_supported(c.weight_dtype, ff);
+  const int dparts = dgemm && gemm_decode_parts(c.weight_dtype, qkvw, d) <= 8 ? gemm_decode_parts(c.weight_dtype, qkvw, d) : 0;
   // Prefill calls with bf16 / uint4 weights take the 256 x 256 tile GEMM, which also applies
   // the q/k norm, RoPE and the KV write in its Q|K|V epilogue (chosen by the configuration
   // alone, so every prefill call of a model computes the same way).
@@ -457,10 +460,16 @@ int run_forward(dec_ctx* ctx, hipStream_t st, const BatchDev& b, const int32_t* 
     g.seg[0] = L.wq; g.seg[1] = L.wk; g.seg[2] = L.wv; g.nseg = 3;
     g.C = qkv; g.ldc = qkvw;
     QkRopeArgs qa{qkv, L.q_norm, L.k_norm, rope, q, pool, l, H, Hkv, D, c.rms_eps, kv_f16, b};
-    if (big)
+    if (big) {
       TLAUNCH(DEC_K_GEMM_QKV, launch_gemm_big(c.weight_dtype, EPI_QKV, g, &qa, st));
-    else
+    } else if (dparts) {
+      // decode: K split into partial products that the attention kernel adds up
+      qa.parts = dparts;
+      qa.part_stride = (int64_t)N * qkvw;
+      TLAUNCH(DEC_K_GEMM_QKV, launch_gemm_decode_parts(c.weight_dtype, g, qa.part_stride, st));
+    } else {
       TLAUNCH(DEC_K_GEMM_QKV, gemm(EPI_STORE, g));
+    }
     if (decode) {
       AttnRowsArgs ra{q, pool, l, H, Hkv, D, kv_f16, nch, part, b};
       TLAUNCH(DEC_K_ATTN_ROWS, launch_attn_decode(qa, ra, o, act_bf16, st));

@@ -357,8 +357,27 @@ __global__ __launch_bounds__(1024) void attn_decode_kernel(QkRopeArgs qk, AttnRo
   if (wave <= GROUP + 1) {
     const int half = D / 2;
     const int hh = wave < GROUP ? kvh * GROUP + wave : (wave == GROUP ? H + kvh : H + Hkv + kvh);
+    // the Q|K|V product of the row: the sum of qk.parts partial products, in order
     const float* src = qk.qkv + (int64_t)row * (H + 2 * Hkv) * D + (int64_t)hh * D;
-    float x1 = lane < half ? src[lane] : 0.f, x2 = lane < half ? src[lane + half] : 0.f;
+    float x1 = 0.f, x2 = 0.f;
+    if (lane < half) {
+      float p1[8], p2[8];
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        const float* sp = src + (int64_t)min(p, qk.parts - 1) * qk.part_stride;
+        p1[p] = sp[lane];
+        p2[p] = sp[lane + half];
+      }
+      x1 = p1[0];
+      x2 = p2[0];
+#pragma unroll
+      for (int p = 1; p < 8; ++p) {
+        if (p < qk.parts) {
+          x1 += p1[p];
+          x2 += p2[p];
+        }
+      }
+    }
     if (wave <= GROUP) {
       const float2 cs = lane < half ? qk.rope[(int64_t)pos * half + lane] : make_float2(1.f, 0.f);
       norm_rope_pair(x1, x2, wave < GROUP ? qk.q_norm : qk.k_norm, cs, lane, D, qk.eps);
