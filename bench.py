@@ -10,8 +10,10 @@ between two device synchronisations. ``value`` is whole-job tokens/s (prompt + g
 tokens per second); prefill and decode rates are reported beside it.
 
 ``roofline``: the kernel with the largest share of the timed region's GPU time (decode
-attention, HBM-bound), timed live with HIP events around its launches on the library's
-stream; achieved = its algorithmic bytes per launch / its mean launch duration.
+attention, HBM-bound), timed live on the library's stream with HIP events that the launch
+itself records at the kernel's start and end, on the attention launches of every 16th decode
+step of the timed steps; achieved = their mean algorithmic bytes per launch / their mean
+duration. ``traffic``: HBM bytes per launch from the committed hardware-counter summary.
 ``roofline_prefill``: the same for the largest prefill GEMM (MFMA-bound). ``cpu_baseline``:
 the float64 CPU oracle on a bounded sample of the same workload (one sequence's prefill and
 a few decode steps), timed on this host.
@@ -47,7 +49,133 @@ def parse():
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (a reference dispatch of known "
                          "traffic for hardware-counter runs)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU work: turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, "
+                         "each with --copy-mb) into the profiles/ traffic summary of the decode attention kernel")
+    ap.add_argument("--summarize-stats", metavar="STATS_DIR",
+                    help="no GPU work: turn a rocprofv3 --kernel-trace --stats run of this script into the "
+                         "profiles/ kernel-time summary")
     return ap.parse_args()
+
+
+ATTN_SOURCES = ["decoder_forward_pass_amd/csrc/k_attn.hip", "decoder_forward_pass_amd/csrc/common.h"]
+TRAFFIC_KERNEL = "attn_decode_kernel"
+
+
+def _sources_sha256(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for src in paths:
+        with open(os.path.join(ROOT, src), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _csv_rows(directory, suffix):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(directory, "**", "*" + suffix), recursive=True))
+    if not files:
+        sys.exit(f"no *{suffix} under {directory}")
+    with open(files[0]) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_counters(fetch_dir, write_dir, wl_name, copy_mb):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of every kernel, scaled by what the same counter
+    reads for the reference copy of known size, and the decode attention's bytes per launch."""
+    from collections import defaultdict
+    per = {}
+    ref = {}
+    for name, directory in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        sums = defaultdict(float)
+        for r in _csv_rows(directory, "counter_collection.csv"):
+            if r["Counter_Name"] == name:
+                sums[(r["Kernel_Name"], r["Dispatch_Id"])] += float(r["Counter_Value"])
+        copies = [v for (k, _), v in sums.items() if "copyBuffer" in k]
+        ref[name] = max(copies)  # the reference copy is the largest copy dispatch
+        agg = defaultdict(list)
+        for (k, _), v in sums.items():
+            agg[k].append(v)
+        per[name] = agg
+    ref_bytes = copy_mb << 20
+    fscale, wscale = ref_bytes / ref["FETCH_SIZE"], ref_bytes / ref["WRITE_SIZE"]
+    rows = []
+    for k, vals in per["FETCH_SIZE"].items():
+        if "copyBuffer" in k or "fillBuffer" in k:
+            continue
+        w = per["WRITE_SIZE"].get(k, [0.0])
+        rows.append((k, len(vals), np.mean(vals) * fscale, np.mean(w) * wscale, np.mean(vals), np.mean(w)))
+    rows.sort(key=lambda r: -(r[1] * (r[2] + r[3])))
+    attn = [r for r in rows if TRAFFIC_KERNEL in r[0]]
+    if not attn:
+        sys.exit("the decode attention kernel is not in the counter runs")
+    k, n, fb, wb, fk, wk = attn[0]
+    wl = __import__("synthetic").WORKLOADS[wl_name]
+    shape = __import__("synthetic").MODELS[wl.model]
+    per_key = shape.n_kv_heads * shape.head_dim * 2 * (2 if shape.kv_dtype == "f16" else 4)
+    alg = float(np.mean([wl.n_seqs * (wl.prompt_len + t + 1) * per_key for t in range(wl.decode_steps)]))
+    summary = {
+        "kernel": k, "workload": f"{wl_name} (decode steps)", "sources": ATTN_SOURCES,
+        "source_sha256": _sources_sha256(ATTN_SOURCES), "dispatches": n,
+        "fetch_kib_mean": fk, "write_kib_mean": wk, "copy_reference_bytes": ref_bytes,
+        "copy_fetch_kib": ref["FETCH_SIZE"], "copy_write_kib": ref["WRITE_SIZE"],
+        "fetch_scale": fscale / 1024, "write_scale": wscale / 1024,
+        "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb, "traffic_bytes_per_launch": fb + wb,
+        "algorithmic_bytes_per_launch": alg,
+    }
+    base = os.path.join(ROOT, "profiles", f"{TRAFFIC_KERNEL}_{wl_name}_pmc")
+    with open(base + ".json", "w") as f:
+        json.dump(summary, f, indent=1)
+    cmd = ("rocprofv3 --pmc {c} -d gpurun_out/{d} -o run --output-format csv -- python -u bench.py --steps 1 "
+           f"--warmup 0 --no-cpu-baseline --copy-mb {copy_mb} --workload {wl_name}")
+    lines = [
+        f"# HBM traffic: `{TRAFFIC_KERNEL}` on {wl_name} (decode steps)", "",
+        "Commands (one MI355X, repo root; one counter per run), then the summary:", "", "```",
+        cmd.format(c="FETCH_SIZE", d="pmc_fetch"), cmd.format(c="WRITE_SIZE", d="pmc_write"),
+        f"python bench.py --summarize-counters gpurun_out/pmc_fetch gpurun_out/pmc_write --workload {wl_name} "
+        f"--copy-mb {copy_mb}", "```", "",
+        f"Per-dispatch `Counter_Value` (KiB), averaged over each kernel's dispatches. Calibration: the "
+        f"{copy_mb} MiB device-to-device copy that `--copy-mb` runs first (the largest copy dispatch; "
+        f"{ref_bytes:,} bytes read and written).", "",
+        "| counter | reference copy (KiB) | bytes per KiB | attention mean (KiB/dispatch) | bytes per launch |",
+        "|---|---:|---:|---:|---:|",
+        f"| FETCH_SIZE | {ref['FETCH_SIZE']:.1f} | {fscale:.1f} | {fk:.1f} | {fb / 1e6:.2f} MB |",
+        f"| WRITE_SIZE | {ref['WRITE_SIZE']:.1f} | {wscale:.1f} | {wk:.1f} | {wb / 1e6:.3f} MB |", "",
+        f"Dispatches: {n}. Algorithmic bytes per launch (every visible key and value read once): "
+        f"{alg / 1e6:.2f} MB, the mean over the decode steps. Measured traffic {(fb + wb) / 1e6:.2f} MB = "
+        f"{100 * (fb + wb) / alg:.1f}% of it (the rest: query rows, block tables, output rows, the new keys "
+        "and values).", "",
+        "All kernels of the run (scaled fetch / write per dispatch):", "",
+        "| kernel | dispatches | fetch MB | write MB |", "|---|---:|---:|---:|",
+    ]
+    for k2, n2, f2, w2, _, _ in rows[:16]:
+        lines.append(f"| `{k2.split('(')[0]}` | {n2} | {f2 / 1e6:.1f} | {w2 / 1e6:.2f} |")
+    lines += ["", f"Source hash (sha256 of {', '.join(ATTN_SOURCES)}) at measurement: "
+              f"`{summary['source_sha256']}`; `bench.py` reports `traffic` only while it matches."]
+    with open(base + ".md", "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {base}.json/.md: {(fb + wb) / 1e6:.2f} MB per launch ({100 * (fb + wb) / alg:.1f}% of algorithmic)")
+
+
+def summarize_stats(stats_dir, wl_name, steps):
+    """Kernel time table from rocprofv3 --kernel-trace --stats."""
+    rows = _csv_rows(stats_dir, "kernel_stats.csv")
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    cmd = (f"rocprofv3 --kernel-trace --stats -d gpurun_out/prof -o bench --output-format csv -- python -u bench.py "
+           f"--steps {steps} --warmup 0 --no-cpu-baseline --workload {wl_name}")
+    lines = [f"# Kernel times: bench.py on {wl_name}", "", "Commands (one MI355X, repo root):", "", "```", cmd,
+             f"python bench.py --summarize-stats gpurun_out/prof --workload {wl_name} --steps {steps}", "```", "",
+             f"{steps} step(s), no warm-up: one prefill of the batch plus its decode steps.", "",
+             "| kernel | calls | total ms | mean us | share |", "|---|---:|---:|---:|---:|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        t = float(r["TotalDurationNs"])
+        lines.append(f"| `{r['Name'].split('(')[0]}` | {r['Calls']} | {t / 1e6:.2f} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{100 * t / total:.1f}% |")
+    path = os.path.join(ROOT, "profiles", f"bench_{wl_name}_kernel_stats.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print(f"wrote {path}")
 
 
 def measured_traffic(name):
@@ -88,6 +216,12 @@ def cpu_baseline(wl, shape, weights, prompts, decode_steps=8):
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters, args.workload, args.copy_mb or 512)
+        return
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats, args.workload, args.steps)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(data-parallel sharding by sequence is described in DESIGN.md but not built).", file=sys.stderr)
@@ -129,6 +263,7 @@ def main():
     # kernel classes timed live over the timed region: the prefill's gate/up GEMM and the
     # decode steps' attention
     K_ROWS, K_GATEUP = 5, 8
+    TIME_EVERY = 16
 
     def one_step(phase_times=None):
         timed = phase_times is not None
@@ -138,11 +273,16 @@ def main():
         s.prefill([0] * S, [P] * S, tokens, tbl, B.DEC_LOGITS_LAST, logits=last, next_tokens=hist[0])
         if timed:
             ev[1].record()
-            B.dec_timing_enable(s.ctx, 1 << K_ROWS)
-        for t in range(steps):
-            s.decode_step(positions[t], tbl, tokens_device=hist[t], logits=logits, next_tokens=hist[t + 1])
-        if timed:
             B.dec_timing_enable(s.ctx, 0)
+        for t in range(steps):
+            # the attention launches of every TIME_EVERY-th decode step are timed (a timed launch
+            # records its events at the kernel's own start and end, which costs a little)
+            if timed and t % TIME_EVERY == 0:
+                B.dec_timing_enable(s.ctx, 1 << K_ROWS)
+            s.decode_step(positions[t], tbl, tokens_device=hist[t], logits=logits, next_tokens=hist[t + 1])
+            if timed and t % TIME_EVERY == 0:
+                B.dec_timing_enable(s.ctx, 0)
+        if timed:
             ev[2].record()
             phase_times.append(None)
 
@@ -177,9 +317,9 @@ def main():
     # (context length) x H_kv x D x 2 (K, V) x 2 bytes.
     kv_el = 2 if shape.kv_dtype == "f16" else 4
     per_key = shape.n_kv_heads * shape.head_dim * 2 * kv_el
-    bytes_per_step_layer = [S * (P + t + 1) * per_key for t in range(steps)]
+    bytes_per_step_layer = [S * (P + t + 1) * per_key for t in range(0, steps, TIME_EVERY)]
     rows_launch_bytes = float(np.mean(bytes_per_step_layer))
-    rows_launches_expected = args.steps * steps * shape.n_layers
+    rows_launches_expected = args.steps * len(bytes_per_step_layer) * shape.n_layers
     rows_avg_ms = rows_ms / max(rows_n, 1)
     achieved = rows_launch_bytes / (rows_avg_ms * 1e-3) / 1e9
     # gate/up GEMM of the prefill: 2 * M * (2 ff) * d flops per launch

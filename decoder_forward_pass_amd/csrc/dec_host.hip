@@ -359,6 +359,15 @@ int upload_meta(dec_ctx* ctx, hipStream_t st, int32_t S, const int32_t* start, c
   return DEC_OK;
 }
 
+}  // namespace
+
+LaunchTiming& dec::launch_timing() {
+  static thread_local LaunchTiming t;
+  return t;
+}
+
+namespace {
+
 hipEvent_t timing_event(dec_ctx* ctx) {
   if (!ctx->timing.pool.empty()) {
     hipEvent_t e = ctx->timing.pool.back();
@@ -370,19 +379,25 @@ hipEvent_t timing_event(dec_ctx* ctx) {
   return e;
 }
 
-// Record the start event of a timed launch; returns false when the class is not timed.
-bool timing_begin(dec_ctx* ctx, int cls, hipStream_t st, hipEvent_t* start) {
+// Start of a timed launch: take two events, record the first on the stream and hand both to
+// the launcher, which records them at the kernel's own start and end when it launches through
+// launch_kernel (the later record supersedes the first). Returns false when the class is not
+// timed.
+bool timing_begin(dec_ctx* ctx, int cls, hipStream_t st, hipEvent_t* start, hipEvent_t* stop) {
   if (!(ctx->timing.mask & (1u << cls))) return false;
   *start = timing_event(ctx);
-  if (!*start) return false;
+  *stop = *start ? timing_event(ctx) : nullptr;
+  if (!*stop) return false;
   (void)hipEventRecord(*start, st);
+  launch_timing() = LaunchTiming{*start, *stop, false};
   return true;
 }
 
-void timing_end(dec_ctx* ctx, int cls, hipStream_t st, hipEvent_t start) {
-  hipEvent_t stop = timing_event(ctx);
-  if (!stop) return;
-  (void)hipEventRecord(stop, st);
+// End of a timed launch: a launcher that did not take the events gets the stop recorded after it.
+void timing_end(dec_ctx* ctx, int cls, hipStream_t st, hipEvent_t start, hipEvent_t stop) {
+  LaunchTiming& lt = launch_timing();
+  if (!lt.used) (void)hipEventRecord(stop, st);
+  lt = LaunchTiming{};
   ctx->timing.rec[cls].push_back({start, stop});
 }
 
@@ -393,12 +408,12 @@ void timing_end(dec_ctx* ctx, int cls, hipStream_t st, hipEvent_t start) {
   } while (0)
 
 // A launch of kernel class `cls`, bracketed by events when that class is timed.
-#define TLAUNCH(cls, expr)                                 \
-  do {                                                     \
-    hipEvent_t t0_ = nullptr;                              \
-    const bool timed_ = timing_begin(ctx, cls, st, &t0_);  \
-    LAUNCH(expr);                                          \
-    if (timed_) timing_end(ctx, cls, st, t0_);             \
+#define TLAUNCH(cls, expr)                                         \
+  do {                                                             \
+    hipEvent_t t0_ = nullptr, t1_ = nullptr;                       \
+    const bool timed_ = timing_begin(ctx, cls, st, &t0_, &t1_);    \
+    LAUNCH(expr);                                                  \
+    if (timed_) timing_end(ctx, cls, st, t0_, t1_);                \
   } while (0)
 
 // The forward pass over the uploaded batch: embedding, layers, final norm + LM head, argmax.

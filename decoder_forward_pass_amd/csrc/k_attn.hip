@@ -364,9 +364,11 @@ __global__ __launch_bounds__(1024) void attn_decode_kernel(QkRopeArgs qk, AttnRo
       float p1[8], p2[8];
 #pragma unroll
       for (int p = 0; p < 8; ++p) {
-        const float* sp = src + (int64_t)min(p, qk.parts - 1) * qk.part_stride;
-        p1[p] = sp[lane];
-        p2[p] = sp[lane + half];
+        if (p < qk.parts) {
+          const float* sp = src + (int64_t)p * qk.part_stride;
+          p1[p] = sp[lane];
+          p2[p] = sp[lane + half];
+        }
       }
       x1 = p1[0];
       x2 = p2[0];
@@ -521,9 +523,9 @@ template <typename KVT, int D, int GROUP>
 static void decode_launch(const QkRopeArgs& qk, const AttnRowsArgs& a, void* o, bool bf16_out, hipStream_t s) {
   dim3 g(a.b.n_rows * a.n_kv_heads);
   if (bf16_out)
-    attn_decode_kernel<KVT, D, GROUP, true><<<g, 1024, 0, s>>>(qk, a, o);
+    launch_kernel(attn_decode_kernel<KVT, D, GROUP, true>, g, dim3(1024), 0, s, qk, a, o);
   else
-    attn_decode_kernel<KVT, D, GROUP, false><<<g, 1024, 0, s>>>(qk, a, o);
+    launch_kernel(attn_decode_kernel<KVT, D, GROUP, false>, g, dim3(1024), 0, s, qk, a, o);
 }
 
 template <typename KVT, int D>
@@ -819,9 +821,9 @@ static hipError_t prefill_launch(const AttnPrefillArgs& a, dim3 g, hipStream_t s
     attr = true;
   }
   if (a.out_bf16)
-    attn_prefill_kernel<D, G, true><<<g, 256 * G, lds, s>>>(a);
+    launch_kernel(attn_prefill_kernel<D, G, true>, g, dim3(256 * G), (uint32_t)lds, s, a);
   else
-    attn_prefill_kernel<D, G, false><<<g, 256 * G, lds, s>>>(a);
+    launch_kernel(attn_prefill_kernel<D, G, false>, g, dim3(256 * G), (uint32_t)lds, s, a);
   return hipGetLastError();
 }
 

@@ -14,6 +14,8 @@
 // block ("Candle model runner" 2.4, silu on the gate only).
 #include "kernels.h"
 
+#include <algorithm>
+
 namespace dec {
 
 template <int WF, int EPI>
@@ -215,9 +217,9 @@ template <int WF>
 static hipError_t gemm_epi(int epi, const GemmArgs& a, hipStream_t s) {
   dim3 g((a.N + 63) / 64, (a.M + 63) / 64), b(256);
   switch (epi) {
-    case EPI_STORE: gemm_tile64<WF, EPI_STORE><<<g, b, 0, s>>>(a); break;
-    case EPI_RESID: gemm_tile64<WF, EPI_RESID><<<g, b, 0, s>>>(a); break;
-    case EPI_SWIGLU: gemm_tile64<WF, EPI_SWIGLU><<<g, b, 0, s>>>(a); break;
+    case EPI_STORE: launch_kernel(gemm_tile64<WF, EPI_STORE>, g, b, 0, s, a); break;
+    case EPI_RESID: launch_kernel(gemm_tile64<WF, EPI_RESID>, g, b, 0, s, a); break;
+    case EPI_SWIGLU: launch_kernel(gemm_tile64<WF, EPI_SWIGLU>, g, b, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -642,13 +644,14 @@ hipError_t launch_gemm_decode_parts(int wdtype, const GemmArgs& a, int64_t part_
 }
 
 // ---- decode LM head ---------------------------------------------------------------------------
-// logits = RMSNorm(x) . E^T for the decode rows (M <= 64). One block of 16 waves covers 256
-// vocabulary columns: it normalises the M residual rows once (final gain; sum of squares over
-// the full row, added per thread in order and then by a fixed butterfly) into bf16 rows in
-// LDS, then each wave streams its 16 rows of E over the whole K in ascending order -- the same
-// per-element MFMA sequence as the tile GEMM -- with the next 8 k-steps of weight fragments
-// loaded while the current ones are consumed. E is read once per step; the normalised rows
-// cost one LDS fill per 256 columns.
+// logits = RMSNorm(x) . E^T for the decode rows (M <= 64). A fixed grid of blocks of 16 waves:
+// each block normalises the M residual rows once (final gain; sum of squares over the full row,
+// added per thread in order and then by a fixed butterfly) into bf16 rows in LDS, then streams
+// its contiguous share of the vocabulary in tiles of 16 rows of E, the waves taking the tiles in
+// turn. A wave's tiles form one stream of weight-fragment groups (G k-steps each), the next
+// group loaded while the current one feeds the MFMAs, across tile boundaries too. Every logit is
+// accumulated over the whole K in ascending order -- the same per-element MFMA sequence for any
+// number of rows. E is read once per step.
 
 template <int WF, int MT>
 __global__ __launch_bounds__(1024) void lmhead_decode(GemmArgs a) {
@@ -684,47 +687,57 @@ __global__ __launch_bounds__(1024) void lmhead_decode(GemmArgs a) {
     }
   }
   __syncthreads();
-  const int n0 = blockIdx.x * 256 + wave * 16;
-  if (n0 >= a.N) return;
+  // this block's tiles of 16 vocabulary rows: [t0, t1); wave w takes t0 + w, t0 + w + 16, ...
   const WMat E = a.seg[0];
-  const int brow = min(n0 + (lane & 15), E.rows - 1);
+  const int ntiles = (a.N + 15) / 16;
+  const int t0 = (int)((int64_t)ntiles * blockIdx.x / gridDim.x);
+  const int t1 = (int)((int64_t)ntiles * (blockIdx.x + 1) / gridDim.x);
+  const int mine = t0 + wave < t1 ? (t1 - 1 - t0 - wave) / 16 + 1 : 0;
+  constexpr int G = 8;  // k-steps per group of weight loads
+  const int ksteps = K / 32, gpt = (ksteps + G - 1) / G, total = mine * gpt;
   const int kl = (lane >> 4) * 8;
-  const int ksteps = K / 32;
+  auto load_group = [&](int j, BRaw<WF> (&dst)[G]) {
+    const int tile = t0 + wave + (j / gpt) * 16, kg = (j % gpt) * G;
+    const int brow = min(tile * 16 + (lane & 15), E.rows - 1);
+#pragma unroll
+    for (int i = 0; i < G; ++i) dst[i] = load_b_raw<WF>(E, brow, K, min(kg + i, ksteps - 1) * 32 + kl);
+  };
   f32x4 acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  constexpr int G = 8;  // k-steps per batch of weight loads
   BRaw<WF> cur[G], nxt[G];
-#pragma unroll
-  for (int i = 0; i < G; ++i) cur[i] = load_b_raw<WF>(E, brow, K, min(i, ksteps - 1) * 32 + kl);
-  for (int kb = 0; kb < ksteps; kb += G) {
-    if (kb + G < ksteps) {
-#pragma unroll
-      for (int i = 0; i < G; ++i) nxt[i] = load_b_raw<WF>(E, brow, K, min(kb + G + i, ksteps - 1) * 32 + kl);
-    }
+  if (total > 0) load_group(0, cur);
+  for (int j = 0; j < total; ++j) {
+    if (j + 1 < total) load_group(j + 1, nxt);
+    const int kg = (j % gpt) * G;
 #pragma unroll
     for (int i = 0; i < G; ++i) {
-      if (kb + i < ksteps) {
+      if (kg + i < ksteps) {
         const bf16x8 bf = b_frag<WF>(cur[i]);
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           const bf16x8 af = __builtin_bit_cast(bf16x8, *(const u32x4*)(s_h + (mt * 16 + (lane & 15)) * KS +
-                                                                       (kb + i) * 32 + kl));
+                                                                       (kg + i) * 32 + kl));
           acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc[mt], 0, 0, 0);
         }
+      }
+    }
+    if (j % gpt == gpt - 1) {  // the tile is complete: store its logits, start the next one
+      const int tile = t0 + wave + (j / gpt) * 16;
+      const int ncol = tile * 16 + (lane & 15);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = mt * 16 + (lane >> 4) * 4 + r;
+          if (m < M && ncol < a.N) ((float*)a.C)[(int64_t)m * a.ldc + ncol] = acc[mt][r];
+        }
+        acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
 #pragma unroll
     for (int i = 0; i < G; ++i) cur[i] = nxt[i];
   }
-  const int ncol = n0 + (lane & 15);
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = mt * 16 + (lane >> 4) * 4 + r;
-      if (m < M && ncol < a.N) ((float*)a.C)[(int64_t)m * a.ldc + ncol] = acc[mt][r];
-    }
 }
 
 template <int WF, int MT>
@@ -737,7 +750,16 @@ static hipError_t lmhead_go(const GemmArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr = true;
   }
-  lmhead_decode<WF, MT><<<(a.N + 255) / 256, 1024, lds, s>>>(a);
+  // one block per compute unit, or fewer when the vocabulary is small
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+  }
+  const int blocks = std::max(1, std::min(cus, (a.N + 255) / 256));
+  launch_kernel(lmhead_decode<WF, MT>, dim3(blocks), dim3(1024), (uint32_t)lds, s, a);
   return hipGetLastError();
 }
 
@@ -763,9 +785,9 @@ template <int WF, int MT, int NKS>
 static hipError_t gemm_decode_go(int epi, const GemmArgs& a, int nw, hipStream_t s) {
   dim3 g((a.N + 15) / 16, (a.M + 16 * MT - 1) / (16 * MT)), b(512);
   switch (epi) {
-    case EPI_STORE: gemm_decode<WF, EPI_STORE, MT, NKS><<<g, b, 0, s>>>(a, nw); break;
-    case EPI_RESID: gemm_decode<WF, EPI_RESID, MT, NKS><<<g, b, 0, s>>>(a, nw); break;
-    case EPI_SWIGLU: gemm_decode<WF, EPI_SWIGLU, MT, NKS><<<g, b, 0, s>>>(a, nw); break;
+    case EPI_STORE: launch_kernel(gemm_decode<WF, EPI_STORE, MT, NKS>, g, b, 0, s, a, nw); break;
+    case EPI_RESID: launch_kernel(gemm_decode<WF, EPI_RESID, MT, NKS>, g, b, 0, s, a, nw); break;
+    case EPI_SWIGLU: launch_kernel(gemm_decode<WF, EPI_SWIGLU, MT, NKS>, g, b, 0, s, a, nw); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -389,7 +389,7 @@ static hipError_t big_go(const GemmArgs& a, const QkRopeArgs& qk, hipStream_t s)
   }
   const int mt = (a.M + kBT - 1) / kBT;
   const int nt = EPI == EPI_SWIGLU ? (a.N + 127) / 128 : (a.N + kBT - 1) / kBT;
-  gemm_big<WF, EPI, D, KV_F16><<<mt * nt, 512, kBigLds, s>>>(a, qk);
+  launch_kernel(gemm_big<WF, EPI, D, KV_F16>, dim3(mt * nt), dim3(512), (uint32_t)kBigLds, s, a, qk);
   return hipGetLastError();
 }
 
