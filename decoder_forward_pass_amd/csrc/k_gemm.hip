@@ -295,19 +295,30 @@ __device__ __forceinline__ bf16x8 b_frag(const BRaw<WF>& r) {
 
 }  // namespace
 
-template <int WF, int EPI, int MT, int NKS>
+// LDSA: the block's activation rows are staged in LDS by direct-to-LDS loads instead of being
+// loaded into registers by each wave. Those rows are the same for every block (they come from
+// L2) and the direct path moves them at several times the rate of vector loads. Row r of the
+// staged tile keeps its 16-byte chunk c at position c ^ (r % 16), so the 16 rows of a fragment
+// read fall on distinct banks; after the products the same LDS holds the wave partials. The
+// K split, the order of the additions and the arithmetic are those of the register path.
+template <int WF, int EPI, int MT, int NKS, bool LDSA>
 __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
   // STORE / SWIGLU read the float32 residual and normalise it on the fly (RMSNorm fused);
   // RESID reads a bf16 activation and writes the sums of squares of the new residual.
   constexpr bool NORM = EPI != EPI_RESID;
   constexpr int NB = EPI == EPI_SWIGLU ? 2 : 1;
-  __shared__ float red[kDecWaves][NB][MT][4][64];
+  constexpr int ES = NORM ? 4 : 2;  // bytes per activation element
+  constexpr int RED = kDecWaves * NB * MT * 4 * 64;
+  __shared__ float red_s[LDSA ? 1 : RED];
+  extern __shared__ __attribute__((aligned(16))) uint8_t s_dyn[];  // LDSA: [16 MT][K] staged, then partials
+  float* red = LDSA ? (float*)s_dyn : red_s;  // [wave][nb][mt][r][lane]
   __shared__ float s_inv[16 * MT];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n0 = blockIdx.x * 16;
   const int m0 = blockIdx.y * 16 * MT;
   const int M = a.M, K = a.K;
+  const int cpr = K * ES / 16;  // 16-byte chunks per activation row
 
   WMat bm[NB];
   int br0;
@@ -339,7 +350,7 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
   const int kl = (lane >> 4) * 8;
   const int k0 = wave * NKS * 32 + kl;
   BRaw<WF> braw[NB][NKS];
-  u32x4 araw[MT][NKS][NORM ? 2 : 1];
+  u32x4 araw[LDSA ? 1 : MT][LDSA ? 1 : NKS][NORM ? 2 : 1];
   float4 graw[NORM ? NKS : 1][2];
   float4 sraw[NORM ? 4 : 1];
   if (active) {
@@ -347,20 +358,22 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
     for (int i = 0; i < NKS; ++i)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) braw[nb][i] = load_b_raw<WF>(bm[nb], brow, K, k0 + i * 32);
+    if constexpr (!LDSA) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int arow = min(m0 + mt * 16 + (lane & 15), M - 1);
-      if constexpr (NORM) {
-        const float* ap = (const float*)a.A + (int64_t)arow * a.lda + k0;
+      for (int mt = 0; mt < MT; ++mt) {
+        const int arow = min(m0 + mt * 16 + (lane & 15), M - 1);
+        if constexpr (NORM) {
+          const float* ap = (const float*)a.A + (int64_t)arow * a.lda + k0;
 #pragma unroll
-        for (int i = 0; i < NKS; ++i) {
-          araw[mt][i][0] = *(const u32x4*)(ap + i * 32);
-          araw[mt][i][1] = *(const u32x4*)(ap + i * 32 + 4);
+          for (int i = 0; i < NKS; ++i) {
+            araw[mt][i][0] = *(const u32x4*)(ap + i * 32);
+            araw[mt][i][1] = *(const u32x4*)(ap + i * 32 + 4);
+          }
+        } else {
+          const uint16_t* ap = (const uint16_t*)a.A + (int64_t)arow * a.lda + k0;
+#pragma unroll
+          for (int i = 0; i < NKS; ++i) araw[mt][i][0] = *(const u32x4*)(ap + i * 32);
         }
-      } else {
-        const uint16_t* ap = (const uint16_t*)a.A + (int64_t)arow * a.lda + k0;
-#pragma unroll
-        for (int i = 0; i < NKS; ++i) araw[mt][i][0] = *(const u32x4*)(ap + i * 32);
       }
     }
     if constexpr (NORM) {
@@ -369,6 +382,16 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
         graw[i][0] = *(const float4*)(a.gain + k0 + i * 32);
         graw[i][1] = *(const float4*)(a.gain + k0 + i * 32 + 4);
       }
+    }
+  }
+  if constexpr (LDSA) {
+    // every wave stages 1 KB pieces (64 chunk slots, row-major over the swizzled tile)
+    const int nins = 16 * MT * cpr / 64;
+    for (int j = wave; j < nins; j += kDecWaves) {
+      const int slot = j * 64 + lane, r = slot / cpr, pc = slot % cpr, c = pc ^ (r & 15);
+      const uint8_t* src = (const uint8_t*)a.A + ((int64_t)min(m0 + r, M - 1) * a.lda) * ES + c * 16;
+      __builtin_amdgcn_global_load_lds((const void*)src, (void __attribute__((address_space(3)))*)(s_dyn + j * 1024),
+                                       16, 0, 0);
     }
   }
   // the rows' sums of squares: 4 threads per row, each adding a quarter of the row's K/16
@@ -397,10 +420,20 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
       s += dpp<kDppXor2>(s);
       if ((threadIdx.x & 3) == 0) s_inv[threadIdx.x >> 2] = 1.0f / sqrtf(s / (float)K + a.eps);
     }
+  }
+  if constexpr (LDSA) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's staging loads have landed
+    __syncthreads();
+  } else if constexpr (NORM) {
     __syncthreads();
   }
+  // fragment of activation row r (local), 8 values from k, from the staged tile
+  auto lds_frag = [&](int r, int k, int h) -> u32x4 {
+    const int c = (k * ES) / 16 + h;
+    return *(const u32x4*)(s_dyn + ((int64_t)r * cpr + (c ^ (r & 15))) * 16);
+  };
+  f32x4 acc[NB][MT];
   if (active) {
-    f32x4 acc[NB][MT];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
@@ -415,10 +448,13 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
         bf16x8 af;
         if constexpr (NORM) {
           const float inv = s_inv[mt * 16 + (lane & 15)];
+          u32x4 xr[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) xr[h] = LDSA ? lds_frag(mt * 16 + (lane & 15), k0 + i * 32, h) : araw[LDSA ? 0 : mt][LDSA ? 0 : i][h];
           u32x4 w;
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
-            const float* xv = (const float*)&araw[mt][i][h];
+            const float* xv = (const float*)&xr[h];
             const float* gv = (const float*)&graw[i][h];
             w[2 * h] = (uint32_t)f32_to_bf16_bits(xv[0] * inv * gv[0]) |
                        ((uint32_t)f32_to_bf16_bits(xv[1] * inv * gv[1]) << 16);
@@ -427,19 +463,23 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
           }
           af = __builtin_bit_cast(bf16x8, w);
         } else {
-          af = __builtin_bit_cast(bf16x8, araw[mt][i][0]);
+          af = __builtin_bit_cast(bf16x8, LDSA ? lds_frag(mt * 16 + (lane & 15), k0 + i * 32, 0)
+                                               : araw[LDSA ? 0 : mt][LDSA ? 0 : i][0]);
         }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
           acc[nb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[nb], acc[nb][mt], 0, 0, 0);
       }
     }
+  }
+  if constexpr (LDSA) __syncthreads();  // the staged tile is done with; the partials reuse it
+  if (active) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red[wave][nb][mt][r][lane] = acc[nb][mt][r];
+        for (int r = 0; r < 4; ++r) red[(((wave * NB + nb) * MT + mt) * 4 + r) * 64 + lane] = acc[nb][mt][r];
   }
   __syncthreads();
 
@@ -451,8 +491,8 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
     float v[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      float s = red[0][nb][mt][r][sl];
-      for (int w = 1; w < nw; ++w) s += red[w][nb][mt][r][sl];
+      float s = red[((nb * MT + mt) * 4 + r) * 64 + sl];
+      for (int w = 1; w < nw; ++w) s += red[(((w * NB + nb) * MT + mt) * 4 + r) * 64 + sl];
       v[nb] = s;
     }
     const int m = m0 + mt * 16 + (sl >> 4) * 4 + r;
@@ -781,16 +821,43 @@ hipError_t launch_lmhead_decode(int wdtype, const GemmArgs& a, hipStream_t s) {
   return lmhead_go<DEC_UINT4_G32, 4>(a, s);
 }
 
-template <int WF, int MT, int NKS>
-static hipError_t gemm_decode_go(int epi, const GemmArgs& a, int nw, hipStream_t s) {
-  dim3 g((a.N + 15) / 16, (a.M + 16 * MT - 1) / (16 * MT)), b(512);
-  switch (epi) {
-    case EPI_STORE: launch_kernel(gemm_decode<WF, EPI_STORE, MT, NKS>, g, b, 0, s, a, nw); break;
-    case EPI_RESID: launch_kernel(gemm_decode<WF, EPI_RESID, MT, NKS>, g, b, 0, s, a, nw); break;
-    case EPI_SWIGLU: launch_kernel(gemm_decode<WF, EPI_SWIGLU, MT, NKS>, g, b, 0, s, a, nw); break;
-    default: return hipErrorInvalidValue;
+// LDS bytes of the staged-activation path (activation tile, or the wave partials if larger)
+template <int EPI, int MT>
+static size_t decode_lds_bytes(int K) {
+  const size_t act = (size_t)16 * MT * K * (EPI == EPI_RESID ? 2 : 4);
+  const size_t part = (size_t)kDecWaves * (EPI == EPI_SWIGLU ? 2 : 1) * MT * 4 * 64 * 4;
+  return act > part ? act : part;
+}
+
+template <int WF, int EPI, int MT, int NKS>
+static hipError_t gemm_decode_launch(const GemmArgs& a, int nw, dim3 g, hipStream_t s) {
+  const int es = EPI == EPI_RESID ? 2 : 4;
+  const size_t lds = decode_lds_bytes<EPI, MT>(a.K);
+  // staged path: chunks per row a multiple of 16 (the swizzle) and the tile within 128 KB
+  if ((a.K * es / 16) % 16 == 0 && lds <= 128 * 1024) {
+    static bool attr = false;
+    if (!attr) {
+      hipError_t e = hipFuncSetAttribute((const void*)gemm_decode<WF, EPI, MT, NKS, true>,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
+      if (e != hipSuccess) return e;
+      attr = true;
+    }
+    launch_kernel(gemm_decode<WF, EPI, MT, NKS, true>, g, dim3(512), (uint32_t)lds, s, a, nw);
+  } else {
+    launch_kernel(gemm_decode<WF, EPI, MT, NKS, false>, g, dim3(512), 0, s, a, nw);
   }
   return hipGetLastError();
+}
+
+template <int WF, int MT, int NKS>
+static hipError_t gemm_decode_go(int epi, const GemmArgs& a, int nw, hipStream_t s) {
+  dim3 g((a.N + 15) / 16, (a.M + 16 * MT - 1) / (16 * MT));
+  switch (epi) {
+    case EPI_STORE: return gemm_decode_launch<WF, EPI_STORE, MT, NKS>(a, nw, g, s);
+    case EPI_RESID: return gemm_decode_launch<WF, EPI_RESID, MT, NKS>(a, nw, g, s);
+    case EPI_SWIGLU: return gemm_decode_launch<WF, EPI_SWIGLU, MT, NKS>(a, nw, g, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int WF, int MT>
