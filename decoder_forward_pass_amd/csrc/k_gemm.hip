@@ -889,10 +889,15 @@ bool gemm_decode_supported(int wdtype, int K) {
 
 hipError_t launch_gemm_decode(int wdtype, int epi, const GemmArgs& a, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  // blocks of 16 rows when M <= 16, when the product has few column groups (twice the blocks
+  // then share the weights), or when only a 16-row activation tile fits in LDS; a row's result
+  // is the same either way
+  const size_t tile32 = (size_t)32 * a.K * (epi == EPI_RESID ? 2 : 4);
+  const bool rows16 = a.M <= 16 || (a.N + 15) / 16 < 128 || (tile32 > 128 * 1024 && tile32 / 2 <= 128 * 1024);
   if (wdtype == DEC_BF16)
-    return a.M <= 16 ? gemm_decode_nks<DEC_BF16, 1>(epi, a, s) : gemm_decode_nks<DEC_BF16, 2>(epi, a, s);
+    return rows16 ? gemm_decode_nks<DEC_BF16, 1>(epi, a, s) : gemm_decode_nks<DEC_BF16, 2>(epi, a, s);
   if (wdtype == DEC_UINT4_G32)
-    return a.M <= 16 ? gemm_decode_nks<DEC_UINT4_G32, 1>(epi, a, s) : gemm_decode_nks<DEC_UINT4_G32, 2>(epi, a, s);
+    return rows16 ? gemm_decode_nks<DEC_UINT4_G32, 1>(epi, a, s) : gemm_decode_nks<DEC_UINT4_G32, 2>(epi, a, s);
   return hipErrorInvalidValue;
 }
 
