@@ -137,14 +137,12 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnRowsArgs a) {
       }
     }
   }
+  const auto add = [](float x, float y) { return x + y; };
 #pragma unroll
-  for (int o = LPK; o < 64; o <<= 1) {
+  for (int i = 0; i < GROUP; ++i) {
+    l[i] = xor_reduce<LPK>(l[i], add);
 #pragma unroll
-    for (int i = 0; i < GROUP; ++i) {
-      l[i] += __shfl_xor(l[i], o, 64);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[i][e] += __shfl_xor(acc[i][e], o, 64);
-    }
+    for (int e = 0; e < EPL; ++e) acc[i][e] = xor_reduce<LPK>(acc[i][e], add);
   }
   if (grp == 0) {
 #pragma unroll
@@ -264,21 +262,27 @@ hipError_t launch_attn_combine(const float* partial, int n_rows, int n_heads, in
 // A decode step has one query row per sequence. The workgroup's 16 waves take fixed chunks of
 // the row's keys in turn: wave w handles chunks w, w+16, ... in increasing order, keeping a
 // running (max, sum, accumulator) per query head. A chunk is KPI keys per wave-wide load times
-// DKPG loads; the chunk's block ids arrive in one load (lane i: the chunk's i-th block; the
-// next chunk's ids are requested before the current chunk is consumed), and all K and V
-// loads of a chunk are issued before any arithmetic (keys past the context read a valid slot
-// of the last block and are masked). The 16 wave states are merged in wave order through
-// LDS and the output row is written: no partials leave the workgroup. The split depends only
-// on the row's context length, so the result does not depend on the other sequences.
+// DKPG loads; the chunk's block ids arrive in one load (lane i: the chunk's i-th block), and
+// all K and V loads of a chunk are issued before any arithmetic (keys past the context read a
+// valid slot of the last block and are masked). Each wave requests its first two chunks before
+// the q/k prologue, so the pool streams while the new query, key and value are formed; the
+// wave whose chunk holds the new position takes that key and value from LDS instead of the
+// pool slot it read early. The 16 wave states are merged in wave order through LDS and the
+// output row is written: no partials leave the workgroup. The split depends only on the row's
+// context length, so the result does not depend on the other sequences.
 
 template <typename KVT, int D, int GROUP>
 struct DecodeGeom {
   static constexpr int EPL = 16 / (int)sizeof(KVT);
   static constexpr int LPK = D / EPL;
   static constexpr int KPI = 64 / LPK;
-  static constexpr int DKPG = (8 / GROUP) > 1 ? 8 / GROUP : 1;  // loads per chunk
+  static constexpr int DKPG = 2;                   // loads per chunk
+  static constexpr int NBUF = GROUP == 4 ? 2 : 3;  // chunk register sets (chunks in flight)
+  static constexpr bool QREG = GROUP <= 2;         // query heads held in registers
   static constexpr int CHUNK = DKPG * KPI;
-  static constexpr int NWV = 16;
+  // waves per workgroup: 16 of at most 128 registers each, or 8 of 256 when eight query heads'
+  // accumulators would not fit in 128
+  static constexpr int NWV = GROUP >= 8 ? 8 : 16;
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -287,129 +291,241 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 // here into a cast of element 0)
 __device__ __forceinline__ half2v as_half2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
 
+template <typename F, int... I>
+__device__ __forceinline__ void unrolled_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void unrolled(F&& f) {  // f(0), ..., f(N - 1) with constant indices
+  unrolled_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// v op v[lane ^ O] for every lane, with no lane-address registers: for O = 16 and 32 the gfx950
+// row swaps hand each lane the pair {v[lane], v[lane ^ O]}, for smaller O a bit-mask swizzle
+// fetches the partner (op is commutative, so either order gives the same bits)
+template <int O, typename Op>
+__device__ __forceinline__ float xor_combine(float v, Op op) {
+  const uint32_t u = __float_as_uint(v);
+  if constexpr (O == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  } else if constexpr (O == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  } else {
+    static_assert(O >= 1 && O < 16, "lane distance");
+    return op(v, __uint_as_float(__builtin_amdgcn_ds_swizzle((int)u, 0x1F | (O << 10))));
+  }
+}
+template <int FROM, typename Op>
+__device__ __forceinline__ float xor_reduce(float v, Op op) {  // over lane bits FROM..32
+  if constexpr (FROM < 64) return xor_reduce<FROM * 2>(xor_combine<FROM>(v, op), op);
+  return v;
+}
+
+// a 16-byte load at a wave-uniform address plus a 32-bit lane offset, through a raw buffer
+// descriptor held in scalar registers (no 64-bit lane addresses; the offsets used here are a
+// few kilobytes, far inside the descriptor's range)
+// With range 0 the load returns zeros without a memory access.
+__device__ __forceinline__ u32x4 load_uniform_base(const char* base, uint32_t lane_off, int range = 0x7fffffff) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, range, 0x00020000);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)lane_off, 0, 0);
+}
+
 template <typename KVT, int D, int GROUP, bool BF16_OUT>
-__global__ __launch_bounds__(1024) void attn_decode_kernel(QkRopeArgs qk, AttnRowsArgs a, void* out) {
+__global__ __launch_bounds__((64 * DecodeGeom<KVT, D, GROUP>::NWV)) void attn_decode_kernel(QkRopeArgs qk,
+                                                                                            AttnRowsArgs a, void* out) {
   using G = DecodeGeom<KVT, D, GROUP>;
   constexpr int EPL = G::EPL, LPK = G::LPK, KPI = G::KPI, KPG = G::DKPG, CHUNK = G::CHUNK, NWV = G::NWV;
+  constexpr bool F16 = sizeof(KVT) == 2;
   static_assert(CHUNK <= 64 * 16, "a chunk spans at most 64 blocks of 16 positions");
-  __shared__ float s_m[NWV][GROUP], s_l[NWV][GROUP];
+  // per-wave states (max, sum, accumulator); state NWV is the new key's
+  __shared__ float s_m[NWV + 1][GROUP], s_l[NWV + 1][GROUP];
   __shared__ float s_acc[NWV][GROUP][D];
-  __shared__ __attribute__((aligned(16))) KVT s_q[GROUP][D];
+  __shared__ __attribute__((aligned(16))) KVT s_q[GROUP + 2][D];  // query heads, new key, new value
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar math
   const int grp = lane / LPK, sub = lane % LPK;
   const int Hkv = a.n_kv_heads, H = a.n_heads;
   const int row = blockIdx.x / Hkv, kvh = blockIdx.x % Hkv;
   const int pos = a.b.row_pos[row];
-  const int ctx = pos + 1;
-  const int nch = (ctx + CHUNK - 1) / CHUNK;
   const int seq = a.b.row_seq[row];
+  // the pool loop covers the keys before the new position; the new key joins at the merge
+  const int nch = (pos + CHUNK - 1) / CHUNK;
   const int32_t* table = a.b.block_tables + (int64_t)seq * a.b.tbl_stride;
   const int bsh = a.pool.block_shift, bmask = a.pool.block_tokens - 1;
-  const int last_blk = (ctx - 1) >> bsh;
+  const int last_blk = max(pos - 1, 0) >> bsh;
   const int64_t slab = (int64_t)Hkv * a.pool.block_tokens * D;
-  const KVT* kbase = (const KVT*)a.pool.base + (int64_t)a.layer * 2 * a.pool.n_blocks * slab +
-                     (int64_t)kvh * a.pool.block_tokens * D + sub * EPL;
-  const KVT* vbase = kbase + a.pool.n_blocks * slab;
+  // pool addresses: a wave-uniform part (layer, K or V, KV head, block, the load's first slot)
+  // and a 32-bit lane part (the lane group's key within the load, the lane's channels)
+  const char* kbase = (const char*)((const KVT*)a.pool.base + (int64_t)a.layer * 2 * a.pool.n_blocks * slab +
+                                    (int64_t)kvh * a.pool.block_tokens * D);
+  const char* vbase = kbase + a.pool.n_blocks * slab * (int64_t)sizeof(KVT);
+  const uint32_t lane_off = (uint32_t)((grp * D + sub * EPL) * sizeof(KVT));
 
-  // block ids of this wave's chunks (see the chunk loop below), requested before the prologue
-  const int bpc = CHUNK > a.pool.block_tokens ? CHUNK >> bsh : 1;  // blocks per chunk
-  const int cpl = 64 / bpc;                                         // chunks per table load
-  auto load_tab = [&](int base) {
-    const int c = wave + (base + lane / bpc) * NWV;
-    return table[min(((min(c, nch - 1) * CHUNK) >> bsh) + lane % bpc, last_blk)];
-  };
-  int tab_base = 0;
-  int tab = load_tab(0);
+  // The sequence's block table goes to LDS (blocks 0 .. last_blk, at most TCAP of them) while
+  // the prologue runs: range-checked loads, so entries past the last block cost nothing. Its
+  // loads are the wave's first, so the wait for them leaves the later loads in flight.
+  constexpr int TCAP = 4096, TPASS = TCAP / (64 * NWV);
+  __shared__ int32_t s_tbl[TCAP];
+  uint32_t tcopy[TPASS];
+  {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc((void*)table, 0, min(last_blk + 1, TCAP) * 4, 0x00020000);
+#pragma unroll
+    for (int p = 0; p < TPASS; ++p)
+      tcopy[p] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)((p * 64 * NWV + threadIdx.x) * 4), 0, 0);
+  }
+  // block ids of the wave's first chunks (the ones requested before the barrier): lane j holds
+  // block j % bpc of the wave's chunk j / bpc
+  const int bpc = CHUNK > a.pool.block_tokens ? CHUNK >> bsh : 1;  // blocks per chunk (64 / bpc >= NBUF)
+  const int tab = table[min(((min(wave + (lane / bpc) * NWV, max(nch - 1, 0)) * CHUNK) >> bsh) + lane % bpc, last_blk)];
 
-  // Software pipeline: the K and V loads of a wave's next chunk are issued before the current
-  // chunk is consumed, so two chunks are in flight per wave. Block ids come from tab (loaded
-  // before the q/k prologue): lane j holds block j % bpc of the wave's chunk number
-  // tab_base + j / bpc; it is reloaded every 64 / bpc chunks.
-  auto issue = [&](int ci, u32x4 (&kr)[KPG], u32x4 (&vr)[KPG]) {
+  const int nmine = wave < nch ? (nch - 1 - wave) / NWV + 1 : 0;  // chunks of this wave
+  // chunks whose blocks the LDS table holds: the first TCAP * B / (CHUNK * NWV) of each wave
+  const int nmain = min(nmine, (TCAP << bsh) / (CHUNK * NWV));
+  // Requests of chunk ci's K and V rows; SRC picks where the block ids come from: 0 the lanes
+  // of tab (the first chunks), 1 the LDS table, 2 the table in memory (past the LDS table).
+  // With SRC < 2 every call issues the same loads whether or not the wave has chunk ci, so
+  // that the count of loads in flight is the same on every path (the wait before each chunk
+  // then waits for that chunk alone): past nmain the loads have range 0 at a valid address.
+  auto issue = [&](auto src, int ci, u32x4 (&kr)[KPG], u32x4 (&vr)[KPG]) __attribute__((always_inline)) {
+    constexpr int SRC = decltype(src)::value;
+    const bool live = SRC == 2 || ci < nmain;  // wave-uniform
     const int key0 = (wave + ci * NWV) * CHUNK;
-    if (ci >= tab_base + cpl) {  // wave-uniform, rare
-      tab_base += cpl;
-      tab = load_tab(tab_base);
-    }
 #pragma unroll
     for (int kk = 0; kk < KPG; ++kk) {
-      // the KPI keys of one load share a block (B is a multiple of KPI); keys past the context
-      // read a slot of the last block and are masked below
+      // the KPI keys of one load share a block (B is a multiple of KPI); keys from the new
+      // position on read a slot of the last block and are masked below
       const int b = min((key0 + kk * KPI) >> bsh, last_blk);
-      const int64_t off = (int64_t)__builtin_amdgcn_readlane(tab, (ci - tab_base) * bpc + b - (key0 >> bsh)) * slab +
-                          ((key0 + kk * KPI + grp) & bmask) * D;
-      kr[kk] = *(const u32x4*)(kbase + off);
-      vr[kk] = *(const u32x4*)(vbase + off);
+      int blk;
+      if constexpr (SRC == 0)
+        blk = __builtin_amdgcn_readlane(tab, ci * bpc + b - (key0 >> bsh));
+      else if constexpr (SRC == 1)
+        blk = __builtin_amdgcn_readfirstlane(s_tbl[min(b, TCAP - 1)]);
+      else
+        blk = table[b];
+      const int64_t off = ((int64_t)blk * slab + ((key0 + kk * KPI) & bmask) * D) * (int64_t)sizeof(KVT);
+      kr[kk] = load_uniform_base(kbase + (live ? off : 0), lane_off, live ? 0x7fffffff : 0);
+      vr[kk] = load_uniform_base(vbase + (live ? off : 0), lane_off, live ? 0x7fffffff : 0);
     }
   };
-  const int nmine = wave < nch ? (nch - 1 - wave) / NWV + 1 : 0;  // chunks of this wave
-  u32x4 kraw[KPG], vraw[KPG], knext[KPG], vnext[KPG];
-  // A wave's first chunk is requested before the q/k prologue, except the chunk that holds the
-  // new position, which is read after the barrier that publishes the new key and value.
-  const bool early = nmine > 0 && wave != nch - 1;
-  if (early) issue(0, kraw, vraw);
-  constexpr bool F16 = sizeof(KVT) == 2;
-  // The row's new query heads, key and value: wave i < GROUP normalises and rotates query head
-  // kvh*GROUP + i into LDS (in the pool's format, as the q buffer holds it for prefill); wave
-  // GROUP does the key and wave GROUP + 1 copies the value into the pool at (table[pos / B],
-  // pos % B). The barrier makes the pool writes visible to the waves that read the last chunk.
-  if (wave <= GROUP + 1) {
-    const int half = D / 2;
-    const int hh = wave < GROUP ? kvh * GROUP + wave : (wave == GROUP ? H + kvh : H + Hkv + kvh);
-    // the Q|K|V product of the row: the sum of qk.parts partial products, in order
-    const float* src = qk.qkv + (int64_t)row * (H + 2 * Hkv) * D + (int64_t)hh * D;
-    float x1 = 0.f, x2 = 0.f;
+  using FromTab = std::integral_constant<int, 0>;
+  using FromLds = std::integral_constant<int, 1>;
+  using FromMem = std::integral_constant<int, 2>;
+
+  // The row's Q|K|V product (the sum of qk.parts partial products, added in order) gives
+  // GROUP + 2 prologue items: query heads kvh*GROUP + it for it < GROUP, then the key and the
+  // value; wave w takes items w, w + NWV, ... . An item's loads are issued ahead of the wave's
+  // first pool loads, so that they are not queued behind them; the waves without items
+  // request their first NBUF chunks at once.
+  const int half = D / 2;
+  constexpr int NBUF = G::NBUF, NITEM = GROUP + 2;
+  u32x4 kb[NBUF][KPG], vb[NBUF][KPG];
+  struct Item {
+    float p1[8], p2[8];
+    float2 cs;
+    int newblk;
+  };
+  auto item_load = [&](int it, Item& t) __attribute__((always_inline)) {
+    t.cs = make_float2(1.f, 0.f);
+    t.newblk = 0;
     if (lane < half) {
-      float p1[8], p2[8];
+      const int hh = it < GROUP ? kvh * GROUP + it : (it == GROUP ? H + kvh : H + Hkv + kvh);
+      const float* src = qk.qkv + (int64_t)row * (H + 2 * Hkv) * D + (int64_t)hh * D;
 #pragma unroll
       for (int p = 0; p < 8; ++p) {
         if (p < qk.parts) {
           const float* sp = src + (int64_t)p * qk.part_stride;
-          p1[p] = sp[lane];
-          p2[p] = sp[lane + half];
+          t.p1[p] = sp[lane];
+          t.p2[p] = sp[lane + half];
         }
       }
-      x1 = p1[0];
-      x2 = p2[0];
+      if (it <= GROUP) t.cs = qk.rope[(int64_t)pos * half + lane];
+      if (it >= GROUP) t.newblk = table[pos >> bsh];
+    }
+  };
+  // the new query heads, key and value: normalised and rotated (q, k), rounded to the pool's
+  // format into LDS, and the key and value written to the pool at (table[pos / B], pos % B)
+  // for later steps
+  auto item_finish = [&](int it, const Item& t) __attribute__((always_inline)) {
+    float x1 = 0.f, x2 = 0.f;
+    if (lane < half) {
+      x1 = t.p1[0];
+      x2 = t.p2[0];
 #pragma unroll
       for (int p = 1; p < 8; ++p) {
         if (p < qk.parts) {
-          x1 += p1[p];
-          x2 += p2[p];
+          x1 += t.p1[p];
+          x2 += t.p2[p];
         }
       }
     }
-    if (wave <= GROUP) {
-      const float2 cs = lane < half ? qk.rope[(int64_t)pos * half + lane] : make_float2(1.f, 0.f);
-      norm_rope_pair(x1, x2, wave < GROUP ? qk.q_norm : qk.k_norm, cs, lane, D, qk.eps);
-    }
+    if (it <= GROUP) norm_rope_pair(x1, x2, it < GROUP ? qk.q_norm : qk.k_norm, t.cs, lane, D, qk.eps);
     if (lane < half) {
-      KVT* dst;
-      if (wave < GROUP) {
-        dst = s_q[wave];
-      } else {
-        const int64_t blk = table[pos >> bsh];
-        dst = (KVT*)a.pool.base + a.pool.offset(a.layer, wave == GROUP ? 0 : 1, blk, kvh, pos & bmask);
-      }
+      KVT* dst = s_q[it];
+      KVT* pdst = (KVT*)a.pool.base + a.pool.offset(a.layer, it == GROUP ? 0 : 1, t.newblk, kvh, pos & bmask);
       if constexpr (F16) {
-        dst[lane] = f32_to_f16_bits(x1);
-        dst[lane + half] = f32_to_f16_bits(x2);
+        const uint16_t b1 = f32_to_f16_bits(x1), b2 = f32_to_f16_bits(x2);
+        dst[lane] = b1;
+        dst[lane + half] = b2;
+        if (it >= GROUP) {
+          pdst[lane] = b1;
+          pdst[lane + half] = b2;
+        }
       } else {
         dst[lane] = x1;
         dst[lane + half] = x2;
+        if (it >= GROUP) {
+          pdst[lane] = x1;
+          pdst[lane + half] = x2;
+        }
       }
     }
+  };
+  if (wave < NITEM) {
+    {
+      Item t;
+      item_load(wave, t);
+      issue(FromTab{}, 0, kb[0], vb[0]);
+      item_finish(wave, t);
+    }
+    for (int it = wave + NWV; it < NITEM; it += NWV) {
+      Item t;
+      item_load(it, t);
+      item_finish(it, t);
+    }
+    // (the other chunks are requested only now: their registers and the prologue's would not
+    // fit together)
+    unrolled<NBUF - 1>([&](auto b) { issue(FromTab{}, b + 1, kb[b + 1], vb[b + 1]); });
+  } else {
+    unrolled<NBUF>([&](auto b) { issue(FromTab{}, b, kb[b], vb[b]); });
   }
+#pragma unroll
+  for (int p = 0; p < TPASS; ++p) s_tbl[p * 64 * NWV + threadIdx.x] = (int32_t)tcopy[p];
   __syncthreads();
-  if (nmine > 0 && !early) issue(0, kraw, vraw);
 
   // q . k: f16 pairs through v_dot2_f32_f16 (products exact in the float32 sum), float32
   // pools through FMAs; the score is scaled by log2(e)/sqrt(D) afterwards
   const float qscale = 1.4426950408889634f / sqrtf((float)D);
-  u32x4 qraw[GROUP];
+  auto score = [&](const u32x4& q, const u32x4& k) __attribute__((always_inline)) {
+    float d = 0.f;
+    if constexpr (F16) {
 #pragma unroll
-  for (int i = 0; i < GROUP; ++i) qraw[i] = *(const u32x4*)(&s_q[i][sub * EPL]);
+      for (int j = 0; j < 4; ++j) d = __builtin_amdgcn_fdot2(as_half2(q[j]), as_half2(k[j]), d, false);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) d += __uint_as_float(q[j]) * __uint_as_float(k[j]);
+    }
+    return group_sum<LPK>(d) * qscale;
+  };
+  // (with eight query heads the registers would not hold them beside the chunks: they are
+  // then read from LDS for each chunk)
+  u32x4 qraw[G::QREG ? GROUP : 1];
+  if constexpr (G::QREG) {
+#pragma unroll
+    for (int i = 0; i < GROUP; ++i) qraw[i] = *(const u32x4*)(&s_q[i][sub * EPL]);
+  }
   float m[GROUP], l[GROUP], acc[GROUP][EPL];
 #pragma unroll
   for (int i = 0; i < GROUP; ++i) {
@@ -419,27 +535,24 @@ __global__ __launch_bounds__(1024) void attn_decode_kernel(QkRopeArgs qk, AttnRo
     for (int e = 0; e < EPL; ++e) acc[i][e] = 0.f;
   }
 
-  for (int ci = 0; ci < nmine; ++ci) {
+  // every chunk of the loop holds at least one key before pos, so m is finite after it
+  auto step = [&](int ci, u32x4 (&kr)[KPG], u32x4 (&vr)[KPG]) __attribute__((always_inline)) {
     const int key0 = (wave + ci * NWV) * CHUNK;
-    if (ci + 1 < nmine) issue(ci + 1, knext, vnext);
-    // keep the loads issued together, ahead of the arithmetic that consumes the current chunk
-    __builtin_amdgcn_sched_barrier(0);
+    // (an empty barrier keeps the per-chunk LDS reads of the query heads inside the loop, so the
+    // compiler does not hold all of them in registers)
+    if constexpr (!G::QREG) asm volatile("" ::: "memory");
     float sc[KPG][GROUP];
 #pragma unroll
     for (int kk = 0; kk < KPG; ++kk) {
-      const bool valid = key0 + kk * KPI + grp < ctx;
+      const bool valid = key0 + kk * KPI + grp < pos;
 #pragma unroll
       for (int i = 0; i < GROUP; ++i) {
-        float d = 0.f;
-        if constexpr (F16) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            d = __builtin_amdgcn_fdot2(as_half2(qraw[i][j]), as_half2(kraw[kk][j]), d, false);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) d += __uint_as_float(qraw[i][j]) * __uint_as_float(kraw[kk][j]);
-        }
-        d = group_sum<LPK>(d) * qscale;
+        u32x4 q;
+        if constexpr (G::QREG)
+          q = qraw[i];
+        else
+          q = *(const u32x4*)(&s_q[i][sub * EPL]);
+        const float d = score(q, kr[kk]);
         sc[kk][i] = valid ? d : -__builtin_inff();
       }
     }
@@ -448,8 +561,7 @@ __global__ __launch_bounds__(1024) void attn_decode_kernel(QkRopeArgs qk, AttnRo
       float mc = sc[0][i];
 #pragma unroll
       for (int kk = 1; kk < KPG; ++kk) mc = fmaxf(mc, sc[kk][i]);
-#pragma unroll
-      for (int o = LPK; o < 64; o <<= 1) mc = fmaxf(mc, __shfl_xor(mc, o, 64));
+      mc = xor_reduce<LPK>(mc, [](float x, float y) { return fmaxf(x, y); });
       const float mn = fmaxf(m[i], mc);
       const float alpha = fast_exp2(m[i] - mn);  // 0 on the first chunk (m = -inf)
       m[i] = mn;
@@ -459,10 +571,11 @@ __global__ __launch_bounds__(1024) void attn_decode_kernel(QkRopeArgs qk, AttnRo
     }
 #pragma unroll
     for (int kk = 0; kk < KPG; ++kk) {
-      // a masked key's slot holds whatever the block held before: zero it, as p * NaN is NaN
-      if (key0 + kk * KPI + grp >= ctx) vraw[kk] = u32x4{0u, 0u, 0u, 0u};
+      // a masked key's slot holds whatever the block holds: zero it, as p * NaN is NaN
+      u32x4 vw = vr[kk];
+      if (key0 + kk * KPI + grp >= pos) vw = u32x4{0u, 0u, 0u, 0u};
       float vv[EPL];
-      load_kv<KVT, EPL>((const KVT*)&vraw[kk], vv);
+      load_kv<KVT, EPL>((const KVT*)&vw, vv);
 #pragma unroll
       for (int i = 0; i < GROUP; ++i) {
         const float p = fast_exp2(sc[kk][i] - m[i]);
@@ -471,21 +584,29 @@ __global__ __launch_bounds__(1024) void attn_decode_kernel(QkRopeArgs qk, AttnRo
         for (int e = 0; e < EPL; ++e) acc[i][e] += p * vv[e];
       }
     }
-#pragma unroll
-    for (int kk = 0; kk < KPG; ++kk) {
-      kraw[kk] = knext[kk];
-      vraw[kk] = vnext[kk];
-    }
+  };
+  // the register sets in turn: while one chunk is consumed the others are in flight, and a
+  // set is refilled with the chunk NBUF further on as soon as it has been consumed
+  for (int c0 = 0; c0 < nmain; c0 += NBUF) {
+    unrolled<NBUF>([&](auto b) {
+      const int ci = c0 + b;
+      if (ci < nmain) step(ci, kb[b], vb[b]);
+      issue(FromLds{}, ci + NBUF, kb[b], vb[b]);
+    });
   }
+  // chunks past the LDS table (contexts beyond TCAP blocks): one at a time
+  for (int ci = nmain; ci < nmine; ++ci) {
+    issue(FromMem{}, ci, kb[0], vb[0]);
+    step(ci, kb[0], vb[0]);
+  }
+
   // this wave's state: sum the lane groups (each holds distinct keys)
+  const auto add = [](float x, float y) { return x + y; };
 #pragma unroll
-  for (int o = LPK; o < 64; o <<= 1) {
+  for (int i = 0; i < GROUP; ++i) {
+    l[i] = xor_reduce<LPK>(l[i], add);
 #pragma unroll
-    for (int i = 0; i < GROUP; ++i) {
-      l[i] += __shfl_xor(l[i], o, 64);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[i][e] += __shfl_xor(acc[i][e], o, 64);
-    }
+    for (int e = 0; e < EPL; ++e) acc[i][e] = xor_reduce<LPK>(acc[i][e], add);
   }
   if (grp == 0) {
 #pragma unroll
@@ -498,18 +619,39 @@ __global__ __launch_bounds__(1024) void attn_decode_kernel(QkRopeArgs qk, AttnRo
       }
     }
   }
+  // the new key's state: its score against each query head (computed as in the loop), sum 1,
+  // accumulator the new value
+  if (wave == NWV - 1) {
+#pragma unroll
+    for (int i = 0; i < GROUP; ++i) {
+      const float d = score(*(const u32x4*)(&s_q[i][sub * EPL]), *(const u32x4*)(&s_q[GROUP][sub * EPL]));
+      if (lane == 0) {
+        s_m[NWV][i] = d;
+        s_l[NWV][i] = 1.f;
+      }
+    }
+  }
   __syncthreads();
+  // merge: the wave states in wave order, then the new key's
   const int nw = min(NWV, nch);  // waves that saw at least one chunk
-  for (int t = threadIdx.x; t < GROUP * D; t += 1024) {
+  for (int t = threadIdx.x; t < GROUP * D; t += 64 * NWV) {
     const int i = t / D, d = t % D;
-    float M = s_m[0][i];
-    for (int w = 1; w < nw; ++w) M = fmaxf(M, s_m[w][i]);
+    float M = s_m[NWV][i];
+    for (int w = 0; w < nw; ++w) M = fmaxf(M, s_m[w][i]);
     float L = 0.f, A = 0.f;
     for (int w = 0; w < nw; ++w) {
       const float sc = fast_exp2(s_m[w][i] - M);
       L += sc * s_l[w][i];
       A += sc * s_acc[w][i][d];
     }
+    float vnew;
+    if constexpr (F16)
+      vnew = f16_bits_to_f32(s_q[GROUP + 1][d]);
+    else
+      vnew = s_q[GROUP + 1][d];
+    const float sn = fast_exp2(s_m[NWV][i] - M);
+    L += sn;
+    A += sn * vnew;
     const float v = A / L;
     const int64_t o = (int64_t)row * H * D + (int64_t)(kvh * GROUP + i) * D + d;
     if constexpr (BF16_OUT)
@@ -522,10 +664,11 @@ __global__ __launch_bounds__(1024) void attn_decode_kernel(QkRopeArgs qk, AttnRo
 template <typename KVT, int D, int GROUP>
 static void decode_launch(const QkRopeArgs& qk, const AttnRowsArgs& a, void* o, bool bf16_out, hipStream_t s) {
   dim3 g(a.b.n_rows * a.n_kv_heads);
+  const dim3 blk(64 * DecodeGeom<KVT, D, GROUP>::NWV);
   if (bf16_out)
-    launch_kernel(attn_decode_kernel<KVT, D, GROUP, true>, g, dim3(1024), 0, s, qk, a, o);
+    launch_kernel(attn_decode_kernel<KVT, D, GROUP, true>, g, blk, 0, s, qk, a, o);
   else
-    launch_kernel(attn_decode_kernel<KVT, D, GROUP, false>, g, dim3(1024), 0, s, qk, a, o);
+    launch_kernel(attn_decode_kernel<KVT, D, GROUP, false>, g, blk, 0, s, qk, a, o);
 }
 
 template <typename KVT, int D>
