@@ -20,12 +20,14 @@ constexpr int kWave = 64;
 
 // ---- scalar conversions (bit exact, no library rounding modes involved) -------------------
 
-// float -> bf16 bits, round to nearest, ties to even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// float -> bf16 bits, round to nearest, ties to even; NaN stays a quiet NaN (gfx950's
+// v_cvt_pk_bf16_f32: one instruction, no per-value branch)
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+// two values -> packed bf16 pair (lo = a, hi = b), one conversion instruction
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+  typedef float f32x2v __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v){a, b}, bf16x2v));
 }
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
@@ -85,6 +87,19 @@ __device__ __forceinline__ float wave_max(float v) {
 // ---- per-head q/k RMSNorm + split-halves RoPE ----------------------------------------------
 // Lane j < D/2 holds channels (j, j + D/2) of one head (other lanes hold zeros). RMSNorm over
 // the D channels with gain g, then rotation of the pair by the angle's (cos, sin).
+// (gains given as the lane's two values g[j], g[j + D/2])
+__device__ __forceinline__ void norm_rope_pair_g(float& x1, float& x2, float g1, float g2, float2 cs, int lane, int D,
+                                                 float eps) {
+  const int half = D / 2;
+  const float ss = wave_sum<64>(x1 * x1 + x2 * x2);
+  const float inv = 1.0f / sqrtf(ss / (float)D + eps);
+  if (lane < half) {
+    const float a = x1 * inv * g1;
+    const float b = x2 * inv * g2;
+    x1 = a * cs.x - b * cs.y;
+    x2 = b * cs.x + a * cs.y;
+  }
+}
 __device__ __forceinline__ void norm_rope_pair(float& x1, float& x2, const float* g, float2 cs, int lane, int D,
                                                float eps) {
   const int half = D / 2;

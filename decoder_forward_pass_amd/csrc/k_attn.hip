@@ -363,9 +363,10 @@ __global__ __launch_bounds__((64 * DecodeGeom<KVT, D, GROUP>::NWV)) void attn_de
   const char* vbase = kbase + a.pool.n_blocks * slab * (int64_t)sizeof(KVT);
   const uint32_t lane_off = (uint32_t)((grp * D + sub * EPL) * sizeof(KVT));
 
-  // The sequence's block table goes to LDS (blocks 0 .. last_blk, at most TCAP of them) while
-  // the prologue runs: range-checked loads, so entries past the last block cost nothing. Its
-  // loads are the wave's first, so the wait for them leaves the later loads in flight.
+  // The sequence's block table goes to LDS (blocks 0 .. last_blk, at most TCAP of them) for
+  // the requests after the barrier: range-checked loads, so entries past the last block cost
+  // nothing. They are waited for together with tab below (which the first requests need), so
+  // no later wait depends on them.
   constexpr int TCAP = 4096, TPASS = TCAP / (64 * NWV);
   __shared__ int32_t s_tbl[TCAP];
   uint32_t tcopy[TPASS];
@@ -380,6 +381,10 @@ __global__ __launch_bounds__((64 * DecodeGeom<KVT, D, GROUP>::NWV)) void attn_de
   // block j % bpc of the wave's chunk j / bpc
   const int bpc = CHUNK > a.pool.block_tokens ? CHUNK >> bsh : 1;  // blocks per chunk (64 / bpc >= NBUF)
   const int tab = table[min(((min(wave + (lane / bpc) * NWV, max(nch - 1, 0)) * CHUNK) >> bsh) + lane % bpc, last_blk)];
+  auto publish_table = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int p = 0; p < TPASS; ++p) s_tbl[p * 64 * NWV + threadIdx.x] = (int32_t)tcopy[p];
+  };
 
   const int nmine = wave < nch ? (nch - 1 - wave) / NWV + 1 : 0;  // chunks of this wave
   // chunks whose blocks the LDS table holds: the first TCAP * B / (CHUNK * NWV) of each wave
@@ -425,10 +430,12 @@ __global__ __launch_bounds__((64 * DecodeGeom<KVT, D, GROUP>::NWV)) void attn_de
   struct Item {
     float p1[8], p2[8];
     float2 cs;
+    float g1, g2;  // q or k norm gains of the lane's two channels
     int newblk;
   };
   auto item_load = [&](int it, Item& t) __attribute__((always_inline)) {
     t.cs = make_float2(1.f, 0.f);
+    t.g1 = t.g2 = 1.f;
     t.newblk = 0;
     if (lane < half) {
       const int hh = it < GROUP ? kvh * GROUP + it : (it == GROUP ? H + kvh : H + Hkv + kvh);
@@ -441,7 +448,12 @@ __global__ __launch_bounds__((64 * DecodeGeom<KVT, D, GROUP>::NWV)) void attn_de
           t.p2[p] = sp[lane + half];
         }
       }
-      if (it <= GROUP) t.cs = qk.rope[(int64_t)pos * half + lane];
+      if (it <= GROUP) {
+        const float* g = it < GROUP ? qk.q_norm : qk.k_norm;
+        t.cs = qk.rope[(int64_t)pos * half + lane];
+        t.g1 = g[lane];
+        t.g2 = g[lane + half];
+      }
       if (it >= GROUP) t.newblk = table[pos >> bsh];
     }
   };
@@ -461,7 +473,7 @@ __global__ __launch_bounds__((64 * DecodeGeom<KVT, D, GROUP>::NWV)) void attn_de
         }
       }
     }
-    if (it <= GROUP) norm_rope_pair(x1, x2, it < GROUP ? qk.q_norm : qk.k_norm, t.cs, lane, D, qk.eps);
+    if (it <= GROUP) norm_rope_pair_g(x1, x2, t.g1, t.g2, t.cs, lane, D, qk.eps);
     if (lane < half) {
       KVT* dst = s_q[it];
       KVT* pdst = (KVT*)a.pool.base + a.pool.offset(a.layer, it == GROUP ? 0 : 1, t.newblk, kvh, pos & bmask);
@@ -487,6 +499,7 @@ __global__ __launch_bounds__((64 * DecodeGeom<KVT, D, GROUP>::NWV)) void attn_de
     {
       Item t;
       item_load(wave, t);
+      publish_table();
       issue(FromTab{}, 0, kb[0], vb[0]);
       item_finish(wave, t);
     }
@@ -499,10 +512,9 @@ __global__ __launch_bounds__((64 * DecodeGeom<KVT, D, GROUP>::NWV)) void attn_de
     // fit together)
     unrolled<NBUF - 1>([&](auto b) { issue(FromTab{}, b + 1, kb[b + 1], vb[b + 1]); });
   } else {
+    publish_table();
     unrolled<NBUF>([&](auto b) { issue(FromTab{}, b, kb[b], vb[b]); });
   }
-#pragma unroll
-  for (int p = 0; p < TPASS; ++p) s_tbl[p * 64 * NWV + threadIdx.x] = (int32_t)tcopy[p];
   __syncthreads();
 
   // q . k: f16 pairs through v_dot2_f32_f16 (products exact in the float32 sum), float32
@@ -937,8 +949,8 @@ __global__ __launch_bounds__(256 * G) void attn_prefill_kernel(AttnPrefillArgs a
                   v3 = o[db][4 * g + 3] * inv;
       if constexpr (BF16_OUT) {
         uint2 w;
-        w.x = (uint32_t)f32_to_bf16_bits(v0) | ((uint32_t)f32_to_bf16_bits(v1) << 16);
-        w.y = (uint32_t)f32_to_bf16_bits(v2) | ((uint32_t)f32_to_bf16_bits(v3) << 16);
+        w.x = pack_bf16x2(v0, v1);
+        w.y = pack_bf16x2(v2, v3);
         *(uint2*)((uint16_t*)a.o + ob + d) = w;
       } else {
         *(float4*)((float*)a.o + ob + d) = make_float4(v0, v1, v2, v3);

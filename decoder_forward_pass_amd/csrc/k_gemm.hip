@@ -120,7 +120,7 @@ __global__ __launch_bounds__(256) void gemm_tile64(GemmArgs a) {
           const uint32_t byte = (codes[j >> 2] >> ((j & 3) * 8)) & 0xffu;
           const float lo = dequant_u4(byte & 15u, zp, sc);
           const float hi = dequant_u4(byte >> 4, zp, sc);
-          d[j] = (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+          d[j] = pack_bf16x2(lo, hi);
         }
       }
     }
@@ -286,8 +286,7 @@ __device__ __forceinline__ bf16x8 b_frag(const BRaw<WF>& r) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t byte = (r.codes >> (8 * j)) & 0xffu;
-      w[j] = (uint32_t)f32_to_bf16_bits(dequant_u4(byte & 15u, zp, sc)) |
-             ((uint32_t)f32_to_bf16_bits(dequant_u4(byte >> 4, zp, sc)) << 16);
+      w[j] = pack_bf16x2(dequant_u4(byte & 15u, zp, sc), dequant_u4(byte >> 4, zp, sc));
     }
     return __builtin_bit_cast(bf16x8, w);
   }
@@ -456,10 +455,8 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
           for (int h = 0; h < 2; ++h) {
             const float* xv = (const float*)&xr[h];
             const float* gv = (const float*)&graw[i][h];
-            w[2 * h] = (uint32_t)f32_to_bf16_bits(xv[0] * inv * gv[0]) |
-                       ((uint32_t)f32_to_bf16_bits(xv[1] * inv * gv[1]) << 16);
-            w[2 * h + 1] = (uint32_t)f32_to_bf16_bits(xv[2] * inv * gv[2]) |
-                           ((uint32_t)f32_to_bf16_bits(xv[3] * inv * gv[3]) << 16);
+            w[2 * h] = pack_bf16x2(xv[0] * inv * gv[0], xv[1] * inv * gv[1]);
+            w[2 * h + 1] = pack_bf16x2(xv[2] * inv * gv[2], xv[3] * inv * gv[3]);
           }
           af = __builtin_bit_cast(bf16x8, w);
         } else {
@@ -614,8 +611,8 @@ __global__ __launch_bounds__(256) void gemm_decode_parts_kernel(GemmArgs a, int6
       const float4 g = *(const float4*)(a.gain + kb + 4 * c4);
       const float4 x = xv[j];
       uint2 w;
-      w.x = (uint32_t)f32_to_bf16_bits(x.x * inv * g.x) | ((uint32_t)f32_to_bf16_bits(x.y * inv * g.y) << 16);
-      w.y = (uint32_t)f32_to_bf16_bits(x.z * inv * g.z) | ((uint32_t)f32_to_bf16_bits(x.w * inv * g.w) << 16);
+      w.x = pack_bf16x2(x.x * inv * g.x, x.y * inv * g.y);
+      w.y = pack_bf16x2(x.z * inv * g.z, x.w * inv * g.w);
       *(uint2*)(sA + row * LS + 4 * c4) = w;
     }
   }
@@ -721,8 +718,8 @@ __global__ __launch_bounds__(1024) void lmhead_decode(GemmArgs a) {
           const float4 v = *(const float4*)(xr + j);
           const float4 g = *(const float4*)(a.gain + c0 + j);
           uint32_t* d = (uint32_t*)(s_h + r * KS + c0 + j);
-          d[0] = (uint32_t)f32_to_bf16_bits(v.x * inv * g.x) | ((uint32_t)f32_to_bf16_bits(v.y * inv * g.y) << 16);
-          d[1] = (uint32_t)f32_to_bf16_bits(v.z * inv * g.z) | ((uint32_t)f32_to_bf16_bits(v.w * inv * g.w) << 16);
+          d[0] = pack_bf16x2(v.x * inv * g.x, v.y * inv * g.y);
+          d[1] = pack_bf16x2(v.z * inv * g.z, v.w * inv * g.w);
         }
     }
   }

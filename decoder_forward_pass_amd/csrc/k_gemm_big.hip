@@ -163,8 +163,7 @@ __global__ __launch_bounds__(512) void gemm_big(GemmArgs a, QkRopeArgs qk) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const uint32_t byte = (rb[0][q] >> (8 * j)) & 0xffu;
-          w[j] = (uint32_t)f32_to_bf16_bits(dequant_u4(byte & 15u, zp, sc)) |
-                 ((uint32_t)f32_to_bf16_bits(dequant_u4(byte >> 4, zp, sc)) << 16);
+          w[j] = pack_bf16x2(dequant_u4(byte & 15u, zp, sc), dequant_u4(byte >> 4, zp, sc));
         }
         *(u32x4*)(d + q * 8) = w;
       }

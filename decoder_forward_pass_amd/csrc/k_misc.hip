@@ -127,8 +127,8 @@ __global__ __launch_bounds__(256) void rmsnorm_vec_kernel(const float* __restric
     const int64_t o = (int64_t)r * d + 4 * (lane + 64 * j);
     if constexpr (BF16_OUT) {
       u32x2 w;
-      w[0] = (uint32_t)f32_to_bf16_bits(y0) | ((uint32_t)f32_to_bf16_bits(y1) << 16);
-      w[1] = (uint32_t)f32_to_bf16_bits(y2) | ((uint32_t)f32_to_bf16_bits(y3) << 16);
+      w[0] = pack_bf16x2(y0, y1);
+      w[1] = pack_bf16x2(y2, y3);
       *(u32x2*)((uint16_t*)out + o) = w;
     } else {
       *(float4*)((float*)out + o) = make_float4(y0, y1, y2, y3);
