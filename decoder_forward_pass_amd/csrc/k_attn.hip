@@ -43,6 +43,47 @@ __device__ __forceinline__ void load_kv(const KVT* p, float (&v)[EPL]) {
   }
 }
 
+template <typename F, int... I>
+__device__ __forceinline__ void unrolled_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void unrolled(F&& f) {  // f(0), ..., f(N - 1) with constant indices
+  unrolled_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// v op v[lane ^ O] for every lane, with no lane-address registers: for O = 16 and 32 the gfx950
+// row swaps hand each lane the pair {v[lane], v[lane ^ O]}, for smaller O a bit-mask swizzle
+// fetches the partner (op is commutative, so either order gives the same bits)
+template <int O, typename Op>
+__device__ __forceinline__ float xor_combine(float v, Op op) {
+  const uint32_t u = __float_as_uint(v);
+  if constexpr (O == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  } else if constexpr (O == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  } else {
+    static_assert(O >= 1 && O < 16, "lane distance");
+    return op(v, __uint_as_float(__builtin_amdgcn_ds_swizzle((int)u, 0x1F | (O << 10))));
+  }
+}
+template <int FROM, typename Op>
+__device__ __forceinline__ float xor_reduce(float v, Op op) {  // over lane bits FROM..32
+  if constexpr (FROM < 64) return xor_reduce<FROM * 2>(xor_combine<FROM>(v, op), op);
+  return v;
+}
+
+// a 16-byte load at a wave-uniform address plus a 32-bit lane offset, through a raw buffer
+// descriptor held in scalar registers (no 64-bit lane addresses; the offsets used here are a
+// few kilobytes, far inside the descriptor's range)
+// With range 0 the load returns zeros without a memory access.
+__device__ __forceinline__ u32x4 load_uniform_base(const char* base, uint32_t lane_off, int range = 0x7fffffff) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, range, 0x00020000);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)lane_off, 0, 0);
+}
+
 template <typename KVT, int D, int GROUP>
 __global__ __launch_bounds__(256) void attn_rows_kernel(AttnRowsArgs a) {
   using G = RowsGeom<KVT, D, GROUP>;
@@ -259,17 +300,18 @@ hipError_t launch_attn_combine(const float* partial, int n_rows, int n_heads, in
 }
 
 // ---- decode attention: one workgroup per (sequence, KV head) ------------------------------
-// A decode step has one query row per sequence. The workgroup's 16 waves take fixed chunks of
-// the row's keys in turn: wave w handles chunks w, w+16, ... in increasing order, keeping a
-// running (max, sum, accumulator) per query head. A chunk is KPI keys per wave-wide load times
-// DKPG loads; the chunk's block ids arrive in one load (lane i: the chunk's i-th block), and
-// all K and V loads of a chunk are issued before any arithmetic (keys past the context read a
-// valid slot of the last block and are masked). Each wave requests its first two chunks before
-// the q/k prologue, so the pool streams while the new query, key and value are formed; the
-// wave whose chunk holds the new position takes that key and value from LDS instead of the
-// pool slot it read early. The 16 wave states are merged in wave order through LDS and the
-// output row is written: no partials leave the workgroup. The split depends only on the row's
-// context length, so the result does not depend on the other sequences.
+// A decode step has one query row per sequence. The workgroup's NWV waves take fixed chunks
+// of the keys before the new position: wave w handles chunks w, w+NWV, ... in increasing
+// order, keeping a running (max, sum, accumulator) per query head. A chunk is two wave-wide
+// loads of KPI keys (16 bytes per lane) for K and the same for V; NBUF chunks per wave are in
+// flight, in register sets used in turn. The prologue waves first add up the new row's Q|K|V
+// partial products, normalise and rotate q and k, and write the new key and value to the pool
+// and to LDS; meanwhile every wave has requested its first chunks, whose block ids come from
+// one table load per wave. The sequence's block table is copied to LDS for the later chunks,
+// so no request after the barrier waits on a table load. The new key enters as one more state
+// (its score, sum 1, the new value) merged after the wave states, in wave order, through LDS;
+// no partials leave the workgroup. The split depends only on the row's position, so the result
+// does not depend on the other sequences.
 
 template <typename KVT, int D, int GROUP>
 struct DecodeGeom {
@@ -290,47 +332,6 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 // (taken by value: a bit cast applied directly to an element of an ext_vector is miscompiled
 // here into a cast of element 0)
 __device__ __forceinline__ half2v as_half2(uint32_t u) { return __builtin_bit_cast(half2v, u); }
-
-template <typename F, int... I>
-__device__ __forceinline__ void unrolled_impl(F&& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void unrolled(F&& f) {  // f(0), ..., f(N - 1) with constant indices
-  unrolled_impl(f, std::make_integer_sequence<int, N>{});
-}
-
-// v op v[lane ^ O] for every lane, with no lane-address registers: for O = 16 and 32 the gfx950
-// row swaps hand each lane the pair {v[lane], v[lane ^ O]}, for smaller O a bit-mask swizzle
-// fetches the partner (op is commutative, so either order gives the same bits)
-template <int O, typename Op>
-__device__ __forceinline__ float xor_combine(float v, Op op) {
-  const uint32_t u = __float_as_uint(v);
-  if constexpr (O == 32) {
-    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
-  } else if constexpr (O == 16) {
-    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    return op(__uint_as_float(r[0]), __uint_as_float(r[1]));
-  } else {
-    static_assert(O >= 1 && O < 16, "lane distance");
-    return op(v, __uint_as_float(__builtin_amdgcn_ds_swizzle((int)u, 0x1F | (O << 10))));
-  }
-}
-template <int FROM, typename Op>
-__device__ __forceinline__ float xor_reduce(float v, Op op) {  // over lane bits FROM..32
-  if constexpr (FROM < 64) return xor_reduce<FROM * 2>(xor_combine<FROM>(v, op), op);
-  return v;
-}
-
-// a 16-byte load at a wave-uniform address plus a 32-bit lane offset, through a raw buffer
-// descriptor held in scalar registers (no 64-bit lane addresses; the offsets used here are a
-// few kilobytes, far inside the descriptor's range)
-// With range 0 the load returns zeros without a memory access.
-__device__ __forceinline__ u32x4 load_uniform_base(const char* base, uint32_t lane_off, int range = 0x7fffffff) {
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, range, 0x00020000);
-  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)lane_off, 0, 0);
-}
 
 template <typename KVT, int D, int GROUP, bool BF16_OUT>
 __global__ __launch_bounds__((64 * DecodeGeom<KVT, D, GROUP>::NWV)) void attn_decode_kernel(QkRopeArgs qk,
