@@ -300,8 +300,9 @@ __device__ __forceinline__ bf16x8 b_frag(const BRaw<WF>& r) {
 // staged tile keeps its 16-byte chunk c at position c ^ (r % 16), so the 16 rows of a fragment
 // read fall on distinct banks; after the products the same LDS holds the wave partials. The
 // K split, the order of the additions and the arithmetic are those of the register path.
-template <int WF, int EPI, int MT, int NKS, bool LDSA>
+template <int WF, int EPI, int MT, int NKS, bool LDSA, int RPB = 16 * MT>
 __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
+  static_assert(RPB == 16 * MT || (RPB == 8 && MT == 1 && LDSA), "8-row blocks: one 16-row MFMA tile, staged rows");
   // STORE / SWIGLU read the float32 residual and normalise it on the fly (RMSNorm fused);
   // RESID reads a bf16 activation and writes the sums of squares of the new residual.
   constexpr bool NORM = EPI != EPI_RESID;
@@ -315,8 +316,9 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n0 = blockIdx.x * 16;
-  const int m0 = blockIdx.y * 16 * MT;
+  const int m0 = blockIdx.y * RPB;
   const int M = a.M, K = a.K;
+  const int mend = min(M, m0 + RPB);  // rows of this block: m0 .. mend - 1
   const int cpr = K * ES / 16;  // 16-byte chunks per activation row
 
   WMat bm[NB];
@@ -342,7 +344,7 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
     if (threadIdx.x < MT * 256) {
       const int t = threadIdx.x, sl = t % 64;
       const int m = m0 + (t / 256) * 16 + (sl >> 4) * 4 + (t / 64) % 4, ncol = n0 + (sl & 15);
-      if (m < M && ncol < a.N) xres = ((const float*)a.C)[(int64_t)m * a.ldc + ncol];
+      if (m < mend && ncol < a.N) xres = ((const float*)a.C)[(int64_t)m * a.ldc + ncol];
     }
   }
   const int brow = min(br0 + (lane & 15), bm[0].rows - 1);
@@ -385,7 +387,7 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
   }
   if constexpr (LDSA) {
     // every wave stages 1 KB pieces (64 chunk slots, row-major over the swizzled tile)
-    const int nins = 16 * MT * cpr / 64;
+    const int nins = RPB * cpr / 64;  // (8-row blocks: MFMA rows 8..15 read unstaged LDS; never stored)
     for (int j = wave; j < nins; j += kDecWaves) {
       const int slot = j * 64 + lane, r = slot / cpr, pc = slot % cpr, c = pc ^ (r & 15);
       const uint8_t* src = (const uint8_t*)a.A + ((int64_t)min(m0 + r, M - 1) * a.lda) * ES + c * 16;
@@ -494,7 +496,7 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
     }
     const int m = m0 + mt * 16 + (sl >> 4) * 4 + r;
     const int ncol = n0 + (sl & 15);
-    const bool in = m < M && ncol < a.N;
+    const bool in = m < mend && ncol < a.N;
     const int64_t o = (int64_t)m * a.ldc + ncol;
     if constexpr (EPI == EPI_STORE) {
       if (in) ((float*)a.C)[o] = v[0];
@@ -506,7 +508,7 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
       }
       if (a.ssq_out) {
         const float sq = group_sum<16>(xn * xn);
-        if (m < M && (sl & 15) == 0) a.ssq_out[(int64_t)m * (a.N / 16) + blockIdx.x] = sq;
+        if (m < mend && (sl & 15) == 0) a.ssq_out[(int64_t)m * (a.N / 16) + blockIdx.x] = sq;
       }
     } else {
       if (in) {
@@ -826,51 +828,64 @@ static size_t decode_lds_bytes(int K) {
   return act > part ? act : part;
 }
 
-template <int WF, int EPI, int MT, int NKS>
-static hipError_t gemm_decode_launch(const GemmArgs& a, int nw, dim3 g, hipStream_t s) {
-  const int es = EPI == EPI_RESID ? 2 : 4;
-  const size_t lds = decode_lds_bytes<EPI, MT>(a.K);
-  // staged path: chunks per row a multiple of 16 (the swizzle) and the tile within 128 KB
-  if ((a.K * es / 16) % 16 == 0 && lds <= 128 * 1024) {
+template <int EPI>
+static bool decode_staged(int K, size_t lds) {  // chunks per row a multiple of 16 (the swizzle), tile <= 128 KB
+  return (K * (EPI == EPI_RESID ? 2 : 4) / 16) % 16 == 0 && lds <= 128 * 1024;
+}
+
+template <int WF, int EPI, int MT, int NKS, bool LDSA, int RPB>
+static hipError_t gemm_decode_kernel_launch(const GemmArgs& a, int nw, dim3 g, size_t lds, hipStream_t s) {
+  if constexpr (LDSA) {
     static bool attr = false;
     if (!attr) {
-      hipError_t e = hipFuncSetAttribute((const void*)gemm_decode<WF, EPI, MT, NKS, true>,
+      hipError_t e = hipFuncSetAttribute((const void*)gemm_decode<WF, EPI, MT, NKS, true, RPB>,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
       if (e != hipSuccess) return e;
       attr = true;
     }
-    launch_kernel(gemm_decode<WF, EPI, MT, NKS, true>, g, dim3(512), (uint32_t)lds, s, a, nw);
-  } else {
-    launch_kernel(gemm_decode<WF, EPI, MT, NKS, false>, g, dim3(512), 0, s, a, nw);
   }
+  launch_kernel(gemm_decode<WF, EPI, MT, NKS, LDSA, RPB>, g, dim3(512), (uint32_t)(LDSA ? lds : 0), s, a, nw);
   return hipGetLastError();
 }
 
+// rows8: blocks of 8 rows (RESID products with few column groups: four blocks per column tile,
+// all on one XCD, so the tile's weights come from HBM once and from L2 after)
+template <int WF, int EPI, int MT, int NKS>
+static hipError_t gemm_decode_launch(const GemmArgs& a, int nw, bool rows8, hipStream_t s) {
+  const size_t lds = decode_lds_bytes<EPI, MT>(a.K);
+  if constexpr (EPI == EPI_RESID && MT == 1) {
+    if (rows8 && decode_staged<EPI>(a.K, lds))
+      return gemm_decode_kernel_launch<WF, EPI, 1, NKS, true, 8>(a, nw, dim3((a.N + 15) / 16, (a.M + 7) / 8), lds, s);
+  }
+  const dim3 g((a.N + 15) / 16, (a.M + 16 * MT - 1) / (16 * MT));
+  if (decode_staged<EPI>(a.K, lds)) return gemm_decode_kernel_launch<WF, EPI, MT, NKS, true, 16 * MT>(a, nw, g, lds, s);
+  return gemm_decode_kernel_launch<WF, EPI, MT, NKS, false, 16 * MT>(a, nw, g, lds, s);
+}
+
 template <int WF, int MT, int NKS>
-static hipError_t gemm_decode_go(int epi, const GemmArgs& a, int nw, hipStream_t s) {
-  dim3 g((a.N + 15) / 16, (a.M + 16 * MT - 1) / (16 * MT));
+static hipError_t gemm_decode_go(int epi, const GemmArgs& a, int nw, bool rows8, hipStream_t s) {
   switch (epi) {
-    case EPI_STORE: return gemm_decode_launch<WF, EPI_STORE, MT, NKS>(a, nw, g, s);
-    case EPI_RESID: return gemm_decode_launch<WF, EPI_RESID, MT, NKS>(a, nw, g, s);
-    case EPI_SWIGLU: return gemm_decode_launch<WF, EPI_SWIGLU, MT, NKS>(a, nw, g, s);
+    case EPI_STORE: return gemm_decode_launch<WF, EPI_STORE, MT, NKS>(a, nw, false, s);
+    case EPI_RESID: return gemm_decode_launch<WF, EPI_RESID, MT, NKS>(a, nw, rows8, s);
+    case EPI_SWIGLU: return gemm_decode_launch<WF, EPI_SWIGLU, MT, NKS>(a, nw, false, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <int WF, int MT>
-static hipError_t gemm_decode_nks(int epi, const GemmArgs& a, hipStream_t s) {
+static hipError_t gemm_decode_nks(int epi, const GemmArgs& a, bool rows8, hipStream_t s) {
   // K split: nw waves of nks k-steps each, nw the largest of 8, 4, 2, 1 dividing K/32
   const int ksteps = a.K / 32;
   int nw = kDecWaves;
   while (ksteps % nw) nw >>= 1;
   switch (ksteps / nw) {
-    case 1: return gemm_decode_go<WF, MT, 1>(epi, a, nw, s);
-    case 2: return gemm_decode_go<WF, MT, 2>(epi, a, nw, s);
-    case 3: return gemm_decode_go<WF, MT, 3>(epi, a, nw, s);
-    case 4: return gemm_decode_go<WF, MT, 4>(epi, a, nw, s);
-    case 6: return gemm_decode_go<WF, MT, 6>(epi, a, nw, s);
-    case 8: return gemm_decode_go<WF, MT, 8>(epi, a, nw, s);
-    case 12: return gemm_decode_go<WF, MT, 12>(epi, a, nw, s);
+    case 1: return gemm_decode_go<WF, MT, 1>(epi, a, nw, rows8, s);
+    case 2: return gemm_decode_go<WF, MT, 2>(epi, a, nw, rows8, s);
+    case 3: return gemm_decode_go<WF, MT, 3>(epi, a, nw, rows8, s);
+    case 4: return gemm_decode_go<WF, MT, 4>(epi, a, nw, rows8, s);
+    case 6: return gemm_decode_go<WF, MT, 6>(epi, a, nw, rows8, s);
+    case 8: return gemm_decode_go<WF, MT, 8>(epi, a, nw, rows8, s);
+    case 12: return gemm_decode_go<WF, MT, 12>(epi, a, nw, rows8, s);
   }
   return hipErrorInvalidValue;
 }
@@ -891,10 +906,12 @@ hipError_t launch_gemm_decode(int wdtype, int epi, const GemmArgs& a, hipStream_
   // is the same either way
   const size_t tile32 = (size_t)32 * a.K * (epi == EPI_RESID ? 2 : 4);
   const bool rows16 = a.M <= 16 || (a.N + 15) / 16 < 128 || (tile32 > 128 * 1024 && tile32 / 2 <= 128 * 1024);
+  const bool rows8 = epi == EPI_RESID && a.M > 8 && (a.N + 15) / 16 * ((a.M + 15) / 16) < 256;
   if (wdtype == DEC_BF16)
-    return rows16 ? gemm_decode_nks<DEC_BF16, 1>(epi, a, s) : gemm_decode_nks<DEC_BF16, 2>(epi, a, s);
+    return rows16 ? gemm_decode_nks<DEC_BF16, 1>(epi, a, rows8, s) : gemm_decode_nks<DEC_BF16, 2>(epi, a, rows8, s);
   if (wdtype == DEC_UINT4_G32)
-    return rows16 ? gemm_decode_nks<DEC_UINT4_G32, 1>(epi, a, s) : gemm_decode_nks<DEC_UINT4_G32, 2>(epi, a, s);
+    return rows16 ? gemm_decode_nks<DEC_UINT4_G32, 1>(epi, a, rows8, s)
+                  : gemm_decode_nks<DEC_UINT4_G32, 2>(epi, a, rows8, s);
   return hipErrorInvalidValue;
 }
 
