@@ -11,7 +11,7 @@ tokens per second); prefill and decode rates are reported beside it.
 
 ``roofline``: the kernel with the largest share of the timed region's GPU time (decode
 attention, HBM-bound), timed live on the library's stream with HIP events that the launch
-itself records at the kernel's start and end, on the attention launches of every 16th decode
+itself records at the kernel's start and end, on the attention launches of every 32nd decode
 step of the timed steps; achieved = their mean algorithmic bytes per launch / their mean
 duration. ``traffic``: HBM bytes per launch from the committed hardware-counter summary.
 ``roofline_prefill``: the same for the largest prefill GEMM (MFMA-bound). ``cpu_baseline``:
@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="q06b_bf16_b32_p1024_d256")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--time-every", type=int, default=32,
+                    help="time the attention launches of every N-th decode step (0: none)")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="first run one device-to-device copy of this many MiB (a reference dispatch of known "
                          "traffic for hardware-counter runs)")
@@ -263,7 +265,7 @@ def main():
     # kernel classes timed live over the timed region: the prefill's gate/up GEMM and the
     # decode steps' attention
     K_ROWS, K_GATEUP = 5, 8
-    TIME_EVERY = 16
+    TIME_EVERY = args.time_every
 
     def one_step(phase_times=None):
         timed = phase_times is not None
@@ -277,10 +279,10 @@ def main():
         for t in range(steps):
             # the attention launches of every TIME_EVERY-th decode step are timed (a timed launch
             # records its events at the kernel's own start and end, which costs a little)
-            if timed and t % TIME_EVERY == 0:
+            if timed and TIME_EVERY and t % TIME_EVERY == 0:
                 B.dec_timing_enable(s.ctx, 1 << K_ROWS)
             s.decode_step(positions[t], tbl, tokens_device=hist[t], logits=logits, next_tokens=hist[t + 1])
-            if timed and t % TIME_EVERY == 0:
+            if timed and TIME_EVERY and t % TIME_EVERY == 0:
                 B.dec_timing_enable(s.ctx, 0)
         if timed:
             ev[2].record()
@@ -317,11 +319,12 @@ def main():
     # (context length) x H_kv x D x 2 (K, V) x 2 bytes.
     kv_el = 2 if shape.kv_dtype == "f16" else 4
     per_key = shape.n_kv_heads * shape.head_dim * 2 * kv_el
-    bytes_per_step_layer = [S * (P + t + 1) * per_key for t in range(0, steps, TIME_EVERY)]
+    bytes_per_step_layer = [S * (P + t + 1) * per_key for t in range(0, steps, TIME_EVERY or steps)]
     rows_launch_bytes = float(np.mean(bytes_per_step_layer))
-    rows_launches_expected = args.steps * len(bytes_per_step_layer) * shape.n_layers
+    rows_launches_expected = args.steps * len(bytes_per_step_layer) * shape.n_layers if TIME_EVERY else 0
     rows_avg_ms = rows_ms / max(rows_n, 1)
-    achieved = rows_launch_bytes / (rows_avg_ms * 1e-3) / 1e9
+    # (--time-every 0 times no launch: the roofline figures are then absent)
+    achieved = rows_launch_bytes / (rows_avg_ms * 1e-3) / 1e9 if rows_n else None
     # gate/up GEMM of the prefill: 2 * M * (2 ff) * d flops per launch
     gu_prefill_flops = 2.0 * S * P * 2 * shape.ff_hidden * shape.d_model
     # (only prefill launches of that class are timed)
@@ -348,8 +351,8 @@ def main():
         "decode_ms_per_step": round(dec_ms / steps, 4),
         "roofline": {
             "kernel": "attn_decode_kernel (decode attention, q/k norm + RoPE + KV write fused)",
-            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "bound": "hbm", "achieved": round(achieved, 1) if achieved else None, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
             "traffic": measured_traffic(f"attn_decode_kernel_{wl.name}_pmc.json"),
             "launches": rows_n, "launches_expected": rows_launches_expected,
             "avg_launch_us": round(rows_avg_ms * 1e3, 2), "algorithmic_bytes_per_launch": rows_launch_bytes,
