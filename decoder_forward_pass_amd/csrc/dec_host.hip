@@ -135,7 +135,7 @@ size_t kv_bytes(const dec_config& c) {
 // ---- workspace layout ----------------------------------------------------------------------
 
 struct Ws {
-  size_t rope, meta, x, h, qkv, q, o, a, part, amax, ssq, total;
+  size_t rope, meta, x, h, qkv, q, o, a, part, amax, ssq, xg, total;
   size_t meta_ints;  // capacity of the metadata region in int32
   int chunk, nch_max, max_blocks_per_seq, max_tiles;
   int act_bytes, kv_el;
@@ -177,6 +177,7 @@ Ws ws_layout(const dec_config& c) {
   w.part = take(prow * H * (size_t)w.nch_max * (D + 2) * 4);
   w.amax = take(argmax_scratch_bytes((int)R));
   w.ssq = take(S * (d / 16) * 4);  // decode: sums of squares of the residual in 16-column partials
+  w.xg = take(S * d * 2);          // decode: bf16(residual * the next norm's gain)
   w.total = off;
   return w;
 }
@@ -433,13 +434,16 @@ int run_forward(dec_ctx* ctx, hipStream_t st, const BatchDev& b, const int32_t* 
   void* act = ctx->wsp + w.a;
   float* part = (float*)(ctx->wsp + w.part);
   float* ssq = (float*)(ctx->wsp + w.ssq);
+  uint16_t* xg = (uint16_t*)(ctx->wsp + w.xg);
   const float2* rope = (const float2*)(ctx->wsp + w.rope);
   PoolDev pool{ctx->pool, c.n_blocks, Hkv, c.block_tokens, D, __builtin_ctz((unsigned)c.block_tokens)};
   const int nch = (max_ctx + w.chunk - 1) / w.chunk;
-  // Decode steps take the decode GEMM (K split inside a block) when the weight format has one:
-  // it normalises its input on the fly from the residual's 16-column sums of squares, which
-  // the embedding and the residual epilogues write, so decode needs no separate RMSNorm
-  // launch. Prefill calls always take the tile GEMM after an RMSNorm launch.
+  // Decode steps take the decode GEMM (K split inside a block) when the weight format has one.
+  // Its RMSNorm is deferred: the embedding and the residual epilogues write, beside x, the
+  // residual's 16-column sums of squares and xg = bf16(x * g) with the gain g of the norm that
+  // reads x next; the normalising products take xg as their input and scale each output row
+  // by 1 / rms(x), so decode needs no separate RMSNorm launch. Prefill calls always take the
+  // tile GEMM after an RMSNorm launch.
   const bool dgemm = decode && gemm_decode_supported(c.weight_dtype, d) &&
                      gemm_decode_supported(c.weight_dtype, qw) && gemm_decode_supported(c.weight_dtype, ff);
   const int dparts = dgemm && gemm_decode_parts(c.weight_dtype, qkvw, d) <= 8 ? gemm_decode_parts(c.weight_dtype, qkvw, d) : 0;
@@ -456,16 +460,18 @@ int run_forward(dec_ctx* ctx, hipStream_t st, const BatchDev& b, const int32_t* 
     return launch_gemm(c.weight_dtype, epi, g, st);
   };
   // A of a normalising GEMM: the residual itself (decode GEMM) or the RMSNorm output
+  // (gain: the norm's gain, applied to xg by the product that wrote it)
   auto norm_input = [&](GemmArgs& g, const float* gain) {
+    (void)gain;
     if (dgemm) {
-      g.A = x; g.lda = d; g.gain = gain; g.ssq_in = ssq; g.eps = c.rms_eps;
+      g.A = xg; g.lda = d; g.ssq_in = ssq; g.eps = c.rms_eps;
     } else {
       g.A = h; g.lda = d;
     }
   };
 
   TLAUNCH(DEC_K_EMBED, launch_embed(tok_dev ? tok_dev : b.row_tok, N, c.vocab, d, c.weight_dtype, ctx->embed, x,
-                                    dgemm ? ssq : nullptr, st));
+                                    dgemm ? ssq : nullptr, dgemm ? xg : nullptr, ctx->layers[0].attn_norm, st));
   for (int l = 0; l < c.n_layers; ++l) {
     const LayerW& L = ctx->layers[l];
     if (!dgemm) TLAUNCH(DEC_K_RMSNORM, launch_rmsnorm(x, nullptr, N, d, L.attn_norm, c.rms_eps, h, act_bf16, st));
@@ -503,6 +509,7 @@ int run_forward(dec_ctx* ctx, hipStream_t st, const BatchDev& b, const int32_t* 
     g.A = o; g.lda = qw; g.M = N; g.N = d; g.K = qw;
     g.seg[0] = L.wo; g.nseg = 1; g.C = x; g.ldc = d;
     g.ssq_out = dgemm ? ssq : nullptr;
+    g.xg_out = dgemm ? xg : nullptr; g.gain_next = L.ffn_norm;
     TLAUNCH(DEC_K_GEMM_O, gemm(EPI_RESID, g));
     if (!dgemm) TLAUNCH(DEC_K_RMSNORM, launch_rmsnorm(x, nullptr, N, d, L.ffn_norm, c.rms_eps, h, act_bf16, st));
     g = GemmArgs{};
@@ -514,6 +521,8 @@ int run_forward(dec_ctx* ctx, hipStream_t st, const BatchDev& b, const int32_t* 
     g.A = act; g.lda = ff; g.M = N; g.N = d; g.K = ff;
     g.seg[0] = L.wd; g.nseg = 1; g.C = x; g.ldc = d;
     g.ssq_out = dgemm ? ssq : nullptr;
+    g.xg_out = dgemm ? xg : nullptr;
+    g.gain_next = l + 1 < c.n_layers ? ctx->layers[l + 1].attn_norm : ctx->final_norm;
     TLAUNCH(DEC_K_GEMM_DOWN, gemm(EPI_RESID, g));
   }
   if (b.n_out > 0 && logits) {

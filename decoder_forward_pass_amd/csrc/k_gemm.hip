@@ -303,11 +303,12 @@ __device__ __forceinline__ bf16x8 b_frag(const BRaw<WF>& r) {
 template <int WF, int EPI, int MT, int NKS, bool LDSA, int RPB = 16 * MT>
 __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
   static_assert(RPB == 16 * MT || (RPB == 8 && MT == 1 && LDSA), "8-row blocks: one 16-row MFMA tile, staged rows");
-  // STORE / SWIGLU read the float32 residual and normalise it on the fly (RMSNorm fused);
-  // RESID reads a bf16 activation and writes the sums of squares of the new residual.
+  // STORE / SWIGLU: A is xg = bf16(x * gain) and each output row is scaled by 1 / rms(x) (the
+  // deferred RMSNorm); RESID reads a bf16 activation and writes the sums of squares of the new
+  // residual and its gain-scaled bf16 copy for the next product.
   constexpr bool NORM = EPI != EPI_RESID;
   constexpr int NB = EPI == EPI_SWIGLU ? 2 : 1;
-  constexpr int ES = NORM ? 4 : 2;  // bytes per activation element
+  constexpr int ES = 2;  // bytes per activation element (bf16)
   constexpr int RED = kDecWaves * NB * MT * 4 * 64;
   __shared__ float red_s[LDSA ? 1 : RED];
   extern __shared__ __attribute__((aligned(16))) uint8_t s_dyn[];  // LDSA: [16 MT][K] staged, then partials
@@ -339,20 +340,22 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
   const bool active = wave < nw;
   // RESID: the residual values this thread updates in the epilogue, requested with the
   // operand loads instead of after the reduction
-  float xres = 0.f;
+  float xres = 0.f, gnext = 0.f;
   if constexpr (EPI == EPI_RESID) {
     if (threadIdx.x < MT * 256) {
       const int t = threadIdx.x, sl = t % 64;
       const int m = m0 + (t / 256) * 16 + (sl >> 4) * 4 + (t / 64) % 4, ncol = n0 + (sl & 15);
-      if (m < mend && ncol < a.N) xres = ((const float*)a.C)[(int64_t)m * a.ldc + ncol];
+      if (m < mend && ncol < a.N) {
+        xres = ((const float*)a.C)[(int64_t)m * a.ldc + ncol];
+        if (a.xg_out) gnext = a.gain_next[ncol];
+      }
     }
   }
   const int brow = min(br0 + (lane & 15), bm[0].rows - 1);
   const int kl = (lane >> 4) * 8;
   const int k0 = wave * NKS * 32 + kl;
   BRaw<WF> braw[NB][NKS];
-  u32x4 araw[LDSA ? 1 : MT][LDSA ? 1 : NKS][NORM ? 2 : 1];
-  float4 graw[NORM ? NKS : 1][2];
+  u32x4 araw[LDSA ? 1 : MT][LDSA ? 1 : NKS];
   float4 sraw[NORM ? 4 : 1];
   if (active) {
 #pragma unroll
@@ -363,25 +366,9 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int arow = min(m0 + mt * 16 + (lane & 15), M - 1);
-        if constexpr (NORM) {
-          const float* ap = (const float*)a.A + (int64_t)arow * a.lda + k0;
+        const uint16_t* ap = (const uint16_t*)a.A + (int64_t)arow * a.lda + k0;
 #pragma unroll
-          for (int i = 0; i < NKS; ++i) {
-            araw[mt][i][0] = *(const u32x4*)(ap + i * 32);
-            araw[mt][i][1] = *(const u32x4*)(ap + i * 32 + 4);
-          }
-        } else {
-          const uint16_t* ap = (const uint16_t*)a.A + (int64_t)arow * a.lda + k0;
-#pragma unroll
-          for (int i = 0; i < NKS; ++i) araw[mt][i][0] = *(const u32x4*)(ap + i * 32);
-        }
-      }
-    }
-    if constexpr (NORM) {
-#pragma unroll
-      for (int i = 0; i < NKS; ++i) {
-        graw[i][0] = *(const float4*)(a.gain + k0 + i * 32);
-        graw[i][1] = *(const float4*)(a.gain + k0 + i * 32 + 4);
+        for (int i = 0; i < NKS; ++i) araw[mt][i] = *(const u32x4*)(ap + i * 32);
       }
     }
   }
@@ -446,25 +433,8 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
       for (int nb = 0; nb < NB; ++nb) bf[nb] = b_frag<WF>(braw[nb][i]);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        bf16x8 af;
-        if constexpr (NORM) {
-          const float inv = s_inv[mt * 16 + (lane & 15)];
-          u32x4 xr[2];
-#pragma unroll
-          for (int h = 0; h < 2; ++h) xr[h] = LDSA ? lds_frag(mt * 16 + (lane & 15), k0 + i * 32, h) : araw[LDSA ? 0 : mt][LDSA ? 0 : i][h];
-          u32x4 w;
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const float* xv = (const float*)&xr[h];
-            const float* gv = (const float*)&graw[i][h];
-            w[2 * h] = pack_bf16x2(xv[0] * inv * gv[0], xv[1] * inv * gv[1]);
-            w[2 * h + 1] = pack_bf16x2(xv[2] * inv * gv[2], xv[3] * inv * gv[3]);
-          }
-          af = __builtin_bit_cast(bf16x8, w);
-        } else {
-          af = __builtin_bit_cast(bf16x8, LDSA ? lds_frag(mt * 16 + (lane & 15), k0 + i * 32, 0)
-                                               : araw[LDSA ? 0 : mt][LDSA ? 0 : i][0]);
-        }
+        const bf16x8 af = __builtin_bit_cast(bf16x8, LDSA ? lds_frag(mt * 16 + (lane & 15), k0 + i * 32, 0)
+                                                          : araw[LDSA ? 0 : mt][LDSA ? 0 : i]);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
           acc[nb][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf[nb], acc[nb][mt], 0, 0, 0);
@@ -498,6 +468,11 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
     const int ncol = n0 + (sl & 15);
     const bool in = m < mend && ncol < a.N;
     const int64_t o = (int64_t)m * a.ldc + ncol;
+    if constexpr (NORM) {  // the deferred RMSNorm of the row
+      const float inv = s_inv[mt * 16 + (sl >> 4) * 4 + r];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) v[nb] *= inv;
+    }
     if constexpr (EPI == EPI_STORE) {
       if (in) ((float*)a.C)[o] = v[0];
     } else if constexpr (EPI == EPI_RESID) {
@@ -505,6 +480,7 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
       if (in) {
         xn = xres + v[0];  // (each thread runs this loop body at most once: MT * 256 <= 512)
         ((float*)a.C)[o] = xn;
+        if (a.xg_out) a.xg_out[o] = f32_to_bf16_bits(xn * gnext);
       }
       if (a.ssq_out) {
         const float sq = group_sum<16>(xn * xn);
@@ -525,11 +501,11 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
 // ---- decode Q|K|V product split along K ------------------------------------------------------
 // Decode steps only. Block (nt, ks, z) computes, for 64 output columns (4 waves x 16) and the
 // rows of group z, the partial product over K-slice ks (NKS k-steps of 32, ascending, one
-// accumulator per output) and stores it as partial product ks. The normalised activation
-// slice (RMSNorm of the float32 residual: the row's 16-column sums of squares added by 8
-// threads in order and paired by a fixed DPP pattern, then x * inv * gain rounded to bf16) is
-// staged once per block in LDS. A block moves 64 columns x KC of weights and M x KC of
-// activations, so the whole residual is read K / KC times in all instead of once per 16 columns.
+// accumulator per output) and stores it, times the row's 1 / rms (the deferred RMSNorm: the
+// row's 16-column sums of squares added by 8 threads in order and paired by a fixed DPP
+// pattern), as partial product ks. The activation slice of xg = bf16(x * gain) is staged once
+// per block in LDS. A block moves 64 columns x KC of weights and M x KC of activations, so the
+// activations are read K / KC times in all instead of once per 16 columns.
 
 namespace {
 struct PartsPlan {
@@ -584,15 +560,15 @@ __global__ __launch_bounds__(256) void gemm_decode_parts_kernel(GemmArgs a, int6
 #pragma unroll
   for (int i = 0; i < NKS; ++i) braw[i] = load_b_raw<WF>(bm, brow, K, kb + i * 32 + kl);
 
-  // activation slice [R][KC]: RMSNorm(x) as bf16 into LDS
-  constexpr int F4 = R * KC / 4, PER = (F4 + 255) / 256;
-  float4 xv[PER];
+  // activation slice [R][KC] of xg (bf16, gain applied) into LDS, 16 bytes per thread per pass
+  constexpr int C8 = R * KC / 8, PER = (C8 + 255) / 256;
+  u32x4 xv[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
-    const int e = min(tid + 256 * j, F4 - 1), row = e / (KC / 4), c4 = e % (KC / 4);
-    xv[j] = *(const float4*)((const float*)a.A + (int64_t)min(m0 + row, M - 1) * a.lda + kb + 4 * c4);
+    const int e = min(tid + 256 * j, C8 - 1), row = e / (KC / 8), c8 = e % (KC / 8);
+    xv[j] = *(const u32x4*)((const uint16_t*)a.A + (int64_t)min(m0 + row, M - 1) * a.lda + kb + 8 * c8);
   }
-  // (32 rows per pass of the 256 threads)
+  // the rows' 1 / rms (deferred RMSNorm), 32 rows per pass of the 256 threads
   for (int rb = 0; rb < R; rb += 32) {
     const int nq = K / 16, per = (nq + 7) / 8;
     const int row = rb + (tid >> 3), sub = tid & 7;
@@ -603,19 +579,12 @@ __global__ __launch_bounds__(256) void gemm_decode_parts_kernel(GemmArgs a, int6
     ss = group_sum<8>(ss);
     if (row < R && sub == 0) s_inv[row] = 1.0f / sqrtf(ss / (float)K + a.eps);
   }
-  __syncthreads();
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const int e = tid + 256 * j;
-    if (e < F4) {
-      const int row = e / (KC / 4), c4 = e % (KC / 4);
-      const float inv = s_inv[row];
-      const float4 g = *(const float4*)(a.gain + kb + 4 * c4);
-      const float4 x = xv[j];
-      uint2 w;
-      w.x = pack_bf16x2(x.x * inv * g.x, x.y * inv * g.y);
-      w.y = pack_bf16x2(x.z * inv * g.z, x.w * inv * g.w);
-      *(uint2*)(sA + row * LS + 4 * c4) = w;
+    if (e < C8) {
+      const int row = e / (KC / 8), c8 = e % (KC / 8);
+      *(u32x4*)(sA + row * LS + 8 * c8) = xv[j];
     }
   }
   __syncthreads();
@@ -639,8 +608,8 @@ __global__ __launch_bounds__(256) void gemm_decode_parts_kernel(GemmArgs a, int6
   for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int m = m0 + mt * 16 + (lane >> 4) * 4 + r;
-      if (m < M) out[(int64_t)m * a.ldc + n] = acc[mt][r];
+      const int lr = mt * 16 + (lane >> 4) * 4 + r, m = m0 + lr;
+      if (m < M) out[(int64_t)m * a.ldc + n] = acc[mt][r] * s_inv[lr];
     }
 }
 
@@ -684,8 +653,8 @@ hipError_t launch_gemm_decode_parts(int wdtype, const GemmArgs& a, int64_t part_
 
 // ---- decode LM head ---------------------------------------------------------------------------
 // logits = RMSNorm(x) . E^T for the decode rows (M <= 64). A fixed grid of blocks of 16 waves:
-// each block normalises the M residual rows once (final gain; sum of squares over the full row,
-// added per thread in order and then by a fixed butterfly) into bf16 rows in LDS, then streams
+// each block stages the M rows of xg = bf16(x * final gain) once in LDS and takes each row's
+// 1 / rms from its sums of squares (the deferred RMSNorm, applied to the logits), then streams
 // its contiguous share of the vocabulary in tiles of 16 rows of E, the waves taking the tiles in
 // turn. A wave's tiles form one stream of weight-fragment groups (G k-steps each), the next
 // group loaded while the current one feeds the MFMAs, across tile boundaries too. Every logit is
@@ -699,30 +668,25 @@ __global__ __launch_bounds__(1024) void lmhead_decode(GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int M = a.M, K = a.K, KS = K + 8;
   const int rows = MT * 16;
-  // normalise: 32 threads per row (a wave half), each 1/32 of the row
+  // the rows of xg = bf16(x * final gain) into LDS, and each row's 1 / rms (the deferred
+  // RMSNorm): 32 threads per row (a wave half), each 1/32 of the row and of its sums of squares
+  __shared__ float s_inv[MT * 16];
   {
-    const int per = K / 32;
+    const int per = K / 32, nq = K / 16, qper = (nq + 31) / 32;
     for (int r0 = 0; r0 < rows; r0 += 32) {
       const int r = r0 + (threadIdx.x >> 5);
       const int c0 = (threadIdx.x & 31) * per;
       const bool live = r < rows;
-      const float* xr = (const float*)a.A + (int64_t)min(r, M - 1) * a.lda + c0;
+      const uint16_t* xr = (const uint16_t*)a.A + (int64_t)min(r, M - 1) * a.lda + c0;
+      const float* sp = a.ssq_in + (int64_t)min(r, M - 1) * nq;
+      const int q0 = (threadIdx.x & 31) * qper, q1 = min(nq, q0 + qper);
       float ss = 0.f;
-      if (live)
-        for (int j = 0; j < per; j += 4) {
-          const float4 v = *(const float4*)(xr + j);
-          ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
-        }
+      if (live) {
+        for (int j = q0; j < q1; ++j) ss += sp[j];
+        for (int j = 0; j < per; j += 8) *(u32x4*)(s_h + r * KS + c0 + j) = *(const u32x4*)(xr + j);
+      }
       ss = group_sum<32>(ss);
-      const float inv = 1.0f / sqrtf(ss / (float)K + a.eps);
-      if (live)
-        for (int j = 0; j < per; j += 4) {
-          const float4 v = *(const float4*)(xr + j);
-          const float4 g = *(const float4*)(a.gain + c0 + j);
-          uint32_t* d = (uint32_t*)(s_h + r * KS + c0 + j);
-          d[0] = pack_bf16x2(v.x * inv * g.x, v.y * inv * g.y);
-          d[1] = pack_bf16x2(v.z * inv * g.z, v.w * inv * g.w);
-        }
+      if (live && (threadIdx.x & 31) == 0) s_inv[r] = 1.0f / sqrtf(ss / (float)K + a.eps);
     }
   }
   __syncthreads();
@@ -769,7 +733,7 @@ __global__ __launch_bounds__(1024) void lmhead_decode(GemmArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int m = mt * 16 + (lane >> 4) * 4 + r;
-          if (m < M && ncol < a.N) ((float*)a.C)[(int64_t)m * a.ldc + ncol] = acc[mt][r];
+          if (m < M && ncol < a.N) ((float*)a.C)[(int64_t)m * a.ldc + ncol] = acc[mt][r] * s_inv[m];
         }
         acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
@@ -803,8 +767,8 @@ static hipError_t lmhead_go(const GemmArgs& a, hipStream_t s) {
 }
 
 bool lmhead_decode_supported(int wdtype, int M, int K) {
-  // each of 32 threads per row normalises K/32 columns in float4 steps
-  return (wdtype == DEC_BF16 || wdtype == DEC_UINT4_G32) && M <= 64 && K % 128 == 0 && (size_t)64 * (K + 8) * 2 <= 160 * 1024;
+  // each of 32 threads per row stages K/32 columns in 16-byte steps
+  return (wdtype == DEC_BF16 || wdtype == DEC_UINT4_G32) && M <= 64 && K % 256 == 0 && (size_t)64 * (K + 8) * 2 <= 160 * 1024;
 }
 
 hipError_t launch_lmhead_decode(int wdtype, const GemmArgs& a, hipStream_t s) {
@@ -823,14 +787,14 @@ hipError_t launch_lmhead_decode(int wdtype, const GemmArgs& a, hipStream_t s) {
 // LDS bytes of the staged-activation path (activation tile, or the wave partials if larger)
 template <int EPI, int MT>
 static size_t decode_lds_bytes(int K) {
-  const size_t act = (size_t)16 * MT * K * (EPI == EPI_RESID ? 2 : 4);
+  const size_t act = (size_t)16 * MT * K * 2;
   const size_t part = (size_t)kDecWaves * (EPI == EPI_SWIGLU ? 2 : 1) * MT * 4 * 64 * 4;
   return act > part ? act : part;
 }
 
 template <int EPI>
 static bool decode_staged(int K, size_t lds) {  // chunks per row a multiple of 16 (the swizzle), tile <= 128 KB
-  return (K * (EPI == EPI_RESID ? 2 : 4) / 16) % 16 == 0 && lds <= 128 * 1024;
+  return (K * 2 / 16) % 16 == 0 && lds <= 128 * 1024;
 }
 
 template <int WF, int EPI, int MT, int NKS, bool LDSA, int RPB>
@@ -904,7 +868,7 @@ hipError_t launch_gemm_decode(int wdtype, int epi, const GemmArgs& a, hipStream_
   // blocks of 16 rows when M <= 16, when the product has few column groups (twice the blocks
   // then share the weights), or when only a 16-row activation tile fits in LDS; a row's result
   // is the same either way
-  const size_t tile32 = (size_t)32 * a.K * (epi == EPI_RESID ? 2 : 4);
+  const size_t tile32 = (size_t)32 * a.K * 2;
   const bool rows16 = a.M <= 16 || (a.N + 15) / 16 < 128 || (tile32 > 128 * 1024 && tile32 / 2 <= 128 * 1024);
   const bool rows8 = epi == EPI_RESID && a.M > 8 && (a.N + 15) / 16 * ((a.M + 15) / 16) < 256;
   if (wdtype == DEC_BF16)

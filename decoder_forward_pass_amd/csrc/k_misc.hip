@@ -14,14 +14,17 @@ __device__ __forceinline__ void embed_row(const WMat& E, int t, int d, float* __
 
 template <int WF>
 __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ tok, int vocab, int d,
-                                                    WMat E, float* __restrict__ x, float* __restrict__ ssq) {
+                                                    WMat E, float* __restrict__ x, float* __restrict__ ssq,
+                                                    uint16_t* __restrict__ xg, const float* __restrict__ g) {
   const int r = blockIdx.x;
   const int t = tok[r];
   float* xr = x + (int64_t)r * d;
   if (t < 0 || t >= vocab) {
     for (int i = threadIdx.x; i < d; i += blockDim.x) xr[i] = __builtin_nanf("");
-    if (ssq)
+    if (ssq) {
       for (int i = threadIdx.x; i < d / 16; i += blockDim.x) ssq[(int64_t)r * (d / 16) + i] = __builtin_nanf("");
+      for (int i = threadIdx.x; i < d; i += blockDim.x) xg[(int64_t)r * d + i] = 0x7fc0;  // NaN
+    }
     return;
   }
   embed_row<WF>(E, t, d, xr);
@@ -33,6 +36,7 @@ __global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ 
       for (int j = 0; j < 16; ++j) s += xr[16 * i + j] * xr[16 * i + j];
       ssq[(int64_t)r * (d / 16) + i] = s;
     }
+    for (int i = threadIdx.x; i < d; i += blockDim.x) xg[(int64_t)r * d + i] = f32_to_bf16_bits(xr[i] * g[i]);
   }
 }
 
@@ -57,15 +61,16 @@ __device__ __forceinline__ void embed_row(const WMat& E, int t, int d, float* __
 }
 
 hipError_t launch_embed(const int32_t* tok, int n_rows, int vocab, int d, int wdtype, const WMat& E,
-                        float* x, float* ssq, hipStream_t s) {
+                        float* x, float* ssq, uint16_t* xg, const float* gain, hipStream_t s) {
   if (n_rows <= 0) return hipSuccess;
+  if (ssq && (!xg || !gain)) return hipErrorInvalidValue;
   dim3 g(n_rows), b(256);
   if (wdtype == DEC_F32)
-    embed_kernel<DEC_F32><<<g, b, 0, s>>>(tok, vocab, d, E, x, ssq);
+    embed_kernel<DEC_F32><<<g, b, 0, s>>>(tok, vocab, d, E, x, ssq, xg, gain);
   else if (wdtype == DEC_BF16)
-    embed_kernel<DEC_BF16><<<g, b, 0, s>>>(tok, vocab, d, E, x, ssq);
+    embed_kernel<DEC_BF16><<<g, b, 0, s>>>(tok, vocab, d, E, x, ssq, xg, gain);
   else
-    embed_kernel<DEC_UINT4_G32><<<g, b, 0, s>>>(tok, vocab, d, E, x, ssq);
+    embed_kernel<DEC_UINT4_G32><<<g, b, 0, s>>>(tok, vocab, d, E, x, ssq, xg, gain);
   return hipGetLastError();
 }
 

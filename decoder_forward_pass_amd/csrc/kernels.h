@@ -31,9 +31,10 @@ inline void launch_kernel(void (*kernel)(KA...), dim3 g, dim3 b, uint32_t shmem,
 }
 
 // x[r][:] = widened/dequantised E[tok[r]][:] as float32; an id outside [0, vocab) gives NaN.
-// ssq (optional, [n_rows][d/16]): sums of squares of each 16 columns of the row.
+// ssq (optional, [n_rows][d/16]): sums of squares of each 16 columns of the row; with it, xg
+// ([n_rows][d] bf16) receives x * g, the input of the first product's deferred RMSNorm.
 hipError_t launch_embed(const int32_t* tok, int n_rows, int vocab, int d, int wdtype, const WMat& E,
-                        float* x, float* ssq, hipStream_t s);
+                        float* x, float* ssq, uint16_t* xg, const float* g, hipStream_t s);
 
 // out[r][:] = x[rows ? rows[r] : r][:] / sqrt(mean(x^2) + eps) * g, stored as float32 or bf16.
 hipError_t launch_rmsnorm(const float* x, const int32_t* rows, int n, int d, const float* g, float eps,
@@ -106,13 +107,17 @@ struct GemmArgs {
   void* C;  // float32 [M][ldc] (STORE, RESID) or act dtype (SWIGLU)
   int ldc;
   bool c_bf16;  // SWIGLU output in bf16
-  // Decode GEMM only. STORE / SWIGLU: A is RMSNorm(x) computed on the fly from the float32
-  // residual x [M][K] (lda), the gain, and ssq_in, per-row sums of squares in K/16 partials
-  // of 16 columns [M][K/16]. RESID: ssq_out receives those partials of the new x [M][N/16].
-  const float* gain;
+  // Decode GEMM only: the RMSNorm in front of a product is deferred, RMSNorm(x) g W =
+  // diag(1 / rms(x)) (x g) W. STORE / SWIGLU with ssq_in: A is xg = bf16(x * g), the residual
+  // times the norm's gain [M][K] (lda), and each output row is scaled by 1 / sqrt(mean(x^2) +
+  // eps), the mean from ssq_in, x's per-row sums of squares in K/16 partials of 16 columns
+  // [M][K/16]. RESID: ssq_out receives those partials of the new x [M][N/16], and xg_out (if
+  // set) bf16(x_new * gain_next) [M][ldc] for the next product's deferred norm.
   const float* ssq_in;
   float* ssq_out;
   float eps;
+  const float* gain_next;
+  uint16_t* xg_out;
 };
 hipError_t launch_gemm(int wdtype, int epi, const GemmArgs& a, hipStream_t s);
 
@@ -131,14 +136,14 @@ bool gemm_decode_supported(int wdtype, int K);
 hipError_t launch_gemm_decode(int wdtype, int epi, const GemmArgs& a, hipStream_t s);
 
 // Decode Q|K|V product split along K: C + p * part_stride ([M][N] float32, p < parts) receives
-// the partial product of K-slice p; A is RMSNorm(x) computed from the float32 residual (a.A,
-// a.lda), a.gain and the 16-column sums of squares a.ssq_in. The number of slices follows
-// from (N, K) alone; the consumer adds the partials in slice order.
+// the partial product of K-slice p of RMSNorm(x) g W, taken as xg (a.A = bf16(x * g), a.lda)
+// times W with each row scaled by 1 / rms(x) from the 16-column sums of squares a.ssq_in. The
+// number of slices follows from (N, K) alone; the consumer adds the partials in slice order.
 int gemm_decode_parts(int wdtype, int N, int K);  // slices, or 0 when unsupported
 hipError_t launch_gemm_decode_parts(int wdtype, const GemmArgs& a, int64_t part_stride, hipStream_t s);
 
-// Decode LM head: logits[M][N] = RMSNorm(x)[M][K] . E^T with the norm computed from the float32
-// residual (a.A, a.lda) and a.gain inside each block; bf16 / uint4 E, M <= 64.
+// Decode LM head: logits[M][N] = RMSNorm(x)[M][K] . E^T, taken as xg (a.A = bf16(x * final
+// gain), a.lda) . E^T with each row scaled by 1 / rms(x) from a.ssq_in; bf16 / uint4 E, M <= 64.
 bool lmhead_decode_supported(int wdtype, int M, int K);
 hipError_t launch_lmhead_decode(int wdtype, const GemmArgs& a, hipStream_t s);
 
