@@ -164,9 +164,7 @@ Ws ws_layout(const dec_config& c) {
   w.meta = take(w.meta_ints * 4);
   w.x = take(R * d * 4);
   w.h = take(R * d * w.act_bytes);
-  // float32 Q|K|V product (prefill rows), or the decode step's partial products along K
-  const int dparts = gemm_decode_parts(c.weight_dtype, (int)qkvw, (int)d);
-  w.qkv = take(std::max(R, (size_t)std::max(dparts, 1) * S) * qkvw * 4);
+  w.qkv = take(std::max(R, S) * qkvw * 4);  // float32 Q|K|V product
   w.q = take(R * qw * w.kv_el);
   w.o = take(R * qw * w.act_bytes);
   w.a = take(R * ff * w.act_bytes);
@@ -446,7 +444,6 @@ int run_forward(dec_ctx* ctx, hipStream_t st, const BatchDev& b, const int32_t* 
   // tile GEMM after an RMSNorm launch.
   const bool dgemm = decode && gemm_decode_supported(c.weight_dtype, d) &&
                      gemm_decode_supported(c.weight_dtype, qw) && gemm_decode_supported(c.weight_dtype, ff);
-  const int dparts = dgemm && gemm_decode_parts(c.weight_dtype, qkvw, d) <= 8 ? gemm_decode_parts(c.weight_dtype, qkvw, d) : 0;
   // Prefill calls with bf16 / uint4 weights take the 256 x 256 tile GEMM, which also applies
   // the q/k norm, RoPE and the KV write in its Q|K|V epilogue (chosen by the configuration
   // alone, so every prefill call of a model computes the same way).
@@ -483,11 +480,6 @@ int run_forward(dec_ctx* ctx, hipStream_t st, const BatchDev& b, const int32_t* 
     QkRopeArgs qa{qkv, L.q_norm, L.k_norm, rope, q, pool, l, H, Hkv, D, c.rms_eps, kv_f16, b};
     if (big) {
       TLAUNCH(DEC_K_GEMM_QKV, launch_gemm_big(c.weight_dtype, EPI_QKV, g, &qa, st));
-    } else if (dparts) {
-      // decode: K split into partial products that the attention kernel adds up
-      qa.parts = dparts;
-      qa.part_stride = (int64_t)N * qkvw;
-      TLAUNCH(DEC_K_GEMM_QKV, launch_gemm_decode_parts(c.weight_dtype, g, qa.part_stride, st));
     } else {
       TLAUNCH(DEC_K_GEMM_QKV, gemm(EPI_STORE, g));
     }

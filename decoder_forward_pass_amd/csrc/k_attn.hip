@@ -420,8 +420,7 @@ __global__ __launch_bounds__((64 * DecodeGeom<KVT, D, GROUP>::NWV)) void attn_de
   using FromLds = std::integral_constant<int, 1>;
   using FromMem = std::integral_constant<int, 2>;
 
-  // The row's Q|K|V product (the sum of qk.parts partial products, added in order) gives
-  // GROUP + 2 prologue items: query heads kvh*GROUP + it for it < GROUP, then the key and the
+  // The row's Q|K|V product gives GROUP + 2 prologue items: query heads kvh*GROUP + it for it < GROUP, then the key and the
   // value; wave w takes items w, w + NWV, ... . An item's loads are issued ahead of the wave's
   // first pool loads, so that they are not queued behind them; the waves without items
   // request their first NBUF chunks at once.
@@ -429,26 +428,21 @@ __global__ __launch_bounds__((64 * DecodeGeom<KVT, D, GROUP>::NWV)) void attn_de
   constexpr int NBUF = G::NBUF, NITEM = GROUP + 2;
   u32x4 kb[NBUF][KPG], vb[NBUF][KPG];
   struct Item {
-    float p1[8], p2[8];
+    float x1, x2;  // the lane's two channels (j, j + D/2) of the item's head
     float2 cs;
     float g1, g2;  // q or k norm gains of the lane's two channels
     int newblk;
   };
   auto item_load = [&](int it, Item& t) __attribute__((always_inline)) {
+    t.x1 = t.x2 = 0.f;
     t.cs = make_float2(1.f, 0.f);
     t.g1 = t.g2 = 1.f;
     t.newblk = 0;
     if (lane < half) {
       const int hh = it < GROUP ? kvh * GROUP + it : (it == GROUP ? H + kvh : H + Hkv + kvh);
       const float* src = qk.qkv + (int64_t)row * (H + 2 * Hkv) * D + (int64_t)hh * D;
-#pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        if (p < qk.parts) {
-          const float* sp = src + (int64_t)p * qk.part_stride;
-          t.p1[p] = sp[lane];
-          t.p2[p] = sp[lane + half];
-        }
-      }
+      t.x1 = src[lane];
+      t.x2 = src[lane + half];
       if (it <= GROUP) {
         const float* g = it < GROUP ? qk.q_norm : qk.k_norm;
         t.cs = qk.rope[(int64_t)pos * half + lane];
@@ -462,18 +456,7 @@ __global__ __launch_bounds__((64 * DecodeGeom<KVT, D, GROUP>::NWV)) void attn_de
   // format into LDS, and the key and value written to the pool at (table[pos / B], pos % B)
   // for later steps
   auto item_finish = [&](int it, const Item& t) __attribute__((always_inline)) {
-    float x1 = 0.f, x2 = 0.f;
-    if (lane < half) {
-      x1 = t.p1[0];
-      x2 = t.p2[0];
-#pragma unroll
-      for (int p = 1; p < 8; ++p) {
-        if (p < qk.parts) {
-          x1 += t.p1[p];
-          x2 += t.p2[p];
-        }
-      }
-    }
+    float x1 = lane < half ? t.x1 : 0.f, x2 = lane < half ? t.x2 : 0.f;
     if (it <= GROUP) norm_rope_pair_g(x1, x2, t.g1, t.g2, t.cs, lane, D, qk.eps);
     if (lane < half) {
       KVT* dst = s_q[it];

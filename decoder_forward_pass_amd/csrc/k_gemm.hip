@@ -498,159 +498,6 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
   }
 }
 
-// ---- decode Q|K|V product split along K ------------------------------------------------------
-// Decode steps only. Block (nt, ks, z) computes, for 64 output columns (4 waves x 16) and the
-// rows of group z, the partial product over K-slice ks (NKS k-steps of 32, ascending, one
-// accumulator per output) and stores it, times the row's 1 / rms (the deferred RMSNorm: the
-// row's 16-column sums of squares added by 8 threads in order and paired by a fixed DPP
-// pattern), as partial product ks. The activation slice of xg = bf16(x * gain) is staged once
-// per block in LDS. A block moves 64 columns x KC of weights and M x KC of activations, so the
-// activations are read K / KC times in all instead of once per 16 columns.
-
-namespace {
-struct PartsPlan {
-  int ks, nks;
-};
-PartsPlan parts_plan(int N, int K) {
-  PartsPlan p{0, 0};
-  if (N % 64 || K % 32) return p;
-  const int ksteps = K / 32, ntiles = N / 64;
-  int ks = 1;
-  while (ks < 8 && ntiles * ks < 256) ks *= 2;  // aim at >= 256 blocks
-  while (ks > 1 && ksteps % ks) ks >>= 1;
-  while (ksteps / ks > 16 && ks < 8 && ksteps % (2 * ks) == 0) ks *= 2;
-  const int nks = ksteps / ks;
-  if (ksteps % ks || nks > 16 || (nks != 1 && nks != 2 && nks != 4 && nks != 8 && nks != 16 && nks != 3 &&
-                                  nks != 6 && nks != 12))
-    return p;
-  p.ks = ks;
-  p.nks = nks;
-  return p;
-}
-}  // namespace
-
-template <int WF, int MT, int NKS>
-__global__ __launch_bounds__(256) void gemm_decode_parts_kernel(GemmArgs a, int64_t part_stride) {
-  constexpr int R = MT * 16, KC = NKS * 32, LS = KC + 8;  // LDS row stride in bf16 (padded)
-  __shared__ __attribute__((aligned(16))) uint16_t sA[R * LS];
-  __shared__ float s_inv[R];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nt = blockIdx.x, ks = blockIdx.y, z = blockIdx.z;
-  const int M = a.M, K = a.K, m0 = z * R, kb = ks * KC;
-
-  // weight fragments of this wave's 16 columns over the slice, all requested up front
-  const int n0 = nt * 64;
-  WMat bm;
-  int base = 0;
-  if (a.nseg > 1 && n0 >= a.seg[0].rows) {
-    base = a.seg[0].rows;
-    if (a.nseg > 2 && n0 >= base + a.seg[1].rows) {
-      base += a.seg[1].rows;
-      bm = a.seg[2];
-    } else {
-      bm = a.seg[1];
-    }
-  } else {
-    bm = a.seg[0];
-  }
-  const int brow = min(n0 - base + wave * 16 + (lane & 15), bm.rows - 1);
-  const int kl = (lane >> 4) * 8;
-  BRaw<WF> braw[NKS];
-#pragma unroll
-  for (int i = 0; i < NKS; ++i) braw[i] = load_b_raw<WF>(bm, brow, K, kb + i * 32 + kl);
-
-  // activation slice [R][KC] of xg (bf16, gain applied) into LDS, 16 bytes per thread per pass
-  constexpr int C8 = R * KC / 8, PER = (C8 + 255) / 256;
-  u32x4 xv[PER];
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int e = min(tid + 256 * j, C8 - 1), row = e / (KC / 8), c8 = e % (KC / 8);
-    xv[j] = *(const u32x4*)((const uint16_t*)a.A + (int64_t)min(m0 + row, M - 1) * a.lda + kb + 8 * c8);
-  }
-  // the rows' 1 / rms (deferred RMSNorm), 32 rows per pass of the 256 threads
-  for (int rb = 0; rb < R; rb += 32) {
-    const int nq = K / 16, per = (nq + 7) / 8;
-    const int row = rb + (tid >> 3), sub = tid & 7;
-    const float* sp = a.ssq_in + (int64_t)min(m0 + min(row, R - 1), M - 1) * nq;
-    float ss = 0.f;
-    const int j1 = min(nq, (sub + 1) * per);
-    for (int j = sub * per; j < j1; ++j) ss += sp[j];
-    ss = group_sum<8>(ss);
-    if (row < R && sub == 0) s_inv[row] = 1.0f / sqrtf(ss / (float)K + a.eps);
-  }
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const int e = tid + 256 * j;
-    if (e < C8) {
-      const int row = e / (KC / 8), c8 = e % (KC / 8);
-      *(u32x4*)(sA + row * LS + 8 * c8) = xv[j];
-    }
-  }
-  __syncthreads();
-
-  f32x4 acc[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < NKS; ++i) {
-    const bf16x8 bf = b_frag<WF>(braw[i]);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const bf16x8 af = __builtin_bit_cast(bf16x8, *(const u32x4*)(sA + (mt * 16 + (lane & 15)) * LS + i * 32 + kl));
-      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc[mt], 0, 0, 0);
-    }
-  }
-  // partial product ks, rows m0.., columns n0 + wave * 16 + (lane & 15)
-  float* out = (float*)a.C + (int64_t)ks * part_stride;
-  const int n = n0 + wave * 16 + (lane & 15);
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int lr = mt * 16 + (lane >> 4) * 4 + r, m = m0 + lr;
-      if (m < M) out[(int64_t)m * a.ldc + n] = acc[mt][r] * s_inv[lr];
-    }
-}
-
-template <int WF, int MT>
-static hipError_t parts_go(const GemmArgs& a, const PartsPlan& p, int64_t part_stride, hipStream_t s) {
-  dim3 g(a.N / 64, p.ks, (a.M + 16 * MT - 1) / (16 * MT)), b(256);
-  switch (p.nks) {
-    case 1: gemm_decode_parts_kernel<WF, MT, 1><<<g, b, 0, s>>>(a, part_stride); break;
-    case 2: gemm_decode_parts_kernel<WF, MT, 2><<<g, b, 0, s>>>(a, part_stride); break;
-    case 3: gemm_decode_parts_kernel<WF, MT, 3><<<g, b, 0, s>>>(a, part_stride); break;
-    case 4: gemm_decode_parts_kernel<WF, MT, 4><<<g, b, 0, s>>>(a, part_stride); break;
-    case 6: gemm_decode_parts_kernel<WF, MT, 6><<<g, b, 0, s>>>(a, part_stride); break;
-    case 8: gemm_decode_parts_kernel<WF, MT, 8><<<g, b, 0, s>>>(a, part_stride); break;
-    case 12: gemm_decode_parts_kernel<WF, MT, 12><<<g, b, 0, s>>>(a, part_stride); break;
-    case 16: gemm_decode_parts_kernel<WF, MT, 16><<<g, b, 0, s>>>(a, part_stride); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
-}
-
-template <int WF>
-static hipError_t parts_mt(const GemmArgs& a, const PartsPlan& p, int64_t part_stride, hipStream_t s) {
-  if (a.M <= 16) return parts_go<WF, 1>(a, p, part_stride, s);
-  if (a.M <= 32) return parts_go<WF, 2>(a, p, part_stride, s);
-  return parts_go<WF, 4>(a, p, part_stride, s);
-}
-
-int gemm_decode_parts(int wdtype, int N, int K) {
-  if (wdtype != DEC_BF16 && wdtype != DEC_UINT4_G32) return 0;
-  return parts_plan(N, K).ks;
-}
-
-hipError_t launch_gemm_decode_parts(int wdtype, const GemmArgs& a, int64_t part_stride, hipStream_t s) {
-  if (a.M <= 0 || a.N <= 0) return hipSuccess;
-  const PartsPlan p = parts_plan(a.N, a.K);
-  if (!p.ks) return hipErrorInvalidValue;
-  if (wdtype == DEC_BF16) return parts_mt<DEC_BF16>(a, p, part_stride, s);
-  if (wdtype == DEC_UINT4_G32) return parts_mt<DEC_UINT4_G32>(a, p, part_stride, s);
-  return hipErrorInvalidValue;
-}
-
 // ---- decode LM head ---------------------------------------------------------------------------
 // logits = RMSNorm(x) . E^T for the decode rows (M <= 64). A fixed grid of blocks of 16 waves:
 // each block stages the M rows of xg = bf16(x * final gain) once in LDS and takes each row's

@@ -42,7 +42,7 @@ hipError_t launch_rmsnorm(const float* x, const int32_t* rows, int n, int d, con
 
 // Per-head q/k RMSNorm + split-halves RoPE on q and k, then q -> q_out and k, v -> pool.
 struct QkRopeArgs {
-  const float* qkv;  // [n_rows][(H + 2 Hkv) D], or `parts` such partial products (see below)
+  const float* qkv;  // [n_rows][(H + 2 Hkv) D]
   const float* q_norm;
   const float* k_norm;
   const float2* rope;  // [max_context][D/2] (cos, sin)
@@ -53,8 +53,6 @@ struct QkRopeArgs {
   float eps;
   bool kv_f16;
   BatchDev b;
-  int parts = 1;            // decode attention: qkv holds this many partial products, added in order
-  int64_t part_stride = 0;  // elements between consecutive partial products
 };
 hipError_t launch_qk_rope_kv(const QkRopeArgs& a, hipStream_t s);
 
@@ -134,13 +132,6 @@ hipError_t launch_gemm_big(int wdtype, int epi, const GemmArgs& a, const QkRopeA
 // summed in wave order; bf16 and uint4 weights, K/32 with a supported per-wave step count.
 bool gemm_decode_supported(int wdtype, int K);
 hipError_t launch_gemm_decode(int wdtype, int epi, const GemmArgs& a, hipStream_t s);
-
-// Decode Q|K|V product split along K: C + p * part_stride ([M][N] float32, p < parts) receives
-// the partial product of K-slice p of RMSNorm(x) g W, taken as xg (a.A = bf16(x * g), a.lda)
-// times W with each row scaled by 1 / rms(x) from the 16-column sums of squares a.ssq_in. The
-// number of slices follows from (N, K) alone; the consumer adds the partials in slice order.
-int gemm_decode_parts(int wdtype, int N, int K);  // slices, or 0 when unsupported
-hipError_t launch_gemm_decode_parts(int wdtype, const GemmArgs& a, int64_t part_stride, hipStream_t s);
 
 // Decode LM head: logits[M][N] = RMSNorm(x)[M][K] . E^T, taken as xg (a.A = bf16(x * final
 // gain), a.lda) . E^T with each row scaled by 1 / rms(x) from a.ssq_in; bf16 / uint4 E, M <= 64.
