@@ -309,6 +309,10 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
   constexpr bool NORM = EPI != EPI_RESID;
   constexpr int NB = EPI == EPI_SWIGLU ? 2 : 1;
   constexpr int ES = 2;  // bytes per activation element (bf16)
+  // bf16 weights of single-matrix products staged in LDS as well (the block's 16 rows, same
+  // swizzle), right after the activation rows; gate/up (measured slower staged: 128 KB of LDS
+  // per block) and uint4 weights are loaded into registers
+  constexpr bool BDMA = LDSA && WF == DEC_BF16 && NB == 1;
   constexpr int RED = kDecWaves * NB * MT * 4 * 64;
   __shared__ float red_s[LDSA ? 1 : RED];
   extern __shared__ __attribute__((aligned(16))) uint8_t s_dyn[];  // LDSA: [16 MT][K] staged, then partials
@@ -354,14 +358,16 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
   const int brow = min(br0 + (lane & 15), bm[0].rows - 1);
   const int kl = (lane >> 4) * 8;
   const int k0 = wave * NKS * 32 + kl;
-  BRaw<WF> braw[NB][NKS];
+  BRaw<WF> braw[BDMA ? 1 : NB][BDMA ? 1 : NKS];
   u32x4 araw[LDSA ? 1 : MT][LDSA ? 1 : NKS];
   float4 sraw[NORM ? 4 : 1];
   if (active) {
+    if constexpr (!BDMA) {
 #pragma unroll
-    for (int i = 0; i < NKS; ++i)
+      for (int i = 0; i < NKS; ++i)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) braw[nb][i] = load_b_raw<WF>(bm[nb], brow, K, k0 + i * 32);
+        for (int nb = 0; nb < NB; ++nb) braw[nb][i] = load_b_raw<WF>(bm[nb], brow, K, k0 + i * 32);
+    }
     if constexpr (!LDSA) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
@@ -380,6 +386,19 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
       const uint8_t* src = (const uint8_t*)a.A + ((int64_t)min(m0 + r, M - 1) * a.lda) * ES + c * 16;
       __builtin_amdgcn_global_load_lds((const void*)src, (void __attribute__((address_space(3)))*)(s_dyn + j * 1024),
                                        16, 0, 0);
+    }
+    if constexpr (BDMA) {
+      // the weight rows br0 .. br0 + 15 of each matrix, at byte offset RPB * cpr * 16
+      const int nb_ins = NB * 16 * cpr / 64;
+      for (int j = wave; j < nb_ins; j += kDecWaves) {
+        const int slot = j * 64 + lane, nb = slot / (16 * cpr), rem = slot % (16 * cpr);
+        const int r = rem / cpr, pc = rem % cpr, c = pc ^ (r & 15);
+        const WMat& w = nb == 0 ? bm[0] : bm[NB - 1];
+        const uint8_t* src = (const uint8_t*)w.w + (int64_t)min(br0 + r, w.rows - 1) * K * 2 + c * 16;
+        __builtin_amdgcn_global_load_lds((const void*)src,
+                                         (void __attribute__((address_space(3)))*)(s_dyn + RPB * cpr * 16 + j * 1024),
+                                         16, 0, 0);
+      }
     }
   }
   // the rows' sums of squares: 4 threads per row, each adding a quarter of the row's K/16
@@ -420,6 +439,11 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
     const int c = (k * ES) / 16 + h;
     return *(const u32x4*)(s_dyn + ((int64_t)r * cpr + (c ^ (r & 15))) * 16);
   };
+  // fragment of weight row n (local) of matrix nb, 8 values from k, from the staged weights
+  auto lds_bfrag = [&](int nb, int n, int k) -> u32x4 {
+    const int c = k / 8;
+    return *(const u32x4*)(s_dyn + RPB * cpr * 16 + ((int64_t)(nb * 16 + n) * cpr + (c ^ (n & 15))) * 16);
+  };
   f32x4 acc[NB][MT];
   if (active) {
 #pragma unroll
@@ -430,7 +454,12 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
     for (int i = 0; i < NKS; ++i) {
       bf16x8 bf[NB];
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) bf[nb] = b_frag<WF>(braw[nb][i]);
+      for (int nb = 0; nb < NB; ++nb) {
+        if constexpr (BDMA)
+          bf[nb] = __builtin_bit_cast(bf16x8, lds_bfrag(nb, lane & 15, k0 + i * 32));
+        else
+          bf[nb] = b_frag<WF>(braw[BDMA ? 0 : nb][BDMA ? 0 : i]);
+      }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const bf16x8 af = __builtin_bit_cast(bf16x8, LDSA ? lds_frag(mt * 16 + (lane & 15), k0 + i * 32, 0)
@@ -631,28 +660,30 @@ hipError_t launch_lmhead_decode(int wdtype, const GemmArgs& a, hipStream_t s) {
   return lmhead_go<DEC_UINT4_G32, 4>(a, s);
 }
 
-// LDS bytes of the staged-activation path (activation tile, or the wave partials if larger)
-template <int EPI, int MT>
-static size_t decode_lds_bytes(int K) {
-  const size_t act = (size_t)16 * MT * K * 2;
-  const size_t part = (size_t)kDecWaves * (EPI == EPI_SWIGLU ? 2 : 1) * MT * 4 * 64 * 4;
+// LDS bytes of the staged path: the activation rows (rpb) and, for bf16 weights, the weight
+// rows (16 per matrix), or the wave partials if larger
+template <int WF, int EPI, int MT>
+static size_t decode_lds_bytes(int K, int rpb) {
+  const size_t nb = EPI == EPI_SWIGLU ? 2 : 1;
+  const size_t act = (size_t)rpb * K * 2 + (WF == DEC_BF16 && nb == 1 ? 16 * K * 2 : 0);
+  const size_t part = (size_t)kDecWaves * nb * MT * 4 * 64 * 4;
   return act > part ? act : part;
 }
 
 template <int EPI>
-static bool decode_staged(int K, size_t lds) {  // chunks per row a multiple of 16 (the swizzle), tile <= 128 KB
-  return (K * 2 / 16) % 16 == 0 && lds <= 128 * 1024;
+static bool decode_staged(int K, size_t lds) {  // chunks per row a multiple of 16 (the swizzle), within LDS
+  return (K * 2 / 16) % 16 == 0 && lds <= 159 * 1024;  // (1 KB left for the kernel's static LDS)
 }
 
 template <int WF, int EPI, int MT, int NKS, bool LDSA, int RPB>
 static hipError_t gemm_decode_kernel_launch(const GemmArgs& a, int nw, dim3 g, size_t lds, hipStream_t s) {
   if constexpr (LDSA) {
-    static bool attr = false;
-    if (!attr) {
+    static size_t limit = 0;  // the dynamic LDS limit raised so far for this instantiation
+    if (lds > limit) {
       hipError_t e = hipFuncSetAttribute((const void*)gemm_decode<WF, EPI, MT, NKS, true, RPB>,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
-      attr = true;
+      limit = lds;
     }
   }
   launch_kernel(gemm_decode<WF, EPI, MT, NKS, LDSA, RPB>, g, dim3(512), (uint32_t)(LDSA ? lds : 0), s, a, nw);
@@ -663,10 +694,12 @@ static hipError_t gemm_decode_kernel_launch(const GemmArgs& a, int nw, dim3 g, s
 // all on one XCD, so the tile's weights come from HBM once and from L2 after)
 template <int WF, int EPI, int MT, int NKS>
 static hipError_t gemm_decode_launch(const GemmArgs& a, int nw, bool rows8, hipStream_t s) {
-  const size_t lds = decode_lds_bytes<EPI, MT>(a.K);
+  const size_t lds = decode_lds_bytes<WF, EPI, MT>(a.K, 16 * MT);
   if constexpr (EPI == EPI_RESID && MT == 1) {
-    if (rows8 && decode_staged<EPI>(a.K, lds))
-      return gemm_decode_kernel_launch<WF, EPI, 1, NKS, true, 8>(a, nw, dim3((a.N + 15) / 16, (a.M + 7) / 8), lds, s);
+    // (the MFMA tile reads activation rows 8..15 too: the allocation covers 16 rows)
+    const size_t lds8 = std::max(decode_lds_bytes<WF, EPI, 1>(a.K, 8), (size_t)16 * a.K * 2);
+    if (rows8 && decode_staged<EPI>(a.K, lds8))
+      return gemm_decode_kernel_launch<WF, EPI, 1, NKS, true, 8>(a, nw, dim3((a.N + 15) / 16, (a.M + 7) / 8), lds8, s);
   }
   const dim3 g((a.N + 15) / 16, (a.M + 16 * MT - 1) / (16 * MT));
   if (decode_staged<EPI>(a.K, lds)) return gemm_decode_kernel_launch<WF, EPI, MT, NKS, true, 16 * MT>(a, nw, g, lds, s);
