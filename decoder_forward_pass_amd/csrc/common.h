@@ -70,6 +70,16 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// ---- greedy choice ("Candle model runner" 2.6: greedy takes the argmax, ties to the lowest
+// id). Keeps (bv, bi) or takes (v, i) when v is larger, or equal with a lower id; NaN never
+// wins. The choice is the same in any order of combination.
+__device__ __forceinline__ void greedy_better(float& bv, int& bi, float v, int i) {
+  if (v > bv || (v == bv && i < bi)) {
+    bv = v;
+    bi = i;
+  }
+}
+
 // ---- wave reductions (fixed butterfly order: deterministic) -------------------------------
 template <int WIDTH>
 __device__ __forceinline__ float wave_sum(float v) {

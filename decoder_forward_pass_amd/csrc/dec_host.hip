@@ -173,7 +173,7 @@ Ws ws_layout(const dec_config& c) {
   w.flash = c.kv_dtype == DEC_F16 && attn_prefill_supported(c.head_dim, c.n_heads / c.n_kv_heads);
   const size_t prow = w.flash ? 0 : R;
   w.part = take(prow * H * (size_t)w.nch_max * (D + 2) * 4);
-  w.amax = take(argmax_scratch_bytes((int)R));
+  w.amax = take(argmax_scratch_bytes((int)R, (int)S));
   w.ssq = take(S * (d / 16) * 4);  // decode: sums of squares of the residual in 16-column partials
   w.xg = take(S * d * 2);          // decode: bf16(residual * the next norm's gain)
   w.total = off;
@@ -528,12 +528,26 @@ int run_forward(dec_ctx* ctx, hipStream_t st, const BatchDev& b, const int32_t* 
     }
     g.M = b.n_out; g.N = c.vocab; g.K = d;
     g.seg[0] = ctx->embed; g.nseg = 1; g.C = logits; g.ldc = c.vocab;
+    // decode with greedy ids: the LM head writes per-block candidates and one pass picks them
+    const int cand = dgemm && next && lmhead_decode_supported(c.weight_dtype, b.n_out, d)
+                         ? lmhead_decode_parts(b.n_out, c.vocab)
+                         : 0;
+    float* cand_v = (float*)(ctx->wsp + w.amax);
+    int32_t* cand_i = (int32_t*)(cand_v + (size_t)b.n_out * std::max(cand, 1));
+    if (cand) {
+      g.am_v = cand_v;
+      g.am_i = cand_i;
+    }
     if (dgemm && lmhead_decode_supported(c.weight_dtype, b.n_out, d)) {
       TLAUNCH(DEC_K_GEMM_LMHEAD, launch_lmhead_decode(c.weight_dtype, g, st));
     } else {
       TLAUNCH(DEC_K_GEMM_LMHEAD, gemm(EPI_STORE, g));
     }
-    if (next) TLAUNCH(DEC_K_ARGMAX, launch_argmax(logits, b.n_out, c.vocab, next, ctx->wsp + w.amax, st));
+    if (next && cand) {
+      TLAUNCH(DEC_K_ARGMAX, launch_argmax_final(cand_v, cand_i, b.n_out, cand, next, st));
+    } else if (next) {
+      TLAUNCH(DEC_K_ARGMAX, launch_argmax(logits, b.n_out, c.vocab, next, ctx->wsp + w.amax, st));
+    }
   }
   return DEC_OK;
 }

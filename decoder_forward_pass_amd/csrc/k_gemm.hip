@@ -584,6 +584,19 @@ __global__ __launch_bounds__(1024) void lmhead_decode(GemmArgs a) {
   f32x4 acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // greedy candidates (a.am_v set, MT <= 2): per lane, the best logit and id of its column over
+  // the tiles it computes, for each of its rows
+  constexpr bool AMX = MT <= 2;
+  const bool amx = AMX && a.am_v != nullptr;
+  float bv[AMX ? MT : 1][4];
+  int bi[AMX ? MT : 1][4];
+#pragma unroll
+  for (int mt = 0; mt < (AMX ? MT : 1); ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      bv[mt][r] = -__builtin_inff();
+      bi[mt][r] = 0x7fffffff;
+    }
   BRaw<WF> cur[G], nxt[G];
   if (total > 0) load_group(0, cur);
   for (int j = 0; j < total; ++j) {
@@ -609,7 +622,12 @@ __global__ __launch_bounds__(1024) void lmhead_decode(GemmArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int m = mt * 16 + (lane >> 4) * 4 + r;
-          if (m < M && ncol < a.N) ((float*)a.C)[(int64_t)m * a.ldc + ncol] = acc[mt][r] * s_inv[m];
+          const float logit = acc[mt][r] * s_inv[m];
+          if (m < M && ncol < a.N) {
+            ((float*)a.C)[(int64_t)m * a.ldc + ncol] = logit;
+            if constexpr (AMX)
+              if (amx) greedy_better(bv[AMX ? mt : 0][r], bi[AMX ? mt : 0][r], logit, ncol);
+          }
         }
         acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
@@ -617,7 +635,53 @@ __global__ __launch_bounds__(1024) void lmhead_decode(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < G; ++i) cur[i] = nxt[i];
   }
+  if constexpr (AMX) {
+    if (amx) {
+      // the 16 lanes of a row group (distinct columns), then the 16 waves through LDS, then one
+      // candidate per (row, block)
+      __shared__ float s_bv[16][MT * 16];
+      __shared__ int s_bi[16][MT * 16];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+#pragma unroll
+          for (int o = 1; o < 16; o <<= 1) {
+            const float v = __shfl_xor(bv[mt][r], o, 64);
+            const int i = __shfl_xor(bi[mt][r], o, 64);
+            greedy_better(bv[mt][r], bi[mt][r], v, i);
+          }
+          if ((lane & 15) == 0) {
+            s_bv[wave][mt * 16 + (lane >> 4) * 4 + r] = bv[mt][r];
+            s_bi[wave][mt * 16 + (lane >> 4) * 4 + r] = bi[mt][r];
+          }
+        }
+      __syncthreads();
+      const int m = threadIdx.x;
+      if (m < MT * 16 && m < M) {
+        float v = s_bv[0][m];
+        int i = s_bi[0][m];
+        for (int w = 1; w < 16; ++w) greedy_better(v, i, s_bv[w][m], s_bi[w][m]);
+        a.am_v[(int64_t)m * gridDim.x + blockIdx.x] = v;
+        a.am_i[(int64_t)m * gridDim.x + blockIdx.x] = i;
+      }
+    }
+  }
 }
+
+// one block per compute unit, or fewer when the vocabulary is small
+static int lmhead_blocks(int N) {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+  }
+  return std::max(1, std::min(std::min(cus, kMaxArgmaxParts), (N + 255) / 256));
+}
+
+int lmhead_decode_parts(int M, int N) { return M >= 1 && M <= 32 ? lmhead_blocks(N) : 0; }
 
 template <int WF, int MT>
 static hipError_t lmhead_go(const GemmArgs& a, hipStream_t s) {
@@ -629,15 +693,7 @@ static hipError_t lmhead_go(const GemmArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr = true;
   }
-  // one block per compute unit, or fewer when the vocabulary is small
-  static int cus = 0;
-  if (!cus) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-  }
-  const int blocks = std::max(1, std::min(cus, (a.N + 255) / 256));
+  const int blocks = lmhead_blocks(a.N);
   launch_kernel(lmhead_decode<WF, MT>, dim3(blocks), dim3(1024), (uint32_t)lds, s, a);
   return hipGetLastError();
 }

@@ -2,6 +2,8 @@
 // q/k RMSNorm + split-halves RoPE + paged KV write, greedy argmax, and the
 // debug dequantisation. Every kernel handles each row independently, so a
 // row's result does not depend on the rest of the batch.
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace dec {
@@ -237,12 +239,6 @@ hipError_t launch_qk_rope_kv(const QkRopeArgs& a, hipStream_t s) {
 // ---- greedy argmax ("Candle model runner" 2.6: greedy takes the argmax, ties to the lowest
 // id). NaN entries never win. -------------------------------------------------------------
 
-__device__ __forceinline__ void better(float& bv, int& bi, float v, int i) {
-  if (v > bv || (v == bv && i < bi)) {
-    bv = v;
-    bi = i;
-  }
-}
 
 // Two passes: 64 slices of each row in parallel, then the 64 candidates of a row in one wave.
 // The comparison (larger value, or equal value and lower id) finds the lowest id of the
@@ -257,12 +253,12 @@ __global__ __launch_bounds__(256) void argmax_slices_kernel(const float* __restr
   const float* row = logits + (int64_t)r * vocab;
   float bv = -__builtin_inff();
   int bi = 0x7fffffff;
-  for (int i = lo + threadIdx.x; i < hi; i += blockDim.x) better(bv, bi, row[i], i);
+  for (int i = lo + threadIdx.x; i < hi; i += blockDim.x) greedy_better(bv, bi, row[i], i);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     float v = __shfl_xor(bv, o, 64);
     int i = __shfl_xor(bi, o, 64);
-    better(bv, bi, v, i);
+    greedy_better(bv, bi, v, i);
   }
   __shared__ float sv[4];
   __shared__ int si[4];
@@ -273,29 +269,40 @@ __global__ __launch_bounds__(256) void argmax_slices_kernel(const float* __restr
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    for (int k = 1; k < 4; ++k) better(bv, bi, sv[k], si[k]);
+    for (int k = 1; k < 4; ++k) greedy_better(bv, bi, sv[k], si[k]);
     pv[r * kArgmaxSlices + sl] = bv;
     pi[r * kArgmaxSlices + sl] = bi;
   }
 }
 
 __global__ __launch_bounds__(256) void argmax_final_kernel(const float* __restrict__ pv, const int32_t* __restrict__ pi,
-                                                           int n_rows, int32_t* __restrict__ next) {
+                                                           int n_rows, int nparts, int32_t* __restrict__ next) {
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= n_rows) return;
-  float bv = pv[r * kArgmaxSlices + lane];
-  int bi = pi[r * kArgmaxSlices + lane];
+  float bv = -__builtin_inff();
+  int bi = 0x7fffffff;
+  for (int j = lane; j < nparts; j += 64) greedy_better(bv, bi, pv[(int64_t)r * nparts + j], pi[(int64_t)r * nparts + j]);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     float v = __shfl_xor(bv, o, 64);
     int i = __shfl_xor(bi, o, 64);
-    better(bv, bi, v, i);
+    greedy_better(bv, bi, v, i);
   }
   if (lane == 0) next[r] = bi == 0x7fffffff ? 0 : bi;
 }
 
-size_t argmax_scratch_bytes(int max_rows) { return (size_t)max_rows * kArgmaxSlices * 8; }
+// (room for kArgmaxSlices candidates per row of a call, or kMaxArgmaxParts per decode row)
+size_t argmax_scratch_bytes(int max_rows, int max_seqs) {
+  return std::max((size_t)max_rows * kArgmaxSlices, (size_t)max_seqs * kMaxArgmaxParts) * 8;
+}
+
+hipError_t launch_argmax_final(const float* pv, const int32_t* pi, int n_rows, int nparts, int32_t* next,
+                               hipStream_t s) {
+  if (n_rows <= 0) return hipSuccess;
+  argmax_final_kernel<<<(n_rows + 3) / 4, 256, 0, s>>>(pv, pi, n_rows, nparts, next);
+  return hipGetLastError();
+}
 
 hipError_t launch_argmax(const float* logits, int n_rows, int vocab, int32_t* next, void* scratch, hipStream_t s) {
   if (n_rows <= 0) return hipSuccess;
@@ -304,8 +311,7 @@ hipError_t launch_argmax(const float* logits, int n_rows, int vocab, int32_t* ne
   argmax_slices_kernel<<<dim3(kArgmaxSlices, n_rows), 256, 0, s>>>(logits, vocab, pv, pi);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  argmax_final_kernel<<<(n_rows + 3) / 4, 256, 0, s>>>(pv, pi, n_rows, next);
-  return hipGetLastError();
+  return launch_argmax_final(pv, pi, n_rows, kArgmaxSlices, next, s);
 }
 
 // ---- debug dequantisation (same device arithmetic as the GEMM B-tile loader and the

@@ -116,6 +116,10 @@ struct GemmArgs {
   float eps;
   const float* gain_next;
   uint16_t* xg_out;
+  // Decode LM head only (optional): per (row, block) greedy candidates, the largest logit of
+  // the block's vocabulary share and its lowest id, at [row][block] (see lmhead_decode_parts)
+  float* am_v;
+  int32_t* am_i;
 };
 hipError_t launch_gemm(int wdtype, int epi, const GemmArgs& a, hipStream_t s);
 
@@ -137,10 +141,18 @@ hipError_t launch_gemm_decode(int wdtype, int epi, const GemmArgs& a, hipStream_
 // gain), a.lda) . E^T with each row scaled by 1 / rms(x) from a.ssq_in; bf16 / uint4 E, M <= 64.
 bool lmhead_decode_supported(int wdtype, int M, int K);
 hipError_t launch_lmhead_decode(int wdtype, const GemmArgs& a, hipStream_t s);
+// Blocks of the LM head launch for (M, N): the candidates per row it writes when a.am_v is set,
+// or 0 when it writes none for this M (then the logits go through launch_argmax).
+int lmhead_decode_parts(int M, int N);
+
+constexpr int kMaxArgmaxParts = 1024;  // greedy candidates per decode row from the LM head, at most
 
 // next[r] = argmax_v logits[r][v], ties to the lowest id; scratch holds argmax_scratch_bytes.
-size_t argmax_scratch_bytes(int max_rows);
+size_t argmax_scratch_bytes(int max_rows, int max_seqs);
 hipError_t launch_argmax(const float* logits, int n_rows, int vocab, int32_t* next, void* scratch, hipStream_t s);
+// next[r] from nparts candidates per row (values pv[r][j], ids pi[r][j]), same comparison.
+hipError_t launch_argmax_final(const float* pv, const int32_t* pi, int n_rows, int nparts, int32_t* next,
+                               hipStream_t s);
 
 // out[rows][cols] = widened / dequantised matrix (float32).
 hipError_t launch_dequant(int wdtype, const WMat& w, int rows, int cols, float* out, hipStream_t s);
