@@ -2,8 +2,10 @@
 // runner" 2.4). A is the bf16 activation; W is bf16, or uint4-g32 dequantised while the tile is
 // staged in LDS: w = (q - zp) * scale ("Byte-identical...", "The bar we set"), rounded to bf16.
 //
-// Tiling: a block of 8 waves computes a 256 x 256 tile of C (waves 4 x 2, 64 x 128 each) over
-// K in steps of 64, with the next step's operands loaded from memory into registers while the
+// Tiling: a block of 8 waves computes a 256 x 256 tile of C (waves 4 x 2, 64 x 128 each). bf16
+// weights: both operands go from memory straight into LDS (direct-to-LDS loads) in K steps of
+// 32 through a ring of four stages, three steps in flight, one barrier per step. uint4 weights:
+// K steps of 64, the next step's operands loaded into registers (and dequantised) while the
 // current step's LDS copy feeds the MFMAs (two LDS stages, one barrier per step). Every output
 // element is accumulated by v_mfma_f32_32x32x16_bf16 (the full-rate bf16 shape on this chip;
 // the 16x16x32 shape issues at half the rate) over K in ascending order into a single
@@ -30,10 +32,16 @@ namespace dec {
 namespace {
 
 constexpr int kBT = 256;            // block tile rows and columns
-constexpr int kBK = 64;             // K per step
+constexpr int kBK = 64;             // K per step (uint4 weights: register staging)
 constexpr int kLR = kBK + 8;        // LDS row stride in bf16 (padded: conflict-free fragment reads)
 constexpr int kStage = kBT * kLR;   // bf16 elements of one operand tile
 constexpr size_t kBigLds = (size_t)2 * 2 * kStage * 2;  // two stages of A and B, bytes
+// bf16 weights: direct-to-LDS staging, K steps of 32 in a ring of 4 stages (3 in flight);
+// a stage holds 256 rows of 32 bf16 (64 B) of A, then of B; row r keeps its 16-byte chunk c at
+// position c ^ ((r / 4) % 4), so the 16 rows of a fragment read fall on distinct banks
+constexpr int kDK = 32, kDStages = 4;
+constexpr int kDStage = 2 * kBT * kDK;                                   // bf16 elements per stage
+constexpr size_t kBigLdsDma = (size_t)kDStages * kDStage * 2;             // bytes
 
 // f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>), expanded at compile time so
 // that accumulator indices are constants (an unroll the optimizer may decline)
@@ -188,9 +196,79 @@ __global__ __launch_bounds__(512) void gemm_big(GemmArgs a, QkRopeArgs qk) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
+  auto mfma_step = [&](const bf16x8 (&af)[2], const bf16x8 (&bf)[4]) {
+#pragma unroll
+    for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < 4; ++bj)
+        acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[bi], bf[bj], acc[bi][bj], 0, 0, 0);
+  };
+  const int fr = lane & 31, fk = (lane >> 5) * 8;
+  if constexpr (WF == DEC_BF16) {
+    // Waves 0-3 stage the A rows, waves 4-7 the B rows, 64 rows per wave in four 1 KB
+    // direct-to-LDS loads per K step (16 rows of 64 B; lane l fills row l / 4, position l % 4,
+    // from the source chunk that position holds). The loads of three K steps are in flight.
+    const int nkd = K / kDK;
+    const int opb = wave >> 2, wq = wave & 3;
+    const int lc = (lane & 3) ^ ((lane >> 4) & 3);
+    const uint16_t* dsrc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wq * 64 + i * 16 + (lane >> 2);
+      if (opb == 0) {
+        dsrc[i] = (const uint16_t*)a.A + (int64_t)min(m0 + r, M - 1) * a.lda + lc * 8;
+      } else {
+        int rr;
+        const WMat m = b_src(r, rr);
+        dsrc[i] = (const uint16_t*)m.w + (int64_t)rr * K + lc * 8;
+      }
+    }
+    uint16_t* const dbase = lds + opb * kBT * kDK + wq * 64 * kDK;
+    auto dma = [&](int t) {
+      uint16_t* d = dbase + (t & (kDStages - 1)) * kDStage;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(dsrc[i] + t * kDK),
+                                         (void __attribute__((address_space(3)))*)(d + i * 16 * kDK), 16, 0, 0);
+    };
+    // fragment (row, k-step ks) of a staged operand: chunk 2 ks + lane / 32 of the row
+    const int fsw = (fr >> 2) & 3;
+    auto dfrag = [&](const uint16_t* S, int row, int ks) {
+      return __builtin_bit_cast(bf16x8, *(const u32x4*)(S + row * kDK + (((ks * 2 + (lane >> 5)) ^ fsw) * 8)));
+    };
+    dma(0);
+    if (nkd > 1) dma(1);
+    if (nkd > 2) dma(2);
+    for (int t = 0; t < nkd; ++t) {
+      // this wave's loads of step t have landed once at most those of the later issued steps
+      // are outstanding; the barrier then publishes step t and frees the stage of step t - 1
+      // (whose fragment reads completed before their MFMAs). A plain s_barrier: the
+      // workgroup fence of __syncthreads would also wait for the loads still in flight.
+      if (t + 2 < nkd)
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else if (t + 1 < nkd)
+        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (t + 3 < nkd) dma(t + 3);
+      const uint16_t* As = lds + (t & (kDStages - 1)) * kDStage;
+      const uint16_t* Bs = As + kBT * kDK;
+      bf16x8 af[2][2], bfr[2][4];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int bi = 0; bi < 2; ++bi) af[ks][bi] = dfrag(As, wm * 64 + bi * 32 + fr, ks);
+#pragma unroll
+        for (int bj = 0; bj < 4; ++bj) bfr[ks][bj] = dfrag(Bs, brow_of(bj) + fr, ks);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) mfma_step(af[ks], bfr[ks]);
+    }
+  } else {
   const int nk = K / kBK;
   constexpr int NKS = kBK / 16;  // MFMA k-steps per K step
-  const int fr = lane & 31, fk = (lane >> 5) * 8;
   // fragments of k-step ks of the LDS stage st
   auto read_frags = [&](int st, int ks, bf16x8 (&af)[2], bf16x8 (&bf)[4]) {
     const uint16_t* As = lds + (size_t)st * 2 * kStage;
@@ -201,13 +279,6 @@ __global__ __launch_bounds__(512) void gemm_big(GemmArgs a, QkRopeArgs qk) {
 #pragma unroll
     for (int bj = 0; bj < 4; ++bj)
       bf[bj] = __builtin_bit_cast(bf16x8, *(const u32x4*)(Bs + (brow_of(bj) + fr) * kLR + ks * 16 + fk));
-  };
-  auto mfma_step = [&](const bf16x8 (&af)[2], const bf16x8 (&bf)[4]) {
-#pragma unroll
-    for (int bi = 0; bi < 2; ++bi)
-#pragma unroll
-      for (int bj = 0; bj < 4; ++bj)
-        acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[bi], bf[bj], acc[bi][bj], 0, 0, 0);
   };
 
   // Pipeline: the fragments of the next k-step are read from LDS while the current k-step's
@@ -232,6 +303,7 @@ __global__ __launch_bounds__(512) void gemm_big(GemmArgs a, QkRopeArgs qk) {
     __syncthreads();
     if (more) read_frags(st ^ 1, 0, fa[NKS & 1], fb[NKS & 1]);
     mfma_step(fa[(NKS - 1) & 1], fb[(NKS - 1) & 1]);
+  }
   }
 
   // ---- epilogue: lane holds column fr of each 32 x 32 block, rows 8 g + 4 (lane / 32) + r
@@ -382,13 +454,13 @@ static hipError_t big_go(const GemmArgs& a, const QkRopeArgs& qk, hipStream_t s)
   static bool attr = false;  // raise the dynamic LDS limit once per instantiation
   if (!attr) {
     hipError_t e = hipFuncSetAttribute((const void*)gemm_big<WF, EPI, D, KV_F16>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kBigLds);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)(WF == DEC_BF16 ? kBigLdsDma : kBigLds));
     if (e != hipSuccess) return e;
     attr = true;
   }
   const int mt = (a.M + kBT - 1) / kBT;
   const int nt = EPI == EPI_SWIGLU ? (a.N + 127) / 128 : (a.N + kBT - 1) / kBT;
-  launch_kernel(gemm_big<WF, EPI, D, KV_F16>, dim3(mt * nt), dim3(512), (uint32_t)kBigLds, s, a, qk);
+  launch_kernel(gemm_big<WF, EPI, D, KV_F16>, dim3(mt * nt), dim3(512), (uint32_t)(WF == DEC_BF16 ? kBigLdsDma : kBigLds), s, a, qk);
   return hipGetLastError();
 }
 

@@ -123,7 +123,7 @@ struct GemmArgs {
 };
 hipError_t launch_gemm(int wdtype, int epi, const GemmArgs& a, hipStream_t s);
 
-// Prefill GEMM for bf16 / uint4 weights: 256 x 256 block tiles, double-buffered LDS, the same
+// Prefill GEMM for bf16 / uint4 weights: 256 x 256 block tiles staged through LDS, the same
 // per-element MFMA sequence as launch_gemm (identical results). Epilogues EPI_STORE,
 // EPI_RESID, EPI_SWIGLU, and EPI_QKV: the Q|K|V product goes through the per-head q/k
 // RMSNorm and RoPE in registers and is stored as q (qk->q_out) and paged K/V (qk->pool), as
