@@ -32,7 +32,7 @@ DEC_E_POSITION = -5
 DEC_E_TOKEN = -6
 DEC_E_HIP = -7
 
-DEC_F32, DEC_BF16, DEC_F16, DEC_UINT4_G32 = 0, 1, 2, 3
+DEC_F32, DEC_BF16, DEC_F16, DEC_UINT4_G32, DEC_INT4_SYM_G32 = 0, 1, 2, 3, 4
 DEC_LOGITS_ALL, DEC_LOGITS_LAST, DEC_LOGITS_NONE = 0, 1, 2
 
 ERROR_NAMES = {DEC_E_ARG: "DEC_E_ARG", DEC_E_UNSUPPORTED: "DEC_E_UNSUPPORTED", DEC_E_CAPACITY: "DEC_E_CAPACITY",

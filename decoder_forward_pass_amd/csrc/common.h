@@ -47,6 +47,33 @@ __device__ __forceinline__ float dequant_u4(uint32_t q, float zp, float scale) {
   return t * scale;
 }
 
+// The 4-bit weight formats, groups of 32 input columns. DEC_UINT4_G32: codes u in [0, 15],
+// bf16 scale and zero point, w = (u - zp) * scale. DEC_INT4_SYM_G32: two's complement nibbles
+// q in [-8, 7] with an f16 scale, w = q * scale ("Candle model runner" 2.5). Flipping a nibble's
+// top bit gives u = q + 8, so the signed format is the unsigned one with zp = 8: u - 8 = q is
+// exact, and q * scale (at most 15 significant bits) is exact in float32.
+constexpr bool is_q4(int wf) { return wf == DEC_UINT4_G32 || wf == DEC_INT4_SYM_G32; }
+// packed nibbles (any number per word) as unsigned codes
+template <int WF>
+__device__ __forceinline__ uint32_t q4_codes(uint32_t packed) {
+  return WF == DEC_INT4_SYM_G32 ? packed ^ 0x88888888u : packed;
+}
+template <int WF>
+__device__ __forceinline__ float q4_scale(uint16_t bits) {
+  if constexpr (WF == DEC_INT4_SYM_G32)
+    return f16_bits_to_f32(bits);
+  else
+    return bf16_bits_to_f32(bits);
+}
+// zero point of group gi (the signed format reads none)
+template <int WF>
+__device__ __forceinline__ float q4_zp(const uint16_t* zp, int64_t gi) {
+  if constexpr (WF == DEC_INT4_SYM_G32)
+    return 8.0f;
+  else
+    return bf16_bits_to_f32(zp[gi]);
+}
+
 // ---- cross-lane data movement -------------------------------------------------------------
 // DPP row operations move data between lanes of a 16-lane row inside a VALU instruction
 // (no LDS traffic): quad_perm [1,0,3,2] pairs lanes i ^ 1, quad_perm [2,3,0,1] pairs i ^ 2,
@@ -158,8 +185,8 @@ struct PoolDev {
 
 // One weight matrix as a GEMM B operand (rows are output features, [out][in]).
 struct WMat {
-  const void* w;         // f32 / bf16 values, or uint4 codes [out][in/2]
-  const uint16_t* scale; // uint4 only: bf16 [out][in/32]
+  const void* w;         // f32 / bf16 values, or 4-bit codes [out][in/2]
+  const uint16_t* scale; // 4-bit formats: bf16 (uint4) or f16 (int4 sym) [out][in/32]
   const uint16_t* zp;    // uint4 only
   int32_t rows;
 };

@@ -54,8 +54,9 @@ int check_config(const dec_config* c, std::string* err) {
   if (c->max_context < 1) return fail(err, DEC_E_UNSUPPORTED, "max_context must be >= 1");
   if (!(c->rms_eps > 0.f) || !std::isfinite(c->rms_eps)) return fail(err, DEC_E_UNSUPPORTED, "rms_eps must be positive");
   if (!(c->rope_base > 1.0) || !std::isfinite(c->rope_base)) return fail(err, DEC_E_UNSUPPORTED, "rope_base must be > 1");
-  if (c->weight_dtype != DEC_F32 && c->weight_dtype != DEC_BF16 && c->weight_dtype != DEC_UINT4_G32)
-    return fail(err, DEC_E_UNSUPPORTED, "weight_dtype must be DEC_F32, DEC_BF16 or DEC_UINT4_G32");
+  if (c->weight_dtype != DEC_F32 && c->weight_dtype != DEC_BF16 && c->weight_dtype != DEC_UINT4_G32 &&
+      c->weight_dtype != DEC_INT4_SYM_G32)
+    return fail(err, DEC_E_UNSUPPORTED, "weight_dtype must be DEC_F32, DEC_BF16, DEC_UINT4_G32 or DEC_INT4_SYM_G32");
   if (c->kv_dtype != DEC_F32 && c->kv_dtype != DEC_F16) return fail(err, DEC_E_UNSUPPORTED, "kv_dtype must be DEC_F32 or DEC_F16");
   if (c->block_tokens != 16 && c->block_tokens != 32 && c->block_tokens != 64)
     return fail(err, DEC_E_UNSUPPORTED, "block_tokens must be 16, 32 or 64");
@@ -101,6 +102,11 @@ Blob blob_layout(const dec_config& c) {
       w.scale_offset = align_up(off + w.bytes);
       w.zp_offset = align_up(w.scale_offset + w.group_bytes);
       off = align_up(w.zp_offset + w.group_bytes);
+    } else if (c.weight_dtype == DEC_INT4_SYM_G32) {
+      w.bytes = (size_t)(rows * cols / 2);
+      w.group_bytes = (size_t)(rows * (cols / 32) * 2);
+      w.scale_offset = align_up(off + w.bytes);
+      off = align_up(w.scale_offset + w.group_bytes);
     } else {
       w.bytes = (size_t)(rows * cols * (c.weight_dtype == DEC_F32 ? 4 : 2));
       off = align_up(off + w.bytes);
@@ -266,7 +272,7 @@ WMat wmat(const dec_ctx* c, int idx) {
   const dec_weight_info& e = c->blob.e[idx];
   WMat m;
   m.w = c->w + e.offset;
-  m.scale = e.dtype == DEC_UINT4_G32 ? (const uint16_t*)(c->w + e.scale_offset) : nullptr;
+  m.scale = e.dtype == DEC_UINT4_G32 || e.dtype == DEC_INT4_SYM_G32 ? (const uint16_t*)(c->w + e.scale_offset) : nullptr;
   m.zp = e.dtype == DEC_UINT4_G32 ? (const uint16_t*)(c->w + e.zp_offset) : nullptr;
   m.rows = (int32_t)e.rows;
   return m;

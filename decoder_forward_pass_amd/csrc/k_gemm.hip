@@ -1,8 +1,9 @@
 // Projections as MFMA GEMMs: C = A . W^T with W stored [out][in] ("Candle model runner"
 // 2.4: W stored [out, in], y = x W^T). A is the activation (float32 for float32 weights,
-// bf16 otherwise); W is float32, bf16, or uint4-g32 dequantised in registers while the tile
-// is staged in LDS: w = (q - zp) * scale ("Byte-identical...", "The bar we set"), rounded to
-// bf16 as the MFMA operand.
+// bf16 otherwise); W is float32, bf16, or 4-bit dequantised in registers while the tile is
+// staged in LDS: uint4-g32 w = (q - zp) * scale ("Byte-identical...", "The bar we set") or
+// symmetric int4-g32 w = q * scale ("Candle model runner" 2.5), rounded to bf16 as the MFMA
+// operand.
 //
 // Batch invariance: every output element is accumulated by one MFMA instruction type per
 // weight format (v_mfma_f32_16x16x4_f32 or v_mfma_f32_32x32x16_bf16), over K in ascending
@@ -112,12 +113,12 @@ __global__ __launch_bounds__(256) void gemm_tile64(GemmArgs a) {
         const u32x2 codes =
             *(const u32x2*)((const uint8_t*)bm[nb].w + (int64_t)gr * (K / 2) + (k0 + kq) / 2);
         const int64_t gi = (int64_t)gr * (K / 32) + (k0 + kq) / 32;
-        const float zp = bf16_bits_to_f32(bm[nb].zp[gi]);
-        const float sc = bf16_bits_to_f32(bm[nb].scale[gi]);
+        const float zp = q4_zp<WF>(bm[nb].zp, gi);
+        const float sc = q4_scale<WF>(bm[nb].scale[gi]);
         uint32_t* d = Bs[nb] + row * RW + kq / 2;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const uint32_t byte = (codes[j >> 2] >> ((j & 3) * 8)) & 0xffu;
+          const uint32_t byte = (q4_codes<WF>(codes[j >> 2]) >> ((j & 3) * 8)) & 0xffu;
           const float lo = dequant_u4(byte & 15u, zp, sc);
           const float hi = dequant_u4(byte >> 4, zp, sc);
           d[j] = pack_bf16x2(lo, hi);
@@ -230,6 +231,7 @@ hipError_t launch_gemm(int wdtype, int epi, const GemmArgs& a, hipStream_t s) {
   if (wdtype == DEC_F32) return gemm_epi<DEC_F32>(epi, a, s);
   if (wdtype == DEC_BF16) return gemm_epi<DEC_BF16>(epi, a, s);
   if (wdtype == DEC_UINT4_G32) return gemm_epi<DEC_UINT4_G32>(epi, a, s);
+  if (wdtype == DEC_INT4_SYM_G32) return gemm_epi<DEC_INT4_SYM_G32>(epi, a, s);
   return hipErrorInvalidValue;
 }
 
@@ -261,6 +263,11 @@ struct BRaw<DEC_UINT4_G32> {
   uint32_t codes;
   uint16_t scale, zp;
 };
+template <>
+struct BRaw<DEC_INT4_SYM_G32> {
+  uint32_t codes;
+  uint16_t scale;
+};
 
 template <int WF>
 __device__ __forceinline__ BRaw<WF> load_b_raw(const WMat& m, int row, int K, int k) {
@@ -271,7 +278,7 @@ __device__ __forceinline__ BRaw<WF> load_b_raw(const WMat& m, int row, int K, in
     r.codes = *(const uint32_t*)((const uint8_t*)m.w + (int64_t)row * (K / 2) + k / 2);
     const int64_t gi = (int64_t)row * (K / 32) + k / 32;
     r.scale = m.scale[gi];
-    r.zp = m.zp[gi];
+    if constexpr (WF == DEC_UINT4_G32) r.zp = m.zp[gi];
   }
   return r;
 }
@@ -281,11 +288,17 @@ __device__ __forceinline__ bf16x8 b_frag(const BRaw<WF>& r) {
   if constexpr (WF == DEC_BF16) {
     return __builtin_bit_cast(bf16x8, r.w);
   } else {
-    const float zp = bf16_bits_to_f32(r.zp), sc = bf16_bits_to_f32(r.scale);
+    float zp;
+    if constexpr (WF == DEC_UINT4_G32)
+      zp = bf16_bits_to_f32(r.zp);
+    else
+      zp = 8.0f;  // signed nibbles read with their top bit flipped
+    const float sc = q4_scale<WF>(r.scale);
+    const uint32_t codes = q4_codes<WF>(r.codes);
     u32x4 w;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t byte = (r.codes >> (8 * j)) & 0xffu;
+      const uint32_t byte = (codes >> (8 * j)) & 0xffu;
       w[j] = pack_bf16x2(dequant_u4(byte & 15u, zp, sc), dequant_u4(byte >> 4, zp, sc));
     }
     return __builtin_bit_cast(bf16x8, w);
@@ -700,7 +713,7 @@ static hipError_t lmhead_go(const GemmArgs& a, hipStream_t s) {
 
 bool lmhead_decode_supported(int wdtype, int M, int K) {
   // each of 32 threads per row stages K/32 columns in 16-byte steps
-  return (wdtype == DEC_BF16 || wdtype == DEC_UINT4_G32) && M <= 64 && K % 256 == 0 && (size_t)64 * (K + 8) * 2 <= 160 * 1024;
+  return (wdtype == DEC_BF16 || is_q4(wdtype)) && M <= 64 && K % 256 == 0 && (size_t)64 * (K + 8) * 2 <= 160 * 1024;
 }
 
 hipError_t launch_lmhead_decode(int wdtype, const GemmArgs& a, hipStream_t s) {
@@ -711,9 +724,17 @@ hipError_t launch_lmhead_decode(int wdtype, const GemmArgs& a, hipStream_t s) {
     if (mt == 2) return lmhead_go<DEC_BF16, 2>(a, s);
     return lmhead_go<DEC_BF16, 4>(a, s);
   }
-  if (mt == 1) return lmhead_go<DEC_UINT4_G32, 1>(a, s);
-  if (mt == 2) return lmhead_go<DEC_UINT4_G32, 2>(a, s);
-  return lmhead_go<DEC_UINT4_G32, 4>(a, s);
+  if (wdtype == DEC_UINT4_G32) {
+    if (mt == 1) return lmhead_go<DEC_UINT4_G32, 1>(a, s);
+    if (mt == 2) return lmhead_go<DEC_UINT4_G32, 2>(a, s);
+    return lmhead_go<DEC_UINT4_G32, 4>(a, s);
+  }
+  if (wdtype == DEC_INT4_SYM_G32) {
+    if (mt == 1) return lmhead_go<DEC_INT4_SYM_G32, 1>(a, s);
+    if (mt == 2) return lmhead_go<DEC_INT4_SYM_G32, 2>(a, s);
+    return lmhead_go<DEC_INT4_SYM_G32, 4>(a, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 // LDS bytes of the staged path: the activation rows (rpb) and, for bf16 weights, the weight
@@ -791,7 +812,7 @@ static hipError_t gemm_decode_nks(int epi, const GemmArgs& a, bool rows8, hipStr
 }
 
 bool gemm_decode_supported(int wdtype, int K) {
-  if (wdtype != DEC_BF16 && wdtype != DEC_UINT4_G32) return false;
+  if (wdtype != DEC_BF16 && !is_q4(wdtype)) return false;
   const int ksteps = K / 32;
   int nw = kDecWaves;
   while (ksteps % nw) nw >>= 1;
@@ -812,6 +833,9 @@ hipError_t launch_gemm_decode(int wdtype, int epi, const GemmArgs& a, hipStream_
   if (wdtype == DEC_UINT4_G32)
     return rows16 ? gemm_decode_nks<DEC_UINT4_G32, 1>(epi, a, rows8, s)
                   : gemm_decode_nks<DEC_UINT4_G32, 2>(epi, a, rows8, s);
+  if (wdtype == DEC_INT4_SYM_G32)
+    return rows16 ? gemm_decode_nks<DEC_INT4_SYM_G32, 1>(epi, a, rows8, s)
+                  : gemm_decode_nks<DEC_INT4_SYM_G32, 2>(epi, a, rows8, s);
   return hipErrorInvalidValue;
 }
 

@@ -1,10 +1,11 @@
 // Prefill projections as large MFMA tiles: C = A . W^T with W stored [out][in] ("Candle model
-// runner" 2.4). A is the bf16 activation; W is bf16, or uint4-g32 dequantised while the tile is
-// staged in LDS: w = (q - zp) * scale ("Byte-identical...", "The bar we set"), rounded to bf16.
+// runner" 2.4). A is the bf16 activation; W is bf16, or 4-bit dequantised while the tile is
+// staged in LDS: uint4-g32 w = (q - zp) * scale ("Byte-identical...", "The bar we set") or
+// symmetric int4-g32 w = q * scale ("Candle model runner" 2.5), rounded to bf16.
 //
 // Tiling: a block of 8 waves computes a 256 x 256 tile of C (waves 4 x 2, 64 x 128 each). bf16
 // weights: both operands go from memory straight into LDS (direct-to-LDS loads) in K steps of
-// 32 through a ring of four stages, three steps in flight, one barrier per step. uint4 weights:
+// 32 through a ring of four stages, three steps in flight, one barrier per step. 4-bit weights:
 // K steps of 64, the next step's operands loaded into registers (and dequantised) while the
 // current step's LDS copy feeds the MFMAs (two LDS stages, one barrier per step). Every output
 // element is accumulated by v_mfma_f32_32x32x16_bf16 (the full-rate bf16 shape on this chip;
@@ -32,7 +33,7 @@ namespace dec {
 namespace {
 
 constexpr int kBT = 256;            // block tile rows and columns
-constexpr int kBK = 64;             // K per step (uint4 weights: register staging)
+constexpr int kBK = 64;             // K per step (4-bit weights: register staging)
 constexpr int kLR = kBK + 8;        // LDS row stride in bf16 (padded: conflict-free fragment reads)
 constexpr int kStage = kBT * kLR;   // bf16 elements of one operand tile
 constexpr size_t kBigLds = (size_t)2 * 2 * kStage * 2;  // two stages of A and B, bytes
@@ -124,8 +125,8 @@ __global__ __launch_bounds__(512) void gemm_big(GemmArgs a, QkRopeArgs qk) {
   };
   BigRowsB bp;
   const uint8_t* qcodes = nullptr;
-  const uint16_t *qscale = nullptr, *qzp = nullptr;
-  const int urow = tid >> 1, uhalf = tid & 1;  // uint4: a thread dequantises 32 k of one row
+  const uint16_t *qscale = nullptr, *qzp = nullptr;  // (the signed format has no zero point)
+  const int urow = tid >> 1, uhalf = tid & 1;  // 4-bit: a thread dequantises 32 k of one row
   if constexpr (WF == DEC_BF16) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -138,11 +139,11 @@ __global__ __launch_bounds__(512) void gemm_big(GemmArgs a, QkRopeArgs qk) {
     const WMat m = b_src(urow, rr);
     qcodes = (const uint8_t*)m.w + (int64_t)rr * (K / 2) + uhalf * 16;
     qscale = m.scale + (int64_t)rr * (K / 32) + uhalf;
-    qzp = m.zp + (int64_t)rr * (K / 32) + uhalf;
+    if constexpr (WF == DEC_UINT4_G32) qzp = m.zp + (int64_t)rr * (K / 32) + uhalf;
   }
 
   u32x4 ra[4], rb[4];
-  uint32_t rsz = 0;  // uint4: scale | zp << 16
+  uint32_t rsz = 0;  // 4-bit: scale | zp << 16 (uint4)
   auto load_step = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) ra[i] = *(const u32x4*)(ap[i] + k0);
@@ -151,7 +152,8 @@ __global__ __launch_bounds__(512) void gemm_big(GemmArgs a, QkRopeArgs qk) {
       for (int i = 0; i < 4; ++i) rb[i] = *(const u32x4*)(bp.p[i] + k0);
     } else {
       rb[0] = *(const u32x4*)(qcodes + k0 / 2);
-      rsz = (uint32_t)qscale[k0 / 32] | ((uint32_t)qzp[k0 / 32] << 16);
+      rsz = (uint32_t)qscale[k0 / 32];
+      if constexpr (WF == DEC_UINT4_G32) rsz |= (uint32_t)qzp[k0 / 32] << 16;
     }
   };
   auto store_step = [&](int st) {
@@ -163,14 +165,19 @@ __global__ __launch_bounds__(512) void gemm_big(GemmArgs a, QkRopeArgs qk) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) *(u32x4*)(Bs + (srow + 64 * i) * kLR + sc8 * 8) = rb[i];
     } else {
-      const float sc = bf16_bits_to_f32(rsz & 0xffffu), zp = bf16_bits_to_f32(rsz >> 16);
+      const float sc = q4_scale<WF>(rsz & 0xffffu);
+      float zp;
+      if constexpr (WF == DEC_UINT4_G32)
+        zp = bf16_bits_to_f32(rsz >> 16);
+      else
+        zp = 8.0f;  // signed nibbles read with their top bit flipped
       uint16_t* d = Bs + urow * kLR + uhalf * 32;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         u32x4 w;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const uint32_t byte = (rb[0][q] >> (8 * j)) & 0xffu;
+          const uint32_t byte = (q4_codes<WF>(rb[0][q]) >> (8 * j)) & 0xffu;
           w[j] = pack_bf16x2(dequant_u4(byte & 15u, zp, sc), dequant_u4(byte >> 4, zp, sc));
         }
         *(u32x4*)(d + q * 8) = w;
@@ -485,7 +492,7 @@ static hipError_t big_epi(int epi, const GemmArgs& a, const QkRopeArgs* qk, hipS
 }
 
 bool gemm_big_supported(int wdtype, int epi, int head_dim) {
-  if (wdtype != DEC_BF16 && wdtype != DEC_UINT4_G32) return false;
+  if (wdtype != DEC_BF16 && !is_q4(wdtype)) return false;
   if (epi == EPI_QKV) return head_dim == 32 || head_dim == 64 || head_dim == 128;
   return epi == EPI_STORE || epi == EPI_RESID || epi == EPI_SWIGLU;
 }
@@ -495,6 +502,7 @@ hipError_t launch_gemm_big(int wdtype, int epi, const GemmArgs& a, const QkRopeA
   if (a.K % kBK) return hipErrorInvalidValue;
   if (wdtype == DEC_BF16) return big_epi<DEC_BF16>(epi, a, qk, s);
   if (wdtype == DEC_UINT4_G32) return big_epi<DEC_UINT4_G32>(epi, a, qk, s);
+  if (wdtype == DEC_INT4_SYM_G32) return big_epi<DEC_INT4_SYM_G32>(epi, a, qk, s);
   return hipErrorInvalidValue;
 }
 

@@ -53,11 +53,11 @@ __device__ __forceinline__ void embed_row(const WMat& E, int t, int d, float* __
   } else {
     const uint8_t* er = (const uint8_t*)E.w + (int64_t)t * (d / 2);
     const uint16_t* sr = E.scale + (int64_t)t * (d / 32);
-    const uint16_t* zr = E.zp + (int64_t)t * (d / 32);
+    const int64_t g0 = (int64_t)t * (d / 32);
     for (int i = threadIdx.x; i < d; i += blockDim.x) {
-      uint32_t byte = er[i >> 1];
-      uint32_t q = (i & 1) ? (byte >> 4) : (byte & 15u);
-      xr[i] = dequant_u4(q, bf16_bits_to_f32(zr[i >> 5]), bf16_bits_to_f32(sr[i >> 5]));
+      uint32_t byte = q4_codes<WF>(er[i >> 1]);
+      uint32_t q = (i & 1) ? ((byte >> 4) & 15u) : (byte & 15u);
+      xr[i] = dequant_u4(q, q4_zp<WF>(E.zp, g0 + (i >> 5)), q4_scale<WF>(sr[i >> 5]));
     }
   }
 }
@@ -71,8 +71,12 @@ hipError_t launch_embed(const int32_t* tok, int n_rows, int vocab, int d, int wd
     embed_kernel<DEC_F32><<<g, b, 0, s>>>(tok, vocab, d, E, x, ssq, xg, gain);
   else if (wdtype == DEC_BF16)
     embed_kernel<DEC_BF16><<<g, b, 0, s>>>(tok, vocab, d, E, x, ssq, xg, gain);
-  else
+  else if (wdtype == DEC_UINT4_G32)
     embed_kernel<DEC_UINT4_G32><<<g, b, 0, s>>>(tok, vocab, d, E, x, ssq, xg, gain);
+  else if (wdtype == DEC_INT4_SYM_G32)
+    embed_kernel<DEC_INT4_SYM_G32><<<g, b, 0, s>>>(tok, vocab, d, E, x, ssq, xg, gain);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
@@ -330,10 +334,10 @@ __global__ __launch_bounds__(256) void dequant_kernel(WMat w, int rows, int cols
     } else if constexpr (WF == DEC_BF16) {
       v = bf16_bits_to_f32(((const uint16_t*)w.w)[i]);
     } else {
-      uint32_t byte = ((const uint8_t*)w.w)[r * (cols / 2) + (c >> 1)];
-      uint32_t q = (c & 1) ? (byte >> 4) : (byte & 15u);
+      uint32_t byte = q4_codes<WF>(((const uint8_t*)w.w)[r * (cols / 2) + (c >> 1)]);
+      uint32_t q = (c & 1) ? ((byte >> 4) & 15u) : (byte & 15u);
       const int64_t gi = r * (cols / 32) + (c >> 5);
-      v = dequant_u4(q, bf16_bits_to_f32(w.zp[gi]), bf16_bits_to_f32(w.scale[gi]));
+      v = dequant_u4(q, q4_zp<WF>(w.zp, gi), q4_scale<WF>(w.scale[gi]));
     }
     out[i] = v;
   }
@@ -348,8 +352,12 @@ hipError_t launch_dequant(int wdtype, const WMat& w, int rows, int cols, float* 
     dequant_kernel<DEC_F32><<<blocks, 256, 0, s>>>(w, rows, cols, out);
   else if (wdtype == DEC_BF16)
     dequant_kernel<DEC_BF16><<<blocks, 256, 0, s>>>(w, rows, cols, out);
-  else
+  else if (wdtype == DEC_UINT4_G32)
     dequant_kernel<DEC_UINT4_G32><<<blocks, 256, 0, s>>>(w, rows, cols, out);
+  else if (wdtype == DEC_INT4_SYM_G32)
+    dequant_kernel<DEC_INT4_SYM_G32><<<blocks, 256, 0, s>>>(w, rows, cols, out);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

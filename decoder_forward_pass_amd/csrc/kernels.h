@@ -123,7 +123,7 @@ struct GemmArgs {
 };
 hipError_t launch_gemm(int wdtype, int epi, const GemmArgs& a, hipStream_t s);
 
-// Prefill GEMM for bf16 / uint4 weights: 256 x 256 block tiles staged through LDS, the same
+// Prefill GEMM for bf16 / 4-bit weights: 256 x 256 block tiles staged through LDS, the same
 // per-element MFMA sequence as launch_gemm (identical results). Epilogues EPI_STORE,
 // EPI_RESID, EPI_SWIGLU, and EPI_QKV: the Q|K|V product goes through the per-head q/k
 // RMSNorm and RoPE in registers and is stored as q (qk->q_out) and paged K/V (qk->pool), as
@@ -133,12 +133,12 @@ bool gemm_big_supported(int wdtype, int epi, int head_dim);
 hipError_t launch_gemm_big(int wdtype, int epi, const GemmArgs& a, const QkRopeArgs* qk, hipStream_t s);
 
 // The same product for decode steps: K split over up to 8 waves of a block (fixed by K),
-// summed in wave order; bf16 and uint4 weights, K/32 with a supported per-wave step count.
+// summed in wave order; bf16 and 4-bit weights, K/32 with a supported per-wave step count.
 bool gemm_decode_supported(int wdtype, int K);
 hipError_t launch_gemm_decode(int wdtype, int epi, const GemmArgs& a, hipStream_t s);
 
 // Decode LM head: logits[M][N] = RMSNorm(x)[M][K] . E^T, taken as xg (a.A = bf16(x * final
-// gain), a.lda) . E^T with each row scaled by 1 / rms(x) from a.ssq_in; bf16 / uint4 E, M <= 64.
+// gain), a.lda) . E^T with each row scaled by 1 / rms(x) from a.ssq_in; bf16 / 4-bit E, M <= 64.
 bool lmhead_decode_supported(int wdtype, int M, int K);
 hipError_t launch_lmhead_decode(int wdtype, const GemmArgs& a, hipStream_t s);
 // Blocks of the LM head launch for (M, N): the candidates per row it writes when a.am_v is set,

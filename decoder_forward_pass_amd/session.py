@@ -17,7 +17,7 @@ import torch
 from . import binding as B
 from .blob import pack_blob
 
-_WDT = {"f32": B.DEC_F32, "bf16": B.DEC_BF16, "uint4": B.DEC_UINT4_G32}
+_WDT = {"f32": B.DEC_F32, "bf16": B.DEC_BF16, "uint4": B.DEC_UINT4_G32, "int4sym": B.DEC_INT4_SYM_G32}
 _KVT = {"f32": B.DEC_F32, "f16": B.DEC_F16}
 
 

@@ -73,6 +73,7 @@ extern "C" {
 #define DEC_BF16 1
 #define DEC_F16 2
 #define DEC_UINT4_G32 3 /* 4-bit codes, bf16 scale and bf16 zero point per 32 input columns */
+#define DEC_INT4_SYM_G32 4 /* signed 4-bit values, f16 scale per 32 input columns, no zero point */
 
 /* which rows get logits */
 #define DEC_LOGITS_ALL 0  /* every new row, in batch order: [sum n_new][vocab] */
@@ -104,7 +105,7 @@ typedef struct dec_config {
   int32_t rope_split;     /* must be 1 */
   int32_t qk_norm;        /* must be 1 */
   int32_t tie_embeddings; /* must be 1 */
-  int32_t weight_dtype;   /* DEC_F32 | DEC_BF16 | DEC_UINT4_G32 */
+  int32_t weight_dtype;   /* DEC_F32 | DEC_BF16 | DEC_UINT4_G32 | DEC_INT4_SYM_G32 */
   int32_t kv_dtype;       /* DEC_F32 | DEC_F16 */
   int32_t block_tokens;   /* B: positions per KV block */
   int32_t n_blocks;       /* blocks in the KV pool */
@@ -129,6 +130,11 @@ int dec_check_config(const dec_config* cfg);
  * nibble, the order of "Candle model runner" 2.5), then scale bf16
  * [out][in/32], then zero point bf16 [out][in/32]; element (o, i) is
  * (code - zp[o][i/32]) * scale[o][i/32].
+ * A DEC_INT4_SYM_G32 matrix is two arrays ("Candle model runner" 2.5, the
+ * symmetric int4-g format): values uint8 [out][in/2], each nibble a 4-bit
+ * two's complement integer q in [-8, 7] in the same column order, then scale
+ * f16 [out][in/32]; element (o, i) is q * scale[o][i/32], exact in float32.
+ * Its entries report zp_offset = 0.
  * The library only reads the blob.
  */
 size_t dec_weight_bytes(const dec_config* cfg);
@@ -139,10 +145,10 @@ typedef struct dec_weight_info {
   int32_t layer;      /* -1 for embed / final_norm */
   int32_t dtype;      /* DEC_F32 (gains) or the config's weight_dtype (matrices) */
   int64_t rows, cols; /* logical shape; gains are [1][n] */
-  size_t offset;      /* byte offset of the data (codes, for uint4) */
-  size_t bytes;       /* bytes of the data (codes, for uint4) */
-  size_t scale_offset, zp_offset; /* uint4 only: byte offsets of scale and zero point */
-  size_t group_bytes;             /* uint4 only: bytes of each of scale and zp */
+  size_t offset;      /* byte offset of the data (codes, for 4-bit formats) */
+  size_t bytes;       /* bytes of the data (codes, for 4-bit formats) */
+  size_t scale_offset, zp_offset; /* 4-bit formats: byte offsets of scale and zero point (0: none) */
+  size_t group_bytes;             /* 4-bit formats: bytes of the scales (and of the zero points) */
 } dec_weight_info;
 int dec_weight_count(const dec_config* cfg);
 int dec_weight_entry(const dec_config* cfg, int index, dec_weight_info* out);

@@ -9,7 +9,8 @@ imports nothing from the library. The two share only the seeded inputs of
 ``synthetic``.
 
 Modules:
-  numerics  -- f16 rounding and widening, bf16 widening, uint4 dequantisation
+  numerics  -- f16 rounding and widening, bf16 widening, uint4 and symmetric int4
+               dequantisation
   paged     -- where a key or value of a position lands in the paged KV pool
   model     -- the numpy float64 decoder: full, cached, chunked, batched, greedy
   loops     -- a second, loop-only decoder for tiny shapes

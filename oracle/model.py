@@ -44,7 +44,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .numerics import bf16_to_f32, dequant_uint4_g32, f16_to_f32, f32_to_f16
+from .numerics import bf16_to_f32, dequant_int4_sym_g32, dequant_uint4_g32, f16_to_f32, f32_to_f16
 
 
 def widen_matrix(m, weight_dtype: str) -> np.ndarray:
@@ -55,6 +55,8 @@ def widen_matrix(m, weight_dtype: str) -> np.ndarray:
         return bf16_to_f32(m).astype(np.float64)
     if weight_dtype == "uint4":
         return dequant_uint4_g32(m.q, m.scale, m.zp).astype(np.float64)
+    if weight_dtype == "int4sym":
+        return dequant_int4_sym_g32(m.q, m.scale).astype(np.float64)
     raise ValueError(weight_dtype)
 
 

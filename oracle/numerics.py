@@ -16,6 +16,10 @@
   nearest even and no fused multiply-add. (With 4-bit q and bf16 zp and scale
   both steps are exact in float32; the tests check that against rational
   arithmetic.)
+* symmetric int4-g32 dequantisation W = q * s ("Candle model runner", section
+  2.5 "Int4 weights"), q a signed 4-bit value in [-8, 7] and s the f16 scale
+  of the element's group of 32 input columns. The product has at most 15
+  significant bits, so it is exact in float32 (and in float64).
 """
 
 from __future__ import annotations
@@ -99,4 +103,18 @@ def dequant_uint4_g32(q, scale_bits, zp_bits) -> np.ndarray:
     sc = bf16_to_f32(scale_bits).reshape(out, g, 1)
     t = (qf - zp).astype(np.float32)
     w = (t * sc).astype(np.float32)
+    return w.reshape(out, inp)
+
+
+def dequant_int4_sym_g32(q, scale_bits) -> np.ndarray:
+    """W = q * s per element, in float32.
+
+    q: int8 [out, in] values -8..7 (unpacked); scale_bits: uint16 [out, in/32] f16 patterns
+    of each group of 32 input columns.
+    """
+    q = np.asarray(q)
+    out, inp = q.shape
+    g = inp // 32
+    sc = f16_to_f32(scale_bits).reshape(out, g, 1)
+    w = (q.reshape(out, g, 32).astype(np.float32) * sc).astype(np.float32)
     return w.reshape(out, inp)

@@ -18,6 +18,7 @@ from .generate import (
     make_context_lengths,
     fp32_to_bf16_bits,
     quantize_uint4_g32,
+    quantize_int4_sym_g32,
 )
 
 __all__ = [
@@ -31,4 +32,5 @@ __all__ = [
     "make_context_lengths",
     "fp32_to_bf16_bits",
     "quantize_uint4_g32",
+    "quantize_int4_sym_g32",
 ]

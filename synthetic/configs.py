@@ -36,7 +36,7 @@ class ModelShape:
     vocab: int
     rms_eps: float = 1e-6
     rope_base: float = 1e6
-    weight_dtype: str = "f32"  # "f32" | "bf16" | "uint4"
+    weight_dtype: str = "f32"  # "f32" | "bf16" | "uint4" | "int4sym"
     kv_dtype: str = "f32"  # "f32" | "f16"
     block_tokens: int = 16
     init_std: float = 0.02
@@ -68,6 +68,8 @@ MODELS = {
                             final_gain=_logit_gain(1024), seed=303),
     "q06b_uint4": ModelShape(name="q06b_uint4", **_Q06B, weight_dtype="uint4", kv_dtype="f16",
                              final_gain=_logit_gain(1024), seed=505),
+    "q06b_int4sym": ModelShape(name="q06b_int4sym", **_Q06B, weight_dtype="int4sym", kv_dtype="f16",
+                               final_gain=_logit_gain(1024), seed=606),
 }
 
 
@@ -100,6 +102,18 @@ WORKLOADS = {
     "q06b_uint4_b64_ragged_d128": Workload("q06b_uint4_b64_ragged_d128", "q06b_uint4", n_seqs=64,
                                            prompt_len=None, decode_steps=128, ctx_lo=512,
                                            ctx_hi=8192, seed=55),
+    # 0.6B symmetric int4-g32 weights, f16 KV; 16 x 1024 prefill (every projection on the large
+    # tile product), then 32 greedy decode steps at batch 16.
+    "q06b_int4sym_b16_p1024_d32": Workload("q06b_int4sym_b16_p1024_d32", "q06b_int4sym", n_seqs=16,
+                                           prompt_len=1024, decode_steps=32, seed=66),
+    # The headline prefill + decode shape (32 x 1024, 256 greedy steps) with symmetric int4-g32
+    # weights: a benchmark workload for the 4-bit path.
+    "q06b_int4sym_b32_p1024_d256": Workload("q06b_int4sym_b32_p1024_d256", "q06b_int4sym", n_seqs=32,
+                                            prompt_len=1024, decode_steps=256, seed=33),
+    # The same format on the ragged batch-64 decode workload of the uint4 weights.
+    "q06b_int4sym_b64_ragged_d128": Workload("q06b_int4sym_b64_ragged_d128", "q06b_int4sym", n_seqs=64,
+                                             prompt_len=None, decode_steps=128, ctx_lo=512,
+                                             ctx_hi=8192, seed=55),
 }
 
 

@@ -16,6 +16,10 @@ layout "Candle model runner" section 2.4 gives for the projections):
   ``quantize_uint4_g32``. The decoder reconstructs W = (q - zp) * scale
   ("Byte-identical: 1,000 tokens of proof", section "The bar we set"); this
   module only chooses the codes and never reconstructs weights.
+* ``int4sym``: the symmetric int4 format of "Candle model runner" section 2.5
+  with groups of 32 input columns: a signed 4-bit value per element and one
+  f16 scale per group, chosen by ``quantize_int4_sym_g32`` (the stored-file
+  form the runner loads; the decoder reconstructs W = q * scale).
 """
 
 from __future__ import annotations
@@ -34,6 +38,11 @@ class Q4(NamedTuple):
     q: np.ndarray  # uint8 [out, in], values 0..15 (one code per element, unpacked)
     scale: np.ndarray  # uint16 [out, in // 32], bfloat16 bit patterns
     zp: np.ndarray  # uint16 [out, in // 32], bfloat16 bit patterns
+
+
+class Q4S(NamedTuple):
+    q: np.ndarray  # int8 [out, in], values -8..7 (one per element, unpacked)
+    scale: np.ndarray  # uint16 [out, in // 32], f16 bit patterns
 
 
 def fp32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -73,6 +82,24 @@ def quantize_uint4_g32(w: np.ndarray) -> Q4:
     return Q4(q.reshape(out, inp), scale_bits, zp_bits)
 
 
+def quantize_int4_sym_g32(w: np.ndarray) -> Q4S:
+    """Choose signed int4 values and f16 scales per 32-column group ("Candle model runner" 2.5).
+
+    Per group, in float32 arithmetic: s = f16(max|W| / 7) (round to nearest even),
+    q = clamp(rint(W / s), -8, 7) with rint rounding half to even and ``s`` the stored f16
+    value. A group of zeros (s = 0, where W / s is undefined) stores q = 0.
+    """
+    out, inp = w.shape
+    assert inp % GROUP == 0
+    g = np.ascontiguousarray(w, dtype=np.float32).reshape(out, inp // GROUP, GROUP)
+    s16 = (np.abs(g).max(axis=-1) / np.float32(7.0)).astype(np.float16)
+    s = s16.astype(np.float32)[..., None]
+    safe = np.where(s > 0, s, np.float32(1.0))
+    r = np.where(s > 0, np.rint(g / safe), np.float32(0.0))
+    q = np.clip(r, -8, 7).astype(np.int8)
+    return Q4S(q.reshape(out, inp), s16.view(np.uint16))
+
+
 MATRIX_NAMES = ("wq", "wk", "wv", "wo", "w_gate", "w_up", "w_down")
 GAIN_NAMES = ("attn_norm", "q_norm", "k_norm", "ffn_norm")
 
@@ -100,6 +127,8 @@ def _store(m: ModelShape, w: np.ndarray):
         return fp32_to_bf16_bits(w)
     if m.weight_dtype == "uint4":
         return quantize_uint4_g32(w)
+    if m.weight_dtype == "int4sym":
+        return quantize_int4_sym_g32(w)
     raise ValueError(m.weight_dtype)
 
 
@@ -124,6 +153,10 @@ def make_weights(m: ModelShape | str, seed: int | None = None) -> Weights:
             parts.append(quantize_uint4_g32(_draw(rng, (min(step, V - r0), d), m.init_std)))
         embed = Q4(np.concatenate([p.q for p in parts]), np.concatenate([p.scale for p in parts]),
                    np.concatenate([p.zp for p in parts]))
+    elif m.weight_dtype == "int4sym":
+        step = 16384
+        parts = [quantize_int4_sym_g32(_draw(rng, (min(step, V - r0), d), m.init_std)) for r0 in range(0, V, step)]
+        embed = Q4S(np.concatenate([p.q for p in parts]), np.concatenate([p.scale for p in parts]))
     else:
         embed = _store(m, _draw(rng, (V, d), m.init_std))
     shapes = matrix_shapes(m)

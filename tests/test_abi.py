@@ -12,7 +12,7 @@ import pytest
 
 from conftest import ROOT, golden_rows
 from decoder_forward_pass_amd import binding as B
-from decoder_forward_pass_amd.blob import pack_blob, pack_uint4
+from decoder_forward_pass_amd.blob import pack_blob, pack_int4_sym, pack_uint4
 from decoder_forward_pass_amd.session import make_config
 from synthetic import MODELS, make_weights, param_count
 
@@ -103,6 +103,49 @@ def test_uint4_nibble_order_worked_example():
     codes = np.array([[int(v) for v in row[0].split()]], np.uint8)
     want = [int(v, 16) for v in row[1].split()]
     assert pack_uint4(codes).reshape(-1).tolist() == want
+
+
+def test_int4_sym_nibble_order_worked_example():
+    (row,) = golden_rows("int4_sym_nibbles.txt")
+    vals = np.array([[int(v) for v in row[0].split()]], np.int8)
+    want = [int(v, 16) for v in row[1].split()]
+    assert pack_int4_sym(vals).reshape(-1).tolist() == want
+    with pytest.raises(ValueError):
+        pack_int4_sym(np.array([[8, 0]]))
+
+
+def test_int4_sym_blob_layout_has_codes_and_f16_scales_only():
+    cfg = tiny_cfg(weight_dtype=B.DEC_INT4_SYM_G32)
+    B.dec_check_config(cfg)
+    u4 = tiny_cfg(weight_dtype=B.DEC_UINT4_G32)
+    for i in range(B.dec_weight_count(cfg)):
+        e, f = B.dec_weight_entry(cfg, i), B.dec_weight_entry(u4, i)
+        if e.dtype == B.DEC_F32:
+            continue
+        assert e.dtype == B.DEC_INT4_SYM_G32
+        assert e.bytes == e.rows * e.cols // 2 == f.bytes
+        assert e.group_bytes == e.rows * (e.cols // 32) * 2
+        assert e.zp_offset == 0
+        assert e.scale_offset >= e.offset + e.bytes and e.scale_offset % 256 == 0
+    # one bf16 zero-point array fewer per matrix than the asymmetric format
+    assert B.dec_weight_bytes(cfg) < B.dec_weight_bytes(u4)
+
+
+def test_pack_blob_places_int4_sym_codes_and_scales():
+    import dataclasses
+    shape = dataclasses.replace(MODELS["tiny_f32"], weight_dtype="int4sym")
+    w = make_weights(shape)
+    cfg = tiny_cfg(weight_dtype=B.DEC_INT4_SYM_G32)
+    blob = pack_blob(cfg, w)
+    e = B.dec_weight_entry(cfg, 2)  # layer 0 W_q
+    src = w.layers[0]["wq"]
+    codes = blob[e.offset:e.offset + e.bytes].reshape(e.rows, e.cols // 2)
+    lo = (codes & 15).astype(np.int16)
+    hi = (codes >> 4).astype(np.int16)
+    assert np.array_equal(np.where(lo > 7, lo - 16, lo), src.q[:, 0::2])
+    assert np.array_equal(np.where(hi > 7, hi - 16, hi), src.q[:, 1::2])
+    sc = blob[e.scale_offset:e.scale_offset + e.group_bytes].view(np.uint16).reshape(e.rows, e.cols // 32)
+    assert np.array_equal(sc, src.scale)
 
 
 def test_pack_blob_places_every_array():

@@ -1,0 +1,134 @@
+"""GPU parity at full size for symmetric int4-g32 weights (W = q * s with signed 4-bit q and an
+f16 scale per 32 input columns, "Candle model runner" section 2.5 "Int4 weights") with an f16 KV
+cache: 16 sequences of 1,024 prompt tokens prefilled in one call (every projection then runs on
+the 256 x 256 tile product), then 32 greedy decode steps at batch 16 with the next token ids
+passed on the device.
+
+Dequantisation is checked bit for bit against the oracle's float32 evaluation of W = q * s on
+whole matrices. The oracle follows sequence 0 (its last prompt logits, then a fixed set of decode
+steps with the GPU's tokens); gate 2e-2 of each row's oracle logit range. Sequence 0 is also run
+alone (a 1,024-row prefill takes the 64 x 64 tile product instead): its last prompt logits and
+its decode logits must equal the batch's bit for bit.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+from gpu_util import compare, report
+import oracle.model as om
+from synthetic import MODELS, WORKLOADS, make_prompts, make_weights
+
+REL = 2e-2
+WL = "q06b_int4sym_b16_p1024_d32"
+CHECK_STEPS = (0, 1, 15, 31)
+
+
+@pytest.fixture(scope="module")
+def weights():
+    return make_weights(MODELS[WORKLOADS[WL].model])
+
+
+@pytest.fixture(scope="module")
+def run(weights):
+    from decoder_forward_pass_amd import binding as B
+    from decoder_forward_pass_amd.session import BlockAllocator, Session
+    wl = WORKLOADS[WL]
+    shape = MODELS[wl.model]
+    prompts = make_prompts(wl)
+    S, T, steps = wl.n_seqs, wl.prompt_len, wl.decode_steps
+    per_seq = math.ceil((T + steps) / shape.block_tokens)
+    n_blocks = (S + 1) * per_seq
+    s = Session(shape, weights, max_context=T + steps, n_blocks=n_blocks, max_rows=S * T, max_seqs=S)
+    alloc = BlockAllocator(n_blocks, shape.block_tokens, seed=7)
+    for i in range(S):
+        alloc.ensure(i, T + steps)
+    alloc.ensure("alone", T + steps)
+    hist = torch.zeros((steps + 1, S), dtype=torch.int32, device="cuda")
+    last = torch.empty((S, shape.vocab), dtype=torch.float32, device="cuda")
+    print(f"[int4sym] prefill {S} x {T}", flush=True)
+    tbl = alloc.table_array(list(range(S)))
+    s.prefill([0] * S, [T] * S, np.concatenate(prompts), tbl, B.DEC_LOGITS_LAST, logits=last, next_tokens=hist[0])
+    tbl_alone = alloc.table_array(["alone"])
+    last_alone = s.prefill([0], [T], prompts[0], tbl_alone, B.DEC_LOGITS_LAST).clone()
+    keep = {}
+    logits = torch.empty((S, shape.vocab), dtype=torch.float32, device="cuda")
+    pos = np.full(S, T, np.int32)
+    print(f"[int4sym] decode {steps} steps", flush=True)
+    for t in range(steps):
+        s.decode_step(pos + t, tbl, tokens_device=hist[t], logits=logits, next_tokens=hist[t + 1])
+        if t in CHECK_STEPS:
+            keep[t] = logits[0].cpu().numpy()
+    hist_cpu = hist.cpu().numpy()
+    la = torch.empty((1, shape.vocab), dtype=torch.float32, device="cuda")
+    alone = {}
+    for t in range(steps):
+        s.decode_step([T + t], tbl_alone, tokens_host=hist_cpu[t, 0:1], logits=la)
+        if t in CHECK_STEPS:
+            alone[t] = la.cpu().numpy()[0]
+    deq = {idx: s.dequant(idx).cpu().numpy() for idx in (0, 2, 7, 11, 1 + 27 * 11 + 9)}
+    out = dict(last=last[0].cpu().numpy(), last_alone=last_alone.cpu().numpy()[0], hist=hist_cpu, keep=keep,
+               alone=alone, deq=deq)
+    torch.cuda.synchronize()
+    s.close()
+    yield wl, shape, weights, prompts, out
+
+
+def test_dequant_is_bit_exact_on_whole_matrices(run):
+    wl, shape, w, prompts, out = run
+    from decoder_forward_pass_amd.session import make_config
+    from decoder_forward_pass_amd import binding as B
+    cfg = make_config(shape, max_context=64, n_blocks=1, max_rows=1, max_seqs=1)
+    for idx, got in out["deq"].items():
+        e = B.dec_weight_entry(cfg, idx)
+        nm = e.name.decode()
+        src = w.embed if nm == "embed" else w.layers[e.layer][nm]
+        ref = om.widen_matrix(src, "int4sym").astype(np.float32)
+        assert got.shape == ref.shape
+        assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), nm
+
+
+def test_batch_invariance_bit_exact(run):
+    wl, shape, w, prompts, out = run
+    assert np.array_equal(out["last"].view(np.uint32), out["last_alone"].view(np.uint32))
+    for t in CHECK_STEPS:
+        assert np.array_equal(out["keep"][t].view(np.uint32), out["alone"][t].view(np.uint32)), t
+
+
+def test_prefill_and_decode_match_oracle(run):
+    wl, shape, w, prompts, out = run
+    dec = om.OracleDecoder(w)
+    c = dec.new_cache(capacity=wl.prompt_len + wl.decode_steps)
+    print(f"[int4sym] oracle prefill ({wl.prompt_len} tokens)", flush=True)
+    ref_last = dec.forward([(prompts[0], c)], logits="last")[0]
+    rows_gpu, rows_ref = [out["last"]], [ref_last]
+    hist = out["hist"]
+    flips = bad = 0
+
+    def choice(ref_row, tok):
+        nonlocal flips, bad
+        top = int(np.argmax(ref_row))
+        if top != tok:
+            flips += 1
+            if ref_row[top] - ref_row[tok] > REL * (ref_row.max() - ref_row.min()):
+                bad += 1
+
+    choice(ref_last, int(hist[0, 0]))
+    for t in range(wl.decode_steps):
+        tok = np.array([hist[t, 0]])
+        if t in CHECK_STEPS:
+            r = dec.forward([(tok, c)], logits="all")[0]
+            rows_gpu.append(out["keep"][t])
+            rows_ref.append(r)
+            choice(r, int(hist[t + 1, 0]))
+        else:
+            dec.forward([(tok, c)], logits="none")
+    row = compare(np.array(rows_gpu), np.array(rows_ref), rel_range=REL)
+    row.update(type="logit_parity", case=wl.name, path="seq0", greedy_flips=flips, greedy_flips_outside_gate=bad)
+    report(row)
+    assert row["pass"], row
+    assert bad == 0

@@ -1,8 +1,9 @@
-"""GPU parity on the two-layer tiny decoder (float32, and bf16 / f16-KV / uint4 variants).
+"""GPU parity on the two-layer tiny decoder (float32, and bf16 / f16-KV / uint4 / symmetric int4
+variants).
 
 Every call goes through the C ABI (ctypes binding); expected values come only from the
 oracle. Gates: float32 max-abs <= 1e-3 ("Proving it's the same model", "Pick the tolerance
-before looking"); bf16 / f16-KV / uint4 per-row max-abs <= 2e-2 of the row's oracle logit
+before looking"); bf16 / f16-KV / 4-bit per-row max-abs <= 2e-2 of the row's oracle logit
 range ("Candle model runner" 2.4, "The f16 bound": 1e-3 of the largest logit, 2e-2).
 """
 
@@ -27,6 +28,8 @@ VARIANTS = {
     "f32": MODELS["tiny_f32"],
     "bf16_f16kv": dataclasses.replace(MODELS["tiny_f32"], name="tiny_bf16", weight_dtype="bf16", kv_dtype="f16"),
     "uint4_f16kv": dataclasses.replace(MODELS["tiny_f32"], name="tiny_uint4", weight_dtype="uint4", kv_dtype="f16"),
+    "int4sym_f16kv": dataclasses.replace(MODELS["tiny_f32"], name="tiny_int4sym", weight_dtype="int4sym",
+                                         kv_dtype="f16"),
     "bf16_f32kv": dataclasses.replace(MODELS["tiny_f32"], name="tiny_bf16_f32kv", weight_dtype="bf16", kv_dtype="f32"),
 }
 

@@ -116,6 +116,69 @@ def test_uint4_dequant_group_boundaries():
     assert np.all(w[1, :32] == 4.0) and np.all(w[1, 32:] == 0.0)
 
 
+# ---- symmetric int4-g32 ("Candle model runner" 2.5) ----------------------------------------
+
+def _example_group():
+    (row,) = golden_rows("int4_sym_example.txt")
+    w = [float(v) for v in row[0].split()]
+    return row, np.array([w + [0.0] * (32 - len(w))], np.float32)
+
+
+def test_int4_sym_chooser_worked_example():
+    from synthetic import quantize_int4_sym_g32
+    row, w = _example_group()
+    q = quantize_int4_sym_g32(w)
+    assert int(q.scale[0, 0]) == int(row[2], 16)
+    assert float(nx.f16_to_f32(q.scale)[0, 0]) == float(row[1])
+    want = [int(v) for v in row[3].split()]
+    assert q.q[0, :4].tolist() == want and not q.q[0, 4:].any()
+    # the unrounded scale gives another last value: the chooser divides by the stored one
+    alt = int(row[4])
+    assert int(np.rint(np.float32(w[0, 3]) / np.float32(0.2))) == alt != want[3]
+
+
+def test_int4_sym_dequant_worked_example_is_exact():
+    row, w = _example_group()
+    s16 = np.array([[int(row[2], 16)]], np.uint16)
+    q = np.zeros((1, 32), np.int8)
+    q[0, :4] = [int(v) for v in row[3].split()]
+    got = nx.dequant_int4_sym_g32(q, s16)
+    s = Fraction(row[1])
+    assert [Fraction(float(v)) for v in got[0, :4]] == [int(v) * s for v in row[3].split()]
+    assert not got[0, 4:].any()
+    # 4 * 0.199951171875 etc.: the reconstruction the page's numbers give
+    assert got[0, :4].tolist() == [0.7998046875, -1.399658203125, 0.0, 0.39990234375]
+
+
+def test_int4_sym_dequant_is_exact_rational_and_per_group():
+    rng = np.random.default_rng(12)
+    out, inp = 6, 96
+    q = rng.integers(-8, 8, size=(out, inp)).astype(np.int8)
+    sb = rng.uniform(1e-5, 2.0, size=(out, inp // 32)).astype(np.float16).view(np.uint16)
+    w = nx.dequant_int4_sym_g32(q, sb)
+    sv = sb.view(np.float16)
+    for o in range(out):
+        for i in range(inp):
+            assert Fraction(float(w[o, i])) == int(q[o, i]) * Fraction(float(sv[o, i // 32]))
+
+
+def test_int4_sym_round_trip_error_bound():
+    # |W - q s| <= s / 2 per element (section 2.5), up to the float32 division's rounding
+    from synthetic import quantize_int4_sym_g32
+    rng = np.random.default_rng(13)
+    w = (rng.standard_normal((64, 256)) * rng.uniform(1e-3, 3.0, size=(64, 1))).astype(np.float32)
+    w[3, 32:64] = 0.0  # a group of zeros: s = 0, q = 0, exact
+    q = quantize_int4_sym_g32(w)
+    wh = nx.dequant_int4_sym_g32(q.q, q.scale).astype(np.float64)
+    s = np.repeat(nx.f16_to_f32(q.scale).astype(np.float64), 32, axis=1)
+    assert np.all(np.abs(w - wh) <= s / 2 * (1 + 1e-6))
+    assert not q.q[3, 32:64].any() and not wh[3, 32:64].any()
+    assert q.q.min() >= -8 and q.q.max() <= 7
+    # symmetric: negating the weights negates the values (rint is odd, no value reaches -8)
+    qn = quantize_int4_sym_g32(-w)
+    assert np.array_equal(qn.q, -q.q) and np.array_equal(qn.scale, q.scale)
+
+
 # ---- paged KV pool addressing ----------------------------------------------------------------
 
 def test_kv_address_worked_example():
