@@ -371,11 +371,39 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
   const int brow = min(br0 + (lane & 15), bm[0].rows - 1);
   const int kl = (lane >> 4) * 8;
   const int k0 = wave * NKS * 32 + kl;
-  BRaw<WF> braw[BDMA ? 1 : NB][BDMA ? 1 : NKS];
+  // 4-bit weights, k-steps in fours (WIDE): lane group g = lane / 16 takes a whole 32-column
+  // group of its weight row per four MFMAs (16 bytes of codes and one scale in single loads):
+  // in k-step 4 j + v it holds columns 32 (4 j + g) + 8 v .. + 8 of the wave's range, and the
+  // activation fragments follow the same order. Each k still enters once, and the order does
+  // not depend on M.
+  constexpr bool WIDE = is_q4(WF) && NKS % 4 == 0;
+  auto kof = [&](int i) {  // first of the 8 columns this lane holds in k-step i
+    if constexpr (WIDE)
+      return wave * NKS * 32 + 32 * (4 * (i >> 2) + (lane >> 4)) + 8 * (i & 3);
+    else
+      return k0 + i * 32;
+  };
+  struct BWide {
+    u32x4 codes;
+    uint16_t scale, zp;
+  };
+  BRaw<WF> braw[BDMA || WIDE ? 1 : NB][BDMA || WIDE ? 1 : NKS];
+  BWide bwide[WIDE ? NB : 1][WIDE ? NKS / 4 : 1];
   u32x4 araw[LDSA ? 1 : MT][LDSA ? 1 : NKS];
   float4 sraw[NORM ? 4 : 1];
   if (active) {
-    if constexpr (!BDMA) {
+    if constexpr (WIDE) {
+#pragma unroll
+      for (int j = 0; j < NKS / 4; ++j)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const int grp = wave * NKS + 4 * j + (lane >> 4);
+          bwide[nb][j].codes = *(const u32x4*)((const uint8_t*)bm[nb].w + (int64_t)brow * (K / 2) + grp * 16);
+          const int64_t gi = (int64_t)brow * (K / 32) + grp;
+          bwide[nb][j].scale = bm[nb].scale[gi];
+          if constexpr (WF == DEC_UINT4_G32) bwide[nb][j].zp = bm[nb].zp[gi];
+        }
+    } else if constexpr (!BDMA) {
 #pragma unroll
       for (int i = 0; i < NKS; ++i)
 #pragma unroll
@@ -385,9 +413,9 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int arow = min(m0 + mt * 16 + (lane & 15), M - 1);
-        const uint16_t* ap = (const uint16_t*)a.A + (int64_t)arow * a.lda + k0;
+        const uint16_t* ap = (const uint16_t*)a.A + (int64_t)arow * a.lda;
 #pragma unroll
-        for (int i = 0; i < NKS; ++i) araw[mt][i] = *(const u32x4*)(ap + i * 32);
+        for (int i = 0; i < NKS; ++i) araw[mt][i] = *(const u32x4*)(ap + kof(i));
       }
     }
   }
@@ -468,14 +496,21 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
       bf16x8 bf[NB];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        if constexpr (BDMA)
+        if constexpr (BDMA) {
           bf[nb] = __builtin_bit_cast(bf16x8, lds_bfrag(nb, lane & 15, k0 + i * 32));
-        else
-          bf[nb] = b_frag<WF>(braw[BDMA ? 0 : nb][BDMA ? 0 : i]);
+        } else if constexpr (WIDE) {
+          BRaw<WF> r;
+          r.codes = bwide[nb][i >> 2].codes[i & 3];
+          r.scale = bwide[nb][i >> 2].scale;
+          if constexpr (WF == DEC_UINT4_G32) r.zp = bwide[nb][i >> 2].zp;
+          bf[nb] = b_frag<WF>(r);
+        } else {
+          bf[nb] = b_frag<WF>(braw[BDMA || WIDE ? 0 : nb][BDMA || WIDE ? 0 : i]);
+        }
       }
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const bf16x8 af = __builtin_bit_cast(bf16x8, LDSA ? lds_frag(mt * 16 + (lane & 15), k0 + i * 32, 0)
+        const bf16x8 af = __builtin_bit_cast(bf16x8, LDSA ? lds_frag(mt * 16 + (lane & 15), kof(i), 0)
                                                           : araw[LDSA ? 0 : mt][LDSA ? 0 : i]);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
@@ -594,6 +629,32 @@ __global__ __launch_bounds__(1024) void lmhead_decode(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < G; ++i) dst[i] = load_b_raw<WF>(E, brow, K, min(kg + i, ksteps - 1) * 32 + kl);
   };
+  // 4-bit E (WIDE; K % 256 == 0, so groups are whole): lane group g = lane / 16 takes a whole
+  // 32-column group of its row per four MFMAs, as in the decode GEMM: in k-step kg + 4 h + v it
+  // holds columns 32 (kg + 4 h + g) + 8 v .. + 8, and the activation fragments follow
+  constexpr bool WIDE = is_q4(WF);
+  struct BWide {
+    u32x4 codes;
+    uint16_t scale, zp;
+  };
+  auto load_wide = [&](int j, BWide (&dst)[G / 4]) {
+    const int tile = t0 + wave + (j / gpt) * 16, kg = (j % gpt) * G;
+    const int brow = min(tile * 16 + (lane & 15), E.rows - 1);
+#pragma unroll
+    for (int h = 0; h < G / 4; ++h) {
+      const int grp = kg + 4 * h + (lane >> 4);
+      dst[h].codes = *(const u32x4*)((const uint8_t*)E.w + (int64_t)brow * (K / 2) + grp * 16);
+      const int64_t gi = (int64_t)brow * (K / 32) + grp;
+      dst[h].scale = E.scale[gi];
+      if constexpr (WF == DEC_UINT4_G32) dst[h].zp = E.zp[gi];
+    }
+  };
+  auto kof = [&](int kg, int i) {  // first of the 8 columns this lane holds in k-step kg + i
+    if constexpr (WIDE)
+      return 32 * (kg + 4 * (i >> 2) + (lane >> 4)) + 8 * (i & 3);
+    else
+      return (kg + i) * 32 + kl;
+  };
   f32x4 acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -610,19 +671,39 @@ __global__ __launch_bounds__(1024) void lmhead_decode(GemmArgs a) {
       bv[mt][r] = -__builtin_inff();
       bi[mt][r] = 0x7fffffff;
     }
-  BRaw<WF> cur[G], nxt[G];
-  if (total > 0) load_group(0, cur);
+  BRaw<WF> cur[WIDE ? 1 : G], nxt[WIDE ? 1 : G];
+  BWide wcur[WIDE ? G / 4 : 1], wnxt[WIDE ? G / 4 : 1];
+  if (total > 0) {
+    if constexpr (WIDE)
+      load_wide(0, wcur);
+    else
+      load_group(0, cur);
+  }
   for (int j = 0; j < total; ++j) {
-    if (j + 1 < total) load_group(j + 1, nxt);
+    if (j + 1 < total) {
+      if constexpr (WIDE)
+        load_wide(j + 1, wnxt);
+      else
+        load_group(j + 1, nxt);
+    }
     const int kg = (j % gpt) * G;
 #pragma unroll
     for (int i = 0; i < G; ++i) {
       if (kg + i < ksteps) {
-        const bf16x8 bf = b_frag<WF>(cur[i]);
+        bf16x8 bf;
+        if constexpr (WIDE) {
+          BRaw<WF> r;
+          r.codes = wcur[i >> 2].codes[i & 3];
+          r.scale = wcur[i >> 2].scale;
+          if constexpr (WF == DEC_UINT4_G32) r.zp = wcur[i >> 2].zp;
+          bf = b_frag<WF>(r);
+        } else {
+          bf = b_frag<WF>(cur[WIDE ? 0 : i]);
+        }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           const bf16x8 af = __builtin_bit_cast(bf16x8, *(const u32x4*)(s_h + (mt * 16 + (lane & 15)) * KS +
-                                                                       (kg + i) * 32 + kl));
+                                                                       kof(kg, i)));
           acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc[mt], 0, 0, 0);
         }
       }
@@ -645,8 +726,13 @@ __global__ __launch_bounds__(1024) void lmhead_decode(GemmArgs a) {
         acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
+    if constexpr (WIDE) {
 #pragma unroll
-    for (int i = 0; i < G; ++i) cur[i] = nxt[i];
+      for (int h = 0; h < G / 4; ++h) wcur[h] = wnxt[h];
+    } else {
+#pragma unroll
+      for (int i = 0; i < G; ++i) cur[i] = nxt[i];
+    }
   }
   if constexpr (AMX) {
     if (amx) {
