@@ -12,6 +12,7 @@ Modules:
   numerics  -- f16 rounding and widening, bf16 widening, uint4 and symmetric int4
                dequantisation
   paged     -- where a key or value of a position lands in the paged KV pool
+  sampling  -- seeded sampling of a token from a row of logits, and its PCG32 streams
   model     -- the numpy float64 decoder: full, cached, chunked, batched, greedy
   loops     -- a second, loop-only decoder for tiny shapes
 
