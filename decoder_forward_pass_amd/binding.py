@@ -67,9 +67,26 @@ class dec_weight_info(ctypes.Structure):
     ]
 
 
+class dec_sampling(ctypes.Structure):
+    _fields_ = [
+        ("temperature", ctypes.c_double), ("top_p", ctypes.c_double), ("min_p", ctypes.c_double),
+        ("repetition_penalty", ctypes.c_double), ("presence_penalty", ctypes.c_double),
+        ("frequency_penalty", ctypes.c_double), ("top_k", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    ]
+
+
+class dec_history(ctypes.Structure):
+    _fields_ = [("prompt_offset", ctypes.c_int32), ("prompt_len", ctypes.c_int32),
+                ("output_offset", ctypes.c_int32), ("output_len", ctypes.c_int32)]
+
+
+DEC_PURPOSE_SAMPLE = 4
+DEC_SAMPLE_MAX_NUCLEUS = 1024
+
 EXPORTS = ["dec_check_config", "dec_weight_bytes", "dec_weight_count", "dec_weight_entry", "dec_kv_pool_bytes",
            "dec_workspace_bytes", "dec_init", "dec_free", "dec_last_error", "dec_prefill", "dec_decode_step",
-           "dec_check_step", "dec_debug_dequant", "dec_timing_enable", "dec_timing_read"]
+           "dec_check_step", "dec_debug_dequant", "dec_rng_stream", "dec_sample", "dec_timing_enable",
+           "dec_timing_read"]
 
 KERNEL_CLASSES = ["embed", "rmsnorm", "gemm_qkv", "qk_rope_kv", "attn_prefill", "attn_rows", "attn_combine",
                   "gemm_o", "gemm_gateup", "gemm_down", "gemm_lmhead", "argmax"]
@@ -96,6 +113,9 @@ def _load():
         "dec_decode_step": (ctypes.c_int, [VP, VP, I32, i32p, VP, i32p, i32p, I32, VP, VP]),
         "dec_check_step": (ctypes.c_int, [cfgp, I32, i32p, i32p, i32p, i32p, I32, I32, ctypes.c_char_p, SZ]),
         "dec_debug_dequant": (ctypes.c_int, [VP, VP, ctypes.c_int, VP]),
+        "dec_rng_stream": (None, [ctypes.c_uint64, ctypes.c_uint64, P(ctypes.c_uint64)]),
+        "dec_sample": (ctypes.c_int, [VP, VP, I32, VP, ctypes.c_int64, P(dec_sampling), P(dec_history), VP,
+                                      ctypes.c_int64, VP, VP, VP]),
         "dec_timing_enable": (ctypes.c_int, [VP, ctypes.c_uint32]),
         "dec_timing_read": (ctypes.c_int, [VP, ctypes.c_int, P(ctypes.c_double), P(ctypes.c_int64)]),
     }
@@ -209,6 +229,25 @@ def dec_check_step(cfg: dec_config, start, n_new, tokens, block_tables, logits_m
 
 def dec_debug_dequant(ctx: int, stream: int, index: int, out: int) -> None:
     _check(_lib.dec_debug_dequant(ctx, stream or None, index, out), ctx)
+
+
+def dec_rng_stream(seed: int, purpose: int = DEC_PURPOSE_SAMPLE):
+    """(state, increment) of the PCG32 stream(seed, purpose)."""
+    out = (ctypes.c_uint64 * 2)()
+    _lib.dec_rng_stream(seed & (2 ** 64 - 1), purpose, out)
+    return int(out[0]), int(out[1])
+
+
+def dec_sample(ctx: int, stream: int, logits: int, ld: int, params, history, ids: int, n_ids: int, rng: int,
+               next_ids: int, logprob: int = 0) -> None:
+    """params: sequence of dec_sampling; history: sequence of dec_history (host); the rest device addresses."""
+    n = len(params)
+    if len(history) != n:
+        raise ValueError("params and history must have one entry per sequence")
+    pa = (dec_sampling * n)(*params)
+    ha = (dec_history * n)(*history)
+    _check(_lib.dec_sample(ctx, stream or None, n, logits, ld, pa, ha, ids or None, n_ids, rng, next_ids,
+                           logprob or None), ctx)
 
 
 def dec_timing_enable(ctx: int, class_mask: int) -> None:

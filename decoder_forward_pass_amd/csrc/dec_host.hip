@@ -141,7 +141,7 @@ size_t kv_bytes(const dec_config& c) {
 // ---- workspace layout ----------------------------------------------------------------------
 
 struct Ws {
-  size_t rope, meta, x, h, qkv, q, o, a, part, amax, ssq, xg, total;
+  size_t rope, meta, x, h, qkv, q, o, a, part, amax, ssq, xg, samp, counts, total;
   size_t meta_ints;  // capacity of the metadata region in int32
   int chunk, nch_max, max_blocks_per_seq, max_tiles;
   int act_bytes, kv_el;
@@ -182,6 +182,8 @@ Ws ws_layout(const dec_config& c) {
   w.amax = take(argmax_scratch_bytes((int)R, (int)S));
   w.ssq = take(S * (d / 16) * 4);  // decode: sums of squares of the residual in 16-column partials
   w.xg = take(S * d * 2);          // decode: bf16(residual * the next norm's gain)
+  w.samp = take(S * sizeof(SampleSeq));           // sampling: per-sequence parameters and history
+  w.counts = take(S * (size_t)c.vocab * 4);       // sampling: per-sequence count table (kept zero)
   w.total = off;
   return w;
 }
@@ -263,6 +265,8 @@ struct dec_ctx {
   int32_t* staging[kSlots];
   hipEvent_t ev[kSlots];
   int slot;
+  SampleSeq* samp_staging;  // pinned: the last dec_sample call's parameters
+  hipEvent_t samp_ev;       // that upload's completion
   std::string err;
 };
 
@@ -633,6 +637,8 @@ int dec_init(const dec_config* cfg, const void* weights, size_t weight_bytes, vo
     ctx->staging[i] = nullptr;
     ctx->ev[i] = nullptr;
   }
+  ctx->samp_staging = nullptr;
+  ctx->samp_ev = nullptr;
   ctx->embed = wmat(ctx, 0);
   for (int l = 0; l < cfg->n_layers; ++l) {
     const int b = 1 + l * kPerLayer;
@@ -663,6 +669,16 @@ int dec_init(const dec_config* cfg, const void* weights, size_t weight_bytes, vo
     if (e != hipSuccess) return bail(e, "hipHostMalloc");
     e = hipEventCreateWithFlags(&ctx->ev[i], hipEventDisableTiming);
     if (e != hipSuccess) return bail(e, "hipEventCreate");
+  }
+  {
+    hipError_t e = hipHostMalloc((void**)&ctx->samp_staging, (size_t)cfg->max_seqs * sizeof(SampleSeq),
+                                 hipHostMallocDefault);
+    if (e != hipSuccess) return bail(e, "hipHostMalloc");
+    e = hipEventCreateWithFlags(&ctx->samp_ev, hipEventDisableTiming);
+    if (e != hipSuccess) return bail(e, "hipEventCreate");
+    // the sampler's count table starts zero; every dec_sample call leaves it zero
+    e = hipMemsetAsync(ctx->wsp + ctx->ws.counts, 0, (size_t)cfg->max_seqs * cfg->vocab * 4, st);
+    if (e != hipSuccess) return bail(e, "hipMemsetAsync(counts)");
   }
   // RoPE table: angle p * base^(-2j/D) in double precision, cos/sin rounded once to float
   const int half = cfg->head_dim / 2;
@@ -725,6 +741,11 @@ void dec_free(dec_ctx* ctx) {
     }
     if (ctx->staging[i]) (void)hipHostFree(ctx->staging[i]);
   }
+  if (ctx->samp_ev) {
+    (void)hipEventSynchronize(ctx->samp_ev);
+    (void)hipEventDestroy(ctx->samp_ev);
+  }
+  if (ctx->samp_staging) (void)hipHostFree(ctx->samp_staging);
   delete ctx;
 }
 
@@ -763,6 +784,65 @@ int dec_decode_step(dec_ctx* ctx, void* stream, int32_t n_seqs, const int32_t* t
   rc = upload_meta(ctx, st, n_seqs, positions, nullptr, tokens_host, block_tables, max_blocks, mode, &b, &max_ctx);
   if (rc) return rc;
   return run_forward(ctx, st, b, tokens_device, max_ctx, true, logits, next_tokens);
+}
+
+void dec_rng_stream(uint64_t seed, uint64_t purpose, uint64_t state_inc[2]) {
+  // child_seed = mix64(seed + purpose * golden gamma), mix64 the splitmix64 finaliser; then
+  // pcg32_srandom_r(child_seed, purpose): inc = 2 purpose + 1, one step from state 0, add the
+  // seed, one more step (the step's output is not needed here)
+  uint64_t z = seed + purpose * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  z ^= z >> 31;
+  const uint64_t inc = (purpose << 1) | 1u;
+  uint64_t st = 0;
+  st = st * 6364136223846793005ull + inc;
+  st += z;
+  st = st * 6364136223846793005ull + inc;
+  state_inc[0] = st;
+  state_inc[1] = inc;
+}
+
+int dec_sample(dec_ctx* ctx, void* stream, int32_t n_seqs, const float* logits, int64_t ld,
+               const dec_sampling* params, const dec_history* history, const int32_t* ids, int64_t n_ids,
+               uint64_t* rng, int32_t* next, double* logprob) {
+  if (!ctx) return fail(&g_err, DEC_E_ARG, "ctx is NULL");
+  const int V = ctx->cfg.vocab;
+  if (n_seqs <= 0) return fail(&ctx->err, DEC_E_ARG, "n_seqs must be >= 1");
+  if (n_seqs > ctx->cfg.max_seqs) return fail(&ctx->err, DEC_E_CAPACITY, "n_seqs %d exceeds max_seqs %d", n_seqs, ctx->cfg.max_seqs);
+  if (!logits || !params || !history || !rng || !next) return fail(&ctx->err, DEC_E_ARG, "a required pointer is NULL");
+  if (ld < V) return fail(&ctx->err, DEC_E_ARG, "ld %lld is below the vocabulary", (long long)ld);
+  if (n_ids < 0 || (n_ids > 0 && !ids)) return fail(&ctx->err, DEC_E_ARG, "ids is NULL or n_ids negative");
+  for (int s = 0; s < n_seqs; ++s) {
+    const dec_sampling& p = params[s];
+    const dec_history& h = history[s];
+    if (!(std::isfinite(p.temperature) && p.temperature >= 0.0)) return fail(&ctx->err, DEC_E_ARG, "sequence %d: temperature must be finite and >= 0", s);
+    if (!(p.top_p > 0.0 && p.top_p <= 1.0)) return fail(&ctx->err, DEC_E_ARG, "sequence %d: top_p must be in (0, 1]", s);
+    if (!(p.min_p >= 0.0 && p.min_p <= 1.0)) return fail(&ctx->err, DEC_E_ARG, "sequence %d: min_p must be in [0, 1]", s);
+    if (!(std::isfinite(p.repetition_penalty) && p.repetition_penalty > 0.0))
+      return fail(&ctx->err, DEC_E_ARG, "sequence %d: repetition_penalty must be finite and > 0", s);
+    if (!std::isfinite(p.presence_penalty) || !std::isfinite(p.frequency_penalty))
+      return fail(&ctx->err, DEC_E_ARG, "sequence %d: presence and frequency penalties must be finite", s);
+    if (p.top_k < 0 || p.reserved != 0) return fail(&ctx->err, DEC_E_ARG, "sequence %d: top_k must be >= 0, reserved 0", s);
+    if (h.prompt_offset < 0 || h.prompt_len < 0 || (int64_t)h.prompt_offset + h.prompt_len > n_ids ||
+        h.output_offset < 0 || h.output_len < 0 || (int64_t)h.output_offset + h.output_len > n_ids)
+      return fail(&ctx->err, DEC_E_ARG, "sequence %d: history ranges outside the id array", s);
+    const int64_t left = p.top_k > 0 && p.top_k < V ? p.top_k : V;
+    if (p.temperature > 0.0 && p.top_p < 1.0 && left > DEC_SAMPLE_MAX_NUCLEUS)
+      return fail(&ctx->err, DEC_E_UNSUPPORTED, "sequence %d: top_p < 1 orders at most %d ids; top_k leaves %lld", s,
+                  DEC_SAMPLE_MAX_NUCLEUS, (long long)left);
+  }
+  hipStream_t st = (hipStream_t)stream;
+  HIPCHECK(hipEventSynchronize(ctx->samp_ev));  // the previous call's upload has finished
+  for (int s = 0; s < n_seqs; ++s) {
+    ctx->samp_staging[s].p = params[s];
+    ctx->samp_staging[s].h = history[s];
+  }
+  SampleSeq* dseq = (SampleSeq*)(ctx->wsp + ctx->ws.samp);
+  HIPCHECK(hipMemcpyAsync(dseq, ctx->samp_staging, (size_t)n_seqs * sizeof(SampleSeq), hipMemcpyHostToDevice, st));
+  HIPCHECK(hipEventRecord(ctx->samp_ev, st));
+  LAUNCH(launch_sample(logits, ld, n_seqs, V, dseq, ids, (uint32_t*)(ctx->wsp + ctx->ws.counts), rng, next, logprob, st));
+  return DEC_OK;
 }
 
 int dec_debug_dequant(dec_ctx* ctx, void* stream, int index, float* out) {

@@ -154,6 +154,16 @@ hipError_t launch_argmax(const float* logits, int n_rows, int vocab, int32_t* ne
 hipError_t launch_argmax_final(const float* pv, const int32_t* pi, int n_rows, int nparts, int32_t* next,
                                hipStream_t s);
 
+// Seeded sampling of one token per sequence (dec_sample): sequence s samples row s of logits
+// with seqs[s]; counts is the [n_seqs][vocab] count table (zero on entry, left zero).
+struct SampleSeq {
+  dec_sampling p;
+  dec_history h;
+};
+hipError_t launch_sample(const float* logits, int64_t ld, int n_seqs, int vocab, const SampleSeq* seqs,
+                         const int32_t* ids, uint32_t* counts, uint64_t* rng, int32_t* next, double* logprob,
+                         hipStream_t s);
+
 // out[rows][cols] = widened / dequantised matrix (float32).
 hipError_t launch_dequant(int wdtype, const WMat& w, int rows, int cols, float* out, hipStream_t s);
 

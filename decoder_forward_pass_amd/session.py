@@ -119,6 +119,27 @@ class Session:
                           tokens_device=tokens_device.data_ptr() if tokens_device is not None else 0)
         return logits
 
+    def sample(self, logits, params, history, ids, rng, next_ids=None, logprob=None):
+        """One dec_sample call over the rows of ``logits`` (device float32 [n, ld]).
+
+        params: list of dec_sampling; history: list of dec_history ranges into ``ids`` (device
+        int32, or None); rng: device uint64 tensor [n, 2] (advanced in place). Returns
+        (next ids int32 [n], logprobs float64 [n]) on the device.
+        """
+        n = logits.shape[0]
+        if logits.dim() != 2 or logits.stride(1) != 1:
+            raise ValueError("logits must be [n, ld] with unit column stride")
+        # (torch reports stride 0 for a dimension of size 1)
+        ld = logits.stride(0) if n > 1 else logits.shape[1]
+        if next_ids is None:
+            next_ids = torch.empty(n, dtype=torch.int32, device=self.device)
+        if logprob is None:
+            logprob = torch.empty(n, dtype=torch.float64, device=self.device)
+        n_ids = ids.numel() if ids is not None else 0
+        B.dec_sample(self.ctx, self.stream, logits.data_ptr(), ld, params, history,
+                     ids.data_ptr() if n_ids else 0, n_ids, rng.data_ptr(), next_ids.data_ptr(), logprob.data_ptr())
+        return next_ids, logprob
+
     def dequant(self, index: int) -> torch.Tensor:
         e = B.dec_weight_entry(self.cfg, index)
         out = torch.empty((e.rows, e.cols), dtype=torch.float32, device=self.device)

@@ -248,6 +248,81 @@ int dec_check_step(const dec_config* cfg, int32_t n_seqs, const int32_t* start,
  */
 int dec_debug_dequant(dec_ctx* ctx, void* stream, int index, float* out);
 
+/* ---- seeded sampling ------------------------------------------------------------------ */
+
+/* Sampling parameters of one sequence ("Candle model runner" section 2.6, SamplingParams). */
+typedef struct dec_sampling {
+  double temperature;        /* >= 0; 0 is greedy: the largest value, ties to the lowest id, no draw */
+  double top_p;              /* in (0, 1]; 1 keeps every id */
+  double min_p;              /* in [0, 1]; 0 keeps every id */
+  double repetition_penalty; /* > 0; 1 leaves the logits as they are */
+  double presence_penalty;   /* finite; 0 for none */
+  double frequency_penalty;  /* finite; 0 for none */
+  int32_t top_k;             /* >= 0; 0 keeps every id */
+  int32_t reserved;          /* must be 0 */
+} dec_sampling;
+
+/* A sequence's history: its prompt ids and its output ids so far, as ranges of one id array. */
+typedef struct dec_history {
+  int32_t prompt_offset, prompt_len;
+  int32_t output_offset, output_len;
+} dec_history;
+
+#define DEC_PURPOSE_SAMPLE 4       /* the purpose id of the sampling stream */
+#define DEC_SAMPLE_MAX_NUCLEUS 1024 /* most ids the nucleus step orders (top_k bound when top_p < 1) */
+
+/*
+ * Host only: state_inc[0], state_inc[1] = the PCG32 state and increment of the
+ * request stream stream(seed, purpose) ("Candle model runner" section 2.6):
+ * pcg32_srandom_r(child_seed(seed, purpose), purpose) with child_seed(s, p) =
+ * mix64(s + p * 0x9E3779B97F4A7C15), mix64 the splitmix64 finaliser. Pass
+ * DEC_PURPOSE_SAMPLE for sampling; copy the pair into dec_sample's rng array.
+ */
+void dec_rng_stream(uint64_t seed, uint64_t purpose, uint64_t state_inc[2]);
+
+/*
+ * One token per sequence from a row of logits (for example dec_decode_step's
+ * logits), drawn on the device in float64 in the order of "Candle model
+ * runner" section 2.6: widen; repetition penalty over the distinct ids of
+ * prompt and output (a positive value divided by it, any other multiplied);
+ * presence and frequency penalties over the output only (an id seen c > 0
+ * times loses frequency * c + presence); the logprob is log softmax of these
+ * values; temperature 0 takes the largest value (ties to the lowest id) with no
+ * draw; otherwise divide by the temperature, keep the top_k by (value
+ * descending, id ascending), keep the nucleus (in that order, up to and
+ * including the id whose cumulative probability reaches top_p), keep the ids
+ * whose probability is at least min_p times the largest, take the softmax over
+ * the kept ids in ascending id order, draw one uniform u from the sequence's
+ * stream and return the first id in ascending order whose cumulative
+ * probability exceeds u. The probabilities of the top-p and min-p steps are
+ * over the ids top_k kept.
+ *   logits:   device float32 [n_seqs][ld], ld >= vocab; row s for sequence s
+ *   params:   host [n_seqs]
+ *   history:  host [n_seqs]; ranges into ids: offset >= 0, len >= 0,
+ *             offset + len <= n_ids
+ *   ids:      device int32 [n_ids] (NULL when n_ids == 0); ids outside
+ *             [0, vocab) are ignored
+ *   rng:      device uint64 [n_seqs][2]: each sequence's PCG32 (state,
+ *             increment), from dec_rng_stream; a sampled row advances it by one
+ *             uniform (two outputs), a greedy row leaves it as it is
+ *   next:     device int32 [n_seqs]
+ *   logprob:  device float64 [n_seqs] or NULL
+ * Sums over the at most DEC_SAMPLE_MAX_NUCLEUS ids of the nucleus path are
+ * left-to-right in ascending id order; sums over the whole vocabulary run
+ * left to right within fixed id ranges, then over the ranges in order (equal
+ * to a left-to-right sum up to rounding). Uses the workspace: a count table
+ * per sequence that every call leaves zero, so calls on one context must not
+ * overlap. Asynchronous on `stream`.
+ * Errors (checked on the host before anything is enqueued): DEC_E_ARG (a
+ * NULL pointer, a bad range, a parameter outside the ranges above),
+ * DEC_E_CAPACITY (n_seqs > max_seqs), DEC_E_UNSUPPORTED (temperature > 0 and
+ * top_p < 1 with more than DEC_SAMPLE_MAX_NUCLEUS ids left by top_k: top_k = 0
+ * or top_k >= vocab keep all vocab ids).
+ */
+int dec_sample(dec_ctx* ctx, void* stream, int32_t n_seqs, const float* logits, int64_t ld,
+               const dec_sampling* params, const dec_history* history, const int32_t* ids,
+               int64_t n_ids, uint64_t* rng, int32_t* next, double* logprob);
+
 /* ---- per-kernel timing (diagnostics) ------------------------------------------------ */
 
 /* kernel classes */

@@ -41,8 +41,9 @@ def test_struct_layout_matches_the_header():
     #include <stddef.h>
     #include "dec.h"
     int main(void) {
-      printf("%zu %zu %zu %zu %zu\n", sizeof(dec_config), offsetof(dec_config, rope_base),
-             offsetof(dec_config, max_seqs), sizeof(dec_weight_info), offsetof(dec_weight_info, group_bytes));
+      printf("%zu %zu %zu %zu %zu %zu %zu %zu\n", sizeof(dec_config), offsetof(dec_config, rope_base),
+             offsetof(dec_config, max_seqs), sizeof(dec_weight_info), offsetof(dec_weight_info, group_bytes),
+             sizeof(dec_sampling), offsetof(dec_sampling, top_k), sizeof(dec_history));
       return 0;
     }
     """
@@ -54,7 +55,8 @@ def test_struct_layout_matches_the_header():
         got = [int(v) for v in subprocess.run([exe], capture_output=True, text=True).stdout.split()]
     import ctypes
     want = [ctypes.sizeof(B.dec_config), B.dec_config.rope_base.offset, B.dec_config.max_seqs.offset,
-            ctypes.sizeof(B.dec_weight_info), B.dec_weight_info.group_bytes.offset]
+            ctypes.sizeof(B.dec_weight_info), B.dec_weight_info.group_bytes.offset,
+            ctypes.sizeof(B.dec_sampling), B.dec_sampling.top_k.offset, ctypes.sizeof(B.dec_history)]
     assert got == want
 
 
@@ -146,6 +148,16 @@ def test_pack_blob_places_int4_sym_codes_and_scales():
     assert np.array_equal(np.where(hi > 7, hi - 16, hi), src.q[:, 1::2])
     sc = blob[e.scale_offset:e.scale_offset + e.group_bytes].view(np.uint16).reshape(e.rows, e.cols // 32)
     assert np.array_equal(sc, src.scale)
+
+
+def test_rng_stream_matches_the_oracle_generator():
+    # the host seeding of a sampling stream: pcg32_srandom_r(child_seed(seed, 4), 4)
+    from oracle import sampling as sm
+    for seed in (0, 1, 42, 2 ** 63 + 5, 2 ** 64 - 1):
+        g = sm.stream(seed)
+        assert B.dec_rng_stream(seed) == (g.state, g.inc)
+    g = sm.Pcg32(sm.child_seed(0, 4), 4)
+    assert B.dec_rng_stream(0)[0] == g.state
 
 
 def test_pack_blob_places_every_array():
