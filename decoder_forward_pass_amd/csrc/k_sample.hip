@@ -3,9 +3,10 @@
 //
 //   1. the sequence's history marks its count table (bit 31: the id occurs in prompt or
 //      output; bits 0..30: its occurrences in the output), with integer atomics whose order
-//      does not matter; every later read of a logit applies the penalties from that entry
-//      (repetition divides a positive value and multiplies any other; an id seen c > 0 times
-//      in the output loses frequency * c + presence, two separately rounded operations);
+//      does not matter; one pass writes every id's penalised value to the sequence's float64
+//      scratch row (repetition divides a positive value and multiplies any other; an id seen
+//      c > 0 times in the output loses frequency * c + presence, two separately rounded
+//      operations), and the later passes read that row;
 //   2. the largest penalised value (ties to the lowest id) and Z = sum exp(l - max): the
 //      logprob of an id is (l - max) - log Z, taken before the temperature;
 //   3. temperature 0 returns the largest; otherwise values are divided by T and
@@ -17,9 +18,13 @@
 //        (value descending, id ascending) for the nucleus walk, min-p drops those below
 //        min_p times the largest probability, and one thread takes the final softmax and the
 //        walk over the kept ids left to right in ascending id order;
-//      - with top-p = 1: min-p and the final softmax over the whole vocabulary, each thread
-//        summing a contiguous range of ids left to right and the ranges combined in order;
-//        the walk finds the first id whose cumulative probability exceeds u;
+//      - with top-p = 1: top-k marks the dropped ids of the scratch row -inf, the row becomes
+//        e = exp(lt - max) (min-p zeroes the dropped ones; an id whose e underflows to 0 is
+//        never drawn); sums over
+//        the whole vocabulary reduce each group of 64 consecutive ids by a fixed lane tree and
+//        add the groups left to right (one lane per span of groups, then the spans); the walk
+//        finds the group where the cumulative probability passes u from those partial sums,
+//        then steps id by id;
 //   4. u takes two outputs of the sequence's PCG32 stream (O'Neill's XSH-RR generator:
 //      state' = state * 6364136223846793005 + inc, output = the 32-bit rotation of
 //      (old ^ old >> 18) >> 27 by old >> 59): u = ((a >> 5) * 2^26 + (b >> 6)) * 2^-53;
@@ -31,7 +36,10 @@ namespace dec {
 namespace {
 
 constexpr int kST = 1024;                     // threads per sequence
+constexpr int kWaves = kST / 64;
 constexpr int kNuc = DEC_SAMPLE_MAX_NUCLEUS;  // candidates the nucleus step orders
+constexpr int kMaxGroups = 4096;              // groups of 64 ids: vocabularies up to 262,144
+constexpr int kU = 8;                         // ids per thread whose loads are issued together
 
 // order-preserving key: a larger double has a larger key (finite values and infinities)
 __device__ __forceinline__ uint64_t okey(double v) {
@@ -89,8 +97,8 @@ __device__ void block_maxarg(double& v, int& id, double* red, int* redi) {
 __global__ __launch_bounds__(kST) void sample_kernel(const float* __restrict__ logits, int64_t ld, int V,
                                                      const SampleSeq* __restrict__ seqs,
                                                      const int32_t* __restrict__ ids, uint32_t* __restrict__ cnt_all,
-                                                     uint64_t* __restrict__ rng, int32_t* __restrict__ next,
-                                                     double* __restrict__ logprob) {
+                                                     double* __restrict__ vals_all, uint64_t* __restrict__ rng,
+                                                     int32_t* __restrict__ next, double* __restrict__ logprob) {
 #pragma clang fp contract(off)
   __shared__ double red[kST];
   __shared__ int redi[kST];
@@ -100,15 +108,23 @@ __global__ __launch_bounds__(kST) void sample_kernel(const float* __restrict__ l
   __shared__ uint64_t cand_key[kNuc];
   __shared__ int ord[kNuc];
   __shared__ uint8_t keepc[kNuc];
+  __shared__ double gp[kMaxGroups];  // per group of 64 ids: a partial sum
+  __shared__ int gc[kMaxGroups];     // per group: a count, then its exclusive prefix
+  __shared__ double sp[kWaves];      // per span of groups: a partial sum
   __shared__ int s_i[4];
   __shared__ double s_d[2];
-  const int s = blockIdx.x, t = threadIdx.x;
+  const int s = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const SampleSeq q = seqs[s];
   const dec_sampling P = q.p;
   const float* lg = logits + (int64_t)s * ld;
   uint32_t* cnt = cnt_all + (int64_t)s * V;
+  double* val = vals_all + (int64_t)s * V;
+  const int NG = (V + 63) / 64;                 // groups of 64 consecutive ids
+  const int span = (NG + kWaves - 1) / kWaves;  // groups per span (one per wave)
+  // Thread t owns the ids v = t (mod kST): in batch i0 the ids i0 + u kST + t, u < kU, whose
+  // loads are all issued before any is used. Group g = v / 64 is then handled by one wave.
 
-  // 1. history marks
+  // 1. history marks, then the penalised values into the scratch row
   for (int i = t; i < q.h.prompt_len; i += kST) {
     const int v = ids[q.h.prompt_offset + i];
     if (v >= 0 && v < V) atomicOr(&cnt[v], 0x80000000u);
@@ -121,9 +137,8 @@ __global__ __launch_bounds__(kST) void sample_kernel(const float* __restrict__ l
     }
   }
   __syncthreads();
-  auto pen = [&](int v) -> double {
-    double l = (double)lg[v];
-    const uint32_t c = __hip_atomic_load(&cnt[v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  auto penal = [&](float x, uint32_t c) -> double {
+    double l = (double)x;
     if (c) {
       l = l > 0.0 ? l / P.repetition_penalty : l * P.repetition_penalty;
       const uint32_t n = c & 0x7fffffffu;
@@ -134,29 +149,123 @@ __global__ __launch_bounds__(kST) void sample_kernel(const float* __restrict__ l
     }
     return l;
   };
-
-  // 2. the largest value, its lowest id, and Z
+  // 2. the largest value (lowest id among equals), the values stored
   double mx = -__builtin_inf();
   int am = 0x7fffffff;
-  for (int v = t; v < V; v += kST) {
-    const double l = pen(v);
-    if (l > mx) {
-      mx = l;
-      am = v;
+  for (int i0 = 0; i0 < V; i0 += kST * kU) {
+    float x[kU];
+    uint32_t c[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int v = i0 + u * kST + t;
+      x[u] = v < V ? lg[v] : 0.f;
+      c[u] = v < V ? __hip_atomic_load(&cnt[v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int v = i0 + u * kST + t;
+      if (v < V) {
+        const double l = penal(x[u], c[u]);
+        val[v] = l;
+        if (l > mx) {
+          mx = l;
+          am = v;
+        }
+      }
     }
   }
-  block_maxarg(mx, am, red, redi);
-  // contiguous id range of this thread (sums and walks in ascending id order)
-  const int C = (V + kST - 1) / kST, r0 = min(V, t * C), r1 = min(V, r0 + C);
-  double zl = 0.0;
-  for (int v = r0; v < r1; ++v) zl += exp(pen(v) - mx);
-  const double Z = ordered_sum(zl, red, &s_d[0]);
+  block_maxarg(mx, am, red, redi);  // (its barriers also order the scratch row's stores)
+
+  // Sum of f(val[v], v) over the vocabulary in a fixed order: each group of 64 ids by a
+  // pairwise lane tree, the groups of a span left to right, the spans left to right.
+  auto vocab_sum = [&](auto f) -> double {
+    for (int g0 = 0; g0 < NG; g0 += kWaves * kU) {
+      double x[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int v = (g0 + u * kWaves) * 64 + t;
+        x[u] = v < V ? val[v] : 0.0;
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int g = g0 + u * kWaves + wave;
+        const int v = g * 64 + lane;
+        double y = v < V ? f(x[u], v) : 0.0;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) y += __shfl_xor(y, o, 64);
+        if (lane == 0 && g < NG) gp[g] = y;
+      }
+    }
+    __syncthreads();
+    if (lane == 0) {
+      double a = 0.0;
+      const int g1 = min(NG, (wave + 1) * span);
+#pragma unroll 8
+      for (int g = wave * span; g < g1; ++g) a += gp[g];
+      sp[wave] = a;
+    }
+    __syncthreads();
+    if (t == 0) {
+      double a = 0.0;
+      for (int w = 0; w < kWaves; ++w) a += sp[w];
+      s_d[0] = a;
+    }
+    __syncthreads();
+    const double r = s_d[0];
+    __syncthreads();
+    return r;
+  };
+  // arr[0 .. NG) := its exclusive prefix in group order (each thread scans 4 groups, then a
+  // doubling scan over the threads); returns the total
+  auto group_prefix = [&](int* arr) -> int {
+    int loc[4], sum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int g = t * 4 + j;
+      loc[j] = g < NG ? arr[g] : 0;
+      sum += loc[j];
+    }
+    redi[t] = sum;
+    __syncthreads();
+    for (int o = 1; o < kST; o <<= 1) {
+      const int add = t >= o ? redi[t - o] : 0;
+      __syncthreads();
+      redi[t] += add;
+      __syncthreads();
+    }
+    int a = redi[t] - sum;  // exclusive
+    const int total = redi[kST - 1];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int g = t * 4 + j;
+      if (g < NG) arr[g] = a;
+      a += loc[j];
+    }
+    __syncthreads();
+    return total;
+  };
+  const uint64_t lanes_below = lane ? (~0ull >> (64 - lane)) : 0ull;
+
+  const double Z = vocab_sum([&](double x, int) { return exp(x - mx); });
   int tok = am;
 
   const double T = P.temperature;
   if (T > 0.0) {
     const double mt = mx / T;  // the largest tempered value (division by T > 0 keeps the order)
-    auto lt = [&](int v) { return pen(v) / T; };
+    for (int i0 = 0; i0 < V; i0 += kST * kU) {
+      double x[kU];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int v = i0 + u * kST + t;
+        x[u] = v < V ? val[v] : 0.0;
+      }
+#pragma unroll
+      for (int u = 0; u < kU; ++u) {
+        const int v = i0 + u * kST + t;
+        if (v < V) val[v] = x[u] / T;
+      }
+    }
+    __syncthreads();
     const int k = P.top_k;
     const bool use_k = k > 0 && k < V;
     // 3a. top-k: the top `bits` bits of the cut key are pv; krem ids are still to be taken
@@ -169,9 +278,19 @@ __global__ __launch_bounds__(kST) void sample_kernel(const float* __restrict__ l
         const int shift = 56 - 8 * pass;
         if (t < 256) hist[t] = 0;
         __syncthreads();
-        for (int v = t; v < V; v += kST) {
-          const uint64_t key = okey(lt(v));
-          if (bits == 0 || (key >> (64 - bits)) == pv) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+        for (int i0 = 0; i0 < V; i0 += kST * kU) {
+          double x[kU];
+#pragma unroll
+          for (int u = 0; u < kU; ++u) {
+            const int v = i0 + u * kST + t;
+            x[u] = v < V ? val[v] : 0.0;
+          }
+#pragma unroll
+          for (int u = 0; u < kU; ++u) {
+            const int v = i0 + u * kST + t;
+            const uint64_t key = okey(x[u]);
+            if (v < V && (bits == 0 || (key >> (64 - bits)) == pv)) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+          }
         }
         __syncthreads();
         if (t == 0) {
@@ -198,62 +317,66 @@ __global__ __launch_bounds__(kST) void sample_kernel(const float* __restrict__ l
         ties = pass == 7;  // 64 bits and more equal keys than places: the lowest ids are taken
       }
     }
-    // rank of this thread's first equal key among all equal keys (ties only)
-    int eq_base = 0;
+    // equal keys at the cut: their ranks in id order (gc: equal keys before each group)
     if (ties) {
-      int n = 0;
-      for (int v = r0; v < r1; ++v) n += okey(lt(v)) == pv;
-      redi[t] = n;
-      __syncthreads();
-      if (t == 0) {
-        int a = 0;
-        for (int i = 0; i < kST; ++i) {
-          const int c = redi[i];
-          redi[i] = a;
-          a += c;
-        }
+      for (int g0 = 0; g0 < NG; g0 += kWaves) {
+        const int g = g0 + wave;
+        const int v = g * 64 + lane;
+        const uint64_t m = __ballot(v < V && okey(val[v]) == pv);
+        if (lane == 0 && g < NG) gc[g] = __popcll(m);
       }
       __syncthreads();
-      eq_base = redi[t];
-      __syncthreads();
+      group_prefix(gc);
     }
-    // kept by top-k: walks the thread's range in ascending id order (eq counts equal keys seen)
-    auto topk_in = [&](uint64_t key, int& eq) -> bool {
-      if (!use_k) return true;
-      const uint64_t top = key >> (64 - bits);
-      if (top > pv) return true;
-      if (top < pv) return false;
-      if (!ties) return true;
-      return eq_base + eq++ < krem;
+    // kept by top-k: value x of lane's id v in group g (called by whole waves: ranks of equal
+    // keys at the cut come from a ballot, after those of earlier groups)
+    auto kept_tk = [&](int g, int v, double x) -> bool {
+      bool in = false, eq = false;
+      if (v < V) {
+        if (!use_k) {
+          in = true;
+        } else {
+          const uint64_t top = okey(x) >> (64 - bits);
+          in = top > pv;
+          eq = top == pv;
+        }
+      }
+      if (ties) {
+        const uint64_t eqm = __ballot(eq);
+        if (eq) in = gc[g] + __popcll(eqm & lanes_below) < krem;
+      } else if (eq) {
+        in = true;
+      }
+      return in;
     };
 
     if (P.top_p < 1.0) {
-      // 3b. nucleus path: the k (<= kNuc) candidates in ascending id order
-      int n = 0, eq = 0;
-      for (int v = r0; v < r1; ++v) n += topk_in(okey(lt(v)), eq);
-      redi[t] = n;
-      __syncthreads();
-      if (t == 0) {
-        int a = 0;
-        for (int i = 0; i < kST; ++i) {
-          const int c = redi[i];
-          redi[i] = a;
-          a += c;
-        }
-        s_i[3] = a;
+      // 3b. nucleus path: the (<= kNuc) candidates in ascending id order (gp's storage holds
+      // the per-group counts and their prefix here)
+      int* cc = (int*)gp;
+      for (int g0 = 0; g0 < NG; g0 += kWaves) {
+        const int g = g0 + wave;
+        const int v = g * 64 + lane;
+        const bool in = kept_tk(g, v, v < V ? val[v] : 0.0);
+        const uint64_t m = __ballot(in);
+        if (lane == 0 && g < NG) cc[g] = __popcll(m);
       }
       __syncthreads();
-      int w = redi[t];
-      const int nc = s_i[3];
-      eq = 0;
-      for (int v = r0; v < r1; ++v) {
-        const double x = lt(v);
-        const uint64_t key = okey(x);
-        if (topk_in(key, eq) && w < kNuc) {
-          cand_id[w] = v;
-          cand_key[w] = key;
-          cand_e[w] = exp(x - mt);
-          ++w;
+      // exclusive prefix of cc (the ties ranks in gc stay as they are)
+      const int nc = group_prefix(cc);
+      for (int g0 = 0; g0 < NG; g0 += kWaves) {
+        const int g = g0 + wave;
+        const int v = g * 64 + lane;
+        const double x = v < V ? val[v] : 0.0;
+        const bool in = kept_tk(g, v, x);
+        const uint64_t m = __ballot(in);
+        if (in) {
+          const int w = cc[g] + __popcll(m & lanes_below);
+          if (w < kNuc) {
+            cand_id[w] = v;
+            cand_key[w] = okey(x);
+            cand_e[w] = exp(x - mt);
+          }
         }
       }
       ord[t] = t < nc ? t : -1;
@@ -282,6 +405,7 @@ __global__ __launch_bounds__(kST) void sample_kernel(const float* __restrict__ l
       if (t == 0) {
         const int m = min(nc, kNuc);
         double zk = 0.0;
+#pragma unroll 8
         for (int i = 0; i < m; ++i) zk += cand_e[i];
         double c = 0.0;
         for (int j = 0; j < m; ++j) {
@@ -296,6 +420,7 @@ __global__ __launch_bounds__(kST) void sample_kernel(const float* __restrict__ l
             if (keepc[i] && cand_e[i] / zk < P.min_p * qmax) keepc[i] = 0;
         }
         double zf = 0.0;
+#pragma unroll 8
         for (int i = 0; i < m; ++i)
           if (keepc[i]) zf += cand_e[i];
         uint64_t st = rng[2 * s];
@@ -317,91 +442,100 @@ __global__ __launch_bounds__(kST) void sample_kernel(const float* __restrict__ l
       tok = s_i[0];
       __syncthreads();
     } else {
-      // 3c. the whole vocabulary: min-p over the top-k kept ids, then softmax and walk
-      double zk = 1.0;
-      if (P.min_p > 0.0) {
-        double zl2 = 0.0;
-        int eq = 0;
-        for (int v = r0; v < r1; ++v) {
-          const double x = lt(v);
-          if (topk_in(okey(x), eq)) zl2 += exp(x - mt);
+      // 3c. the whole vocabulary: top-k, then the row becomes e = exp(lt - max) with 0 for the
+      // dropped ids; min-p; softmax and walk
+      for (int g0 = 0; g0 < NG; g0 += kWaves * kU) {
+        double x[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int v = (g0 + u * kWaves) * 64 + t;
+          x[u] = v < V ? val[v] : 0.0;
         }
-        zk = ordered_sum(zl2, red, &s_d[0]);
-      }
-      const double qmax = 1.0 / zk;  // the largest id's probability: exp(0) / zk
-      auto kept = [&](double x, double e, int& eq) {
-        if (!topk_in(okey(x), eq)) return false;
-        return !(P.min_p > 0.0) || e / zk >= P.min_p * qmax;
-      };
-      double zl3 = 0.0;
-      int eq = 0;
-      for (int v = r0; v < r1; ++v) {
-        const double x = lt(v), e = exp(x - mt);
-        if (kept(x, e, eq)) zl3 += e;
-      }
-      const double zf = ordered_sum(zl3, red, &s_d[0]);
-      // the thread's share of the cumulative probability, then the ranges' starting points
-      double pl = 0.0;
-      int last = -1;
-      eq = 0;
-      for (int v = r0; v < r1; ++v) {
-        const double x = lt(v), e = exp(x - mt);
-        if (kept(x, e, eq)) {
-          pl += e / zf;
-          last = v;
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int g = g0 + u * kWaves + wave;
+          const int v = g * 64 + lane;
+          const bool in = kept_tk(g, v, x[u]);
+          if (v < V) val[v] = in ? exp(x[u] - mt) : 0.0;
         }
       }
-      red[t] = pl;
-      redi[t] = last;
       __syncthreads();
+      if (P.min_p > 0.0) {
+        const double zk = vocab_sum([&](double x, int) { return x; });
+        const double qmax = 1.0 / zk;  // the largest id's probability: exp(0) / zk
+        for (int i0 = 0; i0 < V; i0 += kST * kU) {
+          double x[kU];
+#pragma unroll
+          for (int u = 0; u < kU; ++u) {
+            const int v = i0 + u * kST + t;
+            x[u] = v < V ? val[v] : 0.0;
+          }
+#pragma unroll
+          for (int u = 0; u < kU; ++u) {
+            const int v = i0 + u * kST + t;
+            if (v < V && !(x[u] / zk >= P.min_p * qmax)) val[v] = 0.0;
+          }
+        }
+        __syncthreads();
+      }
+      const double zf = vocab_sum([&](double x, int) { return x; });
+      // group partials of the probabilities (gp), span partials (sp), then the walk
+      vocab_sum([&](double x, int) { return x / zf; });
       if (t == 0) {
         uint64_t st = rng[2 * s];
         const uint64_t inc = rng[2 * s + 1];
         const uint32_t a = pcg32_next(st, inc), b = pcg32_next(st, inc);
         rng[2 * s] = st;
-        s_d[1] = ((double)(a >> 5) * 67108864.0 + (double)(b >> 6)) * (1.0 / 9007199254740992.0);
+        const double u = ((double)(a >> 5) * 67108864.0 + (double)(b >> 6)) * (1.0 / 9007199254740992.0);
+        // the span, then the group, where the cumulative probability passes u; then id by id
+        // from that group on (the id-level running sum decides)
         double acc = 0.0;
-        int lastk = am;
-        for (int i = 0; i < kST; ++i) {
-          const double c = red[i];
-          red[i] = acc;
-          acc += c;
-          if (redi[i] >= 0) lastk = redi[i];
+        int w = 0;
+        for (; w < kWaves - 1; ++w) {
+          if (u < acc + sp[w]) break;
+          acc += sp[w];
         }
-        s_i[0] = lastk;
-      }
-      __syncthreads();
-      const double u = s_d[1];
-      double c = red[t];
-      int found = 0x7fffffff;
-      eq = 0;
-      // (every range walks: its running sum from the range's start may round differently
-      // from the start of the next range; the lowest id found wins)
-      for (int v = r0; v < r1; ++v) {
-        const double x = lt(v), e = exp(x - mt);
-        if (kept(x, e, eq)) {
+        int g = w * span;
+        const int gend = min(NG, (w + 1) * span);
+        for (; g < gend - 1; ++g) {
+          if (u < acc + gp[g]) break;
+          acc += gp[g];
+        }
+        int pick = -1, last = -1;
+        double c = acc;
+        for (int v = max(0, g) * 64; v < V; ++v) {
+          const double e = val[v];
+          if (!(e > 0.0)) continue;
+          last = v;
           c += e / zf;
           if (u < c) {
-            found = v;
+            pick = v;
             break;
           }
         }
+        if (pick < 0) {  // rounding left u beyond the sum: the last id that can be drawn
+          if (last < 0)
+            for (int v = V - 1; v >= 0; --v)
+              if (val[v] > 0.0) {
+                last = v;
+                break;
+              }
+          pick = last >= 0 ? last : am;
+        }
+        s_i[0] = pick;
       }
-      const int lastk = s_i[0];
-      redi[t] = found;
       __syncthreads();
-      for (int sd = kST / 2; sd > 0; sd >>= 1) {
-        if (t < sd) redi[t] = min(redi[t], redi[t + sd]);
-        __syncthreads();
-      }
-      tok = redi[0] != 0x7fffffff ? redi[0] : lastk;
+      tok = s_i[0];
       __syncthreads();
     }
   }
 
   if (t == 0) {
     next[s] = tok;
-    if (logprob) logprob[s] = (pen(tok) - mx) - log(Z);
+    if (logprob) {
+      const uint32_t c = __hip_atomic_load(&cnt[tok], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      logprob[s] = (penal(lg[tok], c) - mx) - log(Z);
+    }
   }
   __syncthreads();
   // 5. leave the count table zero
@@ -416,11 +550,12 @@ __global__ __launch_bounds__(kST) void sample_kernel(const float* __restrict__ l
 }
 
 hipError_t launch_sample(const float* logits, int64_t ld, int n_seqs, int vocab, const SampleSeq* seqs,
-                         const int32_t* ids, uint32_t* counts, uint64_t* rng, int32_t* next, double* logprob,
-                         hipStream_t s) {
+                         const int32_t* ids, uint32_t* counts, double* vals, uint64_t* rng, int32_t* next,
+                         double* logprob, hipStream_t s) {
   if (n_seqs <= 0) return hipSuccess;
-  launch_kernel(sample_kernel, dim3(n_seqs), dim3(kST), 0u, s, logits, ld, vocab, seqs, ids, counts, rng, next,
-                logprob);
+  if (vocab > kMaxGroups * 64) return hipErrorInvalidValue;
+  launch_kernel(sample_kernel, dim3(n_seqs), dim3(kST), 0u, s, logits, ld, vocab, seqs, ids, counts, vals, rng,
+                next, logprob);
   return hipGetLastError();
 }
 
