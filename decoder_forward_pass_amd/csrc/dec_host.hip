@@ -141,7 +141,7 @@ size_t kv_bytes(const dec_config& c) {
 // ---- workspace layout ----------------------------------------------------------------------
 
 struct Ws {
-  size_t rope, meta, x, h, qkv, q, o, a, part, amax, ssq, xg, samp, counts, vals, total;
+  size_t rope, meta, x, h, qkv, q, o, a, part, amax, ssq, xg, samp, counts, total;
   size_t meta_ints;  // capacity of the metadata region in int32
   int chunk, nch_max, max_blocks_per_seq, max_tiles;
   int act_bytes, kv_el;
@@ -184,7 +184,6 @@ Ws ws_layout(const dec_config& c) {
   w.xg = take(S * d * 2);          // decode: bf16(residual * the next norm's gain)
   w.samp = take(S * sizeof(SampleSeq));           // sampling: per-sequence parameters and history
   w.counts = take(S * (size_t)c.vocab * 4);       // sampling: per-sequence count table (kept zero)
-  w.vals = take(S * (size_t)c.vocab * 8);         // sampling: per-sequence float64 values
   w.total = off;
   return w;
 }
@@ -843,8 +842,8 @@ int dec_sample(dec_ctx* ctx, void* stream, int32_t n_seqs, const float* logits, 
   SampleSeq* dseq = (SampleSeq*)(ctx->wsp + ctx->ws.samp);
   HIPCHECK(hipMemcpyAsync(dseq, ctx->samp_staging, (size_t)n_seqs * sizeof(SampleSeq), hipMemcpyHostToDevice, st));
   HIPCHECK(hipEventRecord(ctx->samp_ev, st));
-  LAUNCH(launch_sample(logits, ld, n_seqs, V, dseq, ids, (uint32_t*)(ctx->wsp + ctx->ws.counts),
-                       (double*)(ctx->wsp + ctx->ws.vals), rng, next, logprob, st));
+  LAUNCH(launch_sample(logits, ld, n_seqs, V, dseq, ids, (uint32_t*)(ctx->wsp + ctx->ws.counts), rng, next,
+                       logprob, st));
   return DEC_OK;
 }
 

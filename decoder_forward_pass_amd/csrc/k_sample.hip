@@ -1,12 +1,12 @@
 // Seeded sampling of one token per sequence ("Candle model runner", section 2.6 "The sampler
 // and PCG32"), in float64 on the device. One workgroup of 1024 threads per sequence:
 //
-//   1. the sequence's history marks its count table (bit 31: the id occurs in prompt or
-//      output; bits 0..30: its occurrences in the output), with integer atomics whose order
-//      does not matter; one pass writes every id's penalised value to the sequence's float64
-//      scratch row (repetition divides a positive value and multiplies any other; an id seen
-//      c > 0 times in the output loses frequency * c + presence, two separately rounded
-//      operations), and the later passes read that row;
+//   1. the sequence's history sets one bit per id in LDS (prompt or output) and counts its
+//      output occurrences in the sequence's count table (integer atomics: their order does not
+//      matter); every pass reads the float32 logits and recomputes an id's penalised value
+//      (repetition divides a positive value and multiplies any other; an id seen c > 0 times
+//      in the output loses frequency * c + presence, two separately rounded operations), the
+//      count table being read for the marked ids only;
 //   2. the largest penalised value (ties to the lowest id) and Z = sum exp(l - max): the
 //      logprob of an id is (l - max) - log Z, taken before the temperature;
 //   3. temperature 0 returns the largest; otherwise values are divided by T and
@@ -18,17 +18,16 @@
 //        (value descending, id ascending) for the nucleus walk, min-p drops those below
 //        min_p times the largest probability, and one thread takes the final softmax and the
 //        walk over the kept ids left to right in ascending id order;
-//      - with top-p = 1: top-k marks the dropped ids of the scratch row -inf, the row becomes
-//        e = exp(lt - max) (min-p zeroes the dropped ones; an id whose e underflows to 0 is
-//        never drawn); sums over
+//      - with top-p = 1: e = exp(lt - max) for the ids top-k and min-p keep, 0 for the others
+//        (an id whose e underflows to 0 is never drawn); sums over
 //        the whole vocabulary reduce each group of 64 consecutive ids by a fixed lane tree and
 //        add the groups left to right (one lane per span of groups, then the spans); the walk
 //        finds the group where the cumulative probability passes u from those partial sums,
-//        then steps id by id;
+//        then one wave steps id by id;
 //   4. u takes two outputs of the sequence's PCG32 stream (O'Neill's XSH-RR generator:
 //      state' = state * 6364136223846793005 + inc, output = the 32-bit rotation of
 //      (old ^ old >> 18) >> 27 by old >> 59): u = ((a >> 5) * 2^26 + (b >> 6)) * 2^-53;
-//   5. the history's entries of the count table are set back to zero.
+//   5. the output's entries of the count table are set back to zero.
 #include "kernels.h"
 
 namespace dec {
@@ -97,8 +96,8 @@ __device__ void block_maxarg(double& v, int& id, double* red, int* redi) {
 __global__ __launch_bounds__(kST) void sample_kernel(const float* __restrict__ logits, int64_t ld, int V,
                                                      const SampleSeq* __restrict__ seqs,
                                                      const int32_t* __restrict__ ids, uint32_t* __restrict__ cnt_all,
-                                                     double* __restrict__ vals_all, uint64_t* __restrict__ rng,
-                                                     int32_t* __restrict__ next, double* __restrict__ logprob) {
+                                                     uint64_t* __restrict__ rng, int32_t* __restrict__ next,
+                                                     double* __restrict__ logprob) {
 #pragma clang fp contract(off)
   __shared__ double red[kST];
   __shared__ int redi[kST];
@@ -108,9 +107,10 @@ __global__ __launch_bounds__(kST) void sample_kernel(const float* __restrict__ l
   __shared__ uint64_t cand_key[kNuc];
   __shared__ int ord[kNuc];
   __shared__ uint8_t keepc[kNuc];
-  __shared__ double gp[kMaxGroups];  // per group of 64 ids: a partial sum
-  __shared__ int gc[kMaxGroups];     // per group: a count, then its exclusive prefix
-  __shared__ double sp[kWaves];      // per span of groups: a partial sum
+  __shared__ double gp[kMaxGroups];           // per group of 64 ids: a partial sum
+  __shared__ int gc[kMaxGroups];              // per group: a count, then its exclusive prefix
+  __shared__ uint32_t hbits[kMaxGroups * 2];  // one bit per id: in the prompt or the output
+  __shared__ double sp[kWaves];               // per span of groups: a partial sum
   __shared__ int s_i[4];
   __shared__ double s_d[2];
   const int s = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -118,30 +118,32 @@ __global__ __launch_bounds__(kST) void sample_kernel(const float* __restrict__ l
   const dec_sampling P = q.p;
   const float* lg = logits + (int64_t)s * ld;
   uint32_t* cnt = cnt_all + (int64_t)s * V;
-  double* val = vals_all + (int64_t)s * V;
   const int NG = (V + 63) / 64;                 // groups of 64 consecutive ids
   const int span = (NG + kWaves - 1) / kWaves;  // groups per span (one per wave)
   // Thread t owns the ids v = t (mod kST): in batch i0 the ids i0 + u kST + t, u < kU, whose
-  // loads are all issued before any is used. Group g = v / 64 is then handled by one wave.
+  // loads are all issued before any is used; group g = v / 64 is handled by one wave.
 
-  // 1. history marks, then the penalised values into the scratch row
+  // 1. history: its ids' bits, and the output occurrences in the count table
+  for (int i = t; i < NG * 2; i += kST) hbits[i] = 0;
+  __syncthreads();
   for (int i = t; i < q.h.prompt_len; i += kST) {
     const int v = ids[q.h.prompt_offset + i];
-    if (v >= 0 && v < V) atomicOr(&cnt[v], 0x80000000u);
+    if (v >= 0 && v < V) atomicOr(&hbits[v >> 5], 1u << (v & 31));
   }
   for (int i = t; i < q.h.output_len; i += kST) {
     const int v = ids[q.h.output_offset + i];
     if (v >= 0 && v < V) {
+      atomicOr(&hbits[v >> 5], 1u << (v & 31));
       atomicAdd(&cnt[v], 1u);
-      atomicOr(&cnt[v], 0x80000000u);
     }
   }
   __syncthreads();
-  auto penal = [&](float x, uint32_t c) -> double {
+  // the penalised value of id v with logit x (history ids only read the count table)
+  auto pen = [&](float x, int v) -> double {
     double l = (double)x;
-    if (c) {
+    if ((hbits[v >> 5] >> (v & 31)) & 1u) {
       l = l > 0.0 ? l / P.repetition_penalty : l * P.repetition_penalty;
-      const uint32_t n = c & 0x7fffffffu;
+      const uint32_t n = __hip_atomic_load(&cnt[v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (n) {
         const double f = P.frequency_penalty * (double)n;
         l -= f + P.presence_penalty;
@@ -149,24 +151,21 @@ __global__ __launch_bounds__(kST) void sample_kernel(const float* __restrict__ l
     }
     return l;
   };
-  // 2. the largest value (lowest id among equals), the values stored
+  // 2. the largest value (lowest id among equals)
   double mx = -__builtin_inf();
   int am = 0x7fffffff;
   for (int i0 = 0; i0 < V; i0 += kST * kU) {
     float x[kU];
-    uint32_t c[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int v = i0 + u * kST + t;
       x[u] = v < V ? lg[v] : 0.f;
-      c[u] = v < V ? __hip_atomic_load(&cnt[v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
       const int v = i0 + u * kST + t;
       if (v < V) {
-        const double l = penal(x[u], c[u]);
-        val[v] = l;
+        const double l = pen(x[u], v);
         if (l > mx) {
           mx = l;
           am = v;
@@ -174,23 +173,24 @@ __global__ __launch_bounds__(kST) void sample_kernel(const float* __restrict__ l
       }
     }
   }
-  block_maxarg(mx, am, red, redi);  // (its barriers also order the scratch row's stores)
+  block_maxarg(mx, am, red, redi);
 
-  // Sum of f(val[v], v) over the vocabulary in a fixed order: each group of 64 ids by a
-  // pairwise lane tree, the groups of a span left to right, the spans left to right.
+  // Sum of f(x, v) (x: logit of id v; f is called by every lane, v >= V included, and must
+  // give 0 there) over the vocabulary in a fixed order: each group of 64 ids by a pairwise
+  // lane tree, the groups of a span left to right, the spans left to right.
   auto vocab_sum = [&](auto f) -> double {
     for (int g0 = 0; g0 < NG; g0 += kWaves * kU) {
-      double x[kU];
+      float x[kU];
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const int v = (g0 + u * kWaves) * 64 + t;
-        x[u] = v < V ? val[v] : 0.0;
+        x[u] = v < V ? lg[v] : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < kU; ++u) {
         const int g = g0 + u * kWaves + wave;
         const int v = g * 64 + lane;
-        double y = v < V ? f(x[u], v) : 0.0;
+        double y = f(x[u], v);
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) y += __shfl_xor(y, o, 64);
         if (lane == 0 && g < NG) gp[g] = y;
@@ -246,26 +246,13 @@ __global__ __launch_bounds__(kST) void sample_kernel(const float* __restrict__ l
   };
   const uint64_t lanes_below = lane ? (~0ull >> (64 - lane)) : 0ull;
 
-  const double Z = vocab_sum([&](double x, int) { return exp(x - mx); });
+  const double Z = vocab_sum([&](float x, int v) { return v < V ? exp(pen(x, v) - mx) : 0.0; });
   int tok = am;
 
   const double T = P.temperature;
   if (T > 0.0) {
     const double mt = mx / T;  // the largest tempered value (division by T > 0 keeps the order)
-    for (int i0 = 0; i0 < V; i0 += kST * kU) {
-      double x[kU];
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int v = i0 + u * kST + t;
-        x[u] = v < V ? val[v] : 0.0;
-      }
-#pragma unroll
-      for (int u = 0; u < kU; ++u) {
-        const int v = i0 + u * kST + t;
-        if (v < V) val[v] = x[u] / T;
-      }
-    }
-    __syncthreads();
+    auto lt = [&](float x, int v) { return pen(x, v) / T; };
     const int k = P.top_k;
     const bool use_k = k > 0 && k < V;
     // 3a. top-k: the top `bits` bits of the cut key are pv; krem ids are still to be taken
@@ -279,17 +266,19 @@ __global__ __launch_bounds__(kST) void sample_kernel(const float* __restrict__ l
         if (t < 256) hist[t] = 0;
         __syncthreads();
         for (int i0 = 0; i0 < V; i0 += kST * kU) {
-          double x[kU];
+          float x[kU];
 #pragma unroll
           for (int u = 0; u < kU; ++u) {
             const int v = i0 + u * kST + t;
-            x[u] = v < V ? val[v] : 0.0;
+            x[u] = v < V ? lg[v] : 0.f;
           }
 #pragma unroll
           for (int u = 0; u < kU; ++u) {
             const int v = i0 + u * kST + t;
-            const uint64_t key = okey(x[u]);
-            if (v < V && (bits == 0 || (key >> (64 - bits)) == pv)) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+            if (v < V) {
+              const uint64_t key = okey(lt(x[u], v));
+              if (bits == 0 || (key >> (64 - bits)) == pv) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+            }
           }
         }
         __syncthreads();
@@ -322,21 +311,21 @@ __global__ __launch_bounds__(kST) void sample_kernel(const float* __restrict__ l
       for (int g0 = 0; g0 < NG; g0 += kWaves) {
         const int g = g0 + wave;
         const int v = g * 64 + lane;
-        const uint64_t m = __ballot(v < V && okey(val[v]) == pv);
+        const uint64_t m = __ballot(v < V && okey(lt(lg[v], v)) == pv);
         if (lane == 0 && g < NG) gc[g] = __popcll(m);
       }
       __syncthreads();
       group_prefix(gc);
     }
-    // kept by top-k: value x of lane's id v in group g (called by whole waves: ranks of equal
-    // keys at the cut come from a ballot, after those of earlier groups)
-    auto kept_tk = [&](int g, int v, double x) -> bool {
+    // kept by top-k: tempered value y of lane's id v in group g (called by whole waves: ranks
+    // of equal keys at the cut come from a ballot, after those of earlier groups)
+    auto kept_tk = [&](int g, int v, double y) -> bool {
       bool in = false, eq = false;
       if (v < V) {
         if (!use_k) {
           in = true;
         } else {
-          const uint64_t top = okey(x) >> (64 - bits);
+          const uint64_t top = okey(y) >> (64 - bits);
           in = top > pv;
           eq = top == pv;
         }
@@ -357,25 +346,24 @@ __global__ __launch_bounds__(kST) void sample_kernel(const float* __restrict__ l
       for (int g0 = 0; g0 < NG; g0 += kWaves) {
         const int g = g0 + wave;
         const int v = g * 64 + lane;
-        const bool in = kept_tk(g, v, v < V ? val[v] : 0.0);
+        const bool in = kept_tk(g, v, v < V ? lt(lg[v], v) : 0.0);
         const uint64_t m = __ballot(in);
         if (lane == 0 && g < NG) cc[g] = __popcll(m);
       }
       __syncthreads();
-      // exclusive prefix of cc (the ties ranks in gc stay as they are)
-      const int nc = group_prefix(cc);
+      const int nc = group_prefix(cc);  // (the ties ranks in gc stay as they are)
       for (int g0 = 0; g0 < NG; g0 += kWaves) {
         const int g = g0 + wave;
         const int v = g * 64 + lane;
-        const double x = v < V ? val[v] : 0.0;
-        const bool in = kept_tk(g, v, x);
+        const double y = v < V ? lt(lg[v], v) : 0.0;
+        const bool in = kept_tk(g, v, y);
         const uint64_t m = __ballot(in);
         if (in) {
           const int w = cc[g] + __popcll(m & lanes_below);
           if (w < kNuc) {
             cand_id[w] = v;
-            cand_key[w] = okey(x);
-            cand_e[w] = exp(x - mt);
+            cand_key[w] = okey(y);
+            cand_e[w] = exp(y - mt);
           }
         }
       }
@@ -442,53 +430,33 @@ __global__ __launch_bounds__(kST) void sample_kernel(const float* __restrict__ l
       tok = s_i[0];
       __syncthreads();
     } else {
-      // 3c. the whole vocabulary: top-k, then the row becomes e = exp(lt - max) with 0 for the
-      // dropped ids; min-p; softmax and walk
-      for (int g0 = 0; g0 < NG; g0 += kWaves * kU) {
-        double x[kU];
-#pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          const int v = (g0 + u * kWaves) * 64 + t;
-          x[u] = v < V ? val[v] : 0.0;
-        }
-#pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          const int g = g0 + u * kWaves + wave;
-          const int v = g * 64 + lane;
-          const bool in = kept_tk(g, v, x[u]);
-          if (v < V) val[v] = in ? exp(x[u] - mt) : 0.0;
-        }
-      }
-      __syncthreads();
+      // 3c. the whole vocabulary: e = exp(lt - max) for the ids top-k keeps, 0 otherwise; min-p
+      // over those; softmax and walk
+      auto e_tk = [&](float x, int v, int g) -> double {
+        const double y = v < V ? lt(x, v) : 0.0;
+        const bool in = kept_tk(g, v, y);
+        return in ? exp(y - mt) : 0.0;
+      };
+      double zk = 1.0, qmax = 0.0;
       if (P.min_p > 0.0) {
-        const double zk = vocab_sum([&](double x, int) { return x; });
-        const double qmax = 1.0 / zk;  // the largest id's probability: exp(0) / zk
-        for (int i0 = 0; i0 < V; i0 += kST * kU) {
-          double x[kU];
-#pragma unroll
-          for (int u = 0; u < kU; ++u) {
-            const int v = i0 + u * kST + t;
-            x[u] = v < V ? val[v] : 0.0;
-          }
-#pragma unroll
-          for (int u = 0; u < kU; ++u) {
-            const int v = i0 + u * kST + t;
-            if (v < V && !(x[u] / zk >= P.min_p * qmax)) val[v] = 0.0;
-          }
-        }
-        __syncthreads();
+        zk = vocab_sum([&](float x, int v) { return e_tk(x, v, v >> 6); });
+        qmax = 1.0 / zk;  // the largest id's probability: exp(0) / zk
       }
-      const double zf = vocab_sum([&](double x, int) { return x; });
-      // group partials of the probabilities (gp), span partials (sp), then the walk
-      vocab_sum([&](double x, int) { return x / zf; });
+      auto e_of = [&](float x, int v) -> double {
+        const double e = e_tk(x, v, v >> 6);
+        if (P.min_p > 0.0 && !(e / zk >= P.min_p * qmax)) return 0.0;
+        return e;
+      };
+      const double zf = vocab_sum(e_of);
+      // group partials of the probabilities (gp), span partials (sp)
+      vocab_sum([&](float x, int v) { return e_of(x, v) / zf; });
       if (t == 0) {
         uint64_t st = rng[2 * s];
         const uint64_t inc = rng[2 * s + 1];
         const uint32_t a = pcg32_next(st, inc), b = pcg32_next(st, inc);
         rng[2 * s] = st;
         const double u = ((double)(a >> 5) * 67108864.0 + (double)(b >> 6)) * (1.0 / 9007199254740992.0);
-        // the span, then the group, where the cumulative probability passes u; then id by id
-        // from that group on (the id-level running sum decides)
+        // the span, then the group, where the cumulative probability passes u
         double acc = 0.0;
         int w = 0;
         for (; w < kWaves - 1; ++w) {
@@ -501,48 +469,51 @@ __global__ __launch_bounds__(kST) void sample_kernel(const float* __restrict__ l
           if (u < acc + gp[g]) break;
           acc += gp[g];
         }
-        int pick = -1, last = -1;
-        double c = acc;
-        for (int v = max(0, g) * 64; v < V; ++v) {
-          const double e = val[v];
-          if (!(e > 0.0)) continue;
-          last = v;
-          c += e / zf;
-          if (u < c) {
-            pick = v;
-            break;
-          }
-        }
-        if (pick < 0) {  // rounding left u beyond the sum: the last id that can be drawn
-          if (last < 0)
-            for (int v = V - 1; v >= 0; --v)
-              if (val[v] > 0.0) {
-                last = v;
-                break;
-              }
-          pick = last >= 0 ? last : am;
-        }
-        s_i[0] = pick;
+        s_d[1] = u;
+        s_d[0] = acc;
+        s_i[0] = max(0, g);
       }
       __syncthreads();
-      tok = s_i[0];
+      // wave 0 walks id by id from that group on (the id-level running sum decides): each
+      // group's probabilities go to LDS and lane 0 adds them in id order
+      if (wave == 0) {
+        const double u = s_d[1];
+        double c = s_d[0];
+        int pick = -1, last = -1;
+        for (int g = s_i[0]; g < NG && pick < 0; ++g) {
+          const int v = g * 64 + lane;
+          const double pr = e_of(v < V ? lg[v] : 0.f, v) / zf;
+          red[lane] = pr;
+          if (lane == 0) {
+            for (int j = 0; j < 64 && g * 64 + j < V; ++j) {
+              if (!(red[j] > 0.0)) continue;
+              last = g * 64 + j;
+              c += red[j];
+              if (u < c) {
+                pick = last;
+                break;
+              }
+            }
+          }
+          pick = __shfl(pick, 0, 64);
+          last = __shfl(last, 0, 64);
+          c = __shfl(c, 0, 64);
+        }
+        // (rounding left u beyond the sum: the last id that can be drawn; else the largest)
+        if (lane == 0) s_i[1] = pick >= 0 ? pick : (last >= 0 ? last : am);
+      }
+      __syncthreads();
+      tok = s_i[1];
       __syncthreads();
     }
   }
 
   if (t == 0) {
     next[s] = tok;
-    if (logprob) {
-      const uint32_t c = __hip_atomic_load(&cnt[tok], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      logprob[s] = (penal(lg[tok], c) - mx) - log(Z);
-    }
+    if (logprob) logprob[s] = (pen(lg[tok], tok) - mx) - log(Z);
   }
   __syncthreads();
   // 5. leave the count table zero
-  for (int i = t; i < q.h.prompt_len; i += kST) {
-    const int v = ids[q.h.prompt_offset + i];
-    if (v >= 0 && v < V) __hip_atomic_store(&cnt[v], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
   for (int i = t; i < q.h.output_len; i += kST) {
     const int v = ids[q.h.output_offset + i];
     if (v >= 0 && v < V) __hip_atomic_store(&cnt[v], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -550,12 +521,12 @@ __global__ __launch_bounds__(kST) void sample_kernel(const float* __restrict__ l
 }
 
 hipError_t launch_sample(const float* logits, int64_t ld, int n_seqs, int vocab, const SampleSeq* seqs,
-                         const int32_t* ids, uint32_t* counts, double* vals, uint64_t* rng, int32_t* next,
-                         double* logprob, hipStream_t s) {
+                         const int32_t* ids, uint32_t* counts, uint64_t* rng, int32_t* next, double* logprob,
+                         hipStream_t s) {
   if (n_seqs <= 0) return hipSuccess;
   if (vocab > kMaxGroups * 64) return hipErrorInvalidValue;
-  launch_kernel(sample_kernel, dim3(n_seqs), dim3(kST), 0u, s, logits, ld, vocab, seqs, ids, counts, vals, rng,
-                next, logprob);
+  launch_kernel(sample_kernel, dim3(n_seqs), dim3(kST), 0u, s, logits, ld, vocab, seqs, ids, counts, rng, next,
+                logprob);
   return hipGetLastError();
 }
 

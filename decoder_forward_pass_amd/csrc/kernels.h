@@ -160,10 +160,10 @@ struct SampleSeq {
   dec_sampling p;
   dec_history h;
 };
-// vals: [n_seqs][vocab] float64 scratch; vocab <= 262,144
+// vocab <= 262,144
 hipError_t launch_sample(const float* logits, int64_t ld, int n_seqs, int vocab, const SampleSeq* seqs,
-                         const int32_t* ids, uint32_t* counts, double* vals, uint64_t* rng, int32_t* next,
-                         double* logprob, hipStream_t s);
+                         const int32_t* ids, uint32_t* counts, uint64_t* rng, int32_t* next, double* logprob,
+                         hipStream_t s);
 
 // out[rows][cols] = widened / dequantised matrix (float32).
 hipError_t launch_dequant(int wdtype, const WMat& w, int rows, int cols, float* out, hipStream_t s);
