@@ -45,6 +45,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="q06b_bf16_b32_p1024_d256")
+    ap.add_argument("--no-sampler", action="store_true", help="skip the seeded-sampler timing after the run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--time-every", type=int, default=32,
                     help="time the attention launches of every N-th decode step (0: none)")
@@ -197,6 +198,41 @@ def measured_traffic(name):
         return None
 
 
+SAMPLER_PARAMS = dict(temperature=0.8, top_k=50, top_p=0.95, repetition_penalty=1.1)
+
+
+def time_sampler(s, logits, prompts, reps=10):
+    """dec_sample over the last decode step's logits (one row per sequence, its prompt as the
+    history) with SAMPLER_PARAMS: mean microseconds per call, outside the timed region."""
+    import torch
+    from decoder_forward_pass_amd import binding as B
+    S = logits.shape[0]
+    p = B.dec_sampling()
+    p.temperature, p.top_k, p.top_p = SAMPLER_PARAMS["temperature"], SAMPLER_PARAMS["top_k"], SAMPLER_PARAMS["top_p"]
+    p.min_p, p.repetition_penalty = 0.0, SAMPLER_PARAMS["repetition_penalty"]
+    hist = []
+    off = 0
+    for pr in prompts:
+        h = B.dec_history()
+        h.prompt_offset, h.prompt_len, h.output_offset, h.output_len = off, len(pr), off + len(pr), 0
+        off += len(pr)
+        hist.append(h)
+    ids = torch.tensor(np.concatenate(prompts), dtype=torch.int32, device="cuda")
+    rng = torch.tensor([list(B.dec_rng_stream(i)) for i in range(S)], dtype=torch.uint64, device="cuda")
+    for _ in range(2):
+        s.sample(logits, [p] * S, hist, ids, rng)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        s.sample(logits, [p] * S, hist, ids, rng)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    return {"kernel": "sample_kernel (seeded sampling, float64)", "rows": S, "vocab": int(logits.shape[1]),
+            "params": SAMPLER_PARAMS, "us_per_call": round(us, 1),
+            "bound": "fp64 VALU (exp) of one workgroup per row"}
+
+
 def cpu_baseline(wl, shape, weights, prompts, decode_steps=8):
     """The oracle as it is, on one sequence: its prefill, then a few greedy decode steps."""
     import oracle.model as om
@@ -307,6 +343,7 @@ def main():
     phases = [(a.elapsed_time(b), c.elapsed_time(d)) for (a, b), (c, d) in zip(pre, dec)]
     rows_ms, rows_n = B.dec_timing_read(s.ctx, K_ROWS)
     gu_ms, gu_n = B.dec_timing_read(s.ctx, K_GATEUP)
+    sampler = None if args.no_sampler else time_sampler(s, logits, prompts)
     s.close()
 
     tok_per_step = S * P + S * steps
@@ -366,6 +403,8 @@ def main():
         "frac": round(gu_tfs / MFMA_BF16_PEAK_TFS, 4), "launches": gu_n,
         "avg_launch_us": round(gu_avg_ms * 1e3, 2), "algorithmic_flops_per_launch": gu_prefill_flops,
     }
+    if sampler:
+        result["sampler"] = sampler
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, shape, weights, prompts)
     print(json.dumps(result), flush=True)
