@@ -85,8 +85,13 @@ DEC_SAMPLE_MAX_NUCLEUS = 1024
 
 EXPORTS = ["dec_check_config", "dec_weight_bytes", "dec_weight_count", "dec_weight_entry", "dec_kv_pool_bytes",
            "dec_workspace_bytes", "dec_init", "dec_free", "dec_last_error", "dec_prefill", "dec_decode_step",
-           "dec_check_step", "dec_debug_dequant", "dec_rng_stream", "dec_sample", "dec_timing_enable",
+           "dec_check_step", "dec_debug_dequant", "dec_rng_stream", "dec_sample", "dec_pool_create",
+           "dec_pool_destroy", "dec_pool_last_error", "dec_pool_alloc", "dec_pool_retain", "dec_pool_release",
+           "dec_pool_set_fill", "dec_pool_register", "dec_pool_lookup", "dec_pool_block_info", "dec_pool_counts",
+           "dec_prefix_key", "dec_kv_export_bytes", "dec_kv_export", "dec_kv_import", "dec_timing_enable",
            "dec_timing_read"]
+
+DEC_BLOCK_FREE, DEC_BLOCK_USED, DEC_BLOCK_CACHED = 0, 1, 2
 
 KERNEL_CLASSES = ["embed", "rmsnorm", "gemm_qkv", "qk_rope_kv", "attn_prefill", "attn_rows", "attn_combine",
                   "gemm_o", "gemm_gateup", "gemm_down", "gemm_lmhead", "argmax"]
@@ -116,6 +121,21 @@ def _load():
         "dec_rng_stream": (None, [ctypes.c_uint64, ctypes.c_uint64, P(ctypes.c_uint64)]),
         "dec_sample": (ctypes.c_int, [VP, VP, I32, VP, ctypes.c_int64, P(dec_sampling), P(dec_history), VP,
                                       ctypes.c_int64, VP, VP, VP]),
+        "dec_pool_create": (ctypes.c_int, [I32, I32, I32, P(VP)]),
+        "dec_pool_destroy": (None, [VP]),
+        "dec_pool_last_error": (ctypes.c_char_p, [VP]),
+        "dec_pool_alloc": (ctypes.c_int, [VP, I32, i32p]),
+        "dec_pool_retain": (ctypes.c_int, [VP, I32]),
+        "dec_pool_release": (ctypes.c_int, [VP, I32]),
+        "dec_pool_set_fill": (ctypes.c_int, [VP, I32, I32]),
+        "dec_pool_register": (ctypes.c_int, [VP, I32, ctypes.c_uint64, i32p]),
+        "dec_pool_lookup": (ctypes.c_int, [VP, ctypes.c_uint64, i32p]),
+        "dec_pool_block_info": (ctypes.c_int, [VP, I32, i32p, i32p, i32p]),
+        "dec_pool_counts": (None, [VP, i32p, i32p, i32p]),
+        "dec_prefix_key": (ctypes.c_uint64, [ctypes.c_uint64, i32p, I32]),
+        "dec_kv_export_bytes": (SZ, [VP, I32]),
+        "dec_kv_export": (ctypes.c_int, [VP, VP, i32p, i32p, I32, VP, SZ]),
+        "dec_kv_import": (ctypes.c_int, [VP, VP, VP, SZ, i32p, I32, i32p]),
         "dec_timing_enable": (ctypes.c_int, [VP, ctypes.c_uint32]),
         "dec_timing_read": (ctypes.c_int, [VP, ctypes.c_int, P(ctypes.c_double), P(ctypes.c_int64)]),
     }
@@ -248,6 +268,84 @@ def dec_sample(ctx: int, stream: int, logits: int, ld: int, params, history, ids
     ha = (dec_history * n)(*history)
     _check(_lib.dec_sample(ctx, stream or None, n, logits, ld, pa, ha, ids or None, n_ids, rng, next_ids,
                            logprob or None), ctx)
+
+
+class BlockPool:
+    """The library's KV block manager (dec_pool_*): one method per C call, errors as DecError."""
+
+    def __init__(self, n_blocks: int, block_tokens: int, prefix_cache: bool = True):
+        h = ctypes.c_void_p()
+        rc = _lib.dec_pool_create(n_blocks, block_tokens, int(prefix_cache), ctypes.byref(h))
+        if rc != DEC_OK:
+            raise DecError(rc, "dec_pool_create refused the configuration")
+        self.h = h.value
+
+    def _check(self, rc):
+        if rc != DEC_OK:
+            msg = _lib.dec_pool_last_error(self.h)
+            raise DecError(rc, msg.decode() if msg else "")
+
+    def close(self):
+        if self.h:
+            _lib.dec_pool_destroy(self.h)
+            self.h = None
+
+    def alloc(self, n: int) -> list:
+        ids = (ctypes.c_int32 * max(n, 1))()
+        self._check(_lib.dec_pool_alloc(self.h, n, ids))
+        return list(ids[:n])
+
+    def retain(self, i: int):
+        self._check(_lib.dec_pool_retain(self.h, i))
+
+    def release(self, i: int):
+        self._check(_lib.dec_pool_release(self.h, i))
+
+    def set_fill(self, i: int, n: int):
+        self._check(_lib.dec_pool_set_fill(self.h, i, n))
+
+    def register(self, i: int, key: int) -> int:
+        c = ctypes.c_int32(-1)
+        self._check(_lib.dec_pool_register(self.h, i, key, ctypes.byref(c)))
+        return c.value
+
+    def lookup(self, key: int) -> int:
+        c = ctypes.c_int32(-1)
+        self._check(_lib.dec_pool_lookup(self.h, key, ctypes.byref(c)))
+        return c.value
+
+    def info(self, i: int):
+        st, ref, fill = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        self._check(_lib.dec_pool_block_info(self.h, i, ctypes.byref(st), ctypes.byref(ref), ctypes.byref(fill)))
+        return st.value, ref.value, fill.value
+
+    def counts(self):
+        f, u, c = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _lib.dec_pool_counts(self.h, ctypes.byref(f), ctypes.byref(u), ctypes.byref(c))
+        return f.value, u.value, c.value
+
+
+def dec_prefix_key(parent: int, tokens) -> int:
+    arr, p = _i32(tokens)
+    return int(_lib.dec_prefix_key(parent & (2 ** 64 - 1), p, len(arr)))
+
+
+def dec_kv_export(ctx: int, stream: int, ids, fills) -> bytes:
+    ia, ip = _i32(ids)
+    fa, fp = _i32(fills)
+    n = len(ia)
+    size = _lib.dec_kv_export_bytes(ctx, n)
+    buf = ctypes.create_string_buffer(size)
+    _check(_lib.dec_kv_export(ctx, stream or None, ip, fp, n, buf, size), ctx)
+    return buf.raw
+
+
+def dec_kv_import(ctx: int, stream: int, data: bytes, ids):
+    ia, ip = _i32(ids)
+    n = len(ia)
+    fills = (ctypes.c_int32 * n)()
+    _check(_lib.dec_kv_import(ctx, stream or None, data, len(data), ip, n, fills), ctx)
+    return list(fills)
 
 
 def dec_timing_enable(ctx: int, class_mask: int) -> None:

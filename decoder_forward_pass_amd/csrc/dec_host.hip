@@ -847,6 +847,93 @@ int dec_sample(dec_ctx* ctx, void* stream, int32_t n_seqs, const float* logits, 
   return DEC_OK;
 }
 
+// ---- export / import of blocks' K/V data ---------------------------------------------------
+// Envelope: a header (magic "DECKVB01", n_layers, n_kv_heads, block_tokens, head_dim, kv_dtype,
+// n blocks as int32), the n fills (int32), then per block and per layer its K slab and its V
+// slab ([H_kv][B][D] of the KV dtype each).
+
+namespace {
+struct KvEnvHeader {
+  char magic[8];
+  int32_t n_layers, n_kv_heads, block_tokens, head_dim, kv_dtype, n;
+};
+size_t kv_slab_bytes(const dec_config& c) {
+  return (size_t)c.n_kv_heads * c.block_tokens * c.head_dim * (c.kv_dtype == DEC_F16 ? 2 : 4);
+}
+}  // namespace
+
+size_t dec_kv_export_bytes(const dec_ctx* ctx, int32_t n) {
+  if (!ctx || n < 0) return 0;
+  return sizeof(KvEnvHeader) + (size_t)n * 4 + (size_t)n * ctx->cfg.n_layers * 2 * kv_slab_bytes(ctx->cfg);
+}
+
+int dec_kv_export(dec_ctx* ctx, void* stream, const int32_t* ids, const int32_t* fills, int32_t n, void* buf,
+                  size_t buf_bytes) {
+  if (!ctx) return fail(&g_err, DEC_E_ARG, "ctx is NULL");
+  const dec_config& c = ctx->cfg;
+  if (n < 1 || !ids || !fills || !buf) return fail(&ctx->err, DEC_E_ARG, "export: NULL argument or n < 1");
+  if (buf_bytes < dec_kv_export_bytes(ctx, n)) return fail(&ctx->err, DEC_E_CAPACITY, "export: buffer too small");
+  for (int32_t i = 0; i < n; ++i) {
+    if (ids[i] < 0 || ids[i] >= c.n_blocks) return fail(&ctx->err, DEC_E_BLOCK, "export: block id %d outside the pool", ids[i]);
+    if (fills[i] < 0 || fills[i] > c.block_tokens) return fail(&ctx->err, DEC_E_ARG, "export: fill outside [0, block_tokens]");
+  }
+  KvEnvHeader h{};
+  std::memcpy(h.magic, "DECKVB01", 8);
+  h.n_layers = c.n_layers;
+  h.n_kv_heads = c.n_kv_heads;
+  h.block_tokens = c.block_tokens;
+  h.head_dim = c.head_dim;
+  h.kv_dtype = c.kv_dtype;
+  h.n = n;
+  uint8_t* out = (uint8_t*)buf;
+  std::memcpy(out, &h, sizeof h);
+  std::memcpy(out + sizeof h, fills, (size_t)n * 4);
+  uint8_t* dst = out + sizeof h + (size_t)n * 4;
+  const size_t sb = kv_slab_bytes(c);
+  hipStream_t st = (hipStream_t)stream;
+  for (int32_t i = 0; i < n; ++i)
+    for (int l = 0; l < c.n_layers; ++l)
+      for (int kv = 0; kv < 2; ++kv) {
+        const uint8_t* src = (const uint8_t*)ctx->pool + (((size_t)l * 2 + kv) * c.n_blocks + ids[i]) * sb;
+        HIPCHECK(hipMemcpyAsync(dst, src, sb, hipMemcpyDeviceToHost, st));
+        dst += sb;
+      }
+  HIPCHECK(hipStreamSynchronize(st));
+  return DEC_OK;
+}
+
+int dec_kv_import(dec_ctx* ctx, void* stream, const void* buf, size_t buf_bytes, const int32_t* ids, int32_t n,
+                  int32_t* fills) {
+  if (!ctx) return fail(&g_err, DEC_E_ARG, "ctx is NULL");
+  const dec_config& c = ctx->cfg;
+  if (!buf || !ids || n < 1) return fail(&ctx->err, DEC_E_ARG, "import: NULL argument or n < 1");
+  KvEnvHeader h{};
+  if (buf_bytes < sizeof h) return fail(&ctx->err, DEC_E_ARG, "import: buffer shorter than its header");
+  std::memcpy(&h, buf, sizeof h);
+  if (std::memcmp(h.magic, "DECKVB01", 8) != 0) return fail(&ctx->err, DEC_E_ARG, "import: not a KV block envelope");
+  if (h.n_layers != c.n_layers || h.n_kv_heads != c.n_kv_heads || h.block_tokens != c.block_tokens ||
+      h.head_dim != c.head_dim || h.kv_dtype != c.kv_dtype)
+    return fail(&ctx->err, DEC_E_UNSUPPORTED, "import: the envelope's block format differs from this pool's");
+  if (h.n != n) return fail(&ctx->err, DEC_E_ARG, "import: the envelope holds %d blocks, %d destinations given", h.n, n);
+  if (buf_bytes != dec_kv_export_bytes(ctx, n)) return fail(&ctx->err, DEC_E_ARG, "import: buffer size does not match its header");
+  for (int32_t i = 0; i < n; ++i)
+    if (ids[i] < 0 || ids[i] >= c.n_blocks) return fail(&ctx->err, DEC_E_BLOCK, "import: block id %d outside the pool", ids[i]);
+  const uint8_t* in = (const uint8_t*)buf + sizeof h;
+  if (fills) std::memcpy(fills, in, (size_t)n * 4);
+  const uint8_t* srcp = in + (size_t)n * 4;
+  const size_t sb = kv_slab_bytes(c);
+  hipStream_t st = (hipStream_t)stream;
+  for (int32_t i = 0; i < n; ++i)
+    for (int l = 0; l < c.n_layers; ++l)
+      for (int kv = 0; kv < 2; ++kv) {
+        uint8_t* dst = (uint8_t*)ctx->pool + (((size_t)l * 2 + kv) * c.n_blocks + ids[i]) * sb;
+        HIPCHECK(hipMemcpyAsync(dst, srcp, sb, hipMemcpyHostToDevice, st));
+        srcp += sb;
+      }
+  HIPCHECK(hipStreamSynchronize(st));  // the host buffer may be reused once this returns
+  return DEC_OK;
+}
+
 int dec_debug_dequant(dec_ctx* ctx, void* stream, int index, float* out) {
   if (!ctx) return fail(&g_err, DEC_E_ARG, "ctx is NULL");
   if (!out) return fail(&ctx->err, DEC_E_ARG, "out is NULL");

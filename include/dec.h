@@ -323,6 +323,80 @@ int dec_sample(dec_ctx* ctx, void* stream, int32_t n_seqs, const float* logits, 
                const dec_sampling* params, const dec_history* history, const int32_t* ids,
                int64_t n_ids, uint64_t* rng, int32_t* next, double* logprob);
 
+/* ---- KV block manager (host only) ------------------------------------------------------ */
+
+/*
+ * A manager of the pool's block ids ("Candle model runner" section 2.2, KvPool:
+ * references per block, a prefix index, an LRU cache of released full blocks,
+ * and the KvPool interface of section 4; tests kv_pool_bounds_and_cache_
+ * lifecycle, kv_pool_evicts_the_oldest_cached_block, kv_pool_rejects_zero_
+ * capacity). It keeps host state only and is independent of any dec_ctx;
+ * callers pass the ids it hands out in their block tables. A block is FREE,
+ * USED (reference count >= 1) or CACHED (released while registered, with
+ * prefix caching on).
+ *   create:   n_blocks >= 1 (a pool without blocks is refused), block_tokens
+ *             >= 1; prefix_cache != 0 keeps released registered blocks
+ *   alloc:    n blocks, all or nothing: free blocks lowest id first, then the
+ *             oldest cached blocks (evicted from the index); each USED with
+ *             reference 1 and fill 0; DEC_E_CAPACITY when free + cached < n
+ *   retain / release: reference +1 / -1 of a USED block; at 0 a registered
+ *             block becomes CACHED (newest in the LRU) when prefix caching is
+ *             on, any other block FREE
+ *   set_fill: tokens held by a USED block, 0 .. block_tokens (a registered
+ *             block stays full)
+ *   register: index a full USED block under a prefix key; when the key is
+ *             already indexed to another block that block stays its entry and
+ *             *canonical names it
+ *   lookup:   *id = the block indexed under key (retained; a CACHED block is
+ *             reacquired with reference 1), or -1
+ * Errors: DEC_E_ARG, DEC_E_CAPACITY, DEC_E_BLOCK (an id that is not USED);
+ * a failed call changes nothing. Not thread-safe: one caller at a time.
+ */
+typedef struct dec_block_pool dec_block_pool;
+#define DEC_BLOCK_FREE 0
+#define DEC_BLOCK_USED 1
+#define DEC_BLOCK_CACHED 2
+int dec_pool_create(int32_t n_blocks, int32_t block_tokens, int32_t prefix_cache, dec_block_pool** out);
+void dec_pool_destroy(dec_block_pool* pool);
+const char* dec_pool_last_error(const dec_block_pool* pool);
+int dec_pool_alloc(dec_block_pool* pool, int32_t n, int32_t* ids);
+int dec_pool_retain(dec_block_pool* pool, int32_t id);
+int dec_pool_release(dec_block_pool* pool, int32_t id);
+int dec_pool_set_fill(dec_block_pool* pool, int32_t id, int32_t n);
+int dec_pool_register(dec_block_pool* pool, int32_t id, uint64_t key, int32_t* canonical);
+int dec_pool_lookup(dec_block_pool* pool, uint64_t key, int32_t* id);
+int dec_pool_block_info(const dec_block_pool* pool, int32_t id, int32_t* state, int32_t* ref, int32_t* fill);
+void dec_pool_counts(const dec_block_pool* pool, int32_t* n_free, int32_t* n_used, int32_t* n_cached);
+
+/*
+ * Prefix key of a block: a 64-bit hash of the parent block's key (0 for the
+ * first block) and the block's n token ids, so equal keys mean equal token
+ * prefixes up to hash collisions (FNV-1a over the bytes, then the splitmix64
+ * finaliser).
+ */
+uint64_t dec_prefix_key(uint64_t parent, const int32_t* tokens, int32_t n);
+
+/*
+ * Export / import of blocks' K and V data (the KvPool export/import of section
+ * 4; test kv_pool_exports_and_imports_rust_owned_blocks). The envelope is a
+ * header (magic "DECKVB01", n_layers, n_kv_heads, block_tokens, head_dim,
+ * kv_dtype, n as int32), the n fills (int32), then per block and per layer its
+ * K slab and its V slab ([H_kv][B][D] of the KV dtype each, the pool's own
+ * bytes). Both calls copy between ctx's device pool and the host buffer on
+ * `stream` and return after the copies are done.
+ *   export: ids / fills host [n] (ids < n_blocks, fills <= block_tokens);
+ *           buf of at least dec_kv_export_bytes(ctx, n) bytes
+ *   import: buf as written by export for a pool of the same block format
+ *           (else DEC_E_UNSUPPORTED); ids: host [n] destination blocks (the
+ *           caller allocates them); fills (may be NULL): host [n], receives
+ *           the envelope's fills
+ */
+size_t dec_kv_export_bytes(const dec_ctx* ctx, int32_t n);
+int dec_kv_export(dec_ctx* ctx, void* stream, const int32_t* ids, const int32_t* fills, int32_t n, void* buf,
+                  size_t buf_bytes);
+int dec_kv_import(dec_ctx* ctx, void* stream, const void* buf, size_t buf_bytes, const int32_t* ids, int32_t n,
+                  int32_t* fills);
+
 /* ---- per-kernel timing (diagnostics) ------------------------------------------------ */
 
 /* kernel classes */
