@@ -88,8 +88,8 @@ EXPORTS = ["dec_check_config", "dec_weight_bytes", "dec_weight_count", "dec_weig
            "dec_check_step", "dec_debug_dequant", "dec_rng_stream", "dec_sample", "dec_pool_create",
            "dec_pool_destroy", "dec_pool_last_error", "dec_pool_alloc", "dec_pool_retain", "dec_pool_release",
            "dec_pool_set_fill", "dec_pool_register", "dec_pool_lookup", "dec_pool_block_info", "dec_pool_counts",
-           "dec_prefix_key", "dec_kv_export_bytes", "dec_kv_export", "dec_kv_import", "dec_timing_enable",
-           "dec_timing_read"]
+           "dec_prefix_key", "dec_kv_export_bytes", "dec_kv_export", "dec_kv_import", "dec_config_from_json",
+           "dec_load_safetensors", "dec_timing_enable", "dec_timing_read"]
 
 DEC_BLOCK_FREE, DEC_BLOCK_USED, DEC_BLOCK_CACHED = 0, 1, 2
 
@@ -136,6 +136,8 @@ def _load():
         "dec_kv_export_bytes": (SZ, [VP, I32]),
         "dec_kv_export": (ctypes.c_int, [VP, VP, i32p, i32p, I32, VP, SZ]),
         "dec_kv_import": (ctypes.c_int, [VP, VP, VP, SZ, i32p, I32, i32p]),
+        "dec_config_from_json": (ctypes.c_int, [ctypes.c_char_p, SZ, cfgp, ctypes.c_char_p, SZ]),
+        "dec_load_safetensors": (ctypes.c_int, [ctypes.c_char_p, cfgp, VP, SZ, ctypes.c_char_p, SZ]),
         "dec_timing_enable": (ctypes.c_int, [VP, ctypes.c_uint32]),
         "dec_timing_read": (ctypes.c_int, [VP, ctypes.c_int, P(ctypes.c_double), P(ctypes.c_int64)]),
     }
@@ -346,6 +348,25 @@ def dec_kv_import(ctx: int, stream: int, data: bytes, ids):
     fills = (ctypes.c_int32 * n)()
     _check(_lib.dec_kv_import(ctx, stream or None, data, len(data), ip, n, fills), ctx)
     return list(fills)
+
+
+def dec_config_from_json(text: bytes, cfg: dec_config) -> None:
+    """Fill cfg's shape fields from a config.json's bytes; DecError on a refusal."""
+    buf = ctypes.create_string_buffer(512)
+    rc = _lib.dec_config_from_json(text, len(text), ctypes.byref(cfg), buf, 512)
+    if rc != DEC_OK:
+        raise DecError(rc, buf.value.decode())
+
+
+def dec_load_safetensors(path: str, cfg: dec_config) -> np.ndarray:
+    """The weights blob (host uint8 array) read from a model.safetensors file; DecError on a refusal."""
+    n = dec_weight_bytes(cfg)
+    blob = np.zeros(n, dtype=np.uint8)
+    buf = ctypes.create_string_buffer(512)
+    rc = _lib.dec_load_safetensors(os.fsencode(path), ctypes.byref(cfg), blob.ctypes.data, n, buf, 512)
+    if rc != DEC_OK:
+        raise DecError(rc, buf.value.decode())
+    return blob
 
 
 def dec_timing_enable(ctx: int, class_mask: int) -> None:

@@ -397,6 +397,43 @@ int dec_kv_export(dec_ctx* ctx, void* stream, const int32_t* ids, const int32_t*
 int dec_kv_import(dec_ctx* ctx, void* stream, const void* buf, size_t buf_bytes, const int32_t* ids, int32_t n,
                   int32_t* fills);
 
+/* ---- checkpoint loading (host only) ---------------------------------------------------- */
+
+/*
+ * config.json of a Qwen3 model -> the shape fields of *cfg (vocab, max_context
+ * from max_position_embeddings, d_model, n_heads, n_layers, n_kv_heads,
+ * head_dim, ff_hidden, rms_eps, rope_base; the three switches set to 1). The
+ * settings "A real model in our own decoder" whitelists (qwen_config) must
+ * hold: model_type "qwen3", hidden_act "silu", attention_bias false,
+ * attention_dropout 0, rope_scaling null, use_sliding_window false,
+ * tie_word_embeddings true, rms_norm_eps 1e-6; else DEC_E_UNSUPPORTED (refused
+ * at load, never served wrong: "Candle model runner" 2.3). The memory fields
+ * (dtypes, pool, rows) are left as the caller set them. `msg` (may be NULL)
+ * receives the reason of a refusal.
+ */
+int dec_config_from_json(const char* json, size_t len, dec_config* cfg, char* msg, size_t msg_len);
+
+/*
+ * model.safetensors at `path` -> the weights blob in host memory (blob_bytes >=
+ * dec_weight_bytes(cfg); the caller uploads it), for weight_dtype DEC_F32 or
+ * DEC_BF16. The file is a little-endian u64 header length N, N bytes of JSON,
+ * then the data buffer ("A real model in our own decoder", section "A
+ * safetensors file is a JSON header and raw bytes"). Refused with DEC_E_ARG: N
+ * outside [2, min(1e8, file size - 8)], a header that is not one object,
+ * duplicate keys, metadata that is not strings, an unknown dtype, a byte count
+ * that does not match the shape, ranges (from the start of the data buffer)
+ * that overlap, leave a gap or do not end at the end of the file, a missing or
+ * unexpected tensor, a shape mismatch, and an lm_head.weight whose values
+ * differ from the embedding's (the tied matrix stored twice is accepted when
+ * equal). F16 and BF16 tensors are widened to float32 ("Candle model runner"
+ * 2.3); a bf16 blob stores BF16 tensors as they are and rounds others to
+ * nearest even. Tensor names are Hugging Face's Qwen3 names
+ * (model.embed_tokens.weight, model.layers.<l>.self_attn.q_proj.weight, ...,
+ * model.norm.weight).
+ */
+int dec_load_safetensors(const char* path, const dec_config* cfg, void* blob, size_t blob_bytes, char* msg,
+                         size_t msg_len);
+
 /* ---- per-kernel timing (diagnostics) ------------------------------------------------ */
 
 /* kernel classes */
