@@ -54,21 +54,6 @@ __device__ __forceinline__ uint32_t pcg32_next(uint64_t& state, uint64_t inc) {
   return (xs >> rot) | (xs << ((32u - rot) & 31u));
 }
 
-// sum of one value per thread: thread t's value is added after those of threads < t
-__device__ double ordered_sum(double v, double* red, double* out) {
-  red[threadIdx.x] = v;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    double s = 0.0;
-    for (int i = 0; i < kST; ++i) s += red[i];
-    *out = s;
-  }
-  __syncthreads();
-  const double r = *out;
-  __syncthreads();
-  return r;
-}
-
 // largest value with the lowest id among equals
 __device__ void block_maxarg(double& v, int& id, double* red, int* redi) {
   const int t = threadIdx.x;
@@ -332,7 +317,7 @@ __global__ __launch_bounds__(kST) void sample_kernel(const float* __restrict__ l
       }
       if (ties) {
         const uint64_t eqm = __ballot(eq);
-        if (eq) in = gc[g] + __popcll(eqm & lanes_below) < krem;
+        if (eq) in = gc[g] + (int)__popcll(eqm & lanes_below) < krem;
       } else if (eq) {
         in = true;
       }
@@ -359,7 +344,7 @@ __global__ __launch_bounds__(kST) void sample_kernel(const float* __restrict__ l
         const bool in = kept_tk(g, v, y);
         const uint64_t m = __ballot(in);
         if (in) {
-          const int w = cc[g] + __popcll(m & lanes_below);
+          const int w = cc[g] + (int)__popcll(m & lanes_below);
           if (w < kNuc) {
             cand_id[w] = v;
             cand_key[w] = okey(y);

@@ -1,18 +1,14 @@
-// Host-side manager of the paged KV pool's blocks ("Candle model runner", section 2.2 "Candle
+// Host-side manager of the paged KV pool's block ids ("Candle model runner", section 2.2 "Candle
 // tensors and Rust-owned state" and the KvPool interface of section 4): references per block,
-// all-or-nothing allocation, a prefix index of full blocks, an LRU cache of released full
-// blocks (oldest evicted first when an allocation needs room), and export / import of blocks'
-// K/V data through a self-describing host buffer. Host memory only; export and import copy
-// between the caller's device pool and host buffers on the caller's stream.
+// all-or-nothing allocation, a prefix index of full blocks, and an LRU cache of released full
+// blocks (oldest evicted first when an allocation needs room). Host memory only; the blocks'
+// K/V data are copied by dec_kv_export / dec_kv_import, next to the context that owns the pool.
 #include <cstdint>
-#include <cstring>
 #include <list>
 #include <set>
 #include <string>
 #include <unordered_map>
 #include <vector>
-
-#include <hip/hip_runtime.h>
 
 #include "dec.h"
 
@@ -52,12 +48,6 @@ void make_free(dec_block_pool* p, int32_t id) {
   k = dec_block_pool::Block{};
   p->free_ids.insert(id);
 }
-
-// envelope of exported blocks: header, then per block its fill and, per layer, K then V slab
-struct EnvHeader {
-  char magic[8];  // "DECKVB01"
-  int32_t n_layers, n_kv_heads, block_tokens, head_dim, kv_dtype, n;
-};
 
 }  // namespace
 
