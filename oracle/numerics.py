@@ -19,7 +19,9 @@
 * symmetric int4-g32 dequantisation W = q * s ("Candle model runner", section
   2.5 "Int4 weights"), q a signed 4-bit value in [-8, 7] and s the f16 scale
   of the element's group of 32 input columns. The product has at most 15
-  significant bits, so it is exact in float32 (and in float64).
+  significant bits, so it is exact in float32 (and in float64). The same
+  section's quantisation (the runner's quantise-at-load route) is written out
+  too, in float32, with the f32 -> f16 rounding above.
 """
 
 from __future__ import annotations
@@ -104,6 +106,27 @@ def dequant_uint4_g32(q, scale_bits, zp_bits) -> np.ndarray:
     t = (qf - zp).astype(np.float32)
     w = (t * sc).astype(np.float32)
     return w.reshape(out, inp)
+
+
+def quantize_int4_sym_g32(w) -> tuple:
+    """Signed int4 values and f16 scale bits per 32-column group ("Candle model runner" 2.5).
+
+    In float32, per group: s = f16(max |W| / 7) (the float32 quotient rounded to nearest even
+    in f16), then q = clamp(rint(W / s), -8, 7) with the float32 quotient, rint half to even,
+    and s the stored f16 value; a group whose largest magnitude is 0 stores s = 0 and q = 0.
+    Returns (q int8 [out, in], scale_bits uint16 [out, in/32]).
+    """
+    w = np.asarray(w, dtype=np.float32)
+    out, inp = w.shape
+    grp = w.reshape(out, inp // 32, 32)
+    amax = np.max(np.abs(grp), axis=-1)
+    s_bits = f32_to_f16((amax / np.float32(7.0)).astype(np.float32))
+    s = f16_to_f32(s_bits)[..., None]
+    q = np.zeros(grp.shape, dtype=np.int8)
+    nz = np.broadcast_to(s > 0, grp.shape)
+    ratio = np.divide(grp, s, out=np.zeros_like(grp), where=nz).astype(np.float32)
+    q[nz] = np.clip(np.rint(ratio[nz]), -8, 7).astype(np.int8)
+    return q.reshape(out, inp), s_bits.reshape(out, inp // 32)
 
 
 def dequant_int4_sym_g32(q, scale_bits) -> np.ndarray:

@@ -137,6 +137,30 @@ def test_int4_sym_chooser_worked_example():
     assert int(np.rint(np.float32(w[0, 3]) / np.float32(0.2))) == alt != want[3]
 
 
+def test_int4_sym_oracle_quantiser_worked_example():
+    row, w = _example_group()
+    q, sb = nx.quantize_int4_sym_g32(w)
+    assert int(sb[0, 0]) == int(row[2], 16)
+    assert q[0, :4].tolist() == [int(v) for v in row[3].split()] and not q[0, 4:].any()
+
+
+def test_int4_sym_oracle_quantiser_bounds_and_generator_agreement():
+    # the oracle's quantiser keeps |W - q s| <= s / 2, maps zero groups to zero, and chooses the
+    # same values and scales as the input generator's (two writings of section 2.5)
+    from synthetic import quantize_int4_sym_g32
+    rng = np.random.default_rng(14)
+    w = (rng.standard_normal((32, 128)) * rng.uniform(1e-4, 2.0, size=(32, 1))).astype(np.float32)
+    w[5, :32] = 0.0
+    w[6, 40] = np.float32(2.5) * np.float32(0.25)  # exact multiples of a scale: ties for rint
+    q, sb = nx.quantize_int4_sym_g32(w)
+    g = quantize_int4_sym_g32(w)
+    assert np.array_equal(q, g.q) and np.array_equal(sb, g.scale)
+    wh = nx.dequant_int4_sym_g32(q, sb).astype(np.float64)
+    s = np.repeat(nx.f16_to_f32(sb).astype(np.float64), 32, axis=1)
+    assert np.all(np.abs(w - wh) <= s / 2 * (1 + 1e-6))
+    assert not q[5, :32].any() and not sb[5, 0]
+
+
 def test_int4_sym_dequant_worked_example_is_exact():
     row, w = _example_group()
     s16 = np.array([[int(row[2], 16)]], np.uint16)
