@@ -85,7 +85,7 @@ DEC_SAMPLE_MAX_NUCLEUS = 1024
 
 EXPORTS = ["dec_check_config", "dec_weight_bytes", "dec_weight_count", "dec_weight_entry", "dec_kv_pool_bytes",
            "dec_workspace_bytes", "dec_init", "dec_free", "dec_last_error", "dec_prefill", "dec_decode_step",
-           "dec_check_step", "dec_debug_dequant", "dec_rng_stream", "dec_sample", "dec_pool_create",
+           "dec_check_step", "dec_debug_dequant", "dec_quantize_int4_sym", "dec_rng_stream", "dec_sample", "dec_pool_create",
            "dec_pool_destroy", "dec_pool_last_error", "dec_pool_alloc", "dec_pool_retain", "dec_pool_release",
            "dec_pool_set_fill", "dec_pool_register", "dec_pool_lookup", "dec_pool_block_info", "dec_pool_counts",
            "dec_prefix_key", "dec_kv_export_bytes", "dec_kv_export", "dec_kv_import", "dec_config_from_json",
@@ -118,6 +118,7 @@ def _load():
         "dec_decode_step": (ctypes.c_int, [VP, VP, I32, i32p, VP, i32p, i32p, I32, VP, VP]),
         "dec_check_step": (ctypes.c_int, [cfgp, I32, i32p, i32p, i32p, i32p, I32, I32, ctypes.c_char_p, SZ]),
         "dec_debug_dequant": (ctypes.c_int, [VP, VP, ctypes.c_int, VP]),
+        "dec_quantize_int4_sym": (ctypes.c_int, [VP, VP, ctypes.c_int64, ctypes.c_int64, VP, VP]),
         "dec_rng_stream": (None, [ctypes.c_uint64, ctypes.c_uint64, P(ctypes.c_uint64)]),
         "dec_sample": (ctypes.c_int, [VP, VP, I32, VP, ctypes.c_int64, P(dec_sampling), P(dec_history), VP,
                                       ctypes.c_int64, VP, VP, VP]),
@@ -251,6 +252,11 @@ def dec_check_step(cfg: dec_config, start, n_new, tokens, block_tables, logits_m
 
 def dec_debug_dequant(ctx: int, stream: int, index: int, out: int) -> None:
     _check(_lib.dec_debug_dequant(ctx, stream or None, index, out), ctx)
+
+
+def dec_quantize_int4_sym(stream: int, w: int, rows: int, cols: int, q: int, scale: int) -> None:
+    """Device addresses: w float32 [rows][cols] -> q uint8 [rows][cols/2], scale f16 bits [rows][cols/32]."""
+    _check(_lib.dec_quantize_int4_sym(stream or None, w, rows, cols, q, scale))
 
 
 def dec_rng_stream(seed: int, purpose: int = DEC_PURPOSE_SAMPLE):

@@ -934,6 +934,15 @@ int dec_kv_import(dec_ctx* ctx, void* stream, const void* buf, size_t buf_bytes,
   return DEC_OK;
 }
 
+int dec_quantize_int4_sym(void* stream, const float* w, int64_t rows, int64_t cols, uint8_t* q, uint16_t* scale) {
+  if (!w || !q || !scale) return fail(&g_err, DEC_E_ARG, "quantize: NULL argument");
+  if (rows < 1 || cols < 32 || cols % 32) return fail(&g_err, DEC_E_ARG, "quantize: rows >= 1, cols a positive multiple of 32");
+  if (((uintptr_t)w | (uintptr_t)q) % 16) return fail(&g_err, DEC_E_ARG, "quantize: w and q must be 16-byte aligned");
+  const hipError_t e = launch_quant_int4_sym(w, rows, cols, q, scale, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(&g_err, DEC_E_HIP, "quantize: %s", hipGetErrorString(e));
+  return DEC_OK;
+}
+
 int dec_debug_dequant(dec_ctx* ctx, void* stream, int index, float* out) {
   if (!ctx) return fail(&g_err, DEC_E_ARG, "ctx is NULL");
   if (!out) return fail(&ctx->err, DEC_E_ARG, "out is NULL");

@@ -343,6 +343,51 @@ __global__ __launch_bounds__(256) void dequant_kernel(WMat w, int rows, int cols
   }
 }
 
+// ---- symmetric int4-g32 quantisation ("Candle model runner" 2.5, quantising at load) -------
+// One thread per group of 32 columns, float32 throughout: s = f16(max|W| / 7) (the quotient
+// rounded to nearest even), q = clamp(rint(W / s), -8, 7) with the stored s; a group whose
+// largest magnitude is 0 stores s = 0 and q = 0. Nibbles: column 2b low, 2b + 1 high.
+__global__ __launch_bounds__(256) void quant_int4_sym_kernel(const float* __restrict__ w, int64_t rows, int64_t cols,
+                                                             uint8_t* __restrict__ q, uint16_t* __restrict__ scale) {
+  const int64_t ng = cols / 32, total = rows * ng;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total; i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / ng, g = i - r * ng;
+    const float4* src = (const float4*)(w + r * cols + g * 32);
+    float x[32];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float4 v = src[j];
+      x[4 * j] = v.x;
+      x[4 * j + 1] = v.y;
+      x[4 * j + 2] = v.z;
+      x[4 * j + 3] = v.w;
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(x[j]));
+    const _Float16 sh = (_Float16)(amax / 7.0f);
+    const float sv = (float)sh;
+    u32x4 words = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      int qv = 0;
+      if (sv > 0.f) qv = (int)fminf(fmaxf(__builtin_rintf(x[j] / sv), -8.f), 7.f);
+      words[j >> 3] |= (uint32_t)(qv & 15) << (4 * (j & 7));
+    }
+    *(u32x4*)(q + r * (cols / 2) + g * 16) = words;
+    scale[i] = __builtin_bit_cast(uint16_t, sh);
+  }
+}
+
+hipError_t launch_quant_int4_sym(const float* w, int64_t rows, int64_t cols, uint8_t* q, uint16_t* scale,
+                                 hipStream_t s) {
+  const int64_t total = rows * (cols / 32);
+  if (total <= 0) return hipSuccess;
+  const int blocks = (int)std::min<int64_t>((total + 255) / 256, 65536);
+  quant_int4_sym_kernel<<<blocks, 256, 0, s>>>(w, rows, cols, q, scale);
+  return hipGetLastError();
+}
+
 hipError_t launch_dequant(int wdtype, const WMat& w, int rows, int cols, float* out, hipStream_t s) {
   const int64_t total = (int64_t)rows * cols;
   int blocks = (int)((total + 255) / 256);

@@ -165,6 +165,11 @@ hipError_t launch_sample(const float* logits, int64_t ld, int n_seqs, int vocab,
                          const int32_t* ids, uint32_t* counts, uint64_t* rng, int32_t* next, double* logprob,
                          hipStream_t s);
 
+// Symmetric int4-g32 values q [rows][cols/2] and f16 scales [rows][cols/32] of a float32
+// matrix w [rows][cols] (dec_quantize_int4_sym); cols % 32 == 0, 16-byte aligned buffers.
+hipError_t launch_quant_int4_sym(const float* w, int64_t rows, int64_t cols, uint8_t* q, uint16_t* scale,
+                                 hipStream_t s);
+
 // out[rows][cols] = widened / dequantised matrix (float32).
 hipError_t launch_dequant(int wdtype, const WMat& w, int rows, int cols, float* out, hipStream_t s);
 

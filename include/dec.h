@@ -248,6 +248,21 @@ int dec_check_step(const dec_config* cfg, int32_t n_seqs, const int32_t* start,
  */
 int dec_debug_dequant(dec_ctx* ctx, void* stream, int index, float* out);
 
+/*
+ * Quantise a float32 matrix to the DEC_INT4_SYM_G32 layout on the device (the
+ * runner's quantise-at-load route, "Candle model runner" 2.5): per group of 32
+ * columns s = f16(max |W| / 7) (rounded to nearest even), q = clamp(rint(W /
+ * s), -8, 7) with the stored s, in float32; a group of zeros stores s = 0 and
+ * q = 0 (W / s is undefined there).
+ *   w:     device float32 [rows][cols], 16-byte aligned; cols % 32 == 0
+ *   q:     device uint8 [rows][cols/2], 16-byte aligned (column 2b in the low
+ *          nibble, 2b + 1 in the high nibble, 4-bit two's complement)
+ *   scale: device f16 bits [rows][cols/32]
+ * Asynchronous on `stream`. DEC_E_ARG for NULL, misaligned or misshaped
+ * arguments (message: dec_last_error(NULL)).
+ */
+int dec_quantize_int4_sym(void* stream, const float* w, int64_t rows, int64_t cols, uint8_t* q, uint16_t* scale);
+
 /* ---- seeded sampling ------------------------------------------------------------------ */
 
 /* Sampling parameters of one sequence ("Candle model runner" section 2.6, SamplingParams). */
