@@ -31,6 +31,9 @@ VARIANTS = {
     "int4sym_f16kv": dataclasses.replace(MODELS["tiny_f32"], name="tiny_int4sym", weight_dtype="int4sym",
                                          kv_dtype="f16"),
     "bf16_f32kv": dataclasses.replace(MODELS["tiny_f32"], name="tiny_bf16_f32kv", weight_dtype="bf16", kv_dtype="f32"),
+    # one KV head per query head: grouped-query attention reduced to multi-head attention
+    "mha_bf16_f16kv": dataclasses.replace(MODELS["tiny_f32"], name="tiny_mha", n_kv_heads=4, weight_dtype="bf16",
+                                          kv_dtype="f16"),
 }
 
 
@@ -171,6 +174,20 @@ def test_batch_invariance_is_bit_exact(setup):
         one = s.decode_step([lens[i]], alloc.table_array([("alone", name, i)]), tokens_host=toks[i:i + 1])
         torch.cuda.synchronize()
         assert torch.equal(dec_b[k], one[0]), f"decode row {i} differs when batched"
+
+
+def test_decode_at_position_zero(setup, prompt):
+    # a sequence's first token through dec_decode_step: attention over the new key alone
+    name, shape, w, s, alloc = setup
+    seq = ("first", name)
+    alloc.ensure(seq, 1)
+    lg = s.decode_step([0], alloc.table_array([seq]), tokens_host=prompt[:1]).cpu().numpy()
+    dec = om.OracleDecoder(w)
+    ref = dec.forward([(prompt[:1], dec.new_cache())], logits="all")
+    row = compare(lg, ref, **gate(name))
+    row.update(type="logit_parity", case=f"tiny_{name}", path="decode_pos0")
+    report(row)
+    assert row["pass"], row
 
 
 def test_greedy_next_tokens_are_the_argmax(setup, prompt):
