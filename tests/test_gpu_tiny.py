@@ -31,6 +31,9 @@ VARIANTS = {
     "int4sym_f16kv": dataclasses.replace(MODELS["tiny_f32"], name="tiny_int4sym", weight_dtype="int4sym",
                                          kv_dtype="f16"),
     "bf16_f32kv": dataclasses.replace(MODELS["tiny_f32"], name="tiny_bf16_f32kv", weight_dtype="bf16", kv_dtype="f32"),
+    # eight query heads per KV head (the largest group the decode attention takes)
+    "gqa8_bf16_f16kv": dataclasses.replace(MODELS["tiny_f32"], name="tiny_gqa8", n_heads=16, n_kv_heads=2,
+                                           weight_dtype="bf16", kv_dtype="f16"),
     # one KV head per query head: grouped-query attention reduced to multi-head attention
     "mha_bf16_f16kv": dataclasses.replace(MODELS["tiny_f32"], name="tiny_mha", n_kv_heads=4, weight_dtype="bf16",
                                           kv_dtype="f16"),
@@ -186,6 +189,25 @@ def test_decode_at_position_zero(setup, prompt):
     ref = dec.forward([(prompt[:1], dec.new_cache())], logits="all")
     row = compare(lg, ref, **gate(name))
     row.update(type="logit_parity", case=f"tiny_{name}", path="decode_pos0")
+    report(row)
+    assert row["pass"], row
+
+
+def test_context_filled_to_the_last_position(setup):
+    # prefill positions 0 .. 254, then decode at 255 = max_context - 1, the last valid position
+    name, shape, w, s, alloc = setup
+    from decoder_forward_pass_amd.binding import DEC_LOGITS_LAST
+    T = s.cfg.max_context
+    toks = np.random.default_rng(78).integers(0, shape.vocab, T).astype(np.int32)
+    seq = ("full_ctx", name)
+    alloc.ensure(seq, T)
+    tbl = alloc.table_array([seq])
+    last = s.prefill([0], [T - 1], toks[:T - 1], tbl, DEC_LOGITS_LAST).cpu().numpy()
+    lg = s.decode_step([T - 1], tbl, tokens_host=toks[T - 1:]).cpu().numpy()
+    dec = om.OracleDecoder(w)
+    ref = dec.forward([(toks, dec.new_cache(capacity=T))], logits="all")
+    row = compare(np.concatenate([last, lg]), ref[T - 2:], **gate(name))
+    row.update(type="logit_parity", case=f"tiny_{name}", path="context_full")
     report(row)
     assert row["pass"], row
 
