@@ -13,11 +13,15 @@
 //      - top-k: a radix selection (8-bit digits, most significant first) of the k-th largest
 //        order-preserving 64-bit key of the tempered value; equal keys at the cut are taken
 //        in ascending id order;
-//      - with top-p < 1 (then k <= 1024): the k candidates go to LDS in ascending id order,
-//        their sum of exp(lt - max) is taken left to right, a bitonic network orders them by
-//        (value descending, id ascending) for the nucleus walk, min-p drops those below
-//        min_p times the largest probability, and one thread takes the final softmax and the
-//        walk over the kept ids left to right in ascending id order;
+//      - top-k with k <= 1024 usually avoids the radix passes over the vocabulary: a histogram
+//        of the distance below the largest value (buckets of 1/16) bounds the k-th value, the
+//        ids above that bound (at most 4096) go to LDS in id order, and the exact top-k is
+//        selected among them;
+//      - with top-p < 1 (then k <= 1024), or a top-k selected in LDS: the k candidates sit in
+//        LDS in ascending id order, their sum of exp(lt - max) is taken left to right, a
+//        bitonic network orders them by (value descending, id ascending) for the nucleus walk,
+//        min-p drops those below min_p times the largest probability, and one thread takes
+//        the final softmax and the walk over the kept ids left to right in ascending id order;
 //      - with top-p = 1: e = exp(lt - max) for the ids top-k and min-p keep, 0 for the others
 //        (an id whose e underflows to 0 is never drawn); sums over
 //        the whole vocabulary reduce each group of 64 consecutive ids by a fixed lane tree and
@@ -39,6 +43,7 @@ constexpr int kWaves = kST / 64;
 constexpr int kNuc = DEC_SAMPLE_MAX_NUCLEUS;  // candidates the nucleus step orders
 constexpr int kMaxGroups = 4096;              // groups of 64 ids: vocabularies up to 262,144
 constexpr int kU = 8;                         // ids per thread whose loads are issued together
+constexpr int kCand = 4096;                   // top-k candidates selected in LDS, at most
 
 // order-preserving key: a larger double has a larger key (finite values and infinities)
 __device__ __forceinline__ uint64_t okey(double v) {
@@ -96,6 +101,7 @@ __global__ __launch_bounds__(kST) void sample_kernel(const float* __restrict__ l
   __shared__ int gc[kMaxGroups];              // per group: a count, then its exclusive prefix
   __shared__ uint32_t hbits[kMaxGroups * 2];  // one bit per id: in the prompt or the output
   __shared__ double sp[kWaves];               // per span of groups: a partial sum
+  __shared__ int cidx[kCand];                 // top-k candidates: ids (keys in gp's storage)
   __shared__ int s_i[4];
   __shared__ double s_d[2];
   const int s = blockIdx.x, t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -200,14 +206,14 @@ __global__ __launch_bounds__(kST) void sample_kernel(const float* __restrict__ l
     __syncthreads();
     return r;
   };
-  // arr[0 .. NG) := its exclusive prefix in group order (each thread scans 4 groups, then a
+  // arr[0 .. n) := its exclusive prefix, n <= 4 kST (each thread scans 4 entries, then a
   // doubling scan over the threads); returns the total
-  auto group_prefix = [&](int* arr) -> int {
+  auto prefix4 = [&](int* arr, int n) -> int {
     int loc[4], sum = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int g = t * 4 + j;
-      loc[j] = g < NG ? arr[g] : 0;
+      loc[j] = g < n ? arr[g] : 0;
       sum += loc[j];
     }
     redi[t] = sum;
@@ -223,12 +229,13 @@ __global__ __launch_bounds__(kST) void sample_kernel(const float* __restrict__ l
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int g = t * 4 + j;
-      if (g < NG) arr[g] = a;
+      if (g < n) arr[g] = a;
       a += loc[j];
     }
     __syncthreads();
     return total;
   };
+  auto group_prefix = [&](int* arr) { return prefix4(arr, NG); };
   const uint64_t lanes_below = lane ? (~0ull >> (64 - lane)) : 0ull;
 
   const double Z = vocab_sum([&](float x, int v) { return v < V ? exp(pen(x, v) - mx) : 0.0; });
@@ -240,12 +247,166 @@ __global__ __launch_bounds__(kST) void sample_kernel(const float* __restrict__ l
     auto lt = [&](float x, int v) { return pen(x, v) / T; };
     const int k = P.top_k;
     const bool use_k = k > 0 && k < V;
-    // 3a. top-k: the top `bits` bits of the cut key are pv; krem ids are still to be taken
-    // among those whose key starts with pv (all of them unless `ties`)
+    // 3a. top-k with k <= kNuc: candidates first. A histogram of the distance below the largest
+    // tempered value, in buckets of 1/16 up to 16 (monotone in the value), gives the bucket b*
+    // where the count of larger-or-equal values first reaches k; the ids of buckets <= b* (at
+    // most kCand) go to LDS in id order, and the exact top-k by (value descending, id ascending)
+    // is selected there into cand_*. Otherwise (more candidates, or k beyond kNuc) the radix
+    // selection runs over the whole vocabulary (3a').
+    bool lds = use_k && k <= kNuc;
+    int nc = 0;
+    uint64_t* ckey = (uint64_t*)gp;
+    auto bucket = [&](double y) { return (mt - y) * 16.0; };  // >= 0; the id is a candidate when < b* + 1
+    if (lds) {
+      if (t < 256) hist[t] = 0;
+      __syncthreads();
+      for (int i0 = 0; i0 < V; i0 += kST * kU) {
+        float x[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int v = i0 + u * kST + t;
+          x[u] = v < V ? lg[v] : 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+          const int v = i0 + u * kST + t;
+          if (v < V) {
+            const double d = bucket(lt(x[u], v));
+            if (d < 256.0) atomicAdd(&hist[(int)d], 1u);
+          }
+        }
+      }
+      __syncthreads();
+      if (t == 0) {
+        uint32_t acc = 0;
+        int bs = -1;
+        for (int b = 0; b < 256; ++b) {
+          acc += hist[b];
+          if (acc >= (uint32_t)k) {
+            bs = b;
+            break;
+          }
+        }
+        s_i[0] = bs;
+        s_i[1] = (int)acc;
+      }
+      __syncthreads();
+      const int bstar = s_i[0], C = s_i[1];
+      __syncthreads();
+      lds = bstar >= 0 && C <= kCand;
+      if (lds) {
+        auto is_cand = [&](double y) {
+          const double d = bucket(y);
+          return d < 256.0 && (int)d <= bstar;
+        };
+        for (int g0 = 0; g0 < NG; g0 += kWaves) {
+          const int g = g0 + wave;
+          const int v = g * 64 + lane;
+          const uint64_t m = __ballot(v < V && is_cand(lt(lg[v], v)));
+          if (lane == 0 && g < NG) gc[g] = __popcll(m);
+        }
+        __syncthreads();
+        group_prefix(gc);
+        for (int g0 = 0; g0 < NG; g0 += kWaves) {
+          const int g = g0 + wave;
+          const int v = g * 64 + lane;
+          const double y = v < V ? lt(lg[v], v) : 0.0;
+          const bool in = v < V && is_cand(y);
+          const uint64_t m = __ballot(in);
+          if (in) {
+            const int w = gc[g] + (int)__popcll(m & lanes_below);
+            cidx[w] = v;
+            ckey[w] = okey(y);
+          }
+        }
+        __syncthreads();
+        // the k-th key among the C candidates: radix selection over LDS
+        uint64_t cpv = 0;
+        int cbits = 0, ckrem = k;
+        bool cties = false;
+        for (int pass = 0; pass < 8; ++pass) {
+          const int shift = 56 - 8 * pass;
+          if (t < 256) hist[t] = 0;
+          __syncthreads();
+          for (int i = t; i < C; i += kST) {
+            const uint64_t key = ckey[i];
+            if (cbits == 0 || (key >> (64 - cbits)) == cpv) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+          }
+          __syncthreads();
+          if (t == 0) {
+            uint32_t acc = 0;
+            int sel = 0;
+            for (int d = 255; d >= 0; --d) {
+              if (acc + hist[d] >= (uint32_t)ckrem) {
+                sel = d;
+                break;
+              }
+              acc += hist[d];
+            }
+            s_i[0] = sel;
+            s_i[1] = (int)acc;
+            s_i[2] = (int)hist[sel];
+          }
+          __syncthreads();
+          const int sel = s_i[0], above = s_i[1], in_sel = s_i[2];
+          __syncthreads();
+          ckrem -= above;
+          cpv = (cpv << 8) | (uint64_t)sel;
+          cbits += 8;
+          if (in_sel == ckrem) break;
+          cties = pass == 7;
+        }
+        // equal keys at the cut: their ranks in id order (gc: equal keys before each candidate)
+        if (cties) {
+          for (int i = t; i < C; i += kST) gc[i] = ckey[i] == cpv;
+          __syncthreads();
+          prefix4(gc, C);
+        }
+        // the top-k (exactly k) into cand_* in id order: each thread's 4 consecutive candidates
+        int kf[4], sum = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = t * 4 + j;
+          bool in = false;
+          if (i < C) {
+            const uint64_t top = ckey[i] >> (64 - cbits);
+            in = top > cpv || (top == cpv && (!cties || gc[i] < ckrem));
+          }
+          kf[j] = in;
+          sum += in;
+        }
+        __syncthreads();
+        redi[t] = sum;
+        __syncthreads();
+        for (int o = 1; o < kST; o <<= 1) {
+          const int add = t >= o ? redi[t - o] : 0;
+          __syncthreads();
+          redi[t] += add;
+          __syncthreads();
+        }
+        int w = redi[t] - sum;
+        nc = redi[kST - 1];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = t * 4 + j;
+          if (kf[j] && w < kNuc) {
+            const uint64_t key = ckey[i];
+            const uint64_t b = (key >> 63) ? (key & 0x7fffffffffffffffull) : ~key;  // okey inverted
+            cand_id[w] = cidx[i];
+            cand_key[w] = key;
+            cand_e[w] = exp(__builtin_bit_cast(double, b) - mt);
+          }
+          w += kf[j];
+        }
+        __syncthreads();
+      }
+    }
+    // 3a'. top-k over the whole vocabulary: the top `bits` bits of the cut key are pv; krem ids
+    // are still to be taken among those whose key starts with pv (all of them unless `ties`)
     uint64_t pv = 0;
     int bits = 0, krem = k;
     bool ties = false;
-    if (use_k) {
+    if (use_k && !lds) {
       for (int pass = 0; pass < 8; ++pass) {
         const int shift = 56 - 8 * pass;
         if (t < 256) hist[t] = 0;
@@ -324,9 +485,11 @@ __global__ __launch_bounds__(kST) void sample_kernel(const float* __restrict__ l
       return in;
     };
 
-    if (P.top_p < 1.0) {
-      // 3b. nucleus path: the (<= kNuc) candidates in ascending id order (gp's storage holds
-      // the per-group counts and their prefix here)
+    if (lds || P.top_p < 1.0) {
+      // 3b. nucleus path over the (<= kNuc) candidates in ascending id order: from 3a, or
+      // compacted here from the whole vocabulary (gp's storage holds the per-group counts and
+      // their prefix then)
+      if (!lds) {
       int* cc = (int*)gp;
       for (int g0 = 0; g0 < NG; g0 += kWaves) {
         const int g = g0 + wave;
@@ -336,7 +499,7 @@ __global__ __launch_bounds__(kST) void sample_kernel(const float* __restrict__ l
         if (lane == 0 && g < NG) cc[g] = __popcll(m);
       }
       __syncthreads();
-      const int nc = group_prefix(cc);  // (the ties ranks in gc stay as they are)
+      nc = group_prefix(cc);  // (the ties ranks in gc stay as they are)
       for (int g0 = 0; g0 < NG; g0 += kWaves) {
         const int g = g0 + wave;
         const int v = g * 64 + lane;
@@ -351,6 +514,7 @@ __global__ __launch_bounds__(kST) void sample_kernel(const float* __restrict__ l
             cand_e[w] = exp(y - mt);
           }
         }
+      }
       }
       ord[t] = t < nc ? t : -1;
       keepc[t] = 0;
@@ -381,11 +545,15 @@ __global__ __launch_bounds__(kST) void sample_kernel(const float* __restrict__ l
 #pragma unroll 8
         for (int i = 0; i < m; ++i) zk += cand_e[i];
         double c = 0.0;
-        for (int j = 0; j < m; ++j) {
-          const int i = ord[j];
-          c += cand_e[i] / zk;
-          keepc[i] = 1;
-          if (c >= P.top_p) break;
+        if (P.top_p < 1.0) {
+          for (int j = 0; j < m; ++j) {
+            const int i = ord[j];
+            c += cand_e[i] / zk;
+            keepc[i] = 1;
+            if (c >= P.top_p) break;
+          }
+        } else {
+          for (int i = 0; i < m; ++i) keepc[i] = 1;  // top-p 1 keeps every id top-k kept
         }
         if (P.min_p > 0.0) {
           const double qmax = cand_e[ord[0]] / zk;
