@@ -238,45 +238,40 @@ __global__ __launch_bounds__(kST) void sample_kernel(const float* __restrict__ l
   auto group_prefix = [&](int* arr) { return prefix4(arr, NG); };
   const uint64_t lanes_below = lane ? (~0ull >> (64 - lane)) : 0ull;
 
-  const double Z = vocab_sum([&](float x, int v) { return v < V ? exp(pen(x, v) - mx) : 0.0; });
+  const double T = P.temperature;
+  const int k = P.top_k;
+  const bool use_k = T > 0.0 && k > 0 && k < V;
+  const double mt = T > 0.0 ? mx / T : 0.0;  // the largest tempered value (division by T > 0 keeps the order)
+  auto lt = [&](float x, int v) { return pen(x, v) / T; };
+  auto bucket = [&](double y) { return (mt - y) * 16.0; };  // >= 0; the top-k candidate test of 3a
+  // (with a top-k of at most kNuc the Z pass also fills 3a's histogram of bucket(lt))
+  const bool hist_in_z = use_k && k <= kNuc;
+  if (hist_in_z) {
+    if (t < 256) hist[t] = 0;
+    __syncthreads();
+  }
+  const double Z = vocab_sum([&](float x, int v) {
+    if (v >= V) return 0.0;
+    const double l = pen(x, v);
+    if (hist_in_z) {
+      const double d = bucket(l / T);
+      if (d < 256.0) atomicAdd(&hist[(int)d], 1u);
+    }
+    return exp(l - mx);
+  });
   int tok = am;
 
-  const double T = P.temperature;
   if (T > 0.0) {
-    const double mt = mx / T;  // the largest tempered value (division by T > 0 keeps the order)
-    auto lt = [&](float x, int v) { return pen(x, v) / T; };
-    const int k = P.top_k;
-    const bool use_k = k > 0 && k < V;
     // 3a. top-k with k <= kNuc: candidates first. A histogram of the distance below the largest
     // tempered value, in buckets of 1/16 up to 16 (monotone in the value), gives the bucket b*
     // where the count of larger-or-equal values first reaches k; the ids of buckets <= b* (at
     // most kCand) go to LDS in id order, and the exact top-k by (value descending, id ascending)
     // is selected there into cand_*. Otherwise (more candidates, or k beyond kNuc) the radix
     // selection runs over the whole vocabulary (3a').
-    bool lds = use_k && k <= kNuc;
+    bool lds = hist_in_z;  // the histogram was filled by the Z pass
     int nc = 0;
     uint64_t* ckey = (uint64_t*)gp;
-    auto bucket = [&](double y) { return (mt - y) * 16.0; };  // >= 0; the id is a candidate when < b* + 1
     if (lds) {
-      if (t < 256) hist[t] = 0;
-      __syncthreads();
-      for (int i0 = 0; i0 < V; i0 += kST * kU) {
-        float x[kU];
-#pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          const int v = i0 + u * kST + t;
-          x[u] = v < V ? lg[v] : 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < kU; ++u) {
-          const int v = i0 + u * kST + t;
-          if (v < V) {
-            const double d = bucket(lt(x[u], v));
-            if (d < 256.0) atomicAdd(&hist[(int)d], 1u);
-          }
-        }
-      }
-      __syncthreads();
       if (t == 0) {
         uint32_t acc = 0;
         int bs = -1;
