@@ -534,42 +534,63 @@ __global__ __launch_bounds__(kST) void sample_kernel(const float* __restrict__ l
           __syncthreads();
         }
       }
+      // sums left to right in id order by one thread; the divisions by all threads (red holds
+      // the quotients), so the sequential walks only add
+      const int m = min(nc, kNuc);
       if (t == 0) {
-        const int m = min(nc, kNuc);
-        double zk = 0.0;
+        double z = 0.0;
 #pragma unroll 8
-        for (int i = 0; i < m; ++i) zk += cand_e[i];
-        double c = 0.0;
+        for (int i = 0; i < m; ++i) z += cand_e[i];
+        s_d[0] = z;
+      }
+      __syncthreads();
+      const double zk = s_d[0];
+      if (t < m) red[t] = cand_e[ord[t]] / zk;  // q of the t-th id in walk order
+      __syncthreads();
+      if (t == 0) {
+        int j = m;  // ids kept by the nucleus: the first j in walk order
         if (P.top_p < 1.0) {
-          for (int j = 0; j < m; ++j) {
-            const int i = ord[j];
-            c += cand_e[i] / zk;
-            keepc[i] = 1;
-            if (c >= P.top_p) break;
+          double c = 0.0;
+          for (int i = 0; i < m; ++i) {
+            c += red[i];
+            if (c >= P.top_p) {
+              j = i + 1;
+              break;
+            }
           }
-        } else {
-          for (int i = 0; i < m; ++i) keepc[i] = 1;  // top-p 1 keeps every id top-k kept
         }
-        if (P.min_p > 0.0) {
-          const double qmax = cand_e[ord[0]] / zk;
-          for (int i = 0; i < m; ++i)
-            if (keepc[i] && cand_e[i] / zk < P.min_p * qmax) keepc[i] = 0;
-        }
-        double zf = 0.0;
+        s_i[0] = j;
+      }
+      __syncthreads();
+      const double qmax = red[0];
+      if (t < s_i[0]) keepc[ord[t]] = 1;
+      __syncthreads();
+      if (P.min_p > 0.0 && t < m && keepc[t] && cand_e[t] / zk < P.min_p * qmax) keepc[t] = 0;
+      __syncthreads();
+      if (t == 0) {
+        double z = 0.0;
 #pragma unroll 8
         for (int i = 0; i < m; ++i)
-          if (keepc[i]) zf += cand_e[i];
+          if (keepc[i]) z += cand_e[i];
+        s_d[0] = z;
+      }
+      __syncthreads();
+      const double zf = s_d[0];
+      if (t < m) red[t] = keepc[t] ? cand_e[t] / zf : -1.0;  // the final probabilities; -1: dropped
+      __syncthreads();
+      if (t == 0) {
         uint64_t st = rng[2 * s];
         const uint64_t inc = rng[2 * s + 1];
         const uint32_t a = pcg32_next(st, inc), b = pcg32_next(st, inc);
         rng[2 * s] = st;
         const double u = ((double)(a >> 5) * 67108864.0 + (double)(b >> 6)) * (1.0 / 9007199254740992.0);
         int pick = -1;
-        c = 0.0;
+        double c = 0.0;
         for (int i = 0; i < m; ++i) {
-          if (!keepc[i]) continue;
+          const double pi = red[i];
+          if (pi < 0.0) continue;
           pick = i;
-          c += cand_e[i] / zf;
+          c += pi;
           if (u < c) break;
         }
         s_i[0] = pick >= 0 ? cand_id[pick] : am;
