@@ -261,8 +261,9 @@ def main():
         summarize_stats(args.summarize_stats, args.workload, args.steps)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(data-parallel sharding by sequence is described in DESIGN.md but not built).", file=sys.stderr)
+        print("bench.py runs on one GPU only: the library has no multi-GPU path (sharding the batch by "
+              "sequence would run these kernels unchanged on each GPU's share; it is not implemented).",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
