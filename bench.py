@@ -37,6 +37,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 MFMA_BF16_PEAK_TFS = 2516.6    # dense bf16 MFMA: 256 CUs x 4096 flop/clk x 2.4 GHz
 
 METRIC = "prefill & decode tokens/s on 1 MI355X; % MFMA / HBM roofline"
+MAX_ROWS = 32768               # prompt tokens per prefill call
 
 
 def parse():
@@ -117,7 +118,8 @@ def summarize_counters(fetch_dir, write_dir, wl_name, copy_mb):
     wl = __import__("synthetic").WORKLOADS[wl_name]
     shape = __import__("synthetic").MODELS[wl.model]
     per_key = shape.n_kv_heads * shape.head_dim * 2 * (2 if shape.kv_dtype == "f16" else 4)
-    alg = float(np.mean([wl.n_seqs * (wl.prompt_len + t + 1) * per_key for t in range(wl.decode_steps)]))
+    lens = prompt_lengths(wl)
+    alg = float(np.mean([int((lens + t + 1).sum()) * per_key for t in range(wl.decode_steps)]))
     summary = {
         "kernel": k, "workload": f"{wl_name} (decode steps)", "sources": ATTN_SOURCES,
         "source_sha256": _sources_sha256(ATTN_SOURCES), "dispatches": n,
@@ -233,22 +235,34 @@ def time_sampler(s, logits, prompts, reps=10):
             "bound": "fp64 VALU (exp) of one workgroup per row"}
 
 
+def prompt_lengths(wl):
+    """Prompt length of every sequence of a workload: all equal, or the seeded ragged lengths."""
+    from synthetic import make_context_lengths
+    if wl.prompt_len is not None:
+        return np.full(wl.n_seqs, wl.prompt_len, np.int64)
+    return np.asarray(make_context_lengths(wl), np.int64)
+
+
 def cpu_baseline(wl, shape, weights, prompts, decode_steps=8):
-    """The oracle as it is, on one sequence: its prefill, then a few greedy decode steps."""
+    """The oracle as it is, on one sequence (the first; with ragged prompts the shortest): its
+    prefill, then a few greedy decode steps."""
     import oracle.model as om
     threads = len(os.sched_getaffinity(0))
+    which = int(np.argmin([len(p) for p in prompts])) if wl.prompt_len is None else 0
+    plen = len(prompts[which])
     dec = om.OracleDecoder(weights)
-    c = dec.new_cache(capacity=wl.prompt_len + decode_steps)
+    c = dec.new_cache(capacity=plen + decode_steps)
     t0 = time.perf_counter()
-    lg = dec.forward([(prompts[0], c)], logits="last")
+    lg = dec.forward([(prompts[which], c)], logits="last")
     tok = int(np.argmax(lg[0]))
     for _ in range(decode_steps):
         lg = dec.forward([(np.array([tok]), c)], logits="last")
         tok = int(np.argmax(lg[0]))
     dt = time.perf_counter() - t0
-    n = wl.prompt_len + decode_steps
+    n = plen + decode_steps
+    which_s = "" if wl.prompt_len is not None else " (the shortest)"
     return {"value": n / dt, "unit": "tok/s", "cores": threads, "kind": "oracle",
-            "sample": f"1 of {wl.n_seqs} sequences: {wl.prompt_len}-token prefill + {decode_steps} greedy decode "
+            "sample": f"1 of {wl.n_seqs} sequences{which_s}: {plen}-token prefill + {decode_steps} greedy decode "
                       f"steps, float64 numpy, {dt:.1f} s"}
 
 
@@ -272,24 +286,35 @@ def main():
     from synthetic import MODELS, WORKLOADS, make_prompts, make_weights
 
     wl = WORKLOADS[args.workload]
-    if wl.prompt_len is None or wl.decode_steps == 0:
+    if wl.decode_steps == 0:
         sys.exit(f"workload {wl.name} is a parity case, not a bench workload")
     shape = MODELS[wl.model]
     weights = make_weights(shape)
     prompts = make_prompts(wl)
-    S, P, steps = wl.n_seqs, wl.prompt_len, wl.decode_steps
-    ctx = P + steps
-    n_blocks = S * math.ceil(ctx / shape.block_tokens)
-    s = Session(shape, weights, max_context=ctx, n_blocks=n_blocks, max_rows=S * P, max_seqs=S)
+    S, steps = wl.n_seqs, wl.decode_steps
+    lens = prompt_lengths(wl)
+    ctx = int(lens.max()) + steps
+    n_blocks = sum(math.ceil((int(n) + steps) / shape.block_tokens) for n in lens)
+    # prefill calls of consecutive sequences, each at most MAX_ROWS prompt tokens (one call for
+    # 32 x 1,024)
+    calls, i = [], 0
+    while i < S:
+        j, rows = i, 0
+        while j < S and (j == i or rows + int(lens[j]) <= MAX_ROWS):
+            rows += int(lens[j])
+            j += 1
+        calls.append((i, j, rows))
+        i = j
+    s = Session(shape, weights, max_context=ctx, n_blocks=n_blocks, max_rows=max(c[2] for c in calls), max_seqs=S)
     alloc = BlockAllocator(n_blocks, shape.block_tokens, seed=1)
     for i in range(S):
-        alloc.ensure(i, ctx)
+        alloc.ensure(i, int(lens[i]) + steps)
     tbl = alloc.table_array(list(range(S)))
-    tokens = np.concatenate(prompts)
+    call_args = [(np.concatenate(prompts[i:j]), alloc.table_array(list(range(i, j)))) for i, j, _ in calls]
     hist = torch.zeros((steps + 1, S), dtype=torch.int32, device="cuda")
     last = torch.empty((S, shape.vocab), dtype=torch.float32, device="cuda")
     logits = torch.empty((S, shape.vocab), dtype=torch.float32, device="cuda")
-    positions = [np.full(S, P + t, np.int32) for t in range(steps)]
+    positions = [(lens + t).astype(np.int32) for t in range(steps)]
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     if args.copy_mb:
         src = torch.empty(args.copy_mb << 18, dtype=torch.float32, device="cuda").fill_(1.0)
@@ -309,7 +334,9 @@ def main():
         if timed:
             ev[0].record()
             B.dec_timing_enable(s.ctx, 1 << K_GATEUP)
-        s.prefill([0] * S, [P] * S, tokens, tbl, B.DEC_LOGITS_LAST, logits=last, next_tokens=hist[0])
+        for (i, j, _), (toks, ctbl) in zip(calls, call_args):
+            s.prefill([0] * (j - i), lens[i:j], toks, ctbl, B.DEC_LOGITS_LAST, logits=last[i:j],
+                      next_tokens=hist[0, i:j])
         if timed:
             ev[1].record()
             B.dec_timing_enable(s.ctx, 0)
@@ -347,7 +374,7 @@ def main():
     sampler = None if args.no_sampler else time_sampler(s, logits, prompts)
     s.close()
 
-    tok_per_step = S * P + S * steps
+    tok_per_step = int(lens.sum()) + S * steps
     value = tok_per_step * args.steps / elapsed
     pre_ms = float(np.mean([p[0] for p in phases]))
     dec_ms = float(np.mean([p[1] for p in phases]))
@@ -357,14 +384,15 @@ def main():
     # (context length) x H_kv x D x 2 (K, V) x 2 bytes.
     kv_el = 2 if shape.kv_dtype == "f16" else 4
     per_key = shape.n_kv_heads * shape.head_dim * 2 * kv_el
-    bytes_per_step_layer = [S * (P + t + 1) * per_key for t in range(0, steps, TIME_EVERY or steps)]
+    bytes_per_step_layer = [int((lens + t + 1).sum()) * per_key for t in range(0, steps, TIME_EVERY or steps)]
     rows_launch_bytes = float(np.mean(bytes_per_step_layer))
     rows_launches_expected = args.steps * len(bytes_per_step_layer) * shape.n_layers if TIME_EVERY else 0
     rows_avg_ms = rows_ms / max(rows_n, 1)
     # (--time-every 0 times no launch: the roofline figures are then absent)
     achieved = rows_launch_bytes / (rows_avg_ms * 1e-3) / 1e9 if rows_n else None
-    # gate/up GEMM of the prefill: 2 * M * (2 ff) * d flops per launch
-    gu_prefill_flops = 2.0 * S * P * 2 * shape.ff_hidden * shape.d_model
+    # gate/up GEMM of the prefill: 2 * M * (2 ff) * d flops per launch (M = the call's rows;
+    # every call has the same number of launches, all timed)
+    gu_prefill_flops = float(np.mean([2.0 * rows * 2 * shape.ff_hidden * shape.d_model for _, _, rows in calls]))
     # (only prefill launches of that class are timed)
 
     result = {
@@ -381,9 +409,10 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "model": "Qwen3-0.6B shape, random init", "global_batch": S,
-                   "prompt_len": P, "decode_steps": steps, "weights": shape.weight_dtype,
+                   "prompt_len": wl.prompt_len if wl.prompt_len is not None else f"U[{wl.ctx_lo}, {wl.ctx_hi}]",
+                   "decode_steps": steps, "weights": shape.weight_dtype,
                    "kv_cache": shape.kv_dtype, "parallelism": "none (1 GPU)"},
-        "prefill_tok_s": round(S * P / (pre_ms * 1e-3), 1),
+        "prefill_tok_s": round(int(lens.sum()) / (pre_ms * 1e-3), 1),
         "decode_tok_s": round(S * steps / (dec_ms * 1e-3), 1),
         "prefill_ms": round(pre_ms, 3),
         "decode_ms_per_step": round(dec_ms / steps, 4),

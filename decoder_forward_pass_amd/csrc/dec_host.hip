@@ -63,6 +63,10 @@ int check_config(const dec_config* c, std::string* err) {
   if (c->n_blocks < 1) return fail(err, DEC_E_UNSUPPORTED, "n_blocks must be >= 1 (a pool without blocks is refused)");
   if (c->max_rows < 1 || c->max_seqs < 1 || c->max_seqs > c->max_rows)
     return fail(err, DEC_E_UNSUPPORTED, "need 1 <= max_seqs <= max_rows");
+  // (decode attention work items hold a row in 19 bits and a segment in 12)
+  if ((int64_t)c->max_context > (int64_t)kDecodeSegKeys * kDecodeMaxSegs)
+    return fail(err, DEC_E_UNSUPPORTED, "max_context must be <= %d", kDecodeSegKeys * kDecodeMaxSegs);
+  if (c->max_seqs > (1 << 19)) return fail(err, DEC_E_UNSUPPORTED, "max_seqs must be <= 524288");
   return DEC_OK;
 }
 
@@ -141,9 +145,10 @@ size_t kv_bytes(const dec_config& c) {
 // ---- workspace layout ----------------------------------------------------------------------
 
 struct Ws {
-  size_t rope, meta, x, h, qkv, q, o, a, part, amax, ssq, xg, samp, counts, total;
+  size_t rope, meta, x, h, qkv, q, o, a, part, dpart, amax, ssq, xg, samp, counts, total;
   size_t meta_ints;  // capacity of the metadata region in int32
   int chunk, nch_max, max_blocks_per_seq, max_tiles;
+  int seg_keys, dslots;  // decode attention: keys per segment; state slots per (row, KV head)
   int act_bytes, kv_el;
   bool flash;  // prefill attention by the MFMA tile kernel
 };
@@ -159,7 +164,10 @@ Ws ws_layout(const dec_config& c) {
   w.max_tiles = (int)(R / 64 + S);
   w.chunk = attn_rows_chunk(c.head_dim, c.kv_dtype == DEC_F16, c.n_heads / c.n_kv_heads);
   w.nch_max = w.chunk ? (c.max_context + w.chunk - 1) / w.chunk : 0;
-  w.meta_ints = 3 * R + 3 * S + R + 2 * (size_t)w.max_tiles + S * (size_t)w.max_blocks_per_seq;
+  w.seg_keys = std::max(kDecodeSegKeys, c.block_tokens);
+  w.dslots = (c.max_context + w.seg_keys - 1) / w.seg_keys + 1;
+  w.meta_ints = 3 * R + 3 * S + R + 2 * (size_t)w.max_tiles + S * (size_t)w.max_blocks_per_seq +
+                S * (size_t)(w.dslots - 1);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -179,6 +187,8 @@ Ws ws_layout(const dec_config& c) {
   w.flash = c.kv_dtype == DEC_F16 && attn_prefill_supported(c.head_dim, c.n_heads / c.n_kv_heads);
   const size_t prow = w.flash ? 0 : R;
   w.part = take(prow * H * (size_t)w.nch_max * (D + 2) * 4);
+  // decode rows split into segments: one state per (row, KV head, segment), plus the new key's
+  w.dpart = take(S * H * (size_t)w.dslots * (D + 2) * 4);
   w.amax = take(argmax_scratch_bytes((int)R, (int)S));
   w.ssq = take(S * (d / 16) * 4);  // decode: sums of squares of the residual in 16-column partials
   w.xg = take(S * d * 2);          // decode: bf16(residual * the next norm's gain)
@@ -308,7 +318,17 @@ int upload_meta(dec_ctx* ctx, hipStream_t st, int32_t S, const int32_t* start, c
   for (int s = 0; s < S; ++s) n_tiles += ((n_new ? n_new[s] : 1) + QT - 1) / QT;
   const size_t o_tok = 0, o_pos = N, o_seq = 2 * (size_t)N, o_sst = 3 * (size_t)N, o_snn = o_sst + S,
                o_sr0 = o_snn + S, o_out = o_sr0 + S, o_til = o_out + n_out, o_tbl = o_til + 2 * (size_t)n_tiles;
-  const size_t total = o_tbl + (size_t)S * stride;
+  // decode attention work items: only when a row has more keys than one segment takes
+  const int32_t sk = ctx->ws.seg_keys;
+  int32_t n_items = 0;
+  if (!n_new) {
+    bool split = false;
+    for (int s = 0; s < S; ++s) split |= start[s] > sk;
+    if (split)
+      for (int s = 0; s < S; ++s) n_items += start[s] > sk ? (start[s] + sk - 1) / sk : 1;
+  }
+  const size_t o_itm = o_tbl + (size_t)S * stride;
+  const size_t total = o_itm + n_items;
   if (total > ctx->ws.meta_ints) return fail(&ctx->err, DEC_E_CAPACITY, "call metadata exceeds the workspace");
 
   const int slot = ctx->slot;
@@ -347,6 +367,18 @@ int upload_meta(dec_ctx* ctx, hipStream_t st, int32_t S, const int32_t* start, c
       }
     }
   }
+  if (n_items) {
+    // (row, segment) items ordered by their key count, largest first (ties: row, then segment
+    // order), so that the short items fill in at the end; decode row s is sequence s
+    std::vector<std::pair<int32_t, int32_t>> it;  // (keys, item)
+    it.reserve(n_items);
+    for (int s = 0; s < S; ++s) {
+      const int32_t ns = start[s] > sk ? (start[s] + sk - 1) / sk : 1;
+      for (int32_t g = 0; g < ns; ++g) it.emplace_back(ns > 1 ? std::min(sk, start[s] - g * sk) : start[s], (s << 12) | g);
+    }
+    std::stable_sort(it.begin(), it.end(), [](const auto& x, const auto& y) { return x.first > y.first; });
+    for (int32_t i = 0; i < n_items; ++i) m[o_itm + i] = it[i].second;
+  }
   int32_t* dm = (int32_t*)(ctx->wsp + ctx->ws.meta);
   HIPCHECK(hipMemcpyAsync(dm, m, total * 4, hipMemcpyHostToDevice, st));
   HIPCHECK(hipEventRecord(ctx->ev[slot], st));
@@ -359,6 +391,9 @@ int upload_meta(dec_ctx* ctx, hipStream_t st, int32_t S, const int32_t* start, c
   b->out_rows = dm + o_out;
   b->tiles = dm + o_til;
   b->block_tables = dm + o_tbl;
+  b->dec_items = dm + o_itm;
+  b->n_dec_items = n_items;
+  b->seg_keys = sk;
   b->tbl_stride = stride;
   b->n_rows = N;
   b->n_seqs = S;
@@ -441,6 +476,7 @@ int run_forward(dec_ctx* ctx, hipStream_t st, const BatchDev& b, const int32_t* 
   void* o = ctx->wsp + w.o;
   void* act = ctx->wsp + w.a;
   float* part = (float*)(ctx->wsp + w.part);
+  float* dpart = (float*)(ctx->wsp + w.dpart);
   float* ssq = (float*)(ctx->wsp + w.ssq);
   uint16_t* xg = (uint16_t*)(ctx->wsp + w.xg);
   const float2* rope = (const float2*)(ctx->wsp + w.rope);
@@ -494,8 +530,9 @@ int run_forward(dec_ctx* ctx, hipStream_t st, const BatchDev& b, const int32_t* 
       TLAUNCH(DEC_K_GEMM_QKV, gemm(EPI_STORE, g));
     }
     if (decode) {
-      AttnRowsArgs ra{q, pool, l, H, Hkv, D, kv_f16, nch, part, b};
+      AttnRowsArgs ra{q, pool, l, H, Hkv, D, kv_f16, w.dslots, dpart, b};
       TLAUNCH(DEC_K_ATTN_ROWS, launch_attn_decode(qa, ra, o, act_bf16, st));
+      if (b.n_dec_items) TLAUNCH(DEC_K_ATTN_COMBINE, launch_attn_decode_combine(ra, o, act_bf16, st));
     } else {
       if (!big) TLAUNCH(DEC_K_QK_ROPE_KV, launch_qk_rope_kv(qa, st));
       if (w.flash) {

@@ -312,6 +312,11 @@ hipError_t launch_attn_combine(const float* partial, int n_rows, int n_heads, in
 // (its score, sum 1, the new value) merged after the wave states, in wave order, through LDS;
 // no partials leave the workgroup. The split depends only on the row's position, so the result
 // does not depend on the other sequences.
+// A row with more than seg_keys keys before its position is split into segments of seg_keys
+// keys, one workgroup each (the work items, longest first, so that the chip stays evenly busy
+// over ragged contexts): each runs the same loop over its segment and writes its merged state
+// (max, sum, accumulator) unnormalised; segment 0 also writes the pool and the new key's
+// state; the combine kernel merges the segments in order, then the new key.
 
 template <typename KVT, int D, int GROUP>
 struct DecodeGeom {
@@ -348,14 +353,25 @@ __global__ __launch_bounds__((64 * DecodeGeom<KVT, D, GROUP>::NWV)) void attn_de
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar math
   const int grp = lane / LPK, sub = lane % LPK;
   const int Hkv = a.n_kv_heads, H = a.n_heads;
-  const int row = blockIdx.x / Hkv, kvh = blockIdx.x % Hkv;
+  const int kvh = blockIdx.x % Hkv;
+  int row = blockIdx.x / Hkv, seg = 0;
+  if (a.b.n_dec_items) {
+    const int item = a.b.dec_items[row];
+    row = item >> 12;
+    seg = item & 4095;
+  }
   const int pos = a.b.row_pos[row];
   const int seq = a.b.row_seq[row];
-  // the pool loop covers the keys before the new position; the new key joins at the merge
-  const int nch = (pos + CHUNK - 1) / CHUNK;
+  // the pool loop covers the keys before the new position (of the segment: keys key_lo ..
+  // key_hi - 1); the new key joins at the merge
+  const int sk = a.b.seg_keys;
+  const int nseg = sk > 0 && pos > sk ? (pos + sk - 1) / sk : 1;
+  const int key_lo = seg * sk, key_hi = nseg > 1 ? min(key_lo + sk, pos) : pos;
+  const int nch = (key_hi - key_lo + CHUNK - 1) / CHUNK;
   const int32_t* table = a.b.block_tables + (int64_t)seq * a.b.tbl_stride;
   const int bsh = a.pool.block_shift, bmask = a.pool.block_tokens - 1;
-  const int last_blk = max(pos - 1, 0) >> bsh;
+  const int first_blk = key_lo >> bsh;  // (segments start at a block boundary)
+  const int last_blk = max(key_hi - 1, key_lo) >> bsh;
   const int64_t slab = (int64_t)Hkv * a.pool.block_tokens * D;
   // pool addresses: a wave-uniform part (layer, K or V, KV head, block, the load's first slot)
   // and a 32-bit lane part (the lane group's key within the load, the lane's channels)
@@ -364,7 +380,7 @@ __global__ __launch_bounds__((64 * DecodeGeom<KVT, D, GROUP>::NWV)) void attn_de
   const char* vbase = kbase + a.pool.n_blocks * slab * (int64_t)sizeof(KVT);
   const uint32_t lane_off = (uint32_t)((grp * D + sub * EPL) * sizeof(KVT));
 
-  // The sequence's block table goes to LDS (blocks 0 .. last_blk, at most TCAP of them) for
+  // The sequence's block table goes to LDS (blocks first_blk .. last_blk, at most TCAP) for
   // the requests after the barrier: range-checked loads, so entries past the last block cost
   // nothing. They are waited for together with tab below (which the first requests need), so
   // no later wait depends on them.
@@ -373,7 +389,8 @@ __global__ __launch_bounds__((64 * DecodeGeom<KVT, D, GROUP>::NWV)) void attn_de
   uint32_t tcopy[TPASS];
   {
     const __amdgpu_buffer_rsrc_t r =
-        __builtin_amdgcn_make_buffer_rsrc((void*)table, 0, min(last_blk + 1, TCAP) * 4, 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void*)(table + first_blk), 0, min(last_blk - first_blk + 1, TCAP) * 4,
+                                          0x00020000);
 #pragma unroll
     for (int p = 0; p < TPASS; ++p)
       tcopy[p] = __builtin_amdgcn_raw_buffer_load_b32(r, (int)((p * 64 * NWV + threadIdx.x) * 4), 0, 0);
@@ -381,7 +398,8 @@ __global__ __launch_bounds__((64 * DecodeGeom<KVT, D, GROUP>::NWV)) void attn_de
   // block ids of the wave's first chunks (the ones requested before the barrier): lane j holds
   // block j % bpc of the wave's chunk j / bpc
   const int bpc = CHUNK > a.pool.block_tokens ? CHUNK >> bsh : 1;  // blocks per chunk (64 / bpc >= NBUF)
-  const int tab = table[min(((min(wave + (lane / bpc) * NWV, max(nch - 1, 0)) * CHUNK) >> bsh) + lane % bpc, last_blk)];
+  const int tab =
+      table[min(((key_lo + min(wave + (lane / bpc) * NWV, max(nch - 1, 0)) * CHUNK) >> bsh) + lane % bpc, last_blk)];
   auto publish_table = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int p = 0; p < TPASS; ++p) s_tbl[p * 64 * NWV + threadIdx.x] = (int32_t)tcopy[p];
@@ -398,17 +416,17 @@ __global__ __launch_bounds__((64 * DecodeGeom<KVT, D, GROUP>::NWV)) void attn_de
   auto issue = [&](auto src, int ci, u32x4 (&kr)[KPG], u32x4 (&vr)[KPG]) __attribute__((always_inline)) {
     constexpr int SRC = decltype(src)::value;
     const bool live = SRC == 2 || ci < nmain;  // wave-uniform
-    const int key0 = (wave + ci * NWV) * CHUNK;
+    const int key0 = key_lo + (wave + ci * NWV) * CHUNK;
 #pragma unroll
     for (int kk = 0; kk < KPG; ++kk) {
-      // the KPI keys of one load share a block (B is a multiple of KPI); keys from the new
-      // position on read a slot of the last block and are masked below
+      // the KPI keys of one load share a block (B is a multiple of KPI); keys from key_hi on
+      // read a slot of the last block and are masked below
       const int b = min((key0 + kk * KPI) >> bsh, last_blk);
       int blk;
       if constexpr (SRC == 0)
         blk = __builtin_amdgcn_readlane(tab, ci * bpc + b - (key0 >> bsh));
       else if constexpr (SRC == 1)
-        blk = __builtin_amdgcn_readfirstlane(s_tbl[min(b, TCAP - 1)]);
+        blk = __builtin_amdgcn_readfirstlane(s_tbl[min(b - first_blk, TCAP - 1)]);
       else
         blk = table[b];
       const int64_t off = ((int64_t)blk * slab + ((key0 + kk * KPI) & bmask) * D) * (int64_t)sizeof(KVT);
@@ -465,14 +483,14 @@ __global__ __launch_bounds__((64 * DecodeGeom<KVT, D, GROUP>::NWV)) void attn_de
         const uint16_t b1 = f32_to_f16_bits(x1), b2 = f32_to_f16_bits(x2);
         dst[lane] = b1;
         dst[lane + half] = b2;
-        if (it >= GROUP) {
+        if (it >= GROUP && seg == 0) {
           pdst[lane] = b1;
           pdst[lane + half] = b2;
         }
       } else {
         dst[lane] = x1;
         dst[lane + half] = x2;
-        if (it >= GROUP) {
+        if (it >= GROUP && seg == 0) {
           pdst[lane] = x1;
           pdst[lane + half] = x2;
         }
@@ -531,16 +549,16 @@ __global__ __launch_bounds__((64 * DecodeGeom<KVT, D, GROUP>::NWV)) void attn_de
     for (int e = 0; e < EPL; ++e) acc[i][e] = 0.f;
   }
 
-  // every chunk of the loop holds at least one key before pos, so m is finite after it
+  // every chunk of the loop holds at least one key before key_hi, so m is finite after it
   auto step = [&](int ci, u32x4 (&kr)[KPG], u32x4 (&vr)[KPG]) __attribute__((always_inline)) {
-    const int key0 = (wave + ci * NWV) * CHUNK;
+    const int key0 = key_lo + (wave + ci * NWV) * CHUNK;
     // (an empty barrier keeps the per-chunk LDS reads of the query heads inside the loop, so the
     // compiler does not hold all of them in registers)
     if constexpr (!G::QREG) asm volatile("" ::: "memory");
     float sc[KPG][GROUP];
 #pragma unroll
     for (int kk = 0; kk < KPG; ++kk) {
-      const bool valid = key0 + kk * KPI + grp < pos;
+      const bool valid = key0 + kk * KPI + grp < key_hi;
 #pragma unroll
       for (int i = 0; i < GROUP; ++i) {
         u32x4 q;
@@ -569,7 +587,7 @@ __global__ __launch_bounds__((64 * DecodeGeom<KVT, D, GROUP>::NWV)) void attn_de
     for (int kk = 0; kk < KPG; ++kk) {
       // a masked key's slot holds whatever the block holds: zero it, as p * NaN is NaN
       u32x4 vw = vr[kk];
-      if (key0 + kk * KPI + grp >= pos) vw = u32x4{0u, 0u, 0u, 0u};
+      if (key0 + kk * KPI + grp >= key_hi) vw = u32x4{0u, 0u, 0u, 0u};
       float vv[EPL];
       load_kv<KVT, EPL>((const KVT*)&vw, vv);
 #pragma unroll
@@ -628,8 +646,42 @@ __global__ __launch_bounds__((64 * DecodeGeom<KVT, D, GROUP>::NWV)) void attn_de
     }
   }
   __syncthreads();
-  // merge: the wave states in wave order, then the new key's
   const int nw = min(NWV, nch);  // waves that saw at least one chunk
+  if (nseg > 1) {
+    // a segment of a split row: its wave states merged in wave order (every segment has a
+    // key, so wave 0 has a state), written unnormalised; segment 0 adds the new key's state
+    float* rec = a.partial + ((int64_t)row * Hkv + kvh) * a.n_chunks * (GROUP * (D + 2));
+    for (int t = threadIdx.x; t < GROUP * D; t += 64 * NWV) {
+      const int i = t / D, d = t % D;
+      float M = s_m[0][i];
+      for (int w = 1; w < nw; ++w) M = fmaxf(M, s_m[w][i]);
+      float L = 0.f, A = 0.f;
+      for (int w = 0; w < nw; ++w) {
+        const float sc = fast_exp2(s_m[w][i] - M);
+        L += sc * s_l[w][i];
+        A += sc * s_acc[w][i][d];
+      }
+      float* r = rec + (int64_t)seg * (GROUP * (D + 2)) + i * (D + 2);
+      r[d] = A;
+      if (d == 0) {
+        r[D] = M;
+        r[D + 1] = L;
+      }
+      if (seg == 0) {
+        float* rn = rec + (int64_t)nseg * (GROUP * (D + 2)) + i * (D + 2);
+        if constexpr (F16)
+          rn[d] = f16_bits_to_f32(s_q[GROUP + 1][d]);
+        else
+          rn[d] = s_q[GROUP + 1][d];
+        if (d == 0) {
+          rn[D] = s_m[NWV][i];
+          rn[D + 1] = 1.f;
+        }
+      }
+    }
+    return;
+  }
+  // merge: the wave states in wave order, then the new key's
   for (int t = threadIdx.x; t < GROUP * D; t += 64 * NWV) {
     const int i = t / D, d = t % D;
     float M = s_m[NWV][i];
@@ -659,7 +711,7 @@ __global__ __launch_bounds__((64 * DecodeGeom<KVT, D, GROUP>::NWV)) void attn_de
 
 template <typename KVT, int D, int GROUP>
 static void decode_launch(const QkRopeArgs& qk, const AttnRowsArgs& a, void* o, bool bf16_out, hipStream_t s) {
-  dim3 g(a.b.n_rows * a.n_kv_heads);
+  dim3 g((a.b.n_dec_items ? a.b.n_dec_items : a.b.n_rows) * a.n_kv_heads);
   const dim3 blk(64 * DecodeGeom<KVT, D, GROUP>::NWV);
   if (bf16_out)
     launch_kernel(attn_decode_kernel<KVT, D, GROUP, true>, g, blk, 0, s, qk, a, o);
@@ -692,6 +744,50 @@ hipError_t launch_attn_decode(const QkRopeArgs& qk, const AttnRowsArgs& a, void*
     if (a.head_dim == 128) return decode_dispatch_group<float, 128>(qk, a, o, out_bf16, s);
   }
   return hipErrorInvalidValue;
+}
+
+// ---- combine of split decode rows ------------------------------------------------------------
+// One block per (row, KV head); rows of one segment return at once. Thread t takes query head
+// t / D of the group and channel t % D: M = the largest state max, then the states' sums and
+// accumulators scaled by exp2(m - M), added in slot order (segments 0 .. n_seg - 1, then the
+// new key's state), and o = A / L.
+template <bool BF16_OUT>
+__global__ __launch_bounds__(256) void attn_decode_combine_kernel(AttnRowsArgs a, void* out) {
+  const int Hkv = a.n_kv_heads, G = a.n_heads / Hkv, D = a.head_dim;
+  const int row = blockIdx.x / Hkv, kvh = blockIdx.x % Hkv;
+  const int pos = a.b.row_pos[row], sk = a.b.seg_keys;
+  if (!(sk > 0 && pos > sk)) return;
+  const int nslot = (pos + sk - 1) / sk + 1;
+  const float* rec = a.partial + ((int64_t)row * Hkv + kvh) * a.n_chunks * (G * (D + 2));
+  for (int t = threadIdx.x; t < G * D; t += blockDim.x) {
+    const int i = t / D, d = t % D;
+    const float* r = rec + i * (D + 2);
+    const int64_t st = (int64_t)G * (D + 2);
+    float M = r[D];
+    for (int j = 1; j < nslot; ++j) M = fmaxf(M, r[j * st + D]);
+    float L = 0.f, A = 0.f;
+    for (int j = 0; j < nslot; ++j) {
+      const float sc = fast_exp2(r[j * st + D] - M);
+      L += sc * r[j * st + D + 1];
+      A += sc * r[j * st + d];
+    }
+    const float v = A / L;
+    const int64_t o = (int64_t)row * a.n_heads * D + (int64_t)(kvh * G + i) * D + d;
+    if constexpr (BF16_OUT)
+      ((uint16_t*)out)[o] = f32_to_bf16_bits(v);
+    else
+      ((float*)out)[o] = v;
+  }
+}
+
+hipError_t launch_attn_decode_combine(const AttnRowsArgs& a, void* o, bool out_bf16, hipStream_t s) {
+  if (a.b.n_rows <= 0 || a.b.n_dec_items <= 0) return hipSuccess;
+  const dim3 g(a.b.n_rows * a.n_kv_heads), blk(256);
+  if (out_bf16)
+    launch_kernel(attn_decode_combine_kernel<true>, g, blk, 0, s, a, o);
+  else
+    launch_kernel(attn_decode_combine_kernel<false>, g, blk, 0, s, a, o);
+  return hipGetLastError();
 }
 
 // ---- flash-style prefill attention (f16 pool, MFMA) ----------------------------------------

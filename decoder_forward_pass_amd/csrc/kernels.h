@@ -9,6 +9,11 @@
 namespace dec {
 
 constexpr int kPrefillQueryTile = 128;
+// Decode attention splits a row with more than this many keys before its position (or more
+// than one block of them, if blocks are larger) into segments of that many keys, one
+// workgroup each; the split depends only on the row's own position.
+constexpr int kDecodeSegKeys = 2048;
+constexpr int kDecodeMaxSegs = 4095;  // segment index field of a work item
 
 // Timed launches: while `start` is set and unused, the next kernel launched through
 // launch_kernel records `start` and `stop` at its own dispatch begin and end (HIP's extended
@@ -71,10 +76,16 @@ struct AttnRowsArgs {
 int attn_rows_chunk(int head_dim, bool kv_f16, int group);
 hipError_t launch_attn_rows(const AttnRowsArgs& a, hipStream_t s);
 
-// Decode attention: one workgroup per (row, KV head). It first applies the q/k norm and RoPE
-// of the row (qk.qkv) and writes the row's key and value to the pool, then attends; chunk
-// states merge inside the workgroup; writes o[r][h*D + d] (float32 or bf16) directly.
+// Decode attention: one workgroup per (row, KV head), or per (row, segment, KV head) for rows
+// split into segments (a.b.dec_items). It first applies the q/k norm and RoPE of the row
+// (qk.qkv) and writes the row's key and value to the pool (segment 0), then attends; chunk
+// states merge inside the workgroup. A row of one segment writes o[r][h*D + d] (float32 or
+// bf16) directly; a split row's segments write their states to a.partial, laid out
+// [rows][H_kv][a.n_chunks slots][group][D + 2] (accumulator, then max and sum; slot n_seg holds
+// the new key's state), for launch_attn_decode_combine.
 hipError_t launch_attn_decode(const QkRopeArgs& qk, const AttnRowsArgs& a, void* o, bool out_bf16, hipStream_t s);
+// The split rows' outputs: their segment states merged in segment order, then the new key's.
+hipError_t launch_attn_decode_combine(const AttnRowsArgs& a, void* o, bool out_bf16, hipStream_t s);
 
 // o[r][h*D + d] = combined attention output (float32 or bf16).
 hipError_t launch_attn_combine(const float* partial, int n_rows, int n_heads, int head_dim, int n_chunks,
