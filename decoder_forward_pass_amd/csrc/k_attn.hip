@@ -759,18 +759,50 @@ __global__ __launch_bounds__(256) void attn_decode_combine_kernel(AttnRowsArgs a
   if (!(sk > 0 && pos > sk)) return;
   const int nslot = (pos + sk - 1) / sk + 1;
   const float* rec = a.partial + ((int64_t)row * Hkv + kvh) * a.n_chunks * (G * (D + 2));
+  // the first U slots are loaded at once (one memory round trip); longer rows (contexts past
+  // (U - 1) segments) take further groups of U
+  constexpr int U = 8;
   for (int t = threadIdx.x; t < G * D; t += blockDim.x) {
     const int i = t / D, d = t % D;
     const float* r = rec + i * (D + 2);
     const int64_t st = (int64_t)G * (D + 2);
-    float M = r[D];
-    for (int j = 1; j < nslot; ++j) M = fmaxf(M, r[j * st + D]);
-    float L = 0.f, A = 0.f;
-    for (int j = 0; j < nslot; ++j) {
-      const float sc = fast_exp2(r[j * st + D] - M);
-      L += sc * r[j * st + D + 1];
-      A += sc * r[j * st + d];
+    float mv[U], lv[U], av[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      // (slots past the row's last read its last slot, and are then discarded)
+      const bool in = j < nslot;
+      const float* rj = r + min(j, nslot - 1) * st;
+      const float m = rj[D], l = rj[D + 1], x = rj[d];
+      mv[j] = in ? m : -__builtin_inff();
+      lv[j] = in ? l : 0.f;
+      av[j] = in ? x : 0.f;
     }
+    float M = mv[0];
+#pragma unroll
+    for (int j = 1; j < U; ++j) M = fmaxf(M, mv[j]);
+    for (int j0 = U; j0 < nslot; j0 += U)
+#pragma unroll
+      for (int j = 0; j < U; ++j)
+        if (j0 + j < nslot) M = fmaxf(M, r[(j0 + j) * st + D]);
+    float L = 0.f, A = 0.f;
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      if (j < nslot) {
+        const float sc = fast_exp2(mv[j] - M);
+        L += sc * lv[j];
+        A += sc * av[j];
+      }
+    }
+    for (int j0 = U; j0 < nslot; j0 += U)
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        if (j0 + j < nslot) {
+          const float* rj = r + (j0 + j) * st;
+          const float sc = fast_exp2(rj[D] - M);
+          L += sc * rj[D + 1];
+          A += sc * rj[d];
+        }
+      }
     const float v = A / L;
     const int64_t o = (int64_t)row * a.n_heads * D + (int64_t)(kvh * G + i) * D + d;
     if constexpr (BF16_OUT)
