@@ -318,6 +318,11 @@ hipError_t launch_attn_combine(const float* partial, int n_rows, int n_heads, in
 // (max, sum, accumulator) unnormalised; segment 0 also writes the pool and the new key's
 // state; the combine kernel merges the segments in order, then the new key.
 
+// LDS block-table entries of a decode attention work item: a row of at most seg_keys keys, or
+// one segment of a split row, spans at most seg_keys / B + 1 blocks
+constexpr int kDecodeTableCap = 1024;
+static_assert(kDecodeSegKeys / 16 + 1 <= kDecodeTableCap, "a work item's blocks fit the LDS table (B >= 16)");
+
 template <typename KVT, int D, int GROUP>
 struct DecodeGeom {
   static constexpr int EPL = 16 / (int)sizeof(KVT);
@@ -380,11 +385,12 @@ __global__ __launch_bounds__((64 * DecodeGeom<KVT, D, GROUP>::NWV)) void attn_de
   const char* vbase = kbase + a.pool.n_blocks * slab * (int64_t)sizeof(KVT);
   const uint32_t lane_off = (uint32_t)((grp * D + sub * EPL) * sizeof(KVT));
 
-  // The sequence's block table goes to LDS (blocks first_blk .. last_blk, at most TCAP) for
-  // the requests after the barrier: range-checked loads, so entries past the last block cost
-  // nothing. They are waited for together with tab below (which the first requests need), so
-  // no later wait depends on them.
-  constexpr int TCAP = 4096, TPASS = TCAP / (64 * NWV);
+  // The item's block table entries go to LDS (blocks first_blk .. last_blk: at most
+  // seg_keys / B + 1 of them, within TCAP) for the requests after the barrier: range-checked
+  // loads, so entries past the last block cost nothing. They are waited for together with tab
+  // below (which the first requests need), so no later wait depends on them.
+  constexpr int TCAP = kDecodeTableCap, TPASS = TCAP / (64 * NWV);
+  static_assert(TPASS >= 1, "one table entry per thread at least");
   __shared__ int32_t s_tbl[TCAP];
   uint32_t tcopy[TPASS];
   {
@@ -406,16 +412,14 @@ __global__ __launch_bounds__((64 * DecodeGeom<KVT, D, GROUP>::NWV)) void attn_de
   };
 
   const int nmine = wave < nch ? (nch - 1 - wave) / NWV + 1 : 0;  // chunks of this wave
-  // chunks whose blocks the LDS table holds: the first TCAP * B / (CHUNK * NWV) of each wave
-  const int nmain = min(nmine, (TCAP << bsh) / (CHUNK * NWV));
   // Requests of chunk ci's K and V rows; SRC picks where the block ids come from: 0 the lanes
-  // of tab (the first chunks), 1 the LDS table, 2 the table in memory (past the LDS table).
-  // With SRC < 2 every call issues the same loads whether or not the wave has chunk ci, so
-  // that the count of loads in flight is the same on every path (the wait before each chunk
-  // then waits for that chunk alone): past nmain the loads have range 0 at a valid address.
+  // of tab (the first chunks), 1 the LDS table. Every call issues the same loads whether or
+  // not the wave has chunk ci, so that the count of loads in flight is the same on every path
+  // (the wait before each chunk then waits for that chunk alone): past nmine the loads have
+  // range 0 at a valid address.
   auto issue = [&](auto src, int ci, u32x4 (&kr)[KPG], u32x4 (&vr)[KPG]) __attribute__((always_inline)) {
     constexpr int SRC = decltype(src)::value;
-    const bool live = SRC == 2 || ci < nmain;  // wave-uniform
+    const bool live = ci < nmine;  // wave-uniform
     const int key0 = key_lo + (wave + ci * NWV) * CHUNK;
 #pragma unroll
     for (int kk = 0; kk < KPG; ++kk) {
@@ -425,10 +429,8 @@ __global__ __launch_bounds__((64 * DecodeGeom<KVT, D, GROUP>::NWV)) void attn_de
       int blk;
       if constexpr (SRC == 0)
         blk = __builtin_amdgcn_readlane(tab, ci * bpc + b - (key0 >> bsh));
-      else if constexpr (SRC == 1)
-        blk = __builtin_amdgcn_readfirstlane(s_tbl[min(b - first_blk, TCAP - 1)]);
       else
-        blk = table[b];
+        blk = __builtin_amdgcn_readfirstlane(s_tbl[min(b - first_blk, TCAP - 1)]);
       const int64_t off = ((int64_t)blk * slab + ((key0 + kk * KPI) & bmask) * D) * (int64_t)sizeof(KVT);
       kr[kk] = load_uniform_base(kbase + (live ? off : 0), lane_off, live ? 0x7fffffff : 0);
       vr[kk] = load_uniform_base(vbase + (live ? off : 0), lane_off, live ? 0x7fffffff : 0);
@@ -436,7 +438,6 @@ __global__ __launch_bounds__((64 * DecodeGeom<KVT, D, GROUP>::NWV)) void attn_de
   };
   using FromTab = std::integral_constant<int, 0>;
   using FromLds = std::integral_constant<int, 1>;
-  using FromMem = std::integral_constant<int, 2>;
 
   // The row's Q|K|V product gives GROUP + 2 prologue items: query heads kvh*GROUP + it for it < GROUP, then the key and the
   // value; wave w takes items w, w + NWV, ... . An item's loads are issued ahead of the wave's
@@ -601,17 +602,12 @@ __global__ __launch_bounds__((64 * DecodeGeom<KVT, D, GROUP>::NWV)) void attn_de
   };
   // the register sets in turn: while one chunk is consumed the others are in flight, and a
   // set is refilled with the chunk NBUF further on as soon as it has been consumed
-  for (int c0 = 0; c0 < nmain; c0 += NBUF) {
+  for (int c0 = 0; c0 < nmine; c0 += NBUF) {
     unrolled<NBUF>([&](auto b) {
       const int ci = c0 + b;
-      if (ci < nmain) step(ci, kb[b], vb[b]);
+      if (ci < nmine) step(ci, kb[b], vb[b]);
       issue(FromLds{}, ci + NBUF, kb[b], vb[b]);
     });
-  }
-  // chunks past the LDS table (contexts beyond TCAP blocks): one at a time
-  for (int ci = nmain; ci < nmine; ++ci) {
-    issue(FromMem{}, ci, kb[0], vb[0]);
-    step(ci, kb[0], vb[0]);
   }
 
   // this wave's state: sum the lane groups (each holds distinct keys)
@@ -734,6 +730,8 @@ static hipError_t decode_dispatch_group(const QkRopeArgs& qk, const AttnRowsArgs
 
 hipError_t launch_attn_decode(const QkRopeArgs& qk, const AttnRowsArgs& a, void* o, bool out_bf16, hipStream_t s) {
   if (a.b.n_rows <= 0) return hipSuccess;
+  // every work item must fit the kernel's LDS block table
+  if (a.b.seg_keys <= 0 || a.b.seg_keys / a.pool.block_tokens + 1 > kDecodeTableCap) return hipErrorInvalidValue;
   if (a.kv_f16) {
     if (a.head_dim == 32) return decode_dispatch_group<uint16_t, 32>(qk, a, o, out_bf16, s);
     if (a.head_dim == 64) return decode_dispatch_group<uint16_t, 64>(qk, a, o, out_bf16, s);
