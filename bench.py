@@ -119,7 +119,7 @@ def summarize_counters(fetch_dir, write_dir, wl_name, copy_mb):
     shape = __import__("synthetic").MODELS[wl.model]
     per_key = shape.n_kv_heads * shape.head_dim * 2 * (2 if shape.kv_dtype == "f16" else 4)
     lens = prompt_lengths(wl)
-    alg = float(np.mean([int((lens + t + 1).sum()) * per_key for t in range(wl.decode_steps)]))
+    alg = float(np.mean([attention_bytes(lens, t, per_key) for t in range(wl.decode_steps)]))
     summary = {
         "kernel": k, "workload": f"{wl_name} (decode steps)", "sources": ATTN_SOURCES,
         "source_sha256": _sources_sha256(ATTN_SOURCES), "dispatches": n,
@@ -243,6 +243,26 @@ def prompt_lengths(wl):
     return np.asarray(make_context_lengths(wl), np.int64)
 
 
+def prefill_calls(lens, max_rows=MAX_ROWS):
+    """Consecutive sequences grouped into prefill calls of at most max_rows prompt tokens (a
+    longer prompt alone in its call): a list of (first, end, rows)."""
+    calls, i, S = [], 0, len(lens)
+    while i < S:
+        j, rows = i, 0
+        while j < S and (j == i or rows + int(lens[j]) <= max_rows):
+            rows += int(lens[j])
+            j += 1
+        calls.append((i, j, rows))
+        i = j
+    return calls
+
+
+def attention_bytes(lens, t, per_key):
+    """Algorithmic bytes of one decode attention launch at decode step t: every visible key and
+    value once (the keys before each sequence's position, and the new one)."""
+    return int((np.asarray(lens, np.int64) + t + 1).sum()) * per_key
+
+
 def cpu_baseline(wl, shape, weights, prompts, decode_steps=8):
     """The oracle as it is, on one sequence (the first; with ragged prompts the shortest): its
     prefill, then a few greedy decode steps."""
@@ -297,14 +317,7 @@ def main():
     n_blocks = sum(math.ceil((int(n) + steps) / shape.block_tokens) for n in lens)
     # prefill calls of consecutive sequences, each at most MAX_ROWS prompt tokens (one call for
     # 32 x 1,024)
-    calls, i = [], 0
-    while i < S:
-        j, rows = i, 0
-        while j < S and (j == i or rows + int(lens[j]) <= MAX_ROWS):
-            rows += int(lens[j])
-            j += 1
-        calls.append((i, j, rows))
-        i = j
+    calls = prefill_calls(lens)
     s = Session(shape, weights, max_context=ctx, n_blocks=n_blocks, max_rows=max(c[2] for c in calls), max_seqs=S)
     alloc = BlockAllocator(n_blocks, shape.block_tokens, seed=1)
     for i in range(S):
@@ -384,7 +397,7 @@ def main():
     # (context length) x H_kv x D x 2 (K, V) x 2 bytes.
     kv_el = 2 if shape.kv_dtype == "f16" else 4
     per_key = shape.n_kv_heads * shape.head_dim * 2 * kv_el
-    bytes_per_step_layer = [int((lens + t + 1).sum()) * per_key for t in range(0, steps, TIME_EVERY or steps)]
+    bytes_per_step_layer = [attention_bytes(lens, t, per_key) for t in range(0, steps, TIME_EVERY or steps)]
     rows_launch_bytes = float(np.mean(bytes_per_step_layer))
     rows_launches_expected = args.steps * len(bytes_per_step_layer) * shape.n_layers if TIME_EVERY else 0
     rows_avg_ms = rows_ms / max(rows_n, 1)
