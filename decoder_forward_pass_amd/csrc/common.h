@@ -162,9 +162,9 @@ struct BatchDev {
   const int32_t* block_tables; // [n_seqs][tbl_stride]
   const int32_t* out_rows;     // [n_out] rows that get logits
   const int32_t* tiles;        // [n_tiles][2] (sequence, first query row) for prefill attention
-  // decode attention work items, longest first: (row << 12) | segment; present (n_dec_items >
-  // 0) only when some row has more than seg_keys keys before its position, else one item per
-  // row in row order is implied
+  // decode attention work items, longest first: [n_dec_items][4] (row, segment, position,
+  // sequence), 16-byte aligned; present (n_dec_items > 0) only when some row has more than
+  // seg_keys keys before its position, else one item per row in row order is implied
   const int32_t* dec_items;
   int32_t tbl_stride;
   int32_t n_rows, n_seqs, n_out, n_tiles;

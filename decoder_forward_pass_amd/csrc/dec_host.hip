@@ -63,7 +63,7 @@ int check_config(const dec_config* c, std::string* err) {
   if (c->n_blocks < 1) return fail(err, DEC_E_UNSUPPORTED, "n_blocks must be >= 1 (a pool without blocks is refused)");
   if (c->max_rows < 1 || c->max_seqs < 1 || c->max_seqs > c->max_rows)
     return fail(err, DEC_E_UNSUPPORTED, "need 1 <= max_seqs <= max_rows");
-  // (decode attention work items hold a row in 19 bits and a segment in 12)
+  // (the host orders decode attention work items by row * 4096 + segment, in 32 bits)
   if ((int64_t)c->max_context > (int64_t)kDecodeSegKeys * kDecodeMaxSegs)
     return fail(err, DEC_E_UNSUPPORTED, "max_context must be <= %d", kDecodeSegKeys * kDecodeMaxSegs);
   if (c->max_seqs > (1 << 19)) return fail(err, DEC_E_UNSUPPORTED, "max_seqs must be <= 524288");
@@ -166,8 +166,8 @@ Ws ws_layout(const dec_config& c) {
   w.nch_max = w.chunk ? (c.max_context + w.chunk - 1) / w.chunk : 0;
   w.seg_keys = std::max(kDecodeSegKeys, c.block_tokens);
   w.dslots = (c.max_context + w.seg_keys - 1) / w.seg_keys + 1;
-  w.meta_ints = 3 * R + 3 * S + R + 2 * (size_t)w.max_tiles + S * (size_t)w.max_blocks_per_seq +
-                S * (size_t)(w.dslots - 1);
+  w.meta_ints = 3 * R + 3 * S + R + 2 * (size_t)w.max_tiles + S * (size_t)w.max_blocks_per_seq + 3 +
+                4 * S * (size_t)(w.dslots - 1);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
@@ -327,8 +327,8 @@ int upload_meta(dec_ctx* ctx, hipStream_t st, int32_t S, const int32_t* start, c
     if (split)
       for (int s = 0; s < S; ++s) n_items += start[s] > sk ? (start[s] + sk - 1) / sk : 1;
   }
-  const size_t o_itm = o_tbl + (size_t)S * stride;
-  const size_t total = o_itm + n_items;
+  const size_t o_itm = (o_tbl + (size_t)S * stride + 3) & ~(size_t)3;  // 16-byte aligned
+  const size_t total = o_itm + 4 * (size_t)n_items;
   if (total > ctx->ws.meta_ints) return fail(&ctx->err, DEC_E_CAPACITY, "call metadata exceeds the workspace");
 
   const int slot = ctx->slot;
@@ -369,15 +369,23 @@ int upload_meta(dec_ctx* ctx, hipStream_t st, int32_t S, const int32_t* start, c
   }
   if (n_items) {
     // (row, segment) items ordered by their key count, largest first (ties: row, then segment
-    // order), so that the short items fill in at the end; decode row s is sequence s
-    std::vector<std::pair<int32_t, int32_t>> it;  // (keys, item)
+    // order), so that the short items fill in at the end; each carries its row's position and
+    // sequence (decode row s is sequence s), so a workgroup needs one load to start
+    std::vector<std::pair<int32_t, int32_t>> it;  // (keys, row * 4096 + segment)
     it.reserve(n_items);
     for (int s = 0; s < S; ++s) {
       const int32_t ns = start[s] > sk ? (start[s] + sk - 1) / sk : 1;
-      for (int32_t g = 0; g < ns; ++g) it.emplace_back(ns > 1 ? std::min(sk, start[s] - g * sk) : start[s], (s << 12) | g);
+      for (int32_t g = 0; g < ns; ++g) it.emplace_back(ns > 1 ? std::min(sk, start[s] - g * sk) : start[s], s * 4096 + g);
     }
     std::stable_sort(it.begin(), it.end(), [](const auto& x, const auto& y) { return x.first > y.first; });
-    for (int32_t i = 0; i < n_items; ++i) m[o_itm + i] = it[i].second;
+    for (int32_t i = 0; i < n_items; ++i) {
+      const int32_t s = it[i].second / 4096;
+      int32_t* e = m + o_itm + 4 * (size_t)i;
+      e[0] = s;
+      e[1] = it[i].second % 4096;
+      e[2] = start[s];
+      e[3] = s;
+    }
   }
   int32_t* dm = (int32_t*)(ctx->wsp + ctx->ws.meta);
   HIPCHECK(hipMemcpyAsync(dm, m, total * 4, hipMemcpyHostToDevice, st));

@@ -359,14 +359,17 @@ __global__ __launch_bounds__((64 * DecodeGeom<KVT, D, GROUP>::NWV)) void attn_de
   const int grp = lane / LPK, sub = lane % LPK;
   const int Hkv = a.n_kv_heads, H = a.n_heads;
   const int kvh = blockIdx.x % Hkv;
-  int row = blockIdx.x / Hkv, seg = 0;
-  if (a.b.n_dec_items) {
-    const int item = a.b.dec_items[row];
-    row = item >> 12;
-    seg = item & 4095;
+  int row = blockIdx.x / Hkv, seg = 0, pos, seq;
+  if (a.b.n_dec_items) {  // (row, segment, position, sequence) in one load
+    const int4 item = ((const int4*)a.b.dec_items)[row];
+    row = item.x;
+    seg = item.y;
+    pos = item.z;
+    seq = item.w;
+  } else {
+    pos = a.b.row_pos[row];
+    seq = a.b.row_seq[row];
   }
-  const int pos = a.b.row_pos[row];
-  const int seq = a.b.row_seq[row];
   // the pool loop covers the keys before the new position (of the segment: keys key_lo ..
   // key_hi - 1); the new key joins at the merge
   const int sk = a.b.seg_keys;

@@ -13,7 +13,7 @@ constexpr int kPrefillQueryTile = 128;
 // than one block of them, if blocks are larger) into segments of that many keys, one
 // workgroup each; the split depends only on the row's own position.
 constexpr int kDecodeSegKeys = 2048;
-constexpr int kDecodeMaxSegs = 4095;  // segment index field of a work item
+constexpr int kDecodeMaxSegs = 4095;  // segments per row (the host sorts items by row * 4096 + segment)
 
 // Timed launches: while `start` is set and unused, the next kernel launched through
 // launch_kernel records `start` and `stop` at its own dispatch begin and end (HIP's extended
