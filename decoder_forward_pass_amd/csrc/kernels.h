@@ -12,7 +12,7 @@ constexpr int kPrefillQueryTile = 128;
 // Decode attention splits a row with more than this many keys before its position (or more
 // than one block of them, if blocks are larger) into segments of that many keys, one
 // workgroup each; the split depends only on the row's own position.
-constexpr int kDecodeSegKeys = 2048;
+constexpr int kDecodeSegKeys = 4096;
 constexpr int kDecodeMaxSegs = 4095;  // segments per row (the host sorts items by row * 4096 + segment)
 
 // Timed launches: while `start` is set and unused, the next kernel launched through

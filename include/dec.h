@@ -224,8 +224,8 @@ int dec_prefill(dec_ctx* ctx, void* stream, int32_t n_seqs, const int32_t* start
  *                the row with ties to the lowest id ("Candle model runner"
  *                section 2.6); needs logits != NULL.
  * As in dec_prefill, a row's results do not depend on the other sequences of
- * the call, bit for bit. The attention over a row with more than 2,048 keys
- * before its position is computed in 2,048-key segments merged in order; the
+ * the call, bit for bit. The attention over a row with more than 4,096 keys
+ * before its position is computed in 4,096-key segments merged in order; the
  * segmentation depends on that position alone.
  */
 int dec_decode_step(dec_ctx* ctx, void* stream, int32_t n_seqs, const int32_t* tokens_host,

@@ -1,10 +1,10 @@
-"""GPU parity of decode attention on rows split into key segments: a row with more than 2,048
-keys before its position is attended by one workgroup per 2,048-key segment, and the segments'
+"""GPU parity of decode attention on rows split into key segments: a row with more than 4,096
+keys before its position is attended by one workgroup per 4,096-key segment, and the segments'
 states are merged in order with the new key's ("Candle model runner" 2.4, second equation:
 the softmax over every key up to the position, computed here in parts).
 
 On the two-layer tiny decoder: decode steps at positions on both sides of the one-, two- and
-three-segment boundaries (2,047 .. 2,049 and 4,095 .. 4,097 keys before the position) against
+three-segment boundaries (4,095 .. 4,097 and 8,191 .. 8,193 keys before the position) against
 the oracle's full forward (float32 gate 1e-3, "Proving it's the same model", "Pick the
 tolerance before looking"; f16-KV gate 2e-2 of the row's logit range, "Candle model runner"
 2.4, "The f16 bound"), and a batch that mixes split and unsplit rows against each row alone,
@@ -29,11 +29,11 @@ VARIANTS = {
     "gqa8_bf16_f16kv": dataclasses.replace(MODELS["tiny_f32"], name="tiny_gqa8", n_heads=16, n_kv_heads=2,
                                            weight_dtype="bf16", kv_dtype="f16"),
 }
-T = 4098          # prompt tokens of the long sequence (positions 0 .. 4097)
-FIRST = (2047, 2048, 2049)
-SECOND = (4095, 4096, 4097)
-MAX_CTX = 4200
-N_BLOCKS = 1200
+T = 8194          # prompt tokens of the long sequence (positions 0 .. 8193)
+FIRST = (4095, 4096, 4097)
+SECOND = (8191, 8192, 8193)
+MAX_CTX = 8300
+N_BLOCKS = 2200
 
 
 def gate(name):
@@ -53,7 +53,7 @@ def setup(request):
 
 @pytest.fixture(scope="module")
 def long_prompt():
-    return np.random.default_rng(4098).integers(0, MODELS["tiny_f32"].vocab, T).astype(np.int32)
+    return np.random.default_rng(8194).integers(0, MODELS["tiny_f32"].vocab, T).astype(np.int32)
 
 
 def test_split_decode_matches_oracle(setup, long_prompt):
@@ -82,7 +82,7 @@ def test_split_decode_matches_oracle(setup, long_prompt):
 def test_split_rows_batch_invariance_is_bit_exact(setup, long_prompt):
     name, shape, w, s, alloc = setup
     from decoder_forward_pass_amd.binding import DEC_LOGITS_NONE
-    lens = [4097, 30, 2049]  # three, one and two segments
+    lens = [8193, 30, 4097]  # three, one and two segments
     toks = np.array([long_prompt[n] for n in lens], np.int32)
     for tag in ("alone", "batch"):
         for i, n in enumerate(lens):
