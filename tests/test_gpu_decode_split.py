@@ -28,6 +28,10 @@ VARIANTS = {
     "bf16_f16kv": dataclasses.replace(MODELS["tiny_f32"], name="tiny_bf16", weight_dtype="bf16", kv_dtype="f16"),
     "gqa8_bf16_f16kv": dataclasses.replace(MODELS["tiny_f32"], name="tiny_gqa8", n_heads=16, n_kv_heads=2,
                                            weight_dtype="bf16", kv_dtype="f16"),
+    "gqa4_bf16_f16kv": dataclasses.replace(MODELS["tiny_f32"], name="tiny_gqa4", n_heads=8, n_kv_heads=2,
+                                           weight_dtype="bf16", kv_dtype="f16"),
+    "mha_bf16_f16kv": dataclasses.replace(MODELS["tiny_f32"], name="tiny_mha", n_kv_heads=4, weight_dtype="bf16",
+                                          kv_dtype="f16"),
 }
 T = 8194          # prompt tokens of the long sequence (positions 0 .. 8193)
 FIRST = (4095, 4096, 4097)
