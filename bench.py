@@ -62,7 +62,8 @@ def parse():
     return ap.parse_args()
 
 
-ATTN_SOURCES = ["decoder_forward_pass_amd/csrc/k_attn.hip", "decoder_forward_pass_amd/csrc/common.h"]
+ATTN_SOURCES = ["decoder_forward_pass_amd/csrc/k_attn.hip", "decoder_forward_pass_amd/csrc/common.h",
+                "decoder_forward_pass_amd/csrc/kernels.h"]
 TRAFFIC_KERNEL = "attn_decode_kernel"
 
 
