@@ -58,6 +58,11 @@ def _rotate(vec, pos, base):
     return out
 
 
+def _qk_head(vec, g, pos, eps, base):
+    # one query or key head: RMSNorm over its channels with its gain, then the rotation
+    return _rotate(_rmsnorm(vec, g, eps), pos, base)
+
+
 class LoopDecoder:
     def __init__(self, weights):
         m = weights.shape
@@ -73,8 +78,10 @@ class LoopDecoder:
         # per layer: dict position -> (k heads, v heads)
         return [dict() for _ in range(self.m.n_layers)]
 
-    def step(self, token: int, pos: int, cache):
-        """One token at absolute position ``pos``; returns its logits (list)."""
+    def step(self, token: int, pos: int, cache, trace=None):
+        """One token at absolute position ``pos``; returns its logits (list). ``trace`` (a list, or
+        None) receives (layer, pos, q heads, k heads, v heads) of every layer, q and k after the
+        q/k norm and the rotation."""
         m = self.m
         H, Hkv, D, eps = m.n_heads, m.n_kv_heads, m.head_dim, m.rms_eps
         x = list(self.E[token])
@@ -83,11 +90,11 @@ class LoopDecoder:
             qf = _matvec(L["wq"], h)
             kf = _matvec(L["wk"], h)
             vf = _matvec(L["wv"], h)
-            qs = [_rotate(_rmsnorm(qf[i * D:(i + 1) * D], L["q_norm"], eps), pos, m.rope_base)
-                  for i in range(H)]
-            ks = [_rotate(_rmsnorm(kf[i * D:(i + 1) * D], L["k_norm"], eps), pos, m.rope_base)
-                  for i in range(Hkv)]
+            qs = [_qk_head(qf[i * D:(i + 1) * D], L["q_norm"], pos, eps, m.rope_base) for i in range(H)]
+            ks = [_qk_head(kf[i * D:(i + 1) * D], L["k_norm"], pos, eps, m.rope_base) for i in range(Hkv)]
             vs = [vf[i * D:(i + 1) * D] for i in range(Hkv)]
+            if trace is not None:
+                trace.append((li, pos, qs, ks, vs))
             cache[li][pos] = (ks, vs)
             o = []
             for hq in range(H):
@@ -120,8 +127,8 @@ class LoopDecoder:
         xf = _rmsnorm(x, self.gf, eps)
         return _matvec(self.E, xf)
 
-    def run(self, tokens, start: int = 0, cache=None):
+    def run(self, tokens, start: int = 0, cache=None, trace=None):
         """Logits of every token of ``tokens`` placed at positions start, start+1, ..."""
         if cache is None:
             cache = self.new_cache()
-        return [self.step(int(t), start + i, cache) for i, t in enumerate(tokens)], cache
+        return [self.step(int(t), start + i, cache, trace) for i, t in enumerate(tokens)], cache

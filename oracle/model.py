@@ -80,6 +80,16 @@ def rope(x: np.ndarray, pos: np.ndarray, base: float) -> np.ndarray:
     return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
 
 
+def qk_norm_rope(q: np.ndarray, k: np.ndarray, g_q: np.ndarray, g_k: np.ndarray, pos: np.ndarray, eps: float,
+                 base: float):
+    """The q/k step of the Qwen switches (switch 5): each query head [.., H, D] is RMS-normalised
+    over its D channels with the gain g_q, each key head with g_k, and only then rotated by RoPE
+    at the absolute positions ``pos``."""
+    q = rms_norm(q, g_q, eps)
+    k = rms_norm(k, g_k, eps)
+    return rope(q, pos, base), rope(k, pos, base)
+
+
 def silu(z: np.ndarray) -> np.ndarray:
     return z / (1.0 + np.exp(-z))
 
@@ -152,6 +162,9 @@ class OracleDecoder:
 
     def __init__(self, weights, kv_round: str | None = None):
         m = weights.shape
+        # when a list: forward appends (layer, positions, q, k, v) of every layer, q and k after
+        # the q/k norm and RoPE (for the tests' pins of the gains)
+        self.trace = None
         self.m = m
         wd = m.weight_dtype
         self.E = widen_matrix(weights.embed, wd)
@@ -202,14 +215,13 @@ class OracleDecoder:
 
         x = self.E[ids]
         for li, L in enumerate(self.layers):
-            h = rms_norm(x, L["attn_norm"], eps)
+            h = self._attn_input(L, x)
             q = (h @ L["wq"].T).reshape(-1, H, D)
             k = (h @ L["wk"].T).reshape(-1, Hkv, D)
             v = (h @ L["wv"].T).reshape(-1, Hkv, D)
-            q = rms_norm(q, L["q_norm"], eps)
-            k = rms_norm(k, L["k_norm"], eps)
-            q = rope(q, pos, m.rope_base)
-            k = rope(k, pos, m.rope_base)
+            q, k = qk_norm_rope(q, k, L["q_norm"], L["k_norm"], pos, eps, m.rope_base)
+            if self.trace is not None:
+                self.trace.append((li, pos.copy(), q.copy(), k.copy(), v.copy()))
             o = np.empty_like(q)
             for si, c in enumerate(caches):
                 a, b = offs[si], offs[si + 1]
@@ -217,7 +229,7 @@ class OracleDecoder:
                 self._write_cache(c, li, s0, k[a:b], v[a:b])
                 o[a:b] = attention(q[a:b], c.K[li][:s0 + n], c.V[li][:s0 + n], pos[a:b])
             x = x + o.reshape(-1, H * D) @ L["wo"].T
-            h2 = rms_norm(x, L["ffn_norm"], eps)
+            h2 = self._ffn_input(L, x)
             x = x + swiglu(h2 @ L["w_gate"].T, h2 @ L["w_up"].T) @ L["w_down"].T
         for c, s, n in zip(caches, starts, counts):
             c.length = s + n
@@ -232,6 +244,14 @@ class OracleDecoder:
         n = k.shape[0]
         c.K[layer][start:start + n] = self._store_kv(k)
         c.V[layer][start:start + n] = self._store_kv(v)
+
+    def _attn_input(self, L: dict, x: np.ndarray) -> np.ndarray:
+        """The pre-attention RMSNorm, with the layer's attention-norm gain."""
+        return rms_norm(x, L["attn_norm"], self.m.rms_eps)
+
+    def _ffn_input(self, L: dict, x: np.ndarray) -> np.ndarray:
+        """The post-attention RMSNorm in front of the SwiGLU block, with the layer's FFN-norm gain."""
+        return rms_norm(x, L["ffn_norm"], self.m.rms_eps)
 
     def _final_hidden(self, x: np.ndarray) -> np.ndarray:
         return rms_norm(x, self.final_norm, self.m.rms_eps)

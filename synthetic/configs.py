@@ -13,9 +13,15 @@ model in our own decoder" (section "Everything arrives, nothing extra").
 The final-norm gain ``final_gain`` scales the logits so that their range per
 position is a few tens, the size "Proving it's the same model" reports for the
 real checkpoint (section "Pick the tolerance before looking": median 29 and
-42). All other norm gains are 1.0 and every matrix is drawn N(0, 0.02). The
-logit standard deviation is final_gain * 0.02 * sqrt(d_model); the gain is
-chosen so that it equals 4.
+42). Every matrix is drawn N(0, 0.02). The logit standard deviation is
+final_gain * 0.02 * sqrt(d_model); the gain is chosen so that it equals 4.
+
+Norm gains (``gains``): "unit" sets every per-layer gain to 1.0 and the final
+gain to ``final_gain`` on every channel, as the two-layer configuration states;
+"random" draws each gain vector per channel, uniform in [0.5, 1.5] (the final
+one times ``final_gain``), so that a gain applied to the wrong tensor, to the
+wrong channel or not at all changes the result. The 0.6B configurations leave
+the gains open; they take "random", as a trained checkpoint's gains are not 1.
 """
 
 from __future__ import annotations
@@ -42,6 +48,7 @@ class ModelShape:
     init_std: float = 0.02
     final_gain: float = 1.0
     seed: int = 0
+    gains: str = "unit"  # "unit" | "random" (per-channel gains, uniform in [0.5, 1.5])
 
     @property
     def q_width(self) -> int:
@@ -63,13 +70,13 @@ MODELS = {
     "tiny_f32": ModelShape(name="tiny_f32", **_TINY, weight_dtype="f32", kv_dtype="f32",
                            final_gain=_logit_gain(64), seed=101),
     "q06b_f32": ModelShape(name="q06b_f32", **_Q06B, weight_dtype="f32", kv_dtype="f32",
-                           final_gain=_logit_gain(1024), seed=202),
+                           final_gain=_logit_gain(1024), seed=202, gains="random"),
     "q06b_bf16": ModelShape(name="q06b_bf16", **_Q06B, weight_dtype="bf16", kv_dtype="f16",
-                            final_gain=_logit_gain(1024), seed=303),
+                            final_gain=_logit_gain(1024), seed=303, gains="random"),
     "q06b_uint4": ModelShape(name="q06b_uint4", **_Q06B, weight_dtype="uint4", kv_dtype="f16",
-                             final_gain=_logit_gain(1024), seed=505),
+                             final_gain=_logit_gain(1024), seed=505, gains="random"),
     "q06b_int4sym": ModelShape(name="q06b_int4sym", **_Q06B, weight_dtype="int4sym", kv_dtype="f16",
-                               final_gain=_logit_gain(1024), seed=606),
+                               final_gain=_logit_gain(1024), seed=606, gains="random"),
 }
 
 

@@ -3,7 +3,11 @@
 Every value is drawn from numpy's PCG64 generator under a fixed seed.
 Matrices are drawn N(0, init_std) in float32, one after another in this order:
 the embedding, then for each layer W_q, W_k, W_v, W_o, W_gate, W_up, W_down.
-Norm gains are constants (1.0 per layer; ``final_gain`` for the final norm).
+Norm gains are constants (1.0 per layer; ``final_gain`` for the final norm) for
+``gains="unit"``. For ``gains="random"`` they come from a second stream of
+their own (so the matrices are the same either way): per layer attn_norm [d],
+q_norm [D], k_norm [D], ffn_norm [d], then the final norm [d], each element
+uniform in [0.5, 1.5] (the final norm's times ``final_gain``).
 
 Storage formats of the drawn matrices (all stored [out, in], row-major, the
 layout "Candle model runner" section 2.4 gives for the projections):
@@ -165,13 +169,25 @@ def make_weights(m: ModelShape | str, seed: int | None = None) -> Weights:
         layer = {}
         for name in MATRIX_NAMES:
             layer[name] = _store(m, _draw(rng, shapes[name], m.init_std))
-        layer["attn_norm"] = np.ones(d, np.float32)
-        layer["ffn_norm"] = np.ones(d, np.float32)
-        layer["q_norm"] = np.ones(m.head_dim, np.float32)
-        layer["k_norm"] = np.ones(m.head_dim, np.float32)
         layers.append(layer)
-    final = np.full(d, m.final_gain, np.float32)
+    gain = _gain_source(m, m.seed if seed is None else seed)
+    for layer in layers:
+        layer["attn_norm"] = gain(d)
+        layer["q_norm"] = gain(m.head_dim)
+        layer["k_norm"] = gain(m.head_dim)
+        layer["ffn_norm"] = gain(d)
+    final = (gain(d) * np.float32(m.final_gain)).astype(np.float32)
     return Weights(m, embed, layers, final)
+
+
+def _gain_source(m: ModelShape, seed: int):
+    """Gain vectors in draw order: all ones ("unit") or uniform in [0.5, 1.5] ("random")."""
+    if m.gains == "unit":
+        return lambda n: np.ones(n, np.float32)
+    if m.gains != "random":
+        raise ValueError(m.gains)
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 0x6A1])))
+    return lambda n: rng.uniform(0.5, 1.5, size=n).astype(np.float32)
 
 
 def _streams(wl: Workload):

@@ -116,15 +116,14 @@ def test_prefill_and_greedy_decode_match_oracle(run, seq):
     print(f"[c3] oracle decode seq {seq}", flush=True)
     for t in range(wl.decode_steps):
         tok = np.array([hist[t, seq]])
+        r = dec.forward([(tok, c)], logits="all")[0]
+        check_choice(r, int(hist[t + 1, seq]))  # every step's greedy choice
         if t in CHECK_STEPS:
-            r = dec.forward([(tok, c)], logits="all")[0]
             rows_gpu.append(out["keep"][t][k])
             rows_ref.append(r)
-            check_choice(r, int(hist[t + 1, seq]))
-        else:
-            dec.forward([(tok, c)], logits="none")
     row = compare(np.array(rows_gpu), np.array(rows_ref), rel_range=REL)
     row.update(type="logit_parity", case=wl.name, path=f"seq{seq}_prefill_last+decode", greedy_flips=flips,
+               greedy_steps_checked=wl.decode_steps + 1,
                greedy_flips_outside_gate=bad_flips)
     report(row)
     assert row["pass"], row

@@ -120,13 +120,11 @@ def test_prefill_and_decode_match_oracle(run):
     choice(ref_last, int(hist[0, 0]))
     for t in range(wl.decode_steps):
         tok = np.array([hist[t, 0]])
+        r = dec.forward([(tok, c)], logits="all")[0]
+        choice(r, int(hist[t + 1, 0]))  # every step's greedy choice
         if t in CHECK_STEPS:
-            r = dec.forward([(tok, c)], logits="all")[0]
             rows_gpu.append(out["keep"][t])
             rows_ref.append(r)
-            choice(r, int(hist[t + 1, 0]))
-        else:
-            dec.forward([(tok, c)], logits="none")
     row = compare(np.array(rows_gpu), np.array(rows_ref), rel_range=REL)
     row.update(type="logit_parity", case=wl.name, path="seq0", greedy_flips=flips, greedy_flips_outside_gate=bad)
     report(row)

@@ -136,15 +136,14 @@ def test_ragged_decode_matches_oracle(run, which):
     choice(ref_last, int(hist[0, seq]))
     for t in range(wl.decode_steps):
         tok = np.array([hist[t, seq]])
+        r = dec.forward([(tok, c)], logits="all")[0]
+        choice(r, int(hist[t + 1, seq]))  # every step's greedy choice
         if t in CHECK_STEPS:
-            r = dec.forward([(tok, c)], logits="all")[0]
             rows_gpu.append(out["keep"][t][k])
             rows_ref.append(r)
-            choice(r, int(hist[t + 1, seq]))
-        else:
-            dec.forward([(tok, c)], logits="none")
     row = compare(np.array(rows_gpu), np.array(rows_ref), rel_range=REL)
     row.update(type="logit_parity", case=wl.name, path=f"{which}_seq{seq}_ctx{L}", greedy_flips=flips,
+               greedy_steps_checked=wl.decode_steps + 1,
                greedy_flips_outside_gate=bad)
     report(row)
     assert row["pass"], row

@@ -24,24 +24,40 @@ from synthetic import MODELS, WORKLOADS, make_prompts, make_weights
 FP32_TOL = 1e-3
 REL_RANGE = 2e-2
 
+_R = dict(gains="random")  # per-channel norm gains, uniform in [0.5, 1.5]
 VARIANTS = {
+    # the two-layer configuration as stated: float32, gains 1.0
     "f32": MODELS["tiny_f32"],
-    "bf16_f16kv": dataclasses.replace(MODELS["tiny_f32"], name="tiny_bf16", weight_dtype="bf16", kv_dtype="f16"),
-    "uint4_f16kv": dataclasses.replace(MODELS["tiny_f32"], name="tiny_uint4", weight_dtype="uint4", kv_dtype="f16"),
+    "f32_gains": dataclasses.replace(MODELS["tiny_f32"], name="tiny_f32_gains", **_R),
+    "bf16_f16kv": dataclasses.replace(MODELS["tiny_f32"], name="tiny_bf16", weight_dtype="bf16", kv_dtype="f16", **_R),
+    "uint4_f16kv": dataclasses.replace(MODELS["tiny_f32"], name="tiny_uint4", weight_dtype="uint4", kv_dtype="f16",
+                                       **_R),
     "int4sym_f16kv": dataclasses.replace(MODELS["tiny_f32"], name="tiny_int4sym", weight_dtype="int4sym",
-                                         kv_dtype="f16"),
-    "bf16_f32kv": dataclasses.replace(MODELS["tiny_f32"], name="tiny_bf16_f32kv", weight_dtype="bf16", kv_dtype="f32"),
+                                         kv_dtype="f16", **_R),
+    "bf16_f32kv": dataclasses.replace(MODELS["tiny_f32"], name="tiny_bf16_f32kv", weight_dtype="bf16", kv_dtype="f32",
+                                      **_R),
     # eight query heads per KV head (the largest group the decode attention takes)
     "gqa8_bf16_f16kv": dataclasses.replace(MODELS["tiny_f32"], name="tiny_gqa8", n_heads=16, n_kv_heads=2,
-                                           weight_dtype="bf16", kv_dtype="f16"),
+                                           weight_dtype="bf16", kv_dtype="f16", **_R),
     # one KV head per query head: grouped-query attention reduced to multi-head attention
     "mha_bf16_f16kv": dataclasses.replace(MODELS["tiny_f32"], name="tiny_mha", n_kv_heads=4, weight_dtype="bf16",
-                                          kv_dtype="f16"),
+                                          kv_dtype="f16", **_R),
+    # the other block sizes the library accepts
+    "bf16_f16kv_b32": dataclasses.replace(MODELS["tiny_f32"], name="tiny_bf16_b32", weight_dtype="bf16",
+                                          kv_dtype="f16", block_tokens=32, **_R),
+    "bf16_f16kv_b64": dataclasses.replace(MODELS["tiny_f32"], name="tiny_bf16_b64", weight_dtype="bf16",
+                                          kv_dtype="f16", block_tokens=64, **_R),
+    "f32_b32": dataclasses.replace(MODELS["tiny_f32"], name="tiny_f32_b32", block_tokens=32, **_R),
+    # the other head size the library accepts (Q width 256, four times d_model)
+    "hd64_bf16_f16kv": dataclasses.replace(MODELS["tiny_f32"], name="tiny_hd64", head_dim=64, weight_dtype="bf16",
+                                           kv_dtype="f16", **_R),
+    "hd64_f32": dataclasses.replace(MODELS["tiny_f32"], name="tiny_hd64_f32", head_dim=64, **_R),
 }
 
 
 def gate(name):
-    return dict(tol=FP32_TOL) if name == "f32" else dict(rel_range=REL_RANGE)
+    return dict(tol=FP32_TOL) if VARIANTS[name].weight_dtype == "f32" and VARIANTS[name].kv_dtype == "f32" \
+        else dict(rel_range=REL_RANGE)
 
 
 @pytest.fixture(scope="module", params=list(VARIANTS))
