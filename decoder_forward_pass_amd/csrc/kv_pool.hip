@@ -125,6 +125,9 @@ int dec_pool_register(dec_block_pool* p, int32_t id, uint64_t key, int32_t* cano
   if (!p || !valid(p, id) || p->b[id].state != dec_block_pool::USED) return perr(p, DEC_E_BLOCK, "register: not an allocated block");
   auto& k = p->b[id];
   if (k.fill != p->block_tokens) return perr(p, DEC_E_ARG, "register: only full blocks are registered");
+  // a block holds one prefix, so it has one key: a second, different key would leave the first
+  // key's entry naming the block after it is freed and handed to another sequence
+  if (k.registered && k.key != key) return perr(p, DEC_E_ARG, "register: block already registered under another key");
   auto it = p->index.find(key);
   if (it != p->index.end() && it->second != id) {
     if (canonical) *canonical = it->second;  // the key's first block stays its entry
@@ -144,6 +147,11 @@ int dec_pool_lookup(dec_block_pool* p, uint64_t key, int32_t* id) {
   if (it == p->index.end()) return DEC_OK;
   const int32_t i = it->second;
   auto& k = p->b[i];
+  if (k.state == dec_block_pool::FREE || !k.registered || k.key != key) {
+    // (an entry whose block was freed or re-keyed is stale: a miss, and it is dropped)
+    p->index.erase(it);
+    return DEC_OK;
+  }
   if (k.state == dec_block_pool::CACHED) {  // reacquire a cached block
     p->lru.erase(k.lru);
     k.state = dec_block_pool::USED;

@@ -365,9 +365,10 @@ int dec_sample(dec_ctx* ctx, void* stream, int32_t n_seqs, const float* logits, 
  *             block stays full)
  *   register: index a full USED block under a prefix key; when the key is
  *             already indexed to another block that block stays its entry and
- *             *canonical names it
+ *             *canonical names it; a block registered under one key is refused
+ *             another (DEC_E_ARG; the same key again is accepted)
  *   lookup:   *id = the block indexed under key (retained; a CACHED block is
- *             reacquired with reference 1), or -1
+ *             reacquired with reference 1), or -1; a FREE block is never returned
  * Errors: DEC_E_ARG, DEC_E_CAPACITY, DEC_E_BLOCK (an id that is not USED);
  * a failed call changes nothing. Not thread-safe: one caller at a time.
  */

@@ -116,3 +116,35 @@ def test_prefix_key_names_the_whole_prefix():
     assert k1 != B.dec_prefix_key(0, [1, 2, 4, 3])  # order matters
     assert B.dec_prefix_key(k1, [5, 6]) != B.dec_prefix_key(B.dec_prefix_key(0, [9, 9, 9, 9]), [5, 6])
     assert B.dec_prefix_key(0, []) != B.dec_prefix_key(1, [])
+
+
+def test_a_registered_block_keeps_its_one_key():
+    # a second key for a block would leave the first key's entry naming the block after it is
+    # freed and handed to another sequence, whose K/V a later lookup would then share
+    for cache in (True, False):
+        p = pool(2, bt=4, cache=cache)
+        (i,) = p.alloc(1)
+        p.set_fill(i, 4)
+        assert p.register(i, 101) == i
+        assert p.register(i, 101) == i  # the same key again is fine
+        with pytest.raises(B.DecError) as e:
+            p.register(i, 202)
+        assert e.value.code == B.DEC_E_ARG
+        assert p.lookup(202) == -1
+        p.release(i)
+
+
+def test_lookup_never_returns_a_free_block():
+    # without prefix caching a released registered block is freed and its key dropped: a
+    # lookup misses, and the block goes to a new owner without the old key naming it
+    p = pool(2, bt=4, cache=False)
+    (i,) = p.alloc(1)
+    p.set_fill(i, 4)
+    p.register(i, 7)
+    p.release(i)
+    assert p.info(i)[0] == FREE
+    assert p.lookup(7) == -1
+    a = p.alloc(2)
+    assert i in a
+    assert p.lookup(7) == -1
+    assert p.info(i)[:2] == (USED, 1)

@@ -1,9 +1,12 @@
-"""Checkpoint loading on the host (dec_config_from_json, dec_load_safetensors): the Qwen3 config
-whitelist of "A real model in our own decoder" (qwen_config) and the safetensors reader rules
-of the same page (section "A safetensors file is a JSON header and raw bytes") and of "Candle
-model runner" 2.3 (test safetensors_reader_rules: offsets from the data buffer, F16 and BF16
-widening, gaps and trailing bytes refused; config_refuses_what_the_engine_cannot_run). Files are
-synthetic: the tiny decoder's seeded weights written under Hugging Face's Qwen3 names."""
+"""Checkpoint loading on the host (dec_config_from_json, dec_load_safetensors): the Qwen3
+settings of "A real model in our own decoder" and the safetensors rules of the same page
+(section "A safetensors file is a JSON header and raw bytes") and of "Candle model runner" 2.3
+(test safetensors_reader_rules: offsets from the data buffer, F16 and BF16 widening, gaps and
+trailing bytes refused; config_refuses_what_the_engine_cannot_run), and the two int4 routes of
+"Candle model runner" 2.5 (an int4 file with <name>.qweight / <name>.scales and metadata quant =
+"int4-g32-sym", or float weights quantised at load; test int4_runner_matches_its_dequantized_
+model: the two agree bit for bit). Files are synthetic: seeded weights written under Hugging
+Face's Qwen3 names."""
 
 import dataclasses
 import json
@@ -24,18 +27,34 @@ PER = ["input_layernorm", "self_attn.q_proj", "self_attn.k_proj", "self_attn.v_p
 OURS = ["attn_norm", "wq", "wk", "wv", "q_norm", "k_norm", "wo", "ffn_norm", "w_gate", "w_up", "w_down"]
 
 
+def pack_nibbles(q):
+    """int8 values in [-8, 7] [out, in] -> bytes [out, in/2], column 2b low, 2b+1 high."""
+    u = (q.astype(np.int16) & 15).astype(np.uint8)
+    return (u[:, 0::2] | (u[:, 1::2] << 4)).astype(np.uint8)
+
+
 def hf_tensors(w, bf16_bits=False):
-    """name -> (dtype, numpy array) in checkpoint form."""
+    """name -> (dtype, numpy array) in checkpoint form; int4sym weights as an int4 file."""
     out = {}
+    int4 = w.shape.weight_dtype == "int4sym"
 
-    def mat(a):
-        return ("BF16", np.asarray(a, np.uint16)) if bf16_bits else ("F32", np.asarray(a, np.float32))
+    def put(base, a):
+        if int4:
+            out[base + ".qweight"] = ("U8", pack_nibbles(a.q))
+            out[base + ".scales"] = ("F16", a.scale.view(np.float16))
+        elif bf16_bits:
+            out[base + ".weight"] = ("BF16", np.asarray(a, np.uint16))
+        else:
+            out[base + ".weight"] = ("F32", np.asarray(a, np.float32))
 
-    out["model.embed_tokens.weight"] = mat(w.embed)
+    put("model.embed_tokens", w.embed)
     for l, layer in enumerate(w.layers):
         for hf, ours in zip(PER, OURS):
             a = layer[ours]
-            out[f"model.layers.{l}.{hf}.weight"] = ("F32", a) if a.ndim == 1 else mat(a)
+            if getattr(a, "ndim", 2) == 1:
+                out[f"model.layers.{l}.{hf}.weight"] = ("F32", a)
+            else:
+                put(f"model.layers.{l}.{hf}", a)
     out["model.norm.weight"] = ("F32", w.final_norm)
     return out
 
@@ -92,7 +111,7 @@ def test_tied_lm_head_must_equal_the_embedding(tmp_path):
     e[3, 5] += 1.0
     t["lm_head.weight"] = ("F32", e)
     write_st(p, t)
-    with pytest.raises(B.DecError, match="tied weights differ"):
+    with pytest.raises(B.DecError, match="differs from the tied embedding"):
         B.dec_load_safetensors(str(p), cfg_for(TINY))
 
 
@@ -112,21 +131,34 @@ def _refused(tmp_path, match, **kw):
 def test_reader_refusals(tmp_path):
     w = make_weights(TINY)
     good = json.dumps({"x": {"dtype": "F32", "shape": [1], "data_offsets": [0, 4]}})
-    _refused(tmp_path, "payload", extra=b"\0")  # trailing bytes
-    _refused(tmp_path, "must be an object", header_text=b"[1, 2]")
+    _refused(tmp_path, "payload bytes belong to no tensor", extra=b"\0")  # trailing bytes
+    _refused(tmp_path, "header JSON is not an object", header_text=b"[1, 2]")
     _refused(tmp_path, "duplicate key", header_text=('{"a": 1, "a": 2}').encode())
-    _refused(tmp_path, "metadata", meta={"format": 3})
-    _refused(tmp_path, "unknown or unsupported dtype", mutate=lambda t: t.update(
+    _refused(tmp_path, "__metadata__ entry format is not a string", meta={"format": 3})
+    _refused(tmp_path, "quant format int8 is not supported", meta={"quant": "int8"})
+    _refused(tmp_path, "element type F64 is not supported", mutate=lambda t: t.update(
         {"model.norm.weight": ("F64", np.asarray(w.final_norm, np.float64))}))
-    _refused(tmp_path, "missing checkpoint tensor", mutate=lambda t: t.pop("model.layers.1.mlp.up_proj.weight"))
-    _refused(tmp_path, "unexpected checkpoint tensor", mutate=lambda t: t.update(
+    _refused(tmp_path, "checkpoint lacks model.layers.1.mlp.up_proj.weight",
+             mutate=lambda t: t.pop("model.layers.1.mlp.up_proj.weight"))
+    _refused(tmp_path, "q_proj.bias is not a tensor of this Qwen3 decoder", mutate=lambda t: t.update(
         {"model.layers.0.self_attn.q_proj.bias": ("F32", np.zeros(4, np.float32))}))
-    _refused(tmp_path, "shape mismatch", mutate=lambda t: t.update(
+    _refused(tmp_path, r"k_proj.weight must be a float \[64, 64\], not \[8, 64\]", mutate=lambda t: t.update(
         {"model.layers.0.self_attn.k_proj.weight": ("F32", np.zeros((8, TINY.d_model), np.float32))}))
+    # int4 tensors in a file that does not say it is an int4 file
+    _refused(tmp_path, "qweight is not a tensor", mutate=lambda t: t.update(
+        {"model.layers.0.mlp.up_proj.qweight": ("U8", np.zeros((192, 32), np.uint8))}))
     p = tmp_path / "h.safetensors"
-    with open(p, "wb") as f:  # header length beyond the file
+    with open(p, "wb") as f:  # header size beyond the file
         f.write(struct.pack("<Q", 1000) + good.encode())
-    with pytest.raises(B.DecError, match="header length"):
+    with pytest.raises(B.DecError, match="runs past the"):
+        B.dec_load_safetensors(str(p), cfg_for(TINY))
+    with open(p, "wb") as f:  # header size beyond the reader's bound
+        f.write(struct.pack("<Q", (1 << 24) + 1) + good.encode())
+    with pytest.raises(B.DecError, match="outside"):
+        B.dec_load_safetensors(str(p), cfg_for(TINY))
+    with open(p, "wb") as f:  # no room for the header size
+        f.write(b"\1\0\0")
+    with pytest.raises(B.DecError, match="no room for the 8-byte header size"):
         B.dec_load_safetensors(str(p), cfg_for(TINY))
 
 
@@ -138,7 +170,8 @@ def test_offsets_must_tile_the_data_buffer(tmp_path):
     data = open(p, "rb").read()
     n = struct.unpack("<Q", data[:8])[0]
     body = data[8 + n:]
-    for how, m in (("gap", "gap"), ("overlap", "overlap"), ("count", "byte count")):
+    for how, m in (("gap", "runs past the end of the payload"), ("overlap", "share bytes"),
+                   ("count", "bytes stored, 256 needed")):
         h = json.loads(json.dumps(hdr))
         name = "model.norm.weight"
         s0, e0 = h[name]["data_offsets"]
@@ -174,8 +207,9 @@ def test_config_gives_the_0_6b_shape():
 @pytest.mark.parametrize("key,value", [("rope_scaling", {"rope_type": "yarn", "factor": 4.0}),
                                        ("use_sliding_window", True), ("model_type", "llama"),
                                        ("tie_word_embeddings", False), ("attention_bias", True),
-                                       ("rms_norm_eps", 1e-5), ("hidden_act", "gelu"), ("head_dim", 0),
-                                       ("num_hidden_layers", None)])
+                                       ("rms_norm_eps", 0.0), ("rms_norm_eps", None), ("hidden_act", "gelu"),
+                                       ("head_dim", 0), ("num_hidden_layers", None), ("attention_dropout", 0.1),
+                                       ("rope_theta", 1.0)])
 def test_config_refuses_what_the_library_cannot_run(key, value):
     c = dict(QWEN)
     if value is None:
@@ -191,3 +225,72 @@ def test_config_must_be_json():
     with pytest.raises(B.DecError) as e:
         B.dec_config_from_json(b'{"model_type": "qwen3",', B.dec_config())
     assert e.value.code == B.DEC_E_ARG
+
+
+def test_config_takes_the_files_eps():
+    c = dict(QWEN, rms_norm_eps=1e-5)
+    cfg = B.dec_config()
+    B.dec_config_from_json(json.dumps(c).encode(), cfg)
+    assert abs(cfg.rms_eps - 1e-5) < 1e-12
+
+
+# ---- int4 ("Candle model runner" 2.5: an int4 file, or quantised at load) ------------------------
+
+INT4 = dataclasses.replace(TINY, weight_dtype="int4sym", gains="random")
+
+
+def test_int4_file_loads_into_the_int4_blob(tmp_path):
+    w = make_weights(INT4)
+    p = tmp_path / "q.safetensors"
+    write_st(p, hf_tensors(w), meta={"quant": "int4-g32-sym"})
+    cfg = cfg_for(INT4)
+    assert np.array_equal(B.dec_load_safetensors(str(p), cfg), pack_blob(cfg, w))
+
+
+def test_quantise_at_load_equals_the_int4_file_bit_for_bit(tmp_path):
+    # the same float32 weights: once quantised by the library while loading, once stored as an
+    # int4 file by the input generator's chooser
+    f32 = make_weights(dataclasses.replace(INT4, weight_dtype="f32"))
+    q = make_weights(INT4)
+    pf, pq = tmp_path / "f.safetensors", tmp_path / "q.safetensors"
+    write_st(pf, hf_tensors(f32))
+    write_st(pq, hf_tensors(q), meta={"quant": "int4-g32-sym"})
+    cfg = cfg_for(INT4)
+    a = B.dec_load_safetensors(str(pf), cfg)
+    b = B.dec_load_safetensors(str(pq), cfg)
+    assert np.array_equal(a, b)
+
+
+def test_int4_file_into_a_float32_blob_is_its_dequantised_twin(tmp_path):
+    import oracle.numerics as nx  # the oracle's dequantisation, q * s
+    w = make_weights(INT4)
+    p = tmp_path / "q.safetensors"
+    write_st(p, hf_tensors(w), meta={"quant": "int4-g32-sym"})
+    cfg = cfg_for(dataclasses.replace(INT4, weight_dtype="f32"))
+    blob = B.dec_load_safetensors(str(p), cfg)
+    twin = dataclasses.replace(w, embed=nx.dequant_int4_sym_g32(w.embed.q, w.embed.scale),
+                               layers=[{k: (nx.dequant_int4_sym_g32(v.q, v.scale) if hasattr(v, "q") else v)
+                                        for k, v in L.items()} for L in w.layers])
+    assert np.array_equal(blob, pack_blob(cfg, dataclasses.replace(twin, shape=dataclasses.replace(
+        INT4, weight_dtype="f32"))))
+
+
+def test_int4_file_refusals(tmp_path):
+    w = make_weights(INT4)
+    cfg = cfg_for(INT4)
+    p = tmp_path / "q.safetensors"
+
+    def refused(match, mutate):
+        t = hf_tensors(w)
+        mutate(t)
+        write_st(p, t, meta={"quant": "int4-g32-sym"})
+        with pytest.raises(B.DecError, match=match):
+            B.dec_load_safetensors(str(p), cfg)
+
+    refused("lacks model.layers.0.self_attn.o_proj.qweight or", lambda t: t.pop("model.layers.0.self_attn.o_proj.qweight"))
+    refused(r"scales must be F16 \[64, 6\]", lambda t: t.update(
+        {"model.layers.1.mlp.down_proj.scales": ("BF16", np.zeros((64, 6), np.uint16))}))
+    refused(r"qweight must be U8", lambda t: t.update(
+        {"model.layers.1.mlp.down_proj.qweight": ("U8", np.zeros((64, 32), np.uint8))}))
+    refused("model.layers.0.mlp.up_proj.weight is not a tensor", lambda t: t.update(
+        {"model.layers.0.mlp.up_proj.weight": ("F32", np.zeros((192, 64), np.float32))}))
