@@ -85,7 +85,7 @@ DEC_SAMPLE_MAX_NUCLEUS = 1024
 
 EXPORTS = ["dec_check_config", "dec_weight_bytes", "dec_weight_count", "dec_weight_entry", "dec_kv_pool_bytes",
            "dec_workspace_bytes", "dec_init", "dec_free", "dec_last_error", "dec_prefill", "dec_decode_step",
-           "dec_check_step", "dec_debug_dequant", "dec_quantize_int4_sym", "dec_rng_stream", "dec_sample", "dec_pool_create",
+           "dec_decode_step_static", "dec_check_step", "dec_debug_dequant", "dec_quantize_int4_sym", "dec_rng_stream", "dec_sample", "dec_pool_create",
            "dec_pool_destroy", "dec_pool_last_error", "dec_pool_alloc", "dec_pool_retain", "dec_pool_release",
            "dec_pool_set_fill", "dec_pool_register", "dec_pool_lookup", "dec_pool_block_info", "dec_pool_counts",
            "dec_prefix_key", "dec_kv_export_bytes", "dec_kv_export", "dec_kv_import", "dec_config_from_json",
@@ -116,6 +116,7 @@ def _load():
         "dec_last_error": (ctypes.c_char_p, [VP]),
         "dec_prefill": (ctypes.c_int, [VP, VP, I32, i32p, i32p, i32p, i32p, I32, I32, VP, VP]),
         "dec_decode_step": (ctypes.c_int, [VP, VP, I32, i32p, VP, i32p, i32p, I32, VP, VP]),
+        "dec_decode_step_static": (ctypes.c_int, [VP, VP, I32, i32p, VP, i32p, i32p, I32, VP, VP]),
         "dec_check_step": (ctypes.c_int, [cfgp, I32, i32p, i32p, i32p, i32p, I32, I32, ctypes.c_char_p, SZ]),
         "dec_debug_dequant": (ctypes.c_int, [VP, VP, ctypes.c_int, VP]),
         "dec_quantize_int4_sym": (ctypes.c_int, [VP, VP, ctypes.c_int64, ctypes.c_int64, VP, VP]),
@@ -227,13 +228,15 @@ def dec_prefill(ctx: int, stream: int, start, n_new, tokens, block_tables, logit
 
 
 def dec_decode_step(ctx: int, stream: int, positions, block_tables, logits: int, next_tokens: int = 0,
-                    tokens_host=None, tokens_device: int = 0) -> None:
+                    tokens_host=None, tokens_device: int = 0, static: bool = False) -> None:
+    """dec_decode_step, or dec_decode_step_static (scratch in the library's static device array)."""
     pos, pp = _i32(positions)
     _, tp = _i32(tokens_host)
     bt = np.ascontiguousarray(np.asarray(block_tables, dtype=np.int32))
     bp = bt.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
-    _check(_lib.dec_decode_step(ctx, stream or None, len(pos), tp, tokens_device or None, pp, bp, bt.shape[1],
-                                logits or None, next_tokens or None), ctx)
+    fn = _lib.dec_decode_step_static if static else _lib.dec_decode_step
+    _check(fn(ctx, stream or None, len(pos), tp, tokens_device or None, pp, bp, bt.shape[1], logits or None,
+              next_tokens or None), ctx)
 
 
 def dec_check_step(cfg: dec_config, start, n_new, tokens, block_tables, logits_mode: int):

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -153,9 +154,13 @@ struct Ws {
   bool flash;  // prefill attention by the MFMA tile kernel
 };
 
-Ws ws_layout(const dec_config& c) {
+// `decode_rows` > 0: only the regions a decode step of that many sequences uses (no RoPE table,
+// no prefill partials, no sampler regions), laid out for those rows: the static scratch of
+// dec_decode_step_static
+Ws ws_layout(const dec_config& c, int decode_rows = 0) {
   Ws w{};
-  const size_t R = (size_t)c.max_rows, S = (size_t)c.max_seqs;
+  const bool dec_only = decode_rows > 0;
+  const size_t R = dec_only ? (size_t)decode_rows : (size_t)c.max_rows, S = dec_only ? (size_t)decode_rows : (size_t)c.max_seqs;
   const size_t d = c.d_model, D = c.head_dim, H = c.n_heads;
   const size_t qw = H * D, qkvw = qw + 2 * (size_t)c.n_kv_heads * D, ff = c.ff_hidden;
   w.act_bytes = c.weight_dtype == DEC_F32 ? 4 : 2;
@@ -174,7 +179,7 @@ Ws ws_layout(const dec_config& c) {
     off = align_up(off + bytes);
     return o;
   };
-  w.rope = take((size_t)c.max_context * (D / 2) * sizeof(float2));
+  w.rope = take(dec_only ? 0 : (size_t)c.max_context * (D / 2) * sizeof(float2));
   w.meta = take(w.meta_ints * 4);
   w.x = take(R * d * 4);
   w.h = take(R * d * w.act_bytes);
@@ -185,15 +190,15 @@ Ws ws_layout(const dec_config& c) {
   // split-key partials: only prefill calls that take the per-row kernel (float32 pool, or a
   // head shape the tile kernel does not take) use them; decode merges its chunks in-block
   w.flash = c.kv_dtype == DEC_F16 && attn_prefill_supported(c.head_dim, c.n_heads / c.n_kv_heads);
-  const size_t prow = w.flash ? 0 : R;
+  const size_t prow = w.flash || dec_only ? 0 : R;
   w.part = take(prow * H * (size_t)w.nch_max * (D + 2) * 4);
   // decode rows split into segments: one state per (row, KV head, segment), plus the new key's
   w.dpart = take(S * H * (size_t)w.dslots * (D + 2) * 4);
   w.amax = take(argmax_scratch_bytes((int)R, (int)S));
   w.ssq = take(S * (d / 16) * 4);  // decode: sums of squares of the residual in 16-column partials
   w.xg = take(S * d * 2);          // decode: bf16(residual * the next norm's gain)
-  w.samp = take(S * sizeof(SampleSeq));           // sampling: per-sequence parameters and history
-  w.counts = take(S * (size_t)c.vocab * 4);       // sampling: per-sequence count table (kept zero)
+  w.samp = take(dec_only ? 0 : S * sizeof(SampleSeq));       // sampling: per-sequence parameters and history
+  w.counts = take(dec_only ? 0 : S * (size_t)c.vocab * 4);   // sampling: per-sequence count table (kept zero)
   w.total = off;
   return w;
 }
@@ -277,8 +282,50 @@ struct dec_ctx {
   int slot;
   SampleSeq* samp_staging;  // pinned: the last dec_sample call's parameters
   hipEvent_t samp_ev;       // that upload's completion
+  void* scratch;            // device address of this device's static scratch (dec_decode_step_static)
+  std::string scratch_err;  // why it is unknown, when it is
   std::string err;
 };
+
+namespace {
+
+// The static scratch of dec_decode_step_static: per-call device memory (metadata, activations,
+// split attention states, greedy candidates) for callers that cannot allocate. One copy per
+// device, held until the process ends; every call on a device shares it. Host code never passes
+// the array's name to a kernel or a copy (there it is a host-side stand-in): it uses the device
+// address hipGetSymbolAddress gives for the current device, kept per device.
+constexpr size_t kStaticScratchBytes = DEC_STATIC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices];
+
+// The current device's static scratch address (looked up once per device), or nullptr with `why`.
+void* static_scratch(std::string* why) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *why = std::string("hipGetDevice: ") + hipGetErrorString(e);
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *why = "device index beyond the static scratch table";
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      *why = std::string("hipGetSymbolAddress: ") + hipGetErrorString(e);
+      return nullptr;
+    }
+    g_scratch_addr[dev] = p;
+  }
+  return g_scratch_addr[dev];
+}
+
+}  // namespace
 
 namespace {
 
@@ -301,9 +348,10 @@ const float* gainp(const dec_ctx* c, int idx) { return (const float*)(c->w + c->
   } while (0)
 
 // Pack the call's metadata into a pinned slot, upload it, and describe it for the kernels.
-int upload_meta(dec_ctx* ctx, hipStream_t st, int32_t S, const int32_t* start, const int32_t* n_new,
-                const int32_t* tokens, const int32_t* tables, int32_t max_blocks, int32_t mode, BatchDev* b,
-                int* max_ctx) {
+// `base` / `ws`: the scratch memory of the call (the workspace, or the static scratch) and its layout.
+int upload_meta(dec_ctx* ctx, uint8_t* base, const Ws& ws, hipStream_t st, int32_t S, const int32_t* start,
+                const int32_t* n_new, const int32_t* tokens, const int32_t* tables, int32_t max_blocks, int32_t mode,
+                BatchDev* b, int* max_ctx) {
   const dec_config& c = ctx->cfg;
   int32_t N = 0, stride = 1, mc = 0;
   for (int s = 0; s < S; ++s) {
@@ -319,7 +367,7 @@ int upload_meta(dec_ctx* ctx, hipStream_t st, int32_t S, const int32_t* start, c
   const size_t o_tok = 0, o_pos = N, o_seq = 2 * (size_t)N, o_sst = 3 * (size_t)N, o_snn = o_sst + S,
                o_sr0 = o_snn + S, o_out = o_sr0 + S, o_til = o_out + n_out, o_tbl = o_til + 2 * (size_t)n_tiles;
   // decode attention work items: only when a row has more keys than one segment takes
-  const int32_t sk = ctx->ws.seg_keys;
+  const int32_t sk = ws.seg_keys;
   int32_t n_items = 0;
   if (!n_new) {
     bool split = false;
@@ -329,7 +377,7 @@ int upload_meta(dec_ctx* ctx, hipStream_t st, int32_t S, const int32_t* start, c
   }
   const size_t o_itm = (o_tbl + (size_t)S * stride + 3) & ~(size_t)3;  // 16-byte aligned
   const size_t total = o_itm + 4 * (size_t)n_items;
-  if (total > ctx->ws.meta_ints) return fail(&ctx->err, DEC_E_CAPACITY, "call metadata exceeds the workspace");
+  if (total > ws.meta_ints) return fail(&ctx->err, DEC_E_CAPACITY, "call metadata exceeds the workspace");
 
   const int slot = ctx->slot;
   ctx->slot = (slot + 1) % kSlots;
@@ -387,7 +435,7 @@ int upload_meta(dec_ctx* ctx, hipStream_t st, int32_t S, const int32_t* start, c
       e[3] = s;
     }
   }
-  int32_t* dm = (int32_t*)(ctx->wsp + ctx->ws.meta);
+  int32_t* dm = (int32_t*)(base + ws.meta);
   HIPCHECK(hipMemcpyAsync(dm, m, total * 4, hipMemcpyHostToDevice, st));
   HIPCHECK(hipEventRecord(ctx->ev[slot], st));
   b->row_tok = dm + o_tok;
@@ -469,25 +517,24 @@ void timing_end(dec_ctx* ctx, int cls, hipStream_t st, hipEvent_t start, hipEven
   } while (0)
 
 // The forward pass over the uploaded batch: embedding, layers, final norm + LM head, argmax.
-int run_forward(dec_ctx* ctx, hipStream_t st, const BatchDev& b, const int32_t* tok_dev, int max_ctx,
-                bool decode, float* logits, int32_t* next) {
+int run_forward(dec_ctx* ctx, uint8_t* base, const Ws& w, hipStream_t st, const BatchDev& b, const int32_t* tok_dev,
+                int max_ctx, bool decode, float* logits, int32_t* next) {
   const dec_config& c = ctx->cfg;
-  const Ws& w = ctx->ws;
   const int N = b.n_rows, d = c.d_model, H = c.n_heads, Hkv = c.n_kv_heads, D = c.head_dim;
   const int qw = H * D, qkvw = qw + 2 * Hkv * D, ff = c.ff_hidden;
   const bool act_bf16 = c.weight_dtype != DEC_F32;
   const bool kv_f16 = c.kv_dtype == DEC_F16;
-  float* x = (float*)(ctx->wsp + w.x);
-  void* h = ctx->wsp + w.h;
-  float* qkv = (float*)(ctx->wsp + w.qkv);
-  void* q = ctx->wsp + w.q;
-  void* o = ctx->wsp + w.o;
-  void* act = ctx->wsp + w.a;
-  float* part = (float*)(ctx->wsp + w.part);
-  float* dpart = (float*)(ctx->wsp + w.dpart);
-  float* ssq = (float*)(ctx->wsp + w.ssq);
-  uint16_t* xg = (uint16_t*)(ctx->wsp + w.xg);
-  const float2* rope = (const float2*)(ctx->wsp + w.rope);
+  float* x = (float*)(base + w.x);
+  void* h = base + w.h;
+  float* qkv = (float*)(base + w.qkv);
+  void* q = base + w.q;
+  void* o = base + w.o;
+  void* act = base + w.a;
+  float* part = (float*)(base + w.part);
+  float* dpart = (float*)(base + w.dpart);
+  float* ssq = (float*)(base + w.ssq);
+  uint16_t* xg = (uint16_t*)(base + w.xg);
+  const float2* rope = (const float2*)(ctx->wsp + ctx->ws.rope);
   PoolDev pool{ctx->pool, c.n_blocks, Hkv, c.block_tokens, D, __builtin_ctz((unsigned)c.block_tokens)};
   const int nch = (max_ctx + w.chunk - 1) / w.chunk;
   // Decode steps take the decode GEMM (K split inside a block) when the weight format has one.
@@ -587,7 +634,7 @@ int run_forward(dec_ctx* ctx, hipStream_t st, const BatchDev& b, const int32_t* 
     const int cand = dgemm && next && lmhead_decode_supported(c.weight_dtype, b.n_out, d)
                          ? lmhead_decode_parts(b.n_out, c.vocab)
                          : 0;
-    float* cand_v = (float*)(ctx->wsp + w.amax);
+    float* cand_v = (float*)(base + w.amax);
     int32_t* cand_i = (int32_t*)(cand_v + (size_t)b.n_out * std::max(cand, 1));
     if (cand) {
       g.am_v = cand_v;
@@ -601,10 +648,43 @@ int run_forward(dec_ctx* ctx, hipStream_t st, const BatchDev& b, const int32_t* 
     if (next && cand) {
       TLAUNCH(DEC_K_ARGMAX, launch_argmax_final(cand_v, cand_i, b.n_out, cand, next, st));
     } else if (next) {
-      TLAUNCH(DEC_K_ARGMAX, launch_argmax(logits, b.n_out, c.vocab, next, ctx->wsp + w.amax, st));
+      TLAUNCH(DEC_K_ARGMAX, launch_argmax(logits, b.n_out, c.vocab, next, base + w.amax, st));
     }
   }
   return DEC_OK;
+}
+
+}  // namespace
+
+namespace {
+
+// A decode step with its per-call scratch at `base` (layout `ws`); checks as dec_decode_step.
+int decode_step(dec_ctx* ctx, uint8_t* base, const Ws* ws, void* stream, int32_t n_seqs, const int32_t* tokens_host,
+                const int32_t* tokens_device, const int32_t* positions, const int32_t* block_tables, int32_t max_blocks,
+                float* logits, int32_t* next_tokens) {
+  if ((tokens_host == nullptr) == (tokens_device == nullptr))
+    return fail(&ctx->err, DEC_E_ARG, "exactly one of tokens_host and tokens_device must be given");
+  if (next_tokens && !logits) return fail(&ctx->err, DEC_E_ARG, "next_tokens needs logits");
+  const int mode = logits ? DEC_LOGITS_LAST : DEC_LOGITS_NONE;
+  int rc = check_step(ctx->cfg, n_seqs, positions, nullptr, tokens_host, block_tables, max_blocks, mode, &ctx->err);
+  if (rc) return rc;
+  Ws lw;
+  if (!ws) {  // the static scratch, laid out for this call's sequences
+    lw = ws_layout(ctx->cfg, n_seqs);
+    if (lw.total > kStaticScratchBytes)
+      return fail(&ctx->err, DEC_E_CAPACITY,
+                  "a decode step of %d sequences needs %zu bytes of scratch, above the %zu bytes of the static scratch",
+                  n_seqs, lw.total, kStaticScratchBytes);
+    if (!base) return fail(&ctx->err, DEC_E_HIP, "the static scratch's device address is unknown: %s", ctx->scratch_err.c_str());
+    ws = &lw;
+  }
+  hipStream_t st = (hipStream_t)stream;
+  BatchDev b{};
+  int max_ctx = 0;
+  rc = upload_meta(ctx, base, *ws, st, n_seqs, positions, nullptr, tokens_host, block_tables, max_blocks, mode, &b,
+                   &max_ctx);
+  if (rc) return rc;
+  return run_forward(ctx, base, *ws, st, b, tokens_device, max_ctx, true, logits, next_tokens);
 }
 
 }  // namespace
@@ -684,6 +764,7 @@ int dec_init(const dec_config* cfg, const void* weights, size_t weight_bytes, vo
   }
   ctx->samp_staging = nullptr;
   ctx->samp_ev = nullptr;
+  ctx->scratch = static_scratch(&ctx->scratch_err);  // (with the ctx's device current)
   ctx->embed = wmat(ctx, 0);
   for (int l = 0; l < cfg->n_layers; ++l) {
     const int b = 1 + l * kPerLayer;
@@ -807,28 +888,28 @@ int dec_prefill(dec_ctx* ctx, void* stream, int32_t n_seqs, const int32_t* start
   hipStream_t st = (hipStream_t)stream;
   BatchDev b{};
   int max_ctx = 0;
-  rc = upload_meta(ctx, st, n_seqs, start, n_new, tokens, block_tables, max_blocks, logits_mode, &b, &max_ctx);
+  rc = upload_meta(ctx, ctx->wsp, ctx->ws, st, n_seqs, start, n_new, tokens, block_tables, max_blocks, logits_mode, &b,
+                   &max_ctx);
   if (rc) return rc;
-  return run_forward(ctx, st, b, nullptr, max_ctx, false, logits_mode == DEC_LOGITS_NONE ? nullptr : logits,
-                     next_tokens);
+  return run_forward(ctx, ctx->wsp, ctx->ws, st, b, nullptr, max_ctx, false,
+                     logits_mode == DEC_LOGITS_NONE ? nullptr : logits, next_tokens);
 }
+
 
 int dec_decode_step(dec_ctx* ctx, void* stream, int32_t n_seqs, const int32_t* tokens_host,
                     const int32_t* tokens_device, const int32_t* positions, const int32_t* block_tables,
                     int32_t max_blocks, float* logits, int32_t* next_tokens) {
   if (!ctx) return fail(&g_err, DEC_E_ARG, "ctx is NULL");
-  if ((tokens_host == nullptr) == (tokens_device == nullptr))
-    return fail(&ctx->err, DEC_E_ARG, "exactly one of tokens_host and tokens_device must be given");
-  if (next_tokens && !logits) return fail(&ctx->err, DEC_E_ARG, "next_tokens needs logits");
-  const int mode = logits ? DEC_LOGITS_LAST : DEC_LOGITS_NONE;
-  int rc = check_step(ctx->cfg, n_seqs, positions, nullptr, tokens_host, block_tables, max_blocks, mode, &ctx->err);
-  if (rc) return rc;
-  hipStream_t st = (hipStream_t)stream;
-  BatchDev b{};
-  int max_ctx = 0;
-  rc = upload_meta(ctx, st, n_seqs, positions, nullptr, tokens_host, block_tables, max_blocks, mode, &b, &max_ctx);
-  if (rc) return rc;
-  return run_forward(ctx, st, b, tokens_device, max_ctx, true, logits, next_tokens);
+  return decode_step(ctx, ctx->wsp, &ctx->ws, stream, n_seqs, tokens_host, tokens_device, positions, block_tables,
+                     max_blocks, logits, next_tokens);
+}
+
+int dec_decode_step_static(dec_ctx* ctx, void* stream, int32_t n_seqs, const int32_t* tokens_host,
+                           const int32_t* tokens_device, const int32_t* positions, const int32_t* block_tables,
+                           int32_t max_blocks, float* logits, int32_t* next_tokens) {
+  if (!ctx) return fail(&g_err, DEC_E_ARG, "ctx is NULL");
+  return decode_step(ctx, (uint8_t*)ctx->scratch, nullptr, stream, n_seqs, tokens_host, tokens_device, positions,
+                     block_tables, max_blocks, logits, next_tokens);
 }
 
 void dec_rng_stream(uint64_t seed, uint64_t purpose, uint64_t state_inc[2]) {

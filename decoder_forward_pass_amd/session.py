@@ -110,13 +110,15 @@ class Session:
         return logits
 
     def decode_step(self, positions, block_tables, *, tokens_host=None, tokens_device=None, logits=None,
-                    next_tokens=None):
+                    next_tokens=None, static: bool = False):
+        """One dec_decode_step call (dec_decode_step_static with ``static``); returns the logits."""
         n = len(positions)
         if logits is None:
             logits = torch.empty((n, self.vocab), dtype=torch.float32, device=self.device)
         B.dec_decode_step(self.ctx, self.stream, positions, block_tables, logits.data_ptr(),
                           next_tokens.data_ptr() if next_tokens is not None else 0, tokens_host=tokens_host,
-                          tokens_device=tokens_device.data_ptr() if tokens_device is not None else 0)
+                          tokens_device=tokens_device.data_ptr() if tokens_device is not None else 0,
+                          static=static)
         return logits
 
     def sample(self, logits, params, history, ids, rng, next_ids=None, logprob=None):

@@ -234,6 +234,27 @@ int dec_decode_step(dec_ctx* ctx, void* stream, int32_t n_seqs, const int32_t* t
                     int32_t* next_tokens);
 
 /*
+ * dec_decode_step for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc). The same
+ * kernels, arguments, checks and results as dec_decode_step, bit for bit, but the
+ * step's per-call scratch (its uploaded metadata, the activations, the split
+ * attention states and the greedy candidates) lives in a static device array of
+ * DEC_STATIC_SCRATCH_BYTES that the library holds on each device until the
+ * process ends, not in the ctx's workspace (the ctx's workspace still holds the
+ * RoPE table). Nothing is allocated and nothing needs to start at zero.
+ * Every call on one device shares that device's array: calls that overlap on a
+ * device (on different streams, or from several ctxs or threads without
+ * ordering) race and give wrong results. DEC_E_CAPACITY when the step needs more
+ * than DEC_STATIC_SCRATCH_BYTES (the need grows with n_seqs, the model's widths
+ * and max_context); DEC_E_HIP when the array's device address is unknown.
+ */
+#define DEC_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+int dec_decode_step_static(dec_ctx* ctx, void* stream, int32_t n_seqs, const int32_t* tokens_host,
+                           const int32_t* tokens_device, const int32_t* positions,
+                           const int32_t* block_tables, int32_t max_blocks, float* logits,
+                           int32_t* next_tokens);
+
+/*
  * Host-only validation of a step, exactly as dec_prefill performs it before
  * enqueuing anything (for callers and tests without a GPU). For a decode step
  * pass n_new = NULL (one token each) and positions as start. tokens may be
