@@ -61,6 +61,157 @@ struct BigRowsB {
 
 }  // namespace
 
+// The epilogue of a block's tile from its waves' accumulators: wave (wm, wn) holds rows
+// m0 + 32 NBI wm .. + 32 NBI (NBI blocks of 32) and the four 32-column blocks of brow_of.
+template <int WF, int EPI, int D, bool KV_F16, int NBI>
+__device__ __forceinline__ void big_epilogue(const GemmArgs& a, const QkRopeArgs& qk, f32x16 (&acc)[NBI][4], int m0,
+                                             int n0, int wm, int wn, int lane, const int* s_pos,
+                                             const int64_t* s_blk) {
+  // lane holds column fr of each 32 x 32 block, rows 8 g + 4 (lane / 32) + r
+  const int fr = lane & 31;
+  const int M = a.M;
+  const int rbase = m0 + wm * (32 * NBI) + (lane >> 5) * 4;
+  auto row_of = [&](int bi, int i) { return rbase + bi * 32 + 8 * (i >> 2) + (i & 3); };
+  if constexpr (EPI == EPI_STORE || EPI == EPI_RESID) {
+    // per 32 x 32 block: the 16 residual values are all requested before any is updated
+#pragma unroll
+    for (int bi = 0; bi < NBI; ++bi)
+#pragma unroll
+      for (int bj = 0; bj < 4; ++bj) {
+        const int n = n0 + wn * 128 + bj * 32 + fr;
+        const int nc = min(n, a.N - 1);
+        float xo[16];
+        if constexpr (EPI == EPI_RESID) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) xo[i] = ((const float*)a.C)[(int64_t)min(row_of(bi, i), M - 1) * a.ldc + nc];
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int m = row_of(bi, i);
+          if (m < M && n < a.N) {
+            float* c = (float*)a.C + (int64_t)m * a.ldc + n;
+            if constexpr (EPI == EPI_STORE)
+              *c = acc[bi][bj][i];
+            else
+              *c = xo[i] + acc[bi][bj][i];
+          }
+        }
+      }
+  } else if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+    for (int bi = 0; bi < NBI; ++bi)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int m = row_of(bi, i);
+        if (m >= M) continue;
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj) {
+          const int f = n0 + wn * 64 + bj * 32 + fr;
+          if (f >= a.N) continue;
+          const float g = acc[bi][bj][i], u = acc[bi][bj + 2][i];
+          const float y = g / (1.0f + __expf(-g)) * u;
+          if (a.c_bf16)
+            ((uint16_t*)a.C)[(int64_t)m * a.ldc + f] = f32_to_bf16_bits(y);
+          else
+            ((float*)a.C)[(int64_t)m * a.ldc + f] = y;
+        }
+      }
+  } else {
+    // Q|K|V: heads of D channels; a head spans BPH 32-column blocks, HPW heads per wave
+    constexpr int BPH = D >= 32 ? D / 32 : 1, HPW = 128 / D, HALF = D / 2;
+    const int H = qk.n_heads, Hkv = qk.n_kv_heads;
+    const int hw0 = (n0 + wn * 128) / D;  // global head index of the wave's first head
+    // this lane's channels of a head are b * 32 + fr (D = 32: fr); their q and k gains
+    float gq[BPH], gk[BPH];
+#pragma unroll
+    for (int b = 0; b < BPH; ++b) {
+      gq[b] = qk.q_norm[b * 32 + fr];
+      gk[b] = qk.k_norm[b * 32 + fr];
+    }
+    static_for<2 * NBI>([&](auto q_c) {
+      constexpr int bi = decltype(q_c)::value >> 1, i0 = (decltype(q_c)::value & 1) * 8;
+      // 8 rows' positions, blocks and rotation factors, requested together
+      int pos_r[8];
+      int64_t blk_r[8];
+      constexpr int NCS = D >= 64 ? BPH / 2 : 1;
+      float2 cs_r[8][NCS];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int lr = row_of(bi, i0 + r) - m0;
+        pos_r[r] = s_pos[lr];
+        blk_r[r] = s_blk[lr];
+      }
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+#pragma unroll
+        for (int b = 0; b < NCS; ++b)
+          cs_r[r][b] = qk.rope[(int64_t)pos_r[r] * HALF + (D >= 64 ? b * 32 + fr : (fr & 15))];
+      static_for<8>([&](auto r_c) {
+        constexpr int r = decltype(r_c)::value, i = i0 + r;
+        const int m = row_of(bi, i);
+        const int64_t blk = blk_r[r];
+        const int slot = pos_r[r] & (qk.pool.block_tokens - 1);
+        static_for<HPW>([&](auto hw_c) {
+          constexpr int hw = decltype(hw_c)::value;
+          const int hh = hw0 + hw;  // wave-uniform
+          if (hh >= H + 2 * Hkv) return;
+          float v[BPH];
+#pragma unroll
+          for (int b = 0; b < BPH; ++b) v[b] = acc[bi][(hw * D) / 32 + b][i];
+          if (hh < H + Hkv) {
+            // RMSNorm over the head's D channels: BPH blocks in the lane, then 32 lanes
+            float ss = 0.f;
+#pragma unroll
+            for (int b = 0; b < BPH; ++b) ss += v[b] * v[b];
+            ss = group_sum<32>(ss);
+            const float inv = 1.0f / sqrtf(ss / (float)D + qk.eps);
+            const bool isq = hh < H;
+            if constexpr (D >= 64) {
+#pragma unroll
+              for (int b = 0; b < BPH / 2; ++b) {
+                const float2 cs = cs_r[r][b];
+                const float x1 = v[b] * inv * (isq ? gq[b] : gk[b]);
+                const float x2 = v[b + BPH / 2] * inv * (isq ? gq[b + BPH / 2] : gk[b + BPH / 2]);
+                v[b] = x1 * cs.x - x2 * cs.y;
+                v[b + BPH / 2] = x2 * cs.x + x1 * cs.y;
+              }
+            } else {
+              // D = 32: the head is one block; channel fr pairs with channel fr ^ 16, held by
+              // the lane 16 away
+              const float2 cs = cs_r[r][0];
+              const float xs = v[0] * inv * (isq ? gq[0] : gk[0]);
+              const float xo = __shfl_xor(xs, 16, 64);
+              v[0] = fr < 16 ? xs * cs.x - xo * cs.y : xs * cs.x + xo * cs.y;
+            }
+          }
+          if (m >= M) return;
+          if (hh < H) {
+            const int64_t o = ((int64_t)m * H + hh) * D + fr;
+#pragma unroll
+            for (int b = 0; b < BPH; ++b) {
+              if constexpr (KV_F16)
+                ((uint16_t*)qk.q_out)[o + b * 32] = f32_to_f16_bits(v[b]);
+              else
+                ((float*)qk.q_out)[o + b * 32] = v[b];
+            }
+          } else {
+            const int kv = hh < H + Hkv ? 0 : 1;
+            const int kvh = hh - H - kv * Hkv;
+            const int64_t o = qk.pool.offset(qk.layer, kv, blk, kvh, slot) + fr;
+#pragma unroll
+            for (int b = 0; b < BPH; ++b) {
+              if constexpr (KV_F16)
+                ((uint16_t*)qk.pool.base)[o + b * 32] = f32_to_f16_bits(v[b]);
+              else
+                ((float*)qk.pool.base)[o + b * 32] = v[b];
+            }
+          }
+        });
+      });
+    });
+  }
+}
+
 template <int WF, int EPI, int D, bool KV_F16>
 __global__ __launch_bounds__(512) void gemm_big(GemmArgs a, QkRopeArgs qk) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];  // [stage][A | B][256][kLR]
@@ -313,147 +464,7 @@ __global__ __launch_bounds__(512) void gemm_big(GemmArgs a, QkRopeArgs qk) {
   }
   }
 
-  // ---- epilogue: lane holds column fr of each 32 x 32 block, rows 8 g + 4 (lane / 32) + r
-  const int rbase = m0 + wm * 64 + (lane >> 5) * 4;
-  auto row_of = [&](int bi, int i) { return rbase + bi * 32 + 8 * (i >> 2) + (i & 3); };
-  if constexpr (EPI == EPI_STORE || EPI == EPI_RESID) {
-    // per 32 x 32 block: the 16 residual values are all requested before any is updated
-#pragma unroll
-    for (int bi = 0; bi < 2; ++bi)
-#pragma unroll
-      for (int bj = 0; bj < 4; ++bj) {
-        const int n = n0 + wn * 128 + bj * 32 + fr;
-        const int nc = min(n, a.N - 1);
-        float xo[16];
-        if constexpr (EPI == EPI_RESID) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) xo[i] = ((const float*)a.C)[(int64_t)min(row_of(bi, i), M - 1) * a.ldc + nc];
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int m = row_of(bi, i);
-          if (m < M && n < a.N) {
-            float* c = (float*)a.C + (int64_t)m * a.ldc + n;
-            if constexpr (EPI == EPI_STORE)
-              *c = acc[bi][bj][i];
-            else
-              *c = xo[i] + acc[bi][bj][i];
-          }
-        }
-      }
-  } else if constexpr (EPI == EPI_SWIGLU) {
-#pragma unroll
-    for (int bi = 0; bi < 2; ++bi)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int m = row_of(bi, i);
-        if (m >= M) continue;
-#pragma unroll
-        for (int bj = 0; bj < 2; ++bj) {
-          const int f = n0 + wn * 64 + bj * 32 + fr;
-          if (f >= a.N) continue;
-          const float g = acc[bi][bj][i], u = acc[bi][bj + 2][i];
-          const float y = g / (1.0f + __expf(-g)) * u;
-          if (a.c_bf16)
-            ((uint16_t*)a.C)[(int64_t)m * a.ldc + f] = f32_to_bf16_bits(y);
-          else
-            ((float*)a.C)[(int64_t)m * a.ldc + f] = y;
-        }
-      }
-  } else {
-    // Q|K|V: heads of D channels; a head spans BPH 32-column blocks, HPW heads per wave
-    constexpr int BPH = D >= 32 ? D / 32 : 1, HPW = 128 / D, HALF = D / 2;
-    const int H = qk.n_heads, Hkv = qk.n_kv_heads;
-    const int hw0 = (n0 + wn * 128) / D;  // global head index of the wave's first head
-    // this lane's channels of a head are b * 32 + fr (D = 32: fr); their q and k gains
-    float gq[BPH], gk[BPH];
-#pragma unroll
-    for (int b = 0; b < BPH; ++b) {
-      gq[b] = qk.q_norm[b * 32 + fr];
-      gk[b] = qk.k_norm[b * 32 + fr];
-    }
-    static_for<4>([&](auto q_c) {
-      constexpr int bi = decltype(q_c)::value >> 1, i0 = (decltype(q_c)::value & 1) * 8;
-      // 8 rows' positions, blocks and rotation factors, requested together
-      int pos_r[8];
-      int64_t blk_r[8];
-      constexpr int NCS = D >= 64 ? BPH / 2 : 1;
-      float2 cs_r[8][NCS];
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int lr = row_of(bi, i0 + r) - m0;
-        pos_r[r] = s_pos[lr];
-        blk_r[r] = s_blk[lr];
-      }
-#pragma unroll
-      for (int r = 0; r < 8; ++r)
-#pragma unroll
-        for (int b = 0; b < NCS; ++b)
-          cs_r[r][b] = qk.rope[(int64_t)pos_r[r] * HALF + (D >= 64 ? b * 32 + fr : (fr & 15))];
-      static_for<8>([&](auto r_c) {
-        constexpr int r = decltype(r_c)::value, i = i0 + r;
-        const int m = row_of(bi, i);
-        const int64_t blk = blk_r[r];
-        const int slot = pos_r[r] & (qk.pool.block_tokens - 1);
-        static_for<HPW>([&](auto hw_c) {
-          constexpr int hw = decltype(hw_c)::value;
-          const int hh = hw0 + hw;  // wave-uniform
-          if (hh >= H + 2 * Hkv) return;
-          float v[BPH];
-#pragma unroll
-          for (int b = 0; b < BPH; ++b) v[b] = acc[bi][(hw * D) / 32 + b][i];
-          if (hh < H + Hkv) {
-            // RMSNorm over the head's D channels: BPH blocks in the lane, then 32 lanes
-            float ss = 0.f;
-#pragma unroll
-            for (int b = 0; b < BPH; ++b) ss += v[b] * v[b];
-            ss = group_sum<32>(ss);
-            const float inv = 1.0f / sqrtf(ss / (float)D + qk.eps);
-            const bool isq = hh < H;
-            if constexpr (D >= 64) {
-#pragma unroll
-              for (int b = 0; b < BPH / 2; ++b) {
-                const float2 cs = cs_r[r][b];
-                const float x1 = v[b] * inv * (isq ? gq[b] : gk[b]);
-                const float x2 = v[b + BPH / 2] * inv * (isq ? gq[b + BPH / 2] : gk[b + BPH / 2]);
-                v[b] = x1 * cs.x - x2 * cs.y;
-                v[b + BPH / 2] = x2 * cs.x + x1 * cs.y;
-              }
-            } else {
-              // D = 32: the head is one block; channel fr pairs with channel fr ^ 16, held by
-              // the lane 16 away
-              const float2 cs = cs_r[r][0];
-              const float xs = v[0] * inv * (isq ? gq[0] : gk[0]);
-              const float xo = __shfl_xor(xs, 16, 64);
-              v[0] = fr < 16 ? xs * cs.x - xo * cs.y : xs * cs.x + xo * cs.y;
-            }
-          }
-          if (m >= M) return;
-          if (hh < H) {
-            const int64_t o = ((int64_t)m * H + hh) * D + fr;
-#pragma unroll
-            for (int b = 0; b < BPH; ++b) {
-              if constexpr (KV_F16)
-                ((uint16_t*)qk.q_out)[o + b * 32] = f32_to_f16_bits(v[b]);
-              else
-                ((float*)qk.q_out)[o + b * 32] = v[b];
-            }
-          } else {
-            const int kv = hh < H + Hkv ? 0 : 1;
-            const int kvh = hh - H - kv * Hkv;
-            const int64_t o = qk.pool.offset(qk.layer, kv, blk, kvh, slot) + fr;
-#pragma unroll
-            for (int b = 0; b < BPH; ++b) {
-              if constexpr (KV_F16)
-                ((uint16_t*)qk.pool.base)[o + b * 32] = f32_to_f16_bits(v[b]);
-              else
-                ((float*)qk.pool.base)[o + b * 32] = v[b];
-            }
-          }
-        });
-      });
-    });
-  }
+  big_epilogue<WF, EPI, D, KV_F16, 2>(a, qk, acc, m0, n0, wm, wn, lane, s_pos, s_blk);
 }
 
 template <int WF, int EPI, int D, bool KV_F16>
