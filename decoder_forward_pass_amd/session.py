@@ -67,12 +67,15 @@ class BlockAllocator:
 
 class Session:
     def __init__(self, shape, weights, *, max_context: int, n_blocks: int, max_rows: int, max_seqs: int,
-                 device: str = "cuda"):
+                 device: str = "cuda", blob=None):
+        """``weights`` are packed into the blob; or ``blob`` (a host uint8 array, e.g. from
+        dec_load_safetensors) is uploaded as it is and ``weights`` is ignored."""
         self.shape = shape
         self.cfg = make_config(shape, max_context=max_context, n_blocks=n_blocks, max_rows=max_rows,
                                max_seqs=max_seqs)
         B.dec_check_config(self.cfg)
-        blob = pack_blob(self.cfg, weights)
+        if blob is None:
+            blob = pack_blob(self.cfg, weights)
         self.weights = torch.from_numpy(blob).to(device)
         del blob
         self.pool = torch.empty(B.dec_kv_pool_bytes(self.cfg), dtype=torch.uint8, device=device)
