@@ -954,10 +954,6 @@ int dec_sample(dec_ctx* ctx, void* stream, int32_t n_seqs, const float* logits, 
     if (h.prompt_offset < 0 || h.prompt_len < 0 || (int64_t)h.prompt_offset + h.prompt_len > n_ids ||
         h.output_offset < 0 || h.output_len < 0 || (int64_t)h.output_offset + h.output_len > n_ids)
       return fail(&ctx->err, DEC_E_ARG, "sequence %d: history ranges outside the id array", s);
-    const int64_t left = p.top_k > 0 && p.top_k < V ? p.top_k : V;
-    if (p.temperature > 0.0 && p.top_p < 1.0 && left > DEC_SAMPLE_MAX_NUCLEUS)
-      return fail(&ctx->err, DEC_E_UNSUPPORTED, "sequence %d: top_p < 1 orders at most %d ids; top_k leaves %lld", s,
-                  DEC_SAMPLE_MAX_NUCLEUS, (long long)left);
   }
   hipStream_t st = (hipStream_t)stream;
   HIPCHECK(hipEventSynchronize(ctx->samp_ev));  // the previous call's upload has finished

@@ -17,11 +17,14 @@
 //        of the distance below the largest value (buckets of 1/16) bounds the k-th value, the
 //        ids above that bound (at most 4096) go to LDS in id order, and the exact top-k is
 //        selected among them;
-//      - with top-p < 1 (then k <= 1024), or a top-k selected in LDS: the k candidates sit in
-//        LDS in ascending id order, their sum of exp(lt - max) is taken left to right, a
+//      - with top-p < 1 and top-k keeping at most 1024 ids, or a top-k selected in LDS: the k
+//        candidates sit in LDS in ascending id order, their sum of exp(lt - max) is taken left to right, a
 //        bitonic network orders them by (value descending, id ascending) for the nucleus walk,
 //        min-p drops those below min_p times the largest probability, and one thread takes
 //        the final softmax and the walk over the kept ids left to right in ascending id order;
+//      - with top-p < 1 and top-k keeping more than 1024 ids (or none: top_k = 0), the nucleus
+//        cut comes from a radix descent by probability mass over the keys (fixed-order digit
+//        sums), and the ids it keeps go through the whole-vocabulary path below;
 //      - with top-p = 1: e = exp(lt - max) for the ids top-k and min-p keep, 0 for the others
 //        (an id whose e underflows to 0 is never drawn); sums over
 //        the whole vocabulary reduce each group of 64 consecutive ids by a fixed lane tree and
@@ -480,7 +483,10 @@ __global__ __launch_bounds__(kST) void sample_kernel(const float* __restrict__ l
       return in;
     };
 
-    if (lds || P.top_p < 1.0) {
+    // a nucleus over more ids than the candidate path orders (top_p < 1 with top-k keeping more
+    // than kNuc ids) is cut over the whole vocabulary (3c)
+    const bool big_nuc = P.top_p < 1.0 && !lds && (use_k ? k : V) > kNuc;
+    if (lds || (P.top_p < 1.0 && !big_nuc)) {
       // 3b. nucleus path over the (<= kNuc) candidates in ascending id order: from 3a, or
       // compacted here from the whole vocabulary (gp's storage holds the per-group counts and
       // their prefix then)
@@ -599,17 +605,149 @@ __global__ __launch_bounds__(kST) void sample_kernel(const float* __restrict__ l
       tok = s_i[0];
       __syncthreads();
     } else {
-      // 3c. the whole vocabulary: e = exp(lt - max) for the ids top-k keeps, 0 otherwise; min-p
-      // over those; softmax and walk
+      // 3c. the whole vocabulary: e = exp(lt - max) for the ids top-k (and, with top-p < 1, the
+      // nucleus) keeps, 0 otherwise; min-p over those; softmax and walk
+      //
+      // The nucleus cut (3c'): walking the top-k ids by (value descending, id ascending), the
+      // first id where the cumulative probability reaches top_p is the last one kept. It is found
+      // by a radix descent over the order-preserving 64-bit keys of the tempered values (8-bit
+      // digits, most significant first): each pass adds the probability of the ids of every digit
+      // under the current prefix, and takes the digit where the mass above it plus its own first
+      // reaches top_p; the descent ends when that digit holds one id, or after 64 bits with ids of
+      // equal value, which are taken in id order until the sum reaches top_p. A digit's mass is
+      // a fixed-order sum: within a wave the lanes of one digit are added by a fixed butterfly
+      // (digit by digit, lowest lane's digit first) into the wave's histogram held in registers
+      // (lane l: digits 4l .. 4l + 3), and the 16 waves' histograms are added in wave order, so
+      // the cut is the same on every run; the cumulative probability is the sum of whole digits'
+      // masses, equal to the walk's left-to-right sum up to rounding.
+      bool nuc_on = false;     // the nucleus predicate is in force (after 3c')
+      uint64_t npv = 0;        // the descent's prefix (its top nbits bits of the cut key)
+      int nbits = 0, ntake = 0;
+      bool nties = false;      // equal keys at the cut: the first ntake in id order are kept
+      auto kept_nuc = [&](int g, int v, double y, bool intk) -> bool {  // (whole waves)
+        const uint64_t top = okey(y) >> (64 - nbits);
+        const bool eq = intk && top == npv;
+        bool in = intk && top > npv;
+        if (nties) {
+          const uint64_t eqm = __ballot(eq);
+          if (eq) in = cidx[g] + (int)__popcll(eqm & lanes_below) < ntake;
+        } else if (eq) {
+          in = true;
+        }
+        return in;
+      };
       auto e_tk = [&](float x, int v, int g) -> double {
         const double y = v < V ? lt(x, v) : 0.0;
-        const bool in = kept_tk(g, v, y);
+        bool in = kept_tk(g, v, y);
+        if (nuc_on) in = kept_nuc(g, v, y, in);
         return in ? exp(y - mt) : 0.0;
       };
       double zk = 1.0, qmax = 0.0;
-      if (P.min_p > 0.0) {
+      if (P.min_p > 0.0 || big_nuc) {
         zk = vocab_sum([&](float x, int v) { return e_tk(x, v, v >> 6); });
         qmax = 1.0 / zk;  // the largest id's probability: exp(0) / zk
+      }
+      if (big_nuc) {
+        double above = 0.0;  // probability of the top-k ids above the current prefix's digit
+        for (int pass = 0; pass < 8; ++pass) {
+          const int shift = 56 - 8 * pass;
+          if (t < 256) hist[t] = 0;
+          __syncthreads();
+          double b0 = 0.0, b1 = 0.0, b2 = 0.0, b3 = 0.0;
+          for (int g = wave; g < NG; g += kWaves) {
+            const int v = g * 64 + lane;
+            const double y = v < V ? lt(lg[v], v) : 0.0;
+            const bool intk = kept_tk(g, v, y);
+            const uint64_t key = okey(y);
+            const bool act = intk && (nbits == 0 || (key >> (64 - nbits)) == npv);
+            const int dig = (int)((key >> shift) & 255u);
+            if (act) atomicAdd(&hist[dig], 1u);
+            const double m = act ? exp(y - mt) / zk : 0.0;
+            uint64_t todo = __ballot(act);
+            while (todo) {
+              const int d = __shfl(dig, __builtin_ctzll(todo), 64);
+              const uint64_t mk = __ballot(act && dig == d);
+              double x = ((mk >> lane) & 1ull) ? m : 0.0;
+#pragma unroll
+              for (int o = 1; o < 64; o <<= 1) x += __shfl_xor(x, o, 64);
+              if (lane == (d >> 2)) {
+                const int r = d & 3;
+                if (r == 0) b0 += x;
+                else if (r == 1) b1 += x;
+                else if (r == 2) b2 += x;
+                else b3 += x;
+              }
+              todo &= ~mk;
+            }
+          }
+          // the waves' histograms added in wave order: digit 4 l + r into cand_e
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            red[wave * 64 + lane] = r == 0 ? b0 : (r == 1 ? b1 : (r == 2 ? b2 : b3));
+            __syncthreads();
+            if (t < 64) {
+              double a = 0.0;
+              for (int w = 0; w < kWaves; ++w) a += red[w * 64 + t];
+              cand_e[4 * t + r] = a;
+            }
+            __syncthreads();
+          }
+          if (t == 0) {
+            double acc = above;
+            int sel = -1, last = -1;
+            for (int d = 255; d >= 0; --d) {
+              if (!hist[d]) continue;
+              last = d;
+              if (acc + cand_e[d] >= P.top_p) {
+                sel = d;
+                break;
+              }
+              acc += cand_e[d];
+            }
+            if (sel < 0) {  // (rounding kept the total below top_p: every id is kept)
+              sel = last;
+              acc -= cand_e[last];
+            }
+            s_i[0] = sel;
+            s_i[1] = (int)hist[sel];
+            s_d[0] = acc;
+          }
+          __syncthreads();
+          const int sel = s_i[0], cnt = s_i[1];
+          above = s_d[0];
+          __syncthreads();
+          npv = (npv << 8) | (uint64_t)sel;
+          nbits += 8;
+          if (cnt == 1) break;
+          if (pass == 7) {
+            // equal values at the cut: each has probability q; in id order they are taken
+            // until the walk's sum reaches top_p (their ranks: counts per group, then a ballot)
+            if (t == 0) {
+              const uint64_t b = (npv >> 63) ? (npv & 0x7fffffffffffffffull) : ~npv;  // okey inverted
+              const double qt = exp(__builtin_bit_cast(double, b) - mt) / zk;
+              double c = above;
+              int j = 0;
+              while (j < cnt) {
+                c += qt;
+                ++j;
+                if (c >= P.top_p) break;
+              }
+              s_i[0] = j;
+            }
+            for (int g = wave; g < NG; g += kWaves) {
+              const int v = g * 64 + lane;
+              const double y = v < V ? lt(lg[v], v) : 0.0;
+              const bool eq = kept_tk(g, v, y) && okey(y) == npv;
+              const uint64_t m = __ballot(eq);
+              if (lane == 0) cidx[g] = __popcll(m);
+            }
+            __syncthreads();
+            ntake = s_i[0];
+            group_prefix(cidx);
+            nties = true;
+          }
+        }
+        nuc_on = true;
       }
       auto e_of = [&](float x, int v) -> double {
         const double e = e_tk(x, v, v >> 6);

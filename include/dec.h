@@ -309,7 +309,8 @@ typedef struct dec_history {
 } dec_history;
 
 #define DEC_PURPOSE_SAMPLE 4       /* the purpose id of the sampling stream */
-#define DEC_SAMPLE_MAX_NUCLEUS 1024 /* most ids the nucleus step orders (top_k bound when top_p < 1) */
+#define DEC_SAMPLE_MAX_NUCLEUS 1024 /* most ids the nucleus step orders one by one; beyond, its cut
+                                       is found by a radix descent over the whole vocabulary */
 
 /*
  * Host only: state_inc[0], state_inc[1] = the PCG32 state and increment of the
@@ -350,14 +351,16 @@ void dec_rng_stream(uint64_t seed, uint64_t purpose, uint64_t state_inc[2]);
  * Sums over the at most DEC_SAMPLE_MAX_NUCLEUS ids of the nucleus path are
  * left-to-right in ascending id order; sums over the whole vocabulary run
  * left to right within fixed id ranges, then over the ranges in order (equal
- * to a left-to-right sum up to rounding). Uses the workspace: a count table
- * per sequence that every call leaves zero, so calls on one context must not
- * overlap. Asynchronous on `stream`.
+ * to a left-to-right sum up to rounding). When top_k keeps more than
+ * DEC_SAMPLE_MAX_NUCLEUS ids (top_k = 0 or top_k >= vocab keep all of them) and
+ * top_p < 1, the nucleus's cumulative probability is taken over groups of ids
+ * of equal leading key bits in a fixed order (equal to the walk's
+ * left-to-right sum up to rounding); the same inputs always give the same
+ * token. Uses the workspace: a count table per sequence that every call leaves
+ * zero, so calls on one context must not overlap. Asynchronous on `stream`.
  * Errors (checked on the host before anything is enqueued): DEC_E_ARG (a
  * NULL pointer, a bad range, a parameter outside the ranges above),
- * DEC_E_CAPACITY (n_seqs > max_seqs), DEC_E_UNSUPPORTED (temperature > 0 and
- * top_p < 1 with more than DEC_SAMPLE_MAX_NUCLEUS ids left by top_k: top_k = 0
- * or top_k >= vocab keep all vocab ids).
+ * DEC_E_CAPACITY (n_seqs > max_seqs), DEC_E_UNSUPPORTED (vocab > 262,144).
  */
 int dec_sample(dec_ctx* ctx, void* stream, int32_t n_seqs, const float* logits, int64_t ld,
                const dec_sampling* params, const dec_history* history, const int32_t* ids,

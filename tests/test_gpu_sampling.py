@@ -135,6 +135,57 @@ def test_parameter_grid_matches_oracle(which, request):
     _check(_run(sess, logits, cases, list(range(100, 100 + n))), f"grid_{which}")
 
 
+# nucleus sampling over more ids than the ordered candidate path takes: top_k = 0 (all ids) or a
+# top_k beyond 1,024, with peaked, flat and very flat distributions (nuclei of a few ids up to
+# most of the vocabulary), with and without min-p and penalties
+NUCLEUS = [
+    dict(temperature=1.0, top_p=0.9),
+    dict(temperature=0.6, top_p=0.5),
+    dict(temperature=2.0, top_p=0.95),
+    dict(temperature=8.0, top_p=0.99),
+    dict(temperature=1.0, top_k=5000, top_p=0.8, min_p=0.01),
+    dict(temperature=1.3, top_p=0.7, repetition_penalty=1.2, presence_penalty=0.3, frequency_penalty=0.2),
+    dict(temperature=25.0, top_k=2000, top_p=0.6),
+    dict(temperature=1.0, top_p=0.999999),
+]
+
+
+@pytest.mark.parametrize("which", ["small", "full"])
+def test_nucleus_over_the_whole_vocabulary_matches_oracle(which, request):
+    sess = request.getfixturevalue(which)
+    V = V_SMALL if which == "small" else V_FULL
+    rng = np.random.default_rng(41 if which == "small" else 42)
+    n = len(NUCLEUS)
+    logits = (rng.standard_normal((n, V)) * 3.0).astype(np.float32)
+    cases = []
+    for i, kw in enumerate(NUCLEUS):
+        prompt = rng.integers(0, V, 30).tolist()
+        output = rng.integers(0, V, 10).tolist()
+        cases.append((kw, prompt, output))
+    _check(_run(sess, logits, cases, list(range(300, 300 + n))), f"nucleus_{which}")
+
+
+def test_nucleus_cut_inside_equal_values(full):
+    # integer logits: long runs of equal values; the nucleus cut falls inside one of them, whose
+    # ids are then taken in id order
+    rng = np.random.default_rng(43)
+    logits = rng.integers(-4, 3, size=(4, V_FULL)).astype(np.float32)
+    cases = [(dict(temperature=1.0, top_p=p), [], []) for p in (0.3, 0.5, 0.77, 0.9)]
+    _check(_run(full, logits, cases, [21, 22, 23, 24]), "nucleus_ties")
+
+
+def test_nucleus_is_the_same_on_every_run(full):
+    # the same inputs, three times: the same ids and generator states (fixed-order sums)
+    rng = np.random.default_rng(44)
+    logits = (rng.standard_normal((6, V_FULL)) * 1.5).astype(np.float32)
+    cases = [(dict(temperature=1.5, top_p=0.93), [], [])] * 6
+    runs = [_run(full, logits, cases, list(range(60, 66))) for _ in range(3)]
+    for r in runs[1:]:
+        assert [x["gpu"] for x in r] == [x["gpu"] for x in runs[0]]
+        assert [x["state_gpu"] for x in r] == [x["state_gpu"] for x in runs[0]]
+    _check(runs[0], "nucleus_repeat")
+
+
 def test_equal_logits_across_the_top_k_cut(small):
     # integer-valued logits: many equal values, the cut of top_k falls inside a run of equals
     rng = np.random.default_rng(33)
@@ -184,9 +235,7 @@ def test_refusals(full):
     lg = torch.zeros((1, V_FULL), dtype=torch.float32, device="cuda")
     rng = torch.tensor([list(B.dec_rng_stream(1))], dtype=torch.uint64, device="cuda")
     h = B.dec_history()
-    for kw, code in ((dict(temperature=1.0, top_p=0.9), B.DEC_E_UNSUPPORTED),
-                     (dict(temperature=1.0, top_k=2000, top_p=0.9), B.DEC_E_UNSUPPORTED),
-                     (dict(temperature=1.0, top_p=0.0), B.DEC_E_ARG),
+    for kw, code in ((dict(temperature=1.0, top_p=0.0), B.DEC_E_ARG),
                      (dict(temperature=-1.0), B.DEC_E_ARG),
                      (dict(temperature=1.0, repetition_penalty=0.0), B.DEC_E_ARG)):
         _, cp = _params(**kw)
