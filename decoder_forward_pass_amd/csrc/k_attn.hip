@@ -889,6 +889,7 @@ __global__ __launch_bounds__(256 * G) void attn_prefill_kernel(AttnPrefillArgs a
   const bool qvalid = qi < tile_rows;
   const int qrow = row0 + min(qi, tile_rows - 1);
   const int qpos = p0 + qi;
+  const int wq0 = p0 + qsub * 32;  // the wave's first query position
   f16x8 qf[NDS];
 #pragma unroll
   for (int ks = 0; ks < NDS; ++ks)
@@ -897,7 +898,9 @@ __global__ __launch_bounds__(256 * G) void attn_prefill_kernel(AttnPrefillArgs a
   // ---- staging of key tile kt through registers: K in 16-byte chunks, V in blocks of 2 keys x
   // 8 channels transposed in registers (32 consecutive threads fill one row of V^T). The pool
   // block of every key of a tile is fetched ahead (lane j of each wave: key j of the tile) and
-  // handed out by lane shuffles.
+  // handed out by lane shuffles. A key past the context reads the last key's slot (in bounds)
+  // and is written to LDS as zeros; nothing is applied to the loaded registers before they are
+  // stored, so the loads of a tile stay in flight for a whole step.
   constexpr int KPT = (NKC + NT - 1) / NT;
   constexpr int NV2 = (KT / 2) * (D / 8);  // 2 x 8 V blocks per tile
   constexpr int VPT = (NV2 + NT - 1) / NT;
@@ -916,7 +919,6 @@ __global__ __launch_bounds__(256 * G) void attn_prefill_kernel(AttnPrefillArgs a
       const int kpos = kt * KT + key;
       const int64_t blk = __shfl(bids, key, 64);
       r.k[j] = *(const u32x4*)(kbase + blk * slab + (min(kpos, last_key) & bmask) * D + part * 8);
-      if (kpos > last_key) r.k[j] = u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
@@ -927,27 +929,31 @@ __global__ __launch_bounds__(256 * G) void attn_prefill_kernel(AttnPrefillArgs a
         const int key = k2 * 2 + e, kpos = kt * KT + key;
         const int64_t blk = __shfl(bids, key, 64);
         r.v[j][e] = *(const u32x4*)(vbase + blk * slab + (min(kpos, last_key) & bmask) * D + d8 * 8);
-        if (kpos > last_key) r.v[j][e] = u32x4{0u, 0u, 0u, 0u};
       }
     }
   };
-  auto store_tile = [&](int st, const Regs& r) {
+  auto store_tile = [&](int st, int kt, const Regs& r) {
     uint16_t* Ks = plds + (size_t)st * (L::KS + L::VS);
     uint16_t* Vt = Ks + L::KS;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       const int c = tid + j * NT;
-      if (c < NKC) *(u32x4*)(Ks + (c / (D / 8)) * KSTR + (c % (D / 8)) * 8) = r.k[j];
+      const int key = c / (D / 8);
+      if (NKC % NT == 0 || c < NKC)  // (every thread has KPT chunks when NT divides NKC)
+        *(u32x4*)(Ks + key * KSTR + (c % (D / 8)) * 8) = kt * KT + key > last_key ? zero : r.k[j];
     }
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
       const int vb = tid + j * NT;
-      if (vb >= NV2) continue;
+      if (NV2 % NT != 0 && vb >= NV2) continue;
       const int k2 = vb % (KT / 2), d8 = vb / (KT / 2);
-      // r.v[j][e] word w holds channels (2w, 2w + 1) of key e; row d of V^T gets keys 0..1
+      const u32x4 v0 = kt * KT + k2 * 2 > last_key ? zero : r.v[j][0];
+      const u32x4 v1 = kt * KT + k2 * 2 + 1 > last_key ? zero : r.v[j][1];
+      // v0 / v1 word w holds channels (2w, 2w + 1) of keys 2 k2 / 2 k2 + 1; row d of V^T gets both
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
-        const uint32_t x0 = r.v[j][0][d >> 1], x1 = r.v[j][1][d >> 1];
+        const uint32_t x0 = v0[d >> 1], x1 = v1[d >> 1];
         *(uint32_t*)(Vt + (d8 * 8 + d) * VSTR + k2 * 2) =
             (d & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
       }
@@ -964,21 +970,24 @@ __global__ __launch_bounds__(256 * G) void attn_prefill_kernel(AttnPrefillArgs a
   const int n_kt = pmax / KT + 1;
 
   // Pipeline: tile kt is used from LDS stage kt % 2 while tile kt + 1 (in registers since the
-  // previous step) is written to the other stage and tile kt + 2 is requested from memory.
+  // previous step) is written to the other stage and tile kt + 2 is requested from memory. The
+  // block ids of a tile are requested one step before its data, ahead of the previous tile's
+  // loads, so that waiting for them does not wait for those loads. Every step issues the same
+  // loads (the last tile is requested again near the end, in bounds and unused), so each wait
+  // covers exactly the loads of the step before.
   Regs ra, rb;
-  int bids = block_ids(0);
-  load_tile(0, bids, ra);
-  bids = block_ids(min(1, n_kt - 1));
-  if (n_kt > 1) load_tile(1, bids, rb);
-  bids = block_ids(min(2, n_kt - 1));
-  store_tile(0, ra);
+  const int b0 = block_ids(0);
+  const int b1 = block_ids(min(1, n_kt - 1));
+  load_tile(0, b0, ra);
+  int ba = block_ids(min(2, n_kt - 1)), bb;
+  load_tile(min(1, n_kt - 1), b1, rb);
+  store_tile(0, 0, ra);
   __syncthreads();
-  auto step = [&](int kt, const Regs& next, Regs& fill) {
+  auto step = [&](int kt, const Regs& next, Regs& fill, int buse, int& bload) {
     const int st = kt & 1;
-    if (kt + 2 < n_kt) {
-      load_tile(kt + 2, bids, fill);
-      bids = block_ids(min(kt + 3, n_kt - 1));
-    }
+    bload = block_ids(min(kt + 3, n_kt - 1));
+    load_tile(min(kt + 2, n_kt - 1), buse, fill);
+    if (kt < n_kt) {  // (the step past an odd tile count only keeps the loads and stores in step)
     const uint16_t* Ks = plds + (size_t)st * (L::KS + L::VS);
     const uint16_t* Vt = Ks + L::KS;
 
@@ -994,38 +1003,48 @@ __global__ __launch_bounds__(256 * G) void attn_prefill_kernel(AttnPrefillArgs a
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], sacc[kb], 0, 0, 0);
       }
     }
-    // online softmax of this lane's query over the tile
-    float mt = -__builtin_inff();
+    // online softmax of this lane's query over the tile. Only a tile that reaches past the
+    // wave's first query position needs the causal mask; elsewhere every key is visible.
+    // The tile maximum is taken over the raw scores and scaled afterwards (scaling by a
+    // positive constant is monotone under rounding, so this is the maximum of the scaled
+    // scores), and a weight is exp2(s * scale - m) with one rounding. Key 0 is in tile 0 and
+    // visible to every query, so m is finite from the first tile on.
+    if (kt * KT + KT - 1 > wq0) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kpos = kt * KT + kb * 32 + 8 * (i >> 2) + 4 * hl + (i & 3);
+          if (kpos > qpos) sacc[kb][i] = -__builtin_inff();
+        }
+    }
+    float mt = sacc[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kpos = kt * KT + kb * 32 + 8 * (i >> 2) + 4 * hl + (i & 3);
-        float v = sacc[kb][i] * sl2;
-        if (kpos > qpos) v = -__builtin_inff();
-        sacc[kb][i] = v;
-        mt = fmaxf(mt, v);
-      }
+      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sacc[kb][i]);
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float mnew = fmaxf(m, mt);
-    const bool none = mnew == -__builtin_inff();
-    const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m - mnew);
+    const float mnew = fmaxf(m, mt * sl2);
+    const float alpha = __builtin_amdgcn_exp2f(m - mnew);  // exp2(-inf) = 0 on the first tile
     float ps = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = none ? 0.f : __builtin_amdgcn_exp2f(sacc[kb][i] - mnew);
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i], sl2, -mnew));
         sacc[kb][i] = p;
         ps += p;
       }
     ps += __shfl_xor(ps, 32, 64);
     l = l * alpha + ps;
     m = mnew;
+    // a running maximum that moved in no lane leaves the accumulators as they are (alpha = 1)
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+        for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
+    }
 
     // O^T += V^T . P^T over four 16-key steps
 #pragma unroll
@@ -1042,12 +1061,17 @@ __global__ __launch_bounds__(256 * G) void attn_prefill_kernel(AttnPrefillArgs a
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf, o[db], 0, 0, 0);
       }
     }
-    if (kt + 1 < n_kt) store_tile(st ^ 1, next);
+    }
+    // (on the last steps this fills the other stage with a tile no wave reads: the stage was
+    // last read before the previous barrier, and the loop ends within a step)
+    store_tile(st ^ 1, kt + 1, next);
     __syncthreads();
   };
+  // steps in pairs, so that the two register sets keep their roles; every step issues the same
+  // memory operations, and only the compute of a step past the last tile is skipped
   for (int kt = 0; kt < n_kt; kt += 2) {
-    step(kt, rb, ra);
-    if (kt + 1 < n_kt) step(kt + 1, ra, rb);
+    step(kt, rb, ra, ba, bb);
+    step(kt + 1, ra, rb, bb, ba);
   }
 
   if (!qvalid) return;
