@@ -826,8 +826,11 @@ hipError_t launch_attn_decode_combine(const AttnRowsArgs& a, void* o, bool out_b
 // ---- flash-style prefill attention (f16 pool, MFMA) ----------------------------------------
 // Causal attention of one sequence's new rows over its paged keys ("Candle model runner" 2.4,
 // second equation; keys up to and including the query's absolute position), read in place from
-// the pool. One block per (128-position query tile, KV head); wave w takes head w / 4 of the
-// KV head's group and 32 query positions. Key tiles of 64 positions, aligned to position 0 of
+// the pool. The 128 positions of a query tile are split over SPLIT blocks per KV head (one block
+// of 4 G waves, or two blocks of 2 G waves each taking 64 positions; two smaller blocks share a
+// CU and run out of step, so one's matrix products overlap the other's softmax and staging);
+// wave w takes head w / (4 / SPLIT) of the KV head's group and 32 query positions. The split
+// changes no operation applied to a query. Key tiles of 64 positions, aligned to position 0 of
 // the sequence, are staged in LDS (K row-major, V transposed, two stages, the next tile loaded
 // while the current one is used). Per key tile and wave, with v_mfma_f32_32x32x16_f16:
 //   S^T = K . Q^T (keys x queries), scaled into the exp2 domain and causally masked;
@@ -853,28 +856,32 @@ struct PrefillLds {
 };
 }  // namespace
 
-template <int D, int G, bool BF16_OUT>
-__global__ __launch_bounds__(256 * G) void attn_prefill_kernel(AttnPrefillArgs a) {
+template <int D, int G, int SPLIT, bool BF16_OUT>
+__global__ __launch_bounds__(256 * G / SPLIT) __attribute__((amdgpu_waves_per_eu(SPLIT)))
+void attn_prefill_kernel(AttnPrefillArgs a) {
   using L = PrefillLds<D>;
   constexpr int KT = kPfKT, QT = kPrefillQueryTile;
-  constexpr int NT = 256 * G;              // threads: G heads x 4 waves of 32 queries
+  constexpr int WPH = 4 / SPLIT;           // waves per head
+  constexpr int QB = QT / SPLIT;           // query positions per block
+  constexpr int NT = 64 * WPH * G;         // threads: G heads x WPH waves of 32 queries
   constexpr int KSTR = L::KSTR, VSTR = L::VSTR;
   constexpr int NDS = D / 16;              // k-steps of S^T over the head dimension
   constexpr int NDB = D / 32;              // 32-row blocks of O^T
   constexpr int NKC = KT * (D / 8);        // 16-byte K chunks per tile
-  static_assert(QT == 128, "4 waves of 32 query positions per head");
+  static_assert(QT == 128 && (SPLIT == 1 || SPLIT == 2), "4 / SPLIT waves of 32 query positions per head");
   extern __shared__ __attribute__((aligned(16))) uint16_t plds[];  // [stage][K | V^T]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, ql = lane & 31;
-  const int gh = wave >> 2, qsub = wave & 3;
-  const int kvh = blockIdx.x, tile = blockIdx.y;
+  const int gh = wave / WPH, qsub = wave % WPH;
+  const int kvh = blockIdx.x, tile = blockIdx.y / SPLIT, qb0 = (blockIdx.y % SPLIT) * QB;
   const int seq = a.b.tiles[2 * tile], row0 = a.b.tiles[2 * tile + 1];
   const int s_start = a.b.seq_start[seq], s_n = a.b.seq_nnew[seq], s_row0 = a.b.seq_row0[seq];
   const int ctx_end = s_start + s_n;
   const int p0 = s_start + (row0 - s_row0);
   const int tile_rows = min(QT, s_n - (row0 - s_row0));
-  const int pmax = p0 + tile_rows - 1;
+  if (qb0 >= tile_rows) return;  // (a ragged last tile: this block has no query; block-uniform)
+  const int pmax = p0 + min(qb0 + QB, tile_rows) - 1;  // the block's last query position
   const int H = a.n_heads;
   const int bsh = a.pool.block_shift, bmask = a.pool.block_tokens - 1;
   const int32_t* table = a.b.block_tables + (int64_t)seq * a.b.tbl_stride;
@@ -885,11 +892,11 @@ __global__ __launch_bounds__(256 * G) void attn_prefill_kernel(AttnPrefillArgs a
   const int head = kvh * G + gh;
 
   // this lane's query (column of S^T and O^T)
-  const int qi = qsub * 32 + ql;
+  const int qi = qb0 + qsub * 32 + ql;
   const bool qvalid = qi < tile_rows;
   const int qrow = row0 + min(qi, tile_rows - 1);
   const int qpos = p0 + qi;
-  const int wq0 = p0 + qsub * 32;  // the wave's first query position
+  const int wq0 = p0 + qb0 + qsub * 32;  // the wave's first query position
   f16x8 qf[NDS];
 #pragma unroll
   for (int ks = 0; ks < NDS; ++ks)
@@ -1099,31 +1106,33 @@ bool attn_prefill_supported(int head_dim, int group) {
   return (head_dim == 32 || head_dim == 64 || head_dim == 128) && (group == 1 || group == 2);
 }
 
-template <int D, int G>
+template <int D, int G, int SPLIT>
 static hipError_t prefill_launch(const AttnPrefillArgs& a, dim3 g, hipStream_t s) {
   constexpr size_t lds = PrefillLds<D>::bytes;
   static bool attr = false;  // raise the dynamic LDS limit once per instantiation
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_prefill_kernel<D, G, true>,
+    hipError_t e = hipFuncSetAttribute((const void*)attn_prefill_kernel<D, G, SPLIT, true>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)attn_prefill_kernel<D, G, false>,
+      e = hipFuncSetAttribute((const void*)attn_prefill_kernel<D, G, SPLIT, false>,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr = true;
   }
+  g.y *= SPLIT;
+  const dim3 blk(64 * (4 / SPLIT) * G);
   if (a.out_bf16)
-    launch_kernel(attn_prefill_kernel<D, G, true>, g, dim3(256 * G), (uint32_t)lds, s, a);
+    launch_kernel(attn_prefill_kernel<D, G, SPLIT, true>, g, blk, (uint32_t)lds, s, a);
   else
-    launch_kernel(attn_prefill_kernel<D, G, false>, g, dim3(256 * G), (uint32_t)lds, s, a);
+    launch_kernel(attn_prefill_kernel<D, G, SPLIT, false>, g, blk, (uint32_t)lds, s, a);
   return hipGetLastError();
 }
 
 template <int D>
 static hipError_t prefill_dispatch(const AttnPrefillArgs& a, dim3 g, hipStream_t s) {
   const int group = a.n_heads / a.n_kv_heads;
-  if (group == 1) return prefill_launch<D, 1>(a, g, s);
-  if (group == 2) return prefill_launch<D, 2>(a, g, s);
+  if (group == 1) return prefill_launch<D, 1, 1>(a, g, s);
+  if (group == 2) return prefill_launch<D, 2, 2>(a, g, s);
   return hipErrorInvalidValue;
 }
 
