@@ -171,20 +171,37 @@ size_t dec_workspace_bytes(const dec_config* cfg);
 typedef struct dec_ctx dec_ctx;
 
 /*
- * Bind a configuration to caller-owned device buffers. Checks the config and
- * that each buffer is at least the size above and 256-byte aligned, builds the
- * RoPE cos/sin table (angles in double precision, stored float32) and uploads
- * it into the workspace on `stream`. The weights blob is not modified.
- * On success *out is a new context; on failure *out is NULL.
+ * Bind a configuration to caller-owned device buffers: the runner's load step
+ * ("Candle model runner", section 4, the ModelRunner interface: a runner is
+ * built once from a model and its configuration, and a failure comes back as a
+ * result rather than a crash). Here the model arrives as a packed weights blob,
+ * and every device buffer belongs to the caller, as the pool's blocks do on
+ * that page (the caller allocates the blocks the forward writes into).
+ * Checks the config and that each buffer is at least the size above and
+ * 256-byte aligned, builds the RoPE cos/sin table (angles in double precision,
+ * stored float32) and uploads it into the workspace on `stream`. The weights
+ * blob is not modified. On success *out is a new context; on failure *out is
+ * NULL and dec_last_error(NULL) holds the reason.
  */
 int dec_init(const dec_config* cfg, const void* weights, size_t weight_bytes, void* kv_pool,
              size_t kv_bytes, void* workspace, size_t workspace_bytes, void* stream,
              dec_ctx** out);
 
-/* Release the context's host memory and events. Device buffers stay with the caller. */
+/*
+ * End a context ("Candle model runner", section 4: the runner owns its own state;
+ * the caller owns the blocks): releases the context's host memory and events.
+ * Device buffers stay with the caller. NULL is a no-op.
+ */
 void dec_free(dec_ctx* ctx);
 
-/* Message of the last failure of a call on ctx (or of dec_init, for ctx == NULL). */
+/*
+ * Message of the last failure of a call on ctx (or, for ctx == NULL, of the
+ * calling thread's last dec_init or context-free call). The runner's operations report invalid
+ * dimensions, exhausted capacity, invalid block ids and format errors as
+ * results ("Candle model runner", section 2.2); here the kind is the DEC_E_*
+ * code returned by the call and this string names the check that failed. The
+ * string stays valid until the next call on the same context.
+ */
 const char* dec_last_error(const dec_ctx* ctx);
 
 /* ---- forward ----------------------------------------------------------------------- */
