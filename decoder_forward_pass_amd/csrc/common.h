@@ -22,6 +22,14 @@ constexpr int kWave = 64;
 
 // float -> bf16 bits, round to nearest, ties to even; NaN stays a quiet NaN (gfx950's
 // v_cvt_pk_bf16_f32: one instruction, no per-value branch)
+// a 16-byte load at a wave-uniform address plus a 32-bit lane offset, through a raw buffer
+// descriptor held in scalar registers (no 64-bit lane addresses). With range 0 the load
+// returns zeros without a memory access.
+__device__ __forceinline__ u32x4 load_uniform_base(const char* base, uint32_t lane_off, int range = 0x7fffffff) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, range, 0x00020000);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)lane_off, 0, 0);
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 // two values -> packed bf16 pair (lo = a, hi = b), one conversion instruction
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {

@@ -75,15 +75,6 @@ __device__ __forceinline__ float xor_reduce(float v, Op op) {  // over lane bits
   return v;
 }
 
-// a 16-byte load at a wave-uniform address plus a 32-bit lane offset, through a raw buffer
-// descriptor held in scalar registers (no 64-bit lane addresses; the offsets used here are a
-// few kilobytes, far inside the descriptor's range)
-// With range 0 the load returns zeros without a memory access.
-__device__ __forceinline__ u32x4 load_uniform_base(const char* base, uint32_t lane_off, int range = 0x7fffffff) {
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, range, 0x00020000);
-  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)lane_off, 0, 0);
-}
-
 template <typename KVT, int D, int GROUP>
 __global__ __launch_bounds__(256) void attn_rows_kernel(AttnRowsArgs a) {
   using G = RowsGeom<KVT, D, GROUP>;

@@ -585,9 +585,10 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
 // accumulated over the whole K in ascending order -- the same per-element MFMA sequence for any
 // number of rows. E is read once per step.
 
-template <int WF, int MT>
+template <int WF, int MT, bool STG>
 __global__ __launch_bounds__(1024) void lmhead_decode(GemmArgs a) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t s_h[];  // [MT*16][K + 8]
+  // [MT*16][K + 8] bf16 rows of xg; with STG, then the block's logits [MT*16][stage stride]
+  extern __shared__ __attribute__((aligned(16))) uint16_t s_h[];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int M = a.M, K = a.K, KS = K + 8;
@@ -671,67 +672,207 @@ __global__ __launch_bounds__(1024) void lmhead_decode(GemmArgs a) {
       bv[mt][r] = -__builtin_inff();
       bi[mt][r] = 0x7fffffff;
     }
-  BRaw<WF> cur[WIDE ? 1 : G], nxt[WIDE ? 1 : G];
-  BWide wcur[WIDE ? G / 4 : 1], wnxt[WIDE ? G / 4 : 1];
-  if (total > 0) {
-    if constexpr (WIDE)
-      load_wide(0, wcur);
-    else
-      load_group(0, cur);
-  }
-  for (int j = 0; j < total; ++j) {
-    if (j + 1 < total) {
-      if constexpr (WIDE)
-        load_wide(j + 1, wnxt);
-      else
-        load_group(j + 1, nxt);
-    }
-    const int kg = (j % gpt) * G;
+  if constexpr (!WIDE) {
+    // bf16 E: two register sets of G k-steps used in turn; group j + 1 is requested before
+    // group j feeds the MFMAs. Every group issues the same memory operations, so that each
+    // wait covers exactly what it needs: a group with no tile is requested with an empty range
+    // (zeros, no memory access, at a valid address), and the stores of a group have an empty
+    // range unless it finishes a tile (or, with STG, a round).
+    //
+    // STG (the logits of a round fit in LDS): the block works in rounds; in round r wave w
+    // takes tile t0 + 16 r + w, so a round covers 256 adjacent columns. Every wave runs every
+    // round and the block meets after each: the round's logits gather in LDS, leave as whole
+    // 16-byte pieces of each row while the next round streams in, and the greedy candidates are
+    // taken from LDS. Without STG each tile's logits leave from registers, as 64-byte pieces
+    // of four rows (partial cache lines, which cost several times their bytes).
+    const int nrounds = (t1 - t0 + 15) / 16;
+    const int ngroups = STG ? nrounds * gpt : total;  // groups each wave runs
+    auto tile_of = [&](int j) { return STG ? t0 + 16 * (j / gpt) + wave : t0 + wave + (j / gpt) * 16; };
+    auto load = [&](int j, u32x4 (&dst)[G]) __attribute__((always_inline)) {
+      const bool live = j < ngroups && tile_of(j) < t1;
+      const int tile = live ? tile_of(j) : 0, kg = live ? (j % gpt) * G : 0;
+      const char* base = (const char*)E.w + (int64_t)tile * 16 * K * 2;  // the tile's first row
+      const uint32_t roff = (uint32_t)((min(tile * 16 + (lane & 15), E.rows - 1) - tile * 16) * K) * 2;
 #pragma unroll
-    for (int i = 0; i < G; ++i) {
-      if (kg + i < ksteps) {
-        bf16x8 bf;
-        if constexpr (WIDE) {
-          BRaw<WF> r;
-          r.codes = wcur[i >> 2].codes[i & 3];
-          r.scale = wcur[i >> 2].scale;
-          if constexpr (WF == DEC_UINT4_G32) r.zp = wcur[i >> 2].zp;
-          bf = b_frag<WF>(r);
-        } else {
-          bf = b_frag<WF>(cur[WIDE ? 0 : i]);
-        }
+      for (int i = 0; i < G; ++i)
+        dst[i] = load_uniform_base(base, roff + (uint32_t)(min(kg + i, ksteps - 1) * 32 + kl) * 2,
+                                   live ? 0x7fffffff : 0);
+    };
+    auto consume = [&](int j, const u32x4 (&src)[G]) __attribute__((always_inline)) {
+      const int kg = (j % gpt) * G;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const bf16x8 af = __builtin_bit_cast(bf16x8, *(const u32x4*)(s_h + (mt * 16 + (lane & 15)) * KS +
-                                                                       kof(kg, i)));
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc[mt], 0, 0, 0);
-        }
-      }
-    }
-    if (j % gpt == gpt - 1) {  // the tile is complete: store its logits, start the next one
-      const int tile = t0 + wave + (j / gpt) * 16;
-      const int ncol = tile * 16 + (lane & 15);
+      for (int i = 0; i < G; ++i) {
+        if (kg + i < ksteps) {
+          const bf16x8 bf = __builtin_bit_cast(bf16x8, src[i]);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = mt * 16 + (lane >> 4) * 4 + r;
-          const float logit = acc[mt][r] * s_inv[m];
-          if (m < M && ncol < a.N) {
-            ((float*)a.C)[(int64_t)m * a.ldc + ncol] = logit;
-            if constexpr (AMX)
-              if (amx) greedy_better(bv[AMX ? mt : 0][r], bi[AMX ? mt : 0][r], logit, ncol);
+          for (int mt = 0; mt < MT; ++mt) {
+            const bf16x8 af = __builtin_bit_cast(bf16x8, *(const u32x4*)(s_h + (mt * 16 + (lane & 15)) * KS +
+                                                                         kof(kg, i)));
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc[mt], 0, 0, 0);
           }
         }
-        acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
+    };
+    // STG: the round stage [2][MT * 16][RS] after the activation rows; thread t keeps the
+    // greedy best of row t / 32 over columns 8 (t % 32) .. + 7 of every round
+    constexpr int RS = 256 + 4;
+    float* const rst = (float*)(s_h + MT * 16 * KS);
+    const int grow = threadIdx.x >> 5, gcol = (threadIdx.x & 31) * 8;
+    float gbv = -__builtin_inff();
+    int gbi = 0x7fffffff;
+    auto finish = [&](int j) __attribute__((always_inline)) {
+      const bool end = j >= 0 && j < ngroups && j % gpt == gpt - 1;  // group j completes a tile
+      const int tile = tile_of(max(j, 0));
+      const int ncol = tile * 16 + (lane & 15);
+      if constexpr (STG) {
+        const int r = max(j, 0) / gpt;
+        float* const st = rst + (r & 1) * MT * 16 * RS;
+        const int rc0 = (t0 + 16 * r) * 16;                 // the round's first column
+        const int rcols = max(0, min(256, min(t1 * 16, a.N) - rc0));  // its columns (a multiple of 4)
+        if (end) {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int m = mt * 16 + (lane >> 4) * 4 + q;
+              st[m * RS + wave * 16 + (lane & 15)] = acc[mt][q] * s_inv[m];
+            }
+            acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+          // (the stage writes are done; the loads in flight stay in flight: no fence on them)
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          __builtin_amdgcn_s_barrier();
+          asm volatile("" ::: "memory");
+          if (amx && grow < M) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (gcol + e < rcols) greedy_better(gbv, gbi, st[grow * RS + gcol + e], rc0 + gcol + e);
+          }
+        }
+        // the round's rows, 16 bytes a thread per store (an empty range on the other groups)
+        const __amdgpu_buffer_rsrc_t cr =
+            __builtin_amdgcn_make_buffer_rsrc(a.C, 0, end ? M * a.ldc * 4 : 0, 0x00020000);
+#pragma unroll
+        for (int q = 0; q < MT * 16 * 64 / 1024; ++q) {
+          const int idx = threadIdx.x + 1024 * q, row = idx >> 6, c4 = (idx & 63) * 4;
+          const bool in = end && row < M && c4 < rcols;
+          const u32x4 v = in ? *(const u32x4*)(st + row * RS + c4) : u32x4{0u, 0u, 0u, 0u};
+          __builtin_amdgcn_raw_buffer_store_b128(v, cr, in ? (int)((row * a.ldc + rc0 + c4) * 4) : (int)0x80000000u,
+                                                 0, 0);
+        }
+      } else {
+        const __amdgpu_buffer_rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)((float*)a.C + (end ? (int64_t)tile * 16 : 0)), 0, end ? ((M - 1) * a.ldc + 16) * 4 : 0,
+            0x00020000);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int m = mt * 16 + (lane >> 4) * 4 + q;
+            const float logit = acc[mt][q] * s_inv[m];
+            const bool in = m < M && ncol < a.N;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(logit), cr,
+                                                  in ? (int)((m * a.ldc + (lane & 15)) * 4) : (int)0x80000000u, 0, 0);
+            if constexpr (AMX)
+              if (amx && end && in) greedy_better(bv[AMX ? mt : 0][q], bi[AMX ? mt : 0][q], logit, ncol);
+          }
+          if (end) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    };
+    u32x4 ga[G], gb[G];
+    load(0, ga);
+    // (stores with an empty range after the first loads, as every later group has them: the
+    // loop is then entered with the operations in flight that each later pass sees, so its waits
+    // are not taken for the first pass's smaller count)
+    finish(-1);
+    for (int j = 0; j < ngroups; j += 2) {
+      load(j + 1, gb);
+      consume(j, ga);
+      finish(j);
+      load(j + 2, ga);
+      consume(j + 1, gb);  // (past the last group: zeros into a cleared accumulator)
+      finish(j + 1);
     }
-    if constexpr (WIDE) {
+    if constexpr (STG) {
+      // the greedy candidates: the 32 threads of a row (half a wave) in a fixed butterfly
+      if (amx) {
 #pragma unroll
-      for (int h = 0; h < G / 4; ++h) wcur[h] = wnxt[h];
-    } else {
-#pragma unroll
-      for (int i = 0; i < G; ++i) cur[i] = nxt[i];
+        for (int o = 1; o < 32; o <<= 1) {
+          const float v = __shfl_xor(gbv, o, 64);
+          const int i = __shfl_xor(gbi, o, 64);
+          greedy_better(gbv, gbi, v, i);
+        }
+        if ((threadIdx.x & 31) == 0 && grow < M) {
+          a.am_v[(int64_t)grow * gridDim.x + blockIdx.x] = gbv;
+          a.am_i[(int64_t)grow * gridDim.x + blockIdx.x] = gbi;
+        }
+      }
+      return;
+    }
+  } else {
+  BRaw<WF> cur[WIDE ? 1 : G], nxt[WIDE ? 1 : G];
+    BWide wcur[WIDE ? G / 4 : 1], wnxt[WIDE ? G / 4 : 1];
+    if (total > 0) {
+      if constexpr (WIDE)
+        load_wide(0, wcur);
+      else
+        load_group(0, cur);
+    }
+    for (int j = 0; j < total; ++j) {
+      if (j + 1 < total) {
+        if constexpr (WIDE)
+          load_wide(j + 1, wnxt);
+        else
+          load_group(j + 1, nxt);
+      }
+      const int kg = (j % gpt) * G;
+  #pragma unroll
+      for (int i = 0; i < G; ++i) {
+        if (kg + i < ksteps) {
+          bf16x8 bf;
+          if constexpr (WIDE) {
+            BRaw<WF> r;
+            r.codes = wcur[i >> 2].codes[i & 3];
+            r.scale = wcur[i >> 2].scale;
+            if constexpr (WF == DEC_UINT4_G32) r.zp = wcur[i >> 2].zp;
+            bf = b_frag<WF>(r);
+          } else {
+            bf = b_frag<WF>(cur[WIDE ? 0 : i]);
+          }
+  #pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            const bf16x8 af = __builtin_bit_cast(bf16x8, *(const u32x4*)(s_h + (mt * 16 + (lane & 15)) * KS +
+                                                                         kof(kg, i)));
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc[mt], 0, 0, 0);
+          }
+        }
+      }
+      if (j % gpt == gpt - 1) {  // the tile is complete: store its logits, start the next one
+        const int tile = t0 + wave + (j / gpt) * 16;
+        const int ncol = tile * 16 + (lane & 15);
+  #pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int m = mt * 16 + (lane >> 4) * 4 + r;
+            const float logit = acc[mt][r] * s_inv[m];
+            if (m < M && ncol < a.N) {
+              ((float*)a.C)[(int64_t)m * a.ldc + ncol] = logit;
+              if constexpr (AMX)
+                if (amx) greedy_better(bv[AMX ? mt : 0][r], bi[AMX ? mt : 0][r], logit, ncol);
+            }
+          }
+          acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+      if constexpr (WIDE) {
+  #pragma unroll
+        for (int h = 0; h < G / 4; ++h) wcur[h] = wnxt[h];
+      } else {
+  #pragma unroll
+        for (int i = 0; i < G; ++i) cur[i] = nxt[i];
+      }
     }
   }
   if constexpr (AMX) {
@@ -768,6 +909,10 @@ __global__ __launch_bounds__(1024) void lmhead_decode(GemmArgs a) {
   }
 }
 
+// dynamic LDS of the decode LM head at most: a compute unit's 160 KB (gfx950) less 8 KB for the
+// kernel's static arrays (s_inv and the greedy candidates, 4.2 KB at 64 rows)
+constexpr size_t kLmheadLdsMax = (160 - 8) * 1024;
+
 // one block per compute unit, or fewer when the vocabulary is small
 static int lmhead_blocks(int N) {
   static int cus = 0;
@@ -782,19 +927,27 @@ static int lmhead_blocks(int N) {
 
 int lmhead_decode_parts(int M, int N) { return M >= 1 && M <= 32 ? lmhead_blocks(N) : 0; }
 
-template <int WF, int MT>
-static hipError_t lmhead_go(const GemmArgs& a, hipStream_t s) {
-  const size_t lds = (size_t)MT * 16 * (a.K + 8) * 2;
+template <int WF, int MT, bool STG>
+static hipError_t lmhead_go_stg(const GemmArgs& a, size_t lds, int blocks, hipStream_t s) {
   static bool attr = false;  // raise the dynamic LDS limit once per instantiation
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)lmhead_decode<WF, MT>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
+    hipError_t e = hipFuncSetAttribute((const void*)lmhead_decode<WF, MT, STG>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLmheadLdsMax);
     if (e != hipSuccess) return e;
     attr = true;
   }
-  const int blocks = lmhead_blocks(a.N);
-  launch_kernel(lmhead_decode<WF, MT>, dim3(blocks), dim3(1024), (uint32_t)lds, s, a);
+  launch_kernel(lmhead_decode<WF, MT, STG>, dim3(blocks), dim3(1024), (uint32_t)lds, s, a);
   return hipGetLastError();
+}
+
+template <int WF, int MT>
+static hipError_t lmhead_go(const GemmArgs& a, hipStream_t s) {
+  const int blocks = lmhead_blocks(a.N);
+  const size_t lds = (size_t)MT * 16 * (a.K + 8) * 2;
+  const size_t stage = (size_t)2 * MT * 16 * (256 + 4) * 4;  // two rounds of logits
+  if (WF == DEC_BF16 && MT <= 2 && a.N % 4 == 0 && a.ldc % 4 == 0 && lds + stage <= kLmheadLdsMax)
+    return lmhead_go_stg<WF, MT, true>(a, lds + stage, blocks, s);
+  return lmhead_go_stg<WF, MT, false>(a, lds, blocks, s);
 }
 
 bool lmhead_decode_supported(int wdtype, int M, int K) {
