@@ -22,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libdec.so")
 
-SOURCES = ["dec_host.hip", "k_misc.hip", "k_gemm.hip", "k_gemm_big.hip", "k_attn.hip", "k_sample.hip", "kv_pool.hip", "loader.hip"]
+SOURCES = ["dec_host.hip", "k_misc.hip", "k_gemm.hip", "k_gemm_big.hip", "k_attn.hip", "k_attn_prefill.hip", "k_sample.hip", "kv_pool.hip", "loader.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 CFLAGS = [
