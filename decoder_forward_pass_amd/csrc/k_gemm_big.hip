@@ -394,35 +394,68 @@ __global__ __launch_bounds__(512) void gemm_big(GemmArgs a, QkRopeArgs qk) {
     auto dfrag = [&](const uint16_t* S, int row, int ks) {
       return __builtin_bit_cast(bf16x8, *(const u32x4*)(S + row * kDK + (((ks * 2 + (lane >> 5)) ^ fsw) * 8)));
     };
-    dma(0);
-    if (nkd > 1) dma(1);
-    if (nkd > 2) dma(2);
-    for (int t = 0; t < nkd; ++t) {
-      // this wave's loads of step t have landed once at most those of the later issued steps
-      // are outstanding; the barrier then publishes step t and frees the stage of step t - 1
-      // (whose fragment reads completed before their MFMAs). A plain s_barrier: the
-      // workgroup fence of __syncthreads would also wait for the loads still in flight.
-      if (t + 2 < nkd)
-        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-      else if (t + 1 < nkd)
-        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      if (t + 3 < nkd) dma(t + 3);
+    // Fragments of step t + 1 are read from LDS while step t's MFMAs run (two register sets,
+    // used in turn; K / 32 is even); the loads of the three steps after t + 1 are in flight.
+    struct Frags {
+      bf16x8 a[2][2], b[2][4];
+    };
+    auto read = [&](int t, Frags& f) __attribute__((always_inline)) {
       const uint16_t* As = lds + (t & (kDStages - 1)) * kDStage;
       const uint16_t* Bs = As + kBT * kDK;
-      bf16x8 af[2][2], bfr[2][4];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-        for (int bi = 0; bi < 2; ++bi) af[ks][bi] = dfrag(As, wm * 64 + bi * 32 + fr, ks);
+        for (int bi = 0; bi < 2; ++bi) f.a[ks][bi] = dfrag(As, wm * 64 + bi * 32 + fr, ks);
 #pragma unroll
-        for (int bj = 0; bj < 4; ++bj) bfr[ks][bj] = dfrag(Bs, brow_of(bj) + fr, ks);
+        for (int bj = 0; bj < 4; ++bj) f.b[ks][bj] = dfrag(Bs, brow_of(bj) + fr, ks);
       }
+    };
+    dma(0);
+    if (nkd > 1) dma(1);
+    if (nkd > 2) dma(2);
+    if (nkd > 3) dma(3);
+    // stage 0 has landed for this wave once at most the later stages' loads are outstanding
+    if (nkd > 3)
+      asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    else if (nkd > 2)
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else if (nkd > 1)
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    Frags fa, fb;
+    read(0, fa);
+    auto step = [&](int t, const Frags& cur, Frags& nxt) __attribute__((always_inline)) {
+      // stage t + 1 has landed for this wave (the stages after it, up to t + 3, may be in
+      // flight) and this wave's reads of stage t are done; the barrier then publishes stage
+      // t + 1 and frees stage t for the loads of step t + 4. A plain s_barrier: the workgroup
+      // fence of __syncthreads would also wait for the loads still in flight.
+      const int later = min(nkd - 1, t + 3) - (t + 1);
+      if (later >= 2)
+        asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
+      else if (later == 1)
+        asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (t + 4 < nkd) dma(t + 4);
+      read(min(t + 1, nkd - 1), nxt);  // (the last step reads its own stage again, unused)
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) mfma_step(af[ks], bfr[ks]);
+      for (int ks = 0; ks < 2; ++ks) mfma_step(cur.a[ks], cur.b[ks]);
+      // one fragment read between matrix instructions, so the reads complete under them
+#pragma unroll
+      for (int i = 0; i < 12; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    };
+    for (int t = 0; t < nkd; t += 2) {
+      step(t, fa, fb);
+      step(t + 1, fb, fa);
     }
   } else {
   const int nk = K / kBK;
