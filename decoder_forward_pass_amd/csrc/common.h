@@ -105,6 +105,13 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// SwiGLU of one feature, silu(g) * u = g / (1 + exp(-g)) * u, with the hardware reciprocal
+// (within an ulp; the product is rounded to bf16 or kept as float32 after). Every GEMM family
+// that can compute a prefill row uses this one expression, so their results stay identical.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
+
 // ---- greedy choice ("Candle model runner" 2.6: greedy takes the argmax, ties to the lowest
 // id). Keeps (bv, bi) or takes (v, i) when v is larger, or equal with a lower id; NaN never
 // wins. The choice is the same in any order of combination.

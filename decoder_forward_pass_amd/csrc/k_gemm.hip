@@ -205,7 +205,7 @@ __global__ __launch_bounds__(256) void gemm_tile64(GemmArgs a) {
     } else if constexpr (EPI == EPI_RESID) {
       ((float*)a.C)[o] = xo[e] + ov[e];
     } else {
-      const float y = ov[e] / (1.0f + __expf(-ov[e])) * ou[e];
+      const float y = silu_mul(ov[e], ou[e]);
       if (a.c_bf16)
         ((uint16_t*)a.C)[o] = f32_to_bf16_bits(y);
       else
@@ -565,7 +565,7 @@ __global__ __launch_bounds__(512) void gemm_decode(GemmArgs a, int nw) {
       }
     } else {
       if (in) {
-        const float y = v[0] / (1.0f + __expf(-v[0])) * v[NB - 1];
+        const float y = silu_mul(v[0], v[NB - 1]);
         if (a.c_bf16)
           ((uint16_t*)a.C)[o] = f32_to_bf16_bits(y);
         else

@@ -109,7 +109,7 @@ __device__ __forceinline__ void big_epilogue(const GemmArgs& a, const QkRopeArgs
           const int f = n0 + wn * 64 + bj * 32 + fr;
           if (f >= a.N) continue;
           const float g = acc[bi][bj][i], u = acc[bi][bj + 2][i];
-          const float y = g / (1.0f + __expf(-g)) * u;
+          const float y = silu_mul(g, u);
           if (a.c_bf16)
             ((uint16_t*)a.C)[(int64_t)m * a.ldc + f] = f32_to_bf16_bits(y);
           else
@@ -128,24 +128,34 @@ __device__ __forceinline__ void big_epilogue(const GemmArgs& a, const QkRopeArgs
       gq[b] = qk.q_norm[b * 32 + fr];
       gk[b] = qk.k_norm[b * 32 + fr];
     }
-    static_for<2 * NBI>([&](auto q_c) {
+    // Rows in batches of 8 (2 NBI batches): the next batch's positions, blocks and rotation
+    // factors are requested before the current batch is normalised, rotated and stored, so the
+    // rotation table's latency is paid once rather than once per batch
+    constexpr int NCS = D >= 64 ? BPH / 2 : 1;
+    struct Rows {
+      float2 cs[8][NCS];  // (the rows' positions and blocks are read again from LDS)
+    };
+    auto fetch = [&](auto q_c, Rows& rw) __attribute__((always_inline)) {
       constexpr int bi = decltype(q_c)::value >> 1, i0 = (decltype(q_c)::value & 1) * 8;
-      // 8 rows' positions, blocks and rotation factors, requested together
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int pos = s_pos[row_of(bi, i0 + r) - m0];
+#pragma unroll
+        for (int b = 0; b < NCS; ++b)
+          rw.cs[r][b] = qk.rope[(int64_t)pos * HALF + (D >= 64 ? b * 32 + fr : (fr & 15))];
+      }
+    };
+    auto work = [&](auto q_c, const Rows& rw) __attribute__((always_inline)) {
+      constexpr int bi = decltype(q_c)::value >> 1, i0 = (decltype(q_c)::value & 1) * 8;
       int pos_r[8];
       int64_t blk_r[8];
-      constexpr int NCS = D >= 64 ? BPH / 2 : 1;
-      float2 cs_r[8][NCS];
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         const int lr = row_of(bi, i0 + r) - m0;
         pos_r[r] = s_pos[lr];
         blk_r[r] = s_blk[lr];
       }
-#pragma unroll
-      for (int r = 0; r < 8; ++r)
-#pragma unroll
-        for (int b = 0; b < NCS; ++b)
-          cs_r[r][b] = qk.rope[(int64_t)pos_r[r] * HALF + (D >= 64 ? b * 32 + fr : (fr & 15))];
+      const float2 (&cs_r)[8][NCS] = rw.cs;
       static_for<8>([&](auto r_c) {
         constexpr int r = decltype(r_c)::value, i = i0 + r;
         const int m = row_of(bi, i);
@@ -164,7 +174,7 @@ __device__ __forceinline__ void big_epilogue(const GemmArgs& a, const QkRopeArgs
 #pragma unroll
             for (int b = 0; b < BPH; ++b) ss += v[b] * v[b];
             ss = group_sum<32>(ss);
-            const float inv = 1.0f / sqrtf(ss / (float)D + qk.eps);
+            const float inv = __builtin_amdgcn_rsqf(ss / (float)D + qk.eps);  // (hardware rsqrt, within an ulp)
             const bool isq = hh < H;
             if constexpr (D >= 64) {
 #pragma unroll
@@ -208,6 +218,13 @@ __device__ __forceinline__ void big_epilogue(const GemmArgs& a, const QkRopeArgs
           }
         });
       });
+    };
+    Rows ra, rb;
+    fetch(std::integral_constant<int, 0>{}, ra);
+    static_for<2 * NBI>([&](auto q_c) {
+      constexpr int q = decltype(q_c)::value;
+      if constexpr (q + 1 < 2 * NBI) fetch(std::integral_constant<int, q + 1>{}, (q & 1) ? ra : rb);
+      work(q_c, (q & 1) ? rb : ra);
     });
   }
 }
