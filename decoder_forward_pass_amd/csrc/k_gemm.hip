@@ -19,18 +19,40 @@
 
 namespace dec {
 
-template <int WF, int EPI>
-__global__ __launch_bounds__(256) void gemm_tile64(GemmArgs a) {
+// this wave's direct-to-LDS loads of a stage have landed once at most `later` stages' loads
+// (PER each) issued after them are outstanding (later in 0 .. MAXL)
+template <int PER, int MAXL>
+__device__ __forceinline__ void wait_vm_stages(int later) {
+  if constexpr (MAXL > 0) {
+    if (later >= MAXL) {
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER * MAXL) : "memory");
+      return;
+    }
+    wait_vm_stages<PER, MAXL - 1>(later);
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+}
+
+// BM < 64 (float32 only): one wave per BM x BM tile (32 or 16), for grids of 64 x 64 tiles too
+// small to fill the chip; every output element still gets the same MFMA sequence, so a row's
+// result does not change with the tile size.
+template <int WF, int EPI, int BM>
+__global__ __launch_bounds__(BM == 64 ? 256 : 64) void gemm_tile64(GemmArgs a) {
   constexpr bool F32 = WF == DEC_F32;
-  constexpr int BM = 64, BN = 64;
+  static_assert(BM == 64 || (F32 && (BM == 32 || BM == 16)), "smaller tiles: float32 only");
+  constexpr int WAVES = BM == 64 ? 4 : 1, BN = BM;
+  constexpr int SUB = BM == 16 ? 1 : 2;  // float32: 16 x 16 MFMA blocks per wave, each way
   constexpr int BK = F32 ? 16 : 64;  // elements of K per LDS tile
   constexpr int RW = F32 ? 17 : 36;  // LDS row stride in 32-bit words (padded)
   constexpr int NB = EPI == EPI_SWIGLU ? 2 : 1;
-  __shared__ uint32_t As[BM * RW];
-  __shared__ uint32_t Bs[NB][BN * RW];
+  __shared__ uint32_t As[F32 ? 1 : BM * RW];
+  __shared__ uint32_t Bs[NB][F32 ? 1 : BN * RW];
+  // float32: the direct-to-LDS ring (stages of 16 K-columns: 8 of 64 rows or 16 of 32 rows)
+  extern __shared__ __attribute__((aligned(16))) uint32_t f32_ring[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = WAVES == 4 ? wave >> 1 : 0, wn = WAVES == 4 ? wave & 1 : 0;
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
   const int M = a.M, K = a.K;
 
@@ -52,30 +74,87 @@ __global__ __launch_bounds__(256) void gemm_tile64(GemmArgs a) {
 
   // float32 weights: 2 x 2 blocks of 16 x 16 per wave (v_mfma_f32_16x16x4_f32); bf16 / uint4:
   // one 32 x 32 block per wave (v_mfma_f32_32x32x16_bf16, the full-rate bf16 shape)
-  f32x4 acc[NB][2][2];
+  f32x4 acc[NB][SUB][SUB];
   f32x16 acc32[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < SUB; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[nb][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < SUB; ++j) acc[nb][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc32[nb][e] = 0.f;
   }
 
+  if constexpr (F32) {
+    // float32: both operands go straight from memory to LDS (direct-to-LDS loads) through a
+    // ring of FR stages of 16 K-columns, FR - 1 of them in flight, so the K loop is not one
+    // memory round trip per 16 columns. A stage holds BM rows of 64 B per operand; chunk c (4
+    // floats) of row r sits at position c ^ ((r / 4) % 4), which keeps the 16-row fragment
+    // reads on distinct banks. A load fills 16 rows (1 KB: lane l fills row l / 4, position
+    // l % 4); the waves share the BM / 16 loads of each operand. The MFMA sequence is the one
+    // below.
+    constexpr int LPW = BM / 16 / WAVES;     // 16-row loads per operand per wave
+    constexpr int FR = 8, SROWS = BM * 16;  // stages; floats per operand per stage
+    float* const ring = reinterpret_cast<float*>(f32_ring);
+    const int nk = K / BK;
+    const float* asrc[LPW];
+    const float* bsrc[NB][LPW];
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int lrow = (wave * LPW + i) * 16 + (lane >> 2), lch = (lane & 3) ^ ((lrow >> 2) & 3);
+      asrc[i] = (const float*)a.A + (int64_t)min(m0 + lrow, M - 1) * a.lda + lch * 4;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        bsrc[nb][i] = (const float*)bm[nb].w + (int64_t)min(br0 + lrow, bm[nb].rows - 1) * K + lch * 4;
+    }
+    auto dma = [&](int t) {
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        float* st = ring + (t % FR) * (1 + NB) * SROWS + (wave * LPW + i) * 256;
+        __builtin_amdgcn_global_load_lds((const void*)(asrc[i] + t * BK),
+                                         (void __attribute__((address_space(3)))*)st, 16, 0, 0);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          __builtin_amdgcn_global_load_lds((const void*)(bsrc[nb][i] + t * BK),
+                                           (void __attribute__((address_space(3)))*)(st + (1 + nb) * SROWS), 16, 0,
+                                           0);
+      }
+    };
+    for (int t = 0; t < min(nk, FR - 1); ++t) dma(t);
+    // (a fragment read: row r, chunk ks, lane's k ks * 4 + lane / 16)
+    auto frag = [&](const float* S, int r, int ks) {
+      return S[r * 16 + ((ks ^ ((r >> 2) & 3)) << 2) + (lane >> 4)];
+    };
+    for (int t = 0; t < nk; ++t) {
+      // stage t has landed for this wave once at most the later issued stages' loads are
+      // outstanding; the barrier publishes it and frees stage t - 1 (read in the last step)
+      const int later = min(FR - 2, nk - 1 - t);
+      wait_vm_stages<(1 + NB) * LPW, FR - 2>(later);
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (t + FR - 1 < nk) dma(t + FR - 1);
+      const float* As_ = ring + (t % FR) * (1 + NB) * SROWS;
+#pragma unroll
+      for (int ks = 0; ks < BK / 4; ++ks) {
+        float af[SUB];
+#pragma unroll
+        for (int bi = 0; bi < SUB; ++bi) af[bi] = frag(As_, wm * 32 + bi * 16 + (lane & 15), ks);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int bj = 0; bj < SUB; ++bj) {
+            const float bf = frag(As_ + (1 + nb) * SROWS, wn * 32 + bj * 16 + (lane & 15), ks);
+#pragma unroll
+            for (int bi = 0; bi < SUB; ++bi)
+              acc[nb][bi][bj] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[bi], bf, acc[nb][bi][bj], 0, 0, 0);
+          }
+      }
+    }
+  } else
   for (int k0 = 0; k0 < K; k0 += BK) {
     // ---- stage A
-    if constexpr (F32) {
-      const int row = tid >> 2, c4 = tid & 3;
-      const int gm = min(m0 + row, M - 1);
-      const float4 v = *(const float4*)((const float*)a.A + (int64_t)gm * a.lda + k0 + c4 * 4);
-      uint32_t* d = As + row * RW + c4 * 4;
-      d[0] = __float_as_uint(v.x);
-      d[1] = __float_as_uint(v.y);
-      d[2] = __float_as_uint(v.z);
-      d[3] = __float_as_uint(v.w);
-    } else {
+    {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int c = tid + 256 * i;
@@ -89,16 +168,7 @@ __global__ __launch_bounds__(256) void gemm_tile64(GemmArgs a) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int brows = bm[nb].rows;
-      if constexpr (WF == DEC_F32) {
-        const int row = tid >> 2, c4 = tid & 3;
-        const int gr = min(br0 + row, brows - 1);
-        const float4 v = *(const float4*)((const float*)bm[nb].w + (int64_t)gr * K + k0 + c4 * 4);
-        uint32_t* d = Bs[nb] + row * RW + c4 * 4;
-        d[0] = __float_as_uint(v.x);
-        d[1] = __float_as_uint(v.y);
-        d[2] = __float_as_uint(v.z);
-        d[3] = __float_as_uint(v.w);
-      } else if constexpr (WF == DEC_BF16) {
+      if constexpr (WF == DEC_BF16) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const int c = tid + 256 * i;
@@ -128,25 +198,7 @@ __global__ __launch_bounds__(256) void gemm_tile64(GemmArgs a) {
     __syncthreads();
 
     // ---- MFMA over the tile, K ascending
-    if constexpr (F32) {
-#pragma unroll
-      for (int ks = 0; ks < BK / 4; ++ks) {
-        float af[2];
-#pragma unroll
-        for (int bi = 0; bi < 2; ++bi)
-          af[bi] = __uint_as_float(As[(wm * 32 + bi * 16 + (lane & 15)) * RW + ks * 4 + (lane >> 4)]);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-          for (int bj = 0; bj < 2; ++bj) {
-            const float bf =
-                __uint_as_float(Bs[nb][(wn * 32 + bj * 16 + (lane & 15)) * RW + ks * 4 + (lane >> 4)]);
-#pragma unroll
-            for (int bi = 0; bi < 2; ++bi)
-              acc[nb][bi][bj] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[bi], bf, acc[nb][bi][bj], 0, 0, 0);
-          }
-      }
-    } else {
+    {
       // lane l: row l % 32 of its 32-row block, k = 16 ks + 8 (l / 32) .. +8
 #pragma unroll
       for (int ks = 0; ks < BK / 16; ++ks) {
@@ -167,16 +219,18 @@ __global__ __launch_bounds__(256) void gemm_tile64(GemmArgs a) {
   // 32 x 32 block: lane holds column lane % 32, rows 8 (i / 4) + 4 (lane / 32) + i % 4.
   // the 16 outputs of a lane: (row, column, value, SwiGLU up value); the residual values are
   // all requested before any is updated
+  // (float32 16-row tiles: one 16 x 16 block per wave, NE = 4 outputs per lane)
+  constexpr int NE = F32 ? SUB * SUB * 4 : 16;
   int om[16], on[16];
   float ov[16], ou[16];
   if constexpr (F32) {
 #pragma unroll
-    for (int bi = 0; bi < 2; ++bi)
+    for (int bi = 0; bi < SUB; ++bi)
 #pragma unroll
-      for (int bj = 0; bj < 2; ++bj)
+      for (int bj = 0; bj < SUB; ++bj)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int e = (bi * 2 + bj) * 4 + r;
+          const int e = (bi * SUB + bj) * 4 + r;
           om[e] = m0 + wm * 32 + bi * 16 + (lane >> 4) * 4 + r;
           on[e] = n0 + wn * 32 + bj * 16 + (lane & 15);
           ov[e] = acc[0][bi][bj][r];
@@ -194,10 +248,10 @@ __global__ __launch_bounds__(256) void gemm_tile64(GemmArgs a) {
   float xo[16];
   if constexpr (EPI == EPI_RESID) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) xo[e] = ((const float*)a.C)[(int64_t)min(om[e], M - 1) * a.ldc + min(on[e], a.N - 1)];
+    for (int e = 0; e < NE; ++e) xo[e] = ((const float*)a.C)[(int64_t)min(om[e], M - 1) * a.ldc + min(on[e], a.N - 1)];
   }
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
+  for (int e = 0; e < NE; ++e) {
     if (om[e] >= M || on[e] >= a.N) continue;
     const int64_t o = (int64_t)om[e] * a.ldc + on[e];
     if constexpr (EPI == EPI_STORE) {
@@ -214,16 +268,45 @@ __global__ __launch_bounds__(256) void gemm_tile64(GemmArgs a) {
   }
 }
 
+template <int WF, int EPI, int BM>
+static hipError_t tile64_go(const GemmArgs& a, hipStream_t s) {
+  // float32: the stage ring in dynamic LDS (8 stages x (1 + NB) operands x BM rows x 64 B)
+  constexpr int NB = EPI == EPI_SWIGLU ? 2 : 1;
+  const uint32_t lds = WF == DEC_F32 ? 8 * (1 + NB) * BM * 16 * 4 : 0;
+  if (lds) {
+    static bool attr = false;  // raise the dynamic LDS limit once per instantiation
+    if (!attr) {
+      hipError_t e = hipFuncSetAttribute((const void*)gemm_tile64<WF, EPI, BM>,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      attr = true;
+    }
+  }
+  const dim3 g((a.N + BM - 1) / BM, (a.M + BM - 1) / BM);
+  launch_kernel(gemm_tile64<WF, EPI, BM>, g, dim3(BM == 64 ? 256 : 64), lds, s, a);
+  return hipGetLastError();
+}
+
+template <int WF, int EPI>
+static hipError_t tile64_pick(const GemmArgs& a, hipStream_t s) {
+  // float32: 64 x 64 tiles (4 waves) when there are at least 256 of them, else single-wave
+  // 32 x 32 tiles when there are at least 512, else 16 x 16 (the same results either way)
+  if constexpr (WF == DEC_F32) {
+    auto tiles = [&](int t) { return (int64_t)((a.N + t - 1) / t) * ((a.M + t - 1) / t); };
+    if (tiles(64) < 256) return tiles(32) >= 512 ? tile64_go<WF, EPI, 32>(a, s) : tile64_go<WF, EPI, 16>(a, s);
+  }
+  return tile64_go<WF, EPI, 64>(a, s);
+}
+
 template <int WF>
 static hipError_t gemm_epi(int epi, const GemmArgs& a, hipStream_t s) {
-  dim3 g((a.N + 63) / 64, (a.M + 63) / 64), b(256);
+  if (WF == DEC_F32 && a.K % 16) return hipErrorInvalidValue;
   switch (epi) {
-    case EPI_STORE: launch_kernel(gemm_tile64<WF, EPI_STORE>, g, b, 0, s, a); break;
-    case EPI_RESID: launch_kernel(gemm_tile64<WF, EPI_RESID>, g, b, 0, s, a); break;
-    case EPI_SWIGLU: launch_kernel(gemm_tile64<WF, EPI_SWIGLU>, g, b, 0, s, a); break;
+    case EPI_STORE: return tile64_pick<WF, EPI_STORE>(a, s);
+    case EPI_RESID: return tile64_pick<WF, EPI_RESID>(a, s);
+    case EPI_SWIGLU: return tile64_pick<WF, EPI_SWIGLU>(a, s);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 hipError_t launch_gemm(int wdtype, int epi, const GemmArgs& a, hipStream_t s) {
