@@ -8,18 +8,19 @@ namespace dec {
 // ---- flash-style prefill attention (f16 pool, MFMA) ----------------------------------------
 // Causal attention of one sequence's new rows over its paged keys ("Candle model runner" 2.4,
 // second equation; keys up to and including the query's absolute position), read in place from
-// the pool. The 128 positions of a query tile are split over SPLIT blocks per KV head (one block
-// of 4 G waves, or two blocks of 2 G waves each taking 64 positions; two smaller blocks share a
-// CU and run out of step, so one's matrix products overlap the other's softmax and staging);
-// wave w takes head w / (4 / SPLIT) of the KV head's group and 32 query positions. The split
-// changes no operation applied to a query. Key tiles of 64 positions, aligned to position 0 of
-// the sequence, are staged in LDS (K row-major, V transposed, two stages, the next tile loaded
-// while the current one is used). Per key tile and wave, with v_mfma_f32_32x32x16_f16:
+// the pool. A block has 4 waves of 32 query positions: one head and 128 positions (one-head
+// groups), or two heads and 64 positions (two-head groups, a 128-position query tile split over
+// two blocks). Two blocks share a compute unit and run out of step, so one's matrix products
+// overlap the other's softmax. Key tiles of 64 positions, aligned to position 0 of the
+// sequence, are staged in LDS by direct-to-LDS loads (two stages, the next tile loaded while
+// the current one is used). Per key tile and wave, with v_mfma_f32_32x32x16_f16:
 //   S^T = K . Q^T (keys x queries), scaled into the exp2 domain and causally masked;
 //   online softmax per query (a query's 64 scores sit in lanes l and l ^ 32);
 //   O^T += V^T . P^T, where P^T is taken from the S^T accumulators as they are: a lane's eight
 //   k-slots of k-step s stand for keys 16 s + 8 (j / 4) + 4 (l / 32) + j % 4, a fixed
-//   relabelling of the summation index applied to both operands.
+//   relabelling of the summation index applied to both operands. V stays row-major in LDS;
+//   gfx950's transposing LDS read (ds_read_b64_tr_b16) hands each lane four consecutive keys
+//   of its channel.
 // A query sees the key tiles 0 .. floor(pos / 64) in order; a later, fully masked tile leaves
 // its state unchanged bit for bit (scale exp2(0) = 1, weights exp2(-inf) = 0, masked values
 // zero). The result therefore does not depend on how queries are grouped into tiles, so
@@ -27,33 +28,43 @@ namespace dec {
 
 namespace {
 constexpr int kPfKT = 64;  // keys per tile
+// One LDS stage: the K tile [64 keys][D] and the V tile [64 keys][D], row-major f16. The
+// 16-byte chunk c of row r is stored at chunk position c ^ f(r), so that the fragment reads
+// meet no bank conflict: fk for K (the 16 rows of a 16-byte-per-lane read pass at one chunk
+// index), fv for V (the 4 rows x 4 chunks of a transposing read pass).
 template <int D>
 struct PrefillLds {
-  static constexpr int KSTR = D + 8;      // K row stride (halves): 32-row fragment reads conflict-free
-  // V^T row stride (halves): 34 words, so the 32 rows of a 64-bit fragment read fall on 32
-  // distinct bank pairs
-  static constexpr int VSTR = kPfKT + 4;
-  static constexpr int KS = kPfKT * KSTR, VS = D * VSTR;
-  static constexpr size_t bytes = (size_t)2 * (KS + VS) * 2;  // two stages
+  static constexpr int ROWB = 2 * D;              // bytes per key row
+  static constexpr int TILEB = kPfKT * ROWB;      // one matrix tile
+  static constexpr int STAGEB = 2 * TILEB;        // K | V
+  static constexpr size_t bytes = (size_t)2 * STAGEB;
+  static constexpr int NC = D / 8;                // 16-byte chunks per row
+  static constexpr int RPW = 16 / NC;             // rows per 256-byte bank window
+  static constexpr int RPI = 1024 / ROWB;         // rows per 1 KB direct-to-LDS load of a wave
+  static constexpr int NI = 16 / RPI;             // such loads per wave and matrix (16 rows each)
+  __device__ static int fk(int r) { return (r / RPW) % NC; }
+  __device__ static int fv(int r) { return RPW < 4 ? 4 * ((r / RPW) % (4 / RPW)) : 0; }
 };
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 }  // namespace
 
 template <int D, int G, int SPLIT, bool BF16_OUT>
-__global__ __launch_bounds__(256 * G / SPLIT) __attribute__((amdgpu_waves_per_eu(SPLIT)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void attn_prefill_kernel(AttnPrefillArgs a) {
   using L = PrefillLds<D>;
   constexpr int KT = kPfKT, QT = kPrefillQueryTile;
   constexpr int WPH = 4 / SPLIT;           // waves per head
   constexpr int QB = QT / SPLIT;           // query positions per block
-  constexpr int NT = 64 * WPH * G;         // threads: G heads x WPH waves of 32 queries
-  constexpr int KSTR = L::KSTR, VSTR = L::VSTR;
+  constexpr int ROWB = L::ROWB;
   constexpr int NDS = D / 16;              // k-steps of S^T over the head dimension
   constexpr int NDB = D / 32;              // 32-row blocks of O^T
-  constexpr int NKC = KT * (D / 8);        // 16-byte K chunks per tile
-  static_assert(QT == 128 && (SPLIT == 1 || SPLIT == 2), "4 / SPLIT waves of 32 query positions per head");
-  extern __shared__ __attribute__((aligned(16))) uint16_t plds[];  // [stage][K | V^T]
+  static_assert(QT == 128 && SPLIT == G && WPH * G == 4, "4 waves of 32 query positions per block");
+  static_assert(D == 32 || D == 64 || D == 128, "head dimension");
+  extern __shared__ __attribute__((aligned(16))) char plds[];  // [stage][K | V]
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5, ql = lane & 31;
   const int gh = wave / WPH, qsub = wave % WPH;
   const int kvh = blockIdx.x, tile = blockIdx.y / SPLIT, qb0 = (blockIdx.y % SPLIT) * QB;
@@ -66,11 +77,13 @@ void attn_prefill_kernel(AttnPrefillArgs a) {
   const int pmax = p0 + min(qb0 + QB, tile_rows) - 1;  // the block's last query position
   const int H = a.n_heads;
   const int bsh = a.pool.block_shift, bmask = a.pool.block_tokens - 1;
-  const int32_t* table = a.b.block_tables + (int64_t)seq * a.b.tbl_stride;
-  const int64_t slab = (int64_t)a.n_kv_heads * a.pool.block_tokens * D;
-  const uint16_t* kbase = (const uint16_t*)a.pool.base + (int64_t)a.layer * 2 * a.pool.n_blocks * slab +
-                          (int64_t)kvh * a.pool.block_tokens * D;
-  const uint16_t* vbase = kbase + a.pool.n_blocks * slab;
+  // the table is not written while the kernel runs: read it through the scalar cache
+  const __attribute__((address_space(4))) int32_t* table =
+      (const __attribute__((address_space(4))) int32_t*)(a.b.block_tables + (int64_t)seq * a.b.tbl_stride);
+  const int64_t slab_b = (int64_t)a.n_kv_heads * a.pool.block_tokens * ROWB;  // bytes per pool block
+  const char* kbase = (const char*)a.pool.base + (int64_t)a.layer * 2 * a.pool.n_blocks * slab_b +
+                      (int64_t)kvh * a.pool.block_tokens * ROWB;
+  const char* vbase = kbase + a.pool.n_blocks * slab_b;
   const int head = kvh * G + gh;
 
   // this lane's query (column of S^T and O^T)
@@ -84,70 +97,50 @@ void attn_prefill_kernel(AttnPrefillArgs a) {
   for (int ks = 0; ks < NDS; ++ks)
     qf[ks] = __builtin_bit_cast(f16x8, *(const u32x4*)(a.q + ((int64_t)qrow * H + head) * D + ks * 16 + hl * 8));
 
-  // ---- staging of key tile kt through registers: K in 16-byte chunks, V in blocks of 2 keys x
-  // 8 channels transposed in registers (32 consecutive threads fill one row of V^T). The pool
-  // block of every key of a tile is fetched ahead (lane j of each wave: key j of the tile) and
-  // handed out by lane shuffles. A key past the context reads the last key's slot (in bounds)
-  // and is written to LDS as zeros; nothing is applied to the loaded registers before they are
-  // stored, so the loads of a tile stay in flight for a whole step.
-  constexpr int KPT = (NKC + NT - 1) / NT;
-  constexpr int NV2 = (KT / 2) * (D / 8);  // 2 x 8 V blocks per tile
-  constexpr int VPT = (NV2 + NT - 1) / NT;
+  // ---- staging. Wave w loads rows 16 w .. 16 w + 15 of the K and V tiles (in one pool block,
+  // since blocks hold at least 16 positions) with 1 KB direct-to-LDS loads through a buffer
+  // descriptor whose range ends at the context's last key: rows past it (and a whole tile past
+  // the block's last query) arrive as zeros, and nothing outside the block is read. Lane l of
+  // load i fills row i * RPI + l / NC at chunk position l % NC, so it reads the chunk that
+  // position stands for.
   const int last_key = ctx_end - 1;
-  auto block_ids = [&](int kt) {
-    return table[min(kt * KT + lane, last_key) >> bsh];
+  uint32_t dk[L::NI], dv[L::NI];
+#pragma unroll
+  for (int i = 0; i < L::NI; ++i) {
+    const int x = i * L::RPI + lane / L::NC, pc = lane % L::NC;
+    dk[i] = x * ROWB + ((pc ^ L::fk(x)) * 16);
+    dv[i] = x * ROWB + ((pc ^ L::fv(x)) * 16);
+  }
+  auto block_id = [&](int kt) { return table[min(kt * KT + 16 * wave, last_key) >> bsh]; };
+  auto dma = [&](int kt, int blk, int st, bool live) {
+    const int r0 = kt * KT + 16 * wave;
+    // (wave-uniform; made explicit so that the descriptor stays in scalar registers)
+    const int rows = __builtin_amdgcn_readfirstlane(live ? min(max(last_key + 1 - r0, 0), 16) : 0);
+    const int64_t off = (int64_t)blk * slab_b + (int64_t)(r0 & bmask) * ROWB;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + off), 0, rows * ROWB, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + off), 0, rows * ROWB, 0x00020000);
+    char* sk = plds + st * L::STAGEB + 16 * wave * ROWB;
+#pragma unroll
+    for (int i = 0; i < L::NI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (void __attribute__((address_space(3)))*)(sk + i * 1024), 16, (int)dk[i], 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < L::NI; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (void __attribute__((address_space(3)))*)(sk + L::TILEB + i * 1024), 16, (int)dv[i], 0, 0, 0);
   };
-  struct Regs {
-    u32x4 k[KPT], v[VPT][2];
-  };
-  auto load_tile = [&](int kt, int bids, Regs& r) {
+
+  // fragment read offsets within a stage. K: lane (ql, hl) reads row 32 kb + ql, chunk
+  // 2 ks + hl. V (transposing read): lane l supplies row 16 s + 8 h + 4 (l / 32) + (l / 4) % 4
+  // at channels 32 db + 16 ((l / 16) % 2) + 4 (l % 4) .. + 3 and receives channel 32 db + ql of
+  // that group of four rows.
+  uint32_t ka[NDS], va[NDB];
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int c = min(tid + j * NT, NKC - 1);
-      const int key = c / (D / 8), part = c % (D / 8);
-      const int kpos = kt * KT + key;
-      const int64_t blk = __shfl(bids, key, 64);
-      r.k[j] = *(const u32x4*)(kbase + blk * slab + (min(kpos, last_key) & bmask) * D + part * 8);
-    }
+  for (int ks = 0; ks < NDS; ++ks) ka[ks] = ql * ROWB + (((2 * ks + hl) ^ L::fk(ql)) * 16);
+  {
+    const int g = lane >> 4, jj = (lane >> 2) & 3, t = lane & 3;
 #pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      const int vb = min(tid + j * NT, NV2 - 1);
-      const int k2 = vb % (KT / 2), d8 = vb / (KT / 2);
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int key = k2 * 2 + e, kpos = kt * KT + key;
-        const int64_t blk = __shfl(bids, key, 64);
-        r.v[j][e] = *(const u32x4*)(vbase + blk * slab + (min(kpos, last_key) & bmask) * D + d8 * 8);
-      }
-    }
-  };
-  auto store_tile = [&](int st, int kt, const Regs& r) {
-    uint16_t* Ks = plds + (size_t)st * (L::KS + L::VS);
-    uint16_t* Vt = Ks + L::KS;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int c = tid + j * NT;
-      const int key = c / (D / 8);
-      if (NKC % NT == 0 || c < NKC)  // (every thread has KPT chunks when NT divides NKC)
-        *(u32x4*)(Ks + key * KSTR + (c % (D / 8)) * 8) = kt * KT + key > last_key ? zero : r.k[j];
-    }
-#pragma unroll
-    for (int j = 0; j < VPT; ++j) {
-      const int vb = tid + j * NT;
-      if (NV2 % NT != 0 && vb >= NV2) continue;
-      const int k2 = vb % (KT / 2), d8 = vb / (KT / 2);
-      const u32x4 v0 = kt * KT + k2 * 2 > last_key ? zero : r.v[j][0];
-      const u32x4 v1 = kt * KT + k2 * 2 + 1 > last_key ? zero : r.v[j][1];
-      // v0 / v1 word w holds channels (2w, 2w + 1) of keys 2 k2 / 2 k2 + 1; row d of V^T gets both
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        const uint32_t x0 = v0[d >> 1], x1 = v1[d >> 1];
-        *(uint32_t*)(Vt + (d8 * 8 + d) * VSTR + k2 * 2) =
-            (d & 1) ? ((x0 >> 16) | (x1 & 0xffff0000u)) : ((x0 & 0xffffu) | (x1 << 16));
-      }
-    }
-  };
+    for (int db = 0; db < NDB; ++db)
+      va[db] = L::TILEB + (4 * (g >> 1) + jj) * ROWB + (((db * 4 + 2 * (g & 1) + (t >> 1)) ^ L::fv(jj)) * 16) + (t & 1) * 8;
+  }
 
   f32x16 o[NDB];
 #pragma unroll
@@ -158,27 +151,33 @@ void attn_prefill_kernel(AttnPrefillArgs a) {
   const float sl2 = 1.4426950408889634f / sqrtf((float)D);
   const int n_kt = pmax / KT + 1;
 
-  // Pipeline: tile kt is used from LDS stage kt % 2 while tile kt + 1 (in registers since the
-  // previous step) is written to the other stage and tile kt + 2 is requested from memory. The
-  // block ids of a tile are requested one step before its data, ahead of the previous tile's
-  // loads, so that waiting for them does not wait for those loads. Every step issues the same
-  // loads (the last tile is requested again near the end, in bounds and unused), so each wait
-  // covers exactly the loads of the step before.
-  Regs ra, rb;
-  const int b0 = block_ids(0);
-  const int b1 = block_ids(min(1, n_kt - 1));
-  load_tile(0, b0, ra);
-  int ba = block_ids(min(2, n_kt - 1)), bb;
-  load_tile(min(1, n_kt - 1), b1, rb);
-  store_tile(0, 0, ra);
+  // Pipeline: tile kt is used from stage kt % 2 while tile kt + 1 is loaded into the other
+  // stage (freed by the barrier that ended the step before); each step ends with a wait for
+  // its loads and a barrier. A tile's pool block is read a step before its loads are issued.
+  // Every step issues the same loads (a tile past the last is loaded with an empty range).
+  int bnext = block_id(0);
+  dma(0, bnext, 0, true);
+  bnext = block_id(min(1, n_kt - 1));
   __syncthreads();
-  auto step = [&](int kt, const Regs& next, Regs& fill, int buse, int& bload) {
-    const int st = kt & 1;
-    bload = block_ids(min(kt + 3, n_kt - 1));
-    load_tile(min(kt + 2, n_kt - 1), buse, fill);
-    if (kt < n_kt) {  // (the step past an odd tile count only keeps the loads and stores in step)
-    const uint16_t* Ks = plds + (size_t)st * (L::KS + L::VS);
-    const uint16_t* Vt = Ks + L::KS;
+  auto step = [&](int kt, const int st) {  // (st is a literal at both calls)
+    const char* S = plds + st * L::STAGEB;
+    // V^T fragments of the whole tile, read before the next tile's loads are issued (an LDS
+    // read after them would wait for them: the compiler cannot tell the two stages apart)
+    f16x8 vf[4][NDB];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const char* vr = S + va[db] + 16 * s4 * ROWB;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vr);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vr + 8 * ROWB));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        vf[s4][db] = __builtin_bit_cast(f16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+      }
+    __builtin_amdgcn_sched_barrier(0);  // (keeps the reads above the loads)
+    dma(kt + 1, bnext, st ^ 1, kt + 1 < n_kt);
+    bnext = block_id(min(kt + 2, n_kt - 1));
+    if (kt < n_kt) {  // (the step past an odd tile count only keeps the loads in step)
 
     // S^T = K . Q^T for the tile's 64 keys (two 32-key blocks)
     f32x16 sacc[2];
@@ -188,7 +187,7 @@ void attn_prefill_kernel(AttnPrefillArgs a) {
       for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < NDS; ++ks) {
-        const f16x8 kf = __builtin_bit_cast(f16x8, *(const u32x4*)(Ks + (kb * 32 + ql) * KSTR + ks * 16 + hl * 8));
+        const f16x8 kf = __builtin_bit_cast(f16x8, *(const u32x4*)(S + kb * 32 * ROWB + ka[ks]));
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], sacc[kb], 0, 0, 0);
       }
     }
@@ -242,25 +241,15 @@ void attn_prefill_kernel(AttnPrefillArgs a) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) pf[j] = (_Float16)sacc[s4 >> 1][8 * (s4 & 1) + j];
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const uint16_t* vr = Vt + (db * 32 + ql) * VSTR + 16 * s4 + 4 * hl;
-        const u32x2 lo = *(const u32x2*)vr;
-        const u32x2 hi = *(const u32x2*)(vr + 8);
-        const f16x8 vf = __builtin_bit_cast(f16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf, o[db], 0, 0, 0);
-      }
+      for (int db = 0; db < NDB; ++db) o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[s4][db], pf, o[db], 0, 0, 0);
     }
     }
-    // (on the last steps this fills the other stage with a tile no wave reads: the stage was
-    // last read before the previous barrier, and the loop ends within a step)
-    store_tile(st ^ 1, kt + 1, next);
     __syncthreads();
   };
-  // steps in pairs, so that the two register sets keep their roles; every step issues the same
-  // memory operations, and only the compute of a step past the last tile is skipped
+  // steps in pairs, so that each step's stage is a constant
   for (int kt = 0; kt < n_kt; kt += 2) {
-    step(kt, rb, ra, ba, bb);
-    step(kt + 1, ra, rb, bb, ba);
+    step(kt, 0);
+    step(kt + 1, 1);
   }
 
   if (!qvalid) return;
@@ -302,7 +291,7 @@ static hipError_t prefill_launch(const AttnPrefillArgs& a, dim3 g, hipStream_t s
     attr = true;
   }
   g.y *= SPLIT;
-  const dim3 blk(64 * (4 / SPLIT) * G);
+  const dim3 blk(256);
   if (a.out_bf16)
     launch_kernel(attn_prefill_kernel<D, G, SPLIT, true>, g, blk, (uint32_t)lds, s, a);
   else
