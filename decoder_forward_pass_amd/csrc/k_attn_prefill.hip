@@ -47,6 +47,18 @@ struct PrefillLds {
 };
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+// the reference maximum of a query moves only past this margin (log2 units: weights <= 256)
+constexpr float kLag = 8.0f;
+// max / sum of a value and its partner 32 lanes away (gfx950 row swap: no LDS round trip;
+// both operations are commutative, so both lanes get the same bits)
+__device__ __forceinline__ float swap_halves_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap_halves_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 }  // namespace
 
 template <int D, int G, int SPLIT, bool BF16_OUT>
@@ -195,8 +207,12 @@ void attn_prefill_kernel(AttnPrefillArgs a) {
     // wave's first query position needs the causal mask; elsewhere every key is visible.
     // The tile maximum is taken over the raw scores and scaled afterwards (scaling by a
     // positive constant is monotone under rounding, so this is the maximum of the scaled
-    // scores), and a weight is exp2(s * scale - m) with one rounding. Key 0 is in tile 0 and
-    // visible to every query, so m is finite from the first tile on.
+    // scores). The reference m of a query moves only when a tile's maximum exceeds it by more
+    // than kLag (log2 units): weights are exp2(s * scale - m) <= 2^kLag (exact in f16's range),
+    // and the accumulators are rescaled by exp2(m_old - m_new) only then, so after the first
+    // tiles they are rarely touched. Any reference gives the same quotient O / l; the choice
+    // depends only on the query's own scores, so it is the same in every grouping of queries.
+    // Key 0 is in tile 0 and visible to every query, so m is finite from the first tile on.
     if (kt * KT + KT - 1 > wq0) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -211,22 +227,32 @@ void attn_prefill_kernel(AttnPrefillArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mt = fmaxf(mt, sacc[kb][i]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float mnew = fmaxf(m, mt * sl2);
-    const float alpha = __builtin_amdgcn_exp2f(m - mnew);  // exp2(-inf) = 0 on the first tile
-    float ps = 0.f;
+    mt = swap_halves_max(mt);
+    const float mtile = mt * sl2;
+    const float mnew = mtile > m + kLag ? mtile : m;      // (m = -inf on the first tile)
+    const float alpha = __builtin_amdgcn_exp2f(m - mnew);  // exactly 1 when m stays; 0 on the first tile
+    // weights, rounded to f16 as the MFMA operand; l adds the rounded weights (v_dot2_f32_f16
+    // against ones), the values the products use
+    f16x8 pf[4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[kb][i], sl2, -mnew));
-        sacc[kb][i] = p;
-        ps += p;
-      }
-    ps += __shfl_xor(ps, 32, 64);
+      for (int j = 0; j < 8; ++j)
+        pf[s4][j] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(sacc[s4 >> 1][8 * (s4 & 1) + j], sl2, -mnew));
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+    float ps0 = 0.f, ps1 = 0.f;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      ps0 = __builtin_amdgcn_fdot2(f16x2{pf[s4][0], pf[s4][1]}, ones, ps0, false);
+      ps1 = __builtin_amdgcn_fdot2(f16x2{pf[s4][2], pf[s4][3]}, ones, ps1, false);
+      ps0 = __builtin_amdgcn_fdot2(f16x2{pf[s4][4], pf[s4][5]}, ones, ps0, false);
+      ps1 = __builtin_amdgcn_fdot2(f16x2{pf[s4][6], pf[s4][7]}, ones, ps1, false);
+    }
+    const float ps = swap_halves_sum(ps0 + ps1);
     l = l * alpha + ps;
     m = mnew;
-    // a running maximum that moved in no lane leaves the accumulators as they are (alpha = 1)
+    // accumulators are rescaled only when some lane's reference moved (else alpha = 1)
     if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
@@ -236,13 +262,9 @@ void attn_prefill_kernel(AttnPrefillArgs a) {
 
     // O^T += V^T . P^T over four 16-key steps
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      f16x8 pf;
+    for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) pf[j] = (_Float16)sacc[s4 >> 1][8 * (s4 & 1) + j];
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[s4][db], pf, o[db], 0, 0, 0);
-    }
+      for (int db = 0; db < NDB; ++db) o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[s4][db], pf[s4], o[db], 0, 0, 0);
     }
     __syncthreads();
   };
