@@ -12,8 +12,9 @@ namespace dec {
 // groups), or two heads and 64 positions (two-head groups, a 128-position query tile split over
 // two blocks). Two blocks share a compute unit and run out of step, so one's matrix products
 // overlap the other's softmax. Key tiles of 64 positions, aligned to position 0 of the
-// sequence, are staged in LDS by direct-to-LDS loads (two stages, the next tile loaded while
-// the current one is used). Per key tile and wave, with v_mfma_f32_32x32x16_f16:
+// sequence, are staged in LDS by direct-to-LDS loads, two tiles of K and two of V; while tile
+// t is finished, S^T of tile t + 1 is computed and the next tiles load. Per key tile and
+// wave, with v_mfma_f32_32x32x16_f16:
 //   S^T = K . Q^T (keys x queries), scaled into the exp2 domain and causally masked;
 //   online softmax per query (a query's 64 scores sit in lanes l and l ^ 32);
 //   O^T += V^T . P^T, where P^T is taken from the S^T accumulators as they are: a lane's eight
@@ -28,16 +29,14 @@ namespace dec {
 
 namespace {
 constexpr int kPfKT = 64;  // keys per tile
-// One LDS stage: the K tile [64 keys][D] and the V tile [64 keys][D], row-major f16. The
-// 16-byte chunk c of row r is stored at chunk position c ^ f(r), so that the fragment reads
-// meet no bank conflict: fk for K (the 16 rows of a 16-byte-per-lane read pass at one chunk
-// index), fv for V (the 4 rows x 4 chunks of a transposing read pass).
+// LDS tiles: K or V of 64 keys, [64 keys][D] row-major f16. The 16-byte chunk c of row r is
+// stored at chunk position c ^ f(r), so that the fragment reads meet no bank conflict: fk for
+// K (the 16 rows of a 16-byte-per-lane read pass at one chunk index), fv for V (the 4 rows x 4
+// chunks of a transposing read pass).
 template <int D>
 struct PrefillLds {
   static constexpr int ROWB = 2 * D;              // bytes per key row
-  static constexpr int TILEB = kPfKT * ROWB;      // one matrix tile
-  static constexpr int STAGEB = 2 * TILEB;        // K | V
-  static constexpr size_t bytes = (size_t)2 * STAGEB;
+  static constexpr int TILEB = kPfKT * ROWB;      // one tile
   static constexpr int NC = D / 8;                // 16-byte chunks per row
   static constexpr int RPW = 16 / NC;             // rows per 256-byte bank window
   static constexpr int RPI = 1024 / ROWB;         // rows per 1 KB direct-to-LDS load of a wave
@@ -73,7 +72,9 @@ void attn_prefill_kernel(AttnPrefillArgs a) {
   constexpr int NDB = D / 32;              // 32-row blocks of O^T
   static_assert(QT == 128 && SPLIT == G && WPH * G == 4, "4 waves of 32 query positions per block");
   static_assert(D == 32 || D == 64 || D == 128, "head dimension");
-  extern __shared__ __attribute__((aligned(16))) char plds[];  // [stage][K | V]
+  // two K tiles and two V tiles, as four arrays: the compiler then knows that a tile being read
+  // is not the one being loaded, and places no wait for the loads before the reads
+  __shared__ __attribute__((aligned(16))) char ks0[L::TILEB], ks1[L::TILEB], vs0[L::TILEB], vs1[L::TILEB];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -124,23 +125,20 @@ void attn_prefill_kernel(AttnPrefillArgs a) {
     dv[i] = x * ROWB + ((pc ^ L::fv(x)) * 16);
   }
   auto block_id = [&](int kt) { return table[min(kt * KT + 16 * wave, last_key) >> bsh]; };
-  auto dma = [&](int kt, int blk, int st, bool live) {
+  // rows 16 w .. 16 w + 15 of key tile kt of one matrix into an LDS tile
+  auto dma = [&](const char* base, int kt, int blk, char* dst, bool live, const uint32_t (&dof)[L::NI]) {
     const int r0 = kt * KT + 16 * wave;
     // (wave-uniform; made explicit so that the descriptor stays in scalar registers)
     const int rows = __builtin_amdgcn_readfirstlane(live ? min(max(last_key + 1 - r0, 0), 16) : 0);
     const int64_t off = (int64_t)blk * slab_b + (int64_t)(r0 & bmask) * ROWB;
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + off), 0, rows * ROWB, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + off), 0, rows * ROWB, 0x00020000);
-    char* sk = plds + st * L::STAGEB + 16 * wave * ROWB;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)(base + off), 0, rows * ROWB, 0x00020000);
+    char* d = dst + 16 * wave * ROWB;
 #pragma unroll
     for (int i = 0; i < L::NI; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (void __attribute__((address_space(3)))*)(sk + i * 1024), 16, (int)dk[i], 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < L::NI; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (void __attribute__((address_space(3)))*)(sk + L::TILEB + i * 1024), 16, (int)dv[i], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (void __attribute__((address_space(3)))*)(d + i * 1024), 16, (int)dof[i], 0, 0, 0);
   };
 
-  // fragment read offsets within a stage. K: lane (ql, hl) reads row 32 kb + ql, chunk
+  // fragment read offsets within a tile. K: lane (ql, hl) reads row 32 kb + ql, chunk
   // 2 ks + hl. V (transposing read): lane l supplies row 16 s + 8 h + 4 (l / 32) + (l / 4) % 4
   // at channels 32 db + 16 ((l / 16) % 2) + 4 (l % 4) .. + 3 and receives channel 32 db + ql of
   // that group of four rows.
@@ -151,7 +149,7 @@ void attn_prefill_kernel(AttnPrefillArgs a) {
     const int g = lane >> 4, jj = (lane >> 2) & 3, t = lane & 3;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
-      va[db] = L::TILEB + (4 * (g >> 1) + jj) * ROWB + (((db * 4 + 2 * (g & 1) + (t >> 1)) ^ L::fv(jj)) * 16) + (t & 1) * 8;
+      va[db] = (4 * (g >> 1) + jj) * ROWB + (((db * 4 + 2 * (g & 1) + (t >> 1)) ^ L::fv(jj)) * 16) + (t & 1) * 8;
   }
 
   f32x16 o[NDB];
@@ -163,56 +161,32 @@ void attn_prefill_kernel(AttnPrefillArgs a) {
   const float sl2 = 1.4426950408889634f / sqrtf((float)D);
   const int n_kt = pmax / KT + 1;
 
-  // Pipeline: tile kt is used from stage kt % 2 while tile kt + 1 is loaded into the other
-  // stage (freed by the barrier that ended the step before); each step ends with a wait for
-  // its loads and a barrier. A tile's pool block is read a step before its loads are issued.
-  // Every step issues the same loads (a tile past the last is loaded with an empty range).
-  int bnext = block_id(0);
-  dma(0, bnext, 0, true);
-  bnext = block_id(min(1, n_kt - 1));
-  __syncthreads();
-  auto step = [&](int kt, const int st) {  // (st is a literal at both calls)
-    const char* S = plds + st * L::STAGEB;
-    // V^T fragments of the whole tile, read before the next tile's loads are issued (an LDS
-    // read after them would wait for them: the compiler cannot tell the two stages apart)
-    f16x8 vf[4][NDB];
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const char* vr = S + va[db] + 16 * s4 * ROWB;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vr);
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vr + 8 * ROWB));
-        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-        vf[s4][db] = __builtin_bit_cast(f16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
-      }
-    __builtin_amdgcn_sched_barrier(0);  // (keeps the reads above the loads)
-    dma(kt + 1, bnext, st ^ 1, kt + 1 < n_kt);
-    bnext = block_id(min(kt + 2, n_kt - 1));
-    if (kt < n_kt) {  // (the step past an odd tile count only keeps the loads in step)
-
-    // S^T = K . Q^T for the tile's 64 keys (two 32-key blocks)
-    f32x16 sacc[2];
+  // S^T = K . Q^T for a tile's 64 keys (two 32-key blocks)
+  auto scores = [&](const char* Ks, f32x16 (&sacc)[2]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < NDS; ++ks) {
-        const f16x8 kf = __builtin_bit_cast(f16x8, *(const u32x4*)(S + kb * 32 * ROWB + ka[ks]));
+        const f16x8 kf = __builtin_bit_cast(f16x8, *(const u32x4*)(Ks + kb * 32 * ROWB + ka[ks]));
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[ks], sacc[kb], 0, 0, 0);
       }
     }
-    // online softmax of this lane's query over the tile. Only a tile that reaches past the
-    // wave's first query position needs the causal mask; elsewhere every key is visible.
-    // The tile maximum is taken over the raw scores and scaled afterwards (scaling by a
-    // positive constant is monotone under rounding, so this is the maximum of the scaled
-    // scores). The reference m of a query moves only when a tile's maximum exceeds it by more
-    // than kLag (log2 units): weights are exp2(s * scale - m) <= 2^kLag (exact in f16's range),
-    // and the accumulators are rescaled by exp2(m_old - m_new) only then, so after the first
-    // tiles they are rarely touched. Any reference gives the same quotient O / l; the choice
-    // depends only on the query's own scores, so it is the same in every grouping of queries.
-    // Key 0 is in tile 0 and visible to every query, so m is finite from the first tile on.
+  };
+  // online softmax of this lane's query over tile kt, then O^T += V^T . P^T. Only a tile that
+  // reaches past the wave's first query position needs the causal mask; elsewhere every key
+  // is visible. The tile maximum is taken over the raw scores and scaled afterwards (scaling
+  // by a positive constant is monotone under rounding, so this is the maximum of the scaled
+  // scores). The reference m of a query moves only when a tile's maximum exceeds it by more
+  // than kLag (log2 units): weights are exp2(s * scale - m) <= 2^kLag (exact in f16's range),
+  // and the accumulators are rescaled by exp2(m_old - m_new) only then, so after the first
+  // tiles they are rarely touched. Any reference gives the same quotient O / l; the choice
+  // depends only on the query's own scores, so it is the same in every grouping of queries.
+  // Key 0 is in tile 0 and visible to every query, so m is finite from the first tile on.
+  // (S^T of the next tile, from Kn into sn, is computed here too: its matrix products are
+  // interleaved with this tile's vector work)
+  auto softmax_pv = [&](int kt, f32x16 (&sacc)[2], const char* Vs, const char* Kn, f32x16 (&sn)[2]) {
     if (kt * KT + KT - 1 > wq0) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -222,6 +196,7 @@ void attn_prefill_kernel(AttnPrefillArgs a) {
           if (kpos > qpos) sacc[kb][i] = -__builtin_inff();
         }
     }
+    scores(Kn, sn);
     float mt = sacc[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -252,6 +227,15 @@ void attn_prefill_kernel(AttnPrefillArgs a) {
     const float ps = swap_halves_sum(ps0 + ps1);
     l = l * alpha + ps;
     m = mnew;
+    // issue order: each matrix product of the next tile followed by a share of this tile's
+    // vector instructions; the K fragment reads run four fragments ahead
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // LDS read
+#pragma unroll
+    for (int i = 0; i < 2 * NDS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 128 / NDS, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    }
     // accumulators are rescaled only when some lane's reference moved (else alpha = 1)
     if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
@@ -259,19 +243,52 @@ void attn_prefill_kernel(AttnPrefillArgs a) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[db][e] *= alpha;
     }
-
     // O^T += V^T . P^T over four 16-key steps
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[s4][db], pf[s4], o[db], 0, 0, 0);
+      for (int db = 0; db < NDB; ++db) {
+        const char* vr = Vs + va[db] + 16 * s4 * ROWB;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)vr);
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(vr + 8 * ROWB));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        const f16x8 vf = __builtin_bit_cast(f16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[s4], o[db], 0, 0, 0);
+      }
+  };
+
+  // Pipeline. K tile t sits in ks[t % 2], V tile t in vs[t % 2]. Step kt loads K tile kt + 2
+  // and V tile kt + 1 into the arrays freed by the barrier that ended the step before, computes
+  // S^T of tile kt + 1 (independent of the softmax of tile kt, so the matrix products of one
+  // overlap the other's vector work), and finishes tile kt; it ends with a wait for its loads
+  // and a barrier. A tile's pool block is read a step before its loads are issued. Every step
+  // issues the same loads (a tile past the last is loaded with an empty range: zeros).
+  int bv = block_id(0);
+  dma(kbase, 0, bv, ks0, true, dk);
+  dma(vbase, 0, bv, vs0, true, dv);
+  bv = block_id(min(1, n_kt - 1));
+  dma(kbase, 1, bv, ks1, 1 < n_kt, dk);
+  int bk = block_id(min(2, n_kt - 1));
+  __syncthreads();
+  f32x16 sa[2], sb[2];
+  scores(ks0, sa);
+  __syncthreads();  // (step 0 loads K tile 2 into the array just read)
+  auto step = [&](int kt, f32x16 (&cur)[2], f32x16 (&nxt)[2], char* kload, const char* kread, char* vload,
+                  const char* vread) {
+    dma(kbase, kt + 2, bk, kload, kt + 2 < n_kt, dk);
+    dma(vbase, kt + 1, bv, vload, kt + 1 < n_kt, dv);
+    if (kt < n_kt) {  // (the step past an odd tile count only keeps the loads in step)
+      softmax_pv(kt, cur, vread, kread, nxt);  // (S^T past the last tile: zeros, unused)
     }
+    // (the scalar load shares a counter with the LDS reads: issued last, it delays none of them)
+    bv = bk;
+    bk = block_id(min(kt + 3, n_kt - 1));
     __syncthreads();
   };
-  // steps in pairs, so that each step's stage is a constant
+  // steps in pairs, so that each array's role in a step is fixed
   for (int kt = 0; kt < n_kt; kt += 2) {
-    step(kt, 0);
-    step(kt + 1, 1);
+    step(kt, sa, sb, ks0, ks1, vs1, vs0);
+    step(kt + 1, sb, sa, ks1, ks0, vs0, vs1);
   }
 
   if (!qvalid) return;
@@ -301,23 +318,12 @@ bool attn_prefill_supported(int head_dim, int group) {
 
 template <int D, int G, int SPLIT>
 static hipError_t prefill_launch(const AttnPrefillArgs& a, dim3 g, hipStream_t s) {
-  constexpr size_t lds = PrefillLds<D>::bytes;
-  static bool attr = false;  // raise the dynamic LDS limit once per instantiation
-  if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_prefill_kernel<D, G, SPLIT, true>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)attn_prefill_kernel<D, G, SPLIT, false>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    attr = true;
-  }
   g.y *= SPLIT;
   const dim3 blk(256);
   if (a.out_bf16)
-    launch_kernel(attn_prefill_kernel<D, G, SPLIT, true>, g, blk, (uint32_t)lds, s, a);
+    launch_kernel(attn_prefill_kernel<D, G, SPLIT, true>, g, blk, 0u, s, a);
   else
-    launch_kernel(attn_prefill_kernel<D, G, SPLIT, false>, g, blk, (uint32_t)lds, s, a);
+    launch_kernel(attn_prefill_kernel<D, G, SPLIT, false>, g, blk, 0u, s, a);
   return hipGetLastError();
 }
 
