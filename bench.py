@@ -291,8 +291,21 @@ def summarize_line(path, wl_name, steps, warmup):
         lines.append(f"- decode: {d['decode_ms_per_step']} ms per step, {d['decode_tok_s']:,} tok/s; whole phase "
                      f"{d['decode_phase']['achieved']} GB/s = {100 * d['decode_phase']['frac']:.1f}% of HBM")
     r = d["roofline"]
-    lines += [f"- roofline kernel ({r['kernel']}): {r['achieved']} {r['unit']} = {100 * r['frac']:.1f}% of {r['peak']}",
-              "", "| prefill kernel class | launches | mean us | TFLOP/s | fraction of peak | share of prefill |",
+    lines.append(f"- roofline kernel ({r['kernel']}): {r['achieved']} {r['unit']} = {100 * r['frac']:.1f}% of {r['peak']}")
+    if "hardware" in d:
+        h = d["hardware"]
+        lines.append(f"- device: {h['device']} ({h['arch']}), {h['compute_units']} compute units, clock "
+                     f"{h['clock_mhz']} MHz reported; device-to-device copy of {h['stream_copy_mib']} MiB: "
+                     f"{h['stream_copy_gbs']} GB/s (read + write) against the 8,000 GB/s peak")
+    if "cpu_baseline" in d:
+        c = d["cpu_baseline"]
+        rates = f"prefill {c['prefill_tok_s']:.1f} tok/s" if "prefill_tok_s" in c else ""
+        if "decode_tok_s" in c:
+            rates += f", decode {c['decode_tok_s']:.2f} tok/s"
+        host = c.get("host") or {}
+        lines.append(f"- CPU oracle: {c['value']:.1f} {c['unit']} ({rates}; {c['sample']}) on {c['cores']} cores"
+                     + (f", {host.get('cpu_model')}, BLAS {host.get('blas')}" if host else ""))
+    lines += ["", "| prefill kernel class | launches | mean us | TFLOP/s | fraction of peak | share of prefill |",
               "|---|---:|---:|---:|---:|---:|"]
     for k, v in d["prefill_kernels"].items():
         lines.append(f"| {k} | {v['launches']} | {v['avg_launch_us']} | {v.get('achieved_tflops', '-')} | "
@@ -399,6 +412,7 @@ def cpu_baseline(wl, shape, weights, prompts, decode_steps=8):
     chunk = wl.chunk or plen
     for c0 in range(0, plen, chunk):
         lg = dec.forward([(prompts[which][c0:c0 + chunk], c)], logits="all" if wl.split else "last")
+    t_pre = time.perf_counter() - t0
     tok = int(np.argmax(lg[-1]))
     for _ in range(decode_steps):
         lg = dec.forward([(np.array([tok]), c)], logits="last")
@@ -410,8 +424,61 @@ def cpu_baseline(wl, shape, weights, prompts, decode_steps=8):
         (" (logits of every row)" if wl.split else "")
     if decode_steps:
         what += f" + {decode_steps} greedy decode steps"
-    return {"value": n / dt, "unit": "tok/s", "cores": threads, "kind": "oracle",
-            "sample": f"1 of {wl.n_seqs} sequences{which_s}: {what}, float64 numpy, {dt:.1f} s"}
+    out = {"value": n / dt, "unit": "tok/s", "cores": threads, "kind": "oracle",
+           "sample": f"1 of {wl.n_seqs} sequences{which_s}: {what}, float64 numpy, {dt:.1f} s",
+           "prefill_tok_s": plen / t_pre, "host": host_description(threads)}
+    if decode_steps:
+        out["decode_tok_s"] = decode_steps / (dt - t_pre)
+    return out
+
+
+def host_description(threads):
+    """The host the oracle ran on: CPU model, core counts, numpy's BLAS."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        pass
+    blas = None
+    try:
+        cfg = np.show_config(mode="dicts")
+        dep = cfg.get("Build Dependencies", {}).get("blas", {})
+        blas = " ".join(str(dep[k]) for k in ("name", "version") if dep.get(k))
+    except Exception:  # (numpy builds differ in what they report)
+        pass
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "affinity_cores": threads, "blas": blas}
+
+
+def hardware_line(torch, copy_mib=1024):
+    """The device as the runtime reports it, and a measured device-to-device copy beside the
+    8 TB/s peak (read + write bytes over the copy's event time; outside the timed region)."""
+    import ctypes
+    p = torch.cuda.get_device_properties(0)
+    clock_khz = ctypes.c_int(0)
+    try:  # hipDeviceGetAttribute(hipDeviceAttributeClockRate = 5 in hip_runtime_api.h): peak clock, kHz
+        if ctypes.CDLL("libamdhip64.so").hipDeviceGetAttribute(ctypes.byref(clock_khz), 5, 0) != 0:
+            clock_khz.value = 0
+    except OSError:
+        pass
+    hw = {"device": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+          "clock_mhz": clock_khz.value / 1000 if clock_khz.value else None,
+          "hbm_gib": round(p.total_memory / 2**30, 1)}
+    src = torch.empty(copy_mib << 18, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for _ in range(2):
+        dst.copy_(src)
+    ev[0].record()
+    for _ in range(5):
+        dst.copy_(src)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / 5
+    hw["stream_copy_gbs"] = round(2 * src.numel() * 4 / (ms * 1e-3) / 1e9, 1)
+    hw["stream_copy_mib"] = copy_mib
+    del src, dst
+    return hw
 
 
 # kernel classes of the library's per-launch timing (dec.h DEC_K_*) timed over a prefill
@@ -687,6 +754,7 @@ def main():
         result["roofline"] = dict(roofline_prefill, traffic=None)
     if sampler:
         result["sampler"] = sampler
+    result["hardware"] = hardware_line(torch)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, shape, weights, prompts)
     print(json.dumps(result), flush=True)
