@@ -548,13 +548,20 @@ int run_forward(dec_ctx* ctx, uint8_t* base, const Ws& w, hipStream_t st, const 
   // Prefill calls with bf16 / uint4 weights take the 256 x 256 tile GEMM, which also applies
   // the q/k norm, RoPE and the KV write in its Q|K|V epilogue (chosen by the configuration
   // alone, so every prefill call of a model computes the same way).
-  // The other products take it when it fills the chip (>= 256 tiles, M >= 1024); both give
-  // identical results, so the choice never changes a row's bits.
+  // The other products take it when it fills the chip (>= 256 tiles, M >= 1024; SwiGLU with
+  // bf16 weights: >= 512 tiles, two rounds of blocks), else (bf16 weights) its 128 x 128 form
+  // when that fills the chip, else the 64 x 64 tiles; all give identical results, so the
+  // choice never changes a row's bits.
   const bool big = !decode && gemm_big_supported(c.weight_dtype, EPI_QKV, D);
   auto gemm = [&](int epi, const GemmArgs& g) {
     if (dgemm) return launch_gemm_decode(c.weight_dtype, epi, g, st);
-    const int tiles = (g.M + 255) / 256 * (epi == EPI_SWIGLU ? (g.N + 127) / 128 : (g.N + 255) / 256);
-    if (big && tiles >= 256 && g.M >= 1024) return launch_gemm_big(c.weight_dtype, epi, g, nullptr, st);
+    auto tiles = [&](int t) {
+      return (g.M + t - 1) / t * (epi == EPI_SWIGLU ? (g.N + t / 2 - 1) / (t / 2) : (g.N + t - 1) / t);
+    };
+    const bool mid = big && gemm_mid_supported(c.weight_dtype, epi) && tiles(128) >= 256;
+    const int big_min = mid && epi == EPI_SWIGLU ? 512 : 256;
+    if (big && tiles(256) >= big_min && g.M >= 1024) return launch_gemm_big(c.weight_dtype, epi, g, nullptr, st);
+    if (mid) return launch_gemm_mid(c.weight_dtype, epi, g, st);
     return launch_gemm(c.weight_dtype, epi, g, st);
   };
   // A of a normalising GEMM: the residual itself (decode GEMM) or the RMSNorm output

@@ -41,8 +41,6 @@ constexpr size_t kBigLds = (size_t)2 * 2 * kStage * 2;  // two stages of A and B
 // a stage holds 256 rows of 32 bf16 (64 B) of A, then of B; row r keeps its 16-byte chunk c at
 // position c ^ ((r / 4) % 4), so the 16 rows of a fragment read fall on distinct banks
 constexpr int kDK = 32, kDStages = 4;
-constexpr int kDStage = 2 * kBT * kDK;                                   // bf16 elements per stage
-constexpr size_t kBigLdsDma = (size_t)kDStages * kDStage * 2;             // bytes
 
 // f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>), expanded at compile time so
 // that accumulator indices are constants (an unroll the optimizer may decline)
@@ -62,11 +60,12 @@ struct BigRowsB {
 }  // namespace
 
 // The epilogue of a block's tile from its waves' accumulators: wave (wm, wn) holds rows
-// m0 + 32 NBI wm .. + 32 NBI (NBI blocks of 32) and the four 32-column blocks of brow_of.
-template <int WF, int EPI, int D, bool KV_F16, int NBI>
-__device__ __forceinline__ void big_epilogue(const GemmArgs& a, const QkRopeArgs& qk, f32x16 (&acc)[NBI][4], int m0,
+// m0 + 32 NBI wm .. + 32 NBI (NBI blocks of 32) and the NBJ 32-column blocks of brow_of.
+template <int WF, int EPI, int D, bool KV_F16, int NBI, int NBJ>
+__device__ __forceinline__ void big_epilogue(const GemmArgs& a, const QkRopeArgs& qk, f32x16 (&acc)[NBI][NBJ], int m0,
                                              int n0, int wm, int wn, int lane, const int* s_pos,
                                              const int64_t* s_blk) {
+  static_assert(EPI != EPI_QKV || NBJ == 4, "Q|K|V epilogue: 128 columns (whole heads) per wave");
   // lane holds column fr of each 32 x 32 block, rows 8 g + 4 (lane / 32) + r
   const int fr = lane & 31;
   const int M = a.M;
@@ -77,8 +76,8 @@ __device__ __forceinline__ void big_epilogue(const GemmArgs& a, const QkRopeArgs
 #pragma unroll
     for (int bi = 0; bi < NBI; ++bi)
 #pragma unroll
-      for (int bj = 0; bj < 4; ++bj) {
-        const int n = n0 + wn * 128 + bj * 32 + fr;
+      for (int bj = 0; bj < NBJ; ++bj) {
+        const int n = n0 + wn * (32 * NBJ) + bj * 32 + fr;
         const int nc = min(n, a.N - 1);
         float xo[16];
         if constexpr (EPI == EPI_RESID) {
@@ -105,10 +104,10 @@ __device__ __forceinline__ void big_epilogue(const GemmArgs& a, const QkRopeArgs
         const int m = row_of(bi, i);
         if (m >= M) continue;
 #pragma unroll
-        for (int bj = 0; bj < 2; ++bj) {
-          const int f = n0 + wn * 64 + bj * 32 + fr;
+        for (int bj = 0; bj < NBJ / 2; ++bj) {
+          const int f = n0 + wn * (16 * NBJ) + bj * 32 + fr;
           if (f >= a.N) continue;
-          const float g = acc[bi][bj][i], u = acc[bi][bj + 2][i];
+          const float g = acc[bi][bj][i], u = acc[bi][bj + NBJ / 2][i];
           const float y = silu_mul(g, u);
           if (a.c_bf16)
             ((uint16_t*)a.C)[(int64_t)m * a.ldc + f] = f32_to_bf16_bits(y);
@@ -229,15 +228,21 @@ __device__ __forceinline__ void big_epilogue(const GemmArgs& a, const QkRopeArgs
   }
 }
 
-template <int WF, int EPI, int D, bool KV_F16>
+template <int WF, int EPI, int D, bool KV_F16, int TS>
 __global__ __launch_bounds__(512) void gemm_big(GemmArgs a, QkRopeArgs qk) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];  // [stage][A | B][256][kLR]
+  // TS x TS tiles: 256 (every format and epilogue), or 128 (bf16 weights; store, residual and
+  // SwiGLU epilogues) for grids of 256-tiles too small to fill the chip. Waves 4 x 2, each
+  // TS / 4 rows (NBI blocks of 32) by TS / 2 columns (NBJ blocks of 32).
+  static_assert(TS == 256 || (TS == 128 && WF == DEC_BF16 && EPI != EPI_QKV), "128-tiles: bf16, no Q|K|V");
+  constexpr int NBI = TS / 128, NBJ = TS / 64;
+  constexpr int TN = EPI == EPI_SWIGLU ? TS / 2 : TS;  // output columns (features) per tile
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];  // [stage][A | B][TS][row]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int M = a.M, K = a.K;
-  const int mt_n = (M + kBT - 1) / kBT;
-  const int nt_n = EPI == EPI_SWIGLU ? (a.N + 127) / 128 : (a.N + kBT - 1) / kBT;
+  const int mt_n = (M + TS - 1) / TS;
+  const int nt_n = (a.N + TN - 1) / TN;
 
   // ---- block id -> tile (contiguous runs per L2 domain, 8 M tiles per group)
   const int nblk = gridDim.x;
@@ -246,15 +251,15 @@ __global__ __launch_bounds__(512) void gemm_big(GemmArgs a, QkRopeArgs qk) {
   const int gsz = 8 * nt_n;
   const int grp = bid / gsz, gm0 = grp * 8, gmn = min(8, mt_n - gm0);
   const int tm = gm0 + (bid % gsz) % gmn, tn = (bid % gsz) / gmn;
-  const int m0 = tm * kBT;
-  const int n0 = EPI == EPI_SWIGLU ? tn * 128 : tn * kBT;
+  const int m0 = tm * TS;
+  const int n0 = tn * TN;
 
   // Q|K|V: position and pool block of each of the tile's rows, fetched once up front (the
   // barriers of the main loop publish them)
-  __shared__ int s_pos[EPI == EPI_QKV ? kBT : 1];
-  __shared__ int64_t s_blk[EPI == EPI_QKV ? kBT : 1];
+  __shared__ int s_pos[EPI == EPI_QKV ? TS : 1];
+  __shared__ int64_t s_blk[EPI == EPI_QKV ? TS : 1];
   if constexpr (EPI == EPI_QKV) {
-    if (tid < kBT) {
+    if (tid < TS) {
       const int mc = min(m0 + tid, M - 1);
       const int pos = qk.b.row_pos[mc];
       s_pos[tid] = pos;
@@ -268,13 +273,13 @@ __global__ __launch_bounds__(512) void gemm_big(GemmArgs a, QkRopeArgs qk) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     ap[i] = (const uint16_t*)a.A + (int64_t)min(m0 + srow + 64 * i, M - 1) * a.lda + sc8 * 8;
-  // B row of LDS row r: SwiGLU rows 0..127 gate, 128..255 up (features n0 + r % 128); otherwise
-  // row n0 + r of the Q|K|V (or single) concatenation
+  // B row of LDS row r: SwiGLU rows 0..TS/2-1 gate, TS/2..TS-1 up (features n0 + r % (TS/2));
+  // otherwise row n0 + r of the Q|K|V (or single) concatenation
   // (segments are selected with constant indices, so the arguments stay in registers)
   auto b_src = [&](int r, int& rr) -> WMat {
     if constexpr (EPI == EPI_SWIGLU) {
-      const WMat m = r < 128 ? a.seg[0] : a.seg[1];
-      rr = min(n0 + (r & 127), m.rows - 1);
+      const WMat m = r < TS / 2 ? a.seg[0] : a.seg[1];
+      rr = min(n0 + (r & (TS / 2 - 1)), m.rows - 1);
       return m;
     } else {
       int n = min(n0 + r, a.N - 1);
@@ -353,43 +358,45 @@ __global__ __launch_bounds__(512) void gemm_big(GemmArgs a, QkRopeArgs qk) {
     }
   };
 
-  // LDS row of the wave's 32-column block bj (SwiGLU: blocks 0-1 gate, 2-3 up, same features)
+  // LDS row of the wave's 32-column block bj (SwiGLU: the first NBJ / 2 blocks gate, the others
+  // up, same features)
   auto brow_of = [&](int bj) {
     if constexpr (EPI == EPI_SWIGLU)
-      return (bj >> 1) * 128 + wn * 64 + (bj & 1) * 32;
+      return (bj / (NBJ / 2)) * (TS / 2) + wn * (16 * NBJ) + (bj % (NBJ / 2)) * 32;
     else
-      return wn * 128 + bj * 32;
+      return wn * (32 * NBJ) + bj * 32;
   };
 
   // v_mfma_f32_32x32x16_bf16: operand lane l holds row l % 32, k = 8 * (l / 32) .. +8;
   // accumulator register i of lane l is row 8 * (i / 4) + 4 * (l / 32) + i % 4, column l % 32
-  f32x16 acc[2][4];
+  f32x16 acc[NBI][NBJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NBI; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < NBJ; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  auto mfma_step = [&](const bf16x8 (&af)[2], const bf16x8 (&bf)[4]) {
+  auto mfma_step = [&](const bf16x8 (&af)[NBI], const bf16x8 (&bf)[NBJ]) {
 #pragma unroll
-    for (int bi = 0; bi < 2; ++bi)
+    for (int bi = 0; bi < NBI; ++bi)
 #pragma unroll
-      for (int bj = 0; bj < 4; ++bj)
+      for (int bj = 0; bj < NBJ; ++bj)
         acc[bi][bj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[bi], bf[bj], acc[bi][bj], 0, 0, 0);
   };
   const int fr = lane & 31, fk = (lane >> 5) * 8;
   if constexpr (WF == DEC_BF16) {
-    // Waves 0-3 stage the A rows, waves 4-7 the B rows, 64 rows per wave in four 1 KB
+    // Waves 0-3 stage the A rows, waves 4-7 the B rows, TS / 4 rows per wave in LPW 1 KB
     // direct-to-LDS loads per K step (16 rows of 64 B; lane l fills row l / 4, position l % 4,
     // from the source chunk that position holds). The loads of three K steps are in flight.
+    constexpr int LPW = TS / 64, STG = 2 * TS * kDK;  // loads per wave per step; bf16 per stage
     const int nkd = K / kDK;
     const int opb = wave >> 2, wq = wave & 3;
     const int lc = (lane & 3) ^ ((lane >> 4) & 3);
-    const uint16_t* dsrc[4];
+    const uint16_t* dsrc[LPW];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = wq * 64 + i * 16 + (lane >> 2);
+    for (int i = 0; i < LPW; ++i) {
+      const int r = wq * (TS / 4) + i * 16 + (lane >> 2);
       if (opb == 0) {
         dsrc[i] = (const uint16_t*)a.A + (int64_t)min(m0 + r, M - 1) * a.lda + lc * 8;
       } else {
@@ -398,11 +405,11 @@ __global__ __launch_bounds__(512) void gemm_big(GemmArgs a, QkRopeArgs qk) {
         dsrc[i] = (const uint16_t*)m.w + (int64_t)rr * K + lc * 8;
       }
     }
-    uint16_t* const dbase = lds + opb * kBT * kDK + wq * 64 * kDK;
+    uint16_t* const dbase = lds + opb * TS * kDK + wq * (TS / 4) * kDK;
     auto dma = [&](int t) {
-      uint16_t* d = dbase + (t & (kDStages - 1)) * kDStage;
+      uint16_t* d = dbase + (t & (kDStages - 1)) * STG;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < LPW; ++i)
         __builtin_amdgcn_global_load_lds((const void*)(dsrc[i] + t * kDK),
                                          (void __attribute__((address_space(3)))*)(d + i * 16 * kDK), 16, 0, 0);
     };
@@ -414,17 +421,17 @@ __global__ __launch_bounds__(512) void gemm_big(GemmArgs a, QkRopeArgs qk) {
     // Fragments of step t + 1 are read from LDS while step t's MFMAs run (two register sets,
     // used in turn; K / 32 is even); the loads of the three steps after t + 1 are in flight.
     struct Frags {
-      bf16x8 a[2][2], b[2][4];
+      bf16x8 a[2][NBI], b[2][NBJ];
     };
     auto read = [&](int t, Frags& f) __attribute__((always_inline)) {
-      const uint16_t* As = lds + (t & (kDStages - 1)) * kDStage;
-      const uint16_t* Bs = As + kBT * kDK;
+      const uint16_t* As = lds + (t & (kDStages - 1)) * STG;
+      const uint16_t* Bs = As + TS * kDK;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-        for (int bi = 0; bi < 2; ++bi) f.a[ks][bi] = dfrag(As, wm * 64 + bi * 32 + fr, ks);
+        for (int bi = 0; bi < NBI; ++bi) f.a[ks][bi] = dfrag(As, wm * (32 * NBI) + bi * 32 + fr, ks);
 #pragma unroll
-        for (int bj = 0; bj < 4; ++bj) f.b[ks][bj] = dfrag(Bs, brow_of(bj) + fr, ks);
+        for (int bj = 0; bj < NBJ; ++bj) f.b[ks][bj] = dfrag(Bs, brow_of(bj) + fr, ks);
       }
     };
     dma(0);
@@ -433,11 +440,11 @@ __global__ __launch_bounds__(512) void gemm_big(GemmArgs a, QkRopeArgs qk) {
     if (nkd > 3) dma(3);
     // stage 0 has landed for this wave once at most the later stages' loads are outstanding
     if (nkd > 3)
-      asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * LPW) : "memory");
     else if (nkd > 2)
-      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * LPW) : "memory");
     else if (nkd > 1)
-      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(LPW) : "memory");
     else
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __builtin_amdgcn_s_barrier();
@@ -451,9 +458,9 @@ __global__ __launch_bounds__(512) void gemm_big(GemmArgs a, QkRopeArgs qk) {
       // fence of __syncthreads would also wait for the loads still in flight.
       const int later = min(nkd - 1, t + 3) - (t + 1);
       if (later >= 2)
-        asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(2 * LPW) : "memory");
       else if (later == 1)
-        asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)" ::"n"(LPW) : "memory");
       else
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
       __builtin_amdgcn_s_barrier();
@@ -462,13 +469,15 @@ __global__ __launch_bounds__(512) void gemm_big(GemmArgs a, QkRopeArgs qk) {
       read(min(t + 1, nkd - 1), nxt);  // (the last step reads its own stage again, unused)
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) mfma_step(cur.a[ks], cur.b[ks]);
-      // one fragment read between matrix instructions, so the reads complete under them
-#pragma unroll
-      for (int i = 0; i < 12; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      // the fragment reads spread between the matrix instructions (NR reads, NM MFMAs: one or
+      // two reads before each MFMA), so the reads complete under them
+      constexpr int NR = 2 * (NBI + NBJ), NM = 2 * NBI * NBJ;
+      static_for<NM>([&](auto i_c) {
+        constexpr int i = decltype(i_c)::value;
+        constexpr int nr = NR >= NM ? NR / NM + (i < NR % NM ? 1 : 0) : (i < NR ? 1 : 0);
+        if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      });
     };
     for (int t = 0; t < nkd; t += 2) {
       step(t, fa, fb);
@@ -514,21 +523,23 @@ __global__ __launch_bounds__(512) void gemm_big(GemmArgs a, QkRopeArgs qk) {
   }
   }
 
-  big_epilogue<WF, EPI, D, KV_F16, 2>(a, qk, acc, m0, n0, wm, wn, lane, s_pos, s_blk);
+  big_epilogue<WF, EPI, D, KV_F16, NBI, NBJ>(a, qk, acc, m0, n0, wm, wn, lane, s_pos, s_blk);
 }
 
-template <int WF, int EPI, int D, bool KV_F16>
+template <int WF, int EPI, int D, bool KV_F16, int TS = 256>
 static hipError_t big_go(const GemmArgs& a, const QkRopeArgs& qk, hipStream_t s) {
+  const size_t lds = WF == DEC_BF16 ? (size_t)kDStages * 2 * TS * kDK * 2 : kBigLds;
   static bool attr = false;  // raise the dynamic LDS limit once per instantiation
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_big<WF, EPI, D, KV_F16>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)(WF == DEC_BF16 ? kBigLdsDma : kBigLds));
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_big<WF, EPI, D, KV_F16, TS>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr = true;
   }
-  const int mt = (a.M + kBT - 1) / kBT;
-  const int nt = EPI == EPI_SWIGLU ? (a.N + 127) / 128 : (a.N + kBT - 1) / kBT;
-  launch_kernel(gemm_big<WF, EPI, D, KV_F16>, dim3(mt * nt), dim3(512), (uint32_t)(WF == DEC_BF16 ? kBigLdsDma : kBigLds), s, a, qk);
+  const int tn = EPI == EPI_SWIGLU ? TS / 2 : TS;
+  const int mt = (a.M + TS - 1) / TS;
+  const int nt = (a.N + tn - 1) / tn;
+  launch_kernel(gemm_big<WF, EPI, D, KV_F16, TS>, dim3(mt * nt), dim3(512), (uint32_t)lds, s, a, qk);
   return hipGetLastError();
 }
 
@@ -565,6 +576,21 @@ hipError_t launch_gemm_big(int wdtype, int epi, const GemmArgs& a, const QkRopeA
   if (wdtype == DEC_UINT4_G32) return big_epi<DEC_UINT4_G32>(epi, a, qk, s);
   if (wdtype == DEC_INT4_SYM_G32) return big_epi<DEC_INT4_SYM_G32>(epi, a, qk, s);
   return hipErrorInvalidValue;
+}
+
+bool gemm_mid_supported(int wdtype, int epi) {
+  return wdtype == DEC_BF16 && (epi == EPI_STORE || epi == EPI_RESID || epi == EPI_SWIGLU);
+}
+
+hipError_t launch_gemm_mid(int wdtype, int epi, const GemmArgs& a, hipStream_t s) {
+  if (a.M <= 0 || a.N <= 0) return hipSuccess;
+  if (!gemm_mid_supported(wdtype, epi) || a.K % kBK) return hipErrorInvalidValue;
+  const QkRopeArgs none{};
+  switch (epi) {
+    case EPI_STORE: return big_go<DEC_BF16, EPI_STORE, 128, false, 128>(a, none, s);
+    case EPI_RESID: return big_go<DEC_BF16, EPI_RESID, 128, false, 128>(a, none, s);
+    default: return big_go<DEC_BF16, EPI_SWIGLU, 128, false, 128>(a, none, s);
+  }
 }
 
 }  // namespace dec

@@ -142,6 +142,10 @@ hipError_t launch_gemm(int wdtype, int epi, const GemmArgs& a, hipStream_t s);
 enum { EPI_QKV = 3 };
 bool gemm_big_supported(int wdtype, int epi, int head_dim);
 hipError_t launch_gemm_big(int wdtype, int epi, const GemmArgs& a, const QkRopeArgs* qk, hipStream_t s);
+// The same kernel on 128 x 128 tiles (bf16 weights; EPI_STORE, EPI_RESID, EPI_SWIGLU), for
+// products whose 256 x 256 grid is too small to fill the chip; identical results.
+bool gemm_mid_supported(int wdtype, int epi);
+hipError_t launch_gemm_mid(int wdtype, int epi, const GemmArgs& a, hipStream_t s);
 
 // The same product for decode steps: K split over up to 8 waves of a block (fixed by K),
 // summed in wave order; bf16 and 4-bit weights, K/32 with a supported per-wave step count.

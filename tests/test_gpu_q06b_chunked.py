@@ -8,6 +8,10 @@ library's key tiles are aligned to absolute positions, so they are expected to a
 bit; identical rows are counted and the max difference must stay within the gate), and both
 are compared with the float64 oracle on one sequence: the last row of every chunk plus a
 seeded sample of 1/16 of the positions. Gate: 2e-2 of each row's oracle logit range.
+
+A third copy prefills the first 600 tokens of every prompt in one call (4,800 rows: not a
+multiple of the 128- or 256-row product tiles, and small enough that the output and down
+projections take the 128 x 128 tiles); its logits must equal the single-shot ones bit for bit.
 """
 
 import math
@@ -24,6 +28,7 @@ from synthetic import MODELS, WORKLOADS, make_prompts, make_weights
 
 REL = 2e-2
 ORACLE_SEQ = 3
+RAGGED = 600  # prompt tokens per sequence of the one-call ragged copy
 
 
 @pytest.fixture(scope="module")
@@ -36,12 +41,13 @@ def run():
     prompts = make_prompts(wl)
     S, P, C = wl.n_seqs, wl.prompt_len, wl.chunk
     per_seq = math.ceil(P / shape.block_tokens)
-    n_blocks = 2 * S * per_seq
+    n_blocks = 3 * S * per_seq
     s = Session(shape, w, max_context=P, n_blocks=n_blocks, max_rows=S * P, max_seqs=S)
     alloc = BlockAllocator(n_blocks, shape.block_tokens, seed=4)
     one = [("one", i) for i in range(S)]
     chk = [("chunk", i) for i in range(S)]
-    for a in one + chk:
+    rag = [("ragged", i) for i in range(S)]
+    for a in one + chk + rag:
         alloc.ensure(a, P)
     print(f"[c4] single shot {S}x{P}", flush=True)
     full = s.prefill([0] * S, [P] * S, np.concatenate(prompts), alloc.table_array(one), B.DEC_LOGITS_ALL)
@@ -60,23 +66,37 @@ def run():
         for p in sample[(sample >= c0) & (sample < c0 + C)]:
             chunk_rows[int(p)] = mine[p - c0].cpu().numpy()
         del part, ref
+    print(f"[c4] {S}x{RAGGED} rows in one call", flush=True)
+    part = s.prefill([0] * S, [RAGGED] * S, np.concatenate([p[:RAGGED] for p in prompts]), alloc.table_array(rag),
+                     B.DEC_LOGITS_ALL)
+    ref = full.view(S, P, -1)[:, :RAGGED].reshape(S * RAGGED, -1)
+    ragged_identical = int(torch.sum(torch.all(part == ref, dim=1)))
+    del part, ref
     full_rows = full.view(S, P, -1)[ORACLE_SEQ][torch.from_numpy(sample).cuda()].cpu().numpy()
     torch.cuda.synchronize()
     del full
     s.close()
-    yield wl, shape, w, prompts, sample, full_rows, np.array([chunk_rows[int(p)] for p in sample]), identical, worst
+    yield (wl, shape, w, prompts, sample, full_rows, np.array([chunk_rows[int(p)] for p in sample]), identical, worst,
+           ragged_identical)
 
 
 def test_chunked_equals_single_shot(run):
-    wl, shape, w, prompts, sample, full_rows, chunk_rows, identical, worst = run
+    wl, shape, w, prompts, sample, full_rows, chunk_rows, identical, worst, _ = run
     total = wl.n_seqs * wl.prompt_len
     report({"type": "chunk_invariance", "case": wl.name, "identical_rows": identical, "rows": total,
             "max_absolute_error": worst})
     assert identical == total
 
 
+def test_ragged_row_count_equals_single_shot(run):
+    wl, *_, ragged_identical = run
+    report({"type": "batch_invariance", "case": f"{wl.name}_first{RAGGED}", "identical_rows": ragged_identical,
+            "rows": wl.n_seqs * RAGGED})
+    assert ragged_identical == wl.n_seqs * RAGGED
+
+
 def test_chunked_and_single_shot_match_oracle(run):
-    wl, shape, w, prompts, sample, full_rows, chunk_rows, identical, worst = run
+    wl, shape, w, prompts, sample, full_rows, chunk_rows, identical, worst, _ = run
     dec = om.OracleDecoder(w)
     print("[c4] oracle", flush=True)
     ref = dec.forward([(prompts[ORACLE_SEQ], dec.new_cache(wl.prompt_len))], rows=sample)
