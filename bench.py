@@ -483,9 +483,10 @@ def hardware_line(torch, copy_mib=1024):
 
 # kernel classes of the library's per-launch timing (dec.h DEC_K_*) timed over a prefill
 K_RMSNORM, K_QKV, K_ATTN_PF, K_ROWS, K_COMBINE, K_O, K_GATEUP, K_DOWN, K_LMHEAD = 1, 2, 4, 5, 6, 7, 8, 9, 10
+K_WIDEN = 12
 PREFILL_CLASSES = {K_QKV: "gemm_qkv", K_ATTN_PF: "attn_prefill", K_ROWS: "attn_rows", K_COMBINE: "attn_combine",
                    K_O: "gemm_o", K_GATEUP: "gemm_gateup", K_DOWN: "gemm_down", K_LMHEAD: "gemm_lmhead",
-                   K_RMSNORM: "rmsnorm"}
+                   K_RMSNORM: "rmsnorm", K_WIDEN: "widen_q4"}
 FP32_MFMA_PEAK_TFS = 157.3  # dense fp32 MFMA: 256 CUs x 256 flop/clk x 2.4 GHz
 
 

@@ -146,13 +146,18 @@ size_t kv_bytes(const dec_config& c) {
 // ---- workspace layout ----------------------------------------------------------------------
 
 struct Ws {
-  size_t rope, meta, x, h, qkv, q, o, a, part, dpart, amax, ssq, xg, samp, counts, total;
+  size_t rope, meta, x, h, qkv, q, o, a, part, dpart, amax, ssq, xg, samp, counts, wide, total;
   size_t meta_ints;  // capacity of the metadata region in int32
+  size_t wide_bytes;  // the widened-layer region (0: calls never widen)
   int chunk, nch_max, max_blocks_per_seq, max_tiles;
   int seg_keys, dslots;  // decode attention: keys per segment; state slots per (row, KV head)
   int act_bytes, kv_el;
   bool flash;  // prefill attention by the MFMA tile kernel
 };
+
+// Prefill calls of at least this many rows with 4-bit weights widen each layer's matrices to bf16
+// first (the rows' products then fill the chip with the larger bf16 tiles)
+constexpr int kWidenRows = 4096;
 
 // `decode_rows` > 0: only the regions a decode step of that many sequences uses (no RoPE table,
 // no prefill partials, no sampler regions), laid out for those rows: the static scratch of
@@ -199,6 +204,10 @@ Ws ws_layout(const dec_config& c, int decode_rows = 0) {
   w.xg = take(S * d * 2);          // decode: bf16(residual * the next norm's gain)
   w.samp = take(dec_only ? 0 : S * sizeof(SampleSeq));       // sampling: per-sequence parameters and history
   w.counts = take(dec_only ? 0 : S * (size_t)c.vocab * 4);   // sampling: per-sequence count table (kept zero)
+  // 4-bit weights: one layer's matrices widened to bf16, for prefill calls of at least kWidenRows
+  const bool wide = !dec_only && is_q4(c.weight_dtype) && c.max_rows >= kWidenRows;
+  w.wide_bytes = wide ? (qkvw * d + d * qw + 2 * ff * d + d * ff) * 2 : 0;
+  w.wide = take(w.wide_bytes);
   w.total = off;
   return w;
 }
@@ -553,16 +562,21 @@ int run_forward(dec_ctx* ctx, uint8_t* base, const Ws& w, hipStream_t st, const 
   // when that fills the chip, else the 64 x 64 tiles; all give identical results, so the
   // choice never changes a row's bits.
   const bool big = !decode && gemm_big_supported(c.weight_dtype, EPI_QKV, D);
-  auto gemm = [&](int epi, const GemmArgs& g) {
-    if (dgemm) return launch_gemm_decode(c.weight_dtype, epi, g, st);
+  // 4-bit weights, prefill calls of at least kWidenRows rows: each layer's matrices are first
+  // widened to bf16 in the workspace (the values the 4-bit kernels stage as MFMA operands) and
+  // the layer's products take the bf16 kernels, with identical results
+  const bool widen = big && is_q4(c.weight_dtype) && w.wide_bytes > 0 && N >= kWidenRows;
+  const int lwf = widen ? DEC_BF16 : c.weight_dtype;  // format of the layers' matrices as the products read them
+  auto gemm = [&](int epi, const GemmArgs& g, int wf) {
+    if (dgemm) return launch_gemm_decode(wf, epi, g, st);
     auto tiles = [&](int t) {
       return (g.M + t - 1) / t * (epi == EPI_SWIGLU ? (g.N + t / 2 - 1) / (t / 2) : (g.N + t - 1) / t);
     };
-    const bool mid = big && gemm_mid_supported(c.weight_dtype, epi) && tiles(128) >= 256;
+    const bool mid = big && gemm_mid_supported(wf, epi) && tiles(128) >= 256;
     const int big_min = mid && epi == EPI_SWIGLU ? 512 : 256;
-    if (big && tiles(256) >= big_min && g.M >= 1024) return launch_gemm_big(c.weight_dtype, epi, g, nullptr, st);
-    if (mid) return launch_gemm_mid(c.weight_dtype, epi, g, st);
-    return launch_gemm(c.weight_dtype, epi, g, st);
+    if (big && tiles(256) >= big_min && g.M >= 1024) return launch_gemm_big(wf, epi, g, nullptr, st);
+    if (mid) return launch_gemm_mid(wf, epi, g, st);
+    return launch_gemm(wf, epi, g, st);
   };
   // A of a normalising GEMM: the residual itself (decode GEMM) or the RMSNorm output
   // (gain: the norm's gain, applied to xg by the product that wrote it)
@@ -578,7 +592,24 @@ int run_forward(dec_ctx* ctx, uint8_t* base, const Ws& w, hipStream_t st, const 
   TLAUNCH(DEC_K_EMBED, launch_embed(tok_dev ? tok_dev : b.row_tok, N, c.vocab, d, c.weight_dtype, ctx->embed, x,
                                     dgemm ? ssq : nullptr, dgemm ? xg : nullptr, ctx->layers[0].attn_norm, st));
   for (int l = 0; l < c.n_layers; ++l) {
-    const LayerW& L = ctx->layers[l];
+    LayerW Lw;
+    if (widen) {
+      // the layer's seven matrices, one after another in the widened region
+      const LayerW& L0 = ctx->layers[l];
+      uint16_t* wb = (uint16_t*)(base + w.wide);
+      const WMat src[7] = {L0.wq, L0.wk, L0.wv, L0.wo, L0.wg, L0.wu, L0.wd};
+      const int cols[7] = {d, d, d, qw, d, d, ff};
+      WMat* dst[7] = {&Lw.wq, &Lw.wk, &Lw.wv, &Lw.wo, &Lw.wg, &Lw.wu, &Lw.wd};
+      int64_t offs[7], o = 0;
+      Lw = L0;
+      for (int j = 0; j < 7; ++j) {
+        offs[j] = o;
+        *dst[j] = WMat{wb + o, nullptr, nullptr, src[j].rows};
+        o += (int64_t)src[j].rows * cols[j];
+      }
+      TLAUNCH(DEC_K_WIDEN, launch_widen_q4(c.weight_dtype, src, cols, offs, 7, wb, st));
+    }
+    const LayerW& L = widen ? Lw : ctx->layers[l];
     if (!dgemm) TLAUNCH(DEC_K_RMSNORM, launch_rmsnorm(x, nullptr, N, d, L.attn_norm, c.rms_eps, h, act_bf16, st));
     GemmArgs g{};
     norm_input(g, L.attn_norm);
@@ -587,9 +618,9 @@ int run_forward(dec_ctx* ctx, uint8_t* base, const Ws& w, hipStream_t st, const 
     g.C = qkv; g.ldc = qkvw;
     QkRopeArgs qa{qkv, L.q_norm, L.k_norm, rope, q, pool, l, H, Hkv, D, c.rms_eps, kv_f16, b};
     if (big) {
-      TLAUNCH(DEC_K_GEMM_QKV, launch_gemm_big(c.weight_dtype, EPI_QKV, g, &qa, st));
+      TLAUNCH(DEC_K_GEMM_QKV, launch_gemm_big(lwf, EPI_QKV, g, &qa, st));
     } else {
-      TLAUNCH(DEC_K_GEMM_QKV, gemm(EPI_STORE, g));
+      TLAUNCH(DEC_K_GEMM_QKV, gemm(EPI_STORE, g, lwf));
     }
     if (decode) {
       AttnRowsArgs ra{q, pool, l, H, Hkv, D, kv_f16, w.dslots, dpart, b};
@@ -611,20 +642,20 @@ int run_forward(dec_ctx* ctx, uint8_t* base, const Ws& w, hipStream_t st, const 
     g.seg[0] = L.wo; g.nseg = 1; g.C = x; g.ldc = d;
     g.ssq_out = dgemm ? ssq : nullptr;
     g.xg_out = dgemm ? xg : nullptr; g.gain_next = L.ffn_norm;
-    TLAUNCH(DEC_K_GEMM_O, gemm(EPI_RESID, g));
+    TLAUNCH(DEC_K_GEMM_O, gemm(EPI_RESID, g, lwf));
     if (!dgemm) TLAUNCH(DEC_K_RMSNORM, launch_rmsnorm(x, nullptr, N, d, L.ffn_norm, c.rms_eps, h, act_bf16, st));
     g = GemmArgs{};
     norm_input(g, L.ffn_norm);
     g.M = N; g.N = ff; g.K = d;
     g.seg[0] = L.wg; g.seg[1] = L.wu; g.nseg = 2; g.C = act; g.ldc = ff; g.c_bf16 = act_bf16;
-    TLAUNCH(DEC_K_GEMM_GATEUP, gemm(EPI_SWIGLU, g));
+    TLAUNCH(DEC_K_GEMM_GATEUP, gemm(EPI_SWIGLU, g, lwf));
     g = GemmArgs{};
     g.A = act; g.lda = ff; g.M = N; g.N = d; g.K = ff;
     g.seg[0] = L.wd; g.nseg = 1; g.C = x; g.ldc = d;
     g.ssq_out = dgemm ? ssq : nullptr;
     g.xg_out = dgemm ? xg : nullptr;
     g.gain_next = l + 1 < c.n_layers ? ctx->layers[l + 1].attn_norm : ctx->final_norm;
-    TLAUNCH(DEC_K_GEMM_DOWN, gemm(EPI_RESID, g));
+    TLAUNCH(DEC_K_GEMM_DOWN, gemm(EPI_RESID, g, lwf));
   }
   if (b.n_out > 0 && logits) {
     GemmArgs g{};
@@ -650,7 +681,7 @@ int run_forward(dec_ctx* ctx, uint8_t* base, const Ws& w, hipStream_t st, const 
     if (dgemm && lmhead_decode_supported(c.weight_dtype, b.n_out, d)) {
       TLAUNCH(DEC_K_GEMM_LMHEAD, launch_lmhead_decode(c.weight_dtype, g, st));
     } else {
-      TLAUNCH(DEC_K_GEMM_LMHEAD, gemm(EPI_STORE, g));
+      TLAUNCH(DEC_K_GEMM_LMHEAD, gemm(EPI_STORE, g, c.weight_dtype));
     }
     if (next && cand) {
       TLAUNCH(DEC_K_ARGMAX, launch_argmax_final(cand_v, cand_i, b.n_out, cand, next, st));

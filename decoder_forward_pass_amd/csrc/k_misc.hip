@@ -343,6 +343,66 @@ __global__ __launch_bounds__(256) void dequant_kernel(WMat w, int rows, int cols
   }
 }
 
+// ---- 4-bit weights widened to bf16 (prefill calls of many rows) ----------------------------
+// Each value is the operand the 4-bit GEMM kernels stage: dequant_u4 of the code with its group's
+// zero point and scale, rounded to bf16 by pack_bf16x2 (columns 2j, 2j + 1 from the low and high
+// nibble of byte j). Grid row y takes matrix y; one thread per code word (8 columns), one
+// 16-byte store.
+struct WidenArgs {
+  WMat m[kWidenMats];
+  int cols[kWidenMats];
+  uint32_t words[kWidenMats];  // rows * cols / 8
+  int64_t out_off[kWidenMats];
+  uint16_t* out;
+};
+
+template <int WF>
+__global__ __launch_bounds__(256) void widen_q4_kernel(WidenArgs a) {
+  const int j = blockIdx.y;
+  const WMat m = a.m[j];
+  const uint32_t words = a.words[j], wpr = (uint32_t)a.cols[j] / 8, gpr = wpr / 4;
+  uint16_t* const out = a.out + a.out_off[j];
+  for (uint32_t wi = blockIdx.x * 256u + threadIdx.x; wi < words; wi += gridDim.x * 256u) {
+    const uint32_t r = wi / wpr, c8 = wi - r * wpr;
+    const uint32_t codes = q4_codes<WF>(((const uint32_t*)m.w)[wi]);
+    const uint32_t gi = r * gpr + (c8 >> 2);
+    const float zp = q4_zp<WF>(m.zp, gi);
+    const float sc = q4_scale<WF>(m.scale[gi]);
+    u32x4 v;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const uint32_t byte = (codes >> (8 * b)) & 0xffu;
+      v[b] = pack_bf16x2(dequant_u4(byte & 15u, zp, sc), dequant_u4(byte >> 4, zp, sc));
+    }
+    *(u32x4*)(out + (size_t)wi * 8) = v;
+  }
+}
+
+hipError_t launch_widen_q4(int wdtype, const WMat* mats, const int* cols, const int64_t* out_off, int n,
+                           uint16_t* out, hipStream_t s) {
+  if (n < 1 || n > kWidenMats) return hipErrorInvalidValue;
+  WidenArgs a{};
+  uint32_t most = 0;
+  for (int j = 0; j < n; ++j) {
+    const int64_t words = (int64_t)mats[j].rows * (cols[j] / 8);
+    if (cols[j] <= 0 || cols[j] % 32 || mats[j].rows <= 0 || words > 0x7fffffff) return hipErrorInvalidValue;
+    a.m[j] = mats[j];
+    a.cols[j] = cols[j];
+    a.words[j] = (uint32_t)words;
+    a.out_off[j] = out_off[j];
+    most = std::max(most, (uint32_t)words);
+  }
+  a.out = out;
+  const dim3 grid((unsigned)std::min<uint32_t>((most + 255) / 256, 1024), (unsigned)n);
+  if (wdtype == DEC_UINT4_G32)
+    widen_q4_kernel<DEC_UINT4_G32><<<grid, 256, 0, s>>>(a);
+  else if (wdtype == DEC_INT4_SYM_G32)
+    widen_q4_kernel<DEC_INT4_SYM_G32><<<grid, 256, 0, s>>>(a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 // ---- symmetric int4-g32 quantisation ("Candle model runner" 2.5, quantising at load) -------
 // One thread per group of 32 columns, float32 throughout: s = f16(max|W| / 7) (the quotient
 // rounded to nearest even), q = clamp(rint(W / s), -8, 7) with the stored s; a group whose

@@ -187,5 +187,10 @@ hipError_t launch_quant_int4_sym(const float* w, int64_t rows, int64_t cols, uin
 
 // out[rows][cols] = widened / dequantised matrix (float32).
 hipError_t launch_dequant(int wdtype, const WMat& w, int rows, int cols, float* out, hipStream_t s);
+// 4-bit matrices (at most kWidenMats, each [rows][cols], cols % 32 == 0) widened to the bf16
+// values the 4-bit GEMM kernels stage as MFMA operands, stored row-major at out + out_off[j]
+constexpr int kWidenMats = 8;
+hipError_t launch_widen_q4(int wdtype, const WMat* mats, const int* cols, const int64_t* out_off, int n,
+                           uint16_t* out, hipStream_t s);
 
 }  // namespace dec

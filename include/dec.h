@@ -510,7 +510,8 @@ int dec_load_safetensors(const char* path, const dec_config* cfg, void* blob, si
 #define DEC_K_GEMM_DOWN 9
 #define DEC_K_GEMM_LMHEAD 10
 #define DEC_K_ARGMAX 11
-#define DEC_K_COUNT 12
+#define DEC_K_WIDEN 12 /* 4-bit weights widened to bf16 for a prefill call of many rows */
+#define DEC_K_COUNT 13
 
 /*
  * Bracket every later launch of the kernel classes in `class_mask` (bit k =

@@ -1,14 +1,14 @@
 """GPU parity at full size for symmetric int4-g32 weights (W = q * s with signed 4-bit q and an
 f16 scale per 32 input columns, "Candle model runner" section 2.5 "Int4 weights") with an f16 KV
-cache: 16 sequences of 1,024 prompt tokens prefilled in one call (every projection then runs on
-the 256 x 256 tile product), then 32 greedy decode steps at batch 16 with the next token ids
-passed on the device.
+cache: 16 sequences of 1,024 prompt tokens prefilled in one call (each layer's 4-bit matrices are
+then widened to bf16 and every projection runs on the 256 x 256 tile product), then 32 greedy
+decode steps at batch 16 with the next token ids passed on the device.
 
 Dequantisation is checked bit for bit against the oracle's float32 evaluation of W = q * s on
 whole matrices. The oracle follows sequence 0 (its last prompt logits, then a fixed set of decode
 steps with the GPU's tokens); gate 2e-2 of each row's oracle logit range. Sequence 0 is also run
-alone (a 1,024-row prefill takes the 64 x 64 tile product instead): its last prompt logits and
-its decode logits must equal the batch's bit for bit.
+alone (a 1,024-row prefill dequantises inside the 64 x 64 tile product instead): its last prompt
+logits and its decode logits must equal the batch's bit for bit.
 """
 
 import math

@@ -7,7 +7,10 @@ Dequantisation is checked bit for bit against the oracle's float32 evaluation of
 formula on whole matrices. The oracle follows the shortest and the longest sequence one by one
 (prefill, then every decode step with the GPU's tokens), comparing the last prompt logits and
 a fixed set of decode steps; gate 2e-2 of each row's oracle logit range. The shortest sequence
-is also run alone: its decode logits must equal the batch's bit for bit.
+is also run alone: its decode logits must equal the batch's bit for bit (the batched calls of
+thousands of rows widen each layer's 4-bit matrices to bf16 before the products; the lone call
+of a few hundred rows dequantises inside the products, so this also checks that both give the
+same operands).
 """
 
 import math
