@@ -146,9 +146,10 @@ size_t kv_bytes(const dec_config& c) {
 // ---- workspace layout ----------------------------------------------------------------------
 
 struct Ws {
-  size_t rope, meta, x, h, qkv, q, o, a, part, dpart, amax, ssq, xg, samp, counts, wide, total;
+  size_t rope, meta, x, h, qkv, q, o, a, part, dpart, amax, ssq, xg, samp, counts, wide, fpart, total;
   size_t meta_ints;  // capacity of the metadata region in int32
   size_t wide_bytes;  // the widened-layer region (0: calls never widen)
+  size_t fpart_floats;  // float32 weights: the K-quarter sums of split products (0: none)
   int chunk, nch_max, max_blocks_per_seq, max_tiles;
   int seg_keys, dslots;  // decode attention: keys per segment; state slots per (row, KV head)
   int act_bytes, kv_el;
@@ -208,6 +209,19 @@ Ws ws_layout(const dec_config& c, int decode_rows = 0) {
   const bool wide = !dec_only && is_q4(c.weight_dtype) && c.max_rows >= kWidenRows;
   w.wide_bytes = wide ? (qkvw * d + d * qw + 2 * ff * d + d * ff) * 2 : 0;
   w.wide = take(w.wide_bytes);
+  // float32 weights: a product whose grid of 64 x 64 tiles is under 256 splits K into quarters
+  // over blocks (m tiles * n tiles < 256), 4 * matrices * M * N floats of sums; the largest over
+  // the products for calls of up to R rows (none in the static decode scratch: those products
+  // then take the unsplit kernel, with the same results)
+  w.fpart_floats = 0;
+  if (c.weight_dtype == DEC_F32 && !dec_only) {
+    auto need = [&](size_t N, size_t nb) -> size_t {
+      const size_t mt = 255 / ((N + 63) / 64);
+      return 4 * nb * std::min(R, 64 * mt) * N;
+    };
+    w.fpart_floats = std::max({need(qkvw, 1), need(d, 1), need(ff, 2), need((size_t)c.vocab, 1)});
+  }
+  w.fpart = take(w.fpart_floats * 4);
   w.total = off;
   return w;
 }
@@ -567,8 +581,11 @@ int run_forward(dec_ctx* ctx, uint8_t* base, const Ws& w, hipStream_t st, const 
   // the layer's products take the bf16 kernels, with identical results
   const bool widen = big && is_q4(c.weight_dtype) && w.wide_bytes > 0 && N >= kWidenRows;
   const int lwf = widen ? DEC_BF16 : c.weight_dtype;  // format of the layers' matrices as the products read them
-  auto gemm = [&](int epi, const GemmArgs& g, int wf) {
-    if (dgemm) return launch_gemm_decode(wf, epi, g, st);
+  auto gemm = [&](int epi, const GemmArgs& g0, int wf) {
+    if (dgemm) return launch_gemm_decode(wf, epi, g0, st);
+    GemmArgs g = g0;
+    g.part = (float*)(base + w.fpart);
+    g.part_floats = (int64_t)w.fpart_floats;
     auto tiles = [&](int t) {
       return (g.M + t - 1) / t * (epi == EPI_SWIGLU ? (g.N + t / 2 - 1) / (t / 2) : (g.N + t - 1) / t);
     };
@@ -633,8 +650,12 @@ int run_forward(dec_ctx* ctx, uint8_t* base, const Ws& w, hipStream_t st, const 
         TLAUNCH(DEC_K_ATTN_PREFILL, launch_attn_prefill(pa, st));
       } else {
         AttnRowsArgs ra{q, pool, l, H, Hkv, D, kv_f16, nch, part, b};
-        TLAUNCH(DEC_K_ATTN_ROWS, launch_attn_rows(ra, st));
-        TLAUNCH(DEC_K_ATTN_COMBINE, launch_attn_combine(part, N, H, D, nch, w.chunk, b.row_pos, o, act_bf16, st));
+        if (nch <= attn_rows_merged_max_chunks(D, H / Hkv)) {
+          TLAUNCH(DEC_K_ATTN_ROWS, launch_attn_rows_merged(ra, o, act_bf16, st));
+        } else {
+          TLAUNCH(DEC_K_ATTN_ROWS, launch_attn_rows(ra, st));
+          TLAUNCH(DEC_K_ATTN_COMBINE, launch_attn_combine(part, N, H, D, nch, w.chunk, b.row_pos, o, act_bf16, st));
+        }
       }
     }
     g = GemmArgs{};

@@ -75,25 +75,19 @@ __device__ __forceinline__ float xor_reduce(float v, Op op) {  // over lane bits
   return v;
 }
 
-template <typename KVT, int D, int GROUP>
-__global__ __launch_bounds__(256) void attn_rows_kernel(AttnRowsArgs a) {
+// The partial (max, sum, unnormalised accumulator) of one chunk of keys of (row, KV head) for
+// its GROUP query heads; lanes of group 0 write head i's D + 2 values through dst(i).
+template <typename KVT, int D, int GROUP, typename Dst>
+__device__ __forceinline__ void rows_chunk(const AttnRowsArgs& a, int row, int kvh, int chunk, int lane, Dst dst) {
   using G = RowsGeom<KVT, D, GROUP>;
   constexpr int EPL = G::EPL, LPK = G::LPK, KPI = G::KPI, KPG = G::KPG, CHUNK = G::CHUNK;
-  const int lane = threadIdx.x & 63;
   const int grp = lane / LPK;
   const int sub = lane % LPK;
-  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int nch = a.n_chunks;
   const int Hkv = a.n_kv_heads, H = a.n_heads;
-  const int chunk = (int)(item % nch);
-  const int64_t t = item / nch;
-  const int kvh = (int)(t % Hkv);
-  const int row = (int)(t / Hkv);
-  if (row >= a.b.n_rows) return;
+  (void)Hkv;
   const int pos = a.b.row_pos[row];
   const int ctx = pos + 1;
   const int key0 = chunk * CHUNK;
-  if (key0 >= ctx) return;
   const int seq = a.b.row_seq[row];
   const int32_t* table = a.b.block_tables + (int64_t)seq * a.b.tbl_stride;
   const int B = a.pool.block_tokens;
@@ -179,15 +173,83 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(AttnRowsArgs a) {
   if (grp == 0) {
 #pragma unroll
     for (int i = 0; i < GROUP; ++i) {
-      float* dst = a.partial + (((int64_t)row * H + kvh * GROUP + i) * nch + chunk) * (D + 2);
+      float* out = dst(i);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) dst[sub * EPL + e] = acc[i][e];
+      for (int e = 0; e < EPL; ++e) out[sub * EPL + e] = acc[i][e];
       if (sub == 0) {
-        dst[D] = m[i];
-        dst[D + 1] = l[i];
+        out[D] = m[i];
+        out[D + 1] = l[i];
       }
     }
   }
+}
+
+template <typename KVT, int D, int GROUP>
+__global__ __launch_bounds__(256) void attn_rows_kernel(AttnRowsArgs a) {
+  constexpr int CHUNK = RowsGeom<KVT, D, GROUP>::CHUNK;
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int nch = a.n_chunks;
+  const int Hkv = a.n_kv_heads, H = a.n_heads;
+  const int chunk = (int)(item % nch);
+  const int64_t t = item / nch;
+  const int kvh = (int)(t % Hkv);
+  const int row = (int)(t / Hkv);
+  if (row >= a.b.n_rows) return;
+  if (chunk * CHUNK >= a.b.row_pos[row] + 1) return;
+  rows_chunk<KVT, D, GROUP>(a, row, kvh, chunk, lane, [&](int i) {
+    return a.partial + (((int64_t)row * H + kvh * GROUP + i) * nch + chunk) * (D + 2);
+  });
+}
+
+// log-sum-exp merge of a row's chunk partials (chunk c at p0 + c * stride: D values, max,
+// sum), chunks in ascending order, into the output row of one query head; one wave, lanes over
+// the channels
+template <bool BF16_OUT>
+__device__ __forceinline__ void merge_chunks(const float* p0, int nc, int stride, int D, int lane, void* o,
+                                             int64_t ob) {
+  float M = -__builtin_inff();
+  for (int c = 0; c < nc; ++c) M = fmaxf(M, p0[c * stride + D]);
+  float L = 0.f, a0 = 0.f, a1 = 0.f;
+  for (int c = 0; c < nc; ++c) {
+    const float* p = p0 + c * stride;
+    const float sc = exp2f(p[D] - M);
+    L += sc * p[D + 1];
+    if (lane < D) a0 += sc * p[lane];
+    if (lane + 64 < D) a1 += sc * p[lane + 64];
+  }
+  const float inv = 1.0f / L;
+  if constexpr (BF16_OUT) {
+    uint16_t* out = (uint16_t*)o + ob;
+    if (lane < D) out[lane] = f32_to_bf16_bits(a0 * inv);
+    if (lane + 64 < D) out[lane + 64] = f32_to_bf16_bits(a1 * inv);
+  } else {
+    float* out = (float*)o + ob;
+    if (lane < D) out[lane] = a0 * inv;
+    if (lane + 64 < D) out[lane + 64] = a1 * inv;
+  }
+}
+
+// Rows of at most kRowsMergedBytes / (GROUP (D + 2) 4) chunks: one workgroup per (row, KV head);
+// its four waves take the chunks in turn, the partials stay in LDS, and the workgroup merges
+// them as attn_combine_kernel does (the same arithmetic, so the same results), with no second
+// launch.
+constexpr int kRowsMergedBytes = 64 * 1024;
+
+template <typename KVT, int D, int GROUP, bool BF16_OUT>
+__global__ __launch_bounds__(256) void attn_rows_merged_kernel(AttnRowsArgs a, void* o) {
+  constexpr int CHUNK = RowsGeom<KVT, D, GROUP>::CHUNK;
+  extern __shared__ __attribute__((aligned(16))) float s_part[];  // [chunk][head][D + 2]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int Hkv = a.n_kv_heads, H = a.n_heads;
+  const int kvh = blockIdx.x % Hkv, row = blockIdx.x / Hkv;
+  const int nc = (a.b.row_pos[row] + CHUNK) / CHUNK;  // chunks holding keys 0..pos
+  for (int c = wave; c < nc; c += 4)
+    rows_chunk<KVT, D, GROUP>(a, row, kvh, c, lane, [&](int i) { return s_part + ((int64_t)c * GROUP + i) * (D + 2); });
+  __syncthreads();
+  for (int i = wave; i < GROUP; i += 4)
+    merge_chunks<BF16_OUT>(s_part + i * (D + 2), nc, GROUP * (D + 2), D, lane, o,
+                           (int64_t)row * H * D + (int64_t)(kvh * GROUP + i) * D);
 }
 
 template <typename KVT, int D>
@@ -242,6 +304,47 @@ hipError_t launch_attn_rows(const AttnRowsArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+int attn_rows_merged_max_chunks(int head_dim, int group) {
+  return kRowsMergedBytes / (group * (head_dim + 2) * 4);
+}
+
+template <typename KVT, int D, int GROUP>
+static void rows_merged_go(const AttnRowsArgs& a, void* o, bool bf16_out, hipStream_t s) {
+  const dim3 g((unsigned)(a.b.n_rows * a.n_kv_heads));
+  const uint32_t lds = (uint32_t)(a.n_chunks * GROUP * (D + 2) * 4);
+  if (bf16_out)
+    launch_kernel(attn_rows_merged_kernel<KVT, D, GROUP, true>, g, dim3(256), lds, s, a, o);
+  else
+    launch_kernel(attn_rows_merged_kernel<KVT, D, GROUP, false>, g, dim3(256), lds, s, a, o);
+}
+
+template <typename KVT, int D>
+static hipError_t rows_merged_group(const AttnRowsArgs& a, void* o, bool bf16_out, hipStream_t s) {
+  switch (a.n_heads / a.n_kv_heads) {
+    case 1: rows_merged_go<KVT, D, 1>(a, o, bf16_out, s); break;
+    case 2: rows_merged_go<KVT, D, 2>(a, o, bf16_out, s); break;
+    case 4: rows_merged_go<KVT, D, 4>(a, o, bf16_out, s); break;
+    case 8: rows_merged_go<KVT, D, 8>(a, o, bf16_out, s); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_rows_merged(const AttnRowsArgs& a, void* o, bool out_bf16, hipStream_t s) {
+  if (a.b.n_rows <= 0) return hipSuccess;
+  if (a.n_chunks > attn_rows_merged_max_chunks(a.head_dim, a.n_heads / a.n_kv_heads)) return hipErrorInvalidValue;
+  if (a.kv_f16) {
+    if (a.head_dim == 32) return rows_merged_group<uint16_t, 32>(a, o, out_bf16, s);
+    if (a.head_dim == 64) return rows_merged_group<uint16_t, 64>(a, o, out_bf16, s);
+    if (a.head_dim == 128) return rows_merged_group<uint16_t, 128>(a, o, out_bf16, s);
+  } else {
+    if (a.head_dim == 32) return rows_merged_group<float, 32>(a, o, out_bf16, s);
+    if (a.head_dim == 64) return rows_merged_group<float, 64>(a, o, out_bf16, s);
+    if (a.head_dim == 128) return rows_merged_group<float, 128>(a, o, out_bf16, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 // ---- combine: log-sum-exp merge of the chunk partials, chunks in ascending order ----------
 
 template <bool BF16_OUT>
@@ -254,28 +357,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   if (w >= (int64_t)n_rows * H) return;
   const int row = (int)(w / H), h = (int)(w % H);
   const int nc = (row_pos[row] + chunk) / chunk;  // chunks holding keys 0..pos
-  const float* base = partial + w * nch * (D + 2);
-  float M = -__builtin_inff();
-  for (int c = 0; c < nc; ++c) M = fmaxf(M, base[c * (D + 2) + D]);
-  float L = 0.f, a0 = 0.f, a1 = 0.f;
-  for (int c = 0; c < nc; ++c) {
-    const float* p = base + c * (D + 2);
-    const float sc = exp2f(p[D] - M);
-    L += sc * p[D + 1];
-    if (lane < D) a0 += sc * p[lane];
-    if (lane + 64 < D) a1 += sc * p[lane + 64];
-  }
-  const float inv = 1.0f / L;
-  const int64_t ob = (int64_t)row * H * D + (int64_t)h * D;
-  if constexpr (BF16_OUT) {
-    uint16_t* out = (uint16_t*)o + ob;
-    if (lane < D) out[lane] = f32_to_bf16_bits(a0 * inv);
-    if (lane + 64 < D) out[lane + 64] = f32_to_bf16_bits(a1 * inv);
-  } else {
-    float* out = (float*)o + ob;
-    if (lane < D) out[lane] = a0 * inv;
-    if (lane + 64 < D) out[lane + 64] = a1 * inv;
-  }
+  merge_chunks<BF16_OUT>(partial + w * nch * (D + 2), nc, D + 2, D, lane, o, (int64_t)row * H * D + (int64_t)h * D);
 }
 
 hipError_t launch_attn_combine(const float* partial, int n_rows, int n_heads, int head_dim, int n_chunks,

@@ -34,15 +34,17 @@ __device__ __forceinline__ void wait_vm_stages(int later) {
   }
 }
 
-// BM < 64 (float32 only): one wave per BM x BM tile (32 or 16), for grids of 64 x 64 tiles too
-// small to fill the chip; every output element still gets the same MFMA sequence, so a row's
-// result does not change with the tile size.
-template <int WF, int EPI, int BM>
-__global__ __launch_bounds__(BM == 64 ? 256 : 64) void gemm_tile64(GemmArgs a) {
+// Float32 weights: K is taken in four fixed quarters of its 16-column steps (quarter q: steps
+// q nk / 4 .. (q + 1) nk / 4 - 1, set by K alone). Each quarter is accumulated from zero in
+// ascending order and the quarter sums are added in quarter order, ((p0 + p1) + p2) + p3. A
+// block takes the four quarters in turn, or, for grids too small to fill the chip (PART), one
+// quarter (blockIdx.z) whose sums go to a.part for gemm_f32_combine; the results are the same.
+template <int WF, int EPI, bool PART>
+__global__ __launch_bounds__(256) void gemm_tile64(GemmArgs a) {
   constexpr bool F32 = WF == DEC_F32;
-  static_assert(BM == 64 || (F32 && (BM == 32 || BM == 16)), "smaller tiles: float32 only");
-  constexpr int WAVES = BM == 64 ? 4 : 1, BN = BM;
-  constexpr int SUB = BM == 16 ? 1 : 2;  // float32: 16 x 16 MFMA blocks per wave, each way
+  static_assert(!PART || F32, "K quarters over blocks: float32 only");
+  constexpr int BM = 64, WAVES = 4, BN = BM;
+  constexpr int SUB = 2;  // float32: 16 x 16 MFMA blocks per wave, each way
   constexpr int BK = F32 ? 16 : 64;  // elements of K per LDS tile
   constexpr int RW = F32 ? 17 : 36;  // LDS row stride in 32-bit words (padded)
   constexpr int NB = EPI == EPI_SWIGLU ? 2 : 1;
@@ -75,6 +77,7 @@ __global__ __launch_bounds__(BM == 64 ? 256 : 64) void gemm_tile64(GemmArgs a) {
   // float32 weights: 2 x 2 blocks of 16 x 16 per wave (v_mfma_f32_16x16x4_f32); bf16 / uint4:
   // one 32 x 32 block per wave (v_mfma_f32_32x32x16_bf16, the full-rate bf16 shape)
   f32x4 acc[NB][SUB][SUB];
+  f32x4 sum[NB][SUB][SUB];  // float32: the finished quarters' sum
   f32x16 acc32[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -98,6 +101,9 @@ __global__ __launch_bounds__(BM == 64 ? 256 : 64) void gemm_tile64(GemmArgs a) {
     constexpr int FR = 8, SROWS = BM * 16;  // stages; floats per operand per stage
     float* const ring = reinterpret_cast<float*>(f32_ring);
     const int nk = K / BK;
+    auto kq = [&](int q) { return q * nk / 4; };  // first step of quarter q
+    // this block's steps tbeg + u, u < n (ring stage u % FR)
+    const int tbeg = PART ? kq(blockIdx.z) : 0, n = PART ? kq(blockIdx.z + 1) - tbeg : nk;
     const float* asrc[LPW];
     const float* bsrc[NB][LPW];
 #pragma unroll
@@ -108,33 +114,51 @@ __global__ __launch_bounds__(BM == 64 ? 256 : 64) void gemm_tile64(GemmArgs a) {
       for (int nb = 0; nb < NB; ++nb)
         bsrc[nb][i] = (const float*)bm[nb].w + (int64_t)min(br0 + lrow, bm[nb].rows - 1) * K + lch * 4;
     }
-    auto dma = [&](int t) {
+    auto dma = [&](int u) {
+      const int col = (tbeg + u) * BK;
 #pragma unroll
       for (int i = 0; i < LPW; ++i) {
-        float* st = ring + (t % FR) * (1 + NB) * SROWS + (wave * LPW + i) * 256;
-        __builtin_amdgcn_global_load_lds((const void*)(asrc[i] + t * BK),
+        float* st = ring + (u % FR) * (1 + NB) * SROWS + (wave * LPW + i) * 256;
+        __builtin_amdgcn_global_load_lds((const void*)(asrc[i] + col),
                                          (void __attribute__((address_space(3)))*)st, 16, 0, 0);
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
-          __builtin_amdgcn_global_load_lds((const void*)(bsrc[nb][i] + t * BK),
+          __builtin_amdgcn_global_load_lds((const void*)(bsrc[nb][i] + col),
                                            (void __attribute__((address_space(3)))*)(st + (1 + nb) * SROWS), 16, 0,
                                            0);
       }
     };
-    for (int t = 0; t < min(nk, FR - 1); ++t) dma(t);
+    for (int u = 0; u < min(n, FR - 1); ++u) dma(u);
+    // a quarter ends: sum = acc (the first quarter) or sum + acc, and acc restarts; quarters
+    // end before the first step of the next one
+    int q = 0;
+    auto fold = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int bi = 0; bi < SUB; ++bi)
+#pragma unroll
+          for (int bj = 0; bj < SUB; ++bj) {
+            sum[nb][bi][bj] = q == 0 ? acc[nb][bi][bj] : sum[nb][bi][bj] + acc[nb][bi][bj];
+            acc[nb][bi][bj] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+      ++q;
+    };
     // (a fragment read: row r, chunk ks, lane's k ks * 4 + lane / 16)
     auto frag = [&](const float* S, int r, int ks) {
       return S[r * 16 + ((ks ^ ((r >> 2) & 3)) << 2) + (lane >> 4)];
     };
-    for (int t = 0; t < nk; ++t) {
-      // stage t has landed for this wave once at most the later issued stages' loads are
-      // outstanding; the barrier publishes it and frees stage t - 1 (read in the last step)
-      const int later = min(FR - 2, nk - 1 - t);
+    for (int u = 0; u < n; ++u) {
+      if constexpr (!PART)
+        while (q < 3 && u == kq(q + 1)) fold();  // (empty quarters fold a zero sum)
+      // stage u has landed for this wave once at most the later issued stages' loads are
+      // outstanding; the barrier publishes it and frees stage u - 1 (read in the last step)
+      const int later = min(FR - 2, n - 1 - u);
       wait_vm_stages<(1 + NB) * LPW, FR - 2>(later);
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      if (t + FR - 1 < nk) dma(t + FR - 1);
-      const float* As_ = ring + (t % FR) * (1 + NB) * SROWS;
+      if (u + FR - 1 < n) dma(u + FR - 1);
+      const float* As_ = ring + (u % FR) * (1 + NB) * SROWS;
 #pragma unroll
       for (int ks = 0; ks < BK / 4; ++ks) {
         float af[SUB];
@@ -151,6 +175,8 @@ __global__ __launch_bounds__(BM == 64 ? 256 : 64) void gemm_tile64(GemmArgs a) {
           }
       }
     }
+    if constexpr (!PART)
+      while (q < 4) fold();  // the last quarter, and any empty ones after the steps
   } else
   for (int k0 = 0; k0 < K; k0 += BK) {
     // ---- stage A
@@ -217,10 +243,25 @@ __global__ __launch_bounds__(BM == 64 ? 256 : 64) void gemm_tile64(GemmArgs a) {
 
   // ---- epilogue. 16 x 16 blocks: lane holds column lane % 16, rows 4 (lane / 16) + r.
   // 32 x 32 block: lane holds column lane % 32, rows 8 (i / 4) + 4 (lane / 32) + i % 4.
+  if constexpr (PART) {
+    // the quarter's sums, at [quarter][matrix][M][N] of a.part
+    float* const dst = a.part + (int64_t)blockIdx.z * NB * M * a.N;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int bi = 0; bi < SUB; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < SUB; ++bj)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int m = m0 + wm * 32 + bi * 16 + (lane >> 4) * 4 + r, nc = n0 + wn * 32 + bj * 16 + (lane & 15);
+            if (m < M && nc < a.N) dst[((int64_t)nb * M + m) * a.N + nc] = acc[nb][bi][bj][r];
+          }
+    return;
+  }
   // the 16 outputs of a lane: (row, column, value, SwiGLU up value); the residual values are
   // all requested before any is updated
-  // (float32 16-row tiles: one 16 x 16 block per wave, NE = 4 outputs per lane)
-  constexpr int NE = F32 ? SUB * SUB * 4 : 16;
+  constexpr int NE = 16;
   int om[16], on[16];
   float ov[16], ou[16];
   if constexpr (F32) {
@@ -233,8 +274,8 @@ __global__ __launch_bounds__(BM == 64 ? 256 : 64) void gemm_tile64(GemmArgs a) {
           const int e = (bi * SUB + bj) * 4 + r;
           om[e] = m0 + wm * 32 + bi * 16 + (lane >> 4) * 4 + r;
           on[e] = n0 + wn * 32 + bj * 16 + (lane & 15);
-          ov[e] = acc[0][bi][bj][r];
-          ou[e] = acc[NB - 1][bi][bj][r];
+          ov[e] = sum[0][bi][bj][r];
+          ou[e] = sum[NB - 1][bi][bj][r];
         }
   } else {
 #pragma unroll
@@ -268,34 +309,73 @@ __global__ __launch_bounds__(BM == 64 ? 256 : 64) void gemm_tile64(GemmArgs a) {
   }
 }
 
-template <int WF, int EPI, int BM>
+template <int WF, int EPI, bool PART>
 static hipError_t tile64_go(const GemmArgs& a, hipStream_t s) {
-  // float32: the stage ring in dynamic LDS (8 stages x (1 + NB) operands x BM rows x 64 B)
+  // float32: the stage ring in dynamic LDS (8 stages x (1 + NB) operands x 64 rows x 64 B)
   constexpr int NB = EPI == EPI_SWIGLU ? 2 : 1;
-  const uint32_t lds = WF == DEC_F32 ? 8 * (1 + NB) * BM * 16 * 4 : 0;
+  const uint32_t lds = WF == DEC_F32 ? 8 * (1 + NB) * 64 * 16 * 4 : 0;
   if (lds) {
     static bool attr = false;  // raise the dynamic LDS limit once per instantiation
     if (!attr) {
-      hipError_t e = hipFuncSetAttribute((const void*)gemm_tile64<WF, EPI, BM>,
+      hipError_t e = hipFuncSetAttribute((const void*)gemm_tile64<WF, EPI, PART>,
                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       if (e != hipSuccess) return e;
       attr = true;
     }
   }
-  const dim3 g((a.N + BM - 1) / BM, (a.M + BM - 1) / BM);
-  launch_kernel(gemm_tile64<WF, EPI, BM>, g, dim3(BM == 64 ? 256 : 64), lds, s, a);
+  const dim3 g((a.N + 63) / 64, (a.M + 63) / 64, PART ? 4 : 1);
+  launch_kernel(gemm_tile64<WF, EPI, PART>, g, dim3(256), lds, s, a);
   return hipGetLastError();
+}
+
+// The four quarter sums of gemm_tile64<..., PART> added in quarter order, then the product's
+// epilogue, with the same arithmetic as the tile kernel's own epilogue.
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_f32_combine(GemmArgs a) {
+  constexpr int NB = EPI == EPI_SWIGLU ? 2 : 1;
+  const int64_t plane = (int64_t)a.M * a.N, total = plane;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int m = (int)(i / a.N), nc = (int)(i - (int64_t)m * a.N);
+    float v[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float x = a.part[(int64_t)nb * plane + i];
+#pragma unroll
+      for (int q = 1; q < 4; ++q) x = x + a.part[((int64_t)q * NB + nb) * plane + i];
+      v[nb] = x;
+    }
+    const int64_t o = (int64_t)m * a.ldc + nc;
+    if constexpr (EPI == EPI_STORE) {
+      ((float*)a.C)[o] = v[0];
+    } else if constexpr (EPI == EPI_RESID) {
+      ((float*)a.C)[o] = ((const float*)a.C)[o] + v[0];
+    } else {
+      const float y = silu_mul(v[0], v[NB - 1]);
+      if (a.c_bf16)
+        ((uint16_t*)a.C)[o] = f32_to_bf16_bits(y);
+      else
+        ((float*)a.C)[o] = y;
+    }
+  }
 }
 
 template <int WF, int EPI>
 static hipError_t tile64_pick(const GemmArgs& a, hipStream_t s) {
-  // float32: 64 x 64 tiles (4 waves) when there are at least 256 of them, else single-wave
-  // 32 x 32 tiles when there are at least 512, else 16 x 16 (the same results either way)
+  // float32 products whose 64 x 64 grid has fewer than 256 tiles split K into its quarters over
+  // blocks when the partial buffer holds them (the same results either way)
   if constexpr (WF == DEC_F32) {
-    auto tiles = [&](int t) { return (int64_t)((a.N + t - 1) / t) * ((a.M + t - 1) / t); };
-    if (tiles(64) < 256) return tiles(32) >= 512 ? tile64_go<WF, EPI, 32>(a, s) : tile64_go<WF, EPI, 16>(a, s);
+    constexpr int NB = EPI == EPI_SWIGLU ? 2 : 1;
+    const int64_t tiles = (int64_t)((a.N + 63) / 64) * ((a.M + 63) / 64);
+    if (tiles < 256 && a.part && 4ll * NB * a.M * a.N <= a.part_floats) {
+      hipError_t e = tile64_go<WF, EPI, true>(a, s);
+      if (e != hipSuccess) return e;
+      const int64_t total = (int64_t)a.M * a.N;
+      const int blocks = (int)std::min<int64_t>((total + 255) / 256, 4096);
+      launch_kernel(gemm_f32_combine<EPI>, dim3(blocks), dim3(256), 0u, s, a);
+      return hipGetLastError();
+    }
   }
-  return tile64_go<WF, EPI, 64>(a, s);
+  return tile64_go<WF, EPI, false>(a, s);
 }
 
 template <int WF>

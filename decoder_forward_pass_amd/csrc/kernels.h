@@ -75,6 +75,10 @@ struct AttnRowsArgs {
 };
 int attn_rows_chunk(int head_dim, bool kv_f16, int group);
 hipError_t launch_attn_rows(const AttnRowsArgs& a, hipStream_t s);
+// The same partials kept in LDS and merged as launch_attn_combine does (identical results), one
+// workgroup per (row, KV head), when a.n_chunks <= attn_rows_merged_max_chunks(D, group)
+int attn_rows_merged_max_chunks(int head_dim, int group);
+hipError_t launch_attn_rows_merged(const AttnRowsArgs& a, void* o, bool out_bf16, hipStream_t s);
 
 // Decode attention: one workgroup per (row, KV head), or per (row, segment, KV head) for rows
 // split into segments (a.b.dec_items). It first applies the q/k norm and RoPE of the row
@@ -131,6 +135,10 @@ struct GemmArgs {
   // the block's vocabulary share and its lowest id, at [row][block] (see lmhead_decode_parts)
   float* am_v;
   int32_t* am_i;
+  // Float32 weights (optional): room for the quarter sums of products whose grid is split
+  // over K (4 * matrices * M * N floats); without it the products take the unsplit kernel
+  float* part;
+  int64_t part_floats;
 };
 hipError_t launch_gemm(int wdtype, int epi, const GemmArgs& a, hipStream_t s);
 
