@@ -6,9 +6,11 @@
 // operand.
 //
 // Batch invariance: every output element is accumulated by one MFMA instruction type per
-// weight format (v_mfma_f32_16x16x4_f32 or v_mfma_f32_32x32x16_bf16), over K in ascending
-// order into a single accumulator, with no split of K. The row's result therefore does not
-// depend on M, on the tile a row falls in, or on the other rows.
+// weight format (v_mfma_f32_16x16x4_f32 or v_mfma_f32_32x32x16_bf16) over K in ascending
+// order: bf16 and 4-bit weights into a single accumulator with no split of K, float32 weights
+// in four fixed quarters of K (set by K alone) whose sums are added in quarter order. The
+// row's result therefore does not depend on M, on the tile a row falls in, or on the other
+// rows. (The decode kernels below split K by K alone as well, over the waves of a block.)
 //
 // Epilogues: store float32 (Q/K/V, logits), add into the float32 residual stream (output
 // projection, down projection), SwiGLU silu(gate) * up on two B matrices computed by the same

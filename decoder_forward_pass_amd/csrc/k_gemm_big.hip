@@ -3,7 +3,9 @@
 // staged in LDS: uint4-g32 w = (q - zp) * scale ("Byte-identical...", "The bar we set") or
 // symmetric int4-g32 w = q * scale ("Candle model runner" 2.5), rounded to bf16.
 //
-// Tiling: a block of 8 waves computes a 256 x 256 tile of C (waves 4 x 2, 64 x 128 each). bf16
+// Tiling: a block of 8 waves computes a 256 x 256 tile of C (waves 4 x 2, 64 x 128 each), or,
+// for bf16 products whose 256 x 256 grid would not fill the chip, a 128 x 128 tile (waves 4 x 2,
+// 32 x 64 each; the same loop with half the loads per wave and a 64 KB ring). bf16
 // weights: both operands go from memory straight into LDS (direct-to-LDS loads) in K steps of
 // 32 through a ring of four stages, three steps in flight, one barrier per step. 4-bit weights:
 // K steps of 64, the next step's operands loaded into registers (and dequantised) while the
