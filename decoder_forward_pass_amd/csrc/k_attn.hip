@@ -104,25 +104,46 @@ __device__ __forceinline__ void rows_chunk(const AttnRowsArgs& a, int row, int k
     for (int e = 0; e < EPL; ++e) qv[i][e] *= qscale;
   }
 
+  // The KPI keys of one load share a pool block (B is a multiple of KPI), so its id is one
+  // scalar load. When the chunk's K and V rows fit in 128 registers of the lane (PRE), all are
+  // requested before the scores; otherwise each K row is loaded for its scores and each V row
+  // in the second pass.
+  constexpr bool PRE = KPG * EPL <= 64;
+  auto block_of = [&](int kk) -> int64_t { return table[__builtin_amdgcn_readfirstlane((key0 + kk * KPI) / B)]; };
+  auto load_row = [&](int kv_sel, int kk, float (&dst)[EPL]) __attribute__((always_inline)) {
+    const int key = key0 + kk * KPI + grp;
+    if (key < ctx) {
+      load_kv<KVT, EPL>(pool + a.pool.offset(a.layer, kv_sel, block_of(kk), kvh, key % B) + sub * EPL, dst);
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) dst[e] = 0.f;
+    }
+  };
+  float kpre[PRE ? KPG : 1][EPL], vpre[PRE ? KPG : 1][EPL];
+  if constexpr (PRE) {
+#pragma unroll
+    for (int kk = 0; kk < KPG; ++kk) {
+      load_row(0, kk, kpre[kk]);
+      load_row(1, kk, vpre[kk]);
+    }
+  }
   // pass 1: scores of this lane group's keys
   float sc[KPG][GROUP];
 #pragma unroll
   for (int kk = 0; kk < KPG; ++kk) {
-    const int key = key0 + kk * KPI + grp;
-    const bool valid = key < ctx;
-    float kv[EPL];
-    if (valid) {
-      const int64_t blk = table[key / B];
-      load_kv<KVT, EPL>(pool + a.pool.offset(a.layer, 0, blk, kvh, key % B) + sub * EPL, kv);
-    } else {
+    const bool valid = key0 + kk * KPI + grp < ctx;
+    float kr[EPL];
+    if constexpr (PRE) {
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) kv[e] = 0.f;
+      for (int e = 0; e < EPL; ++e) kr[e] = kpre[kk][e];
+    } else {
+      load_row(0, kk, kr);
     }
 #pragma unroll
     for (int i = 0; i < GROUP; ++i) {
       float d = 0.f;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) d += qv[i][e] * kv[e];
+      for (int e = 0; e < EPL; ++e) d += qv[i][e] * kr[e];
       d = group_sum<LPK>(d);
       sc[kk][i] = valid ? d : -__builtin_inff();
     }
@@ -151,15 +172,19 @@ __device__ __forceinline__ void rows_chunk(const AttnRowsArgs& a, int row, int k
   for (int kk = 0; kk < KPG; ++kk) {
     const int key = key0 + kk * KPI + grp;
     if (key < ctx) {
-      float vv[EPL];
-      const int64_t blk = table[key / B];
-      load_kv<KVT, EPL>(pool + a.pool.offset(a.layer, 1, blk, kvh, key % B) + sub * EPL, vv);
+      float v2[EPL];
+      if constexpr (PRE) {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) v2[e] = vpre[kk][e];
+      } else {
+        load_row(1, kk, v2);
+      }
 #pragma unroll
       for (int i = 0; i < GROUP; ++i) {
         const float p = exp2f(sc[kk][i] - m[i]);
         l[i] += p;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[i][e] += p * vv[e];
+        for (int e = 0; e < EPL; ++e) acc[i][e] += p * v2[e];
       }
     }
   }
