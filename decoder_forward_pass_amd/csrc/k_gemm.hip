@@ -36,6 +36,9 @@ __device__ __forceinline__ void wait_vm_stages(int later) {
   }
 }
 
+// float32 weights: stages of the direct-to-LDS ring (16 K-columns each)
+constexpr int kF32Stages = 3;
+
 // Float32 weights: K is taken in four fixed quarters of its 16-column steps (quarter q: steps
 // q nk / 4 .. (q + 1) nk / 4 - 1, set by K alone). Each quarter is accumulated from zero in
 // ascending order and the quarter sums are added in quarter order, ((p0 + p1) + p2) + p3. A
@@ -100,7 +103,7 @@ __global__ __launch_bounds__(256) void gemm_tile64(GemmArgs a) {
     // l % 4); the waves share the BM / 16 loads of each operand. The MFMA sequence is the one
     // below.
     constexpr int LPW = BM / 16 / WAVES;     // 16-row loads per operand per wave
-    constexpr int FR = 8, SROWS = BM * 16;  // stages; floats per operand per stage
+    constexpr int FR = kF32Stages, SROWS = BM * 16;  // stages; floats per operand per stage
     float* const ring = reinterpret_cast<float*>(f32_ring);
     const int nk = K / BK;
     auto kq = [&](int q) { return q * nk / 4; };  // first step of quarter q
@@ -313,9 +316,9 @@ __global__ __launch_bounds__(256) void gemm_tile64(GemmArgs a) {
 
 template <int WF, int EPI, bool PART>
 static hipError_t tile64_go(const GemmArgs& a, hipStream_t s) {
-  // float32: the stage ring in dynamic LDS (8 stages x (1 + NB) operands x 64 rows x 64 B)
+  // float32: the stage ring in dynamic LDS (stages x (1 + NB) operands x 64 rows x 64 B)
   constexpr int NB = EPI == EPI_SWIGLU ? 2 : 1;
-  const uint32_t lds = WF == DEC_F32 ? 8 * (1 + NB) * 64 * 16 * 4 : 0;
+  const uint32_t lds = WF == DEC_F32 ? kF32Stages * (1 + NB) * 64 * 16 * 4 : 0;
   if (lds) {
     static bool attr = false;  // raise the dynamic LDS limit once per instantiation
     if (!attr) {
