@@ -755,7 +755,9 @@ def main():
         result["roofline"] = dict(roofline_prefill, traffic=None)
     if sampler:
         result["sampler"] = sampler
-    result["hardware"] = hardware_line(torch)
+    if not args.copy_mb:
+        # (not in the counter runs: their reference copy must stay the largest copy dispatch)
+        result["hardware"] = hardware_line(torch)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, shape, weights, prompts)
     print(json.dumps(result), flush=True)
