@@ -195,7 +195,9 @@ def summarize_stats(stats_dir, wl_name, steps):
            f"--steps {steps} --warmup 0 --no-cpu-baseline --workload {wl_name}")
     lines = [f"# Kernel times: bench.py on {wl_name}", "", "Commands (one MI355X, repo root):", "", "```", cmd,
              f"python bench.py --summarize-stats gpurun_out/prof --workload {wl_name} --steps {steps}", "```", "",
-             f"{steps} step(s), no warm-up: one prefill of the batch plus its decode steps.", "",
+             f"{steps} timed step(s) (the workload's prefill calls, then its decode steps), no warm-up; before "
+             "them the bench runs the prefill calls once more, untimed, for its per-kernel breakdown, so each "
+             "prefill kernel appears once per step plus once.", "",
              "| kernel | calls | total ms | mean us | share |", "|---|---:|---:|---:|---:|"]
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
         t = float(r["TotalDurationNs"])
