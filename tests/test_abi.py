@@ -239,3 +239,19 @@ def test_decode_step_validation_uses_positions():
     rc, msg = B.dec_check_step(cfg, [16, 33], None, [1, 2], np.array([[1, 2], [3, 4]], np.int32),
                                B.DEC_LOGITS_LAST)
     assert rc == B.DEC_E_BLOCK
+
+
+def test_workspace_holds_one_widened_layer_for_large_4bit_prefill_calls():
+    # 4-bit weights: prefill calls of 4,096 rows or more widen one layer's seven matrices to bf16
+    # in the workspace, so the region exists from max_rows 4,096 on; bf16 weights never need it
+    # (the two configurations differ in nothing else the workspace holds)
+    m = MODELS["q06b_uint4"]
+    d, qw, kvw, ff = m.d_model, m.n_heads * m.head_dim, m.n_kv_heads * m.head_dim, m.ff_hidden
+    layer = ((qw + 2 * kvw) * d + d * qw + 2 * ff * d + d * ff) * 2
+
+    def extra(rows):
+        kw = dict(max_context=64, n_blocks=8, max_rows=rows, max_seqs=4)
+        return B.dec_workspace_bytes(make_config(m, **kw)) - B.dec_workspace_bytes(make_config(MODELS["q06b_bf16"], **kw))
+
+    assert extra(4095) == 0
+    assert extra(4096) == layer == 31_457_280
