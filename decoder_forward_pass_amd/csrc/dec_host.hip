@@ -149,7 +149,7 @@ struct Ws {
   size_t rope, meta, x, h, qkv, q, o, a, part, dpart, amax, ssq, xg, samp, counts, wide, fpart, total;
   size_t meta_ints;  // capacity of the metadata region in int32
   size_t wide_bytes;  // the widened-layer region (0: calls never widen)
-  size_t fpart_floats;  // float32 weights: the K-quarter sums of split products (0: none)
+  size_t fpart_floats;  // float32 weights: the K-part sums of split products (0: none)
   int chunk, nch_max, max_blocks_per_seq, max_tiles;
   int seg_keys, dslots;  // decode attention: keys per segment; state slots per (row, KV head)
   int act_bytes, kv_el;
@@ -209,15 +209,15 @@ Ws ws_layout(const dec_config& c, int decode_rows = 0) {
   const bool wide = !dec_only && is_q4(c.weight_dtype) && c.max_rows >= kWidenRows;
   w.wide_bytes = wide ? (qkvw * d + d * qw + 2 * ff * d + d * ff) * 2 : 0;
   w.wide = take(w.wide_bytes);
-  // float32 weights: a product whose grid of 64 x 64 tiles is under 256 splits K into quarters
-  // over blocks (m tiles * n tiles < 256), 4 * matrices * M * N floats of sums; the largest over
-  // the products for calls of up to R rows (none in the static decode scratch: those products
-  // then take the unsplit kernel, with the same results)
+  // float32 weights: a product whose grid of 64 x 64 tiles is under 256 splits K into its parts
+  // over blocks (m tiles * n tiles < 256), kF32KParts * matrices * M * N floats of sums; the
+  // largest over the products for calls of up to R rows (none in the static decode scratch:
+  // those products then take the unsplit kernel, with the same results)
   w.fpart_floats = 0;
   if (c.weight_dtype == DEC_F32 && !dec_only) {
     auto need = [&](size_t N, size_t nb) -> size_t {
       const size_t mt = 255 / ((N + 63) / 64);
-      return 4 * nb * std::min(R, 64 * mt) * N;
+      return kF32KParts * nb * std::min(R, 64 * mt) * N;
     };
     w.fpart_floats = std::max({need(qkvw, 1), need(d, 1), need(ff, 2), need((size_t)c.vocab, 1)});
   }

@@ -8,7 +8,7 @@
 // Batch invariance: every output element is accumulated by one MFMA instruction type per
 // weight format (v_mfma_f32_16x16x4_f32 or v_mfma_f32_32x32x16_bf16) over K in ascending
 // order: bf16 and 4-bit weights into a single accumulator with no split of K, float32 weights
-// in four fixed quarters of K (set by K alone) whose sums are added in quarter order. The
+// in eight fixed parts of K (set by K alone) whose sums are added in part order. The
 // row's result therefore does not depend on M, on the tile a row falls in, or on the other
 // rows. (The decode kernels below split K by K alone as well, over the waves of a block.)
 //
@@ -39,15 +39,15 @@ __device__ __forceinline__ void wait_vm_stages(int later) {
 // float32 weights: stages of the direct-to-LDS ring (16 K-columns each)
 constexpr int kF32Stages = 3;
 
-// Float32 weights: K is taken in four fixed quarters of its 16-column steps (quarter q: steps
-// q nk / 4 .. (q + 1) nk / 4 - 1, set by K alone). Each quarter is accumulated from zero in
-// ascending order and the quarter sums are added in quarter order, ((p0 + p1) + p2) + p3. A
-// block takes the four quarters in turn, or, for grids too small to fill the chip (PART), one
-// quarter (blockIdx.z) whose sums go to a.part for gemm_f32_combine; the results are the same.
+// Float32 weights: K is taken in kF32KParts = 8 fixed parts of its 16-column steps (part q:
+// steps q nk / 8 .. (q + 1) nk / 8 - 1, set by K alone). Each part is accumulated from zero in
+// ascending order and the part sums are added in part order, ((p0 + p1) + p2) + ... + p7. A
+// block takes the eight parts in turn, or, for grids too small to fill the chip (PART), one
+// part (blockIdx.z) whose sums go to a.part for gemm_f32_combine; the results are the same.
 template <int WF, int EPI, bool PART>
 __global__ __launch_bounds__(256) void gemm_tile64(GemmArgs a) {
   constexpr bool F32 = WF == DEC_F32;
-  static_assert(!PART || F32, "K quarters over blocks: float32 only");
+  static_assert(!PART || F32, "K parts over blocks: float32 only");
   constexpr int BM = 64, WAVES = 4, BN = BM;
   constexpr int SUB = 2;  // float32: 16 x 16 MFMA blocks per wave, each way
   constexpr int BK = F32 ? 16 : 64;  // elements of K per LDS tile
@@ -82,7 +82,7 @@ __global__ __launch_bounds__(256) void gemm_tile64(GemmArgs a) {
   // float32 weights: 2 x 2 blocks of 16 x 16 per wave (v_mfma_f32_16x16x4_f32); bf16 / uint4:
   // one 32 x 32 block per wave (v_mfma_f32_32x32x16_bf16, the full-rate bf16 shape)
   f32x4 acc[NB][SUB][SUB];
-  f32x4 sum[NB][SUB][SUB];  // float32: the finished quarters' sum
+  f32x4 sum[NB][SUB][SUB];  // float32: the finished parts' sum
   f32x16 acc32[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
@@ -106,7 +106,8 @@ __global__ __launch_bounds__(256) void gemm_tile64(GemmArgs a) {
     constexpr int FR = kF32Stages, SROWS = BM * 16;  // stages; floats per operand per stage
     float* const ring = reinterpret_cast<float*>(f32_ring);
     const int nk = K / BK;
-    auto kq = [&](int q) { return q * nk / 4; };  // first step of quarter q
+    constexpr int KP = kF32KParts;
+    auto kq = [&](int q) { return q * nk / KP; };  // first step of part q
     // this block's steps tbeg + u, u < n (ring stage u % FR)
     const int tbeg = PART ? kq(blockIdx.z) : 0, n = PART ? kq(blockIdx.z + 1) - tbeg : nk;
     const float* asrc[LPW];
@@ -134,8 +135,8 @@ __global__ __launch_bounds__(256) void gemm_tile64(GemmArgs a) {
       }
     };
     for (int u = 0; u < min(n, FR - 1); ++u) dma(u);
-    // a quarter ends: sum = acc (the first quarter) or sum + acc, and acc restarts; quarters
-    // end before the first step of the next one
+    // a part ends: sum = acc (the first part) or sum + acc, and acc restarts; parts end
+    // before the first step of the next one
     int q = 0;
     auto fold = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(256) void gemm_tile64(GemmArgs a) {
     };
     for (int u = 0; u < n; ++u) {
       if constexpr (!PART)
-        while (q < 3 && u == kq(q + 1)) fold();  // (empty quarters fold a zero sum)
+        while (q < KP - 1 && u == kq(q + 1)) fold();  // (empty parts fold a zero sum)
       // stage u has landed for this wave once at most the later issued stages' loads are
       // outstanding; the barrier publishes it and frees stage u - 1 (read in the last step)
       const int later = min(FR - 2, n - 1 - u);
@@ -181,7 +182,7 @@ __global__ __launch_bounds__(256) void gemm_tile64(GemmArgs a) {
       }
     }
     if constexpr (!PART)
-      while (q < 4) fold();  // the last quarter, and any empty ones after the steps
+      while (q < KP) fold();  // the last part, and any empty ones after the steps
   } else
   for (int k0 = 0; k0 < K; k0 += BK) {
     // ---- stage A
@@ -249,7 +250,7 @@ __global__ __launch_bounds__(256) void gemm_tile64(GemmArgs a) {
   // ---- epilogue. 16 x 16 blocks: lane holds column lane % 16, rows 4 (lane / 16) + r.
   // 32 x 32 block: lane holds column lane % 32, rows 8 (i / 4) + 4 (lane / 32) + i % 4.
   if constexpr (PART) {
-    // the quarter's sums, at [quarter][matrix][M][N] of a.part
+    // the part's sums, at [part][matrix][M][N] of a.part
     float* const dst = a.part + (int64_t)blockIdx.z * NB * M * a.N;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
@@ -328,12 +329,12 @@ static hipError_t tile64_go(const GemmArgs& a, hipStream_t s) {
       attr = true;
     }
   }
-  const dim3 g((a.N + 63) / 64, (a.M + 63) / 64, PART ? 4 : 1);
+  const dim3 g((a.N + 63) / 64, (a.M + 63) / 64, PART ? kF32KParts : 1);
   launch_kernel(gemm_tile64<WF, EPI, PART>, g, dim3(256), lds, s, a);
   return hipGetLastError();
 }
 
-// The four quarter sums of gemm_tile64<..., PART> added in quarter order, then the product's
+// The eight part sums of gemm_tile64<..., PART> added in part order, then the product's
 // epilogue, with the same arithmetic as the tile kernel's own epilogue.
 template <int EPI>
 __global__ __launch_bounds__(256) void gemm_f32_combine(GemmArgs a) {
@@ -346,7 +347,7 @@ __global__ __launch_bounds__(256) void gemm_f32_combine(GemmArgs a) {
     for (int nb = 0; nb < NB; ++nb) {
       float x = a.part[(int64_t)nb * plane + i];
 #pragma unroll
-      for (int q = 1; q < 4; ++q) x = x + a.part[((int64_t)q * NB + nb) * plane + i];
+      for (int q = 1; q < kF32KParts; ++q) x = x + a.part[((int64_t)q * NB + nb) * plane + i];
       v[nb] = x;
     }
     const int64_t o = (int64_t)m * a.ldc + nc;
@@ -366,12 +367,12 @@ __global__ __launch_bounds__(256) void gemm_f32_combine(GemmArgs a) {
 
 template <int WF, int EPI>
 static hipError_t tile64_pick(const GemmArgs& a, hipStream_t s) {
-  // float32 products whose 64 x 64 grid has fewer than 256 tiles split K into its quarters over
+  // float32 products whose 64 x 64 grid has fewer than 256 tiles split K into its parts over
   // blocks when the partial buffer holds them (the same results either way)
   if constexpr (WF == DEC_F32) {
     constexpr int NB = EPI == EPI_SWIGLU ? 2 : 1;
     const int64_t tiles = (int64_t)((a.N + 63) / 64) * ((a.M + 63) / 64);
-    if (tiles < 256 && a.part && 4ll * NB * a.M * a.N <= a.part_floats) {
+    if (tiles < 256 && a.part && (int64_t)kF32KParts * NB * a.M * a.N <= a.part_floats) {
       hipError_t e = tile64_go<WF, EPI, true>(a, s);
       if (e != hipSuccess) return e;
       const int64_t total = (int64_t)a.M * a.N;

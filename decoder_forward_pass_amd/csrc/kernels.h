@@ -135,11 +135,14 @@ struct GemmArgs {
   // the block's vocabulary share and its lowest id, at [row][block] (see lmhead_decode_parts)
   float* am_v;
   int32_t* am_i;
-  // Float32 weights (optional): room for the quarter sums of products whose grid is split
-  // over K (4 * matrices * M * N floats); without it the products take the unsplit kernel
+  // Float32 weights (optional): room for the part sums of products whose grid is split over K
+  // (kF32KParts * matrices * M * N floats); without it the products take the unsplit kernel
   float* part;
   int64_t part_floats;
 };
+// Float32 products take K in this many fixed parts (part q: steps q * nk / 8 up to the next), each
+// accumulated from zero, the part sums then added in order
+constexpr int kF32KParts = 8;
 hipError_t launch_gemm(int wdtype, int epi, const GemmArgs& a, hipStream_t s);
 
 // Prefill GEMM for bf16 / 4-bit weights: 256 x 256 block tiles staged through LDS, the same

@@ -3,7 +3,7 @@ dec_decode_step, through the C ABI: the same logits and greedy ids bit for bit, 
 written to the pool, on two calls in a row (the second with fewer sequences), on the full-width
 two-layer decoder (decode GEMMs, LM-head candidates, a row long enough for the split attention's
 segment states) and on the tiny float32 decoder (the two-pass argmax; the static array holds
-no K-quarter sums, so its float32 products add the quarters inside one block where the workspace
+no K-part sums, so its float32 products add the parts inside one block where the workspace
 step splits them over blocks). A step whose scratch would not fit the static array is refused
 before anything runs."""
 
