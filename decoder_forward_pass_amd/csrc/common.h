@@ -129,6 +129,24 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int o = WIDTH / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, WIDTH);
   return v;
 }
+// ---- RMSNorm of one row of d = 256 * VPL floats by one wave ("Candle model runner" 2.4:
+// x / sqrt(mean(x^2) + eps) * g): lane l holds the row's float4s l + 64 j, j < VPL. Every
+// kernel that normalises a row this way calls these, so a row gets the same bits whichever
+// kernel computes it (contraction off: no kernel may fuse a square into a sum differently).
+template <int VPL>
+__device__ __forceinline__ float rms_inv_row(const float4 (&v)[VPL], int d, float eps) {
+#pragma clang fp contract(off)
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) ss = ss + (((v[j].x * v[j].x + v[j].y * v[j].y) + v[j].z * v[j].z) + v[j].w * v[j].w);
+  ss = wave_sum<64>(ss);
+  return 1.0f / sqrtf(ss / (float)d + eps);
+}
+__device__ __forceinline__ float4 rms_scale4(float4 v, float inv, float4 g) {
+#pragma clang fp contract(off)
+  return make_float4(v.x * inv * g.x, v.y * inv * g.y, v.z * inv * g.z, v.w * inv * g.w);
+}
+
 template <int WIDTH>
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -564,8 +564,9 @@ int run_forward(dec_ctx* ctx, uint8_t* base, const Ws& w, hipStream_t st, const 
   // Its RMSNorm is deferred: the embedding and the residual epilogues write, beside x, the
   // residual's 16-column sums of squares and xg = bf16(x * g) with the gain g of the norm that
   // reads x next; the normalising products take xg as their input and scale each output row
-  // by 1 / rms(x), so decode needs no separate RMSNorm launch. Prefill calls always take the
-  // tile GEMM after an RMSNorm launch.
+  // by 1 / rms(x), so decode needs no separate RMSNorm launch. Prefill calls take the tile
+  // GEMMs after an RMSNorm, launched on its own or (float32 residual products split over K)
+  // written by the product's combine.
   const bool dgemm = decode && gemm_decode_supported(c.weight_dtype, d) &&
                      gemm_decode_supported(c.weight_dtype, qw) && gemm_decode_supported(c.weight_dtype, ff);
   // Prefill calls with bf16 / uint4 weights take the 256 x 256 tile GEMM, which also applies
@@ -595,6 +596,23 @@ int run_forward(dec_ctx* ctx, uint8_t* base, const Ws& w, hipStream_t st, const 
     if (mid) return launch_gemm_mid(wf, epi, g, st);
     return launch_gemm(wf, epi, g, st);
   };
+  // Float32 residual products that split K over blocks write the next RMSNorm's output h
+  // themselves, in their combine (same arithmetic as the norm launch): set the product's norm
+  // arguments when it does, and report whether it does
+  auto fuse_norm = [&](GemmArgs& g0, int wf, const float* gain) {
+    if (dgemm || big || act_bf16) return false;
+    GemmArgs t = g0;
+    t.part = (float*)(base + w.fpart);
+    t.part_floats = (int64_t)w.fpart_floats;
+    t.norm_g = gain;
+    t.norm_out = (float*)h;
+    t.norm_eps = c.rms_eps;
+    if (!gemm_fuses_norm(wf, EPI_RESID, t)) return false;
+    g0.norm_g = t.norm_g;
+    g0.norm_out = t.norm_out;
+    g0.norm_eps = t.norm_eps;
+    return true;
+  };
   // A of a normalising GEMM: the residual itself (decode GEMM) or the RMSNorm output
   // (gain: the norm's gain, applied to xg by the product that wrote it)
   auto norm_input = [&](GemmArgs& g, const float* gain) {
@@ -608,6 +626,7 @@ int run_forward(dec_ctx* ctx, uint8_t* base, const Ws& w, hipStream_t st, const 
 
   TLAUNCH(DEC_K_EMBED, launch_embed(tok_dev ? tok_dev : b.row_tok, N, c.vocab, d, c.weight_dtype, ctx->embed, x,
                                     dgemm ? ssq : nullptr, dgemm ? xg : nullptr, ctx->layers[0].attn_norm, st));
+  bool h_ready = false;  // h already holds this layer's attention-norm output (fused above)
   for (int l = 0; l < c.n_layers; ++l) {
     LayerW Lw;
     if (widen) {
@@ -627,7 +646,9 @@ int run_forward(dec_ctx* ctx, uint8_t* base, const Ws& w, hipStream_t st, const 
       TLAUNCH(DEC_K_WIDEN, launch_widen_q4(c.weight_dtype, src, cols, offs, 7, wb, st));
     }
     const LayerW& L = widen ? Lw : ctx->layers[l];
-    if (!dgemm) TLAUNCH(DEC_K_RMSNORM, launch_rmsnorm(x, nullptr, N, d, L.attn_norm, c.rms_eps, h, act_bf16, st));
+    if (!dgemm && !h_ready)
+      TLAUNCH(DEC_K_RMSNORM, launch_rmsnorm(x, nullptr, N, d, L.attn_norm, c.rms_eps, h, act_bf16, st));
+    h_ready = false;
     GemmArgs g{};
     norm_input(g, L.attn_norm);
     g.M = N; g.N = qkvw; g.K = d;
@@ -663,8 +684,10 @@ int run_forward(dec_ctx* ctx, uint8_t* base, const Ws& w, hipStream_t st, const 
     g.seg[0] = L.wo; g.nseg = 1; g.C = x; g.ldc = d;
     g.ssq_out = dgemm ? ssq : nullptr;
     g.xg_out = dgemm ? xg : nullptr; g.gain_next = L.ffn_norm;
+    const bool o_norm = fuse_norm(g, lwf, L.ffn_norm);
     TLAUNCH(DEC_K_GEMM_O, gemm(EPI_RESID, g, lwf));
-    if (!dgemm) TLAUNCH(DEC_K_RMSNORM, launch_rmsnorm(x, nullptr, N, d, L.ffn_norm, c.rms_eps, h, act_bf16, st));
+    if (!dgemm && !o_norm)
+      TLAUNCH(DEC_K_RMSNORM, launch_rmsnorm(x, nullptr, N, d, L.ffn_norm, c.rms_eps, h, act_bf16, st));
     g = GemmArgs{};
     norm_input(g, L.ffn_norm);
     g.M = N; g.N = ff; g.K = d;
@@ -676,6 +699,7 @@ int run_forward(dec_ctx* ctx, uint8_t* base, const Ws& w, hipStream_t st, const 
     g.ssq_out = dgemm ? ssq : nullptr;
     g.xg_out = dgemm ? xg : nullptr;
     g.gain_next = l + 1 < c.n_layers ? ctx->layers[l + 1].attn_norm : ctx->final_norm;
+    if (l + 1 < c.n_layers) h_ready = fuse_norm(g, lwf, ctx->layers[l + 1].attn_norm);
     TLAUNCH(DEC_K_GEMM_DOWN, gemm(EPI_RESID, g, lwf));
   }
   if (b.n_out > 0 && logits) {

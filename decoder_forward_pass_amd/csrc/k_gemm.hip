@@ -365,16 +365,67 @@ __global__ __launch_bounds__(256) void gemm_f32_combine(GemmArgs a) {
   }
 }
 
+// EPI_RESID with the row's RMSNorm: one wave per row m of N = 256 VPL columns. The new x is
+// formed per element exactly as in gemm_f32_combine (parts in order, then old x + sum) and
+// normalised as launch_rmsnorm does (rms_inv_row / rms_scale4, the same lane layout).
+template <int VPL>
+__global__ __launch_bounds__(64) void gemm_f32_combine_norm(GemmArgs a) {
+  const int m = blockIdx.x, lane = threadIdx.x;
+  const int64_t plane = (int64_t)a.M * a.N;
+  float* xr = (float*)a.C + (int64_t)m * a.ldc;
+  const float4* g4 = (const float4*)a.norm_g;
+  float4 v[VPL], gv[VPL];
+#pragma unroll
+  for (int j = 0; j < VPL; ++j) {
+    const int c = 4 * (lane + 64 * j);
+    const float* p = a.part + (int64_t)m * a.N + c;
+    float4 t = *(const float4*)p;
+#pragma unroll
+    for (int q = 1; q < kF32KParts; ++q) {
+      const float4 u = *(const float4*)(p + q * plane);
+      t = make_float4(t.x + u.x, t.y + u.y, t.z + u.z, t.w + u.w);
+    }
+    const float4 old = *(const float4*)(xr + c);
+    v[j] = make_float4(old.x + t.x, old.y + t.y, old.z + t.z, old.w + t.w);
+    gv[j] = g4[lane + 64 * j];
+    *(float4*)(xr + c) = v[j];
+  }
+  const float inv = rms_inv_row<VPL>(v, a.N, a.norm_eps);
+#pragma unroll
+  for (int j = 0; j < VPL; ++j)
+    *(float4*)(a.norm_out + (int64_t)m * a.N + 4 * (lane + 64 * j)) = rms_scale4(v[j], inv, gv[j]);
+}
+
+// float32 products whose 64 x 64 grid has fewer than 256 tiles split K into its parts over
+// blocks when the partial buffer holds them (the same results either way)
+static bool f32_splits(int epi, const GemmArgs& a) {
+  const int NB = epi == EPI_SWIGLU ? 2 : 1;
+  const int64_t tiles = (int64_t)((a.N + 63) / 64) * ((a.M + 63) / 64);
+  return tiles < 256 && a.part && (int64_t)kF32KParts * NB * a.M * a.N <= a.part_floats;
+}
+
+bool gemm_fuses_norm(int wdtype, int epi, const GemmArgs& a) {
+  const int n = a.N;
+  return wdtype == DEC_F32 && epi == EPI_RESID && a.norm_out && a.norm_g && a.M > 0 && a.ldc % 4 == 0 &&
+         (n == 256 || n == 512 || n == 1024 || n == 2048 || n == 4096) && f32_splits(epi, a);
+}
+
 template <int WF, int EPI>
 static hipError_t tile64_pick(const GemmArgs& a, hipStream_t s) {
-  // float32 products whose 64 x 64 grid has fewer than 256 tiles split K into its parts over
-  // blocks when the partial buffer holds them (the same results either way)
   if constexpr (WF == DEC_F32) {
-    constexpr int NB = EPI == EPI_SWIGLU ? 2 : 1;
-    const int64_t tiles = (int64_t)((a.N + 63) / 64) * ((a.M + 63) / 64);
-    if (tiles < 256 && a.part && (int64_t)kF32KParts * NB * a.M * a.N <= a.part_floats) {
+    if (f32_splits(EPI, a)) {
       hipError_t e = tile64_go<WF, EPI, true>(a, s);
       if (e != hipSuccess) return e;
+      if (gemm_fuses_norm(WF, EPI, a)) {
+        switch (a.N) {
+          case 256: launch_kernel(gemm_f32_combine_norm<1>, dim3(a.M), dim3(64), 0u, s, a); break;
+          case 512: launch_kernel(gemm_f32_combine_norm<2>, dim3(a.M), dim3(64), 0u, s, a); break;
+          case 1024: launch_kernel(gemm_f32_combine_norm<4>, dim3(a.M), dim3(64), 0u, s, a); break;
+          case 2048: launch_kernel(gemm_f32_combine_norm<8>, dim3(a.M), dim3(64), 0u, s, a); break;
+          default: launch_kernel(gemm_f32_combine_norm<16>, dim3(a.M), dim3(64), 0u, s, a); break;
+        }
+        return hipGetLastError();
+      }
       const int64_t total = (int64_t)a.M * a.N;
       const int blocks = (int)std::min<int64_t>((total + 255) / 256, 4096);
       launch_kernel(gemm_f32_combine<EPI>, dim3(blocks), dim3(256), 0u, s, a);

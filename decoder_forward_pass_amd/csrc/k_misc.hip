@@ -108,7 +108,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
 }
 
 // Widths that are multiples of 256: each lane loads its d/256 float4 of the row at once, the
-// sum of squares is added per lane in a fixed order and then by a butterfly.
+// sum of squares is added per lane in a fixed order and then by a butterfly (rms_inv_row).
 template <bool BF16_OUT, int VPL>
 __global__ __launch_bounds__(256) void rmsnorm_vec_kernel(const float* __restrict__ x,
                                                           const int32_t* __restrict__ rows, int n, int d,
@@ -126,23 +126,18 @@ __global__ __launch_bounds__(256) void rmsnorm_vec_kernel(const float* __restric
     v[j] = xr[lane + 64 * j];
     gv[j] = g4[lane + 64 * j];
   }
-  float ss = 0.f;
-#pragma unroll
-  for (int j = 0; j < VPL; ++j) ss += v[j].x * v[j].x + v[j].y * v[j].y + v[j].z * v[j].z + v[j].w * v[j].w;
-  ss = wave_sum<64>(ss);
-  const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+  const float inv = rms_inv_row<VPL>(v, d, eps);
 #pragma unroll
   for (int j = 0; j < VPL; ++j) {
-    const float y0 = v[j].x * inv * gv[j].x, y1 = v[j].y * inv * gv[j].y;
-    const float y2 = v[j].z * inv * gv[j].z, y3 = v[j].w * inv * gv[j].w;
+    const float4 y = rms_scale4(v[j], inv, gv[j]);
     const int64_t o = (int64_t)r * d + 4 * (lane + 64 * j);
     if constexpr (BF16_OUT) {
       u32x2 w;
-      w[0] = pack_bf16x2(y0, y1);
-      w[1] = pack_bf16x2(y2, y3);
+      w[0] = pack_bf16x2(y.x, y.y);
+      w[1] = pack_bf16x2(y.z, y.w);
       *(u32x2*)((uint16_t*)out + o) = w;
     } else {
-      *(float4*)((float*)out + o) = make_float4(y0, y1, y2, y3);
+      *(float4*)((float*)out + o) = y;
     }
   }
 }

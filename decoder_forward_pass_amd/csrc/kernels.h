@@ -139,11 +139,21 @@ struct GemmArgs {
   // (kF32KParts * matrices * M * N floats); without it the products take the unsplit kernel
   float* part;
   int64_t part_floats;
+  // Float32 residual products split over K (optional, norm_out set): the combine also writes
+  // the RMSNorm of each new row of x, x / rms(x) * norm_g with norm_eps, to norm_out (float32
+  // [M][N]) with the arithmetic of launch_rmsnorm, so the caller skips that launch; only when
+  // gemm_fuses_norm says so
+  const float* norm_g;
+  float* norm_out;
+  float norm_eps;
 };
 // Float32 products take K in this many fixed parts (part q: steps q * nk / 8 up to the next), each
 // accumulated from zero, the part sums then added in order
 constexpr int kF32KParts = 8;
 hipError_t launch_gemm(int wdtype, int epi, const GemmArgs& a, hipStream_t s);
+// launch_gemm with these arguments also writes the RMSNorm of the new x (norm_out): a float32
+// residual product (EPI_RESID) that splits K over blocks, with N one of the vector norm's widths
+bool gemm_fuses_norm(int wdtype, int epi, const GemmArgs& a);
 
 // Prefill GEMM for bf16 / 4-bit weights: 256 x 256 block tiles staged through LDS, the same
 // per-element MFMA sequence as launch_gemm (identical results). Epilogues EPI_STORE,
