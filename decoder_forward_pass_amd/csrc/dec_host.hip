@@ -655,9 +655,18 @@ int run_forward(dec_ctx* ctx, uint8_t* base, const Ws& w, hipStream_t st, const 
     g.seg[0] = L.wq; g.seg[1] = L.wk; g.seg[2] = L.wv; g.nseg = 3;
     g.C = qkv; g.ldc = qkvw;
     QkRopeArgs qa{qkv, L.q_norm, L.k_norm, rope, q, pool, l, H, Hkv, D, c.rms_eps, kv_f16, b};
+    bool qk_done = false;  // the product's combine did the q/k norm, RoPE and K/V write
     if (big) {
       TLAUNCH(DEC_K_GEMM_QKV, launch_gemm_big(lwf, EPI_QKV, g, &qa, st));
     } else {
+      if (!decode && !dgemm) {
+        GemmArgs t = g;
+        t.part = (float*)(base + w.fpart);
+        t.part_floats = (int64_t)w.fpart_floats;
+        t.qk = &qa;
+        qk_done = gemm_fuses_qk(lwf, EPI_STORE, t);
+        if (qk_done) g.qk = &qa;
+      }
       TLAUNCH(DEC_K_GEMM_QKV, gemm(EPI_STORE, g, lwf));
     }
     if (decode) {
@@ -665,7 +674,7 @@ int run_forward(dec_ctx* ctx, uint8_t* base, const Ws& w, hipStream_t st, const 
       TLAUNCH(DEC_K_ATTN_ROWS, launch_attn_decode(qa, ra, o, act_bf16, st));
       if (b.n_dec_items) TLAUNCH(DEC_K_ATTN_COMBINE, launch_attn_decode_combine(ra, o, act_bf16, st));
     } else {
-      if (!big) TLAUNCH(DEC_K_QK_ROPE_KV, launch_qk_rope_kv(qa, st));
+      if (!big && !qk_done) TLAUNCH(DEC_K_QK_ROPE_KV, launch_qk_rope_kv(qa, st));
       if (w.flash) {
         AttnPrefillArgs pa{(const uint16_t*)q, pool, l, H, Hkv, D, o, act_bf16, b};
         TLAUNCH(DEC_K_ATTN_PREFILL, launch_attn_prefill(pa, st));

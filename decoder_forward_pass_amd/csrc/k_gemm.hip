@@ -396,12 +396,44 @@ __global__ __launch_bounds__(64) void gemm_f32_combine_norm(GemmArgs a) {
     *(float4*)(a.norm_out + (int64_t)m * a.N + 4 * (lane + 64 * j)) = rms_scale4(v[j], inv, gv[j]);
 }
 
+// EPI_STORE of the Q|K|V product with its q/k norm, RoPE and K/V write: one wave per (row,
+// head), lane j < D/2 summing the parts of channels j and j + D/2 as gemm_f32_combine does,
+// then the head's arithmetic of qk_rope_kv_kernel (qk_rope_kv_head); C is not written.
+template <bool KV_F16>
+__global__ __launch_bounds__(256) void gemm_f32_combine_qk(GemmArgs a, QkRopeArgs qk) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x;
+  const int hh = blockIdx.y * 4 + (threadIdx.x >> 6);
+  const int H = qk.n_heads, Hkv = qk.n_kv_heads, D = qk.head_dim, half = D / 2;
+  if (hh >= H + 2 * Hkv) return;
+  const int64_t plane = (int64_t)a.M * a.N;
+  float x[2] = {0.f, 0.f};
+  if (lane < half) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int64_t i = (int64_t)r * a.N + (int64_t)hh * D + lane + e * half;
+      float t = a.part[i];
+#pragma unroll
+      for (int q = 1; q < kF32KParts; ++q) t = t + a.part[q * plane + i];
+      x[e] = t;
+    }
+  }
+  qk_rope_kv_head<KV_F16>(qk, r, hh, lane, x[0], x[1]);
+}
+
 // float32 products whose 64 x 64 grid has fewer than 256 tiles split K into its parts over
 // blocks when the partial buffer holds them (the same results either way)
 static bool f32_splits(int epi, const GemmArgs& a) {
   const int NB = epi == EPI_SWIGLU ? 2 : 1;
   const int64_t tiles = (int64_t)((a.N + 63) / 64) * ((a.M + 63) / 64);
   return tiles < 256 && a.part && (int64_t)kF32KParts * NB * a.M * a.N <= a.part_floats;
+}
+
+bool gemm_fuses_qk(int wdtype, int epi, const GemmArgs& a) {
+  if (wdtype != DEC_F32 || epi != EPI_STORE || !a.qk) return false;
+  const QkRopeArgs& q = *a.qk;
+  return a.M > 0 && a.M == q.b.n_rows && a.N == (q.n_heads + 2 * q.n_kv_heads) * q.head_dim &&
+         q.head_dim <= 128 && f32_splits(epi, a);
 }
 
 bool gemm_fuses_norm(int wdtype, int epi, const GemmArgs& a) {
@@ -416,6 +448,14 @@ static hipError_t tile64_pick(const GemmArgs& a, hipStream_t s) {
     if (f32_splits(EPI, a)) {
       hipError_t e = tile64_go<WF, EPI, true>(a, s);
       if (e != hipSuccess) return e;
+      if (gemm_fuses_qk(WF, EPI, a)) {
+        const dim3 g(a.M, (a.qk->n_heads + 2 * a.qk->n_kv_heads + 3) / 4);
+        if (a.qk->kv_f16)
+          launch_kernel(gemm_f32_combine_qk<true>, g, dim3(256), 0u, s, a, *a.qk);
+        else
+          launch_kernel(gemm_f32_combine_qk<false>, g, dim3(256), 0u, s, a, *a.qk);
+        return hipGetLastError();
+      }
       if (gemm_fuses_norm(WF, EPI, a)) {
         switch (a.N) {
           case 256: launch_kernel(gemm_f32_combine_norm<1>, dim3(a.M), dim3(64), 0u, s, a); break;

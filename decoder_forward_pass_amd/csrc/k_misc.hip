@@ -185,43 +185,9 @@ __global__ __launch_bounds__(256) void qk_rope_kv_kernel(QkRopeArgs a) {
   const int hh = blockIdx.y * 4 + (threadIdx.x >> 6);
   const int H = a.n_heads, Hkv = a.n_kv_heads, D = a.head_dim, half = D / 2;
   if (hh >= H + 2 * Hkv) return;
-  const int pos = a.b.row_pos[r];
   const float* src = a.qkv + (int64_t)r * (H + 2 * Hkv) * D + (int64_t)hh * D;
   const bool active = lane < half;
-  float x1 = active ? src[lane] : 0.f;
-  float x2 = active ? src[lane + half] : 0.f;
-  const bool is_v = hh >= H + Hkv;
-  if (!is_v) {
-    const float2 cs = active ? a.rope[(int64_t)pos * half + lane] : make_float2(1.f, 0.f);
-    norm_rope_pair(x1, x2, hh < H ? a.q_norm : a.k_norm, cs, lane, D, a.eps);
-  }
-  if (!active) return;
-  if (hh < H) {
-    const int64_t o = ((int64_t)r * H + hh) * D;
-    if constexpr (KV_F16) {
-      uint16_t* q = (uint16_t*)a.q_out;
-      q[o + lane] = f32_to_f16_bits(x1);
-      q[o + lane + half] = f32_to_f16_bits(x2);
-    } else {
-      float* q = (float*)a.q_out;
-      q[o + lane] = x1;
-      q[o + lane + half] = x2;
-    }
-    return;
-  }
-  const int kvh = is_v ? hh - H - Hkv : hh - H;
-  const int seq = a.b.row_seq[r];
-  const int64_t blk = a.b.block_tables[(int64_t)seq * a.b.tbl_stride + (pos >> a.pool.block_shift)];
-  const int64_t off = a.pool.offset(a.layer, is_v ? 1 : 0, blk, kvh, pos & (a.pool.block_tokens - 1));
-  if constexpr (KV_F16) {
-    uint16_t* p = (uint16_t*)a.pool.base + off;
-    p[lane] = f32_to_f16_bits(x1);
-    p[lane + half] = f32_to_f16_bits(x2);
-  } else {
-    float* p = (float*)a.pool.base + off;
-    p[lane] = x1;
-    p[lane + half] = x2;
-  }
+  qk_rope_kv_head<KV_F16>(a, r, hh, lane, active ? src[lane] : 0.f, active ? src[lane + half] : 0.f);
 }
 
 hipError_t launch_qk_rope_kv(const QkRopeArgs& a, hipStream_t s) {

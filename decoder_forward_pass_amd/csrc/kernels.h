@@ -60,6 +60,49 @@ struct QkRopeArgs {
   BatchDev b;
 };
 hipError_t launch_qk_rope_kv(const QkRopeArgs& a, hipStream_t s);
+// One (row r, head hh) of the Q|K|V row, its channels j and j + D/2 in lane j < D/2 (x1, x2):
+// q and k heads RMS-normalised over D with their gains and rotated by RoPE at the row's
+// position, q stored to q_out, k and v to the pool at (table[pos / B], pos % B) (the v head
+// as it is). Shared by qk_rope_kv_kernel and the float32 Q|K|V combine, so both give the same
+// bits.
+template <bool KV_F16>
+__device__ __forceinline__ void qk_rope_kv_head(const QkRopeArgs& a, int r, int hh, int lane, float x1, float x2) {
+  const int H = a.n_heads, Hkv = a.n_kv_heads, D = a.head_dim, half = D / 2;
+  const int pos = a.b.row_pos[r];
+  const bool active = lane < half;
+  const bool is_v = hh >= H + Hkv;
+  if (!is_v) {
+    const float2 cs = active ? a.rope[(int64_t)pos * half + lane] : make_float2(1.f, 0.f);
+    norm_rope_pair(x1, x2, hh < H ? a.q_norm : a.k_norm, cs, lane, D, a.eps);
+  }
+  if (!active) return;
+  if (hh < H) {
+    const int64_t o = ((int64_t)r * H + hh) * D;
+    if constexpr (KV_F16) {
+      uint16_t* q = (uint16_t*)a.q_out;
+      q[o + lane] = f32_to_f16_bits(x1);
+      q[o + lane + half] = f32_to_f16_bits(x2);
+    } else {
+      float* q = (float*)a.q_out;
+      q[o + lane] = x1;
+      q[o + lane + half] = x2;
+    }
+    return;
+  }
+  const int kvh = is_v ? hh - H - Hkv : hh - H;
+  const int seq = a.b.row_seq[r];
+  const int64_t blk = a.b.block_tables[(int64_t)seq * a.b.tbl_stride + (pos >> a.pool.block_shift)];
+  const int64_t off = a.pool.offset(a.layer, is_v ? 1 : 0, blk, kvh, pos & (a.pool.block_tokens - 1));
+  if constexpr (KV_F16) {
+    uint16_t* p = (uint16_t*)a.pool.base + off;
+    p[lane] = f32_to_f16_bits(x1);
+    p[lane + half] = f32_to_f16_bits(x2);
+  } else {
+    float* p = (float*)a.pool.base + off;
+    p[lane] = x1;
+    p[lane + half] = x2;
+  }
+}
 
 // Attention of single query rows over their sequence's paged keys, split in
 // fixed chunks of keys; writes per-chunk partial (max, sum, unnormalised acc).
@@ -146,6 +189,10 @@ struct GemmArgs {
   const float* norm_g;
   float* norm_out;
   float norm_eps;
+  // Float32 Q|K|V products split over K (optional, host pointer): the combine applies the q/k
+  // norm, RoPE and the K/V write of these arguments (qk_rope_kv_head) to the summed row
+  // instead of storing C, so the caller skips launch_qk_rope_kv; only when gemm_fuses_qk says so
+  const QkRopeArgs* qk;
 };
 // Float32 products take K in this many fixed parts (part q: steps q * nk / 8 up to the next), each
 // accumulated from zero, the part sums then added in order
@@ -154,6 +201,9 @@ hipError_t launch_gemm(int wdtype, int epi, const GemmArgs& a, hipStream_t s);
 // launch_gemm with these arguments also writes the RMSNorm of the new x (norm_out): a float32
 // residual product (EPI_RESID) that splits K over blocks, with N one of the vector norm's widths
 bool gemm_fuses_norm(int wdtype, int epi, const GemmArgs& a);
+// launch_gemm with these arguments does qk's work instead of storing C: a float32 Q|K|V product
+// (EPI_STORE, N = (H + 2 H_kv) D, one row per row of qk's batch) that splits K over blocks
+bool gemm_fuses_qk(int wdtype, int epi, const GemmArgs& a);
 
 // Prefill GEMM for bf16 / 4-bit weights: 256 x 256 block tiles staged through LDS, the same
 // per-element MFMA sequence as launch_gemm (identical results). Epilogues EPI_STORE,
