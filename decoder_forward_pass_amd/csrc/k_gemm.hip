@@ -14,7 +14,10 @@
 //
 // Epilogues: store float32 (Q/K/V, logits), add into the float32 residual stream (output
 // projection, down projection), SwiGLU silu(gate) * up on two B matrices computed by the same
-// block ("Candle model runner" 2.4, silu on the gate only).
+// block ("Candle model runner" 2.4, silu on the gate only). Float32 products split over K
+// finish in a combine kernel, which for the residual products can also write the next RMSNorm
+// and for Q|K|V in prefill applies the q/k norm, RoPE and K/V write, each through the device
+// code the standalone kernels use.
 #include "kernels.h"
 
 #include <algorithm>
