@@ -21,7 +21,10 @@ struct RowsGeom {
   static constexpr int EPL = 16 / (int)sizeof(KVT);  // elements per lane per load
   static constexpr int LPK = D / EPL;                 // lanes per key
   static constexpr int KPI = 64 / LPK;                // keys per wave-wide load
-  static constexpr int KPG = 32 / GROUP;              // keys per lane group per chunk
+  // keys per lane group per chunk: 32 / GROUP for f16 pools; for float32 pools (16 bytes hold
+  // half the channels) 16 / GROUP, so that a chunk's preloaded keys and values fit beside the
+  // rest in under 128 registers (four waves per SIMD instead of two)
+  static constexpr int KPG = (sizeof(KVT) == 4 ? 16 : 32) / GROUP;
   static constexpr int CHUNK = KPG * KPI;
 };
 
