@@ -210,16 +210,17 @@ Ws ws_layout(const dec_config& c, int decode_rows = 0) {
   w.wide_bytes = wide ? (qkvw * d + d * qw + 2 * ff * d + d * ff) * 2 : 0;
   w.wide = take(w.wide_bytes);
   // float32 weights: a product whose grid of 64 x 64 tiles is under 256 splits K into its parts
-  // over blocks (m tiles * n tiles < 256), kF32KParts * matrices * M * N floats of sums; the
+  // over blocks (m tiles * n tiles < 256), f32_k_parts(epi) * matrices * M * N floats of sums; the
   // largest over the products for calls of up to R rows (none in the static decode scratch:
   // those products then take the unsplit kernel, with the same results)
   w.fpart_floats = 0;
   if (c.weight_dtype == DEC_F32 && !dec_only) {
-    auto need = [&](size_t N, size_t nb) -> size_t {
+    auto need = [&](int epi, size_t N, size_t nb) -> size_t {
       const size_t mt = 255 / ((N + 63) / 64);
-      return kF32KParts * nb * std::min(R, 64 * mt) * N;
+      return f32_k_parts(epi) * nb * std::min(R, 64 * mt) * N;
     };
-    w.fpart_floats = std::max({need(qkvw, 1), need(d, 1), need(ff, 2), need((size_t)c.vocab, 1)});
+    w.fpart_floats = std::max({need(EPI_STORE, qkvw, 1), need(EPI_RESID, d, 1), need(EPI_SWIGLU, ff, 2),
+                               need(EPI_STORE, (size_t)c.vocab, 1)});
   }
   w.fpart = take(w.fpart_floats * 4);
   w.total = off;

@@ -8,7 +8,8 @@
 // Batch invariance: every output element is accumulated by one MFMA instruction type per
 // weight format (v_mfma_f32_16x16x4_f32 or v_mfma_f32_32x32x16_bf16) over K in ascending
 // order: bf16 and 4-bit weights into a single accumulator with no split of K, float32 weights
-// in eight fixed parts of K (set by K alone) whose sums are added in part order. The
+// in fixed parts of K (16 for the residual products, 8 for the others: set by the product
+// alone) whose sums are added in part order. The
 // row's result therefore does not depend on M, on the tile a row falls in, or on the other
 // rows. (The decode kernels below split K by K alone as well, over the waves of a block.)
 //
@@ -42,10 +43,11 @@ __device__ __forceinline__ void wait_vm_stages(int later) {
 // float32 weights: stages of the direct-to-LDS ring (16 K-columns each)
 constexpr int kF32Stages = 3;
 
-// Float32 weights: K is taken in kF32KParts = 8 fixed parts of its 16-column steps (part q:
-// steps q nk / 8 .. (q + 1) nk / 8 - 1, set by K alone). Each part is accumulated from zero in
-// ascending order and the part sums are added in part order, ((p0 + p1) + p2) + ... + p7. A
-// block takes the eight parts in turn, or, for grids too small to fill the chip (PART), one
+// Float32 weights: K is taken in P = f32_k_parts(EPI) fixed parts of its 16-column steps (part
+// q: steps q nk / P .. (q + 1) nk / P - 1, set by K and the product alone; P = 16 for the
+// residual products, 8 for the others). Each part is accumulated from zero in ascending order
+// and the part sums are added in part order, ((p0 + p1) + p2) + ... A block takes the parts in
+// turn, or, for grids too small to fill the chip (PART), one
 // part (blockIdx.z) whose sums go to a.part for gemm_f32_combine; the results are the same.
 template <int WF, int EPI, bool PART>
 __global__ __launch_bounds__(256) void gemm_tile64(GemmArgs a) {
@@ -109,7 +111,7 @@ __global__ __launch_bounds__(256) void gemm_tile64(GemmArgs a) {
     constexpr int FR = kF32Stages, SROWS = BM * 16;  // stages; floats per operand per stage
     float* const ring = reinterpret_cast<float*>(f32_ring);
     const int nk = K / BK;
-    constexpr int KP = kF32KParts;
+    constexpr int KP = f32_k_parts(EPI);
     auto kq = [&](int q) { return q * nk / KP; };  // first step of part q
     // this block's steps tbeg + u, u < n (ring stage u % FR)
     const int tbeg = PART ? kq(blockIdx.z) : 0, n = PART ? kq(blockIdx.z + 1) - tbeg : nk;
@@ -332,12 +334,12 @@ static hipError_t tile64_go(const GemmArgs& a, hipStream_t s) {
       attr = true;
     }
   }
-  const dim3 g((a.N + 63) / 64, (a.M + 63) / 64, PART ? kF32KParts : 1);
+  const dim3 g((a.N + 63) / 64, (a.M + 63) / 64, PART ? f32_k_parts(EPI) : 1);
   launch_kernel(gemm_tile64<WF, EPI, PART>, g, dim3(256), lds, s, a);
   return hipGetLastError();
 }
 
-// The eight part sums of gemm_tile64<..., PART> added in part order, then the product's
+// The part sums of gemm_tile64<..., PART> added in part order, then the product's
 // epilogue, with the same arithmetic as the tile kernel's own epilogue.
 template <int EPI>
 __global__ __launch_bounds__(256) void gemm_f32_combine(GemmArgs a) {
@@ -350,7 +352,7 @@ __global__ __launch_bounds__(256) void gemm_f32_combine(GemmArgs a) {
     for (int nb = 0; nb < NB; ++nb) {
       float x = a.part[(int64_t)nb * plane + i];
 #pragma unroll
-      for (int q = 1; q < kF32KParts; ++q) x = x + a.part[((int64_t)q * NB + nb) * plane + i];
+      for (int q = 1; q < f32_k_parts(EPI); ++q) x = x + a.part[((int64_t)q * NB + nb) * plane + i];
       v[nb] = x;
     }
     const int64_t o = (int64_t)m * a.ldc + nc;
@@ -384,7 +386,7 @@ __global__ __launch_bounds__(64) void gemm_f32_combine_norm(GemmArgs a) {
     const float* p = a.part + (int64_t)m * a.N + c;
     float4 t = *(const float4*)p;
 #pragma unroll
-    for (int q = 1; q < kF32KParts; ++q) {
+    for (int q = 1; q < f32_k_parts(EPI_RESID); ++q) {
       const float4 u = *(const float4*)(p + q * plane);
       t = make_float4(t.x + u.x, t.y + u.y, t.z + u.z, t.w + u.w);
     }
@@ -417,7 +419,7 @@ __global__ __launch_bounds__(256) void gemm_f32_combine_qk(GemmArgs a, QkRopeArg
       const int64_t i = (int64_t)r * a.N + (int64_t)hh * D + lane + e * half;
       float t = a.part[i];
 #pragma unroll
-      for (int q = 1; q < kF32KParts; ++q) t = t + a.part[q * plane + i];
+      for (int q = 1; q < f32_k_parts(EPI_STORE); ++q) t = t + a.part[q * plane + i];
       x[e] = t;
     }
   }
@@ -429,7 +431,7 @@ __global__ __launch_bounds__(256) void gemm_f32_combine_qk(GemmArgs a, QkRopeArg
 static bool f32_splits(int epi, const GemmArgs& a) {
   const int NB = epi == EPI_SWIGLU ? 2 : 1;
   const int64_t tiles = (int64_t)((a.N + 63) / 64) * ((a.M + 63) / 64);
-  return tiles < 256 && a.part && (int64_t)kF32KParts * NB * a.M * a.N <= a.part_floats;
+  return tiles < 256 && a.part && (int64_t)f32_k_parts(epi) * NB * a.M * a.N <= a.part_floats;
 }
 
 bool gemm_fuses_qk(int wdtype, int epi, const GemmArgs& a) {

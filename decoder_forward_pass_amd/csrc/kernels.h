@@ -179,7 +179,7 @@ struct GemmArgs {
   float* am_v;
   int32_t* am_i;
   // Float32 weights (optional): room for the part sums of products whose grid is split over K
-  // (kF32KParts * matrices * M * N floats); without it the products take the unsplit kernel
+  // (f32_k_parts(epi) * matrices * M * N floats); without it the products take the unsplit kernel
   float* part;
   int64_t part_floats;
   // Float32 residual products split over K (optional, norm_out set): the combine also writes
@@ -194,9 +194,10 @@ struct GemmArgs {
   // instead of storing C, so the caller skips launch_qk_rope_kv; only when gemm_fuses_qk says so
   const QkRopeArgs* qk;
 };
-// Float32 products take K in this many fixed parts (part q: steps q * nk / 8 up to the next), each
-// accumulated from zero, the part sums then added in order
-constexpr int kF32KParts = 8;
+// Float32 products take K in P fixed parts (part q: steps q * nk / P up to the next), each
+// accumulated from zero, the part sums then added in order; P is fixed per epilogue, so per
+// product: 16 for the residual products (O, down), 8 for the others
+__host__ __device__ constexpr int f32_k_parts(int epi) { return epi == EPI_RESID ? 16 : 8; }
 hipError_t launch_gemm(int wdtype, int epi, const GemmArgs& a, hipStream_t s);
 // launch_gemm with these arguments also writes the RMSNorm of the new x (norm_out): a float32
 // residual product (EPI_RESID) that splits K over blocks, with N one of the vector norm's widths

@@ -5,7 +5,7 @@ fixed before the first run).
 
 Batch invariance across the float32 paths: the 188-token prompt run alone and inside one call
 with a 2,100-token prompt must give bit-identical logits. Alone, every product's grid is small,
-so K is split into eight parts over blocks and a second kernel adds them, and the attention merges
+so K is split into parts (16 for O and down, 8 for the others) over blocks and a second kernel adds them, and the attention merges
 each row's key chunks inside one workgroup. In the 2,288-row call every product adds the parts
 inside one block, and the attention (a row of 66 chunks, beyond what the workgroup merge holds)
 writes chunk partials that a second kernel merges."""

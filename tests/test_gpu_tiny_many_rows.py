@@ -6,7 +6,7 @@ At that row count the products take paths that small calls never take, on shapes
 multiples of the tiles. bf16 weights: the output and down products (N = 64) and gate/up (192
 features) run on the 128 x 128 tiles, the LM head on the 256 x 256 tiles. uint4 weights: each
 layer's seven matrices (64 to 192 columns) are widened to bf16 first. float32 weights: every
-product adds its eight K parts inside one block, where the lone prompt's products split them
+product adds its K parts inside one block, where the lone prompt's products split them
 over blocks. The lone prompt (1,000 rows) takes the 64 x 64 tiles, dequantising uint4 in the
 products. Expected values: the library's own lone call (the results must not depend on the rows
 around a prompt, "Candle model runner" 2.4); the oracle checks the lone path in the other tests.
